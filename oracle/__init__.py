@@ -1,0 +1,20 @@
+"""CPU oracle (test infrastructure only; never called by the library)."""
+
+from .kvq_oracle import (  # noqa: F401
+    CACHE_KEYS,
+    GROUP,
+    attention,
+    decode_all,
+    decode_slab,
+    default_scale,
+    dequant_slab,
+    pack_all,
+    pack_codes,
+    pack_slab,
+    quantize_groups,
+    retained_mask,
+    slab_of,
+    split_positions,
+    unpack_codes,
+    upcast,
+)

@@ -1,0 +1,260 @@
+"""CPU oracle: group-wise asymmetric low-bit KV cache + single-token decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The HIP library never
+calls it, and it shares no code, constant or table with the HIP library.
+
+Plain NumPy, written for a reader to check against the pages by eye:
+
+* quantize side in float32 with round-half-to-even, exactly as spelled out in
+  ``quantize_groups``;
+* dequantization and attention in float64.
+
+Sources (the pages are secondary machine-written summaries; where they leave a step
+open the plainest reading is taken and listed in the design notes):
+
+* "Quantize What Counts: More for Keys, Less for Values" (technical summary,
+  methodology / results): keys and values take separate bit widths (K4V2), group
+  size 32 for keys.
+* "LogQuant: Log-Distributed 2-Bit Quantization of KV Cache" (technical summary,
+  section 2 "log-based filtering strategy", section 4 "position-independent
+  optimisation", section 5 "implementation"): newest tokens kept in full
+  precision, log-spaced full-precision tokens further back, per-channel key
+  quantization, attention over an arbitrary concatenation of full-precision and
+  quantized tokens (A.V = A_P.V_P).
+* "HeadQ" (section 2.1): score s_j = q^T k_j / sqrt(d); a constant vector added to
+  every key shifts every score by the same amount (softmax-null direction).
+* "Thin Keys, Full Values" (section 2): softmax(Q K^T / sqrt(d_select)) V with
+  d_select (key width) different from the value width.
+
+Canonical packed layout for one (b, kv-head) slab (the same index formulas appear in
+``include/kvq.h``; the oracle writes them out here independently):
+
+* retained (fp16) positions r = sorted retained set, compacted positions
+  u = sorted(the rest); Tq = len(u), groups of 32 consecutive compacted tokens;
+* k_codes  u32 [Tq, Dk*kb/32]: word w of row t holds channel w*(32/kb)+k at bits
+  [k*kb, k*kb+kb), little-endian;
+* k_scale, k_zero fp16 [Tq/32, Dk]  (one pair per token group and channel);
+* v_codes  u32 [Tq, Dv*vb/32]   (same packing along channels);
+* v_scale, v_zero fp16 [Tq, Dv/32]  (one pair per token and 32-channel group);
+* k_fp16 [R, Dk], v_fp16 [R, Dv] fp16 rows of the retained positions, ascending.
+"""
+
+import numpy as np
+
+GROUP = 32  # tokens per key group and channels per value group
+
+
+# ----------------------------------------------------------------------------- inputs
+
+def upcast(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage dtype -> float32, exactly.  bf16 arrives as uint16 bit patterns: a bf16
+    number is the upper half of the float32 with the same bits."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return (np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    if dtype == "f16":
+        return np.asarray(x, dtype=np.uint16).view(np.float16).astype(np.float32)
+    raise ValueError(dtype)
+
+
+def default_scale(Dk: int) -> np.float32:
+    """Softmax scale 1/sqrt(d) of the score s = q^T k / sqrt(d) (HeadQ 2.1; Thin Keys 2,
+    with d the key width), as one float32 value."""
+    return np.float32(1.0) / np.sqrt(np.float32(Dk))
+
+
+# ------------------------------------------------------------------------- retention
+
+def retained_mask(T: int, n_recent: int, log_window: int) -> np.ndarray:
+    """Which of the T cached positions stay in fp16 (LogQuant section 2).
+
+    * the newest ``n_recent`` positions;
+    * with W = log_window > 0, for j = 1, 2, ...: inside the span
+      [T - W*2^j, T - W*2^(j-1)) (clipped at 0), every position that is a multiple
+      of 2^j.  Going one span back doubles both the span and the stride: every 2nd
+      token in [T-2W, T-W), every 4th in [T-4W, T-2W), and so on.
+    """
+    keep = np.zeros(T, dtype=bool)
+    keep[max(0, T - n_recent):] = True
+    if log_window > 0:
+        j = 1
+        while T - log_window * 2 ** (j - 1) > 0:
+            hi = T - log_window * 2 ** (j - 1)
+            lo = max(0, T - log_window * 2 ** j)
+            pos = np.arange(lo, hi)
+            keep[pos[pos % 2 ** j == 0]] = True
+            j += 1
+    return keep
+
+
+def split_positions(T: int, n_recent: int, log_window: int):
+    """(retained positions r, quantized positions u), both ascending (LogQuant section 4:
+    the two sets are stored apart; the order inside attention does not matter)."""
+    keep = retained_mask(T, n_recent, log_window)
+    return np.nonzero(keep)[0], np.nonzero(~keep)[0]
+
+
+# ---------------------------------------------------------------------- quantization
+
+def quantize_groups(x: np.ndarray, bits: int):
+    """Asymmetric min/max quantization of each group along the last axis.
+
+    x float32 [..., n].  For each group (all float32, IEEE rounding):
+        mn, mx = min x, max x
+        s = fp16(fp32(mx - mn) / fp32(2^bits - 1))     (round to nearest even)
+        z = fp16(mn)
+        code = clamp(rint((x - z_f32) / s_f32), 0, 2^bits - 1), rint ties to even;
+        code = 0 everywhere when s == 0.
+    A stored zero of either sign is written as +0.
+    Returns codes uint8 [..., n], s and z as float16 [...].
+    """
+    x = np.asarray(x, dtype=np.float32)
+    levels = np.float32(2 ** bits - 1)
+    mn = x.min(axis=-1)
+    mx = x.max(axis=-1)
+    s16 = ((mx - mn) / levels).astype(np.float16)
+    z16 = mn.astype(np.float16)
+    s16 = np.where(s16 == 0, np.float16(0.0), s16)
+    z16 = np.where(z16 == 0, np.float16(0.0), z16)
+    s = s16.astype(np.float32)[..., None]
+    z = z16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = (x - z) / s
+    codes = np.where(s == 0, np.float32(0), np.clip(np.rint(t), np.float32(0), levels))
+    return codes.astype(np.uint8), s16, z16
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes [..., n] -> uint32 [..., n*bits/32]; code k of each word at bits [k*bits, k*bits+bits)."""
+    per = 32 // bits
+    c = np.asarray(codes, dtype=np.uint32)
+    c = c.reshape(c.shape[:-1] + (c.shape[-1] // per, per))
+    shifts = (np.arange(per, dtype=np.uint32) * np.uint32(bits))
+    return np.bitwise_or.reduce(c << shifts, axis=-1).astype(np.uint32)
+
+
+def unpack_codes(words: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of pack_codes: uint32 [..., w] -> uint8 [..., w*32/bits]."""
+    per = 32 // bits
+    w = np.asarray(words, dtype=np.uint32)[..., None]
+    shifts = (np.arange(per, dtype=np.uint32) * np.uint32(bits))
+    c = (w >> shifts) & np.uint32(2 ** bits - 1)
+    return c.reshape(c.shape[:-2] + (c.shape[-2] * per,)).astype(np.uint8)
+
+
+def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_window: int):
+    """Quantize and pack one (b, kv-head) slab.  K [T, Dk], V [T, Dv] in storage dtype.
+
+    Keys per channel over groups of 32 consecutive quantized tokens (LogQuant
+    section 5, "per-channel" keys; group 32 from "Quantize What Counts", results);
+    values per token over groups of 32 channels; retained positions copied to fp16.
+    """
+    K32 = upcast(K, dtype)
+    V32 = upcast(V, dtype)
+    T, Dk = K32.shape
+    Dv = V32.shape[1]
+    r, u = split_positions(T, n_recent, log_window)
+    Tq = len(u)
+    if Dk % GROUP or Dv % GROUP:
+        raise ValueError("head widths must be multiples of %d" % GROUP)
+    if Tq % GROUP:
+        raise ValueError("quantized token count %d is not a multiple of %d" % (Tq, GROUP))
+    nG = Tq // GROUP
+
+    # keys: group g = compacted tokens 32g..32g+31, one (s, z) per channel
+    Kg = K32[u].reshape(nG, GROUP, Dk).transpose(0, 2, 1)          # [nG, Dk, 32]
+    kc, ks, kz = quantize_groups(Kg, k_bits)                          # [nG, Dk, 32], [nG, Dk]
+    kc = kc.transpose(0, 2, 1).reshape(Tq, Dk)
+    # values: one (s, z) per token and 32-channel group
+    Vg = V32[u].reshape(Tq, Dv // GROUP, GROUP)
+    vc, vs, vz = quantize_groups(Vg, v_bits)                          # [Tq, Dv/32, 32], [Tq, Dv/32]
+    vc = vc.reshape(Tq, Dv)
+
+    return {
+        "k_codes": pack_codes(kc, k_bits),
+        "k_scale": ks.view(np.uint16),
+        "k_zero": kz.view(np.uint16),
+        "v_codes": pack_codes(vc, v_bits),
+        "v_scale": vs.view(np.uint16),
+        "v_zero": vz.view(np.uint16),
+        "k_fp16": K32[r].astype(np.float16).view(np.uint16),
+        "v_fp16": V32[r].astype(np.float16).view(np.uint16),
+    }
+
+
+CACHE_KEYS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_fp16", "v_fp16")
+
+
+def pack_all(K, V, w):
+    """pack_slab over every (b, h); returns arrays with leading [B, Hkv] axes."""
+    out = {key: [] for key in CACHE_KEYS}
+    for b in range(K.shape[0]):
+        rows = {key: [] for key in CACHE_KEYS}
+        for h in range(K.shape[1]):
+            p = pack_slab(K[b, h], V[b, h], w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window)
+            for key in CACHE_KEYS:
+                rows[key].append(p[key])
+        for key in CACHE_KEYS:
+            out[key].append(np.stack(rows[key]))
+    return {key: np.stack(v) for key, v in out.items()}
+
+
+# ---------------------------------------------------------------------- dequant + attn
+
+def dequant_slab(p, k_bits: int, v_bits: int):
+    """float64 keys and values of one packed slab: quantized tokens (compacted order)
+    followed by the retained fp16 tokens.  x_hat = code * s + z (exact in float64)."""
+    kc = unpack_codes(p["k_codes"], k_bits).astype(np.float64)      # [Tq, Dk]
+    Tq, Dk = kc.shape
+    ks = p["k_scale"].view(np.float16).astype(np.float64)            # [nG, Dk]
+    kz = p["k_zero"].view(np.float16).astype(np.float64)
+    g = np.arange(Tq) // GROUP
+    Khat_q = kc * ks[g] + kz[g]
+    vc = unpack_codes(p["v_codes"], v_bits).astype(np.float64)      # [Tq, Dv]
+    Dv = vc.shape[1]
+    vs = np.repeat(p["v_scale"].view(np.float16).astype(np.float64), GROUP, axis=1)
+    vz = np.repeat(p["v_zero"].view(np.float16).astype(np.float64), GROUP, axis=1)
+    Vhat_q = vc * vs + vz
+    Kr = p["k_fp16"].view(np.float16).astype(np.float64)              # [R, Dk]
+    Vr = p["v_fp16"].view(np.float16).astype(np.float64)              # [R, Dv]
+    return np.concatenate([Khat_q, Kr]), np.concatenate([Vhat_q, Vr])
+
+
+def attention(q, K, V, scale) -> np.ndarray:
+    """Single-token softmax attention in float64 for the rows of q sharing one KV head.
+
+    q [G, Dk], K [N, Dk], V [N, Dv] -> [G, Dv];  s = scale * q K^T,
+    p = exp(s - max s), out = p V / sum p  (Thin Keys section 2; HeadQ 2.1).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    s = np.float64(scale) * (q @ np.asarray(K, dtype=np.float64).T)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    return (p @ np.asarray(V, dtype=np.float64)) / p.sum(axis=-1, keepdims=True)
+
+
+def decode_slab(q_group, p, q_dtype: str, k_bits: int, v_bits: int, scale) -> np.ndarray:
+    """Decode attention of the G query heads of one KV head over its packed slab."""
+    Khat, Vhat = dequant_slab(p, k_bits, v_bits)
+    return attention(upcast(q_group, q_dtype), Khat, Vhat, scale)
+
+
+def decode_all(q, packed, w, scale=None) -> np.ndarray:
+    """q [B, Hq, Dk] (storage dtype) over a pack_all cache -> out float64 [B, Hq, Dv].
+    Query head i reads KV head i // (Hq / Hkv)."""
+    if scale is None:
+        scale = default_scale(w.Dk)
+    G = w.Hq // w.Hkv
+    out = np.empty((w.B, w.Hq, w.Dv), dtype=np.float64)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            p = {key: packed[key][b, h] for key in CACHE_KEYS}
+            out[b, h * G:(h + 1) * G] = decode_slab(q[b, h * G:(h + 1) * G], p, w.dtype,
+                                                    w.k_bits, w.v_bits, scale)
+    return out
+
+
+def slab_of(packed, b: int, h: int):
+    return {key: packed[key][b, h] for key in CACHE_KEYS}

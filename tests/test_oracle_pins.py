@@ -1,0 +1,414 @@
+"""Pins of the CPU oracle against what the pages and plain mathematics fix.
+
+Every test here checks the oracle against something other than itself: values worked
+by hand (tests/golden), a different formulation of the same rule, exact rational
+arithmetic, textbook attention written as explicit loops, or an invariance the pages
+state.  CPU only.
+"""
+
+import math
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import Workload, f32_to_bf16_bits, make_queries, make_all
+
+from conftest import load_golden
+
+
+# ----------------------------------------------------------------- quantizer pins
+
+def test_quantizer_hand_examples():
+    for case in load_golden("quantizer_hand_examples.json")["cases"]:
+        x = np.array(case["x"], dtype=np.float32)
+        codes, s16, z16 = O.quantize_groups(x, case["bits"])
+        assert codes.tolist() == case["codes"], case["why"]
+        assert int(s16.view(np.uint16)) == case["s_bits"], case["why"]
+        assert int(z16.view(np.uint16)) == case["z_bits"], case["why"]
+
+
+def _rand_groups(rng, n_groups, n, scale_choices=(0.01, 1.0, 8.0, 300.0)):
+    xs = []
+    for _ in range(n_groups):
+        sc = rng.choice(scale_choices)
+        off = rng.normal() * sc * 3
+        xs.append((rng.standard_normal(n) * sc + off).astype(np.float32))
+    return np.stack(xs)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_quantizer_error_bound(bits):
+    """|x - x_hat| <= s/2 + |z - min| + L*|s - s_fp32| (+ float32 slack): the grid
+    z + k s, k = 0..L, spans [min, max] up to the fp16 rounding of z and s, and the
+    nearest grid point is at most half a step away."""
+    rng = np.random.default_rng(100 + bits)
+    x = _rand_groups(rng, 400, 32)
+    codes, s16, z16 = O.quantize_groups(x, bits)
+    L = 2 ** bits - 1
+    s = s16.astype(np.float64)[:, None]
+    z = z16.astype(np.float64)[:, None]
+    x64 = x.astype(np.float64)
+    mn = x64.min(1, keepdims=True)
+    mx = x64.max(1, keepdims=True)
+    s_exact = (mx - mn) / L
+    xhat = codes * s + z
+    bound = s / 2 + np.abs(z - mn) + L * np.abs(s - s_exact) + 1e-6 * (np.abs(x64).max(1, keepdims=True) + s)
+    assert np.all(np.abs(x64 - xhat) <= bound)
+    assert codes.max() <= L
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_quantizer_is_nearest_grid_point(bits):
+    """Brute force in exact rational arithmetic: the code is the grid index k in [0, L]
+    minimising |x - (z + k s)| for the stored fp16 s, z; ties (and float32 near-ties
+    within 1e-6 of a step) may go either way and are skipped."""
+    rng = np.random.default_rng(7 + bits)
+    x = _rand_groups(rng, 60, 32)
+    codes, s16, z16 = O.quantize_groups(x, bits)
+    L = 2 ** bits - 1
+    checked = 0
+    for g in range(x.shape[0]):
+        s = Fraction(float(s16[g]))
+        z = Fraction(float(z16[g]))
+        if s == 0:
+            assert np.all(codes[g] == 0)
+            continue
+        for j in range(x.shape[1]):
+            xv = Fraction(float(x[g, j]))
+            d = [abs(xv - (z + k * s)) for k in range(L + 1)]
+            best = min(range(L + 1), key=lambda k: d[k])
+            second = sorted(d)[1]
+            if second - d[best] <= s * Fraction(1, 10 ** 6):
+                continue
+            assert codes[g, j] == best, (g, j, float(xv), float(s), float(z))
+            checked += 1
+    assert checked > 0.9 * x.size
+
+
+def test_quantizer_more_bits_less_error():
+    """The 2-bit grid is a subset of the 4-bit grid which is a subset of the 8-bit grid
+    (3 | 15 | 255), so reconstruction error falls as bits grow."""
+    rng = np.random.default_rng(3)
+    x = _rand_groups(rng, 500, 32)
+    mse = []
+    for bits in (2, 4, 8):
+        codes, s16, z16 = O.quantize_groups(x, bits)
+        xhat = codes * s16.astype(np.float64)[:, None] + z16.astype(np.float64)[:, None]
+        mse.append(np.mean((xhat - x) ** 2 / (x.std(1, keepdims=True) ** 2 + 1e-30)))
+    assert mse[0] > mse[1] > mse[2]
+    assert mse[1] < mse[0] / 10 and mse[2] < mse[1] / 100
+
+
+# -------------------------------------------------------------------- packing pins
+
+def test_pack_hand_examples():
+    for case in load_golden("pack_hand_examples.json")["cases"]:
+        w = O.pack_codes(np.array(case["codes"], dtype=np.uint8), case["bits"])
+        assert w.tolist() == case["words"], case["why"]
+        assert O.unpack_codes(w, case["bits"]).tolist() == case["codes"]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_pack_roundtrip_and_bit_positions(bits):
+    rng = np.random.default_rng(bits)
+    c = rng.integers(0, 2 ** bits, size=(5, 3, 64), dtype=np.uint8)
+    w = O.pack_codes(c, bits)
+    assert w.shape == (5, 3, 64 * bits // 32) and w.dtype == np.uint32
+    assert np.array_equal(O.unpack_codes(w, bits), c)
+    # independent extraction with plain Python integers
+    per = 32 // bits
+    for idx in [(0, 0, 0), (4, 2, 63), (2, 1, 17)]:
+        word = int(w[idx[0], idx[1], idx[2] // per])
+        assert (word >> ((idx[2] % per) * bits)) & (2 ** bits - 1) == c[idx]
+
+
+# ------------------------------------------------------------------- retention pins
+
+def test_retention_hand_examples():
+    for case in load_golden("retention_hand_examples.json")["cases"]:
+        expect = sorted(set(p for a, b, st in case["ranges"] for p in range(a, b, st)))
+        r, u = O.split_positions(case["T"], case["n_recent"], case["log_window"])
+        assert r.tolist() == expect, case["why"]
+        assert len(r) == case["count"]
+        assert len(r) + len(u) == case["T"]
+
+
+def _retained_by_distance(i, T, n_recent, W):
+    """Per-position form of the rule: position i at distance d = T - i is kept if it is
+    among the n_recent newest, or if for the j with W*2^(j-1) < d <= W*2^j it is a
+    multiple of 2^j."""
+    d = T - i
+    if d <= n_recent:
+        return True
+    if W <= 0 or d <= W:
+        return False
+    j = 1
+    while W * 2 ** j < d:
+        j += 1
+    return i % 2 ** j == 0
+
+
+@pytest.mark.parametrize("T,n_recent,W", [(32768, 128, 128), (1000, 0, 16), (579, 0, 32), (777, 50, 32),
+                                          (4096, 128, 0), (300, 7, 5), (64, 64, 8), (2048, 64, 64)])
+def test_retention_distance_rule(T, n_recent, W):
+    mask = O.retained_mask(T, n_recent, W)
+    expect = np.array([_retained_by_distance(i, T, n_recent, W) for i in range(T)])
+    assert np.array_equal(mask, expect)
+
+
+@pytest.mark.parametrize("J", [1, 3, 8, 10])
+def test_retention_closed_form(J):
+    """T = W * 2^J with the newest W tokens kept: each of the J log spans holds
+    W*2^(j-1) positions with stride 2^j, i.e. W/2 kept tokens, so R = W + J*W/2
+    (640 at T = 32768, W = 128)."""
+    W = 128
+    T = W * 2 ** J
+    r, _ = O.split_positions(T, W, W)
+    assert len(r) == W + J * W // 2
+    # anchoring the stride at the start of each span gives the same set here
+    alt = set(range(T - W, T))
+    for j in range(1, J + 1):
+        lo, hi = max(0, T - W * 2 ** j), T - W * 2 ** (j - 1)
+        alt.update(range(lo, hi, 2 ** j))
+    assert set(r.tolist()) == alt
+
+
+# ---------------------------------------------------------------- attention pins
+
+def _explicit_attention(q, K, V, scale):
+    """Textbook softmax attention with explicit loops and math.exp / math.fsum."""
+    out = []
+    for qi in q:
+        s = [scale * math.fsum(float(a) * float(b) for a, b in zip(qi, k)) for k in K]
+        m = max(s)
+        p = [math.exp(x - m) for x in s]
+        den = math.fsum(p)
+        out.append([math.fsum(pj * float(v[c]) for pj, v in zip(p, V)) / den for c in range(len(V[0]))])
+    return np.array(out)
+
+
+def test_attention_bruteforce_tiny():
+    rng = np.random.default_rng(5)
+    for N, D, Dv, G in [(1, 1, 1, 1), (3, 2, 4, 2), (8, 4, 3, 3), (5, 4, 4, 1)]:
+        q = rng.standard_normal((G, D))
+        K = rng.standard_normal((N, D)) * 3
+        V = rng.standard_normal((N, Dv))
+        sc = 1 / math.sqrt(D)
+        ref = _explicit_attention(q, K, V, sc)
+        got = O.attention(q, K, V, sc)
+        assert np.abs(got - ref).max() <= 1e-12
+
+
+def test_attention_matches_torch_sdpa_fp64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((4, 8))
+    K = rng.standard_normal((7, 8)) * 2
+    V = rng.standard_normal((7, 5))
+    sc = 1 / math.sqrt(8)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None, :], torch.from_numpy(K)[None, None].expand(1, 4, 7, 8),
+        torch.from_numpy(V)[None, None].expand(1, 4, 7, 5), scale=sc)[0, :, 0].numpy()
+    assert np.abs(O.attention(q, K, V, sc) - ref).max() <= 1e-12
+
+
+def test_attention_uniform_keys_is_mean_value():
+    rng = np.random.default_rng(8)
+    K = np.tile(rng.standard_normal(16), (50, 1))
+    V = rng.standard_normal((50, 6))
+    out = O.attention(rng.standard_normal((3, 16)), K, V, 0.25)
+    assert np.abs(out - V.mean(0)).max() <= 1e-12
+
+
+def test_attention_shift_invariance():
+    """HeadQ 2.1: adding one constant vector mu to every key adds q.mu to every score,
+    which softmax ignores."""
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((4, 32))
+    K = rng.standard_normal((200, 32))
+    V = rng.standard_normal((200, 16))
+    mu = rng.standard_normal(32) * 5
+    a = O.attention(q, K, V, 0.2)
+    b = O.attention(q, K + mu, V, 0.2)
+    assert np.abs(a - b).max() <= 1e-12
+
+
+def test_attention_permutation_invariance():
+    """LogQuant section 4: A.V = A_P.V_P, token order inside attention does not matter."""
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((2, 16))
+    K = rng.standard_normal((300, 16)) * 2
+    V = rng.standard_normal((300, 8))
+    perm = rng.permutation(300)
+    assert np.abs(O.attention(q, K, V, 0.3) - O.attention(q, K[perm], V[perm], 0.3)).max() <= 1e-12
+
+
+# ----------------------------------------------------------- whole-pipeline pins
+
+def _w(**kw):
+    base = dict(name="t", B=1, Hq=2, Hkv=1, Dk=64, Dv=64, T=256, k_bits=4, v_bits=2,
+                dtype="bf16", seed=21)
+    base.update(kw)
+    return Workload(**base)
+
+
+def _fp16_round_py(x):
+    """float -> nearest IEEE half (ties to even) via the struct module."""
+    return struct.unpack("<e", struct.pack("<e", float(x)))[0]
+
+
+def test_sixteen_bit_mode_is_exact_attention():
+    """All tokens retained (n_recent = T): the oracle must equal plain attention over
+    the fp16-rounded inputs (the pages' 16-bit reference)."""
+    w = _w(T=96, n_recent=96, dtype="f32", Dk=32, Dv=32, Hq=3)
+    K, V = make_all(w, workers=1)
+    q = make_queries(w)
+    packed = O.pack_all(K, V, w)
+    assert packed["k_codes"].shape[2] == 0
+    got = O.decode_all(q, packed, w)
+    Kr = [[_fp16_round_py(v) for v in row] for row in K[0, 0]]
+    Vr = [[_fp16_round_py(v) for v in row] for row in V[0, 0]]
+    ref = _explicit_attention(q[0].astype(np.float64), Kr, Vr, float(O.default_scale(32)))
+    assert np.abs(got[0] - ref).max() <= 1e-12
+
+
+def test_decode_matches_explicit_dequant_loops():
+    """Small packed slab decoded with plain-Python bit extraction and explicit loops."""
+    w = _w(T=96, n_recent=32, k_bits=4, v_bits=2, Dk=32, Dv=64, Hq=2)
+    K, V = make_all(w, workers=1)
+    q = make_queries(w)
+    p = O.slab_of(O.pack_all(K, V, w), 0, 0)
+    kb, vb = w.k_bits, w.v_bits
+    f16 = lambda a: a.view(np.float16).astype(np.float64)
+    ks, kz, vs, vz = f16(p["k_scale"]), f16(p["k_zero"]), f16(p["v_scale"]), f16(p["v_zero"])
+    rows_k, rows_v = [], []
+    for t in range(p["k_codes"].shape[0]):
+        kr = []
+        for c in range(w.Dk):
+            word = int(p["k_codes"][t, c * kb // 32])
+            code = (word >> ((c % (32 // kb)) * kb)) & (2 ** kb - 1)
+            kr.append(code * ks[t // 32, c] + kz[t // 32, c])
+        vr = []
+        for c in range(w.Dv):
+            word = int(p["v_codes"][t, c * vb // 32])
+            code = (word >> ((c % (32 // vb)) * vb)) & (2 ** vb - 1)
+            vr.append(code * vs[t, c // 32] + vz[t, c // 32])
+        rows_k.append(kr)
+        rows_v.append(vr)
+    rows_k += f16(p["k_fp16"]).tolist()
+    rows_v += f16(p["v_fp16"]).tolist()
+    qf = (q[0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = _explicit_attention(qf, rows_k, rows_v, float(O.default_scale(w.Dk)))
+    got = O.decode_all(q, O.pack_all(K, V, w), w)[0]
+    assert np.abs(got - ref).max() <= 1e-12
+
+
+def test_key_quantization_is_shift_equivariant():
+    """Per-channel key quantization commutes with adding a per-channel constant when
+    every value involved is exact (inputs on a 2^-6 grid, |x| < 8, shifts of +-16):
+    codes and scales stay the same, zeros move by the shift, and the decode output
+    is unchanged (HeadQ 2.1 softmax-null shift; HeadQ 4 notes that grids lacking
+    this property are hurt by such shifts)."""
+    rng = np.random.default_rng(12)
+    w = _w(T=160, n_recent=32, Dk=64, Dv=32, Hq=4, dtype="f32")
+    K = np.clip(np.round(rng.standard_normal((1, 1, 160, 64)) * 2 * 64) / 64, -7.9, 7.9).astype(np.float32)
+    V = (rng.standard_normal((1, 1, 160, 32)) * 0.5).astype(np.float32)
+    mu = rng.choice([-16.0, 16.0], size=64).astype(np.float32)
+    q = rng.standard_normal((1, 4, 64)).astype(np.float32)
+    a = O.pack_all(K, V, w)
+    b = O.pack_all(K + mu, V, w)
+    assert np.array_equal(a["k_codes"], b["k_codes"])
+    assert np.array_equal(a["k_scale"], b["k_scale"])
+    za = a["k_zero"].view(np.float16).astype(np.float64)
+    zb = b["k_zero"].view(np.float16).astype(np.float64)
+    assert np.array_equal(zb, za + mu)
+    oa = O.decode_all(q, a, w)
+    ob = O.decode_all(q, b, w)
+    assert np.abs(oa - ob).max() <= 1e-12
+
+
+def test_decode_permutation_of_retained_and_quantized():
+    """Moving tokens between the fp16 and quantized parts only changes their values, not
+    their order dependence: reversing both the quantized and retained rows of a packed
+    slab (keeping key groups intact) leaves the output unchanged."""
+    w = _w(T=352, n_recent=32, Hq=4)
+    K, V = make_all(w, workers=1)
+    q = make_queries(w)
+    p = O.slab_of(O.pack_all(K, V, w), 0, 0)
+    Khat, Vhat = O.dequant_slab(p, w.k_bits, w.v_bits)
+    qf = O.upcast(q[0], "bf16")
+    a = O.attention(qf, Khat, Vhat, O.default_scale(w.Dk))
+    b = O.attention(qf, Khat[::-1], Vhat[::-1], O.default_scale(w.Dk))
+    assert np.abs(a - b).max() <= 1e-12
+
+
+def test_error_falls_with_bits():
+    """Output error against exact float64 attention on the unquantized inputs falls as
+    key bits grow (values exact) and as value bits grow (keys exact)."""
+    w = _w(T=1024, Dk=128, Dv=128, Hq=4)
+    K, V = make_all(w, workers=1)
+    q = make_queries(w)
+    K32, V32 = O.upcast(K[0, 0], "bf16"), O.upcast(V[0, 0], "bf16")
+    qf = O.upcast(q[0], "bf16")
+    sc = O.default_scale(w.Dk)
+    exact = O.attention(qf, K32, V32, sc)
+
+    def kq(bits):
+        c, s, z = O.quantize_groups(K32.reshape(-1, 32, 128).transpose(0, 2, 1), bits)
+        return (c * s.astype(np.float64)[..., None] + z.astype(np.float64)[..., None]).transpose(0, 2, 1).reshape(-1, 128)
+
+    def vq(bits):
+        c, s, z = O.quantize_groups(V32.reshape(-1, 4, 32), bits)
+        return (c * s.astype(np.float64)[..., None] + z.astype(np.float64)[..., None]).reshape(-1, 128)
+
+    ek = [np.abs(O.attention(qf, kq(b), V32, sc) - exact).max() for b in (2, 4, 8)]
+    ev = [np.abs(O.attention(qf, K32, vq(b), sc) - exact).max() for b in (2, 4, 8)]
+    assert ek[0] > ek[1] > ek[2]
+    assert ev[0] > ev[1] > ev[2]
+
+
+def test_oracle_rejects_partial_group():
+    w = _w(T=100, n_recent=0)
+    K, V = make_all(w, workers=1)
+    with pytest.raises(ValueError):
+        O.pack_all(K, V, w)
+
+
+def test_bf16_inputs_upcast_exactly():
+    x = np.array([1.0, -2.5, 3.140625, 1e-30, -65280.0], dtype=np.float32)
+    bits = f32_to_bf16_bits(x)
+    back = O.upcast(bits, "bf16")
+    for a, b in zip(x, back):
+        # every value here is representable in bf16 except 1e-30, which must be the nearest one
+        if a != np.float32(1e-30):
+            assert a == b
+    assert abs(float(back[3]) - 1e-30) <= 1e-30 * 2 ** -8
+
+
+# ------------------------------------------------------------------- reports
+
+def test_report_keys_get_more_bits(capsys):
+    """Reported, not asserted (parity unpinned: the pages' claim rests on trained
+    weights).  Output error of K4V2 vs K2V4 and relative reconstruction error of K vs V
+    at equal bits, on the synthetic outlier-channel keys."""
+    w = _w(T=1024, Dk=128, Dv=128, Hq=4, B=1)
+    K, V = make_all(w, workers=1)
+    q = make_queries(w)
+    K32, V32 = O.upcast(K[0, 0], "bf16"), O.upcast(V[0, 0], "bf16")
+    qf = O.upcast(q[0], "bf16")
+    exact = O.attention(qf, K32, V32, O.default_scale(128))
+    lines = []
+    for kb, vb in [(4, 2), (2, 4), (4, 4), (2, 2)]:
+        p = O.pack_slab(K[0, 0], V[0, 0], "bf16", kb, vb, 0, 0)
+        out = O.decode_slab(q[0], p, "bf16", kb, vb, O.default_scale(128))
+        lines.append("K%dV%d max|err| %.3e" % (kb, vb, np.abs(out - exact).max()))
+    for bits in (2, 4):
+        p = O.pack_slab(K[0, 0], V[0, 0], "bf16", bits, bits, 0, 0)
+        Kh, Vh = O.dequant_slab(p, bits, bits)
+        rk = np.linalg.norm(Kh - K32) / np.linalg.norm(K32)
+        rv = np.linalg.norm(Vh - V32) / np.linalg.norm(V32)
+        lines.append("%d-bit relative reconstruction error K %.3e V %.3e" % (bits, rk, rv))
+    print("\n".join(lines))

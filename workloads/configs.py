@@ -1,0 +1,91 @@
+"""The five benchmark workloads plus small parity cases.
+
+Shapes follow the pages' settings: a Llama-3.1-8B-like GQA attention shape (32 query
+heads sharing 8 KV heads of width 128) as evaluated by LogQuant (page
+"LogQuant: Log-Distributed 2-Bit Quantization of KV Cache", experimental results) and
+by AATC (page "KV Cache Compression Through the Lens of Transform Coding", results);
+K4V2 bit allocation ("Quantize What Counts: More for Keys, Less for Values",
+methodology and results); log-spaced full-precision retention (LogQuant, log-based
+filtering strategy); thin keys with d_select = d_model/4 ("Thin Keys, Full Values",
+asymmetric attention).
+"""
+
+from dataclasses import dataclass, field, replace
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Dk: int
+    Dv: int
+    T: int
+    k_bits: int
+    v_bits: int
+    n_recent: int = 0        # newest tokens kept in fp16
+    log_window: int = 0      # W of the log-spaced fp16 regions (0 = off)
+    dtype: str = "bf16"      # dtype of q, K and V as handed to both sides: "f32" | "bf16"
+    partitions: int = 1      # split-K sequence partitions used by decode
+    seed: int = 0
+    prefill_chunk: int = 0   # tokens of the newest chunk re-packed inside one bench step
+    k_group: int = 32
+    v_group: int = 32
+    n_outliers: int = 4
+    outlier_scale: float = 8.0
+    k_offset_std: float = 2.0
+    v_std: float = 0.5
+    notes: str = field(default="", compare=False)
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = [
+    Workload("tiny_ref", B=1, Hq=1, Hkv=1, Dk=64, Dv=64, T=256, k_bits=4, v_bits=2,
+             dtype="f32", partitions=1, seed=0,
+             notes="one fp32 query, no fp16 window"),
+    Workload("llama8b_gqa_4k", B=8, Hq=32, Hkv=8, Dk=128, Dv=128, T=4096, k_bits=4, v_bits=2,
+             n_recent=128, dtype="bf16", partitions=4, seed=1,
+             notes="K4V2, newest 128 tokens fp16"),
+    Workload("logquant_32k", B=32, Hq=32, Hkv=8, Dk=128, Dv=128, T=32768, k_bits=2, v_bits=2,
+             n_recent=128, log_window=128, dtype="bf16", partitions=16, seed=2,
+             notes="K2V2, 128 fp16 window + log-spaced fp16 tokens (640 kept)"),
+    Workload("thin_keys_16k", B=16, Hq=32, Hkv=8, Dk=32, Dv=128, T=16384, k_bits=8, v_bits=4,
+             dtype="bf16", partitions=8, seed=3,
+             notes="d_select = 32 keys, full 128-wide values, K8V4"),
+    Workload("long_128k", B=4, Hq=32, Hkv=8, Dk=128, Dv=128, T=131072, k_bits=4, v_bits=2,
+             n_recent=128, dtype="bf16", partitions=64, seed=4, prefill_chunk=8192,
+             notes="K4V2, 128 fp16 window, 64 split-K partitions, 8192-token prefill chunk"),
+]
+
+
+def workload(key) -> Workload:
+    if isinstance(key, int):
+        return WORKLOADS[key]
+    for w in WORKLOADS:
+        if w.name == key:
+            return w
+    raise KeyError(key)
+
+
+def small_cases():
+    """Shapes the oracle finishes in well under a second that still cover several
+    groups, several partitions, uneven partition sizes and every bit width."""
+    return [
+        Workload("small_k4v2_win", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=1064, k_bits=4, v_bits=2,
+                 n_recent=40, dtype="bf16", partitions=5, seed=11),
+        Workload("small_k2v2_log", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=2048, k_bits=2, v_bits=2,
+                 n_recent=64, log_window=64, dtype="bf16", partitions=7, seed=12),
+        Workload("small_k8v4_thin", B=2, Hq=8, Hkv=2, Dk=32, Dv=128, T=800, k_bits=8, v_bits=4,
+                 dtype="bf16", partitions=3, seed=13),
+        Workload("small_k4v8_f32", B=1, Hq=2, Hkv=1, Dk=64, Dv=96, T=352, k_bits=4, v_bits=8,
+                 n_recent=32, dtype="f32", partitions=4, seed=14),
+        Workload("small_g8_k2v4", B=1, Hq=16, Hkv=2, Dk=96, Dv=64, T=576, k_bits=2, v_bits=4,
+                 n_recent=0, log_window=32, dtype="bf16", partitions=2, seed=15),
+    ]
