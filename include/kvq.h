@@ -1,0 +1,165 @@
+/*
+ * kvq.h — packed low-bit KV cache and fused single-token decode attention for
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers, sizes and enums.
+ *
+ * What is computed (sources are the pages' technical summaries):
+ *  - Keys and values of the attention KV cache are quantized group-wise and
+ *    asymmetrically with separate bit widths for keys and values ("Quantize What
+ *    Counts: More for Keys, Less for Values": methodology, K4V2; group size 32 for
+ *    keys, results).  Keys are quantized per channel over groups of 32 tokens
+ *    ("LogQuant: Log-Distributed 2-Bit Quantization of KV Cache", section 5,
+ *    per-channel keys); values per token over groups of 32 channels.
+ *  - A subset of tokens stays in fp16: the newest n_recent positions and, when
+ *    log_window = W > 0, log-spaced positions further back (LogQuant section 2,
+ *    log-based filtering): for j = 1, 2, ... every multiple of 2^j inside
+ *    [T - W*2^j, T - W*2^(j-1)), clipped at 0.
+ *  - Decode attention for one new token per sequence reads the packed cache
+ *    directly: out = softmax(scale * q K^T) V over all T cached tokens, where
+ *    quantized and fp16 tokens may be visited in any order (LogQuant section 4,
+ *    A.V = A_P.V_P); scale defaults to 1/sqrt(Dk) ("HeadQ" section 2.1; "Thin Keys,
+ *    Full Values" section 2 with Dk = d_select, which may differ from Dv).
+ *
+ * Quantizer (bit-exact contract, all in IEEE float32 unless stated):
+ *   mn, mx = min, max of the 32 values of a group
+ *   s = fp16_rne(fp32(mx - mn) / fp32(2^bits - 1)),  z = fp16_rne(mn)
+ *   (a stored zero of either sign is written as +0)
+ *   code = 0 if s == 0, else clamp(rint_half_even((x - float(z)) / float(s)), 0, 2^bits-1)
+ *   with the correctly rounded division.  Dequantized value: code * s + z.
+ *
+ * Packed cache layout (all buffers caller-allocated, contiguous, row-major;
+ * "slab" = one (batch b, kv head h) pair, slabs ordered b-major):
+ *   Tq = T - R quantized tokens in ascending position order ("compacted" order),
+ *   n_groups = Tq / 32 key groups (group g = compacted tokens 32g .. 32g+31).
+ *   k_codes  uint32 [B, Hkv, Tq, Dk*k_bits/32]  word w of a row holds channel
+ *            w*(32/k_bits)+k at bits [k*k_bits, (k+1)*k_bits), little-endian
+ *   k_scale  fp16   [B, Hkv, n_groups, Dk]
+ *   k_zero   fp16   [B, Hkv, n_groups, Dk]
+ *   v_codes  uint32 [B, Hkv, Tq, Dv*v_bits/32]  same packing along channels
+ *   v_scale  fp16   [B, Hkv, Tq, Dv/32]
+ *   v_zero   fp16   [B, Hkv, Tq, Dv/32]
+ *   k_fp16   fp16   [B, Hkv, R, Dk]   retained positions, ascending
+ *   v_fp16   fp16   [B, Hkv, R, Dv]
+ *
+ * Threading and ownership: the library allocates no device memory, keeps no
+ * state between calls (apart from the thread-local last-error text), never
+ * synchronizes, and enqueues work only on the stream it is given.  Every pointer
+ * stays owned by the caller and must stay valid until the enqueued work is done.
+ *
+ * Errors: every call validates its arguments on the host before launching
+ * anything and returns KVQ_ERR_INVALID / KVQ_ERR_UNSUPPORTED without touching the
+ * GPU; a failed launch returns KVQ_ERR_HIP.  kvq_last_error() gives the reason.
+ * Unchecked preconditions: inputs are finite, |values| and group ranges stay
+ * inside the fp16 range, buffers have the sizes kvq_cache_sizes() reports, and
+ * device pointers are 16-byte aligned device memory.
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = 1,      /* bad argument (null pointer, out-of-range value, misalignment) */
+  KVQ_ERR_UNSUPPORTED = 2,  /* valid request this build does not handle (see limits below) */
+  KVQ_ERR_HIP = 3           /* a HIP runtime call or kernel launch failed */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_F16 = 1, KVQ_BF16 = 2 } kvq_dtype;
+
+enum { KVQ_GROUP = 32, KVQ_MAX_HEAD_DIM = 256, KVQ_MAX_GQA = 16, KVQ_NUM_CACHE_BUFFERS = 8 };
+
+/* Shape and policy of one packed cache.  Fill with kvq_layout_init(); treat as
+ * read-only afterwards (calls re-derive and check R, Tq, n_groups). */
+typedef struct {
+  int32_t B, Hq, Hkv, Dk, Dv, T;
+  int32_t k_bits, v_bits;         /* each in {2, 4, 8} */
+  int32_t n_recent;               /* newest positions kept in fp16 (0..T; T = no quantization) */
+  int32_t log_window;             /* W of the log-spaced fp16 positions; 0 = none */
+  int32_t R, Tq, n_groups;        /* derived: retained count, quantized count, Tq / 32 */
+} kvq_layout;
+
+/* Device pointers of the eight cache buffers described above.  Buffers a call
+ * does not touch may be NULL (e.g. k_fp16 / v_fp16 when R == 0). */
+typedef struct {
+  void *k_codes, *k_scale, *k_zero;
+  void *v_codes, *v_scale, *v_zero;
+  void *k_fp16, *v_fp16;
+} kvq_cache;
+
+/* Fill *L and derive R, Tq, n_groups.  Limits (else KVQ_ERR_INVALID, or
+ * KVQ_ERR_UNSUPPORTED where the request is well-formed): all sizes >= 1,
+ * Hq % Hkv == 0 with Hq / Hkv <= KVQ_MAX_GQA, Dk and Dv multiples of 32 up to
+ * KVQ_MAX_HEAD_DIM, bits in {2, 4, 8}, 0 <= n_recent <= T, log_window >= 0, and
+ * the quantized token count Tq a multiple of 32 (choose n_recent accordingly). */
+int kvq_layout_init(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T,
+                    int k_bits, int v_bits, int n_recent, int log_window);
+
+/* Byte sizes of the eight kvq_cache buffers, in kvq_cache field order. */
+int kvq_cache_sizes(const kvq_layout* L, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]);
+
+/* Host-side list of the R retained positions (ascending) into out[0..capacity).
+ * Returns KVQ_ERR_INVALID if capacity < R.  No GPU work. */
+int kvq_retained_positions(const kvq_layout* L, int32_t* out, int32_t capacity);
+
+/* Number of quantized (non-retained) positions in [0, t).  Host-side, no GPU work;
+ * a chunk [t0, t1) can be packed on its own when both counts are multiples of 32. */
+int64_t kvq_quantized_before(const kvq_layout* L, int64_t t);
+
+/* Workspace kv_decode_attn needs for num_partitions sequence partitions:
+ * B * Hq * num_partitions * (Dv + 2) floats (0 when num_partitions == 1).
+ * Returns 0 for an invalid layout. */
+size_t kvq_decode_workspace_bytes(const kvq_layout* L, int num_partitions);
+
+/*
+ * kv_quant_pack — quantize and pack positions [t_begin, t_begin + t_count) of the
+ * cache described by L (the whole cache: t_begin = 0, t_count = T).
+ *   K: [B, Hkv, t_count, Dk], V: [B, Hkv, t_count, Dv] device arrays of dtype
+ *      kv_dtype (KVQ_F32 / KVQ_F16 / KVQ_BF16), contiguous; row j is position
+ *      t_begin + j.
+ *   cache: buffers for the WHOLE cache; the call writes the key groups, value rows
+ *      and fp16 rows that belong to the chunk and nothing else, so chunks can be
+ *      packed independently (e.g. a prefill chunk appended to an existing cache).
+ *   stream: hipStream_t to enqueue on (NULL = default stream).
+ * The number of quantized positions before t_begin and before t_begin + t_count
+ * must both be multiples of 32 (else KVQ_ERR_UNSUPPORTED).  Output is
+ * deterministic: codes, scales and zeros follow the quantizer contract above bit
+ * for bit.
+ */
+int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count,
+                  const void* K, const void* V, int kv_dtype,
+                  const kvq_cache* cache, void* stream);
+
+/*
+ * kv_decode_attn — single-token decode attention over a packed cache.
+ *   q:   [B, Hq, Dk] device array of dtype q_dtype; query head i reads KV head
+ *        i / (Hq / Hkv) (grouped-query attention: the Hq/Hkv queries of one KV head
+ *        share each read of its cache).
+ *   softmax_scale: scale of the scores (finite; pass 1/sqrtf(Dk) for the usual one).
+ *   num_partitions: P sequence partitions processed in parallel (split-K); partition
+ *        p takes key groups [p*n_groups/P, (p+1)*n_groups/P) and retained tokens
+ *        [p*R/P, (p+1)*R/P) (integer division).  1 <= P <= max(1, ceil(T/32)).
+ *   workspace / workspace_bytes: at least kvq_decode_workspace_bytes(L, P) bytes of
+ *        device memory (may be NULL when P == 1); contents on entry do not matter.
+ *   out: [B, Hq, Dv] float32 device array.
+ * Partial results of the partitions are merged on the device.
+ */
+int kv_decode_attn(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache,
+                   float softmax_scale, int num_partitions, void* workspace,
+                   size_t workspace_bytes, float* out, void* stream);
+
+/* Static text for a status code. */
+const char* kvq_status_string(int status);
+
+/* Reason for the last non-OK status returned on the calling thread ("" if none). */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */

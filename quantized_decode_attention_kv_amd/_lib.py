@@ -1,0 +1,83 @@
+"""ctypes view of include/kvq.h.  Loading fails loudly if libkvq.so was not built."""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP = 0, 1, 2, 3
+KVQ_F32, KVQ_F16, KVQ_BF16 = 0, 1, 2
+KVQ_GROUP = 32
+KVQ_NUM_CACHE_BUFFERS = 8
+
+LAYOUT_FIELDS = ["B", "Hq", "Hkv", "Dk", "Dv", "T", "k_bits", "v_bits", "n_recent", "log_window",
+                 "R", "Tq", "n_groups"]
+CACHE_FIELDS = ["k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_fp16", "v_fp16"]
+
+# every entry point declared in include/kvq.h
+EXPORTS = ["kvq_layout_init", "kvq_cache_sizes", "kvq_retained_positions", "kvq_quantized_before",
+           "kvq_decode_workspace_bytes", "kv_quant_pack", "kv_decode_attn", "kvq_status_string",
+           "kvq_last_error"]
+
+
+class KvqLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in LAYOUT_FIELDS]
+
+
+class KvqCache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in CACHE_FIELDS]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libkvq.so and declare the signatures.  Raises if the library is missing:
+    there is no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libkvq.so is not built (%s); run `python -m quantized_decode_attention_kv_amd.build`"
+                           % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_i32, c_i64, c_sz, vp = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    LP = ctypes.POINTER(KvqLayout)
+    CP = ctypes.POINTER(KvqCache)
+    lib.kvq_layout_init.argtypes = [LP] + [c_int] * 10
+    lib.kvq_layout_init.restype = c_int
+    lib.kvq_cache_sizes.argtypes = [LP, ctypes.POINTER(c_sz)]
+    lib.kvq_cache_sizes.restype = c_int
+    lib.kvq_retained_positions.argtypes = [LP, ctypes.POINTER(c_i32), c_i32]
+    lib.kvq_retained_positions.restype = c_int
+    lib.kvq_quantized_before.argtypes = [LP, c_i64]
+    lib.kvq_quantized_before.restype = c_i64
+    lib.kvq_decode_workspace_bytes.argtypes = [LP, c_int]
+    lib.kvq_decode_workspace_bytes.restype = c_sz
+    lib.kv_quant_pack.argtypes = [LP, c_i64, c_i64, vp, vp, c_int, CP, vp]
+    lib.kv_quant_pack.restype = c_int
+    lib.kv_decode_attn.argtypes = [LP, vp, c_int, CP, ctypes.c_float, c_int, vp, c_sz, vp, vp]
+    lib.kv_decode_attn.restype = c_int
+    lib.kvq_status_string.argtypes = [c_int]
+    lib.kvq_status_string.restype = ctypes.c_char_p
+    lib.kvq_last_error.argtypes = []
+    lib.kvq_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (%s)" % (message, status_name(status)))
+        self.status = status
+
+
+def status_name(status: int) -> str:
+    return {KVQ_OK: "KVQ_OK", KVQ_ERR_INVALID: "KVQ_ERR_INVALID", KVQ_ERR_UNSUPPORTED: "KVQ_ERR_UNSUPPORTED",
+            KVQ_ERR_HIP: "KVQ_ERR_HIP"}.get(status, "status %d" % status)
+
+
+def check(status: int):
+    if status != KVQ_OK:
+        raise KvqError(status, load().kvq_last_error().decode())

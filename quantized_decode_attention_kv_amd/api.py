@@ -1,0 +1,142 @@
+"""Python binding of libkvq: argument marshalling only.
+
+PyTorch provides device memory and the current stream; every step of the
+computation runs in the library's HIP kernels.  Names follow include/kvq.h.
+"""
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib as L_
+
+_DTYPE_CODES = {torch.float32: L_.KVQ_F32, torch.float16: L_.KVQ_F16, torch.bfloat16: L_.KVQ_BF16}
+
+
+class Layout:
+    """Shape and fp16-retention policy of one packed cache (kvq_layout)."""
+
+    def __init__(self, B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits, n_recent=0, log_window=0):
+        lib = L_.load()
+        self._c = L_.KvqLayout()
+        L_.check(lib.kvq_layout_init(ctypes.byref(self._c), B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits,
+                                     n_recent, log_window))
+
+    @classmethod
+    def from_workload(cls, w, T=None):
+        return cls(w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T if T is None else T, w.k_bits, w.v_bits,
+                   w.n_recent, w.log_window)
+
+    def __getattr__(self, name):
+        if name in L_.LAYOUT_FIELDS:
+            return getattr(self._c, name)
+        raise AttributeError(name)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._c)
+
+    def cache_sizes(self):
+        arr = (ctypes.c_size_t * L_.KVQ_NUM_CACHE_BUFFERS)()
+        L_.check(L_.load().kvq_cache_sizes(self.ref, arr))
+        return dict(zip(L_.CACHE_FIELDS, list(arr)))
+
+    def retained_positions(self):
+        n = max(1, self.R)
+        arr = (ctypes.c_int32 * n)()
+        L_.check(L_.load().kvq_retained_positions(self.ref, arr, n))
+        return list(arr)[: self.R]
+
+    def quantized_before(self, t: int) -> int:
+        return int(L_.load().kvq_quantized_before(self.ref, t))
+
+    def workspace_bytes(self, num_partitions: int) -> int:
+        return int(L_.load().kvq_decode_workspace_bytes(self.ref, num_partitions))
+
+    def shapes(self):
+        """Tensor shape and dtype of each cache buffer (codes as int32 bit patterns)."""
+        B, H, Tq, nG, R = self.B, self.Hkv, self.Tq, self.n_groups, self.R
+        return {
+            "k_codes": ((B, H, Tq, self.Dk * self.k_bits // 32), torch.int32),
+            "k_scale": ((B, H, nG, self.Dk), torch.float16),
+            "k_zero": ((B, H, nG, self.Dk), torch.float16),
+            "v_codes": ((B, H, Tq, self.Dv * self.v_bits // 32), torch.int32),
+            "v_scale": ((B, H, Tq, self.Dv // 32), torch.float16),
+            "v_zero": ((B, H, Tq, self.Dv // 32), torch.float16),
+            "k_fp16": ((B, H, R, self.Dk), torch.float16),
+            "v_fp16": ((B, H, R, self.Dv), torch.float16),
+        }
+
+
+def alloc_cache(layout: Layout, device="cuda"):
+    """Caller-owned cache buffers (uninitialised) for a layout."""
+    return {k: torch.empty(shape, dtype=dt, device=device) for k, (shape, dt) in layout.shapes().items()}
+
+
+def _cache_struct(layout: Layout, cache):
+    c = L_.KvqCache()
+    for k, (shape, dt) in layout.shapes().items():
+        t = cache.get(k)
+        if t is None:
+            setattr(c, k, None)
+            continue
+        if tuple(t.shape) != tuple(shape) or t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("cache[%r] must be a contiguous CUDA %s tensor of shape %s" % (k, dt, shape))
+        setattr(c, k, t.data_ptr() if t.numel() else None)
+    return c
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_tensor(name, t, shape):
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError("%s must be a contiguous CUDA tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype not in _DTYPE_CODES:
+        raise ValueError("%s dtype %s not supported (float32, float16, bfloat16)" % (name, t.dtype))
+
+
+def kv_quant_pack(layout: Layout, K, V, cache=None, t_begin: int = 0, stream=None):
+    """Quantize and pack positions [t_begin, t_begin + K.shape[2]) into ``cache``
+    (allocated if None).  K [B, Hkv, t, Dk], V [B, Hkv, t, Dv] on the GPU."""
+    t_count = K.shape[2]
+    _check_tensor("K", K, (layout.B, layout.Hkv, t_count, layout.Dk))
+    _check_tensor("V", V, (layout.B, layout.Hkv, t_count, layout.Dv))
+    if K.dtype != V.dtype:
+        raise ValueError("K and V must share a dtype")
+    if cache is None:
+        cache = alloc_cache(layout, K.device)
+    cs = _cache_struct(layout, cache)
+    L_.check(L_.load().kv_quant_pack(layout.ref, t_begin, t_count, ctypes.c_void_p(K.data_ptr()),
+                                     ctypes.c_void_p(V.data_ptr()), _DTYPE_CODES[K.dtype], ctypes.byref(cs),
+                                     _stream(stream)))
+    return cache
+
+
+def kv_decode_attn(layout: Layout, q, cache, num_partitions: int = 1, softmax_scale=None, out=None,
+                   workspace=None, stream=None):
+    """Decode attention of q [B, Hq, Dk] over a packed cache -> float32 [B, Hq, Dv]."""
+    _check_tensor("q", q, (layout.B, layout.Hq, layout.Dk))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(layout.Dk)
+    if out is None:
+        out = torch.empty((layout.B, layout.Hq, layout.Dv), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (layout.B, layout.Hq, layout.Dv) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor [B, Hq, Dv]")
+    need = layout.workspace_bytes(num_partitions)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    cs = _cache_struct(layout, cache)
+    L_.check(L_.load().kv_decode_attn(layout.ref, ctypes.c_void_p(q.data_ptr()), _DTYPE_CODES[q.dtype],
+                                      ctypes.byref(cs), ctypes.c_float(softmax_scale), num_partitions,
+                                      ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(out.data_ptr()),
+                                      _stream(stream)))
+    return out

@@ -1,0 +1,254 @@
+// C ABI of the library: argument validation, size queries and launches.
+// Every check runs on the host before any HIP call, so invalid requests never
+// reach the GPU.  See include/kvq.h for the contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.hpp"
+#include "kvq_retention.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return KVQ_OK;
+}
+
+bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
+bool valid_gqa(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kvq::RetentionRule rule_of(const kvq_layout& L) { return kvq::RetentionRule{L.T, L.n_recent, L.log_window}; }
+
+// Full validation of a layout (also of one the caller may have edited by hand).
+int check_layout(const kvq_layout* L) {
+  if (!L) return fail(KVQ_ERR_INVALID, "layout is NULL");
+  if (L->B < 1 || L->Hq < 1 || L->Hkv < 1 || L->T < 1)
+    return fail(KVQ_ERR_INVALID, "B, Hq, Hkv and T must be >= 1 (got %d, %d, %d, %d)", L->B, L->Hq, L->Hkv, L->T);
+  if (L->Hq % L->Hkv != 0) return fail(KVQ_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", L->Hq, L->Hkv);
+  if (!valid_gqa(L->Hq / L->Hkv))
+    return fail(KVQ_ERR_UNSUPPORTED, "Hq/Hkv = %d; supported group sizes are 1, 2, 4, 8, 16", L->Hq / L->Hkv);
+  if (L->Dk < KVQ_GROUP || L->Dk % KVQ_GROUP || L->Dv < KVQ_GROUP || L->Dv % KVQ_GROUP)
+    return fail(KVQ_ERR_INVALID, "Dk (%d) and Dv (%d) must be positive multiples of 32", L->Dk, L->Dv);
+  if (L->Dk > KVQ_MAX_HEAD_DIM || L->Dv > KVQ_MAX_HEAD_DIM)
+    return fail(KVQ_ERR_UNSUPPORTED, "Dk (%d) and Dv (%d) must be <= %d", L->Dk, L->Dv, KVQ_MAX_HEAD_DIM);
+  if (!valid_bits(L->k_bits) || !valid_bits(L->v_bits))
+    return fail(KVQ_ERR_UNSUPPORTED, "k_bits (%d) and v_bits (%d) must be 2, 4 or 8", L->k_bits, L->v_bits);
+  if (L->n_recent < 0 || L->n_recent > L->T)
+    return fail(KVQ_ERR_INVALID, "n_recent (%d) must be in [0, T=%d]", L->n_recent, L->T);
+  if (L->log_window < 0) return fail(KVQ_ERR_INVALID, "log_window (%d) must be >= 0", L->log_window);
+  const int64_t R = kvq::retained_before(rule_of(*L), L->T);
+  const int64_t Tq = L->T - R;
+  if (Tq % KVQ_GROUP != 0)
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "%lld quantized tokens is not a multiple of 32; adjust n_recent so T - R is",
+                (long long)Tq);
+  if (L->R != R || L->Tq != Tq || L->n_groups != Tq / KVQ_GROUP)
+    return fail(KVQ_ERR_INVALID, "layout derived fields are stale; call kvq_layout_init");
+  // every buffer offset used by the kernels must fit comfortably in int64 and the
+  // per-slab token counts in int32 (T <= INT32_MAX by type)
+  return ok();
+}
+
+int check_cache_ptr(const void* p, const char* name) {
+  if (!p) return fail(KVQ_ERR_INVALID, "cache buffer %s is NULL", name);
+  if (!aligned16(p)) return fail(KVQ_ERR_INVALID, "cache buffer %s is not 16-byte aligned", name);
+  return KVQ_OK;
+}
+
+bool valid_dtype(int d) { return d == KVQ_F32 || d == KVQ_F16 || d == KVQ_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+int kvq_layout_init(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T, int k_bits, int v_bits,
+                    int n_recent, int log_window) {
+  if (!L) return fail(KVQ_ERR_INVALID, "layout is NULL");
+  kvq_layout l{};
+  l.B = B;
+  l.Hq = Hq;
+  l.Hkv = Hkv;
+  l.Dk = Dk;
+  l.Dv = Dv;
+  l.T = T;
+  l.k_bits = k_bits;
+  l.v_bits = v_bits;
+  l.n_recent = n_recent;
+  l.log_window = log_window;
+  if (T >= 1 && n_recent >= 0 && n_recent <= T && log_window >= 0) {
+    const int64_t R = kvq::retained_before(rule_of(l), T);
+    l.R = int32_t(R);
+    l.Tq = int32_t(T - R);
+    l.n_groups = l.Tq / KVQ_GROUP;
+  }
+  const int st = check_layout(&l);
+  if (st != KVQ_OK) return st;
+  *L = l;
+  return ok();
+}
+
+int kvq_cache_sizes(const kvq_layout* L, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (!bytes_out) return fail(KVQ_ERR_INVALID, "bytes_out is NULL");
+  const size_t slabs = size_t(L->B) * size_t(L->Hkv);
+  const size_t Tq = size_t(L->Tq), nG = size_t(L->n_groups), R = size_t(L->R);
+  bytes_out[0] = slabs * Tq * size_t(L->Dk * L->k_bits / 32) * 4;   // k_codes
+  bytes_out[1] = slabs * nG * size_t(L->Dk) * 2;                    // k_scale
+  bytes_out[2] = bytes_out[1];                                      // k_zero
+  bytes_out[3] = slabs * Tq * size_t(L->Dv * L->v_bits / 32) * 4;   // v_codes
+  bytes_out[4] = slabs * Tq * size_t(L->Dv / KVQ_GROUP) * 2;        // v_scale
+  bytes_out[5] = bytes_out[4];                                      // v_zero
+  bytes_out[6] = slabs * R * size_t(L->Dk) * 2;                     // k_fp16
+  bytes_out[7] = slabs * R * size_t(L->Dv) * 2;                     // v_fp16
+  return ok();
+}
+
+int kvq_retained_positions(const kvq_layout* L, int32_t* out, int32_t capacity) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (capacity < L->R) return fail(KVQ_ERR_INVALID, "capacity %d < R = %d", capacity, L->R);
+  if (L->R > 0 && !out) return fail(KVQ_ERR_INVALID, "out is NULL");
+  const kvq::RetentionRule r = rule_of(*L);
+  int32_t n = 0;
+  // walk positions once; a position is retained when the running count steps
+  int64_t before = 0;
+  for (int64_t p = 0; p < L->T; ++p) {
+    const int64_t after = kvq::retained_before(r, p + 1);
+    if (after != before) out[n++] = int32_t(p);
+    before = after;
+  }
+  return ok();
+}
+
+int64_t kvq_quantized_before(const kvq_layout* L, int64_t t) {
+  if (check_layout(L) != KVQ_OK) return -1;
+  if (t < 0) t = 0;
+  if (t > L->T) t = L->T;
+  return kvq::quantized_before(rule_of(*L), t);
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_layout* L, int num_partitions) {
+  if (check_layout(L) != KVQ_OK || num_partitions < 1) return 0;
+  if (num_partitions == 1) return 0;
+  return size_t(L->B) * size_t(L->Hq) * size_t(num_partitions) * size_t(L->Dv + 2) * sizeof(float);
+}
+
+int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count, const void* K, const void* V,
+                  int kv_dtype, const kvq_cache* cache, void* stream) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (!cache) return fail(KVQ_ERR_INVALID, "cache is NULL");
+  if (!valid_dtype(kv_dtype)) return fail(KVQ_ERR_INVALID, "kv_dtype %d is not KVQ_F32/F16/BF16", kv_dtype);
+  if (t_begin < 0 || t_count < 1 || t_begin + t_count > L->T)
+    return fail(KVQ_ERR_INVALID, "chunk [%lld, %lld) is not inside [0, %d)", (long long)t_begin,
+                (long long)(t_begin + t_count), L->T);
+  if (!K || !V) return fail(KVQ_ERR_INVALID, "K or V is NULL");
+  if (!aligned16(K) || !aligned16(V)) return fail(KVQ_ERR_INVALID, "K and V must be 16-byte aligned");
+  const kvq::RetentionRule r = rule_of(*L);
+  const int64_t q0 = kvq::quantized_before(r, t_begin), q1 = kvq::quantized_before(r, t_begin + t_count);
+  if (q0 % KVQ_GROUP || q1 % KVQ_GROUP)
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "chunk [%lld, %lld) splits a key group (%lld and %lld quantized tokens before its ends)",
+                (long long)t_begin, (long long)(t_begin + t_count), (long long)q0, (long long)q1);
+  kvq::PackArgs a{};
+  a.L = *L;
+  a.t_begin = t_begin;
+  a.t_count = t_count;
+  a.g_begin = q0 / KVQ_GROUP;
+  a.n_groups_chunk = (q1 - q0) / KVQ_GROUP;
+  a.r_begin = t_begin - q0;
+  a.n_ret_chunk = (t_begin + t_count - q1) - a.r_begin;
+  a.K = K;
+  a.V = V;
+  a.dtype = kv_dtype;
+  a.cache = *cache;
+  if (a.n_groups_chunk > 0) {
+    if ((st = check_cache_ptr(cache->k_codes, "k_codes")) || (st = check_cache_ptr(cache->k_scale, "k_scale")) ||
+        (st = check_cache_ptr(cache->k_zero, "k_zero")) || (st = check_cache_ptr(cache->v_codes, "v_codes")) ||
+        (st = check_cache_ptr(cache->v_scale, "v_scale")) || (st = check_cache_ptr(cache->v_zero, "v_zero")))
+      return st;
+  }
+  if (a.n_ret_chunk > 0) {
+    if ((st = check_cache_ptr(cache->k_fp16, "k_fp16")) || (st = check_cache_ptr(cache->v_fp16, "v_fp16")))
+      return st;
+  }
+  const hipError_t e = kvq::launch_pack(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "pack launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kv_decode_attn(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache, float softmax_scale,
+                   int num_partitions, void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (!cache) return fail(KVQ_ERR_INVALID, "cache is NULL");
+  if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID, "q_dtype %d is not KVQ_F32/F16/BF16", q_dtype);
+  if (!q || !out) return fail(KVQ_ERR_INVALID, "q or out is NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(KVQ_ERR_INVALID, "q and out must be 16-byte aligned");
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID, "softmax_scale is not finite");
+  const int64_t max_p = (int64_t(L->T) + KVQ_GROUP - 1) / KVQ_GROUP;
+  if (num_partitions < 1 || num_partitions > (max_p > 1 ? max_p : 1))
+    return fail(KVQ_ERR_INVALID, "num_partitions %d must be in [1, %lld]", num_partitions, (long long)max_p);
+  if (num_partitions > 65535) return fail(KVQ_ERR_UNSUPPORTED, "num_partitions %d > 65535", num_partitions);
+  const size_t need = kvq_decode_workspace_bytes(L, num_partitions);
+  if (need > 0) {
+    if (!workspace) return fail(KVQ_ERR_INVALID, "workspace is NULL but %zu bytes are needed", need);
+    if (!aligned16(workspace)) return fail(KVQ_ERR_INVALID, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(KVQ_ERR_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  if (L->n_groups > 0) {
+    if ((st = check_cache_ptr(cache->k_codes, "k_codes")) || (st = check_cache_ptr(cache->k_scale, "k_scale")) ||
+        (st = check_cache_ptr(cache->k_zero, "k_zero")) || (st = check_cache_ptr(cache->v_codes, "v_codes")) ||
+        (st = check_cache_ptr(cache->v_scale, "v_scale")) || (st = check_cache_ptr(cache->v_zero, "v_zero")))
+      return st;
+  }
+  if (L->R > 0) {
+    if ((st = check_cache_ptr(cache->k_fp16, "k_fp16")) || (st = check_cache_ptr(cache->v_fp16, "v_fp16")))
+      return st;
+  }
+  if (L->B > 65535 || L->Hkv > 65535) return fail(KVQ_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  kvq::DecodeArgs a{};
+  a.L = *L;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.cache = *cache;
+  a.scale = softmax_scale;
+  a.P = num_partitions;
+  a.workspace = static_cast<float*>(workspace);
+  a.out = out;
+  const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_INVALID: return "KVQ_ERR_INVALID: invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED: request outside this build's limits";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP: HIP runtime error";
+    default: return "unknown kvq status";
+  }
+}
+
+const char* kvq_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,402 @@
+// kv_decode_attn kernels for gfx950.
+//
+// Single-token decode attention, out = softmax(scale * q K^T) V, computed
+// directly from the packed cache: key x_hat = code * s + z with one (s, z) per
+// (key group, channel), value x_hat = code * s + z with one (s, z) per (token,
+// 32-channel group).  The retained fp16 tokens are visited as a separate segment;
+// attention does not depend on token order ("LogQuant: Log-Distributed 2-Bit
+// Quantization of KV Cache", section 4, A.V = A_P.V_P).  Scores use the scale of
+// "HeadQ" section 2.1 / "Thin Keys, Full Values" section 2 (Dk may differ from Dv).
+//
+// Work split: one workgroup per (partition, kv head, batch row).  The Hq/Hkv query
+// heads sharing a kv head are all handled by that workgroup, so each packed byte is
+// read from HBM once per decode step.  Within the workgroup each wave owns every
+// 4th key group of the partition and keeps its own online-softmax state (running
+// max m, running sum l, unnormalised output o); waves are merged through LDS at the
+// end, partitions by a second small kernel (log-sum-exp merge).
+//
+// Dequantization is folded into the dot products so no dequantized tile is ever
+// materialised:
+//   q . k_hat_t = sum_c (q_c s_c) code_tc + sum_c q_c z_c          (keys, per group)
+//   sum_t p_t v_hat_tc = sum_t (p_t s_t,g(c)) code_tc + sum_t p_t z_t,g(c)   (values)
+// so the inner loops are one integer extract, one int->float convert and G fused
+// multiply-adds per code.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.hpp"
+
+namespace kvq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxVChansPerLane = KVQ_MAX_HEAD_DIM / 64;
+
+__device__ __forceinline__ float h2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
+
+template <int DT>
+__device__ __forceinline__ float load_q(const void* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_q<KVQ_F32>(const void* p, int64_t i) {
+  return static_cast<const float*>(p)[i];
+}
+template <>
+__device__ __forceinline__ float load_q<KVQ_F16>(const void* p, int64_t i) {
+  return __half2float(static_cast<const __half*>(p)[i]);
+}
+template <>
+__device__ __forceinline__ float load_q<KVQ_BF16>(const void* p, int64_t i) {
+  return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
+}
+
+__device__ __forceinline__ float sum32(float v) {
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) v += __shfl_xor(v, m, 32);
+  return v;
+}
+__device__ __forceinline__ float max32(float v) {
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 32));
+  return v;
+}
+__device__ __forceinline__ float sum64(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Online-softmax state of one wave for G queries.  m, l are wave-uniform; o holds
+// the lane's value channels c = lane + 64 j.
+template <int G>
+struct SoftmaxState {
+  float m[G], l[G];
+  float o[G][kMaxVChansPerLane];
+};
+
+// Fold 32 new scores (lane t and t+32 hold the same score of token t; tokens
+// beyond the valid count carry -inf) into the state; returns p_t in pv[].
+template <int G>
+__device__ __forceinline__ void softmax_update(SoftmaxState<G>& st, const float (&s)[G], float (&pv)[G]) {
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const float gmax = max32(s[i]);
+    const float m_new = fmaxf(st.m[i], gmax);
+    // m_new is finite as soon as one real token was seen
+    const float alpha = st.m[i] == -INFINITY ? 0.0f : __expf(st.m[i] - m_new);
+    pv[i] = s[i] == -INFINITY ? 0.0f : __expf(s[i] - m_new);
+    const float lsum = sum32(pv[i]);
+    st.l[i] = st.l[i] * alpha + lsum;
+    st.m[i] = m_new;
+#pragma unroll
+    for (int j = 0; j < kMaxVChansPerLane; ++j) st.o[i][j] *= alpha;
+  }
+}
+
+// Dynamic LDS layout (floats):
+//   qs   [G][Dk]                   scaled queries, shared by the waves
+//   per wave w: kq [Dk][G]          q_c * s_c of the current key group
+//               pp [32][ngv][G]     p_t * s_t,g of the current value rows
+//               pz [ngv][G]         sum_t p_t * z_t,g
+// After the loops the per-wave area is reused for the wave merge.
+template <int G>
+__host__ __device__ inline int wave_lds_floats(int Dk, int Dv) {
+  const int ngv = Dv / KVQ_GROUP;
+  return Dk * G + KVQ_GROUP * ngv * G + ngv * G;
+}
+
+template <int G, int QDT>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
+  extern __shared__ float lds[];
+  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Dk = a.L.Dk, Dv = a.L.Dv, kb = a.L.k_bits, vb = a.L.v_bits;
+  const int ngv = Dv / KVQ_GROUP;
+  const int nG = a.L.n_groups, R = a.L.R, P = a.P, Tq = a.L.Tq;
+  const int64_t slab = int64_t(b) * a.L.Hkv + h;
+
+  const int g0 = int(int64_t(p) * nG / P), g1 = int(int64_t(p + 1) * nG / P);
+  const int r0 = int(int64_t(p) * R / P), r1 = int(int64_t(p + 1) * R / P);
+
+  float* qs = lds;
+  float* wbase = lds + G * Dk + wave * wave_lds_floats<G>(Dk, Dv);
+  float* kq = wbase;
+  float* pp = kq + Dk * G;
+  float* pz = pp + KVQ_GROUP * ngv * G;
+
+  // scaled queries of the G heads sharing this kv head
+  for (int i = tid; i < G * Dk; i += kThreads) {
+    const int qi = i / Dk, c = i - qi * Dk;
+    qs[i] = a.scale * load_q<QDT>(a.q, (int64_t(b) * a.L.Hq + int64_t(h) * G + qi) * Dk + c);
+  }
+
+  SoftmaxState<G> st;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    st.m[i] = -INFINITY;
+    st.l[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxVChansPerLane; ++j) st.o[i][j] = 0.0f;
+  }
+  __syncthreads();
+
+  const int t = lane & 31, hf = lane >> 5;
+  const int kw = Dk * kb / 32, kper = 32 / kb;
+  const int vw = Dv * vb / 32;
+  const int vper_log = vb == 2 ? 4 : (vb == 4 ? 3 : 2);  // log2(32 / vb)
+  const uint32_t kmask = (1u << kb) - 1u, vmask = (1u << vb) - 1u;
+
+  // ------------------------------------------------------------ quantized groups
+  const int n_iter = (g1 - g0 + kWaves - 1) / kWaves;
+  for (int it = 0; it < n_iter; ++it) {
+    const int g = g0 + it * kWaves + wave;
+    const bool active = g < g1;
+    float bias[G];
+    if (active) {
+      // q'_c = q_c s_c for this group and the zero-point term sum_c q_c z_c
+      const uint16_t* ks = static_cast<const uint16_t*>(a.cache.k_scale) + (slab * nG + g) * Dk;
+      const uint16_t* kz = static_cast<const uint16_t*>(a.cache.k_zero) + (slab * nG + g) * Dk;
+#pragma unroll
+      for (int i = 0; i < G; ++i) bias[i] = 0.0f;
+      for (int c = lane; c < Dk; c += 64) {
+        const float s = h2f(ks[c]), z = h2f(kz[c]);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          const float qv = qs[i * Dk + c];
+          kq[c * G + i] = qv * s;
+          bias[i] += qv * z;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < G; ++i) bias[i] = sum64(bias[i]);
+    }
+    __syncthreads();
+
+    float pv[G];
+    if (active) {
+      // scores: lane (t, hf) takes token t and half the key channels
+      const uint32_t* row = static_cast<const uint32_t*>(a.cache.k_codes) + (slab * Tq + int64_t(g) * KVQ_GROUP + t) * kw;
+      float acc[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) acc[i] = 0.0f;
+      for (int w = hf * (kw / 2); w < (hf + 1) * (kw / 2); ++w) {
+        const uint32_t word = row[w];
+        for (int k = 0; k < kper; ++k) {
+          const float cf = float((word >> (k * kb)) & kmask);
+          const float* kqc = kq + (w * kper + k) * G;
+#pragma unroll
+          for (int i = 0; i < G; ++i) acc[i] = fmaf(kqc[i], cf, acc[i]);
+        }
+      }
+      float s[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) s[i] = acc[i] + __shfl_xor(acc[i], 32, 64) + bias[i];
+      softmax_update<G>(st, s, pv);
+
+      // p_t s_t,g into LDS and the zero-point sums
+      const int64_t vrow = slab * Tq + int64_t(g) * KVQ_GROUP + t;
+      const uint16_t* vs = static_cast<const uint16_t*>(a.cache.v_scale) + vrow * ngv;
+      const uint16_t* vz = static_cast<const uint16_t*>(a.cache.v_zero) + vrow * ngv;
+      for (int gc = 0; gc < ngv; ++gc) {
+        const float s_v = h2f(vs[gc]), z_v = h2f(vz[gc]);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          if (hf == 0) pp[(t * ngv + gc) * G + i] = pv[i] * s_v;
+          const float zsum = sum32(pv[i] * z_v);
+          if (lane == 0) pz[gc * G + i] = zsum;
+        }
+      }
+    }
+    __syncthreads();
+
+    if (active) {
+      // values: lane owns channels c = lane + 64 j
+      const uint32_t* vc = static_cast<const uint32_t*>(a.cache.v_codes) + (slab * Tq + int64_t(g) * KVQ_GROUP) * vw;
+      for (int tt = 0; tt < KVQ_GROUP; ++tt) {
+        const uint32_t* row = vc + tt * vw;
+#pragma unroll
+        for (int j = 0; j < kMaxVChansPerLane; ++j) {
+          const int c = lane + 64 * j;
+          if (c < Dv) {
+            const uint32_t word = row[c >> vper_log];
+            const float cf = float((word >> ((c & ((1 << vper_log) - 1)) * vb)) & vmask);
+            const float* ppt = pp + (tt * ngv + c / KVQ_GROUP) * G;
+#pragma unroll
+            for (int i = 0; i < G; ++i) st.o[i][j] = fmaf(ppt[i], cf, st.o[i][j]);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxVChansPerLane; ++j) {
+        const int c = lane + 64 * j;
+        if (c < Dv) {
+#pragma unroll
+          for (int i = 0; i < G; ++i) st.o[i][j] += pz[(c / KVQ_GROUP) * G + i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------- retained fp16 rows
+  const int n_rchunks = (r1 - r0 + KVQ_GROUP - 1) / KVQ_GROUP;
+  const int n_riter = (n_rchunks + kWaves - 1) / kWaves;
+  for (int it = 0; it < n_riter; ++it) {
+    const int ck = it * kWaves + wave;
+    const int rbeg = r0 + ck * KVQ_GROUP;
+    const bool active = ck < n_rchunks;
+    if (active) {
+      const int r = rbeg + t;
+      const bool valid = r < r1;
+      float acc[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) acc[i] = 0.0f;
+      if (valid) {
+        const uint16_t* krow = static_cast<const uint16_t*>(a.cache.k_fp16) + (slab * R + r) * Dk;
+        for (int c = hf * (Dk / 2); c < (hf + 1) * (Dk / 2); ++c) {
+          const float kv = h2f(krow[c]);
+#pragma unroll
+          for (int i = 0; i < G; ++i) acc[i] = fmaf(qs[i * Dk + c], kv, acc[i]);
+        }
+      }
+      float s[G], pv[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float full = acc[i] + __shfl_xor(acc[i], 32, 64);
+        s[i] = valid ? full : -INFINITY;
+      }
+      softmax_update<G>(st, s, pv);
+      if (hf == 0) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) pp[t * G + i] = pv[i];
+      }
+    }
+    __syncthreads();
+    if (active) {
+      const int nrow = min(KVQ_GROUP, r1 - rbeg);
+      for (int tt = 0; tt < nrow; ++tt) {
+        const uint16_t* vrow = static_cast<const uint16_t*>(a.cache.v_fp16) + (slab * R + rbeg + tt) * Dv;
+#pragma unroll
+        for (int j = 0; j < kMaxVChansPerLane; ++j) {
+          const int c = lane + 64 * j;
+          if (c < Dv) {
+            const float vv = h2f(vrow[c]);
+#pragma unroll
+            for (int i = 0; i < G; ++i) st.o[i][j] = fmaf(pp[tt * G + i], vv, st.o[i][j]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------- merge the waves
+  // per wave: m[G], l[G], o[G][Dv]
+  const int mstride = G * (Dv + 2);
+  float* mw = lds + G * Dk + wave * mstride;
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      mw[i] = st.m[i];
+      mw[G + i] = st.l[i];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxVChansPerLane; ++j) {
+    const int c = lane + 64 * j;
+    if (c < Dv) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) mw[2 * G + i * Dv + c] = st.o[i][j];
+    }
+  }
+  __syncthreads();
+  const float* m0 = lds + G * Dk;
+  for (int idx = tid; idx < G * Dv; idx += kThreads) {
+    const int i = idx / Dv, c = idx - i * Dv;
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m0[w * mstride + i]);
+    float Lsum = 0.0f, O = 0.0f;
+    for (int w = 0; w < kWaves; ++w) {
+      const float mwv = m0[w * mstride + i];
+      const float e = mwv == -INFINITY ? 0.0f : __expf(mwv - M);
+      Lsum += e * m0[w * mstride + G + i];
+      O += e * m0[w * mstride + 2 * G + i * Dv + c];
+    }
+    const int64_t qh = int64_t(b) * a.L.Hq + int64_t(h) * G + i;
+    if (P == 1) {
+      a.out[qh * Dv + c] = O / Lsum;
+    } else {
+      float* ws = a.workspace + (qh * P + p) * (Dv + 2);
+      if (c == 0) {
+        ws[0] = M;
+        ws[1] = Lsum;
+      }
+      ws[2 + c] = O;
+    }
+  }
+}
+
+// out[b, i, :] = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p over the partitions
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws, float* __restrict__ out,
+                                                    int P, int Dv) {
+  const int64_t qh = blockIdx.x;
+  const float* base = ws + qh * P * (Dv + 2);
+  float M = -INFINITY;
+  for (int p = 0; p < P; ++p) M = fmaxf(M, base[p * (Dv + 2)]);
+  for (int c = threadIdx.x; c < Dv; c += blockDim.x) {
+    float L = 0.0f, O = 0.0f;
+    for (int p = 0; p < P; ++p) {
+      const float* e = base + p * (Dv + 2);
+      const float w = e[0] == -INFINITY ? 0.0f : __expf(e[0] - M);
+      L += w * e[1];
+      O += w * e[2 + c];
+    }
+    out[qh * Dv + c] = O / L;
+  }
+}
+
+template <int G, int QDT>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  const int Dk = a.L.Dk, Dv = a.L.Dv;
+  const int loop_floats = G * Dk + kWaves * wave_lds_floats<G>(Dk, Dv);
+  const int merge_floats = G * Dk + kWaves * G * (Dv + 2);
+  const size_t lds = size_t(loop_floats > merge_floats ? loop_floats : merge_floats) * sizeof(float);
+  const dim3 grid(unsigned(a.P), unsigned(a.L.Hkv), unsigned(a.L.B));
+  if (lds > 64 * 1024) {
+    // gfx950 has 160 KB of LDS per CU; opt in to more than the default 64 KB
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<G, QDT>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((decode_kernel<G, QDT>), grid, dim3(kThreads), lds, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.P == 1) return e;
+  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(a.L.B * a.L.Hq)), dim3(256), 0, stream,
+                     a.workspace, a.out, a.P, Dv);
+  return hipGetLastError();
+}
+
+template <int QDT>
+hipError_t launch_q(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.L.Hq / a.L.Hkv) {
+    case 1: return launch_g<1, QDT>(a, stream);
+    case 2: return launch_g<2, QDT>(a, stream);
+    case 4: return launch_g<4, QDT>(a, stream);
+    case 8: return launch_g<8, QDT>(a, stream);
+    case 16: return launch_g<16, QDT>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.q_dtype) {
+    case KVQ_F32: return launch_q<KVQ_F32>(a, stream);
+    case KVQ_F16: return launch_q<KVQ_F16>(a, stream);
+    case KVQ_BF16: return launch_q<KVQ_BF16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

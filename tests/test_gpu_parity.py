@@ -1,0 +1,201 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+* kv_quant_pack: codes and fp16 scale/zero bit patterns equal the oracle's bit for
+  bit (the quantizer is a deterministic float32 recipe; nothing may differ).
+* kv_decode_attn: float32 output within 2e-3 (max abs) of the oracle's float64
+  attention over the same dequantized cache, fed first the oracle's packed cache,
+  then the GPU's own.  Partition count and order are free (any split of the
+  tokens gives the same attention), so several partition counts are checked.
+
+Small shapes run whole; the five benchmark workloads run at full size, comparing
+every packed byte where the oracle is fast enough and a sample of (batch, kv head)
+slabs otherwise.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_helpers import MAX_ABS_ERR, cache_from_numpy, cache_to_numpy, to_device, upload_workload
+from quantized_decode_attention_kv_amd import api
+from workloads import WORKLOADS, Workload, make_all, make_queries, small_cases, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _compare_pack(gpu: dict, ref: dict, where=""):
+    for k in O.CACHE_KEYS:
+        g, r = gpu[k], ref[k]
+        assert g.shape == r.shape, (k, g.shape, r.shape)
+        if not np.array_equal(g, r):
+            bad = np.argwhere(g != r)
+            raise AssertionError("%s%s: %d mismatches, first at %s: gpu %s oracle %s"
+                                 % (where, k, len(bad), bad[0].tolist(), g[tuple(bad[0])], r[tuple(bad[0])]))
+
+
+def _run_small(w: Workload, partitions=None):
+    _log("case %s" % w.name)
+    K, V = make_all(w, workers=4)
+    q = make_queries(w)
+    lay = api.Layout.from_workload(w)
+    Kd, Vd, qd = to_device(K, w.dtype), to_device(V, w.dtype), to_device(q, w.dtype)
+    cache = api.kv_quant_pack(lay, Kd, Vd)
+    torch.cuda.synchronize()
+    ref = O.pack_all(K, V, w)
+    _compare_pack(cache_to_numpy(cache), ref, w.name + " ")
+    scale = float(O.default_scale(w.Dk))
+    want = O.decode_all(q, ref, w, scale)
+    oracle_cache = cache_from_numpy(ref)
+    max_p = max(1, (w.T + 31) // 32)
+    for P in partitions or sorted(p for p in {1, 2, w.partitions, max_p} if p <= max_p):
+        for name, c in (("oracle-packed", oracle_cache), ("gpu-packed", cache)):
+            out = api.kv_decode_attn(lay, qd, c, num_partitions=P, softmax_scale=scale)
+            torch.cuda.synchronize()
+            err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
+            assert err <= MAX_ABS_ERR, (w.name, name, P, err)
+    return cache, ref
+
+
+@pytest.mark.parametrize("w", small_cases(), ids=lambda w: w.name)
+def test_small_cases(w):
+    _run_small(w)
+
+
+def test_tiny_ref_full():
+    """The 256-token fp32 reference workload, whole."""
+    _run_small(workload("tiny_ref"))
+
+
+def test_llama8b_gqa_4k_full():
+    """Llama-8B-shaped GQA decode at 4096 tokens, every slab compared."""
+    _run_small(workload("llama8b_gqa_4k"), partitions=[1, 4, 16])
+
+
+@pytest.mark.parametrize("w", [
+    Workload("one_group", B=1, Hq=4, Hkv=4, Dk=32, Dv=32, T=32, k_bits=2, v_bits=8, dtype="bf16", seed=31),
+    Workload("all_fp16", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=200, k_bits=4, v_bits=2, n_recent=200,
+             dtype="bf16", partitions=3, seed=32),
+    Workload("one_group_plus_fp16", B=1, Hq=2, Hkv=2, Dk=64, Dv=64, T=33, k_bits=4, v_bits=4, n_recent=1,
+             dtype="f32", seed=33),
+    Workload("max_dims_g16", B=1, Hq=16, Hkv=1, Dk=256, Dv=256, T=608, k_bits=8, v_bits=8, n_recent=32,
+             dtype="bf16", partitions=5, seed=34),
+    Workload("g1_wide_v", B=3, Hq=3, Hkv=3, Dk=32, Dv=256, T=256, k_bits=4, v_bits=2, dtype="bf16",
+             partitions=8, seed=35),
+], ids=lambda w: w.name)
+def test_edge_cases(w):
+    _run_small(w)
+
+
+def test_pack_deterministic_and_chunked():
+    """Two packs are bit-identical, and packing the cache in chunks that end on key
+    group boundaries gives the same bytes as one pack (the prefill-append path)."""
+    w = small_cases()[1]   # log-spaced retention: chunks cut through retained regions
+    K, V = make_all(w, workers=4)
+    lay = api.Layout.from_workload(w)
+    Kd, Vd = to_device(K, w.dtype), to_device(V, w.dtype)
+    a = cache_to_numpy(api.kv_quant_pack(lay, Kd, Vd))
+    b = cache_to_numpy(api.kv_quant_pack(lay, Kd, Vd))
+    _compare_pack(a, b, "repeat ")
+    # cut points where the quantized count before the cut is a multiple of 32
+    u = O.split_positions(w.T, w.n_recent, w.log_window)[1]
+    cuts = [0] + [int(u[k]) for k in range(32 * 7, len(u), 32 * 13)] + [w.T]
+    chunked = {k: torch.zeros_like(v) for k, v in api.alloc_cache(lay).items()}
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        api.kv_quant_pack(lay, Kd[:, :, t0:t1].contiguous(), Vd[:, :, t0:t1].contiguous(), cache=chunked, t_begin=t0)
+    torch.cuda.synchronize()
+    _compare_pack(cache_to_numpy(chunked), a, "chunked ")
+
+
+def test_pack_rejects_group_splitting_chunk():
+    w = small_cases()[0]
+    lay = api.Layout.from_workload(w)
+    K = torch.zeros((w.B, w.Hkv, 100, w.Dk), dtype=torch.bfloat16, device="cuda")
+    V = torch.zeros((w.B, w.Hkv, 100, w.Dv), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(api.L_.KvqError):
+        api.kv_quant_pack(lay, K, V, cache=api.alloc_cache(lay), t_begin=0)
+
+
+def test_constant_and_degenerate_groups():
+    """Constant key channels and value rows quantize to all-zero codes with s = +0 and
+    the dequantized value equal to fp16(x); signed zeros are stored as +0."""
+    w = Workload("const", B=1, Hq=2, Hkv=1, Dk=64, Dv=64, T=64, k_bits=4, v_bits=2, dtype="f32", seed=41)
+    rng = np.random.default_rng(0)
+    K = rng.standard_normal((1, 1, 64, 64)).astype(np.float32)
+    V = rng.standard_normal((1, 1, 64, 64)).astype(np.float32)
+    K[:, :, :32, 5] = 1.25
+    K[:, :, :32, 6] = -0.0
+    K[:, :, 32:, 7] = 0.0
+    K[:, :, 32:, 7][:, :, ::2] = -0.0
+    V[:, :, 3, :32] = -3.5
+    V[:, :, 4, 32:] = -0.0
+    lay = api.Layout.from_workload(w)
+    cache = api.kv_quant_pack(lay, to_device(K, "f32"), to_device(V, "f32"))
+    torch.cuda.synchronize()
+    _compare_pack(cache_to_numpy(cache), O.pack_all(K, V, w))
+
+
+# ------------------------------------------------------------------ full-size runs
+
+def _sample_slabs(w, n):
+    rng = np.random.default_rng(1234)
+    picks = {(0, 0), (w.B - 1, w.Hkv - 1)}
+    while len(picks) < min(n, w.B * w.Hkv):
+        picks.add((int(rng.integers(w.B)), int(rng.integers(w.Hkv))))
+    return sorted(picks)
+
+
+def _full_size(w: Workload, n_slabs: int):
+    _log("full-size %s: generating and uploading" % w.name)
+    Kd, Vd, qd = upload_workload(w)
+    lay = api.Layout.from_workload(w)
+    _log("full-size %s: pack" % w.name)
+    cache = api.kv_quant_pack(lay, Kd, Vd)
+    scale = float(O.default_scale(w.Dk))
+    _log("full-size %s: decode P=%d" % (w.name, w.partitions))
+    out = api.kv_decode_attn(lay, qd, cache, num_partitions=w.partitions, softmax_scale=scale)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().astype(np.float64)
+    q = make_queries(w)
+    G = w.G
+    for (b, h) in _sample_slabs(w, n_slabs):
+        _log("full-size %s: oracle slab (%d, %d)" % (w.name, b, h))
+        from workloads import make_slab
+        s = make_slab(w, b, h)
+        ref = O.pack_slab(s.K, s.V, w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window)
+        gpu = cache_to_numpy({k: t[b, h] for k, t in cache.items()})
+        _compare_pack(gpu, ref, "%s slab (%d,%d) " % (w.name, b, h))
+        want = O.decode_slab(q[b, h * G:(h + 1) * G], ref, w.dtype, w.k_bits, w.v_bits, scale)
+        err = np.abs(out[b, h * G:(h + 1) * G] - want).max()
+        assert err <= MAX_ABS_ERR, (w.name, b, h, err)
+    return Kd, Vd, qd, lay, cache
+
+
+@pytest.mark.slow
+def test_logquant_32k_full_size():
+    _full_size(workload("logquant_32k"), 4)
+
+
+@pytest.mark.slow
+def test_thin_keys_16k_full_size():
+    _full_size(workload("thin_keys_16k"), 4)
+
+
+@pytest.mark.slow
+def test_long_128k_full_size_and_prefill_chunk():
+    """128K-token cache at 64 partitions, then the 8192-token prefill chunk re-packed
+    on its own into the same cache must leave every byte unchanged."""
+    w = workload("long_128k")
+    Kd, Vd, qd, lay, cache = _full_size(w, 3)
+    before = {k: v.clone() for k, v in cache.items()}
+    t0 = w.T - w.prefill_chunk
+    api.kv_quant_pack(lay, Kd[:, :, t0:].contiguous(), Vd[:, :, t0:].contiguous(), cache=cache, t_begin=t0)
+    torch.cuda.synchronize()
+    for k in cache:
+        assert torch.equal(before[k], cache[k]), k

@@ -86,6 +86,6 @@ def small_cases():
                  dtype="bf16", partitions=3, seed=13),
         Workload("small_k4v8_f32", B=1, Hq=2, Hkv=1, Dk=64, Dv=96, T=352, k_bits=4, v_bits=8,
                  n_recent=32, dtype="f32", partitions=4, seed=14),
-        Workload("small_g8_k2v4", B=1, Hq=16, Hkv=2, Dk=96, Dv=64, T=576, k_bits=2, v_bits=4,
+        Workload("small_g8_k2v4", B=1, Hq=16, Hkv=2, Dk=96, Dv=64, T=579, k_bits=2, v_bits=4,
                  n_recent=0, log_window=32, dtype="bf16", partitions=2, seed=15),
     ]
