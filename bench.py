@@ -1,0 +1,276 @@
+"""Benchmark of the packed-KV decode hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input on the
+128K-token workload (B=4, 32 query / 8 KV heads, head dim 128, K4V2, 128-token fp16
+window):  kv_quant_pack of the newest 8192-token prefill chunk into its place in
+the packed cache, then kv_decode_attn of one new token per sequence over all
+131072 cached tokens with 64 split-K partitions.  Inputs are resident in HBM
+before timing starts.
+
+Prints one JSON line.  ``value`` is the effective HBM throughput of a whole step:
+the algorithmic bytes of the step (each packed byte, scale, zero, fp16 row, query
+and output moved once; the prefill chunk read once and its packed form written
+once) divided by the measured step time.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak, 8 TB/s
+METRIC = "quantized-KV decode attn: effective HBM GB/s (% of peak) + decode steps/sec"
+DECODE_SRC = os.path.join(ROOT, "quantized_decode_attention_kv_amd", "csrc", "kvq_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_long_128k_hbm_traffic.txt")
+
+
+# ----------------------------------------------------------------- byte accounting
+
+def decode_bytes(w, R, Tq):
+    """Algorithmic bytes of one decode call: packed codes, scales and zeros, fp16
+    retained rows, the queries (storage dtype) and the float32 output, each once."""
+    slabs = w.B * w.Hkv
+    qb = 4 if w.dtype == "f32" else 2
+    k_codes = slabs * Tq * w.Dk * w.k_bits // 8
+    k_sz = slabs * (Tq // 32) * w.Dk * 2 * 2
+    v_codes = slabs * Tq * w.Dv * w.v_bits // 8
+    v_sz = slabs * Tq * (w.Dv // 32) * 2 * 2
+    fp16 = slabs * R * (w.Dk + w.Dv) * 2
+    return k_codes + k_sz + v_codes + v_sz + fp16 + w.B * w.Hq * w.Dk * qb + w.B * w.Hq * w.Dv * 4
+
+
+def pack_bytes(w, n_tokens, n_quant):
+    """Algorithmic bytes of packing n_tokens positions of which n_quant are quantized:
+    K and V read once, codes / scales / zeros / fp16 rows written once."""
+    slabs = w.B * w.Hkv
+    eb = 4 if w.dtype == "f32" else 2
+    read = slabs * n_tokens * (w.Dk + w.Dv) * eb
+    n_ret = n_tokens - n_quant
+    write = (slabs * n_quant * (w.Dk * w.k_bits + w.Dv * w.v_bits) // 8
+             + slabs * (n_quant // 32) * w.Dk * 4 + slabs * n_quant * (w.Dv // 32) * 4
+             + slabs * n_ret * (w.Dk + w.Dv) * 2)
+    return read + write
+
+
+def kernel_source_hash():
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per decode launch from the committed counter summary, if it was taken
+    on the current decode kernel source (else None)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def _cpu_worker(args):
+    """Runs in a spawned process: oracle on a list of (b, h) slabs of the workload.
+    Returns (seconds spent in the oracle, bytes covered)."""
+    wname, slabs = args
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    import numpy as np
+    import oracle as O
+    from workloads import make_queries, make_slab, workload
+    w = workload(wname)
+    q = make_queries(w)
+    t_chunk = w.T - w.prefill_chunk
+    spent = 0.0
+    for b, h in slabs:
+        s = make_slab(w, b, h)
+        # the packed cache before the step (setup, not timed)
+        full = O.pack_slab(s.K, s.V, w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window)
+        t0 = time.perf_counter()
+        # the step: pack the prefill chunk ...
+        if w.prefill_chunk:
+            _oracle_pack_chunk(O, s, w, t_chunk)
+        # ... and decode the G query heads of this kv head over the whole slab
+        G = w.Hq // w.Hkv
+        O.decode_slab(q[b, h * G:(h + 1) * G], full, w.dtype, w.k_bits, w.v_bits, O.default_scale(w.Dk))
+        spent += time.perf_counter() - t0
+    return spent, len(slabs)
+
+
+def _oracle_pack_chunk(O, s, w, t0):
+    """Oracle pack of positions [t0, T) of a slab.  With a recent window only (no
+    log-spaced positions) the chunk's retained tokens are its newest ones and the
+    rest are whole key groups, so the chunk packs like a cache of its own length."""
+    assert w.log_window == 0
+    n = w.T - t0
+    return O.pack_slab(s.K[t0:], s.V[t0:], w.dtype, w.k_bits, w.v_bits, min(w.n_recent, n), 0)
+
+
+def cpu_baseline(w, step_bytes, budget_workers=None):
+    import multiprocessing as mp
+    cores = budget_workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    slabs = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    per = [slabs[i::cores] for i in range(cores)]
+    per = [p[:1] for p in per if p]          # one slab per worker: about 1-2 s of oracle work each
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(len(per)) as pool:
+        res = pool.map(_cpu_worker, [(w.name, p) for p in per])
+    wall = time.perf_counter() - t0
+    busiest = max(r[0] for r in res)
+    n_slabs = sum(r[1] for r in res)
+    covered = step_bytes * n_slabs / (w.B * w.Hkv)
+    return {
+        "value": covered / busiest / 1e9,
+        "unit": "GB/s",
+        "cores": len(per),
+        "kind": "oracle",
+        "sample": ("%d of %d (batch, kv-head) slabs of the step, one per worker process (1 BLAS thread each): "
+                   "%sfloat64 decode over the whole %d-token slab; throughput = the slabs' share of the step's "
+                   "algorithmic bytes / the busiest worker's oracle time (%.2f s; %.1f s wall incl. input "
+                   "generation and the untimed full-slab pack)"
+                   % (n_slabs, w.B * w.Hkv,
+                      ("oracle pack of the %d-token prefill chunk + " % w.prefill_chunk) if w.prefill_chunk else "",
+                      w.T, busiest, wall)),
+    }
+
+
+# ------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long_128k",
+                    help="workload name (the headline step is long_128k; others are for exploration)")
+    ap.add_argument("--partitions", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path has no multi-GPU mode (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_decode_attention_kv_amd import api
+    from workloads import workload
+    from workloads.device import upload_workload
+
+    w = workload(args.workload)
+    P = args.partitions or w.partitions
+    lay = api.Layout.from_workload(w)
+    dev = torch.device("cuda:0")
+    print("# %s: generating inputs" % w.name, file=sys.stderr, flush=True)
+    Kd, Vd, qd = upload_workload(w)
+    cache = api.alloc_cache(lay, dev)
+    # the cache before the step: everything packed once (untimed setup)
+    api.kv_quant_pack(lay, Kd, Vd, cache=cache)
+    chunk = w.prefill_chunk
+    t0 = w.T - chunk
+    if chunk:
+        Kc = Kd[:, :, t0:].contiguous()
+        Vc = Vd[:, :, t0:].contiguous()
+    del Kd, Vd
+    ws = torch.zeros(max(1, lay.workspace_bytes(P)), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.float32, device=dev)
+    scale = 1.0 / (w.Dk ** 0.5)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if chunk:
+            api.kv_quant_pack(lay, Kc, Vc, cache=cache, t_begin=t0)
+        if ev is not None:
+            ev[1].record()
+        api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    print("# %s: warmup %d" % (w.name, args.warmup), file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - start
+    pack_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    n_quant_chunk = lay.quantized_before(w.T) - lay.quantized_before(t0) if chunk else 0
+    db = decode_bytes(w, lay.R, lay.Tq)
+    pb = pack_bytes(w, chunk, n_quant_chunk) if chunk else 0
+    step_bytes = db + pb
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_gbps = db / (dec_ms * 1e-3) / 1e9
+    traffic = read_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded N(0,1) keys with 4 outlier channels x8 and per-channel N(0,2) offsets, "
+                "N(0,0.5) values, N(0,1) queries; bf16 in HBM",
+        "config": {
+            "workload": "%s: B%d Hq%d Hkv%d Dk%d Dv%d T%d K%dV%d fp16-window %d log-window %d, %d partitions%s"
+                        % (w.name, w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T, w.k_bits, w.v_bits, w.n_recent,
+                           w.log_window, P, (", + %d-token prefill pack" % chunk) if chunk else ""),
+            "batch": w.B, "cached_tokens": w.T, "partitions": P,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "steps_per_s": round(1e3 / ms_per_step, 1),
+        "decode": {"us": round(dec_ms * 1e3, 2), "GBps": round(dec_gbps, 1),
+                   "pct_of_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
+                   "steps_per_s": round(1e3 / dec_ms, 1), "tokens_per_s": round(w.B * 1e3 / dec_ms, 1),
+                   "algorithmic_bytes": db},
+        "pack": ({"us": round(pack_ms * 1e3, 2), "GBps": round(pb / (pack_ms * 1e-3) / 1e9, 1),
+                  "algorithmic_bytes": pb} if chunk else None),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "decode_kernel (kv_decode_attn)",
+                     "kernel_source_sha256_16": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        print("# %s: cpu baseline (oracle)" % w.name, file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, step_bytes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

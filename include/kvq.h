@@ -34,9 +34,14 @@
  *            w*(32/k_bits)+k at bits [k*k_bits, (k+1)*k_bits), little-endian
  *   k_scale  fp16   [B, Hkv, n_groups, Dk]
  *   k_zero   fp16   [B, Hkv, n_groups, Dk]
- *   v_codes  uint32 [B, Hkv, Tq, Dv*v_bits/32]  same packing along channels
- *   v_scale  fp16   [B, Hkv, Tq, Dv/32]
- *   v_zero   fp16   [B, Hkv, Tq, Dv/32]
+ *   v_codes  uint8  [B, Hkv, n_groups, 4, Dv, v_bits]  values are stored channel
+ *            by channel inside each key group, in four 8-token octets: the v_bits
+ *            bytes of (group g, octet o, channel c) form one little-endian field
+ *            of 8*v_bits bits whose bits [k*v_bits, (k+1)*v_bits) hold the code of
+ *            compacted token 32g + 8o + k
+ *   v_scale  fp16   [B, Hkv, n_groups, Dv/32, 32]  one per token and 32-channel
+ *            group; the 32 tokens of a group are contiguous
+ *   v_zero   fp16   [B, Hkv, n_groups, Dv/32, 32]
  *   k_fp16   fp16   [B, Hkv, R, Dk]   retained positions, ascending
  *   v_fp16   fp16   [B, Hkv, R, Dv]
  *
@@ -110,9 +115,10 @@ int kvq_retained_positions(const kvq_layout* L, int32_t* out, int32_t capacity);
  * a chunk [t0, t1) can be packed on its own when both counts are multiples of 32. */
 int64_t kvq_quantized_before(const kvq_layout* L, int64_t t);
 
-/* Workspace kv_decode_attn needs for num_partitions sequence partitions:
- * B * Hq * num_partitions * (Dv + 2) floats (0 when num_partitions == 1).
- * Returns 0 for an invalid layout. */
+/* Workspace kv_decode_attn needs for num_partitions sequence partitions (0 when
+ * num_partitions == 1): B*Hkv 32-bit arrival counters padded to a multiple of 256
+ * bytes, then B*Hq*num_partitions*(Dv+2) floats of partial results.  Returns 0 for
+ * an invalid layout. */
 size_t kvq_decode_workspace_bytes(const kvq_layout* L, int num_partitions);
 
 /*
@@ -135,7 +141,9 @@ int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count,
                   const kvq_cache* cache, void* stream);
 
 /*
- * kv_decode_attn — single-token decode attention over a packed cache.
+ * kv_decode_attn — single-token decode attention over a packed cache (one kernel
+ * launch; partitions are merged by the last workgroup of each (batch, kv head) to
+ * finish).
  *   q:   [B, Hq, Dk] device array of dtype q_dtype; query head i reads KV head
  *        i / (Hq / Hkv) (grouped-query attention: the Hq/Hkv queries of one KV head
  *        share each read of its cache).
@@ -144,7 +152,11 @@ int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count,
  *        p takes key groups [p*n_groups/P, (p+1)*n_groups/P) and retained tokens
  *        [p*R/P, (p+1)*R/P) (integer division).  1 <= P <= max(1, ceil(T/32)).
  *   workspace / workspace_bytes: at least kvq_decode_workspace_bytes(L, P) bytes of
- *        device memory (may be NULL when P == 1); contents on entry do not matter.
+ *        device memory (may be NULL when P == 1).  Its leading arrival counters
+ *        must be zero before the first call that uses it (allocate it zeroed);
+ *        every call leaves them zero again, the rest needs no initialisation.  A
+ *        workspace serves one call at a time: calls that overlap on the GPU
+ *        (different streams) need separate workspaces.
  *   out: [B, Hq, Dv] float32 device array.
  * Partial results of the partitions are merged on the device.
  */

@@ -10,11 +10,13 @@ from .kvq_oracle import (  # noqa: F401
     dequant_slab,
     pack_all,
     pack_codes,
+    pack_octets,
     pack_slab,
     quantize_groups,
     retained_mask,
     slab_of,
     split_positions,
     unpack_codes,
+    unpack_octets,
     upcast,
 )

@@ -33,10 +33,14 @@ Canonical packed layout for one (b, kv-head) slab (the same index formulas appea
 * retained (fp16) positions r = sorted retained set, compacted positions
   u = sorted(the rest); Tq = len(u), groups of 32 consecutive compacted tokens;
 * k_codes  u32 [Tq, Dk*kb/32]: word w of row t holds channel w*(32/kb)+k at bits
-  [k*kb, k*kb+kb), little-endian;
+  [k*kb, k*kb+kb), little-endian (keys stored token by token);
 * k_scale, k_zero fp16 [Tq/32, Dk]  (one pair per token group and channel);
-* v_codes  u32 [Tq, Dv*vb/32]   (same packing along channels);
-* v_scale, v_zero fp16 [Tq, Dv/32]  (one pair per token and 32-channel group);
+* v_codes  u8 [Tq/32, 4, Dv, vb]: values stored channel by channel inside each
+  32-token group, in four 8-token octets: the vb bytes of (group g, octet o,
+  channel c) are one little-endian field of 8*vb bits holding the code of token
+  32g+8o+k at bits [k*vb, k*vb+vb);
+* v_scale, v_zero fp16 [Tq/32, Dv/32, 32]  (one pair per token and 32-channel
+  group, the 32 tokens of a group contiguous);
 * k_fp16 [R, Dk], v_fp16 [R, Dv] fp16 rows of the retained positions, ascending.
 """
 
@@ -144,6 +148,24 @@ def unpack_codes(words: np.ndarray, bits: int) -> np.ndarray:
     return c.reshape(c.shape[:-2] + (c.shape[-2] * per,)).astype(np.uint8)
 
 
+def pack_octets(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes [..., 8] -> uint8 [..., bits]: the little-endian field of 8*bits bits with
+    code k at bits [k*bits, k*bits+bits)."""
+    c = np.asarray(codes, dtype=np.uint64)
+    shifts = np.arange(8, dtype=np.uint64) * np.uint64(bits)
+    field = np.bitwise_or.reduce(c << shifts, axis=-1)                # < 2^(8*bits) <= 2^64
+    by = (field[..., None] >> (np.arange(bits, dtype=np.uint64) * np.uint64(8))) & np.uint64(0xFF)
+    return by.astype(np.uint8)
+
+
+def unpack_octets(fields: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of pack_octets: uint8 [..., bits] -> codes uint8 [..., 8]."""
+    by = np.asarray(fields, dtype=np.uint64)
+    field = np.bitwise_or.reduce(by << (np.arange(bits, dtype=np.uint64) * np.uint64(8)), axis=-1)
+    c = (field[..., None] >> (np.arange(8, dtype=np.uint64) * np.uint64(bits))) & np.uint64(2 ** bits - 1)
+    return c.astype(np.uint8)
+
+
 def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_window: int):
     """Quantize and pack one (b, kv-head) slab.  K [T, Dk], V [T, Dv] in storage dtype.
 
@@ -170,15 +192,18 @@ def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_win
     # values: one (s, z) per token and 32-channel group
     Vg = V32[u].reshape(Tq, Dv // GROUP, GROUP)
     vc, vs, vz = quantize_groups(Vg, v_bits)                          # [Tq, Dv/32, 32], [Tq, Dv/32]
-    vc = vc.reshape(Tq, Dv)
+    # storage order: group, octet, channel, 8 tokens of the octet
+    vc = vc.reshape(nG, 4, 8, Dv).transpose(0, 1, 3, 2)              # [nG, 4, Dv, 8]
+    vs = vs.reshape(nG, GROUP, Dv // GROUP).transpose(0, 2, 1)       # [nG, Dv/32, 32]
+    vz = vz.reshape(nG, GROUP, Dv // GROUP).transpose(0, 2, 1)
 
     return {
         "k_codes": pack_codes(kc, k_bits),
         "k_scale": ks.view(np.uint16),
         "k_zero": kz.view(np.uint16),
-        "v_codes": pack_codes(vc, v_bits),
-        "v_scale": vs.view(np.uint16),
-        "v_zero": vz.view(np.uint16),
+        "v_codes": pack_octets(vc, v_bits),
+        "v_scale": np.ascontiguousarray(vs).view(np.uint16),
+        "v_zero": np.ascontiguousarray(vz).view(np.uint16),
         "k_fp16": K32[r].astype(np.float16).view(np.uint16),
         "v_fp16": V32[r].astype(np.float16).view(np.uint16),
     }
@@ -212,11 +237,12 @@ def dequant_slab(p, k_bits: int, v_bits: int):
     kz = p["k_zero"].view(np.float16).astype(np.float64)
     g = np.arange(Tq) // GROUP
     Khat_q = kc * ks[g] + kz[g]
-    vc = unpack_codes(p["v_codes"], v_bits).astype(np.float64)      # [Tq, Dv]
-    Dv = vc.shape[1]
-    vs = np.repeat(p["v_scale"].view(np.float16).astype(np.float64), GROUP, axis=1)
-    vz = np.repeat(p["v_zero"].view(np.float16).astype(np.float64), GROUP, axis=1)
-    Vhat_q = vc * vs + vz
+    vc = unpack_octets(p["v_codes"], v_bits)                         # [nG, 4, Dv, 8]
+    nG, _, Dv, _ = vc.shape
+    vc = vc.transpose(0, 1, 3, 2).reshape(Tq, Dv).astype(np.float64)  # token 32g + 8o + k
+    vs = p["v_scale"].view(np.float16).astype(np.float64).transpose(0, 2, 1).reshape(Tq, Dv // GROUP)
+    vz = p["v_zero"].view(np.float16).astype(np.float64).transpose(0, 2, 1).reshape(Tq, Dv // GROUP)
+    Vhat_q = vc * np.repeat(vs, GROUP, axis=1) + np.repeat(vz, GROUP, axis=1)
     Kr = p["k_fp16"].view(np.float16).astype(np.float64)              # [R, Dk]
     Vr = p["v_fp16"].view(np.float16).astype(np.float64)              # [R, Dv]
     return np.concatenate([Khat_q, Kr]), np.concatenate([Vhat_q, Vr])

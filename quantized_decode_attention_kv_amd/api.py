@@ -55,18 +55,26 @@ class Layout:
         return int(L_.load().kvq_decode_workspace_bytes(self.ref, num_partitions))
 
     def shapes(self):
-        """Tensor shape and dtype of each cache buffer (codes as int32 bit patterns)."""
+        """Tensor shape and dtype of each cache buffer (key codes as int32 bit patterns,
+        value codes as bytes)."""
         B, H, Tq, nG, R = self.B, self.Hkv, self.Tq, self.n_groups, self.R
         return {
             "k_codes": ((B, H, Tq, self.Dk * self.k_bits // 32), torch.int32),
             "k_scale": ((B, H, nG, self.Dk), torch.float16),
             "k_zero": ((B, H, nG, self.Dk), torch.float16),
-            "v_codes": ((B, H, Tq, self.Dv * self.v_bits // 32), torch.int32),
-            "v_scale": ((B, H, Tq, self.Dv // 32), torch.float16),
-            "v_zero": ((B, H, Tq, self.Dv // 32), torch.float16),
+            "v_codes": ((B, H, nG, 4, self.Dv, self.v_bits), torch.uint8),
+            "v_scale": ((B, H, nG, self.Dv // 32, 32), torch.float16),
+            "v_zero": ((B, H, nG, self.Dv // 32, 32), torch.float16),
             "k_fp16": ((B, H, R, self.Dk), torch.float16),
             "v_fp16": ((B, H, R, self.Dv), torch.float16),
         }
+
+
+def alloc_workspace(layout: Layout, num_partitions: int, device="cuda"):
+    """Decode workspace for num_partitions partitions, zero-initialised as the library
+    requires (its arrival counters start at zero and every call leaves them zero)."""
+    need = layout.workspace_bytes(num_partitions)
+    return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
 
 
 def alloc_cache(layout: Layout, device="cuda"):
@@ -131,7 +139,7 @@ def kv_decode_attn(layout: Layout, q, cache, num_partitions: int = 1, softmax_sc
         raise ValueError("out must be a contiguous float32 tensor [B, Hq, Dv]")
     need = layout.workspace_bytes(num_partitions)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = alloc_workspace(layout, num_partitions, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     cs = _cache_struct(layout, cache)

@@ -147,7 +147,7 @@ int64_t kvq_quantized_before(const kvq_layout* L, int64_t t) {
 size_t kvq_decode_workspace_bytes(const kvq_layout* L, int num_partitions) {
   if (check_layout(L) != KVQ_OK || num_partitions < 1) return 0;
   if (num_partitions == 1) return 0;
-  return size_t(L->B) * size_t(L->Hq) * size_t(num_partitions) * size_t(L->Dv + 2) * sizeof(float);
+  return kvq::ws_counter_bytes(*L) + kvq::ws_partial_bytes(*L, num_partitions);
 }
 
 int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count, const void* K, const void* V,
@@ -232,7 +232,10 @@ int kv_decode_attn(const kvq_layout* L, const void* q, int q_dtype, const kvq_ca
   a.cache = *cache;
   a.scale = softmax_scale;
   a.P = num_partitions;
-  a.workspace = static_cast<float*>(workspace);
+  if (need > 0) {
+    a.counters = static_cast<uint32_t*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + kvq::ws_counter_bytes(*L));
+  }
   a.out = out;
   const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));

@@ -1,0 +1,123 @@
+// Pieces shared by the decode kernels: query loads, the log-sum-exp combination of
+// partial softmax states and the cross-partition merge epilogue.
+//
+// Scores are kept in the log2 domain (s * log2 e) so every exponential is a single
+// exp2.  A partial result is (m, l, o): running max m, sum l of 2^(s - m) and the
+// unnormalised output o = sum 2^(s - m) v.  Two partials combine as
+//   M = max(m1, m2),  l = 2^(m1-M) l1 + 2^(m2-M) l2,  o = 2^(m1-M) o1 + 2^(m2-M) o2,
+// which is exact in real arithmetic for any split of the tokens (attention does not
+// depend on token order: "LogQuant: Log-Distributed 2-Bit Quantization of KV
+// Cache", section 4).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.hpp"
+
+namespace kvq {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeWaves = kDecodeThreads / 64;
+
+__device__ __forceinline__ float h2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
+
+template <int DT>
+__device__ __forceinline__ float load_q(const void* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_q<KVQ_F32>(const void* p, int64_t i) {
+  return static_cast<const float*>(p)[i];
+}
+template <>
+__device__ __forceinline__ float load_q<KVQ_F16>(const void* p, int64_t i) {
+  return __half2float(static_cast<const __half*>(p)[i]);
+}
+template <>
+__device__ __forceinline__ float load_q<KVQ_BF16>(const void* p, int64_t i) {
+  return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
+}
+
+// query element i of a q array of dtype qdt (wave-uniform branch)
+__device__ __forceinline__ float load_q_any(const void* p, int qdt, int64_t i) {
+  if (qdt == KVQ_BF16) return load_q<KVQ_BF16>(p, i);
+  if (qdt == KVQ_F16) return load_q<KVQ_F16>(p, i);
+  return load_q<KVQ_F32>(p, i);
+}
+
+__device__ __forceinline__ float lse_weight(float m, float M) { return m == -INFINITY ? 0.0f : exp2f(m - M); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Finish one workgroup's (batch b, kv head h, partition p) result for its G query
+// heads.  res: LDS [G][Dv + 2] = (m, l, o[Dv]); flag: one int of LDS.
+// P == 1: write out = o / l.  P > 1: publish the partial; the last workgroup of the
+// (b, h) pair to arrive merges all P partials (one wave per query head, lanes over
+// channels) and resets the pair's counter to zero for the next call.  All
+// kDecodeThreads threads must call this.
+__device__ inline void finish_partition(const DecodeArgs& a, int G, int b, int h, int p, const float* res,
+                                        int* flag) {
+  const int tid = threadIdx.x, Dv = a.L.Dv, P = a.P;
+  const int64_t qh0 = int64_t(b) * a.L.Hq + int64_t(h) * G;
+  if (P == 1) {
+    for (int idx = tid; idx < G * Dv; idx += kDecodeThreads) {
+      const int i = idx / Dv, c = idx - i * Dv;
+      a.out[(qh0 + i) * Dv + c] = res[i * (Dv + 2) + 2 + c] / res[i * (Dv + 2) + 1];
+    }
+    return;
+  }
+  for (int idx = tid; idx < G * (Dv + 2); idx += kDecodeThreads) {
+    const int i = idx / (Dv + 2), e = idx - i * (Dv + 2);
+    a.partials[((qh0 + i) * P + p) * (Dv + 2) + e] = res[idx];
+  }
+  __threadfence();  // make this partial visible device-wide before counting it
+  __syncthreads();
+  const int64_t slab = int64_t(b) * a.L.Hkv + h;
+  if (tid == 0) *flag = atomicAdd(a.counters + slab, 1u) == unsigned(P - 1);
+  __syncthreads();
+  if (!*flag) return;
+  __threadfence();  // acquire: the other partitions' partials are visible now
+
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int i = wave; i < G; i += kDecodeWaves) {
+    const float* base = a.partials + (qh0 + i) * P * (Dv + 2);
+    float M = -INFINITY;
+    for (int pp = lane; pp < P; pp += 64) M = fmaxf(M, base[pp * (Dv + 2)]);
+    M = wave_max(M);
+    float L = 0.0f;
+    for (int pp = lane; pp < P; pp += 64) L += lse_weight(base[pp * (Dv + 2)], M) * base[pp * (Dv + 2) + 1];
+    L = wave_sum(L);
+    float O[KVQ_MAX_HEAD_DIM / 64] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p0 = 0; p0 < P; p0 += 64) {
+      const int mine = p0 + lane;
+      const float wl = mine < P ? lse_weight(base[mine * (Dv + 2)], M) : 0.0f;
+      const int cnt = P - p0 < 64 ? P - p0 : 64;
+      for (int k = 0; k < cnt; ++k) {
+        const float w = __shfl(wl, k, 64);
+        const float* src = base + (p0 + k) * (Dv + 2) + 2;
+#pragma unroll
+        for (int j = 0; j < KVQ_MAX_HEAD_DIM / 64; ++j) {
+          const int c = lane + 64 * j;
+          if (c < Dv) O[j] += w * src[c];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KVQ_MAX_HEAD_DIM / 64; ++j) {
+      const int c = lane + 64 * j;
+      if (c < Dv) a.out[(qh0 + i) * Dv + c] = O[j] / L;
+    }
+  }
+  if (tid == 0) a.counters[slab] = 0u;
+}
+
+}  // namespace kvq

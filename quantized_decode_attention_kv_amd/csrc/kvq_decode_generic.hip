@@ -1,4 +1,7 @@
-// kv_decode_attn kernels for gfx950.
+// kv_decode_attn, generic kernel for gfx950: any supported shape (head widths that
+// are multiples of 32 up to 256, 1..16 query heads per KV head, 2/4/8-bit codes).
+// The MFMA kernel (kvq_decode_mfma.hip) takes the common shapes; this one is the
+// reference-style fallback and the dispatcher of both.
 //
 // Single-token decode attention, out = softmax(scale * q K^T) V, computed
 // directly from the packed cache: key x_hat = code * s + z with one (s, z) per
@@ -13,7 +16,7 @@
 // read from HBM once per decode step.  Within the workgroup each wave owns every
 // 4th key group of the partition and keeps its own online-softmax state (running
 // max m, running sum l, unnormalised output o); waves are merged through LDS at the
-// end, partitions by a second small kernel (log-sum-exp merge).
+// end, partitions by the last workgroup to finish (finish_partition).
 //
 // Dequantization is folded into the dot products so no dequantized tile is ever
 // materialised:
@@ -24,31 +27,20 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include "kvq_decode_common.hpp"
 #include "kvq_internal.hpp"
 
 namespace kvq {
+
+// MFMA kernel launcher (kvq_decode_mfma.hip); returns hipErrorNotSupported for
+// shapes it does not take.
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = kDecodeWaves;
+constexpr int kThreads = kDecodeThreads;
 constexpr int kMaxVChansPerLane = KVQ_MAX_HEAD_DIM / 64;
-
-__device__ __forceinline__ float h2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
-
-template <int DT>
-__device__ __forceinline__ float load_q(const void* p, int64_t i);
-template <>
-__device__ __forceinline__ float load_q<KVQ_F32>(const void* p, int64_t i) {
-  return static_cast<const float*>(p)[i];
-}
-template <>
-__device__ __forceinline__ float load_q<KVQ_F16>(const void* p, int64_t i) {
-  return __half2float(static_cast<const __half*>(p)[i]);
-}
-template <>
-__device__ __forceinline__ float load_q<KVQ_BF16>(const void* p, int64_t i) {
-  return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
-}
 
 __device__ __forceinline__ float sum32(float v) {
 #pragma unroll
@@ -83,8 +75,8 @@ __device__ __forceinline__ void softmax_update(SoftmaxState<G>& st, const float 
     const float gmax = max32(s[i]);
     const float m_new = fmaxf(st.m[i], gmax);
     // m_new is finite as soon as one real token was seen
-    const float alpha = st.m[i] == -INFINITY ? 0.0f : __expf(st.m[i] - m_new);
-    pv[i] = s[i] == -INFINITY ? 0.0f : __expf(s[i] - m_new);
+    const float alpha = st.m[i] == -INFINITY ? 0.0f : exp2f(st.m[i] - m_new);
+    pv[i] = s[i] == -INFINITY ? 0.0f : exp2f(s[i] - m_new);
     const float lsum = sum32(pv[i]);
     st.l[i] = st.l[i] * alpha + lsum;
     st.m[i] = m_new;
@@ -124,10 +116,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
   float* pp = kq + Dk * G;
   float* pz = pp + KVQ_GROUP * ngv * G;
 
-  // scaled queries of the G heads sharing this kv head
+  // scaled queries of the G heads sharing this kv head (log2-domain scores)
   for (int i = tid; i < G * Dk; i += kThreads) {
     const int qi = i / Dk, c = i - qi * Dk;
-    qs[i] = a.scale * load_q<QDT>(a.q, (int64_t(b) * a.L.Hq + int64_t(h) * G + qi) * Dk + c);
+    qs[i] = a.scale * kLog2e * load_q<QDT>(a.q, (int64_t(b) * a.L.Hq + int64_t(h) * G + qi) * Dk + c);
   }
 
   SoftmaxState<G> st;
@@ -142,8 +134,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
 
   const int t = lane & 31, hf = lane >> 5;
   const int kw = Dk * kb / 32, kper = 32 / kb;
-  const int vw = Dv * vb / 32;
-  const int vper_log = vb == 2 ? 4 : (vb == 4 ? 3 : 2);  // log2(32 / vb)
   const uint32_t kmask = (1u << kb) - 1u, vmask = (1u << vb) - 1u;
 
   // ------------------------------------------------------------ quantized groups
@@ -194,11 +184,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
       softmax_update<G>(st, s, pv);
 
       // p_t s_t,g into LDS and the zero-point sums
-      const int64_t vrow = slab * Tq + int64_t(g) * KVQ_GROUP + t;
-      const uint16_t* vs = static_cast<const uint16_t*>(a.cache.v_scale) + vrow * ngv;
-      const uint16_t* vz = static_cast<const uint16_t*>(a.cache.v_zero) + vrow * ngv;
+      const int64_t vblk = (slab * nG + g) * ngv * KVQ_GROUP;
+      const uint16_t* vs = static_cast<const uint16_t*>(a.cache.v_scale) + vblk;
+      const uint16_t* vz = static_cast<const uint16_t*>(a.cache.v_zero) + vblk;
       for (int gc = 0; gc < ngv; ++gc) {
-        const float s_v = h2f(vs[gc]), z_v = h2f(vz[gc]);
+        const float s_v = h2f(vs[gc * KVQ_GROUP + t]), z_v = h2f(vz[gc * KVQ_GROUP + t]);
 #pragma unroll
         for (int i = 0; i < G; ++i) {
           if (hf == 0) pp[(t * ngv + gc) * G + i] = pv[i] * s_v;
@@ -210,16 +200,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     __syncthreads();
 
     if (active) {
-      // values: lane owns channels c = lane + 64 j
-      const uint32_t* vc = static_cast<const uint32_t*>(a.cache.v_codes) + (slab * Tq + int64_t(g) * KVQ_GROUP) * vw;
+      // values: lane owns channels c = lane + 64 j; code of token tt, channel c is
+      // field (octet tt/8, channel c), bits [(tt%8)*vb, (tt%8)*vb + vb)
+      const uint8_t* vc = static_cast<const uint8_t*>(a.cache.v_codes) + (slab * nG + g) * (4 * Dv * vb);
       for (int tt = 0; tt < KVQ_GROUP; ++tt) {
-        const uint32_t* row = vc + tt * vw;
+        const uint8_t* oct = vc + (tt >> 3) * Dv * vb;
+        const int bit = (tt & 7) * vb;
 #pragma unroll
         for (int j = 0; j < kMaxVChansPerLane; ++j) {
           const int c = lane + 64 * j;
           if (c < Dv) {
-            const uint32_t word = row[c >> vper_log];
-            const float cf = float((word >> ((c & ((1 << vper_log) - 1)) * vb)) & vmask);
+            const uint32_t byte = oct[c * vb + (bit >> 3)];
+            const float cf = float((byte >> (bit & 7)) & vmask);
             const float* ppt = pp + (tt * ngv + c / KVQ_GROUP) * G;
 #pragma unroll
             for (int i = 0; i < G; ++i) st.o[i][j] = fmaf(ppt[i], cf, st.o[i][j]);
@@ -291,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
   }
 
   // ------------------------------------------------------------- merge the waves
-  // per wave: m[G], l[G], o[G][Dv]
+  // per wave: m[G], l[G], o[G][Dv]; the merged result goes to res [G][Dv + 2]
   const int mstride = G * (Dv + 2);
   float* mw = lds + G * Dk + wave * mstride;
   if (lane == 0) {
@@ -311,55 +303,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
   }
   __syncthreads();
   const float* m0 = lds + G * Dk;
+  float* res = lds + G * Dk + kWaves * mstride;
   for (int idx = tid; idx < G * Dv; idx += kThreads) {
     const int i = idx / Dv, c = idx - i * Dv;
     float M = -INFINITY;
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m0[w * mstride + i]);
     float Lsum = 0.0f, O = 0.0f;
     for (int w = 0; w < kWaves; ++w) {
-      const float mwv = m0[w * mstride + i];
-      const float e = mwv == -INFINITY ? 0.0f : __expf(mwv - M);
+      const float e = lse_weight(m0[w * mstride + i], M);
       Lsum += e * m0[w * mstride + G + i];
       O += e * m0[w * mstride + 2 * G + i * Dv + c];
     }
-    const int64_t qh = int64_t(b) * a.L.Hq + int64_t(h) * G + i;
-    if (P == 1) {
-      a.out[qh * Dv + c] = O / Lsum;
-    } else {
-      float* ws = a.workspace + (qh * P + p) * (Dv + 2);
-      if (c == 0) {
-        ws[0] = M;
-        ws[1] = Lsum;
-      }
-      ws[2 + c] = O;
+    res[i * (Dv + 2) + 2 + c] = O;
+    if (c == 0) {
+      res[i * (Dv + 2)] = M;
+      res[i * (Dv + 2) + 1] = Lsum;
     }
   }
-}
-
-// out[b, i, :] = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p over the partitions
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws, float* __restrict__ out,
-                                                    int P, int Dv) {
-  const int64_t qh = blockIdx.x;
-  const float* base = ws + qh * P * (Dv + 2);
-  float M = -INFINITY;
-  for (int p = 0; p < P; ++p) M = fmaxf(M, base[p * (Dv + 2)]);
-  for (int c = threadIdx.x; c < Dv; c += blockDim.x) {
-    float L = 0.0f, O = 0.0f;
-    for (int p = 0; p < P; ++p) {
-      const float* e = base + p * (Dv + 2);
-      const float w = e[0] == -INFINITY ? 0.0f : __expf(e[0] - M);
-      L += w * e[1];
-      O += w * e[2 + c];
-    }
-    out[qh * Dv + c] = O / L;
-  }
+  __syncthreads();
+  finish_partition(a, G, b, h, p, res, reinterpret_cast<int*>(res + G * (Dv + 2)));
 }
 
 template <int G, int QDT>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int Dk = a.L.Dk, Dv = a.L.Dv;
   const int loop_floats = G * Dk + kWaves * wave_lds_floats<G>(Dk, Dv);
-  const int merge_floats = G * Dk + kWaves * G * (Dv + 2);
+  const int merge_floats = G * Dk + (kWaves + 1) * G * (Dv + 2) + 4;
   const size_t lds = size_t(loop_floats > merge_floats ? loop_floats : merge_floats) * sizeof(float);
   const dim3 grid(unsigned(a.P), unsigned(a.L.Hkv), unsigned(a.L.B));
   if (lds > 64 * 1024) {
@@ -369,10 +338,6 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((decode_kernel<G, QDT>), grid, dim3(kThreads), lds, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.P == 1) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(a.L.B * a.L.Hq)), dim3(256), 0, stream,
-                     a.workspace, a.out, a.P, Dv);
   return hipGetLastError();
 }
 
@@ -391,6 +356,8 @@ hipError_t launch_q(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  const hipError_t e = launch_decode_mfma(a, stream);
+  if (e != hipErrorNotSupported) return e;
   switch (a.q_dtype) {
     case KVQ_F32: return launch_q<KVQ_F32>(a, stream);
     case KVQ_F16: return launch_q<KVQ_F16>(a, stream);

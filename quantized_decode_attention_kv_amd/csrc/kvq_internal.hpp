@@ -27,9 +27,19 @@ struct DecodeArgs {
   kvq_cache cache;
   float scale;
   int P;
-  float* workspace;  // [B, Hq, P, Dv + 2] when P > 1
-  float* out;        // [B, Hq, Dv]
+  uint32_t* counters;  // [B * Hkv] arrival counters, zero between calls (P > 1)
+  float* partials;     // [B * Hq, P, Dv + 2]: m (log2 domain), l, unnormalised o (P > 1)
+  float* out;          // [B, Hq, Dv]
 };
+
+// Workspace of kv_decode_attn: arrival counters first (padded to 256 bytes), then
+// the per-partition partial results.
+inline size_t ws_counter_bytes(const kvq_layout& L) {
+  return ((size_t(L.B) * size_t(L.Hkv) * 4 + 255) / 256) * 256;
+}
+inline size_t ws_partial_bytes(const kvq_layout& L, int P) {
+  return size_t(L.B) * size_t(L.Hq) * size_t(P) * size_t(L.Dv + 2) * sizeof(float);
+}
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
         const float mx = group32_max(x);
         const QParams q = make_qparams(mn, mx, v_levels);
         if ((c & (KVQ_GROUP - 1)) == 0) {
-          const int64_t so = (slab * a.L.Tq + g * KVQ_GROUP + t) * ngv + c / KVQ_GROUP;
+          const int64_t so = ((slab * a.L.n_groups + g) * ngv + c / KVQ_GROUP) * KVQ_GROUP + t;
           static_cast<uint16_t*>(a.cache.v_scale)[so] = q.s_bits;
           static_cast<uint16_t*>(a.cache.v_zero)[so] = q.z_bits;
         }
@@ -163,14 +163,18 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
       }
     }
     {
-      const int vb = a.L.v_bits, per = 32 / vb, vw = Dv * vb / 32;
-      uint32_t* dst = static_cast<uint32_t*>(a.cache.v_codes) + (slab * a.L.Tq + g * KVQ_GROUP) * vw;
-      for (int i = tid; i < KVQ_GROUP * vw; i += kPackThreads) {
-        const int t = i / vw, w = i - t * vw;
-        const uint8_t* src = &vcodes_s[t * Dv + w * per];
-        uint32_t word = 0;
-        for (int k = 0; k < per; ++k) word |= uint32_t(src[k]) << (k * vb);
-        dst[i] = word;
+      // values: per 8-token octet o and channel c one little-endian field of 8*vb
+      // bits, token 8o+k at bits [k*vb, k*vb+vb)
+      const int vb = a.L.v_bits;
+      uint8_t* dst = static_cast<uint8_t*>(a.cache.v_codes) + (slab * a.L.n_groups + g) * (4 * Dv * vb);
+      for (int i = tid; i < 4 * Dv; i += kPackThreads) {
+        const int o = i / Dv, c = i - o * Dv;
+        uint64_t field = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) field |= uint64_t(vcodes_s[(8 * o + k) * Dv + c]) << (k * vb);
+        if (vb == 2) reinterpret_cast<uint16_t*>(dst)[i] = uint16_t(field);
+        else if (vb == 4) reinterpret_cast<uint32_t*>(dst)[i] = uint32_t(field);
+        else reinterpret_cast<uint64_t*>(dst)[i] = field;
       }
     }
   } else {

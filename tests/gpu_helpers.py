@@ -4,18 +4,9 @@ packed buffers back.  No arithmetic of the method lives here."""
 import numpy as np
 import torch
 
-from workloads import make_all, make_queries
+from workloads.device import to_device, upload_workload  # noqa: F401
 
 MAX_ABS_ERR = 2e-3   # decode output bound against the oracle's float64 attention
-
-
-def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
-    """Storage-dtype numpy array -> torch tensor on the GPU (bf16 travels as bit patterns)."""
-    if dtype == "f32":
-        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
-    raise ValueError(dtype)
 
 
 def cache_to_numpy(cache) -> dict:
@@ -23,7 +14,8 @@ def cache_to_numpy(cache) -> dict:
     out = {}
     for k, t in cache.items():
         a = t.cpu().numpy()
-        out[k] = a.view(np.uint32) if a.dtype == np.int32 else a.view(np.uint16)
+        out[k] = {np.dtype(np.int32): np.uint32, np.dtype(np.float16): np.uint16}.get(a.dtype, None)
+        out[k] = a.view(out[k]) if out[k] is not None else a
     return out
 
 
@@ -33,26 +25,8 @@ def cache_from_numpy(packed: dict, device="cuda") -> dict:
     for k, a in packed.items():
         if a.dtype == np.uint32:
             out[k] = torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(device)
+        elif a.dtype == np.uint8:
+            out[k] = torch.from_numpy(np.ascontiguousarray(a)).to(device)
         else:
             out[k] = torch.from_numpy(np.ascontiguousarray(a).view(np.float16)).to(device)
     return out
-
-
-def upload_workload(w, t_lo=0, t_hi=None, device="cuda"):
-    """Draw every slab of K/V positions [t_lo, t_hi) and upload slab by slab (bounded
-    host memory), plus the queries.  Returns (K, V, q) device tensors."""
-    if t_hi is None:
-        t_hi = w.T
-    n = t_hi - t_lo
-    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
-    K = torch.empty((w.B, w.Hkv, n, w.Dk), dtype=tdt, device=device)
-    V = torch.empty((w.B, w.Hkv, n, w.Dv), dtype=tdt, device=device)
-
-    def sink(b, h, s):
-        K[b, h].copy_(to_device(s.K, w.dtype, "cpu"))
-        V[b, h].copy_(to_device(s.V, w.dtype, "cpu"))
-
-    make_all(w, t_lo, t_hi, sink=sink)
-    torch.cuda.synchronize()
-    q = to_device(make_queries(w), w.dtype, device)
-    return K, V, q

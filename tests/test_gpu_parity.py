@@ -199,3 +199,27 @@ def test_long_128k_full_size_and_prefill_chunk():
     torch.cuda.synchronize()
     for k in cache:
         assert torch.equal(before[k], cache[k]), k
+
+
+def test_workspace_reuse_and_counter_reset():
+    """One zeroed workspace serves consecutive calls: each call leaves the arrival
+    counters at zero, repeated calls give bit-identical output (the merge always
+    combines partitions in index order), and a smaller partition count reuses it."""
+    w = small_cases()[0]
+    K, V = make_all(w, workers=4)
+    q = make_queries(w)
+    lay = api.Layout.from_workload(w)
+    cache = api.kv_quant_pack(lay, to_device(K, w.dtype), to_device(V, w.dtype))
+    qd = to_device(q, w.dtype)
+    ws = api.alloc_workspace(lay, 7)
+    scale = float(O.default_scale(w.Dk))
+    want = O.decode_all(q, O.pack_all(K, V, w), w, scale)
+    outs = []
+    for P in (7, 7, 3, 7):
+        out = api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:256].view(torch.int32).abs().sum()) == 0, P
+        err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
+        assert err <= MAX_ABS_ERR, (P, err)
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[3])

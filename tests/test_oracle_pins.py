@@ -105,10 +105,27 @@ def test_quantizer_more_bits_less_error():
 # -------------------------------------------------------------------- packing pins
 
 def test_pack_hand_examples():
-    for case in load_golden("pack_hand_examples.json")["cases"]:
+    g = load_golden("pack_hand_examples.json")
+    for case in g["cases"]:
         w = O.pack_codes(np.array(case["codes"], dtype=np.uint8), case["bits"])
         assert w.tolist() == case["words"], case["why"]
         assert O.unpack_codes(w, case["bits"]).tolist() == case["codes"]
+    for case in g["octet_cases"]:
+        f = O.pack_octets(np.array(case["codes"], dtype=np.uint8), case["bits"])
+        assert f.tolist() == case["bytes"], case["why"]
+        assert O.unpack_octets(f, case["bits"]).tolist() == case["codes"]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_octet_roundtrip(bits):
+    rng = np.random.default_rng(20 + bits)
+    c = rng.integers(0, 2 ** bits, size=(3, 5, 8), dtype=np.uint8)
+    f = O.pack_octets(c, bits)
+    assert f.shape == (3, 5, bits) and f.dtype == np.uint8
+    assert np.array_equal(O.unpack_octets(f, bits), c)
+    # token k of the octet at bits [k*bits, k*bits+bits) of the little-endian field
+    field = int.from_bytes(bytes(f[1, 2].tolist()), "little")
+    assert all((field >> (k * bits)) & (2 ** bits - 1) == c[1, 2, k] for k in range(8))
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
@@ -284,6 +301,7 @@ def test_decode_matches_explicit_dequant_loops():
     kb, vb = w.k_bits, w.v_bits
     f16 = lambda a: a.view(np.float16).astype(np.float64)
     ks, kz, vs, vz = f16(p["k_scale"]), f16(p["k_zero"]), f16(p["v_scale"]), f16(p["v_zero"])
+    assert p["v_codes"].shape == (p["k_codes"].shape[0] // 32, 4, w.Dv, vb)
     rows_k, rows_v = [], []
     for t in range(p["k_codes"].shape[0]):
         kr = []
@@ -292,10 +310,11 @@ def test_decode_matches_explicit_dequant_loops():
             code = (word >> ((c % (32 // kb)) * kb)) & (2 ** kb - 1)
             kr.append(code * ks[t // 32, c] + kz[t // 32, c])
         vr = []
+        g, o, k = t // 32, (t % 32) // 8, t % 8
         for c in range(w.Dv):
-            word = int(p["v_codes"][t, c * vb // 32])
-            code = (word >> ((c % (32 // vb)) * vb)) & (2 ** vb - 1)
-            vr.append(code * vs[t, c // 32] + vz[t, c // 32])
+            field = int.from_bytes(bytes(p["v_codes"][g, o, c].tolist()), "little")
+            code = (field >> (k * vb)) & (2 ** vb - 1)
+            vr.append(code * vs[g, c // 32, t % 32] + vz[g, c // 32, t % 32])
         rows_k.append(kr)
         rows_v.append(vr)
     rows_k += f16(p["k_fp16"]).tolist()
