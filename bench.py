@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak, 8 TB/s
 METRIC = "quantized-KV decode attn: effective HBM GB/s (% of peak) + decode steps/sec"
-DECODE_SRC = os.path.join(ROOT, "quantized_decode_attention_kv_amd", "csrc", "kvq_decode.hip")
+CSRC = os.path.join(ROOT, "quantized_decode_attention_kv_amd", "csrc")
+DECODE_SRCS = [os.path.join(CSRC, f) for f in ("kvq_decode_mfma.hip", "kvq_decode_common.hpp", "kvq_decode_generic.hip", "kvq_decode_merge.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_long_128k_hbm_traffic.txt")
 
 
@@ -59,8 +60,12 @@ def pack_bytes(w, n_tokens, n_quant):
 
 
 def kernel_source_hash():
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the decode kernel sources, to tell whether stored counter data is current."""
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -188,7 +193,7 @@ def main():
         Kc = Kd[:, :, t0:].contiguous()
         Vc = Vd[:, :, t0:].contiguous()
     del Kd, Vd
-    ws = torch.zeros(max(1, lay.workspace_bytes(P)), dtype=torch.uint8, device=dev)
+    ws = api.alloc_workspace(lay, P, dev)
     out = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.float32, device=dev)
     scale = 1.0 / (w.Dk ** 0.5)
     torch.cuda.synchronize()
@@ -263,7 +268,7 @@ def main():
                   "algorithmic_bytes": pb} if chunk else None),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "decode_kernel (kv_decode_attn)",
+                     "traffic": traffic, "kernel": "decode_mfma_kernel (kv_decode_attn)",
                      "kernel_source_sha256_16": kernel_source_hash()},
     }
     if not args.no_cpu_baseline:

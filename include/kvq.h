@@ -34,11 +34,15 @@
  *            w*(32/k_bits)+k at bits [k*k_bits, (k+1)*k_bits), little-endian
  *   k_scale  fp16   [B, Hkv, n_groups, Dk]
  *   k_zero   fp16   [B, Hkv, n_groups, Dk]
- *   v_codes  uint8  [B, Hkv, n_groups, 4, Dv, v_bits]  values are stored channel
- *            by channel inside each key group, in four 8-token octets: the v_bits
- *            bytes of (group g, octet o, channel c) form one little-endian field
- *            of 8*v_bits bits whose bits [k*v_bits, (k+1)*v_bits) hold the code of
- *            compacted token 32g + 8o + k
+ *   v_codes  uint32 [B, Hkv, n_groups, Dv*v_bits]  the codes of one key group
+ *            form a little-endian bit stream (bit i is bit i%32 of word i/32).
+ *            With vb = v_bits, TPW = 16/vb, F = Dv*vb/8, the code of compacted
+ *            token 32g + 8o + j (0 <= j < 8) and channel c = 16t + n (0 <= n < 16)
+ *            sits at bit
+ *              ((16o + n)*4 + j%4)*F + (t/TPW)*32 + (j/4)*r*vb + (t%TPW)*vb,
+ *            r = min(TPW, Dv/16 - (t/TPW)*TPW).  When Dv*vb is a multiple of 256
+ *            each 32-bit word holds, for one (o, n, j%4), the codes of TPW tiles
+ *            of token j%4 in its low half and of token j%4 + 4 in its high half.
  *   v_scale  fp16   [B, Hkv, n_groups, Dv/32, 32]  one per token and 32-channel
  *            group; the 32 tokens of a group are contiguous
  *   v_zero   fp16   [B, Hkv, n_groups, Dv/32, 32]
@@ -116,9 +120,8 @@ int kvq_retained_positions(const kvq_layout* L, int32_t* out, int32_t capacity);
 int64_t kvq_quantized_before(const kvq_layout* L, int64_t t);
 
 /* Workspace kv_decode_attn needs for num_partitions sequence partitions (0 when
- * num_partitions == 1): B*Hkv 32-bit arrival counters padded to a multiple of 256
- * bytes, then B*Hq*num_partitions*(Dv+2) floats of partial results.  Returns 0 for
- * an invalid layout. */
+ * num_partitions == 1): B*Hq*num_partitions*(Dv+4) floats of partial results.
+ * Returns 0 for an invalid layout. */
 size_t kvq_decode_workspace_bytes(const kvq_layout* L, int num_partitions);
 
 /*
@@ -141,22 +144,20 @@ int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count,
                   const kvq_cache* cache, void* stream);
 
 /*
- * kv_decode_attn — single-token decode attention over a packed cache (one kernel
- * launch; partitions are merged by the last workgroup of each (batch, kv head) to
- * finish).
+ * kv_decode_attn — single-token decode attention over a packed cache: one decode
+ * kernel over (partition, kv head, batch row) workgroups and, when P > 1, one merge
+ * kernel after it on the same stream.
  *   q:   [B, Hq, Dk] device array of dtype q_dtype; query head i reads KV head
  *        i / (Hq / Hkv) (grouped-query attention: the Hq/Hkv queries of one KV head
  *        share each read of its cache).
  *   softmax_scale: scale of the scores (finite; pass 1/sqrtf(Dk) for the usual one).
  *   num_partitions: P sequence partitions processed in parallel (split-K); partition
- *        p takes key groups [p*n_groups/P, (p+1)*n_groups/P) and retained tokens
- *        [p*R/P, (p+1)*R/P) (integer division).  1 <= P <= max(1, ceil(T/32)).
+ *        p takes key groups [p*n_groups/P, (p+1)*n_groups/P) (integer division)
+ *        and a share of the retained tokens.  1 <= P <= max(1, ceil(T/32)).
  *   workspace / workspace_bytes: at least kvq_decode_workspace_bytes(L, P) bytes of
- *        device memory (may be NULL when P == 1).  Its leading arrival counters
- *        must be zero before the first call that uses it (allocate it zeroed);
- *        every call leaves them zero again, the rest needs no initialisation.  A
- *        workspace serves one call at a time: calls that overlap on the GPU
- *        (different streams) need separate workspaces.
+ *        16-byte aligned device memory (may be NULL when P == 1); no
+ *        initialisation needed.  A workspace serves one call at a time: calls that
+ *        overlap on the GPU (different streams) need separate workspaces.
  *   out: [B, Hq, Dv] float32 device array.
  * Partial results of the partitions are merged on the device.
  */

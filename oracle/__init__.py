@@ -10,13 +10,14 @@ from .kvq_oracle import (  # noqa: F401
     dequant_slab,
     pack_all,
     pack_codes,
-    pack_octets,
     pack_slab,
+    pack_value_codes,
     quantize_groups,
     retained_mask,
     slab_of,
     split_positions,
     unpack_codes,
-    unpack_octets,
+    unpack_value_codes,
+    value_bit_position,
     upcast,
 )

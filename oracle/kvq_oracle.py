@@ -35,10 +35,15 @@ Canonical packed layout for one (b, kv-head) slab (the same index formulas appea
 * k_codes  u32 [Tq, Dk*kb/32]: word w of row t holds channel w*(32/kb)+k at bits
   [k*kb, k*kb+kb), little-endian (keys stored token by token);
 * k_scale, k_zero fp16 [Tq/32, Dk]  (one pair per token group and channel);
-* v_codes  u8 [Tq/32, 4, Dv, vb]: values stored channel by channel inside each
-  32-token group, in four 8-token octets: the vb bytes of (group g, octet o,
-  channel c) are one little-endian field of 8*vb bits holding the code of token
-  32g+8o+k at bits [k*vb, k*vb+vb);
+* v_codes  u32 [Tq/32, Dv*vb]: each 32-token group's value codes form one
+  little-endian bit stream (bit i of the stream is bit i%32 of word i/32); the
+  code of token 8o+j of the group (octet o, j < 8) and channel c = 16t+n (tile t,
+  column n < 16) sits at bit
+      ((16o + n)*4 + j%4)*F + chunk*32 + (j//4)*r*vb + (t%TPW)*vb,
+  with TPW = 16/vb tiles per chunk, chunk = t//TPW, r = min(TPW, Dv/16 - chunk*TPW)
+  tiles in that chunk and F = Dv*vb/8 bits per (o, n, j%4) field: one field pairs
+  tokens j and j+4 of an octet, the first of them in the low half of every chunk
+  (library format choice, see ``value_bit_position``);
 * v_scale, v_zero fp16 [Tq/32, Dv/32, 32]  (one pair per token and 32-channel
   group, the 32 tokens of a group contiguous);
 * k_fp16 [R, Dk], v_fp16 [R, Dv] fp16 rows of the retained positions, ascending.
@@ -148,22 +153,50 @@ def unpack_codes(words: np.ndarray, bits: int) -> np.ndarray:
     return c.reshape(c.shape[:-2] + (c.shape[-2] * per,)).astype(np.uint8)
 
 
-def pack_octets(codes: np.ndarray, bits: int) -> np.ndarray:
-    """codes [..., 8] -> uint8 [..., bits]: the little-endian field of 8*bits bits with
-    code k at bits [k*bits, k*bits+bits)."""
+def value_bit_position(tau, c, Dv: int, bits: int):
+    """Bit offset, inside its group's value bit stream, of the code of token tau
+    (0..31 within the group) and channel c (library format choice; documented in the
+    module header).  Works elementwise on integer arrays."""
+    tau = np.asarray(tau, dtype=np.int64)
+    c = np.asarray(c, dtype=np.int64)
+    n_tiles = Dv // 16
+    per_chunk = 16 // bits                     # tiles whose codes share one chunk
+    field = Dv * bits // 8                     # bits per (octet, column, token pair)
+    octet, j = tau // 8, tau % 8
+    pair, upper = j % 4, j // 4
+    col, tile = c % 16, c // 16
+    chunk, slot = tile // per_chunk, tile % per_chunk
+    in_chunk = np.minimum(per_chunk, n_tiles - chunk * per_chunk)
+    return (((octet * 16 + col) * 4 + pair) * field + chunk * 2 * per_chunk * bits
+            + upper * in_chunk * bits + slot * bits)
+
+
+def pack_value_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes [..., 32, Dv] (token, channel of one group) -> uint32 [..., Dv*bits]."""
     c = np.asarray(codes, dtype=np.uint64)
-    shifts = np.arange(8, dtype=np.uint64) * np.uint64(bits)
-    field = np.bitwise_or.reduce(c << shifts, axis=-1)                # < 2^(8*bits) <= 2^64
-    by = (field[..., None] >> (np.arange(bits, dtype=np.uint64) * np.uint64(8))) & np.uint64(0xFF)
-    return by.astype(np.uint8)
+    Dv = c.shape[-1]
+    if c.shape[-2] != GROUP or Dv % GROUP:
+        raise ValueError("value codes must be [..., 32, Dv] with Dv a multiple of 32")
+    tau, ch = np.meshgrid(np.arange(GROUP), np.arange(Dv), indexing="ij")
+    pos = value_bit_position(tau, ch, Dv, bits).reshape(-1)
+    assert np.unique(pos).size == pos.size and pos.max() < GROUP * Dv * bits
+    lead = c.shape[:-2]
+    flat = c.reshape((-1, GROUP * Dv))
+    words = np.zeros((flat.shape[0], Dv * bits), dtype=np.uint64)
+    for row in range(flat.shape[0]):
+        # disjoint fields: adding each code at its position is the same as OR-ing it in
+        np.add.at(words[row], pos // 32, flat[row] << (pos % 32).astype(np.uint64))
+    return words.astype(np.uint32).reshape(lead + (Dv * bits,))
 
 
-def unpack_octets(fields: np.ndarray, bits: int) -> np.ndarray:
-    """Inverse of pack_octets: uint8 [..., bits] -> codes uint8 [..., 8]."""
-    by = np.asarray(fields, dtype=np.uint64)
-    field = np.bitwise_or.reduce(by << (np.arange(bits, dtype=np.uint64) * np.uint64(8)), axis=-1)
-    c = (field[..., None] >> (np.arange(8, dtype=np.uint64) * np.uint64(bits))) & np.uint64(2 ** bits - 1)
-    return c.astype(np.uint8)
+def unpack_value_codes(words: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of pack_value_codes: uint32 [..., Dv*bits] -> codes uint8 [..., 32, Dv]."""
+    w = np.asarray(words, dtype=np.uint64)
+    Dv = w.shape[-1] // bits
+    tau, ch = np.meshgrid(np.arange(GROUP), np.arange(Dv), indexing="ij")
+    pos = value_bit_position(tau, ch, Dv, bits)
+    codes = (w[..., pos // 32] >> (pos % 32).astype(np.uint64)) & np.uint64(2 ** bits - 1)
+    return codes.astype(np.uint8)
 
 
 def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_window: int):
@@ -192,8 +225,7 @@ def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_win
     # values: one (s, z) per token and 32-channel group
     Vg = V32[u].reshape(Tq, Dv // GROUP, GROUP)
     vc, vs, vz = quantize_groups(Vg, v_bits)                          # [Tq, Dv/32, 32], [Tq, Dv/32]
-    # storage order: group, octet, channel, 8 tokens of the octet
-    vc = vc.reshape(nG, 4, 8, Dv).transpose(0, 1, 3, 2)              # [nG, 4, Dv, 8]
+    vc = vc.reshape(nG, GROUP, Dv)                                     # [nG, 32 tokens, Dv]
     vs = vs.reshape(nG, GROUP, Dv // GROUP).transpose(0, 2, 1)       # [nG, Dv/32, 32]
     vz = vz.reshape(nG, GROUP, Dv // GROUP).transpose(0, 2, 1)
 
@@ -201,7 +233,7 @@ def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_win
         "k_codes": pack_codes(kc, k_bits),
         "k_scale": ks.view(np.uint16),
         "k_zero": kz.view(np.uint16),
-        "v_codes": pack_octets(vc, v_bits),
+        "v_codes": pack_value_codes(vc, v_bits),
         "v_scale": np.ascontiguousarray(vs).view(np.uint16),
         "v_zero": np.ascontiguousarray(vz).view(np.uint16),
         "k_fp16": K32[r].astype(np.float16).view(np.uint16),
@@ -237,9 +269,9 @@ def dequant_slab(p, k_bits: int, v_bits: int):
     kz = p["k_zero"].view(np.float16).astype(np.float64)
     g = np.arange(Tq) // GROUP
     Khat_q = kc * ks[g] + kz[g]
-    vc = unpack_octets(p["v_codes"], v_bits)                         # [nG, 4, Dv, 8]
-    nG, _, Dv, _ = vc.shape
-    vc = vc.transpose(0, 1, 3, 2).reshape(Tq, Dv).astype(np.float64)  # token 32g + 8o + k
+    vc = unpack_value_codes(p["v_codes"], v_bits)                    # [nG, 32, Dv]
+    nG, _, Dv = vc.shape
+    vc = vc.reshape(Tq, Dv).astype(np.float64)                       # token 32g + t
     vs = p["v_scale"].view(np.float16).astype(np.float64).transpose(0, 2, 1).reshape(Tq, Dv // GROUP)
     vz = p["v_zero"].view(np.float16).astype(np.float64).transpose(0, 2, 1).reshape(Tq, Dv // GROUP)
     Vhat_q = vc * np.repeat(vs, GROUP, axis=1) + np.repeat(vz, GROUP, axis=1)

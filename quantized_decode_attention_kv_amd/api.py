@@ -55,14 +55,13 @@ class Layout:
         return int(L_.load().kvq_decode_workspace_bytes(self.ref, num_partitions))
 
     def shapes(self):
-        """Tensor shape and dtype of each cache buffer (key codes as int32 bit patterns,
-        value codes as bytes)."""
+        """Tensor shape and dtype of each cache buffer (codes as int32 bit patterns)."""
         B, H, Tq, nG, R = self.B, self.Hkv, self.Tq, self.n_groups, self.R
         return {
             "k_codes": ((B, H, Tq, self.Dk * self.k_bits // 32), torch.int32),
             "k_scale": ((B, H, nG, self.Dk), torch.float16),
             "k_zero": ((B, H, nG, self.Dk), torch.float16),
-            "v_codes": ((B, H, nG, 4, self.Dv, self.v_bits), torch.uint8),
+            "v_codes": ((B, H, nG, self.Dv * self.v_bits), torch.int32),
             "v_scale": ((B, H, nG, self.Dv // 32, 32), torch.float16),
             "v_zero": ((B, H, nG, self.Dv // 32, 32), torch.float16),
             "k_fp16": ((B, H, R, self.Dk), torch.float16),
@@ -71,10 +70,9 @@ class Layout:
 
 
 def alloc_workspace(layout: Layout, num_partitions: int, device="cuda"):
-    """Decode workspace for num_partitions partitions, zero-initialised as the library
-    requires (its arrival counters start at zero and every call leaves them zero)."""
+    """Decode workspace for num_partitions partitions (needs no initialisation)."""
     need = layout.workspace_bytes(num_partitions)
-    return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
+    return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
 
 
 def alloc_cache(layout: Layout, device="cuda"):

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["kvq_api.cpp", "kvq_pack.hip", "kvq_decode_generic.hip", "kvq_decode_mfma.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_pack.hip", "kvq_decode_generic.hip", "kvq_decode_mfma.hip", "kvq_decode_merge.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-x", "hip",
@@ -26,6 +26,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # the quantizer contract needs the correctly rounded fp32 divide
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # matrix-core results stay in ordinary VGPRs: the decode loop scales its
+    # accumulators on the VALU, which would otherwise copy them out of AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]
 

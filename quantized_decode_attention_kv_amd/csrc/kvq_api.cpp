@@ -147,7 +147,7 @@ int64_t kvq_quantized_before(const kvq_layout* L, int64_t t) {
 size_t kvq_decode_workspace_bytes(const kvq_layout* L, int num_partitions) {
   if (check_layout(L) != KVQ_OK || num_partitions < 1) return 0;
   if (num_partitions == 1) return 0;
-  return kvq::ws_counter_bytes(*L) + kvq::ws_partial_bytes(*L, num_partitions);
+  return kvq::ws_partial_bytes(*L, num_partitions);
 }
 
 int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count, const void* K, const void* V,
@@ -233,8 +233,7 @@ int kv_decode_attn(const kvq_layout* L, const void* q, int q_dtype, const kvq_ca
   a.scale = softmax_scale;
   a.P = num_partitions;
   if (need > 0) {
-    a.counters = static_cast<uint32_t*>(workspace);
-    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + kvq::ws_counter_bytes(*L));
+    a.partials = static_cast<float*>(workspace);
   }
   a.out = out;
   const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));

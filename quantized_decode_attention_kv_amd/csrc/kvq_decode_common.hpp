@@ -59,13 +59,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Finish one workgroup's (batch b, kv head h, partition p) result for its G query
-// heads.  res: LDS [G][Dv + 2] = (m, l, o[Dv]); flag: one int of LDS.
-// P == 1: write out = o / l.  P > 1: publish the partial; the last workgroup of the
-// (b, h) pair to arrive merges all P partials (one wave per query head, lanes over
-// channels) and resets the pair's counter to zero for the next call.  All
-// kDecodeThreads threads must call this.
-__device__ inline void finish_partition(const DecodeArgs& a, int G, int b, int h, int p, const float* res,
-                                        int* flag) {
+// heads.  res: LDS [G][Dv + 2] = (m, l, o[Dv]).  P == 1: write out = o / l.
+// P > 1: write the partial row (m, l, two unused floats, o[Dv]; o 16-byte
+// aligned) for merge_partitions_kernel, launched after this kernel on the same
+// stream, to combine.  Plain stores: the kernel boundary makes them visible, so no
+// workgroup needs a device-wide fence (each one would write back and invalidate
+// the L2 of its XCD).
+__device__ inline void finish_partition(const DecodeArgs& a, int G, int b, int h, int p, const float* res) {
   const int tid = threadIdx.x, Dv = a.L.Dv, P = a.P;
   const int64_t qh0 = int64_t(b) * a.L.Hq + int64_t(h) * G;
   if (P == 1) {
@@ -75,49 +75,12 @@ __device__ inline void finish_partition(const DecodeArgs& a, int G, int b, int h
     }
     return;
   }
-  for (int idx = tid; idx < G * (Dv + 2); idx += kDecodeThreads) {
-    const int i = idx / (Dv + 2), e = idx - i * (Dv + 2);
-    a.partials[((qh0 + i) * P + p) * (Dv + 2) + e] = res[idx];
+  const int PS = Dv + 4;
+  for (int idx = tid; idx < G * PS; idx += kDecodeThreads) {
+    const int i = idx / PS, e = idx - i * PS;
+    const float v = e < 2 ? res[i * (Dv + 2) + e] : (e < 4 ? 0.0f : res[i * (Dv + 2) + e - 2]);
+    a.partials[((qh0 + i) * P + p) * PS + e] = v;
   }
-  __threadfence();  // make this partial visible device-wide before counting it
-  __syncthreads();
-  const int64_t slab = int64_t(b) * a.L.Hkv + h;
-  if (tid == 0) *flag = atomicAdd(a.counters + slab, 1u) == unsigned(P - 1);
-  __syncthreads();
-  if (!*flag) return;
-  __threadfence();  // acquire: the other partitions' partials are visible now
-
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int i = wave; i < G; i += kDecodeWaves) {
-    const float* base = a.partials + (qh0 + i) * P * (Dv + 2);
-    float M = -INFINITY;
-    for (int pp = lane; pp < P; pp += 64) M = fmaxf(M, base[pp * (Dv + 2)]);
-    M = wave_max(M);
-    float L = 0.0f;
-    for (int pp = lane; pp < P; pp += 64) L += lse_weight(base[pp * (Dv + 2)], M) * base[pp * (Dv + 2) + 1];
-    L = wave_sum(L);
-    float O[KVQ_MAX_HEAD_DIM / 64] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int p0 = 0; p0 < P; p0 += 64) {
-      const int mine = p0 + lane;
-      const float wl = mine < P ? lse_weight(base[mine * (Dv + 2)], M) : 0.0f;
-      const int cnt = P - p0 < 64 ? P - p0 : 64;
-      for (int k = 0; k < cnt; ++k) {
-        const float w = __shfl(wl, k, 64);
-        const float* src = base + (p0 + k) * (Dv + 2) + 2;
-#pragma unroll
-        for (int j = 0; j < KVQ_MAX_HEAD_DIM / 64; ++j) {
-          const int c = lane + 64 * j;
-          if (c < Dv) O[j] += w * src[c];
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < KVQ_MAX_HEAD_DIM / 64; ++j) {
-      const int c = lane + 64 * j;
-      if (c < Dv) a.out[(qh0 + i) * Dv + c] = O[j] / L;
-    }
-  }
-  if (tid == 0) a.counters[slab] = 0u;
 }
 
 }  // namespace kvq

@@ -16,7 +16,7 @@
 // read from HBM once per decode step.  Within the workgroup each wave owns every
 // 4th key group of the partition and keeps its own online-softmax state (running
 // max m, running sum l, unnormalised output o); waves are merged through LDS at the
-// end, partitions by the last workgroup to finish (finish_partition).
+// end, partitions by the merge kernel that follows (kvq_decode_merge.hip).
 //
 // Dequantization is folded into the dot products so no dequantized tile is ever
 // materialised:
@@ -29,12 +29,14 @@
 
 #include "kvq_decode_common.hpp"
 #include "kvq_internal.hpp"
+#include "kvq_vlayout.hpp"
 
 namespace kvq {
 
 // MFMA kernel launcher (kvq_decode_mfma.hip); returns hipErrorNotSupported for
 // shapes it does not take.
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
 
 namespace {
 
@@ -200,18 +202,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     __syncthreads();
 
     if (active) {
-      // values: lane owns channels c = lane + 64 j; code of token tt, channel c is
-      // field (octet tt/8, channel c), bits [(tt%8)*vb, (tt%8)*vb + vb)
-      const uint8_t* vc = static_cast<const uint8_t*>(a.cache.v_codes) + (slab * nG + g) * (4 * Dv * vb);
+      // values: lane owns channels c = lane + 64 j; codes read from the group's
+      // bit stream (layout in kvq_vlayout.hpp)
+      const uint32_t* vc = static_cast<const uint32_t*>(a.cache.v_codes) + (slab * nG + g) * (Dv * vb);
       for (int tt = 0; tt < KVQ_GROUP; ++tt) {
-        const uint8_t* oct = vc + (tt >> 3) * Dv * vb;
-        const int bit = (tt & 7) * vb;
 #pragma unroll
         for (int j = 0; j < kMaxVChansPerLane; ++j) {
           const int c = lane + 64 * j;
           if (c < Dv) {
-            const uint32_t byte = oct[c * vb + (bit >> 3)];
-            const float cf = float((byte >> (bit & 7)) & vmask);
+            const int bit = value_bit_position(tt, c, Dv, vb);
+            const float cf = float((vc[bit >> 5] >> (bit & 31)) & vmask);
             const float* ppt = pp + (tt * ngv + c / KVQ_GROUP) * G;
 #pragma unroll
             for (int i = 0; i < G; ++i) st.o[i][j] = fmaf(ppt[i], cf, st.o[i][j]);
@@ -321,14 +321,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     }
   }
   __syncthreads();
-  finish_partition(a, G, b, h, p, res, reinterpret_cast<int*>(res + G * (Dv + 2)));
+  finish_partition(a, G, b, h, p, res);
 }
 
 template <int G, int QDT>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int Dk = a.L.Dk, Dv = a.L.Dv;
   const int loop_floats = G * Dk + kWaves * wave_lds_floats<G>(Dk, Dv);
-  const int merge_floats = G * Dk + (kWaves + 1) * G * (Dv + 2) + 4;
+  const int merge_floats = G * Dk + (kWaves + 1) * G * (Dv + 2);
   const size_t lds = size_t(loop_floats > merge_floats ? loop_floats : merge_floats) * sizeof(float);
   const dim3 grid(unsigned(a.P), unsigned(a.L.Hkv), unsigned(a.L.B));
   if (lds > 64 * 1024) {
@@ -356,14 +356,17 @@ hipError_t launch_q(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  const hipError_t e = launch_decode_mfma(a, stream);
-  if (e != hipErrorNotSupported) return e;
-  switch (a.q_dtype) {
-    case KVQ_F32: return launch_q<KVQ_F32>(a, stream);
-    case KVQ_F16: return launch_q<KVQ_F16>(a, stream);
-    case KVQ_BF16: return launch_q<KVQ_BF16>(a, stream);
-    default: return hipErrorInvalidValue;
+  hipError_t e = launch_decode_mfma(a, stream);
+  if (e == hipErrorNotSupported) {
+    switch (a.q_dtype) {
+      case KVQ_F32: e = launch_q<KVQ_F32>(a, stream); break;
+      case KVQ_F16: e = launch_q<KVQ_F16>(a, stream); break;
+      case KVQ_BF16: e = launch_q<KVQ_BF16>(a, stream); break;
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (e != hipSuccess || a.P == 1) return e;
+  return launch_merge(a, stream);
 }
 
 }  // namespace kvq

@@ -27,21 +27,18 @@ struct DecodeArgs {
   kvq_cache cache;
   float scale;
   int P;
-  uint32_t* counters;  // [B * Hkv] arrival counters, zero between calls (P > 1)
-  float* partials;     // [B * Hq, P, Dv + 2]: m (log2 domain), l, unnormalised o (P > 1)
+  float* partials;     // [B * Hq, P, Dv + 4]: m (log2 domain), l, 2 unused, unnormalised o (P > 1)
   float* out;          // [B, Hq, Dv]
 };
 
-// Workspace of kv_decode_attn: arrival counters first (padded to 256 bytes), then
-// the per-partition partial results.
-inline size_t ws_counter_bytes(const kvq_layout& L) {
-  return ((size_t(L.B) * size_t(L.Hkv) * 4 + 255) / 256) * 256;
-}
+// Workspace of kv_decode_attn: the per-partition partial results.
 inline size_t ws_partial_bytes(const kvq_layout& L, int P) {
-  return size_t(L.B) * size_t(L.Hq) * size_t(P) * size_t(L.Dv + 2) * sizeof(float);
+  return size_t(L.B) * size_t(L.Hq) * size_t(P) * size_t(L.Dv + 4) * sizeof(float);
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
+// Decode kernel (matrix-core kernel where it applies, else the generic one)
+// followed, when P > 1, by the partition merge.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace kvq

@@ -11,8 +11,8 @@
 // (batch, kv-head) slab: its 32 token rows of K and V are read once, coalesced
 // along channels; per-channel key min/max is a register reduction over the 32
 // tokens a thread holds, per-token value min/max is a 32-lane shuffle reduction;
-// codes are staged in LDS and packed into little-endian 32-bit words by
-// consecutive threads, so every global store is a coalesced run.  The remaining
+// codes are staged in LDS and packed into 32-bit words by consecutive threads, so
+// every global store is a coalesced run.  The remaining
 // blocks copy the chunk's retained rows to fp16.
 //
 // The quantize arithmetic is kept in the exact float32 order of the contract in
@@ -23,6 +23,7 @@
 
 #include "kvq_internal.hpp"
 #include "kvq_retention.hpp"
+#include "kvq_vlayout.hpp"
 
 #pragma clang fp contract(off)
 
@@ -163,18 +164,17 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
       }
     }
     {
-      // values: per 8-token octet o and channel c one little-endian field of 8*vb
-      // bits, token 8o+k at bits [k*vb, k*vb+vb)
-      const int vb = a.L.v_bits;
-      uint8_t* dst = static_cast<uint8_t*>(a.cache.v_codes) + (slab * a.L.n_groups + g) * (4 * Dv * vb);
-      for (int i = tid; i < 4 * Dv; i += kPackThreads) {
-        const int o = i / Dv, c = i - o * Dv;
-        uint64_t field = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) field |= uint64_t(vcodes_s[(8 * o + k) * Dv + c]) << (k * vb);
-        if (vb == 2) reinterpret_cast<uint16_t*>(dst)[i] = uint16_t(field);
-        else if (vb == 4) reinterpret_cast<uint32_t*>(dst)[i] = uint32_t(field);
-        else reinterpret_cast<uint64_t*>(dst)[i] = field;
+      // values: the group's bit stream of Dv*vb words (layout in kvq_vlayout.hpp);
+      // thread i assembles word i from the 32/vb codes it holds
+      const int vb = a.L.v_bits, per = 32 / vb, nw = Dv * vb;
+      uint32_t* dst = static_cast<uint32_t*>(a.cache.v_codes) + (slab * a.L.n_groups + g) * nw;
+      for (int i = tid; i < nw; i += kPackThreads) {
+        uint32_t word = 0;
+        for (int k = 0; k < per; ++k) {
+          const ValueCodeSpot sp = value_code_at(32 * i + k * vb, Dv, vb);
+          word |= uint32_t(vcodes_s[sp.tau * Dv + sp.c]) << (k * vb);
+        }
+        dst[i] = word;
       }
     }
   } else {

@@ -201,10 +201,10 @@ def test_long_128k_full_size_and_prefill_chunk():
         assert torch.equal(before[k], cache[k]), k
 
 
-def test_workspace_reuse_and_counter_reset():
-    """One zeroed workspace serves consecutive calls: each call leaves the arrival
-    counters at zero, repeated calls give bit-identical output (the merge always
-    combines partitions in index order), and a smaller partition count reuses it."""
+def test_workspace_reuse_needs_no_initialisation():
+    """One workspace serves consecutive calls whatever it holds on entry (it is
+    filled with garbage first): repeated calls give bit-identical output (the merge
+    combines partitions in a fixed order), and a smaller partition count reuses it."""
     w = small_cases()[0]
     K, V = make_all(w, workers=4)
     q = make_queries(w)
@@ -212,13 +212,13 @@ def test_workspace_reuse_and_counter_reset():
     cache = api.kv_quant_pack(lay, to_device(K, w.dtype), to_device(V, w.dtype))
     qd = to_device(q, w.dtype)
     ws = api.alloc_workspace(lay, 7)
+    ws.fill_(0xA5)
     scale = float(O.default_scale(w.Dk))
     want = O.decode_all(q, O.pack_all(K, V, w), w, scale)
     outs = []
     for P in (7, 7, 3, 7):
         out = api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, workspace=ws)
         torch.cuda.synchronize()
-        assert int(ws[:256].view(torch.int32).abs().sum()) == 0, P
         err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
         assert err <= MAX_ABS_ERR, (P, err)
         outs.append(out.cpu())

@@ -110,22 +110,37 @@ def test_pack_hand_examples():
         w = O.pack_codes(np.array(case["codes"], dtype=np.uint8), case["bits"])
         assert w.tolist() == case["words"], case["why"]
         assert O.unpack_codes(w, case["bits"]).tolist() == case["codes"]
-    for case in g["octet_cases"]:
-        f = O.pack_octets(np.array(case["codes"], dtype=np.uint8), case["bits"])
-        assert f.tolist() == case["bytes"], case["why"]
-        assert O.unpack_octets(f, case["bits"]).tolist() == case["codes"]
+    for case in g["value_cases"]:
+        codes = np.zeros((32, case["Dv"]), dtype=np.uint8)
+        for tau, c, code in case["codes"]:
+            codes[tau, c] = code
+        words = O.pack_value_codes(codes, case["bits"])
+        assert words.shape == (case["Dv"] * case["bits"],) and words.dtype == np.uint32
+        want = np.zeros_like(words)
+        for idx, val in case["words"].items():
+            want[int(idx)] = val
+        assert words.tolist() == want.tolist(), case["why"]
+        assert np.array_equal(O.unpack_value_codes(words, case["bits"]), codes)
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
-def test_octet_roundtrip(bits):
-    rng = np.random.default_rng(20 + bits)
-    c = rng.integers(0, 2 ** bits, size=(3, 5, 8), dtype=np.uint8)
-    f = O.pack_octets(c, bits)
-    assert f.shape == (3, 5, bits) and f.dtype == np.uint8
-    assert np.array_equal(O.unpack_octets(f, bits), c)
-    # token k of the octet at bits [k*bits, k*bits+bits) of the little-endian field
-    field = int.from_bytes(bytes(f[1, 2].tolist()), "little")
-    assert all((field >> (k * bits)) & (2 ** bits - 1) == c[1, 2, k] for k in range(8))
+@pytest.mark.parametrize("Dv", [32, 64, 96, 128, 256])
+def test_value_code_roundtrip(bits, Dv):
+    rng = np.random.default_rng(20 + bits + Dv)
+    c = rng.integers(0, 2 ** bits, size=(3, 32, Dv), dtype=np.uint8)
+    words = O.pack_value_codes(c, bits)
+    assert words.shape == (3, Dv * bits) and words.dtype == np.uint32
+    assert np.array_equal(O.unpack_value_codes(words, bits), c)
+    # every bit of the stream carries exactly one code bit: all-ones codes fill it
+    full = O.pack_value_codes(np.full((32, Dv), 2 ** bits - 1, dtype=np.uint8), bits)
+    assert np.all(full == np.uint32(0xFFFFFFFF))
+    # a code never straddles a word, and each code of a token pair lands in the
+    # same chunk half as its partner token's code of the same channel
+    pos = O.value_bit_position(np.arange(32)[:, None], np.arange(Dv)[None, :], Dv, bits)
+    assert np.all(pos % 32 + bits <= 32)
+    if Dv * bits % 256 == 0:
+        low, high = pos[[0, 1, 2, 3, 8, 9]], pos[[4, 5, 6, 7, 12, 13]]
+        assert np.all(high - low == 16)
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
@@ -301,7 +316,7 @@ def test_decode_matches_explicit_dequant_loops():
     kb, vb = w.k_bits, w.v_bits
     f16 = lambda a: a.view(np.float16).astype(np.float64)
     ks, kz, vs, vz = f16(p["k_scale"]), f16(p["k_zero"]), f16(p["v_scale"]), f16(p["v_zero"])
-    assert p["v_codes"].shape == (p["k_codes"].shape[0] // 32, 4, w.Dv, vb)
+    assert p["v_codes"].shape == (p["k_codes"].shape[0] // 32, w.Dv * vb)
     rows_k, rows_v = [], []
     for t in range(p["k_codes"].shape[0]):
         kr = []
@@ -310,10 +325,17 @@ def test_decode_matches_explicit_dequant_loops():
             code = (word >> ((c % (32 // kb)) * kb)) & (2 ** kb - 1)
             kr.append(code * ks[t // 32, c] + kz[t // 32, c])
         vr = []
-        g, o, k = t // 32, (t % 32) // 8, t % 8
+        g, o, j = t // 32, (t % 32) // 8, t % 8
+        stream = sum(int(x) << (32 * i) for i, x in enumerate(p["v_codes"][g]))
+        F = w.Dv * vb // 8
         for c in range(w.Dv):
-            field = int.from_bytes(bytes(p["v_codes"][g, o, c].tolist()), "little")
-            code = (field >> (k * vb)) & (2 ** vb - 1)
+            # tile t, column n; one chunk holds 16/vb tiles, pairs tokens j and j+4
+            tile, col = c // 16, c % 16
+            per = 16 // vb
+            chunk, slot = tile // per, tile % per
+            r = min(per, w.Dv // 16 - chunk * per)
+            bit = ((16 * o + col) * 4 + j % 4) * F + chunk * 32 + (j // 4) * r * vb + slot * vb
+            code = (stream >> bit) & (2 ** vb - 1)
             vr.append(code * vs[g, c // 32, t % 32] + vz[g, c // 32, t % 32])
         rows_k.append(kr)
         rows_v.append(vr)
