@@ -7,17 +7,26 @@
 // channels, separate key / value bit widths (Quantize What Counts, methodology).
 // Retained positions (LogQuant section 2) are copied to fp16 rows.
 //
-// One launch per call.  Blocks [0, n_groups_chunk) each own one key group of one
-// (batch, kv-head) slab: its 32 token rows of K and V are read once, coalesced
-// along channels; per-channel key min/max is a register reduction over the 32
-// tokens a thread holds, per-token value min/max is a 32-lane shuffle reduction;
-// codes are staged in LDS and packed into 32-bit words by consecutive threads, so
-// every global store is a coalesced run.  The remaining
-// blocks copy the chunk's retained rows to fp16.
+// One launch per call.  Workgroups [0, n_groups_chunk) each own one key group of
+// one (batch, kv-head) slab; the remaining workgroups copy the chunk's retained
+// rows to fp16.  In a group workgroup, wave w holds tokens 8w..8w+7 and lane l the
+// channel pair (2l, 2l+1) (and 2l+128, 2l+129 for heads wider than 128), so every
+// global load is a coalesced row segment:
+//   keys    per-channel min / max over the wave's 8 tokens in registers, across
+//           the 4 waves through LDS;
+//   values  per-(token, 32-channel group) min / max with a DPP reduction inside
+//           each 16-lane row: a row of lanes holds exactly one channel group;
+//   codes   OR-ed into LDS words at their final bit positions, then stored as one
+//           contiguous run per group.
 //
-// The quantize arithmetic is kept in the exact float32 order of the contract in
-// kvq.h (correctly rounded division, no contraction) so codes and fp16 bits are
-// reproducible bit for bit.
+// The codes follow the quantizer contract of kvq.h bit for bit: code =
+// clamp(rint(fl(x - z) / s)) with the correctly rounded division.  The division is
+// replaced by a multiply with fl(1/s): the two quotients differ by at most
+// 3 * 2^-24 * |t| (< 5e-5 while |t| <= 256; a larger |t| clamps the same way), so
+// rint gives the same integer unless the quotient lies within 2^-12 of a
+// half-integer; such elements (about one in two thousand) take the exact division.
+// Scale and zero use the exact division, with contraction off, as the contract
+// spells out.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -31,7 +40,9 @@ namespace kvq {
 namespace {
 
 constexpr int kPackThreads = 256;
+constexpr int kPackWaves = kPackThreads / 64;
 constexpr int kRetRowsPerBlock = 4;
+constexpr int kMaxPairBlocks = KVQ_MAX_HEAD_DIM / 128;  // 64-lane blocks of channel pairs
 
 template <int DT>
 __device__ __forceinline__ float load_elem(const void* p, int64_t i);
@@ -48,6 +59,22 @@ __device__ __forceinline__ float load_elem<KVQ_BF16>(const void* p, int64_t i) {
   return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
 }
 
+// elements i, i + 1 (i even) as fp32
+template <int DT>
+__device__ __forceinline__ float2 load_pair(const void* p, int64_t i) {
+  if constexpr (DT == KVQ_F32) {
+    return *reinterpret_cast<const float2*>(static_cast<const float*>(p) + i);
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + i);
+    if constexpr (DT == KVQ_BF16) {
+      return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
+    } else {
+      return make_float2(__half2float(__ushort_as_half(uint16_t(w & 0xFFFFu))),
+                         __half2float(__ushort_as_half(uint16_t(w >> 16))));
+    }
+  }
+}
+
 __device__ __forceinline__ uint16_t f16_bits_rne(float x) {
   return __half_as_ushort(__float2half_rn(x));
 }
@@ -56,7 +83,7 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
 }
 
 struct QParams {
-  float s, z;
+  float s, z, r;  // scale and zero (their fp16 values) and fl(1/s) (0 when s == 0)
   uint16_t s_bits, z_bits;
 };
 
@@ -73,35 +100,44 @@ __device__ __forceinline__ QParams make_qparams(float mn, float mx, float levels
   q.z_bits = zb;
   q.s = f16_bits_to_f32(sb);
   q.z = f16_bits_to_f32(zb);
+  q.r = q.s == 0.0f ? 0.0f : 1.0f / q.s;
   return q;
 }
 
-__device__ __forceinline__ uint32_t quant_code(float x, const QParams& q, float levels) {
-  if (q.s == 0.0f) return 0u;
-  const float t = (x - q.z) / q.s;
-  float r = __builtin_rintf(t);
-  r = fminf(fmaxf(r, 0.0f), levels);
-  return uint32_t(r);
+// code = 0 if s == 0 else clamp(rint(fl(x - z) / s), 0, levels) (see the header)
+__device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float r, float levels) {
+  const float u = x - z;
+  float t = u * r;  // s == 0: r == 0, t == 0, code 0
+  float rt = __builtin_rintf(t);
+  if (__builtin_expect(fabsf(t - rt) > 0.5f - 1.0f / 4096.0f, 0)) {
+    t = u / s;
+    rt = __builtin_rintf(t);
+  }
+  rt = fminf(fmaxf(rt, 0.0f), levels);
+  return uint32_t(rt);
 }
 
-__device__ __forceinline__ float group32_min(float v) {
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, 32));
-  return v;
-}
-__device__ __forceinline__ float group32_max(float v) {
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 32));
+// min / max over the 16 lanes of a DPP row (every lane gets the result)
+template <bool MAX>
+__device__ __forceinline__ float row16_reduce(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));  // row_mirror
   return v;
 }
 
-template <int DT>
+template <int DT, int KB, int VB>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
   __shared__ int32_t row_s[KVQ_GROUP];
-  __shared__ uint8_t kcodes_s[KVQ_GROUP * KVQ_MAX_HEAD_DIM];
-  __shared__ uint8_t vcodes_s[KVQ_GROUP * KVQ_MAX_HEAD_DIM];
+  __shared__ float kmn_s[kPackWaves][KVQ_MAX_HEAD_DIM], kmx_s[kPackWaves][KVQ_MAX_HEAD_DIM];
+  __shared__ float ks_s[KVQ_MAX_HEAD_DIM], kz_s[KVQ_MAX_HEAD_DIM], kr_s[KVQ_MAX_HEAD_DIM];
+  __shared__ uint32_t kw_s[KVQ_GROUP * KVQ_MAX_HEAD_DIM * KB / 32];  // key code words of the group
+  __shared__ uint32_t vw_s[KVQ_MAX_HEAD_DIM * VB];                   // value code stream of the group
+  __shared__ uint16_t vs_s[KVQ_MAX_HEAD_DIM / KVQ_GROUP][KVQ_GROUP], vz_s[KVQ_MAX_HEAD_DIM / KVQ_GROUP][KVQ_GROUP];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b = blockIdx.z;
   const int Dk = a.L.Dk, Dv = a.L.Dv;
   const int64_t slab = int64_t(b) * a.L.Hkv + h;
@@ -110,72 +146,113 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
   if (int64_t(blockIdx.x) < a.n_groups_chunk) {
     // ------------------------------------------------ one key group of 32 tokens
     const int64_t g = a.g_begin + blockIdx.x;
+    const int kwords = Dk * KB / 32, vwords = Dv * VB;
     if (tid < KVQ_GROUP) row_s[tid] = int32_t(quantized_position(rr, g * KVQ_GROUP + tid) - a.t_begin);
+    for (int i = tid; i < KVQ_GROUP * kwords; i += kPackThreads) kw_s[i] = 0u;
+    for (int i = tid; i < vwords; i += kPackThreads) vw_s[i] = 0u;
     __syncthreads();
 
-    // keys: thread c owns channel c of all 32 rows
-    const float k_levels = float((1 << a.L.k_bits) - 1);
-    for (int c = tid; c < Dk; c += kPackThreads) {
-      float x[KVQ_GROUP];
-      float mn = 0.0f, mx = 0.0f;
+    // keys: lane holds channels (2cp, 2cp+1) of the wave's 8 tokens
+    constexpr float k_levels = float((1 << KB) - 1);
+    float2 kx[kMaxPairBlocks][8];
 #pragma unroll
-      for (int t = 0; t < KVQ_GROUP; ++t) {
-        x[t] = load_elem<DT>(a.K, (slab * a.t_count + row_s[t]) * Dk + c);
-        mn = t == 0 ? x[t] : fminf(mn, x[t]);
-        mx = t == 0 ? x[t] : fmaxf(mx, x[t]);
+    for (int k = 0; k < kMaxPairBlocks; ++k) {
+      const int cp = lane + 64 * k;
+      if (2 * cp < Dk) {
+        float2 mn = make_float2(0.0f, 0.0f), mx = mn;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          kx[k][t] = load_pair<DT>(a.K, (slab * a.t_count + row_s[8 * wave + t]) * Dk + 2 * cp);
+          mn = t == 0 ? kx[k][t] : make_float2(fminf(mn.x, kx[k][t].x), fminf(mn.y, kx[k][t].y));
+          mx = t == 0 ? kx[k][t] : make_float2(fmaxf(mx.x, kx[k][t].x), fmaxf(mx.y, kx[k][t].y));
+        }
+        kmn_s[wave][2 * cp] = mn.x;
+        kmn_s[wave][2 * cp + 1] = mn.y;
+        kmx_s[wave][2 * cp] = mx.x;
+        kmx_s[wave][2 * cp + 1] = mx.y;
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < Dk; c += kPackThreads) {
+      float mn = kmn_s[0][c], mx = kmx_s[0][c];
+#pragma unroll
+      for (int w = 1; w < kPackWaves; ++w) {
+        mn = fminf(mn, kmn_s[w][c]);
+        mx = fmaxf(mx, kmx_s[w][c]);
       }
       const QParams q = make_qparams(mn, mx, k_levels);
       const int64_t so = (slab * a.L.n_groups + g) * Dk + c;
       static_cast<uint16_t*>(a.cache.k_scale)[so] = q.s_bits;
       static_cast<uint16_t*>(a.cache.k_zero)[so] = q.z_bits;
+      ks_s[c] = q.s;
+      kz_s[c] = q.z;
+      kr_s[c] = q.r;
+    }
+    __syncthreads();
+    {
+      // key words: row t, word c / (32/KB), channel c at bit (c % (32/KB)) * KB;
+      // the lane's two channels are adjacent fields of one word
+      constexpr int per = 32 / KB;
 #pragma unroll
-      for (int t = 0; t < KVQ_GROUP; ++t) kcodes_s[t * Dk + c] = uint8_t(quant_code(x[t], q, k_levels));
+      for (int k = 0; k < kMaxPairBlocks; ++k) {
+        const int cp = lane + 64 * k;
+        if (2 * cp < Dk) {
+          const float s0 = ks_s[2 * cp], z0 = kz_s[2 * cp], r0 = kr_s[2 * cp];
+          const float s1 = ks_s[2 * cp + 1], z1 = kz_s[2 * cp + 1], r1 = kr_s[2 * cp + 1];
+          const int word = (2 * cp) / per, bit = ((2 * cp) % per) * KB;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const uint32_t c0 = quant_code(kx[k][t].x, s0, z0, r0, k_levels);
+            const uint32_t c1 = quant_code(kx[k][t].y, s1, z1, r1, k_levels);
+            atomicOr(&kw_s[(8 * wave + t) * kwords + word], (c0 | (c1 << KB)) << bit);
+          }
+        }
+      }
     }
 
-    // values: thread c owns channel c; a 32-lane group owns one channel group
-    const float v_levels = float((1 << a.L.v_bits) - 1);
-    const int ngv = Dv / KVQ_GROUP;
-    for (int c = tid; c < Dv; c += kPackThreads) {
-      for (int t = 0; t < KVQ_GROUP; ++t) {
-        const float x = load_elem<DT>(a.V, (slab * a.t_count + row_s[t]) * Dv + c);
-        const float mn = group32_min(x);
-        const float mx = group32_max(x);
-        const QParams q = make_qparams(mn, mx, v_levels);
-        if ((c & (KVQ_GROUP - 1)) == 0) {
-          const int64_t so = ((slab * a.L.n_groups + g) * ngv + c / KVQ_GROUP) * KVQ_GROUP + t;
-          static_cast<uint16_t*>(a.cache.v_scale)[so] = q.s_bits;
-          static_cast<uint16_t*>(a.cache.v_zero)[so] = q.z_bits;
+    // values: per (token, 32-channel group); lanes 16r..16r+15 of a pair block
+    // hold one group
+    constexpr float v_levels = float((1 << VB) - 1);
+#pragma unroll
+    for (int k = 0; k < kMaxPairBlocks; ++k) {
+      const int cp = lane + 64 * k;
+      if (128 * k < Dv) {  // wave-uniform: the pair block reaches into the head
+        const bool on = 2 * cp < Dv;
+        const int gc = (2 * cp) / KVQ_GROUP;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int tok = 8 * wave + t;
+          const float2 x = on ? load_pair<DT>(a.V, (slab * a.t_count + row_s[tok]) * Dv + 2 * cp)
+                              : make_float2(0.0f, 0.0f);
+          const float mn = row16_reduce<false>(fminf(x.x, x.y));
+          const float mx = row16_reduce<true>(fmaxf(x.x, x.y));
+          if (on) {
+            const QParams q = make_qparams(mn, mx, v_levels);
+            if ((lane & 15) == 0) {
+              vs_s[gc][tok] = q.s_bits;
+              vz_s[gc][tok] = q.z_bits;
+            }
+            const uint32_t c0 = quant_code(x.x, q.s, q.z, q.r, v_levels);
+            const uint32_t c1 = quant_code(x.y, q.s, q.z, q.r, v_levels);
+            const int p0 = value_bit_position(tok, 2 * cp, Dv, VB), p1 = value_bit_position(tok, 2 * cp + 1, Dv, VB);
+            atomicOr(&vw_s[p0 >> 5], c0 << (p0 & 31));
+            atomicOr(&vw_s[p1 >> 5], c1 << (p1 & 31));
+          }
         }
-        vcodes_s[t * Dv + c] = uint8_t(quant_code(x, q, v_levels));
       }
     }
     __syncthreads();
 
-    // pack: word w of a row holds channels w*per .. w*per+per-1, code k at bits k*bits
-    {
-      const int kb = a.L.k_bits, per = 32 / kb, kw = Dk * kb / 32;
-      uint32_t* dst = static_cast<uint32_t*>(a.cache.k_codes) + (slab * a.L.Tq + g * KVQ_GROUP) * kw;
-      for (int i = tid; i < KVQ_GROUP * kw; i += kPackThreads) {
-        const int t = i / kw, w = i - t * kw;
-        const uint8_t* src = &kcodes_s[t * Dk + w * per];
-        uint32_t word = 0;
-        for (int k = 0; k < per; ++k) word |= uint32_t(src[k]) << (k * kb);
-        dst[i] = word;
-      }
-    }
-    {
-      // values: the group's bit stream of Dv*vb words (layout in kvq_vlayout.hpp);
-      // thread i assembles word i from the 32/vb codes it holds
-      const int vb = a.L.v_bits, per = 32 / vb, nw = Dv * vb;
-      uint32_t* dst = static_cast<uint32_t*>(a.cache.v_codes) + (slab * a.L.n_groups + g) * nw;
-      for (int i = tid; i < nw; i += kPackThreads) {
-        uint32_t word = 0;
-        for (int k = 0; k < per; ++k) {
-          const ValueCodeSpot sp = value_code_at(32 * i + k * vb, Dv, vb);
-          word |= uint32_t(vcodes_s[sp.tau * Dv + sp.c]) << (k * vb);
-        }
-        dst[i] = word;
-      }
+    // contiguous stores of the group's key words, value stream and value scale / zero
+    uint32_t* kdst = static_cast<uint32_t*>(a.cache.k_codes) + (slab * a.L.Tq + g * KVQ_GROUP) * kwords;
+    for (int i = tid; i < KVQ_GROUP * kwords; i += kPackThreads) kdst[i] = kw_s[i];
+    uint32_t* vdst = static_cast<uint32_t*>(a.cache.v_codes) + (slab * a.L.n_groups + g) * vwords;
+    for (int i = tid; i < vwords; i += kPackThreads) vdst[i] = vw_s[i];
+    const int ngv = Dv / KVQ_GROUP;
+    const int64_t vso = (slab * a.L.n_groups + g) * ngv * KVQ_GROUP;
+    for (int i = tid; i < ngv * KVQ_GROUP; i += kPackThreads) {
+      static_cast<uint16_t*>(a.cache.v_scale)[vso + i] = vs_s[i / KVQ_GROUP][i % KVQ_GROUP];
+      static_cast<uint16_t*>(a.cache.v_zero)[vso + i] = vz_s[i / KVQ_GROUP][i % KVQ_GROUP];
     }
   } else {
     // ------------------------------------------------ retained rows -> fp16
@@ -183,7 +260,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
     const int lt = tid % (kPackThreads / kRetRowsPerBlock);
     const int64_t j = (int64_t(blockIdx.x) - a.n_groups_chunk) * kRetRowsPerBlock + sub;
     if (j >= a.n_ret_chunk) return;
-    const int64_t r = a.r_begin + j;                       // rank among all retained rows
+    const int64_t r = a.r_begin + j;                           // rank among all retained rows
     const int64_t row = retained_position(rr, r) - a.t_begin;  // row in the chunk
     uint16_t* kd = static_cast<uint16_t*>(a.cache.k_fp16) + (slab * a.L.R + r) * Dk;
     uint16_t* vd = static_cast<uint16_t*>(a.cache.v_fp16) + (slab * a.L.R + r) * Dv;
@@ -194,6 +271,21 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
   }
 }
 
+template <int DT>
+hipError_t launch_dt(const PackArgs& a, dim3 grid, hipStream_t stream) {
+  const int kb = a.L.k_bits, vb = a.L.v_bits;
+#define KVQ_PACK_CASE(K_, V_)                                                                     \
+  if (kb == K_ && vb == V_) {                                                                     \
+    hipLaunchKernelGGL((pack_kernel<DT, K_, V_>), grid, dim3(kPackThreads), 0, stream, a);       \
+    return hipGetLastError();                                                                     \
+  }
+  KVQ_PACK_CASE(2, 2) KVQ_PACK_CASE(2, 4) KVQ_PACK_CASE(2, 8)
+  KVQ_PACK_CASE(4, 2) KVQ_PACK_CASE(4, 4) KVQ_PACK_CASE(4, 8)
+  KVQ_PACK_CASE(8, 2) KVQ_PACK_CASE(8, 4) KVQ_PACK_CASE(8, 8)
+#undef KVQ_PACK_CASE
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
@@ -201,12 +293,11 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
   if (nblk == 0) return hipSuccess;
   const dim3 grid(unsigned(nblk), unsigned(a.L.Hkv), unsigned(a.L.B));
   switch (a.dtype) {
-    case KVQ_F32: hipLaunchKernelGGL(pack_kernel<KVQ_F32>, grid, dim3(kPackThreads), 0, stream, a); break;
-    case KVQ_F16: hipLaunchKernelGGL(pack_kernel<KVQ_F16>, grid, dim3(kPackThreads), 0, stream, a); break;
-    case KVQ_BF16: hipLaunchKernelGGL(pack_kernel<KVQ_BF16>, grid, dim3(kPackThreads), 0, stream, a); break;
+    case KVQ_F32: return launch_dt<KVQ_F32>(a, grid, stream);
+    case KVQ_F16: return launch_dt<KVQ_F16>(a, grid, stream);
+    case KVQ_BF16: return launch_dt<KVQ_BF16>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace kvq

@@ -141,6 +141,39 @@ def test_constant_and_degenerate_groups():
     _compare_pack(cache_to_numpy(cache), O.pack_all(K, V, w))
 
 
+def test_pack_rounding_ties_and_near_ties():
+    """Quotients (x - z) / s exactly on a half-integer (round half to even) and one
+    float32 step either side of it, for every bit width and dtype: the codes must be
+    the contract's, which the kernel gets by multiplying with 1/s and falling back
+    to the exact division near a rounding boundary."""
+    for bits in (2, 4, 8):
+        for dtype in ("f32", "bf16"):
+            w = Workload("ties%d_%s" % (bits, dtype), B=1, Hq=4, Hkv=1, Dk=64, Dv=64, T=64, k_bits=bits,
+                         v_bits=bits, dtype=dtype, seed=42)
+            levels = 2 ** bits - 1
+            # s = 1, z = 0 for every group: min 0 and max = levels in each column / row
+            grid = np.arange(64, dtype=np.float32) % (levels + 1)
+            K = np.zeros((1, 1, 64, 64), dtype=np.float32)
+            V = np.zeros((1, 1, 64, 64), dtype=np.float32)
+            for t in range(64):
+                K[0, 0, t, :] = (grid + 0.5 * (t % 3 == 1)) % (levels + 0.5)
+                V[0, 0, t, :] = (grid + 0.5 * (t % 2)) % (levels + 0.5)
+            K[0, 0, 0, :], K[0, 0, 31, :], K[0, 0, 32, :], K[0, 0, 63, :] = 0.0, levels, 0.0, levels
+            V[0, 0, :, 0::32], V[0, 0, :, 31::32] = 0.0, levels
+            if dtype == "f32":
+                # one float32 step below / above a tie on a few elements
+                K[0, 0, 4, 1::4] = np.nextafter(K[0, 0, 4, 1::4], np.float32(-1))
+                V[0, 0, 5, 2::5] = np.nextafter(V[0, 0, 5, 2::5], np.float32(levels + 1))
+                Kin, Vin = K, V
+            else:
+                Kin = (K.view(np.uint32) >> 16).astype(np.uint16)
+                Vin = (V.view(np.uint32) >> 16).astype(np.uint16)
+            lay = api.Layout.from_workload(w)
+            cache = api.kv_quant_pack(lay, to_device(Kin, dtype), to_device(Vin, dtype))
+            torch.cuda.synchronize()
+            _compare_pack(cache_to_numpy(cache), O.pack_all(Kin, Vin, w), w.name + " ")
+
+
 # ------------------------------------------------------------------ full-size runs
 
 def _sample_slabs(w, n):
