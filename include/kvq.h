@@ -120,7 +120,8 @@ int kvq_retained_positions(const kvq_layout* L, int32_t* out, int32_t capacity);
 int64_t kvq_quantized_before(const kvq_layout* L, int64_t t);
 
 /* Workspace kv_decode_attn needs for num_partitions sequence partitions (0 when
- * num_partitions == 1): B*Hq*num_partitions*(Dv+4) floats of partial results.
+ * num_partitions == 1): B*Hq*4*num_partitions*(Dv+4) floats of partial results
+ * (the decode kernel may cut each partition into up to 4 work units).
  * Returns 0 for an invalid layout. */
 size_t kvq_decode_workspace_bytes(const kvq_layout* L, int num_partitions);
 
@@ -145,8 +146,9 @@ int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count,
 
 /*
  * kv_decode_attn — single-token decode attention over a packed cache: one decode
- * kernel over (partition, kv head, batch row) workgroups and, when P > 1, one merge
- * kernel after it on the same stream.
+ * kernel whose workgroups each take a contiguous run of key groups of one
+ * (batch row, kv head) pair (a partition, or a half or quarter of one) and, when
+ * P > 1, one merge kernel after it on the same stream.
  *   q:   [B, Hq, Dk] device array of dtype q_dtype; query head i reads KV head
  *        i / (Hq / Hkv) (grouped-query attention: the Hq/Hkv queries of one KV head
  *        share each read of its cache).

@@ -35,8 +35,8 @@ namespace kvq {
 
 // MFMA kernel launcher (kvq_decode_mfma.hip); returns hipErrorNotSupported for
 // shapes it does not take.
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream, int* parts);
+hipError_t launch_merge(const DecodeArgs& a, int parts, hipStream_t stream);
 
 namespace {
 
@@ -356,8 +356,10 @@ hipError_t launch_q(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  hipError_t e = launch_decode_mfma(a, stream);
+  int parts = a.P;  // partial rows per query head written by the decode kernel
+  hipError_t e = launch_decode_mfma(a, stream, &parts);
   if (e == hipErrorNotSupported) {
+    parts = a.P;
     switch (a.q_dtype) {
       case KVQ_F32: e = launch_q<KVQ_F32>(a, stream); break;
       case KVQ_F16: e = launch_q<KVQ_F16>(a, stream); break;
@@ -365,8 +367,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
       default: return hipErrorInvalidValue;
     }
   }
-  if (e != hipSuccess || a.P == 1) return e;
-  return launch_merge(a, stream);
+  if (e != hipSuccess || parts == 1) return e;
+  return launch_merge(a, parts, stream);
 }
 
 }  // namespace kvq

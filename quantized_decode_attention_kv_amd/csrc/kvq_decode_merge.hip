@@ -1,4 +1,4 @@
-// Partition merge of kv_decode_attn: combines the P partial results (m, l, o) of
+// Partition merge of kv_decode_attn: combines the partial results (m, l, o) of
 // every query head by log-sum-exp (see kvq_decode_common.hpp) into
 // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
 //
@@ -100,9 +100,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partitions_kernel(const f
 
 }  // namespace
 
-hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_merge(const DecodeArgs& a, int parts, hipStream_t stream) {
   const unsigned rows = unsigned(int64_t(a.L.B) * a.L.Hq);
-  hipLaunchKernelGGL(merge_partitions_kernel, dim3(rows), dim3(kMergeThreads), 0, stream, a.partials, a.P, a.L.Dv,
+  hipLaunchKernelGGL(merge_partitions_kernel, dim3(rows), dim3(kMergeThreads), 0, stream, a.partials, parts, a.L.Dv,
                      a.out);
   return hipGetLastError();
 }

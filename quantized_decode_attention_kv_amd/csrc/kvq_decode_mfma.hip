@@ -20,18 +20,24 @@
 // The folded operands q_c s_c and p_t s_t,g are split into fp16 hi + lo parts
 // (each rounded to nearest, about 22 significant bits together).
 //
-// One wave owns every fourth key group of the workgroup's partition and keeps one
-// group's loads in flight while it computes the previous one.  Per group:
+// Work units: one workgroup of one wave per contiguous run of key groups of one
+// (batch, kv head) slab; a split-K partition is one run or is cut into 2 or 4
+// (see decode_mfma_units).  Units share nothing and need no barriers: each stages
+// its groups through a two-slot LDS ring (buffer loads straight into LDS, so
+// groups j + 1 and j + 2 are in flight while group j is computed), keeps its own
+// online-softmax state and writes its own partial result.  A unit needs 10 KB of
+// LDS and at most 128 VGPRs for the common shapes, so 16 waves share a compute
+// unit.  Per group:
 //   1. Q' = q s (hi, lo) for 64 (query, 8-channel block) tasks, one per lane, into
 //      a wave-private LDS tile;
 //   2. scores S^T[token, column] = codes (A: 16 tokens x 32 channels) x Q' (B), two
-//      16-token tiles.  Column n holds query n%4, part (n/4)%2, so one DPP rotate
-//      adds the lo part to the hi part and every lane ends up with the scores of
-//      query n%4.  Tile rows are ordered so that lane group j holds tokens
+//      16-token tiles, with the hi and lo parts of Q' as two K steps of the same
+//      accumulator.  Column n holds query n%4, so every lane holds the scores of
+//      query n%4; tile rows are ordered so that lane group j holds tokens
 //      8j..8j+7;
-//   3. the key zero-point term sum_c q_c z_c comes from a 16-group batch MFMA
-//      (A = the zero points of 16 groups, B = q split hi/lo) done once per 16
-//      groups, read back from LDS;
+//   3. the key zero-point term sum_c q_c z_c: each Q' lane forms the partial sum
+//      of its block, and the 16 partial sums of a query are added across lanes
+//      (two row rotations, two half swaps) in fp32;
 //   4. online softmax in the log2 domain on the 8 scores of each lane; the running
 //      maximum of a query only moves (and the state is rescaled) when a score
 //      exceeds it by more than 2^kHeadroom, so most groups skip the rescale;
@@ -60,6 +66,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kG = 4;  // query heads per KV head handled here
 
+
 // log2 of the headroom a score may exceed its query's reference maximum by before
 // the state is rescaled: probabilities stay <= 2^kHeadroom, so p * s stays inside
 // fp16 while value scales are below 65504 / 2^kHeadroom.
@@ -74,12 +81,6 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                 0, 0);
 }
 
-// v plus the value of the lane four columns away inside its row of 16.  Columns
-// n and n^4 hold the two parts of the same query and the pattern repeats every 8
-// columns, so either rotation direction pairs them.
-__device__ __forceinline__ float add_ror4(float v) {
-  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
-}
 // Reinterpret a packed fp16 pair.  Takes its argument by value: clang's
 // __builtin_bit_cast applied directly to an element of an ext_vector_type lvalue
 // reads element 0 whatever the index.
@@ -88,6 +89,35 @@ __device__ __forceinline__ float readlane_f32(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------- LDS staging of loads
+// buffer_load ... lds: each active lane copies `bytes` (4 or 16) from
+// base + voffset + soffset to lds + lane * bytes, without passing through VGPRs.
+// The base sits in a buffer resource (scalar registers), the per-lane offset is
+// loop-invariant and the group offset is scalar, so staging a group costs no
+// vector instructions.  The wave counts the copy in vmcnt; the compiler does not
+// relate it to later LDS reads, so every read of staged data follows an
+// explicit wait_vmcnt.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+// raw buffer over [base, base + 2^31): 32-bit dword format (gfx9 family)
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(buf_rsrc r, uint32_t voffset, uint32_t soffset, void* lds) {
+  static_assert(BYTES == 4 || BYTES == 16, "copy size");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voffset, soffset, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voffset, soffset, 0, 0);
+}
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // ---------------------------------------------------------------- fp16 hi/lo split
 // v_fma_mix{lo,hi}_f16: fp32 fma of an fp32 and an fp16 (half H of a packed pair),
@@ -213,31 +243,54 @@ __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t (&w)[NB < 
   }
 }
 
-// LDS bytes of the kernel: [shared head][4 wave areas], reused for the epilogue
-template <int DK, int DV>
+// LDS of one workgroup (one wave), in bytes: 10 KB for the common shapes, so
+// that 16 waves fit on a compute unit.
+//   QB  Q' operand tile, KK chunks of 32 channels; holds the q hi/lo operand B2
+//       during set-up and the retained rows;
+//   PA  P' operand tile; shares the Q' tile when it fits there (within a group
+//       the Q' operand is consumed before P' is written, and P' before the next
+//       group's Q');
+//   ring of two staging slots, one key group each: key codes, value codes, key
+//       scales, value scales, value zeros, key zeros.  Slot 1 holds the scaled
+//       query during set-up and the retained-row probabilities before it is
+//       first filled; the ring holds the output accumulator and the value
+//       zero-point sums at the end.
+template <int DK, int DV, int KB, int VB>
 struct Lds {
   static constexpr int KK = DK / 32, NGV = DV / 32;
-  static constexpr int kQs = kG * DK * 4;      // scaled q, fp32 [4][DK]
-  static constexpr int kQexp = 16;             // [4] power-of-two query scalings
-  static constexpr int kB2 = KK * 32 * 16;     // q hi/lo operand tile
-  static constexpr int kShared = kQs + kQexp + kB2;
-  static constexpr int kQB = KK * 32 * 16;     // Q' operand tile
-  static constexpr int kPA = NGV * 32 * 16;    // P' operand tile
-  static constexpr int kBT = kG * 16 * 4;      // zero-point terms of 16 groups
-  static constexpr int kPT = kG * 32 * 4;      // retained-row probabilities
-  static constexpr int kWave = kQB + kPA + kBT + kPT;
-  static constexpr int kLoop = kShared + kDecodeWaves * kWave;
-  // epilogue: wave states [4][4][DV + 2], zero sums [4][4][NGV], res [4][DV + 2]
-  static constexpr int kSt = kDecodeWaves * kG * (DV + 2) * 4;
-  static constexpr int kZs = kDecodeWaves * kG * NGV * 4;
-  static constexpr int kRes = kG * (DV + 2) * 4;
-  static constexpr int kMerge = kShared + kSt + kZs + kRes;
-  static constexpr int kBytes = kLoop > kMerge ? kLoop : kMerge;
+  static constexpr int kQB = KK * 32 * 16;
+  static constexpr int kPA = NGV * 32 * 16;
+  static constexpr int kStK = 32 * DK * KB / 8;
+  static constexpr int kStV = 32 * DV * VB / 8;
+  static constexpr int kStS = 256;
+  static constexpr int kStage = kStK + kStV + 4 * kStS;
+  static constexpr bool kShare = kPA <= kQB;
+  static constexpr int oQB = 0, oPA = kShare ? 0 : kQB;
+  static constexpr int oRing = kShare ? kQB : kQB + kPA;
+  static constexpr int oLast = oRing + kStage;
+  static constexpr int kBytes = oRing + 2 * kStage;
+  static_assert(kG * DK * 4 <= kStage && kG * 32 * 4 <= kStage && kG * (DV + NGV) * 4 <= 2 * kStage, "aliases");
 };
 
+// max over the 64 lanes of a wave (DPP inside rows, then the four row results)
+__device__ __forceinline__ float wave_max_rows(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));  // row_mirror
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+// x[i] for a per-lane index i < 4 into a wave-uniform array (select chain)
+__device__ __forceinline__ float pick4(const float (&x)[kG], int i) {
+  return i == 0 ? x[0] : (i == 1 ? x[1] : (i == 2 ? x[2] : x[3]));
+}
+
+// One workgroup = one wave = one unit: a contiguous piece of a split-K partition
+// of one (batch, kv head) slab (the whole slab when P == 1).  Units are
+// independent: no barriers, and each writes its own partial result.
 template <int DK, int DV, int KB, int VB>
-__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(const DecodeArgs a) {
-  using LL = Lds<DK, DV>;
+__global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
+  using LL = Lds<DK, DV, KB, VB>;
   constexpr int KK = DK / 32;          // 32-channel score steps
   constexpr int NV = DV / 16;          // 16-channel value tiles
   constexpr int NGV = DV / 32;         // 32-channel value groups
@@ -248,81 +301,163 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(const Decod
   constexpr int KLB = KROW / 4;        // key-row bytes per lane (a quarter row)
   constexpr int KLW = KLB < 4 ? 1 : KLB / 4;
   constexpr uint32_t kVMask = ((1u << VB) - 1u) * 0x00010001u;
-  static_assert(DV == 128 && NV % TPW == 0 && KLB >= 2 && DK % 32 == 0 && DK <= 256, "shape");
+  static_assert(DV == 128 && NV % TPW == 0 && KLB >= 4 && DK % 32 == 0 && DK <= 128, "shape");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  float* qs_lds = reinterpret_cast<float*>(smem);                            // [4][DK]
-  float* qexp = reinterpret_cast<float*>(smem + LL::kQs);                    // [4]
-  u32x4* B2 = reinterpret_cast<u32x4*>(smem + LL::kQs + LL::kQexp);          // [KK*4][8]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, gq = lane >> 4;
-  unsigned char* wb = smem + LL::kShared + wave * LL::kWave;
-  u32x4* QB = reinterpret_cast<u32x4*>(wb);                                  // [KK*4][8]
-  u32x4* PA = reinterpret_cast<u32x4*>(wb + LL::kQB);                        // [NGV*4][8]
-  float* BT = reinterpret_cast<float*>(wb + LL::kQB + LL::kPA);              // [4][16]
-  float* PT = reinterpret_cast<float*>(wb + LL::kQB + LL::kPA + LL::kBT);    // [4][32]
+  u32x4* QB = reinterpret_cast<u32x4*>(smem + LL::oQB);       // [(KK+1)*4][8]
+  u32x4* PA = reinterpret_cast<u32x4*>(smem + LL::oPA);       // [NGV*4][8]
+  unsigned char* stage = smem + LL::oRing;                    // [2][kStage]
+  u32x4* B2 = QB;                                             // q hi/lo, set-up and retained rows
+  float* qs_lds = reinterpret_cast<float*>(smem + LL::oLast); // [4][DK], set-up only
+  float* PT = reinterpret_cast<float*>(smem + LL::oLast);     // [4][32], retained rows only
+  const int lane = threadIdx.x, n = lane & 15, gq = lane >> 4;
 
-  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int nG = a.L.n_groups, R = a.L.R, P = a.P;
+  const int unit = blockIdx.x, U = gridDim.x, h = blockIdx.y, b = blockIdx.z;
+  const int nG = a.L.n_groups, R = a.L.R;
   const int64_t slab = int64_t(b) * a.L.Hkv + h;
-  const int g0 = int(int64_t(p) * nG / P), g1 = int(int64_t(p + 1) * nG / P);
+  const int g0 = int(int64_t(unit) * nG / U), g1 = int(int64_t(unit + 1) * nG / U);
   const int nRT = (R + 31) / 32;  // 32-row tiles of retained rows
-  const int rt0 = int(int64_t(p) * nRT / P), rt1 = int(int64_t(p + 1) * nRT / P);
+  const int rt0 = int(int64_t(unit) * nRT / U), rt1 = int(int64_t(unit + 1) * nRT / U);
+  const int nj = g1 - g0;
+
+  // per-slab bases (wave-uniform)
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.cache.k_codes) + slab * int64_t(a.L.Tq) * KROW;
+  const uint16_t* ksbase = static_cast<const uint16_t*>(a.cache.k_scale) + slab * int64_t(nG) * DK;
+  const uint16_t* kzbase = static_cast<const uint16_t*>(a.cache.k_zero) + slab * int64_t(nG) * DK;
+  const uint32_t* vbase = static_cast<const uint32_t*>(a.cache.v_codes) + slab * int64_t(nG) * (DV * VB);
+  const uint16_t* vsbase = static_cast<const uint16_t*>(a.cache.v_scale) + slab * int64_t(nG) * DV;
+  const uint16_t* vzbase = static_cast<const uint16_t*>(a.cache.v_zero) + slab * int64_t(nG) * DV;
+
+  // Q' task of this lane: (block tb = 8-channel block kk_t of lane group gq_t,
+  // query i_t); it also forms the block's key zero-point partial sum
+  const int kk_t = lane >> 4, gq_t = (lane >> 2) & 3, i_t = lane & 3;
+  const bool qtask = kk_t < KK;
+  const int tb = gq_t * KK + (qtask ? kk_t : 0);
+  // score columns: query iq = n % 4; P' task: (query iq, channel group n / 4, octet gq)
+  const int iq = n & 3;
+  const int gcP = n >> 2;
+
+  // ------------------------------------------------- staging of key groups
+  // Every piece of a group is copied so that the lane that consumes it reads it
+  // back from the place of its own lane id (LDS reads contiguous across the wave):
+  //   key codes: per tile, KNP pieces of KPB bytes (the lane's quarter row);
+  //   value codes: VLW / 4 pieces of 16 bytes (the lane's words);
+  //   key scales and zeros: one 16-byte block per 8 channels (lanes < DK / 8);
+  //   value scales and zeros: one 16-byte (channel group, octet) chunk each
+  //   (lanes < 4 * NGV).
+  constexpr int KPB = KLB >= 16 ? 16 : 4;   // bytes per key piece
+  constexpr int KNP = KLB / KPB;            // key pieces per tile
+  constexpr int VNP = VLW / 4;              // value pieces
+  constexpr int kDmas = 2 * KNP + VNP + 4;  // copies per group
+  static_assert(kDmas < 64, "vmcnt");
+  static_assert(KLB % KPB == 0 && VLW % 4 == 0 && DK / 8 <= 64 && 4 * NGV <= 64, "staging");
+  // per-lane byte offsets inside a group (the group base itself is wave-uniform)
+  uint32_t koff[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) koff[tt] = uint32_t(8 * (n >> 2) + 4 * tt + (n & 3)) * KROW + gq * KLB;
+  const uint32_t voff = uint32_t(lane) * (VLW * 4);
+  const uint32_t koffs = uint32_t(lane) * 16;                          // key scales / zeros
+  const uint32_t coffs = uint32_t((lane >> 2) * 32 + 8 * (lane & 3)) * 2;  // value scales / zeros
+  const buf_rsrc rk = make_rsrc(kbase), rv = make_rsrc(vbase);
+  const buf_rsrc rks = make_rsrc(ksbase), rkz = make_rsrc(kzbase);
+  const buf_rsrc rvs = make_rsrc(vsbase), rvz = make_rsrc(vzbase);
+  auto stage_group = [&](int g, int slot) {
+    unsigned char* sb = stage + slot * LL::kStage;
+    const uint32_t gk = uint32_t(g) * (32 * KROW);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int hp = 0; hp < KNP; ++hp) lds_dma<KPB>(rk, koff[tt] + hp * KPB, gk, sb + (tt * KNP + hp) * 64 * KPB);
+    }
+    const uint32_t gv = uint32_t(g) * (DV * VB * 4);
+#pragma unroll
+    for (int k = 0; k < VNP; ++k) lds_dma<16>(rv, voff + 16 * k, gv, sb + LL::kStK + k * 1024);
+    unsigned char* ss = sb + LL::kStK + LL::kStV;
+    if (lane < DK / 8) {
+      lds_dma<16>(rks, koffs, uint32_t(g) * (DK * 2), ss);
+      lds_dma<16>(rkz, koffs, uint32_t(g) * (DK * 2), ss + 3 * LL::kStS);
+    }
+    if (lane < 4 * NGV) {
+      lds_dma<16>(rvs, coffs, uint32_t(g) * (DV * 2), ss + LL::kStS);
+      lds_dma<16>(rvz, coffs, uint32_t(g) * (DV * 2), ss + 2 * LL::kStS);
+    }
+  };
+  // the query first (vector-memory operations complete in order, so it would
+  // otherwise wait for the staged group), then group 0 into slot 0 (slot 1 serves
+  // the set-up and the retained rows first)
+  float qv[kG * DK / 64];
+#pragma unroll
+  for (int e = 0; e < kG * DK / 64; ++e)
+    qv[e] = load_q_any(a.q, a.q_dtype, (int64_t(b) * a.L.Hq + int64_t(h) * kG) * DK + lane + 64 * e);
+  if (nj > 0) stage_group(g0, 0);
 
   // ---------------------------------------------------------------- set-up
-  for (int idx = tid; idx < kG * DK; idx += kDecodeThreads)
-    qs_lds[idx] = a.scale * kLog2e * load_q_any(a.q, a.q_dtype, (int64_t(b) * a.L.Hq + int64_t(h) * kG) * DK + idx);
-  __syncthreads();
-  if (wave == 0) {
-    // per query: 2^-E with E >= 0 the smallest exponent such that |q * 2^-E| <= 1,
-    // keeping q_c s_c inside the fp16 range
-    for (int i = 0; i < kG; ++i) {
-      float mx = 0.0f;
-      for (int c = lane; c < DK; c += 64) mx = fmaxf(mx, fabsf(qs_lds[i * DK + c]));
-      mx = wave_max(mx);
-      if (lane == 0) {
-        int e = 0;
-        frexpf(mx, &e);
-        qexp[i] = mx > 1.0f ? ldexpf(1.0f, -e) : 1.0f;
-      }
-    }
+#pragma unroll
+  for (int e = 0; e < kG * DK / 64; ++e) qs_lds[lane + 64 * e] = a.scale * kLog2e * qv[e];
+  wave_lds_sync();
+  // per query: 2^-E with E >= 0 the smallest exponent such that |q * 2^-E| <= 1,
+  // keeping q_c s_c inside the fp16 range (wave-uniform)
+  float qexp[kG];
+#pragma unroll
+  for (int i = 0; i < kG; ++i) {
+    float mx = 0.0f;
+    for (int c = lane; c < DK; c += 64) mx = fmaxf(mx, fabsf(qs_lds[i * DK + c]));
+    mx = wave_max_rows(mx);
+    int e = 0;
+    frexpf(mx, &e);
+    qexp[i] = mx > 1.0f ? ldexpf(1.0f, -e) : 1.0f;
   }
-  __syncthreads();
   // B2: q 2^-E split hi/lo, entry (kk*4 + gq)*8 + i + 4*part, channels of block
   // gq*KK + kk in natural order (dword d = channels 2d, 2d+1)
-  for (int e = tid; e < KK * 32; e += kDecodeThreads) {
+  for (int e = lane; e < KK * 32; e += 64) {
     const int c8 = e & 7, gqe = (e >> 3) & 3, kke = e >> 5;
     const int i = c8 & 3, part = c8 >> 2;
+    const float qe = pick4(qexp, i);
     const float* src = qs_lds + i * DK + 8 * (gqe * KK + kke);
     u32x4 v;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const float x0 = src[2 * d] * qexp[i], x1 = src[2 * d + 1] * qexp[i];
+      const float x0 = src[2 * d] * qe, x1 = src[2 * d + 1] * qe;
       const half2_t hh = __builtin_convertvector(float2_t{x0, x1}, half2_t);
       const half2_t ll = __builtin_convertvector(float2_t{x0 - float(hh[0]), x1 - float(hh[1])}, half2_t);
       v[d] = __builtin_bit_cast(uint32_t, part ? ll : hh);
     }
     B2[e] = v;
   }
-
-  // Q' task of this lane: (block kk_t of lane group gq_t, query i_t); q 2^-E
-  // divided by the code scale of each operand slot
-  const int kk_t = lane >> 4, gq_t = (lane >> 2) & 3, i_t = lane & 3;
-  const bool qtask = kk_t < KK;
-  const int tb = gq_t * KK + (qtask ? kk_t : 0);
-  float qsv[8];
+  // the lane's Q' task: q 2^-E divided by the code scale of each operand slot,
+  // and q 2^-E itself for the zero-point partial sum
+  float qsv[8], qzv[8];
+  {
+    const float qe = pick4(qexp, i_t);
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-    qsv[k] = qtask ? qs_lds[i_t * DK + 8 * tb + k] * qexp[i_t] * (1.0f / key_code_scale<KB>(k & 3)) : 0.0f;
+    for (int k = 0; k < 8; ++k) {
+      qzv[k] = qtask ? qs_lds[i_t * DK + 8 * tb + k] * qe : 0.0f;
+      qsv[k] = qzv[k] * (1.0f / key_code_scale<KB>(k & 3));
+    }
+  }
   const int qb_entry = ((qtask ? kk_t : 0) * 4 + gq_t) * 8 + i_t;
-  // score columns: query iq = n % 4
-  const int iq = n & 3;
-  const float coefD = 16777216.0f / qexp[iq];  // codes are n 2^-24; q was scaled by 2^-E
-  const float coefB = 1.0f / qexp[iq];
-  // P' task: (query iq, channel group n / 4, octet gq)
-  const int gcP = n >> 2;
+  // Key zero-point term of query lane % 4: sum_c q_c z_c (times 2^-E), from the
+  // lanes' 8-channel partial sums: the 16 lanes of a query are lane % 4 + 4 m, so
+  // two rotations inside each row of 16 and two row swaps give every lane the
+  // total of its query.
+  auto zero_term = [&](const u32x4& kz) -> float {
+    float zp = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const half2_t zz = as_half2(kz[k >> 1]);
+      zp = fmaf(qzv[k], float(zz[k & 1]), zp);
+    }
+    zp += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(zp), 0x124, 0xF, 0xF, false));  // row_ror:4
+    zp += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(zp), 0x128, 0xF, 0xF, false));  // row_ror:8
+    const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(zp), __float_as_uint(zp), false, false);
+    zp = __uint_as_float(h32[0]) + __uint_as_float(h32[1]);
+    const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(zp), __float_as_uint(zp), false, false);
+    return __uint_as_float(h16[0]) + __uint_as_float(h16[1]);
+  };
+  const float coefB = 1.0f / pick4(qexp, iq);  // q was scaled by 2^-E
+  const float coefD = 16777216.0f * coefB;     // codes are n 2^-24
   const int pa_entry = (gcP * 4 + gq) * 8 + iq;
-  __syncthreads();  // B2 complete
+  wave_lds_sync();  // B2 written; the set-up reads of qs_lds are done
 
   // online-softmax state: reference maxima per query (wave-uniform) and this
   // lane's copy for its query; l over the lane's tokens; value accumulators
@@ -333,14 +468,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(const Decod
   f32x4 oacc[NV];
 #pragma unroll
   for (int t = 0; t < NV; ++t) oacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float o_r[kG][2];  // retained rows: channels 2 lane, 2 lane + 1
+  float o_r[kG][2];  // retained rows (VALU): channels 2 lane, 2 lane + 1
 #pragma unroll
   for (int i = 0; i < kG; ++i) o_r[i][0] = o_r[i][1] = 0.0f;
 
-  // Softmax update of 8 new scores per lane: v = raw combined MFMA outputs,
-  // score = v * coef + bias (log2 domain).  Returns the probabilities relative to
-  // the (possibly moved) reference maximum.
-  auto softmax_step = [&](const float (&v)[8], float coef, float bias, float (&pv)[8]) {
+  // Softmax update of 8 new scores per lane: v = raw MFMA outputs, score =
+  // v * coef + bias (log2 domain).  Returns the probabilities relative to the
+  // (possibly moved) reference maximum; rescale_acc(alpha) rescales the value
+  // accumulators when a reference moves.
+  auto softmax_step = [&](const float (&v)[8], float coef, float bias, float (&pv)[8], auto&& rescale_acc) {
     const float bterm = bias - m_lane;
     float sv[8];
     float mloc = -INFINITY;
@@ -380,16 +516,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(const Decod
       }
       l_run *= al;
       zacc *= al;
-#pragma unroll
-      for (int t = 0; t < NV; ++t) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[t][r] *= alpha[r];
-      }
-#pragma unroll
-      for (int i = 0; i < kG; ++i) {
-        o_r[i][0] *= alpha[i];
-        o_r[i][1] *= alpha[i];
-      }
+      rescale_acc(alpha);
 #pragma unroll
       for (int k = 0; k < 8; ++k) sv[k] = sabs[k] - m_lane;
     }
@@ -399,12 +526,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(const Decod
       l_run += pv[k];
     }
   };
+  auto rescale_retained = [&](const float (&alpha)[kG]) {
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {
+      o_r[i][0] *= alpha[i];
+      o_r[i][1] *= alpha[i];
+    }
+  };
+  auto rescale_groups = [&](const float (&alpha)[kG]) {
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[t][r] *= alpha[r];
+    }
+    rescale_retained(alpha);
+  };
 
   // ----------------------------------------------- retained fp16 rows first
   {
     const uint8_t* kr = static_cast<const uint8_t*>(a.cache.k_fp16) + slab * int64_t(R) * (DK * 2);
     const uint8_t* vr = static_cast<const uint8_t*>(a.cache.v_fp16) + slab * int64_t(R) * (DV * 2);
-    for (int rt = rt0 + wave; rt < rt1; rt += kDecodeWaves) {
+    for (int rt = rt0; rt < rt1; ++rt) {
       const int rbase = rt * 32;
       f32x4 sacc[2];
 #pragma unroll
@@ -414,7 +556,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(const Decod
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const u32x4 ak = *reinterpret_cast<const u32x4*>(kr + (uint32_t(row) * (DK * 2) + 16 * (gq * KK + kk)));
-          sacc[tt] = mfma16(ak, B2[(kk * 4 + gq) * 8 + (n & 7)], sacc[tt]);
+#pragma unroll
+          for (int part = 0; part < 2; ++part) sacc[tt] = mfma16(ak, B2[(kk * 4 + gq) * 8 + 4 * part + iq], sacc[tt]);
         }
       }
       // lane (n, gq): tile tt, register r -> token 8 gq + 4 tt + r
@@ -422,12 +565,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(const Decod
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float x = add_ror4(sacc[tt][r]);
-          v[4 * tt + r] = rbase + 8 * gq + 4 * tt + r < R ? x : -INFINITY;
-        }
+        for (int r = 0; r < 4; ++r) v[4 * tt + r] = rbase + 8 * gq + 4 * tt + r < R ? sacc[tt][r] : -INFINITY;
       }
-      softmax_step(v, coefB, 0.0f, pv);
+      softmax_step(v, coefB, 0.0f, pv, rescale_retained);
       if (n < kG) {
         *reinterpret_cast<f32x4*>(PT + n * 32 + 8 * gq) = f32x4{pv[0], pv[1], pv[2], pv[3]};
         *reinterpret_cast<f32x4*>(PT + n * 32 + 8 * gq + 4) = f32x4{pv[4], pv[5], pv[6], pv[7]};
@@ -462,70 +602,48 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(const Decod
     }
   }
 
-  // ------------------------------------------------------------ key groups
-  // per-slab bases (wave-uniform) and 32-bit lane offsets
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.cache.k_codes) + slab * int64_t(a.L.Tq) * KROW;
-  const uint16_t* ksbase = static_cast<const uint16_t*>(a.cache.k_scale) + slab * int64_t(nG) * DK;
-  const uint16_t* kzbase = static_cast<const uint16_t*>(a.cache.k_zero) + slab * int64_t(nG) * DK;
-  const uint32_t* vbase = static_cast<const uint32_t*>(a.cache.v_codes) + slab * int64_t(nG) * (DV * VB);
-  const uint16_t* vsbase = static_cast<const uint16_t*>(a.cache.v_scale) + slab * int64_t(nG) * DV;
-  const uint16_t* vzbase = static_cast<const uint16_t*>(a.cache.v_zero) + slab * int64_t(nG) * DV;
-  uint32_t koff[2];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) koff[tt] = uint32_t(8 * (n >> 2) + 4 * tt + (n & 3)) * KROW + gq * KLB;
-  const uint32_t voff = uint32_t(lane) * VLW;
-  const uint32_t ksoff = uint32_t(8 * tb);
-  const uint32_t vsoff = uint32_t(gcP * 32 + 8 * gq);
+  // slot 1 is free now for group 1
+  wave_lds_sync();
+  if (nj > 1) stage_group(g0 + 1, 1);
 
-  // everything one key group needs from HBM, held in registers so the next
-  // group's loads are in flight while the current one is computed
+  // ------------------------------------------------------------ key groups
+  // everything one key group needs, read back from its ring slot
   struct GroupLoads {
     uint32_t kw[2][KLW];  // key codes of tiles 0, 1 (row n = token 8(n/4) + 4tt + n%4)
     uint32_t vw[VLW];     // value code words: pair m, chunk c at m*NCH + c
-    u32x4 ks;             // key scales of the lane's Q' block
+    u32x4 ks, kz;         // key scales / zeros of the lane's Q' block
     u32x4 vs, vz;         // value scale / zero of the lane's P' channel group, tokens 8gq..
   };
-  // Branch-free: every lane issues the same loads, so the compiler can count
-  // outstanding loads and wait only for the current group's.
-  auto load_group = [&](int g, GroupLoads& d) {
-    const uint8_t* kg = kbase + uint32_t(g) * (32 * KROW);
+  auto read_group = [&](int slot, GroupLoads& d) {
+    const unsigned char* sb = stage + slot * LL::kStage;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) load_bytes<KLB>(kg + koff[tt], d.kw[tt]);
-    const uint32_t* vg = vbase + uint32_t(g) * (DV * VB);
+    for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-    for (int k = 0; k < VLW / 4; ++k) {
-      const u32x4 w4 = *reinterpret_cast<const u32x4*>(vg + voff + 4 * k);
-      d.vw[4 * k] = w4[0];
-      d.vw[4 * k + 1] = w4[1];
-      d.vw[4 * k + 2] = w4[2];
-      d.vw[4 * k + 3] = w4[3];
+      for (int hp = 0; hp < KNP; ++hp) {
+        const unsigned char* src = sb + (tt * KNP + hp) * 64 * KPB + lane * KPB;
+        if constexpr (KPB == 16) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d.kw[tt][4 * hp + e] = w[e];
+        } else {
+          d.kw[tt][hp] = *reinterpret_cast<const uint32_t*>(src);
+        }
+      }
     }
-    d.ks = *reinterpret_cast<const u32x4*>(ksbase + uint32_t(g) * DK + ksoff);
-    d.vs = *reinterpret_cast<const u32x4*>(vsbase + uint32_t(g) * DV + vsoff);
-    d.vz = *reinterpret_cast<const u32x4*>(vzbase + uint32_t(g) * DV + vsoff);
+#pragma unroll
+    for (int k = 0; k < VNP; ++k) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(sb + LL::kStK + k * 1024 + lane * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d.vw[4 * k + e] = w[e];
+    }
+    const unsigned char* ss = sb + LL::kStK + LL::kStV;
+    d.ks = *reinterpret_cast<const u32x4*>(ss + tb * 16);
+    d.kz = *reinterpret_cast<const u32x4*>(ss + 3 * LL::kStS + tb * 16);
+    d.vs = *reinterpret_cast<const u32x4*>(ss + LL::kStS + (gcP * 4 + gq) * 16);
+    d.vz = *reinterpret_cast<const u32x4*>(ss + 2 * LL::kStS + (gcP * 4 + gq) * 16);
   };
 
-  const int nj = g1 - g0 - wave > 0 ? (g1 - g0 - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
-  auto group_of = [&](int j) { return g0 + wave + kDecodeWaves * j; };
-
-  // zero-point terms of the wave's groups j0 .. j0 + 15: A = the zero points of
-  // the 16 groups (row = group), B = q split hi/lo; into BT [query][group]
-  auto bias_batch = [&](int j0) {
-    const int gr = group_of(min(j0 + n, nj - 1));
-    const uint16_t* zr = kzbase + uint32_t(gr) * DK;
-    f32x4 db = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 az = *reinterpret_cast<const u32x4*>(zr + 8 * (gq * KK + kk));
-      db = mfma16(az, B2[(kk * 4 + gq) * 8 + (n & 7)], db);
-    }
-    f32x4 bz;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) bz[r] = add_ror4(db[r]) * coefB;
-    if (n < kG) *reinterpret_cast<f32x4*>(BT + n * 16 + 4 * gq) = bz;
-  };
-
-  auto process_group = [&](const GroupLoads& d, int j) {
+  auto process_group = [&](const GroupLoads& d) {
     if (qtask) {
       u32x4 hi, lo;
       split8(qsv, d.ks, hi, lo);
@@ -533,21 +651,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(const Decod
       QB[qb_entry + 4] = lo;
     }
     wave_lds_sync();
-    const float bias = BT[iq * 16 + (j & 15)];
     f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 bq = QB[(kk * 4 + gq) * 8 + (n & 7)];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(key_field<KB>(d.kw[tt], kk), bq, sacc[tt]);
+      for (int part = 0; part < 2; ++part) {
+        const u32x4 bq = QB[(kk * 4 + gq) * 8 + 4 * part + iq];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(key_field<KB>(d.kw[tt], kk), bq, sacc[tt]);
+      }
     }
     float v[8], pv[8];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * tt + r] = add_ror4(sacc[tt][r]);
+      for (int r = 0; r < 4; ++r) v[4 * tt + r] = sacc[tt][r];
     }
-    softmax_step(v, coefD, bias, pv);
+    softmax_step(v, coefD, zero_term(d.kz) * coefB, pv, rescale_groups);
 
     // P' = p s (hi, lo) for the lane's (query, channel group, octet) and the
     // zero-point sum of the same task
@@ -585,111 +705,101 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(const Decod
   };
 
   {
-    // the prefetch past the last group re-reads the last group (always in bounds)
-    GroupLoads buf0, buf1;
-    if (nj > 0) load_group(group_of(0), buf0);
-    for (int j = 0; j < nj; j += 2) {
-      if ((j & 15) == 0) bias_batch(j);
-      load_group(group_of(min(j + 1, nj - 1)), buf1);
-      process_group(buf0, j);
-      if (j + 1 >= nj) break;
-      load_group(group_of(min(j + 2, nj - 1)), buf0);
-      process_group(buf1, j + 1);
+    // Two staging slots: group j sits in slot j % 2.  As soon as group j has been
+    // read into registers its slot takes the copies of group j + 2, so groups
+    // j + 1 and j + 2 are in flight while group j is computed.
+    // Issue priority falls by one level per quarter of the unit's groups: the
+    // waves of a SIMD are otherwise served oldest first and would finish far
+    // apart; this way a wave that is ahead yields to the ones behind it.
+    __builtin_amdgcn_s_setprio(3);
+    const int q1 = nj / 4, q2 = nj / 2, q3 = (3 * nj) / 4;
+    for (int j = 0; j < nj; ++j) {
+      const int slot = j & 1;
+      if (j == q1) __builtin_amdgcn_s_setprio(2);
+      if (j == q2) __builtin_amdgcn_s_setprio(1);
+      if (j == q3) __builtin_amdgcn_s_setprio(0);
+      if (j + 1 < nj)
+        wait_vmcnt<kDmas>();
+      else
+        wait_vmcnt<0>();
+      GroupLoads d;
+      read_group(slot, d);
+      wave_lds_sync();
+      if (j + 2 < nj) stage_group(g0 + j + 2, slot);
+      process_group(d);
     }
   }
 
-  // -------------------------------------------- combine the 4 wave states
-  __syncthreads();  // every wave is out of its loops; the loop LDS is free now
-  float* st = reinterpret_cast<float*>(smem + LL::kShared);                       // [4][4][DV + 2]
-  float* zsm = reinterpret_cast<float*>(smem + LL::kShared + LL::kSt);            // [4][4][NGV]
-  float* res = reinterpret_cast<float*>(smem + LL::kShared + LL::kSt + LL::kZs);  // [4][DV + 2]
+  // ------------------------------------------------------- the unit's result
+  // the ring is idle now (the last group waited for every copy): it holds the
+  // output accumulator OL [4][DV] and the value zero-point sums zsm [4][NGV]
+  float* OL = reinterpret_cast<float*>(stage);
+  float* zsm = OL + kG * DV;
+#pragma unroll
+  for (int i = 0; i < kG; ++i) {
+    OL[i * DV + 2 * lane] = o_r[i][0];
+    OL[i * DV + 2 * lane + 1] = o_r[i][1];
+  }
   {
-    float* sw = st + wave * kG * (DV + 2);
-    // l per query: lanes i, 16 + i, 32 + i, 48 + i hold its four token octets
-    float lq[kG];
-#pragma unroll
-    for (int i = 0; i < kG; ++i)
-      lq[i] = readlane_f32(l_run, i) + readlane_f32(l_run, 16 + i) + readlane_f32(l_run, 32 + i) +
-              readlane_f32(l_run, 48 + i);
-    if (lane == 0) {
-#pragma unroll
-      for (int i = 0; i < kG; ++i) {
-        sw[i * (DV + 2)] = m_q[i];
-        sw[i * (DV + 2) + 1] = lq[i];
-      }
-    }
     // zero-point sums per (query, channel group): lanes 16 gq + 4 gc + i
     const float z16 = zacc + __shfl_xor(zacc, 16, 64);
     const float z = z16 + __shfl_xor(z16, 32, 64);
-    if (gq == 0) zsm[(wave * kG + iq) * NGV + gcP] = z;
-    // matrix-core output: lane (n, 0) holds the hi rows, lane (n, 1) the lo rows
-    // of column n; tile t's codes carried 2^(slot * VB)
-    if (gq == 0) {
+    if (gq == 0) zsm[iq * NGV + gcP] = z;
+  }
+  wave_lds_sync();
+  // matrix-core accumulators (hi and lo rows, in output units) into OL
+  if (gq < 2) {  // lane groups 0 / 1 hold the hi / lo rows of the 4 queries
 #pragma unroll
-      for (int t = 0; t < NV; ++t) {
-        const float sc = 16777216.0f / float(1 << value_tile_shift<VB>(t % TPW));
+    for (int t = 0; t < NV; ++t) {
+      const float sc = 16777216.0f / float(1 << value_tile_shift<VB>(t % TPW));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sw[r * (DV + 2) + 2 + 16 * t + n] = oacc[t][r] * sc;
-      }
-    }
-    wave_lds_sync();
-    if (gq == 1) {
-#pragma unroll
-      for (int t = 0; t < NV; ++t) {
-        const float sc = 16777216.0f / float(1 << value_tile_shift<VB>(t % TPW));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sw[r * (DV + 2) + 2 + 16 * t + n] += oacc[t][r] * sc;
-      }
-    }
-    wave_lds_sync();
-    // zero-point terms and the retained rows' values
-#pragma unroll
-    for (int i = 0; i < kG; ++i) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int c = 2 * lane + e;
-        sw[i * (DV + 2) + 2 + c] += zsm[(wave * kG + i) * NGV + c / 32] + o_r[i][e];
-      }
+      for (int r = 0; r < 4; ++r) atomicAdd(&OL[r * DV + 16 * t + n], oacc[t][r] * sc);
     }
   }
-  __syncthreads();
-  for (int idx = tid; idx < kG * DV; idx += kDecodeThreads) {
-    const int i = idx / DV, c = idx - i * DV;
-    float M = -INFINITY;
+  wave_lds_sync();
+  // l per query: lanes i, 16 + i, 32 + i, 48 + i hold its four token octets
+  float lq[kG];
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, st[(w * kG + i) * (DV + 2)]);
-    float L = 0.0f, O = 0.0f;
+  for (int i = 0; i < kG; ++i)
+    lq[i] = readlane_f32(l_run, i) + readlane_f32(l_run, 16 + i) + readlane_f32(l_run, 32 + i) +
+            readlane_f32(l_run, 48 + i);
+  const int64_t qh0 = int64_t(b) * a.L.Hq + int64_t(h) * kG;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float* e = st + (w * kG + i) * (DV + 2);
-      const float wt = lse_weight(e[0], M);
-      L += wt * e[1];
-      O += wt * e[2 + c];
-    }
-    res[i * (DV + 2) + 2 + c] = O;
-    if (c == 0) {
-      res[i * (DV + 2)] = M;
-      res[i * (DV + 2) + 1] = L;
+  for (int i = 0; i < kG; ++i) {
+    float2 o;
+    o.x = OL[i * DV + 2 * lane] + zsm[i * NGV + (2 * lane) / 32];
+    o.y = OL[i * DV + 2 * lane + 1] + zsm[i * NGV + (2 * lane + 1) / 32];
+    if (U == 1) {
+      const float inv = 1.0f / lq[i];
+      o.x *= inv;
+      o.y *= inv;
+      *reinterpret_cast<float2*>(a.out + (qh0 + i) * DV + 2 * lane) = o;
+    } else {
+      // partial row of (query, unit): m, l, two unused floats, o[DV]
+      float* row = a.partials + ((qh0 + i) * U + unit) * (DV + 4);
+      *reinterpret_cast<float2*>(row + 4 + 2 * lane) = o;
+      if (lane == 0) *reinterpret_cast<float4*>(row) = make_float4(m_q[i], lq[i], 0.0f, 0.0f);
     }
   }
-  __syncthreads();
-  finish_partition(a, kG, b, h, p, res);
 }
 
 template <int DK, int DV, int KB, int VB>
 hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
-  constexpr size_t lds = Lds<DK, DV>::kBytes;
+  constexpr size_t lds = Lds<DK, DV, KB, VB>::kBytes;
   static_assert(lds <= 64 * 1024, "LDS budget");
-  const dim3 grid(unsigned(a.P), unsigned(a.L.Hkv), unsigned(a.L.B));
-  hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, KB, VB>), grid, dim3(kDecodeThreads), lds, stream, a);
+  const dim3 grid(unsigned(decode_mfma_units(a.L, a.P)), unsigned(a.L.Hkv), unsigned(a.L.B));
+  hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, KB, VB>), grid, dim3(64), lds, stream, a);
   return hipGetLastError();
 }
 
 template <int DK, int DV>
 hipError_t launch_bits(const DecodeArgs& a, hipStream_t stream) {
   const int kb = a.L.k_bits, vb = a.L.v_bits;
-#define KVQ_BITS_CASE(K_, V_) \
-  if (kb == K_ && vb == V_) return launch_one<DK, DV, K_, V_>(a, stream);
+  // key rows must give every lane at least 4 bytes of a tile (staged as dwords)
+#define KVQ_BITS_CASE(K_, V_)                                             \
+  if constexpr (DK * K_ / 32 >= 4) {                                      \
+    if (kb == K_ && vb == V_) return launch_one<DK, DV, K_, V_>(a, stream); \
+  }
   KVQ_BITS_CASE(2, 2) KVQ_BITS_CASE(2, 4) KVQ_BITS_CASE(2, 8)
   KVQ_BITS_CASE(4, 2) KVQ_BITS_CASE(4, 4) KVQ_BITS_CASE(4, 8)
   KVQ_BITS_CASE(8, 2) KVQ_BITS_CASE(8, 4) KVQ_BITS_CASE(8, 8)
@@ -699,7 +809,8 @@ hipError_t launch_bits(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream, int* parts) {
+  *parts = decode_mfma_units(a.L, a.P);
   if (a.L.Hq != kG * a.L.Hkv || a.L.Dv != 128) return hipErrorNotSupported;
   // per-slab offsets are 32-bit in this kernel
   const int64_t widest = a.L.Dk > a.L.Dv ? a.L.Dk : a.L.Dv;

@@ -27,13 +27,35 @@ struct DecodeArgs {
   kvq_cache cache;
   float scale;
   int P;
-  float* partials;     // [B * Hq, P, Dv + 4]: m (log2 domain), l, 2 unused, unnormalised o (P > 1)
+  float* partials;     // [B * Hq, units, Dv + 4]: m (log2 domain), l, 2 unused, unnormalised o (P > 1)
   float* out;          // [B, Hq, Dv]
 };
 
-// Workspace of kv_decode_attn: the per-partition partial results.
+// Work units of the matrix-core decode kernel: each of the P split-K partitions
+// is cut into c = 1, 2 or 4 contiguous pieces, one single-wave workgroup each.
+// c is the largest that keeps the grid within kUnitWaves waves (about what the
+// device holds at once), so short caches still fill the chip while long ones
+// keep each wave on a long run of key groups.  P == 1 is one unit, which
+// writes the output directly.
+constexpr int kMaxUnitsPerPartition = 4;
+#ifndef KVQ_UNIT_WAVES
+#define KVQ_UNIT_WAVES 4096
+#endif
+constexpr int64_t kUnitWaves = KVQ_UNIT_WAVES;
+inline int decode_mfma_units(const kvq_layout& L, int P) {
+  if (P == 1) return 1;
+  const int64_t slabs = int64_t(L.B) * L.Hkv;
+  int c = kMaxUnitsPerPartition;
+  while (c > 1 && slabs * P * c > kUnitWaves) c >>= 1;
+  return c * P;
+}
+
+// Workspace of kv_decode_attn: partial results, one row of Dv + 4 floats per
+// (query head, work unit); sized for the largest unit count of the matrix-core
+// kernel (the generic kernel writes one row per partition).
 inline size_t ws_partial_bytes(const kvq_layout& L, int P) {
-  return size_t(L.B) * size_t(L.Hq) * size_t(P) * size_t(L.Dv + 4) * sizeof(float);
+  const size_t units = P == 1 ? 0 : size_t(kMaxUnitsPerPartition) * size_t(P);
+  return size_t(L.B) * size_t(L.Hq) * units * size_t(L.Dv + 4) * sizeof(float);
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream);

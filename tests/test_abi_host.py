@@ -151,7 +151,7 @@ def test_decode_errors(lib):
     st, lay = _layout(lib, 2, 8, 2, 128, 128, 1088, 4, 2, 64, 0)   # 32 groups, R = 64
     assert st == 0
     need = lib.kvq_decode_workspace_bytes(ctypes.byref(lay), 4)
-    assert need == 2 * 8 * 4 * 132 * 4                # B * Hq * P * (Dv + 4) floats of partials
+    assert need == 2 * 8 * 4 * 4 * 132 * 4            # B * Hq * 4P * (Dv + 4) floats of partials
     assert lib.kvq_decode_workspace_bytes(ctypes.byref(lay), 1) == 0
     c = _cache()
     dec = lambda q=FAKE, qd=L_.KVQ_BF16, sc=0.1, P=4, ws=FAKE, wsb=need, out=FAKE, cache=c: lib.kv_decode_attn(
