@@ -167,6 +167,18 @@ int kv_decode_attn(const kvq_layout* L, const void* q, int q_dtype, const kvq_ca
                    float softmax_scale, int num_partitions, void* workspace,
                    size_t workspace_bytes, float* out, void* stream);
 
+/*
+ * kv_decode_attn_ex — kv_decode_attn with a timing hook for callers that measure
+ * the two kernels separately.  event_after_decode: a hipEvent_t created by the
+ * caller (NULL = none, then identical to kv_decode_attn); it is recorded on
+ * `stream` right after the decode kernel is enqueued and before the merge kernel
+ * (when P == 1 there is no merge and it is recorded after the only kernel).  A
+ * failed record returns KVQ_ERR_HIP.  All other arguments as kv_decode_attn.
+ */
+int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache,
+                      float softmax_scale, int num_partitions, void* workspace, size_t workspace_bytes,
+                      float* out, void* stream, void* event_after_decode);
+
 /* Static text for a status code. */
 const char* kvq_status_string(int status);
 

@@ -126,8 +126,12 @@ def kv_quant_pack(layout: Layout, K, V, cache=None, t_begin: int = 0, stream=Non
 
 
 def kv_decode_attn(layout: Layout, q, cache, num_partitions: int = 1, softmax_scale=None, out=None,
-                   workspace=None, stream=None):
-    """Decode attention of q [B, Hq, Dk] over a packed cache -> float32 [B, Hq, Dv]."""
+                   workspace=None, stream=None, after_decode_event=None):
+    """Decode attention of q [B, Hq, Dk] over a packed cache -> float32 [B, Hq, Dv].
+
+    after_decode_event: optional torch.cuda.Event, recorded on the stream between
+    the decode kernel and the merge kernel (it must have been recorded once
+    before, so that torch has created it)."""
     _check_tensor("q", q, (layout.B, layout.Hq, layout.Dk))
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(layout.Dk)
@@ -141,8 +145,13 @@ def kv_decode_attn(layout: Layout, q, cache, num_partitions: int = 1, softmax_sc
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     cs = _cache_struct(layout, cache)
-    L_.check(L_.load().kv_decode_attn(layout.ref, ctypes.c_void_p(q.data_ptr()), _DTYPE_CODES[q.dtype],
-                                      ctypes.byref(cs), ctypes.c_float(softmax_scale), num_partitions,
-                                      ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(out.data_ptr()),
-                                      _stream(stream)))
+    ev = None
+    if after_decode_event is not None:
+        ev = after_decode_event.cuda_event
+        if not ev:
+            raise ValueError("after_decode_event has not been created yet (record it once first)")
+    L_.check(L_.load().kv_decode_attn_ex(layout.ref, ctypes.c_void_p(q.data_ptr()), _DTYPE_CODES[q.dtype],
+                                         ctypes.byref(cs), ctypes.c_float(softmax_scale), num_partitions,
+                                         ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(out.data_ptr()),
+                                         _stream(stream), ctypes.c_void_p(ev)))
     return out

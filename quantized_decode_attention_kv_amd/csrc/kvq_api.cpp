@@ -196,6 +196,13 @@ int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count, const v
 
 int kv_decode_attn(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache, float softmax_scale,
                    int num_partitions, void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  return kv_decode_attn_ex(L, q, q_dtype, cache, softmax_scale, num_partitions, workspace, workspace_bytes, out,
+                           stream, nullptr);
+}
+
+int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache, float softmax_scale,
+                      int num_partitions, void* workspace, size_t workspace_bytes, float* out, void* stream,
+                      void* event_after_decode) {
   int st = check_layout(L);
   if (st != KVQ_OK) return st;
   if (!cache) return fail(KVQ_ERR_INVALID, "cache is NULL");
@@ -236,7 +243,8 @@ int kv_decode_attn(const kvq_layout* L, const void* q, int q_dtype, const kvq_ca
     a.partials = static_cast<float*>(workspace);
   }
   a.out = out;
-  const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(event_after_decode));
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -355,7 +355,7 @@ hipError_t launch_q(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t after_decode) {
   int parts = a.P;  // partial rows per query head written by the decode kernel
   hipError_t e = launch_decode_mfma(a, stream, &parts);
   if (e == hipErrorNotSupported) {
@@ -367,7 +367,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
       default: return hipErrorInvalidValue;
     }
   }
-  if (e != hipSuccess || parts == 1) return e;
+  if (e != hipSuccess) return e;
+  if (after_decode && (e = hipEventRecord(after_decode, stream)) != hipSuccess) return e;
+  if (parts == 1) return hipSuccess;
   return launch_merge(a, parts, stream);
 }
 

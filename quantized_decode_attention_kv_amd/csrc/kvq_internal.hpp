@@ -60,7 +60,8 @@ inline size_t ws_partial_bytes(const kvq_layout& L, int P) {
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
 // Decode kernel (matrix-core kernel where it applies, else the generic one)
-// followed, when P > 1, by the partition merge.
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// followed, when P > 1, by the partition merge; after_decode (if not null) is
+// recorded on the stream between the two.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t after_decode);
 
 }  // namespace kvq
