@@ -100,9 +100,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // explicit wait_vmcnt.
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
-// raw buffer over [base, base + 2^31): 32-bit dword format (gfx9 family)
-__device__ __forceinline__ buf_rsrc make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+// raw buffer over [base, base + bytes): 32-bit dword format (gfx9 family).  Loads
+// past the end return zeros without touching memory, so bytes = 0 turns every
+// copy from the buffer into a no-op.
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 template <int BYTES>
 __device__ __forceinline__ void lds_dma(buf_rsrc r, uint32_t voffset, uint32_t soffset, void* lds) {
@@ -272,6 +274,49 @@ struct Lds {
   static_assert(kG * DK * 4 <= kStage && kG * 32 * 4 <= kStage && kG * (DV + NGV) * 4 <= 2 * kStage, "aliases");
 };
 
+// 8 consecutive query elements starting at i0 (a multiple of 8; the array is
+// 16-byte aligned) as floats
+__device__ __forceinline__ void load_q8(const void* p, int qdt, int64_t i0, float (&x)[8]) {
+  if (qdt == KVQ_BF16) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + i0);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      x[2 * d] = __uint_as_float(w[d] << 16);
+      x[2 * d + 1] = __uint_as_float(w[d] & 0xFFFF0000u);
+    }
+  } else if (qdt == KVQ_F16) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + i0);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const half2_t hh = as_half2(w[d]);
+      x[2 * d] = float(hh[0]);
+      x[2 * d + 1] = float(hh[1]);
+    }
+  } else {
+    const f32x4* f = reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i0);
+    const f32x4 u = f[0], v = f[1];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      x[d] = u[d];
+      x[4 + d] = v[d];
+    }
+  }
+}
+
+// Sum (or max) of v over the 16 lanes l with l % 4 == lane % 4: two rotations
+// inside each row of 16, then the two gfx950 half swaps across rows; every lane
+// gets its class's total.
+template <bool MAX>
+__device__ __forceinline__ float mod4_allreduce(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false)));  // row_ror:4
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false)));  // row_ror:8
+  const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(h32[0]), __uint_as_float(h32[1]));
+  const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(h16[0]), __uint_as_float(h16[1]));
+}
+
 // max over the 64 lanes of a wave (DPP inside rows, then the four row results)
 __device__ __forceinline__ float wave_max_rows(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
@@ -288,8 +333,17 @@ __device__ __forceinline__ float pick4(const float (&x)[kG], int i) {
 // One workgroup = one wave = one unit: a contiguous piece of a split-K partition
 // of one (batch, kv head) slab (the whole slab when P == 1).  Units are
 // independent: no barriers, and each writes its own partial result.
+// Waves per SIMD that the LDS of one unit allows on a 160 KB compute unit (at most
+// 4, which is the 16 waves per CU of the common shapes); the register budget
+// is set to match, so registers never limit occupancy below what LDS allows.
 template <int DK, int DV, int KB, int VB>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
+constexpr int lds_waves_per_simd() {
+  const int per_cu = (160 * 1024) / Lds<DK, DV, KB, VB>::kBytes;
+  return per_cu >= 16 ? 4 : (per_cu >= 4 ? per_cu / 4 : 1);
+}
+
+template <int DK, int DV, int KB, int VB>
+__global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void decode_mfma_kernel(const DecodeArgs a) {
   using LL = Lds<DK, DV, KB, VB>;
   constexpr int KK = DK / 32;          // 32-channel score steps
   constexpr int NV = DV / 16;          // 16-channel value tiles
@@ -307,9 +361,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
   u32x4* QB = reinterpret_cast<u32x4*>(smem + LL::oQB);       // [(KK+1)*4][8]
   u32x4* PA = reinterpret_cast<u32x4*>(smem + LL::oPA);       // [NGV*4][8]
   unsigned char* stage = smem + LL::oRing;                    // [2][kStage]
-  u32x4* B2 = QB;                                             // q hi/lo, set-up and retained rows
-  float* qs_lds = reinterpret_cast<float*>(smem + LL::oLast); // [4][DK], set-up only
-  float* PT = reinterpret_cast<float*>(smem + LL::oLast);     // [4][32], retained rows only
+  u32x4* B2 = QB;                                             // q hi/lo, retained rows
+  float* PT = reinterpret_cast<float*>(stage);                // [4][32], retained rows
   const int lane = threadIdx.x, n = lane & 15, gq = lane >> 4;
 
   const int unit = blockIdx.x, U = gridDim.x, h = blockIdx.y, b = blockIdx.z;
@@ -342,13 +395,18 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
   // back from the place of its own lane id (LDS reads contiguous across the wave):
   //   key codes: per tile, KNP pieces of KPB bytes (the lane's quarter row);
   //   value codes: VLW / 4 pieces of 16 bytes (the lane's words);
-  //   key scales and zeros: one 16-byte block per 8 channels (lanes < DK / 8);
-  //   value scales and zeros: one 16-byte (channel group, octet) chunk each
-  //   (lanes < 4 * NGV).
+  //   key scales, key zeros, value scales, value zeros: one 4-byte copy per lane
+  //   each, 256 bytes per array and group (the key arrays of DK < 128 have fewer
+  //   bytes; the surplus lanes read past the end of the buffer, which returns
+  //   zeros into the unused part of the array's 256-byte area).
+  // Every copy is a buffer load with all lanes active, so the wave's copies
+  // complete in issue order and the waits below can count them.
   constexpr int KPB = KLB >= 16 ? 16 : 4;   // bytes per key piece
   constexpr int KNP = KLB / KPB;            // key pieces per tile
   constexpr int VNP = VLW / 4;              // value pieces
   constexpr int kDmas = 2 * KNP + VNP + 4;  // copies per group
+  constexpr int oKZ = LL::kStS, oVS = 2 * LL::kStS, oVZ = 3 * LL::kStS;  // scale area offsets
+  static_assert(DK * 2 <= LL::kStS && DV * 2 == LL::kStS, "scale area");
   static_assert(kDmas < 64, "vmcnt");
   static_assert(KLB % KPB == 0 && VLW % 4 == 0 && DK / 8 <= 64 && 4 * NGV <= 64, "staging");
   // per-lane byte offsets inside a group (the group base itself is wave-uniform)
@@ -356,11 +414,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) koff[tt] = uint32_t(8 * (n >> 2) + 4 * tt + (n & 3)) * KROW + gq * KLB;
   const uint32_t voff = uint32_t(lane) * (VLW * 4);
-  const uint32_t koffs = uint32_t(lane) * 16;                          // key scales / zeros
-  const uint32_t coffs = uint32_t((lane >> 2) * 32 + 8 * (lane & 3)) * 2;  // value scales / zeros
-  const buf_rsrc rk = make_rsrc(kbase), rv = make_rsrc(vbase);
-  const buf_rsrc rks = make_rsrc(ksbase), rkz = make_rsrc(kzbase);
-  const buf_rsrc rvs = make_rsrc(vsbase), rvz = make_rsrc(vzbase);
+  // scale copies: byte offset of this lane's dword (past the end for surplus lanes)
+  const uint32_t kso = lane < DK / 2 ? uint32_t(lane) * 4 : 0x80000000u;
+  const uint32_t vso = uint32_t(lane) * 4;
+  // a unit without key groups gets empty buffers (its cache buffers may be null)
+  const int nrec = nj > 0 ? 0x7fffffff : 0;
+  const buf_rsrc rk = make_rsrc(kbase, nrec), rv = make_rsrc(vbase, nrec);
+  const int nsk = nj > 0 ? nG * DK * 2 : 0, nsv = nj > 0 ? nG * DV * 2 : 0;
+  const buf_rsrc rks = make_rsrc(ksbase, nsk), rkz = make_rsrc(kzbase, nsk);
+  const buf_rsrc rvs = make_rsrc(vsbase, nsv), rvz = make_rsrc(vzbase, nsv);
   auto stage_group = [&](int g, int slot) {
     unsigned char* sb = stage + slot * LL::kStage;
     const uint32_t gk = uint32_t(g) * (32 * KROW);
@@ -373,67 +435,73 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < VNP; ++k) lds_dma<16>(rv, voff + 16 * k, gv, sb + LL::kStK + k * 1024);
     unsigned char* ss = sb + LL::kStK + LL::kStV;
-    if (lane < DK / 8) {
-      lds_dma<16>(rks, koffs, uint32_t(g) * (DK * 2), ss);
-      lds_dma<16>(rkz, koffs, uint32_t(g) * (DK * 2), ss + 3 * LL::kStS);
-    }
-    if (lane < 4 * NGV) {
-      lds_dma<16>(rvs, coffs, uint32_t(g) * (DV * 2), ss + LL::kStS);
-      lds_dma<16>(rvz, coffs, uint32_t(g) * (DV * 2), ss + 2 * LL::kStS);
-    }
+    lds_dma<4>(rks, kso, uint32_t(g) * (DK * 2), ss);
+    lds_dma<4>(rkz, kso, uint32_t(g) * (DK * 2), ss + oKZ);
+    lds_dma<4>(rvs, vso, uint32_t(g) * (DV * 2), ss + oVS);
+    lds_dma<4>(rvz, vso, uint32_t(g) * (DV * 2), ss + oVZ);
   };
-  // the query first (vector-memory operations complete in order, so it would
-  // otherwise wait for the staged group), then group 0 into slot 0 (slot 1 serves
-  // the set-up and the retained rows first)
-  float qv[kG * DK / 64];
-#pragma unroll
-  for (int e = 0; e < kG * DK / 64; ++e)
-    qv[e] = load_q_any(a.q, a.q_dtype, (int64_t(b) * a.L.Hq + int64_t(h) * kG) * DK + lane + 64 * e);
-  if (nj > 0) stage_group(g0, 0);
-
-  // ---------------------------------------------------------------- set-up
-#pragma unroll
-  for (int e = 0; e < kG * DK / 64; ++e) qs_lds[lane + 64 * e] = a.scale * kLog2e * qv[e];
-  wave_lds_sync();
-  // per query: 2^-E with E >= 0 the smallest exponent such that |q * 2^-E| <= 1,
-  // keeping q_c s_c inside the fp16 range (wave-uniform)
-  float qexp[kG];
-#pragma unroll
-  for (int i = 0; i < kG; ++i) {
-    float mx = 0.0f;
-    for (int c = lane; c < DK; c += 64) mx = fmaxf(mx, fabsf(qs_lds[i * DK + c]));
-    mx = wave_max_rows(mx);
-    int e = 0;
-    frexpf(mx, &e);
-    qexp[i] = mx > 1.0f ? ldexpf(1.0f, -e) : 1.0f;
-  }
-  // B2: q 2^-E split hi/lo, entry (kk*4 + gq)*8 + i + 4*part, channels of block
-  // gq*KK + kk in natural order (dword d = channels 2d, 2d+1)
-  for (int e = lane; e < KK * 32; e += 64) {
-    const int c8 = e & 7, gqe = (e >> 3) & 3, kke = e >> 5;
-    const int i = c8 & 3, part = c8 >> 2;
-    const float qe = pick4(qexp, i);
-    const float* src = qs_lds + i * DK + 8 * (gqe * KK + kke);
-    u32x4 v;
+  // The query first (vector-memory operations complete in order, so it would
+  // otherwise wait for the staged groups): the 8 elements of the lane's Q' task.
+  // Then groups 0 and 1 into the two slots (a unit with a single group stages it
+  // twice; a unit without groups issues copies that touch no memory).
+  // Raw bytes, converted only after the copies are issued (a conversion next to
+  // the load would make the wave wait for it first); the buffer spans the kG
+  // query rows of this KV head, so the 32-byte read of a 16-bit query stays inside.
+  const int64_t qhead = (int64_t(b) * a.L.Hq + int64_t(h) * kG) * DK;
+  const int qesz = a.q_dtype == KVQ_F32 ? 4 : 2;
+  const buf_rsrc rq = make_rsrc(static_cast<const uint8_t*>(a.q) + qhead * qesz, kG * DK * qesz);
+  const uint32_t qoff = uint32_t(i_t * DK + 8 * tb) * uint32_t(qesz);
+  const u32x4 qw0 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff, 0, 0);
+  const u32x4 qw1 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 16, 0, 0);
+  stage_group(g0, 0);
+  stage_group(g0 + (nj > 1 ? 1 : 0), 1);
+  __builtin_amdgcn_sched_barrier(0);
+  float qx[8];
+  if (a.q_dtype == KVQ_BF16) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const float x0 = src[2 * d] * qe, x1 = src[2 * d + 1] * qe;
-      const half2_t hh = __builtin_convertvector(float2_t{x0, x1}, half2_t);
-      const half2_t ll = __builtin_convertvector(float2_t{x0 - float(hh[0]), x1 - float(hh[1])}, half2_t);
-      v[d] = __builtin_bit_cast(uint32_t, part ? ll : hh);
+      qx[2 * d] = __uint_as_float(qw0[d] << 16);
+      qx[2 * d + 1] = __uint_as_float(qw0[d] & 0xFFFF0000u);
     }
-    B2[e] = v;
+  } else if (a.q_dtype == KVQ_F16) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const half2_t hh = as_half2(qw0[d]);
+      qx[2 * d] = float(hh[0]);
+      qx[2 * d + 1] = float(hh[1]);
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      qx[d] = __uint_as_float(qw0[d]);
+      qx[4 + d] = __uint_as_float(qw1[d]);
+    }
+  }
+
+  // ---------------------------------------------------------------- set-up
+  // Query lane % 4 is scaled by 2^-E, E >= 0 the smallest exponent such that
+  // |q 2^-E| <= 1, which keeps q_c s_c inside the fp16 range; every use of the
+  // exponent in this lane concerns query lane % 4.
+  float qmax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    qx[k] *= a.scale * kLog2e;
+    qmax = fmaxf(qmax, fabsf(qx[k]));
+  }
+  qmax = mod4_allreduce<true>(qtask ? qmax : 0.0f);
+  float qe;
+  {
+    int e = 0;
+    frexpf(qmax, &e);
+    qe = qmax > 1.0f ? ldexpf(1.0f, -e) : 1.0f;
   }
   // the lane's Q' task: q 2^-E divided by the code scale of each operand slot,
   // and q 2^-E itself for the zero-point partial sum
   float qsv[8], qzv[8];
-  {
-    const float qe = pick4(qexp, i_t);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      qzv[k] = qtask ? qs_lds[i_t * DK + 8 * tb + k] * qe : 0.0f;
-      qsv[k] = qzv[k] * (1.0f / key_code_scale<KB>(k & 3));
-    }
+  for (int k = 0; k < 8; ++k) {
+    qzv[k] = qtask ? qx[k] * qe : 0.0f;
+    qsv[k] = qzv[k] * (1.0f / key_code_scale<KB>(k & 3));
   }
   const int qb_entry = ((qtask ? kk_t : 0) * 4 + gq_t) * 8 + i_t;
   // Key zero-point term of query lane % 4: sum_c q_c z_c (times 2^-E), from the
@@ -447,17 +515,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
       const half2_t zz = as_half2(kz[k >> 1]);
       zp = fmaf(qzv[k], float(zz[k & 1]), zp);
     }
-    zp += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(zp), 0x124, 0xF, 0xF, false));  // row_ror:4
-    zp += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(zp), 0x128, 0xF, 0xF, false));  // row_ror:8
-    const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(zp), __float_as_uint(zp), false, false);
-    zp = __uint_as_float(h32[0]) + __uint_as_float(h32[1]);
-    const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(zp), __float_as_uint(zp), false, false);
-    return __uint_as_float(h16[0]) + __uint_as_float(h16[1]);
+    return mod4_allreduce<false>(zp);
   };
-  const float coefB = 1.0f / pick4(qexp, iq);  // q was scaled by 2^-E
-  const float coefD = 16777216.0f * coefB;     // codes are n 2^-24
+  const float coefB = 1.0f / qe;           // q was scaled by 2^-E (query iq = lane % 4)
+  const float coefD = 16777216.0f * coefB;  // codes are n 2^-24
   const int pa_entry = (gcP * 4 + gq) * 8 + iq;
-  wave_lds_sync();  // B2 written; the set-up reads of qs_lds are done
 
   // online-softmax state: reference maxima per query (wave-uniform) and this
   // lane's copy for its query; l over the lane's tokens; value accumulators
@@ -542,70 +604,6 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     rescale_retained(alpha);
   };
 
-  // ----------------------------------------------- retained fp16 rows first
-  {
-    const uint8_t* kr = static_cast<const uint8_t*>(a.cache.k_fp16) + slab * int64_t(R) * (DK * 2);
-    const uint8_t* vr = static_cast<const uint8_t*>(a.cache.v_fp16) + slab * int64_t(R) * (DV * 2);
-    for (int rt = rt0; rt < rt1; ++rt) {
-      const int rbase = rt * 32;
-      f32x4 sacc[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int row = min(rbase + 8 * (n >> 2) + 4 * tt + (n & 3), R - 1);
-        sacc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 ak = *reinterpret_cast<const u32x4*>(kr + (uint32_t(row) * (DK * 2) + 16 * (gq * KK + kk)));
-#pragma unroll
-          for (int part = 0; part < 2; ++part) sacc[tt] = mfma16(ak, B2[(kk * 4 + gq) * 8 + 4 * part + iq], sacc[tt]);
-        }
-      }
-      // lane (n, gq): tile tt, register r -> token 8 gq + 4 tt + r
-      float v[8], pv[8];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[4 * tt + r] = rbase + 8 * gq + 4 * tt + r < R ? sacc[tt][r] : -INFINITY;
-      }
-      softmax_step(v, coefB, 0.0f, pv, rescale_retained);
-      if (n < kG) {
-        *reinterpret_cast<f32x4*>(PT + n * 32 + 8 * gq) = f32x4{pv[0], pv[1], pv[2], pv[3]};
-        *reinterpret_cast<f32x4*>(PT + n * 32 + 8 * gq + 4) = f32x4{pv[4], pv[5], pv[6], pv[7]};
-      }
-      wave_lds_sync();
-      // values on the VALU: lane owns channels 2 lane, 2 lane + 1 of every row
-#pragma unroll
-      for (int t0 = 0; t0 < 32; t0 += 8) {
-        uint32_t vv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int row = min(rbase + t0 + u, R - 1);
-          vv[u] = *reinterpret_cast<const uint32_t*>(vr + (uint32_t(row) * (DV * 2) + 4 * lane));
-        }
-#pragma unroll
-        for (int u4 = 0; u4 < 8; u4 += 4) {
-          f32x4 pq[kG];
-#pragma unroll
-          for (int i = 0; i < kG; ++i) pq[i] = *reinterpret_cast<const f32x4*>(PT + i * 32 + t0 + u4);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const half2_t hv = as_half2(vv[u4 + u]);
-#pragma unroll
-            for (int i = 0; i < kG; ++i) {
-              o_r[i][0] = fmaf(pq[i][u], float(hv[0]), o_r[i][0]);
-              o_r[i][1] = fmaf(pq[i][u], float(hv[1]), o_r[i][1]);
-            }
-          }
-        }
-      }
-      wave_lds_sync();
-    }
-  }
-
-  // slot 1 is free now for group 1
-  wave_lds_sync();
-  if (nj > 1) stage_group(g0 + 1, 1);
-
   // ------------------------------------------------------------ key groups
   // everything one key group needs, read back from its ring slot
   struct GroupLoads {
@@ -638,9 +636,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     }
     const unsigned char* ss = sb + LL::kStK + LL::kStV;
     d.ks = *reinterpret_cast<const u32x4*>(ss + tb * 16);
-    d.kz = *reinterpret_cast<const u32x4*>(ss + 3 * LL::kStS + tb * 16);
-    d.vs = *reinterpret_cast<const u32x4*>(ss + LL::kStS + (gcP * 4 + gq) * 16);
-    d.vz = *reinterpret_cast<const u32x4*>(ss + 2 * LL::kStS + (gcP * 4 + gq) * 16);
+    d.kz = *reinterpret_cast<const u32x4*>(ss + oKZ + tb * 16);
+    d.vs = *reinterpret_cast<const u32x4*>(ss + oVS + (gcP * 4 + gq) * 16);
+    d.vz = *reinterpret_cast<const u32x4*>(ss + oVZ + (gcP * 4 + gq) * 16);
   };
 
   auto process_group = [&](const GroupLoads& d) {
@@ -730,9 +728,90 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     }
   }
 
+  // --------------------------------------------------- retained fp16 rows
+  // After the key groups (the order of tokens does not matter): the ring is idle
+  // (the last group waited for every copy) and holds the probabilities PT; the
+  // Q' tile takes the q hi/lo operand B2 again.
+  if (rt0 < rt1) {
+    // B2: q 2^-E split hi/lo, entry (kk*4 + gq)*8 + i + 4*part, channels of block
+    // gq*KK + kk in natural order (dword d = channels 2d, 2d+1); query i = e % 4
+    // is this lane's query
+    for (int e = lane; e < KK * 32; e += 64) {
+      const int gqe = (e >> 3) & 3, kke = e >> 5, part = (e >> 2) & 1;
+      float x[8];
+      load_q8(a.q, a.q_dtype, qhead + (e & 3) * DK + 8 * (gqe * KK + kke), x);
+      u32x4 v;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float x0 = x[2 * d] * (a.scale * kLog2e) * qe, x1 = x[2 * d + 1] * (a.scale * kLog2e) * qe;
+        const half2_t hh = __builtin_convertvector(float2_t{x0, x1}, half2_t);
+        const half2_t ll = __builtin_convertvector(float2_t{x0 - float(hh[0]), x1 - float(hh[1])}, half2_t);
+        v[d] = __builtin_bit_cast(uint32_t, part ? ll : hh);
+      }
+      B2[e] = v;
+    }
+    wave_lds_sync();
+    const uint8_t* kr = static_cast<const uint8_t*>(a.cache.k_fp16) + slab * int64_t(R) * (DK * 2);
+    const uint8_t* vr = static_cast<const uint8_t*>(a.cache.v_fp16) + slab * int64_t(R) * (DV * 2);
+    for (int rt = rt0; rt < rt1; ++rt) {
+      const int rbase = rt * 32;
+      f32x4 sacc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int row = min(rbase + 8 * (n >> 2) + 4 * tt + (n & 3), R - 1);
+        sacc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4 ak = *reinterpret_cast<const u32x4*>(kr + (uint32_t(row) * (DK * 2) + 16 * (gq * KK + kk)));
+#pragma unroll
+          for (int part = 0; part < 2; ++part) sacc[tt] = mfma16(ak, B2[(kk * 4 + gq) * 8 + 4 * part + iq], sacc[tt]);
+        }
+      }
+      // lane (n, gq): tile tt, register r -> token 8 gq + 4 tt + r
+      float v[8], pv[8];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[4 * tt + r] = rbase + 8 * gq + 4 * tt + r < R ? sacc[tt][r] : -INFINITY;
+      }
+      softmax_step(v, coefB, 0.0f, pv, rescale_groups);
+      if (n < kG) {
+        *reinterpret_cast<f32x4*>(PT + n * 32 + 8 * gq) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+        *reinterpret_cast<f32x4*>(PT + n * 32 + 8 * gq + 4) = f32x4{pv[4], pv[5], pv[6], pv[7]};
+      }
+      wave_lds_sync();
+      // values on the VALU: lane owns channels 2 lane, 2 lane + 1 of every row
+#pragma unroll
+      for (int t0 = 0; t0 < 32; t0 += 8) {
+        uint32_t vv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = min(rbase + t0 + u, R - 1);
+          vv[u] = *reinterpret_cast<const uint32_t*>(vr + (uint32_t(row) * (DV * 2) + 4 * lane));
+        }
+#pragma unroll
+        for (int u4 = 0; u4 < 8; u4 += 4) {
+          f32x4 pq[kG];
+#pragma unroll
+          for (int i = 0; i < kG; ++i) pq[i] = *reinterpret_cast<const f32x4*>(PT + i * 32 + t0 + u4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const half2_t hv = as_half2(vv[u4 + u]);
+#pragma unroll
+            for (int i = 0; i < kG; ++i) {
+              o_r[i][0] = fmaf(pq[i][u], float(hv[0]), o_r[i][0]);
+              o_r[i][1] = fmaf(pq[i][u], float(hv[1]), o_r[i][1]);
+            }
+          }
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+
   // ------------------------------------------------------- the unit's result
-  // the ring is idle now (the last group waited for every copy): it holds the
-  // output accumulator OL [4][DV] and the value zero-point sums zsm [4][NGV]
+  // the ring is idle now: it holds the output accumulator OL [4][DV] and the value
+  // zero-point sums zsm [4][NGV]
   float* OL = reinterpret_cast<float*>(stage);
   float* zsm = OL + kG * DV;
 #pragma unroll
