@@ -121,7 +121,7 @@ int64_t kvq_quantized_before(const kvq_layout* L, int64_t t);
 
 /* Workspace kv_decode_attn needs for num_partitions sequence partitions (0 when
  * num_partitions == 1): B*Hq*4*num_partitions*(Dv+4) floats of partial results
- * (the decode kernel may cut each partition into up to 4 work units).
+ * (the decode kernel may cut the key groups into up to 4*num_partitions runs).
  * Returns 0 for an invalid layout. */
 size_t kvq_decode_workspace_bytes(const kvq_layout* L, int num_partitions);
 
@@ -147,15 +147,19 @@ int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count,
 /*
  * kv_decode_attn — single-token decode attention over a packed cache: one decode
  * kernel whose workgroups each take a contiguous run of key groups of one
- * (batch row, kv head) pair (a partition, or a half or quarter of one) and, when
- * P > 1, one merge kernel after it on the same stream.
+ * (batch row, kv head) pair and, when P > 1, one merge kernel after it on the
+ * same stream.
  *   q:   [B, Hq, Dk] device array of dtype q_dtype; query head i reads KV head
  *        i / (Hq / Hkv) (grouped-query attention: the Hq/Hkv queries of one KV head
  *        share each read of its cache).
  *   softmax_scale: scale of the scores (finite; pass 1/sqrtf(Dk) for the usual one).
- *   num_partitions: P sequence partitions processed in parallel (split-K); partition
- *        p takes key groups [p*n_groups/P, (p+1)*n_groups/P) (integer division)
- *        and a share of the retained tokens.  1 <= P <= max(1, ceil(T/32)).
+ *   num_partitions: P, the split-K factor: the key groups of every (batch row, kv
+ *        head) pair are cut into P contiguous runs processed in parallel, each with
+ *        a share of the retained tokens, and the partial results are merged.  The
+ *        library chooses the run boundaries: near-equal (integer division) for the
+ *        vector-ALU kernel; for the matrix-core kernel the P runs may be cut further
+ *        into 2P or 4P and sized by dispatch order (within about +-20% of equal).
+ *        Results differ only in rounding.  1 <= P <= max(1, ceil(T/32)).
  *   workspace / workspace_bytes: at least kvq_decode_workspace_bytes(L, P) bytes of
  *        16-byte aligned device memory (may be NULL when P == 1); no
  *        initialisation needed.  A workspace serves one call at a time: calls that

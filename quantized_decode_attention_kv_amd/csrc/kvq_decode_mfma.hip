@@ -333,6 +333,28 @@ __device__ __forceinline__ float pick4(const float (&x)[kG], int i) {
 // One workgroup = one wave = one unit: a contiguous piece of a split-K partition
 // of one (batch, kv head) slab (the whole slab when P == 1).  Units are
 // independent: no barriers, and each writes its own partial result.
+// First key group of unit u of U over nG groups.  The workgroup dispatcher fills
+// the SIMDs round-robin in grid order, so with the unit-major grid the units
+// u < U/4 become the oldest wave on their SIMD, the next quarter the second
+// oldest, and so on; waves are served oldest first, so unit sizes fall by
+// quarter (integer weights 100 + s (3 - 2 r) for quarter r) and the waves of a
+// SIMD finish together.  Any weights give the same result up to rounding.
+#ifndef KVQ_UNIT_SKEW
+#define KVQ_UNIT_SKEW 6
+#endif
+__device__ __forceinline__ int unit_start(int u, int U, int nG) {
+  constexpr int64_t s = KVQ_UNIT_SKEW;
+  int64_t wu = 0, wall = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t lo = (int64_t(r) * U + 3) / 4, hi = (int64_t(r + 1) * U + 3) / 4;  // units of quarter r
+    const int64_t w = 100 + s * (3 - 2 * r);
+    wall += w * (hi - lo);
+    wu += w * (u < lo ? 0 : (u < hi ? u - lo : hi - lo));
+  }
+  return int(int64_t(nG) * wu / wall);
+}
+
 // Waves per SIMD that the LDS of one unit allows on a 160 KB compute unit (at most
 // 4, which is the 16 waves per CU of the common shapes); the register budget
 // is set to match, so registers never limit occupancy below what LDS allows.
@@ -365,10 +387,13 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   float* PT = reinterpret_cast<float*>(stage);                // [4][32], retained rows
   const int lane = threadIdx.x, n = lane & 15, gq = lane >> 4;
 
-  const int unit = blockIdx.x, U = gridDim.x, h = blockIdx.y, b = blockIdx.z;
+  // unit-major grid: workgroup L takes unit L / slabs of slab L % slabs
+  const int U = a.units, slabs = a.L.B * a.L.Hkv;
+  const int unit = int(blockIdx.x) / slabs, sl = int(blockIdx.x) % slabs;
+  const int h = sl % a.L.Hkv, b = sl / a.L.Hkv;
   const int nG = a.L.n_groups, R = a.L.R;
   const int64_t slab = int64_t(b) * a.L.Hkv + h;
-  const int g0 = int(int64_t(unit) * nG / U), g1 = int(int64_t(unit + 1) * nG / U);
+  const int g0 = unit_start(unit, U, nG), g1 = unit_start(unit + 1, U, nG);
   const int nRT = (R + 31) / 32;  // 32-row tiles of retained rows
   const int rt0 = int(int64_t(unit) * nRT / U), rt1 = int(int64_t(unit + 1) * nRT / U);
   const int nj = g1 - g0;
@@ -866,7 +891,7 @@ template <int DK, int DV, int KB, int VB>
 hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
   constexpr size_t lds = Lds<DK, DV, KB, VB>::kBytes;
   static_assert(lds <= 64 * 1024, "LDS budget");
-  const dim3 grid(unsigned(decode_mfma_units(a.L, a.P)), unsigned(a.L.Hkv), unsigned(a.L.B));
+  const dim3 grid(unsigned(a.units) * unsigned(a.L.B) * unsigned(a.L.Hkv));
   hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, KB, VB>), grid, dim3(64), lds, stream, a);
   return hipGetLastError();
 }
@@ -888,12 +913,15 @@ hipError_t launch_bits(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream, int* parts) {
-  *parts = decode_mfma_units(a.L, a.P);
+hipError_t launch_decode_mfma(const DecodeArgs& a_in, hipStream_t stream, int* parts) {
+  DecodeArgs a = a_in;
+  a.units = decode_mfma_units(a.L, a.P);
+  *parts = a.units;
   if (a.L.Hq != kG * a.L.Hkv || a.L.Dv != 128) return hipErrorNotSupported;
-  // per-slab offsets are 32-bit in this kernel
+  // per-slab offsets are 32-bit in this kernel, and so is the grid
   const int64_t widest = a.L.Dk > a.L.Dv ? a.L.Dk : a.L.Dv;
-  if (int64_t(a.L.Tq) * widest >= (int64_t(1) << 31) || int64_t(a.L.R) * widest * 2 >= (int64_t(1) << 31))
+  if (int64_t(a.L.Tq) * widest >= (int64_t(1) << 31) || int64_t(a.L.R) * widest * 2 >= (int64_t(1) << 31) ||
+      int64_t(a.units) * a.L.B * a.L.Hkv >= (int64_t(1) << 31))
     return hipErrorNotSupported;
   switch (a.L.Dk) {
     case 32: return launch_bits<32, 128>(a, stream);

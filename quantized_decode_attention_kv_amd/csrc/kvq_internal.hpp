@@ -27,6 +27,7 @@ struct DecodeArgs {
   kvq_cache cache;
   float scale;
   int P;
+  int units;           // work units per slab of the matrix-core kernel (set by its launcher)
   float* partials;     // [B * Hq, units, Dv + 4]: m (log2 domain), l, 2 unused, unnormalised o (P > 1)
   float* out;          // [B, Hq, Dv]
 };
