@@ -75,6 +75,44 @@ __device__ __forceinline__ float2 load_pair(const void* p, int64_t i) {
   }
 }
 
+// 16 consecutive elements starting at i (16 * element size bytes, aligned) as
+// raw words (f32: 16 words; 16-bit types: 8 words), converted by cvt16
+template <int DT>
+struct Raw16 {
+  static constexpr int kWords = DT == KVQ_F32 ? 16 : 8;
+  uint32_t w[kWords];
+};
+template <int DT>
+__device__ __forceinline__ Raw16<DT> load16(const void* p, int64_t i) {
+  Raw16<DT> r;
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(p) + i * (DT == KVQ_F32 ? 4 : 2));
+#pragma unroll
+  for (int k = 0; k < Raw16<DT>::kWords / 4; ++k) {
+    const uint4 v = src[k];
+    r.w[4 * k] = v.x;
+    r.w[4 * k + 1] = v.y;
+    r.w[4 * k + 2] = v.z;
+    r.w[4 * k + 3] = v.w;
+  }
+  return r;
+}
+template <int DT>
+__device__ __forceinline__ void cvt16(const Raw16<DT>& r, float (&x)[16]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if constexpr (DT == KVQ_F32) {
+      x[2 * k] = __uint_as_float(r.w[2 * k]);
+      x[2 * k + 1] = __uint_as_float(r.w[2 * k + 1]);
+    } else if constexpr (DT == KVQ_BF16) {
+      x[2 * k] = __uint_as_float(r.w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(r.w[k] & 0xFFFF0000u);
+    } else {
+      x[2 * k] = __half2float(__ushort_as_half(uint16_t(r.w[k] & 0xFFFFu)));
+      x[2 * k + 1] = __half2float(__ushort_as_half(uint16_t(r.w[k] >> 16)));
+    }
+  }
+}
+
 __device__ __forceinline__ uint16_t f16_bits_rne(float x) {
   return __half_as_ushort(__float2half_rn(x));
 }
@@ -147,24 +185,45 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
     // ------------------------------------------------ one key group of 32 tokens
     const int64_t g = a.g_begin + blockIdx.x;
     const int kwords = Dk * KB / 32, vwords = Dv * VB;
-    if (tid < KVQ_GROUP) row_s[tid] = int32_t(quantized_position(rr, g * KVQ_GROUP + tid) - a.t_begin);
+    // rows of the wave's 8 tokens in the chunk: a group wholly below the first
+    // retained position holds positions 32g .. 32g + 31 (one closed-form count
+    // decides it); otherwise each token's position comes from the search
+    const bool plain = quantized_before(rr, (g + 1) * KVQ_GROUP) == (g + 1) * KVQ_GROUP;
+    if (!plain) {
+      if (tid < KVQ_GROUP) row_s[tid] = int32_t(quantized_position(rr, g * KVQ_GROUP + tid) - a.t_begin);
+      __syncthreads();
+    }
+    auto row_of = [&](int tok) -> int32_t {
+      return plain ? int32_t(g * KVQ_GROUP + tok - a.t_begin) : row_s[tok];
+    };
+    int32_t rows[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) rows[t] = row_of(8 * wave + t);
+    // Dv == 128: thread (token tid / 8, 16-channel tile tid % 8) takes its value
+    // row segment now, so that its load latency overlaps the key phase
+    const bool v128 = Dv == 128;
+    const int vtok = tid >> 3, vtile = tid & 7;
+    Raw16<DT> vraw;
+    if (v128) vraw = load16<DT>(a.V, (slab * a.t_count + row_of(vtok)) * 128 + 16 * vtile);
+
     for (int i = tid; i < KVQ_GROUP * kwords; i += kPackThreads) kw_s[i] = 0u;
     for (int i = tid; i < vwords; i += kPackThreads) vw_s[i] = 0u;
-    __syncthreads();
 
-    // keys: lane holds channels (2cp, 2cp+1) of the wave's 8 tokens
+    // keys: lane holds channels (2cp, 2cp+1) of the wave's 8 tokens; per-channel
+    // min / max over them, then across waves
     constexpr float k_levels = float((1 << KB) - 1);
     float2 kx[kMaxPairBlocks][8];
 #pragma unroll
     for (int k = 0; k < kMaxPairBlocks; ++k) {
       const int cp = lane + 64 * k;
       if (2 * cp < Dk) {
-        float2 mn = make_float2(0.0f, 0.0f), mx = mn;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          kx[k][t] = load_pair<DT>(a.K, (slab * a.t_count + row_s[8 * wave + t]) * Dk + 2 * cp);
-          mn = t == 0 ? kx[k][t] : make_float2(fminf(mn.x, kx[k][t].x), fminf(mn.y, kx[k][t].y));
-          mx = t == 0 ? kx[k][t] : make_float2(fmaxf(mx.x, kx[k][t].x), fmaxf(mx.y, kx[k][t].y));
+        for (int t = 0; t < 8; ++t) kx[k][t] = load_pair<DT>(a.K, (slab * a.t_count + rows[t]) * Dk + 2 * cp);
+        float2 mn = kx[k][0], mx = kx[k][0];
+#pragma unroll
+        for (int t = 1; t < 8; ++t) {
+          mn = make_float2(fminf(mn.x, kx[k][t].x), fminf(mn.y, kx[k][t].y));
+          mx = make_float2(fmaxf(mx.x, kx[k][t].x), fmaxf(mx.y, kx[k][t].y));
         }
         kmn_s[wave][2 * cp] = mn.x;
         kmn_s[wave][2 * cp + 1] = mn.y;
@@ -210,11 +269,36 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
       }
     }
 
-    // values: per (token, 32-channel group); lanes 16r..16r+15 of a pair block
-    // hold one group
+    // values: per (token, 32-channel group)
     constexpr float v_levels = float((1 << VB) - 1);
+    if (v128) {
+      // the thread's 16 channels are one half of a 32-channel group (the other
+      // half is the neighbouring lane) and one 16-channel tile of the code stream:
+      // their codes sit at one bit offset in words 2 * VB apart
+      float x[16];
+      cvt16<DT>(vraw, x);
+      float mn = x[0], mx = x[0];
 #pragma unroll
-    for (int k = 0; k < kMaxPairBlocks; ++k) {
+      for (int k = 1; k < 16; ++k) {
+        mn = fminf(mn, x[k]);
+        mx = fmaxf(mx, x[k]);
+      }
+      mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xF, 0xF, false)));
+      const QParams q = make_qparams(mn, mx, v_levels);
+      if ((vtile & 1) == 0) {
+        vs_s[vtile >> 1][vtok] = q.s_bits;
+        vz_s[vtile >> 1][vtok] = q.z_bits;
+      }
+      const int p0 = value_bit_position(vtok, 16 * vtile, 128, VB);
+      const int w0 = p0 >> 5, sh = p0 & 31;
+#pragma unroll
+      for (int n = 0; n < 16; ++n)
+        atomicOr(&vw_s[w0 + n * 2 * VB], quant_code(x[n], q.s, q.z, q.r, v_levels) << sh);
+    }
+    // other head widths: lanes 16r..16r+15 of a pair block hold one group
+#pragma unroll
+    for (int k = 0; k < kMaxPairBlocks && !v128; ++k) {
       const int cp = lane + 64 * k;
       if (128 * k < Dv) {  // wave-uniform: the pair block reaches into the head
         const bool on = 2 * cp < Dv;
@@ -222,7 +306,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int tok = 8 * wave + t;
-          const float2 x = on ? load_pair<DT>(a.V, (slab * a.t_count + row_s[tok]) * Dv + 2 * cp)
+          const float2 x = on ? load_pair<DT>(a.V, (slab * a.t_count + rows[t]) * Dv + 2 * cp)
                               : make_float2(0.0f, 0.0f);
           const float mn = row16_reduce<false>(fminf(x.x, x.y));
           const float mx = row16_reduce<true>(fmaxf(x.x, x.y));
