@@ -245,33 +245,40 @@ __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t (&w)[NB < 
   }
 }
 
-// LDS of one workgroup (one wave), in bytes: 10 KB for the common shapes, so
-// that 16 waves fit on a compute unit.
-//   QB  Q' operand tile, KK chunks of 32 channels; holds the q hi/lo operand B2
-//       during set-up and the retained rows;
-//   PA  P' operand tile; shares the Q' tile when it fits there (within a group
-//       the Q' operand is consumed before P' is written, and P' before the next
-//       group's Q');
-//   ring of two staging slots, one key group each: key codes, value codes, key
-//       scales, value scales, value zeros, key zeros.  Slot 1 holds the scaled
-//       query during set-up and the retained-row probabilities before it is
-//       first filled; the ring holds the output accumulator and the value
-//       zero-point sums at the end.
+// Key groups a wave computes per step: their dependency chains interleave and one
+// set of LDS round trips serves all of them.
+#ifndef KVQ_DECODE_GPS
+#define KVQ_DECODE_GPS 1
+#endif
+constexpr int kGps = KVQ_DECODE_GPS;
+
+// LDS of one workgroup (one wave), in bytes (20 KB for the common shapes: 8
+// waves per compute unit):
+//   QB  kGps Q' operand tiles, KK chunks of 32 channels each; the first holds the
+//       q hi/lo operand B2 for the retained rows;
+//   PA  kGps P' operand tiles; they share the Q' tiles when they fit there
+//       (within a step the Q' operands are consumed before P' is written, and
+//       P' before the next step's Q');
+//   ring of 2 * kGps staging slots, one key group each: key codes, value codes,
+//       key scales, key zeros, value scales, value zeros.  At the end the ring
+//       holds the retained-row probabilities, then the output accumulator and
+//       the value zero-point sums.
 template <int DK, int DV, int KB, int VB>
 struct Lds {
   static constexpr int KK = DK / 32, NGV = DV / 32;
-  static constexpr int kQB = KK * 32 * 16;
-  static constexpr int kPA = NGV * 32 * 16;
+  static constexpr int kQB1 = KK * 32 * 16;   // one Q' tile
+  static constexpr int kPA1 = NGV * 32 * 16;  // one P' tile
   static constexpr int kStK = 32 * DK * KB / 8;
   static constexpr int kStV = 32 * DV * VB / 8;
   static constexpr int kStS = 256;
   static constexpr int kStage = kStK + kStV + 4 * kStS;
-  static constexpr bool kShare = kPA <= kQB;
-  static constexpr int oQB = 0, oPA = kShare ? 0 : kQB;
-  static constexpr int oRing = kShare ? kQB : kQB + kPA;
-  static constexpr int oLast = oRing + kStage;
-  static constexpr int kBytes = oRing + 2 * kStage;
-  static_assert(kG * DK * 4 <= kStage && kG * 32 * 4 <= kStage && kG * (DV + NGV) * 4 <= 2 * kStage, "aliases");
+  static constexpr bool kShare = kPA1 <= kQB1;
+  static constexpr int oQB = 0, oPA = kShare ? 0 : kGps * kQB1;
+  static constexpr int kPAStride = kShare ? kQB1 : kPA1;  // bytes between P' tiles
+  static constexpr int oRing = kShare ? kGps * kQB1 : kGps * (kQB1 + kPA1);
+  static constexpr int kSlots = 2 * kGps;
+  static constexpr int kBytes = oRing + kSlots * kStage;
+  static_assert(kG * 32 * 4 <= kSlots * kStage && kG * (DV + NGV) * 4 <= kSlots * kStage, "aliases");
 };
 
 // 8 consecutive query elements starting at i0 (a multiple of 8; the array is
@@ -333,22 +340,24 @@ __device__ __forceinline__ float pick4(const float (&x)[kG], int i) {
 // One workgroup = one wave = one unit: a contiguous piece of a split-K partition
 // of one (batch, kv head) slab (the whole slab when P == 1).  Units are
 // independent: no barriers, and each writes its own partial result.
-// First key group of unit u of U over nG groups.  The workgroup dispatcher fills
-// the SIMDs round-robin in grid order, so with the unit-major grid the units
-// u < U/4 become the oldest wave on their SIMD, the next quarter the second
-// oldest, and so on; waves are served oldest first, so unit sizes fall by
-// quarter (integer weights 100 + s (3 - 2 r) for quarter r) and the waves of a
-// SIMD finish together.  Any weights give the same result up to rounding.
+// First key group of unit u of U over nG groups, for R waves per SIMD.  The
+// workgroup dispatcher fills the SIMDs round-robin in grid order, so with the
+// unit-major grid and one unit per resident wave the units u < U/R become the
+// oldest wave on their SIMD, the next U/R the second oldest, and so on; waves are
+// served oldest first, so unit sizes fall by rank (integer weights
+// 100 + s (R - 1 - 2 r) for rank r) and the waves of a SIMD finish closer
+// together.  Any weights give the same result up to rounding.
 #ifndef KVQ_UNIT_SKEW
 #define KVQ_UNIT_SKEW 6
 #endif
+template <int R>
 __device__ __forceinline__ int unit_start(int u, int U, int nG) {
   constexpr int64_t s = KVQ_UNIT_SKEW;
   int64_t wu = 0, wall = 0;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t lo = (int64_t(r) * U + 3) / 4, hi = (int64_t(r + 1) * U + 3) / 4;  // units of quarter r
-    const int64_t w = 100 + s * (3 - 2 * r);
+  for (int r = 0; r < R; ++r) {
+    const int64_t lo = (int64_t(r) * U + R - 1) / R, hi = (int64_t(r + 1) * U + R - 1) / R;  // units of rank r
+    const int64_t w = 100 + s * (R - 1 - 2 * r);
     wall += w * (hi - lo);
     wu += w * (u < lo ? 0 : (u < hi ? u - lo : hi - lo));
   }
@@ -380,9 +389,9 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   static_assert(DV == 128 && NV % TPW == 0 && KLB >= 4 && DK % 32 == 0 && DK <= 128, "shape");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  u32x4* QB = reinterpret_cast<u32x4*>(smem + LL::oQB);       // [(KK+1)*4][8]
-  u32x4* PA = reinterpret_cast<u32x4*>(smem + LL::oPA);       // [NGV*4][8]
-  unsigned char* stage = smem + LL::oRing;                    // [2][kStage]
+  u32x4* QB = reinterpret_cast<u32x4*>(smem + LL::oQB);       // [kGps][KK*4][8]
+  u32x4* PA = reinterpret_cast<u32x4*>(smem + LL::oPA);       // [kGps][NGV*4][8], stride kPAStride
+  unsigned char* stage = smem + LL::oRing;                    // [2 kGps][kStage]
   u32x4* B2 = QB;                                             // q hi/lo, retained rows
   float* PT = reinterpret_cast<float*>(stage);                // [4][32], retained rows
   const int lane = threadIdx.x, n = lane & 15, gq = lane >> 4;
@@ -393,7 +402,8 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   const int h = sl % a.L.Hkv, b = sl / a.L.Hkv;
   const int nG = a.L.n_groups, R = a.L.R;
   const int64_t slab = int64_t(b) * a.L.Hkv + h;
-  const int g0 = unit_start(unit, U, nG), g1 = unit_start(unit + 1, U, nG);
+  constexpr int kRanks = lds_waves_per_simd<DK, DV, KB, VB>();
+  const int g0 = unit_start<kRanks>(unit, U, nG), g1 = unit_start<kRanks>(unit + 1, U, nG);
   const int nRT = (R + 31) / 32;  // 32-row tiles of retained rows
   const int rt0 = int(int64_t(unit) * nRT / U), rt1 = int(int64_t(unit + 1) * nRT / U);
   const int nj = g1 - g0;
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   constexpr int kDmas = 2 * KNP + VNP + 4;  // copies per group
   constexpr int oKZ = LL::kStS, oVS = 2 * LL::kStS, oVZ = 3 * LL::kStS;  // scale area offsets
   static_assert(DK * 2 <= LL::kStS && DV * 2 == LL::kStS, "scale area");
-  static_assert(kDmas < 64, "vmcnt");
+  static_assert(kDmas * kGps < 64, "vmcnt");
   static_assert(KLB % KPB == 0 && VLW % 4 == 0 && DK / 8 <= 64 && 4 * NGV <= 64, "staging");
   // per-lane byte offsets inside a group (the group base itself is wave-uniform)
   uint32_t koff[2];
@@ -467,8 +477,9 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   };
   // The query first (vector-memory operations complete in order, so it would
   // otherwise wait for the staged groups): the 8 elements of the lane's Q' task.
-  // Then groups 0 and 1 into the two slots (a unit with a single group stages it
-  // twice; a unit without groups issues copies that touch no memory).
+  // Then the groups of the first two steps into the ring (a unit with fewer
+  // groups re-reads its last one; a unit without groups issues copies that touch
+  // no memory).
   // Raw bytes, converted only after the copies are issued (a conversion next to
   // the load would make the wave wait for it first); the buffer spans the kG
   // query rows of this KV head, so the 32-byte read of a 16-bit query stays inside.
@@ -478,8 +489,8 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   const uint32_t qoff = uint32_t(i_t * DK + 8 * tb) * uint32_t(qesz);
   const u32x4 qw0 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff, 0, 0);
   const u32x4 qw1 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 16, 0, 0);
-  stage_group(g0, 0);
-  stage_group(g0 + (nj > 1 ? 1 : 0), 1);
+#pragma unroll
+  for (int u = 0; u < 2 * kGps; ++u) stage_group(g0 + min(u, nj > 0 ? nj - 1 : 0), u);
   __builtin_amdgcn_sched_barrier(0);
   float qx[8];
   if (a.q_dtype == KVQ_BF16) {
@@ -559,27 +570,27 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
 #pragma unroll
   for (int i = 0; i < kG; ++i) o_r[i][0] = o_r[i][1] = 0.0f;
 
-  // Softmax update of 8 new scores per lane: v = raw MFMA outputs, score =
-  // v * coef + bias (log2 domain).  Returns the probabilities relative to the
-  // (possibly moved) reference maximum; rescale_acc(alpha) rescales the value
-  // accumulators when a reference moves.
-  auto softmax_step = [&](const float (&v)[8], float coef, float bias, float (&pv)[8], auto&& rescale_acc) {
-    const float bterm = bias - m_lane;
-    float sv[8];
+  // Softmax update of 8 new scores per lane and key group: v = raw MFMA outputs,
+  // score = v * coef + bias of the group (log2 domain).  Returns the
+  // probabilities relative to the (possibly moved) reference maximum;
+  // rescale_acc(alpha) rescales the value accumulators when a reference moves.
+  auto softmax_step = [&](const auto& v, float coef, const auto& bias, auto& pv, auto&& rescale_acc) {
+    constexpr int N = sizeof(v) / sizeof(float);
+    float sv[N];
     float mloc = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      sv[k] = fmaf(v[k], coef, bterm);
+    for (int k = 0; k < N; ++k) {
+      sv[k] = fmaf(v[k], coef, bias[k / 8] - m_lane);
       mloc = fmaxf(mloc, sv[k]);
     }
     if (__builtin_expect(__any(mloc > float(kHeadroom)), 0)) {
       // some score left the headroom: move those references to the group maxima
       // (queries repeat every 4 columns; the 4 lane groups hold different tokens)
-      float sabs[8];
+      float sabs[N];
       float mab = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        sabs[k] = fmaf(v[k], coef, bias);
+      for (int k = 0; k < N; ++k) {
+        sabs[k] = fmaf(v[k], coef, bias[k / 8]);
         mab = fmaxf(mab, sabs[k]);
       }
       float alpha[kG];
@@ -605,10 +616,10 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
       zacc *= al;
       rescale_acc(alpha);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sv[k] = sabs[k] - m_lane;
+      for (int k = 0; k < N; ++k) sv[k] = sabs[k] - m_lane;
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < N; ++k) {
       pv[k] = fast_exp2(sv[k]);
       l_run += pv[k];
     }
@@ -666,90 +677,121 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
     d.vz = *reinterpret_cast<const u32x4*>(ss + oVZ + (gcP * 4 + gq) * 16);
   };
 
-  auto process_group = [&](const GroupLoads& d) {
+  // One step: kGps key groups (valid[g] false: a stand-in whose scores are
+  // masked, for the end of an odd run).
+  auto process_step = [&](const GroupLoads (&d)[kGps], const bool (&valid)[kGps]) {
     if (qtask) {
-      u32x4 hi, lo;
-      split8(qsv, d.ks, hi, lo);
-      QB[qb_entry] = hi;
-      QB[qb_entry + 4] = lo;
-    }
-    wave_lds_sync();
-    f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const u32x4 bq = QB[(kk * 4 + gq) * 8 + 4 * part + iq];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(key_field<KB>(d.kw[tt], kk), bq, sacc[tt]);
+      for (int g = 0; g < kGps; ++g) {
+        u32x4 hi, lo;
+        split8(qsv, d[g].ks, hi, lo);
+        QB[g * (KK * 32) + qb_entry] = hi;
+        QB[g * (KK * 32) + qb_entry + 4] = lo;
       }
     }
-    float v[8], pv[8];
+    float bias[kGps];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int g = 0; g < kGps; ++g) bias[g] = zero_term(d[g].kz) * coefB;
+    wave_lds_sync();
+    float v[8 * kGps], pv[8 * kGps];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * tt + r] = sacc[tt][r];
+    for (int g = 0; g < kGps; ++g) {
+      f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const u32x4 bq = QB[g * (KK * 32) + (kk * 4 + gq) * 8 + 4 * part + iq];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(key_field<KB>(d[g].kw[tt], kk), bq, sacc[tt]);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[8 * g + 4 * tt + r] = valid[g] ? sacc[tt][r] : -INFINITY;
+      }
     }
-    softmax_step(v, coefD, zero_term(d.kz) * coefB, pv, rescale_groups);
+    softmax_step(v, coefD, bias, pv, rescale_groups);
 
-    // P' = p s (hi, lo) for the lane's (query, channel group, octet) and the
-    // zero-point sum of the same task
-    {
+    // P' = p s (hi, lo) for the lane's (query, channel group, octet) of each
+    // group and the zero-point sums of the same tasks
+#pragma unroll
+    for (int g = 0; g < kGps; ++g) {
       u32x4 hi, lo;
-      split8(pv, d.vs, hi, lo);
-      PA[pa_entry] = hi;
-      PA[pa_entry + 4] = lo;
+      float pg[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pg[k] = pv[8 * g + k];
+      split8(pg, d[g].vs, hi, lo);
+      u32x4* pa = reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(PA) + g * LL::kPAStride);
+      pa[pa_entry] = hi;
+      pa[pa_entry + 4] = lo;
       float zs = 0.0f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const half2_t zz = as_half2(d.vz[k >> 1]);
-        zs = fmaf(pv[k], float(zz[k & 1]), zs);
+        const half2_t zz = as_half2(d[g].vz[k >> 1]);
+        zs = fmaf(pg[k], float(zz[k & 1]), zs);
       }
       zacc += zs;
     }
     wave_lds_sync();
 #pragma unroll
-    for (int gc = 0; gc < NGV; ++gc) {
-      const u32x4 ap = PA[(gc * 4 + gq) * 8 + (n & 7)];
+    for (int g = 0; g < kGps; ++g) {
+      const u32x4* pa = reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(PA) + g * LL::kPAStride);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int t = 2 * gc + half;
-        const int chunk = t / TPW, sh = value_tile_shift<VB>(t % TPW);
-        const bool down = (t % TPW) * VB != sh;
-        u32x4 bv;
+      for (int gc = 0; gc < NGV; ++gc) {
+        const u32x4 ap = pa[(gc * 4 + gq) * 8 + (n & 7)];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t w = d.vw[m * NCH + chunk];
-          bv[m] = (down ? w >> 8 : w) & (kVMask << sh);
+        for (int half = 0; half < 2; ++half) {
+          const int t = 2 * gc + half;
+          const int chunk = t / TPW, sh = value_tile_shift<VB>(t % TPW);
+          const bool down = (t % TPW) * VB != sh;
+          u32x4 bv;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t w = d[g].vw[m * NCH + chunk];
+            bv[m] = (down ? w >> 8 : w) & (kVMask << sh);
+          }
+          oacc[t] = mfma16(ap, bv, oacc[t]);
         }
-        oacc[t] = mfma16(ap, bv, oacc[t]);
       }
     }
   };
 
   {
-    // Two staging slots: group j sits in slot j % 2.  As soon as group j has been
-    // read into registers its slot takes the copies of group j + 2, so groups
-    // j + 1 and j + 2 are in flight while group j is computed.
-    // Issue priority falls by one level per quarter of the unit's groups: the
+    // Steps of kGps groups: step i takes groups kGps i .. kGps i + kGps - 1 from
+    // slot half i % 2 of the ring.  As soon as a step's groups have been read into
+    // registers their slots take the copies of step i + 2, so steps i + 1 and
+    // i + 2 are in flight while step i is computed (past the end of the run the
+    // copies re-read its last group, which is always in bounds).
+    // Issue priority falls by one level per quarter of the unit's steps: the
     // waves of a SIMD are otherwise served oldest first and would finish far
     // apart; this way a wave that is ahead yields to the ones behind it.
+    const int ns = (nj + kGps - 1) / kGps;
     __builtin_amdgcn_s_setprio(3);
-    const int q1 = nj / 4, q2 = nj / 2, q3 = (3 * nj) / 4;
-    for (int j = 0; j < nj; ++j) {
-      const int slot = j & 1;
-      if (j == q1) __builtin_amdgcn_s_setprio(2);
-      if (j == q2) __builtin_amdgcn_s_setprio(1);
-      if (j == q3) __builtin_amdgcn_s_setprio(0);
-      if (j + 1 < nj)
-        wait_vmcnt<kDmas>();
+    const int q1 = ns / 4, q2 = ns / 2, q3 = (3 * ns) / 4;
+    for (int i = 0; i < ns; ++i) {
+      const int half = i & 1;
+      if (i == q1) __builtin_amdgcn_s_setprio(2);
+      if (i == q2) __builtin_amdgcn_s_setprio(1);
+      if (i == q3) __builtin_amdgcn_s_setprio(0);
+      if (i + 1 < ns)
+        wait_vmcnt<kDmas * kGps>();
       else
         wait_vmcnt<0>();
-      GroupLoads d;
-      read_group(slot, d);
+      GroupLoads d[kGps];
+      bool valid[kGps];
+#pragma unroll
+      for (int g = 0; g < kGps; ++g) {
+        read_group(half * kGps + g, d[g]);
+        valid[g] = kGps * i + g < nj;
+      }
       wave_lds_sync();
-      if (j + 2 < nj) stage_group(g0 + j + 2, slot);
-      process_group(d);
+      if (i + 2 < ns) {
+#pragma unroll
+        for (int g = 0; g < kGps; ++g) stage_group(g0 + min(kGps * (i + 2) + g, nj - 1), half * kGps + g);
+      }
+      process_step(d, valid);
     }
   }
 
@@ -799,7 +841,8 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[4 * tt + r] = rbase + 8 * gq + 4 * tt + r < R ? sacc[tt][r] : -INFINITY;
       }
-      softmax_step(v, coefB, 0.0f, pv, rescale_groups);
+      const float no_bias[1] = {0.0f};
+      softmax_step(v, coefB, no_bias, pv, rescale_groups);
       if (n < kG) {
         *reinterpret_cast<f32x4*>(PT + n * 32 + 8 * gq) = f32x4{pv[0], pv[1], pv[2], pv[3]};
         *reinterpret_cast<f32x4*>(PT + n * 32 + 8 * gq + 4) = f32x4{pv[4], pv[5], pv[6], pv[7]};
@@ -888,21 +931,29 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
 }
 
 template <int DK, int DV, int KB, int VB>
-hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_one(DecodeArgs a, hipStream_t stream, int cus, int* parts) {
   constexpr size_t lds = Lds<DK, DV, KB, VB>::kBytes;
   static_assert(lds <= 64 * 1024, "LDS budget");
+  // Units are cut only as far as 8 waves per compute unit: measured on the 128K
+  // workload, 2048 long runs stream HBM better than 4096 half-length ones (the
+  // memory system serves the larger set of requests less evenly), and the
+  // kernel still holds two waves per SIMD.
+  const int per_cu = 4 * lds_waves_per_simd<DK, DV, KB, VB>();
+  a.units = decode_mfma_units(a.L, a.P, int64_t(cus) * (per_cu < 8 ? per_cu : 8));
+  *parts = a.units;
+  if (int64_t(a.units) * a.L.B * a.L.Hkv >= (int64_t(1) << 31)) return hipErrorNotSupported;
   const dim3 grid(unsigned(a.units) * unsigned(a.L.B) * unsigned(a.L.Hkv));
   hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, KB, VB>), grid, dim3(64), lds, stream, a);
   return hipGetLastError();
 }
 
 template <int DK, int DV>
-hipError_t launch_bits(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_bits(const DecodeArgs& a, hipStream_t stream, int cus, int* parts) {
   const int kb = a.L.k_bits, vb = a.L.v_bits;
   // key rows must give every lane at least 4 bytes of a tile (staged as dwords)
 #define KVQ_BITS_CASE(K_, V_)                                             \
   if constexpr (DK * K_ / 32 >= 4) {                                      \
-    if (kb == K_ && vb == V_) return launch_one<DK, DV, K_, V_>(a, stream); \
+    if (kb == K_ && vb == V_) return launch_one<DK, DV, K_, V_>(a, stream, cus, parts); \
   }
   KVQ_BITS_CASE(2, 2) KVQ_BITS_CASE(2, 4) KVQ_BITS_CASE(2, 8)
   KVQ_BITS_CASE(4, 2) KVQ_BITS_CASE(4, 4) KVQ_BITS_CASE(4, 8)
@@ -913,20 +964,21 @@ hipError_t launch_bits(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a_in, hipStream_t stream, int* parts) {
-  DecodeArgs a = a_in;
-  a.units = decode_mfma_units(a.L, a.P);
-  *parts = a.units;
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream, int* parts) {
+  *parts = a.P;
   if (a.L.Hq != kG * a.L.Hkv || a.L.Dv != 128) return hipErrorNotSupported;
-  // per-slab offsets are 32-bit in this kernel, and so is the grid
+  // per-slab offsets are 32-bit in this kernel
   const int64_t widest = a.L.Dk > a.L.Dv ? a.L.Dk : a.L.Dv;
-  if (int64_t(a.L.Tq) * widest >= (int64_t(1) << 31) || int64_t(a.L.R) * widest * 2 >= (int64_t(1) << 31) ||
-      int64_t(a.units) * a.L.B * a.L.Hkv >= (int64_t(1) << 31))
+  if (int64_t(a.L.Tq) * widest >= (int64_t(1) << 31) || int64_t(a.L.R) * widest * 2 >= (int64_t(1) << 31))
     return hipErrorNotSupported;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
   switch (a.L.Dk) {
-    case 32: return launch_bits<32, 128>(a, stream);
-    case 64: return launch_bits<64, 128>(a, stream);
-    case 128: return launch_bits<128, 128>(a, stream);
+    case 32: return launch_bits<32, 128>(a, stream, cus, parts);
+    case 64: return launch_bits<64, 128>(a, stream, cus, parts);
+    case 128: return launch_bits<128, 128>(a, stream, cus, parts);
     default: return hipErrorNotSupported;
   }
 }

@@ -33,21 +33,17 @@ struct DecodeArgs {
 };
 
 // Work units of the matrix-core decode kernel: each of the P split-K partitions
-// is cut into c = 1, 2 or 4 contiguous pieces, one single-wave workgroup each.
-// c is the largest that keeps the grid within kUnitWaves waves (about what the
-// device holds at once), so short caches still fill the chip while long ones
-// keep each wave on a long run of key groups.  P == 1 is one unit, which
-// writes the output directly.
+// is cut into c = 1, 2 or 4 contiguous runs, one single-wave workgroup each.  c
+// is the largest that keeps the grid within `resident` waves (what the device
+// holds at once for the kernel's occupancy), so short caches still fill the chip
+// while long ones keep each wave on a long run of key groups.  P == 1 is one
+// unit, which writes the output directly.
 constexpr int kMaxUnitsPerPartition = 4;
-#ifndef KVQ_UNIT_WAVES
-#define KVQ_UNIT_WAVES 4096
-#endif
-constexpr int64_t kUnitWaves = KVQ_UNIT_WAVES;
-inline int decode_mfma_units(const kvq_layout& L, int P) {
+inline int decode_mfma_units(const kvq_layout& L, int P, int64_t resident) {
   if (P == 1) return 1;
   const int64_t slabs = int64_t(L.B) * L.Hkv;
   int c = kMaxUnitsPerPartition;
-  while (c > 1 && slabs * P * c > kUnitWaves) c >>= 1;
+  while (c > 1 && slabs * P * c > resident) c >>= 1;
   return c * P;
 }
 
