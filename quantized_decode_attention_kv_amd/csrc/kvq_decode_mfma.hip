@@ -49,6 +49,8 @@
 //      one shift per word for the slots above the mantissa).
 // Retained fp16 rows (recent window, log-spaced tokens) are folded into the same
 // online state first: scores on the MFMA (A = fp16 key rows), values on the VALU.
+#include <algorithm>
+
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -75,6 +77,11 @@ constexpr int kHeadroom = 4;
 // Order LDS traffic of one wave: wait for its outstanding LDS operations; the
 // memory clobber keeps the compiler from moving LDS accesses across.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Order LDS accesses of one wave without waiting: the LDS unit executes a wave's
+// ds_ operations in issue order, so a read issued after a write (or a write
+// after a read) of the same wave sees the right data; only the compiler must not
+// move the accesses across (it would, between lanes' different addresses).
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0,
@@ -119,6 +126,20 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `ahead` (0..A) later steps of PER copies each are in
+// flight: the counter bound must be an immediate, so the cases are spelled out.
+template <int PER, int A>
+__device__ __forceinline__ void wait_steps_ahead(int ahead) {
+  if constexpr (A == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= A)
+      wait_vmcnt<PER * A>();
+    else
+      wait_steps_ahead<PER, A - 1>(ahead);
+  }
 }
 
 // ---------------------------------------------------------------- fp16 hi/lo split
@@ -259,11 +280,12 @@ constexpr int kGps = KVQ_DECODE_GPS;
 //   PA  kGps P' operand tiles; they share the Q' tiles when they fit there
 //       (within a step the Q' operands are consumed before P' is written, and
 //       P' before the next step's Q');
-//   ring of 2 * kGps staging slots, one key group each: key codes, value codes,
+//   ring of D * kGps staging slots (D steps in flight), one key group each: key
+//       codes, value codes,
 //       key scales, key zeros, value scales, value zeros.  At the end the ring
 //       holds the retained-row probabilities, then the output accumulator and
 //       the value zero-point sums.
-template <int DK, int DV, int KB, int VB>
+template <int DK, int DV, int KB, int VB, int D>
 struct Lds {
   static constexpr int KK = DK / 32, NGV = DV / 32;
   static constexpr int kQB1 = KK * 32 * 16;   // one Q' tile
@@ -276,7 +298,7 @@ struct Lds {
   static constexpr int oQB = 0, oPA = kShare ? 0 : kGps * kQB1;
   static constexpr int kPAStride = kShare ? kQB1 : kPA1;  // bytes between P' tiles
   static constexpr int oRing = kShare ? kGps * kQB1 : kGps * (kQB1 + kPA1);
-  static constexpr int kSlots = 2 * kGps;
+  static constexpr int kSlots = D * kGps;
   static constexpr int kBytes = oRing + kSlots * kStage;
   static_assert(kG * 32 * 4 <= kSlots * kStage && kG * (DV + NGV) * 4 <= kSlots * kStage, "aliases");
 };
@@ -350,11 +372,9 @@ __device__ __forceinline__ float pick4(const float (&x)[kG], int i) {
 #ifndef KVQ_UNIT_SKEW
 #define KVQ_UNIT_SKEW 6
 #endif
-template <int R>
-__device__ __forceinline__ int unit_start(int u, int U, int nG) {
+__device__ __forceinline__ int unit_start(int u, int U, int nG, int R) {
   constexpr int64_t s = KVQ_UNIT_SKEW;
   int64_t wu = 0, wall = 0;
-#pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t lo = (int64_t(r) * U + R - 1) / R, hi = (int64_t(r + 1) * U + R - 1) / R;  // units of rank r
     const int64_t w = 100 + s * (R - 1 - 2 * r);
@@ -367,15 +387,15 @@ __device__ __forceinline__ int unit_start(int u, int U, int nG) {
 // Waves per SIMD that the LDS of one unit allows on a 160 KB compute unit (at most
 // 4, which is the 16 waves per CU of the common shapes); the register budget
 // is set to match, so registers never limit occupancy below what LDS allows.
-template <int DK, int DV, int KB, int VB>
+template <int DK, int DV, int KB, int VB, int D>
 constexpr int lds_waves_per_simd() {
-  const int per_cu = (160 * 1024) / Lds<DK, DV, KB, VB>::kBytes;
+  const int per_cu = (160 * 1024) / Lds<DK, DV, KB, VB, D>::kBytes;
   return per_cu >= 16 ? 4 : (per_cu >= 4 ? per_cu / 4 : 1);
 }
 
-template <int DK, int DV, int KB, int VB>
-__global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void decode_mfma_kernel(const DecodeArgs a) {
-  using LL = Lds<DK, DV, KB, VB>;
+template <int DK, int DV, int KB, int VB, int D>
+__global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void decode_mfma_kernel(const DecodeArgs a) {
+  using LL = Lds<DK, DV, KB, VB, D>;
   constexpr int KK = DK / 32;          // 32-channel score steps
   constexpr int NV = DV / 16;          // 16-channel value tiles
   constexpr int NGV = DV / 32;         // 32-channel value groups
@@ -391,7 +411,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   extern __shared__ __align__(16) unsigned char smem[];
   u32x4* QB = reinterpret_cast<u32x4*>(smem + LL::oQB);       // [kGps][KK*4][8]
   u32x4* PA = reinterpret_cast<u32x4*>(smem + LL::oPA);       // [kGps][NGV*4][8], stride kPAStride
-  unsigned char* stage = smem + LL::oRing;                    // [2 kGps][kStage]
+  unsigned char* stage = smem + LL::oRing;                    // [D kGps][kStage]
   u32x4* B2 = QB;                                             // q hi/lo, retained rows
   float* PT = reinterpret_cast<float*>(stage);                // [4][32], retained rows
   const int lane = threadIdx.x, n = lane & 15, gq = lane >> 4;
@@ -402,8 +422,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   const int h = sl % a.L.Hkv, b = sl / a.L.Hkv;
   const int nG = a.L.n_groups, R = a.L.R;
   const int64_t slab = int64_t(b) * a.L.Hkv + h;
-  constexpr int kRanks = lds_waves_per_simd<DK, DV, KB, VB>();
-  const int g0 = unit_start<kRanks>(unit, U, nG), g1 = unit_start<kRanks>(unit + 1, U, nG);
+  const int g0 = unit_start(unit, U, nG, a.ranks), g1 = unit_start(unit + 1, U, nG, a.ranks);
   const int nRT = (R + 31) / 32;  // 32-row tiles of retained rows
   const int rt0 = int(int64_t(unit) * nRT / U), rt1 = int(int64_t(unit + 1) * nRT / U);
   const int nj = g1 - g0;
@@ -442,7 +461,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   constexpr int kDmas = 2 * KNP + VNP + 4;  // copies per group
   constexpr int oKZ = LL::kStS, oVS = 2 * LL::kStS, oVZ = 3 * LL::kStS;  // scale area offsets
   static_assert(DK * 2 <= LL::kStS && DV * 2 == LL::kStS, "scale area");
-  static_assert(kDmas * kGps < 64, "vmcnt");
+  static_assert((D - 1) * kDmas * kGps < 64 && D >= 2, "vmcnt");
   static_assert(KLB % KPB == 0 && VLW % 4 == 0 && DK / 8 <= 64 && 4 * NGV <= 64, "staging");
   // per-lane byte offsets inside a group (the group base itself is wave-uniform)
   uint32_t koff[2];
@@ -477,7 +496,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   };
   // The query first (vector-memory operations complete in order, so it would
   // otherwise wait for the staged groups): the 8 elements of the lane's Q' task.
-  // Then the groups of the first two steps into the ring (a unit with fewer
+  // Then the groups of the first D steps into the ring (a unit with fewer
   // groups re-reads its last one; a unit without groups issues copies that touch
   // no memory).
   // Raw bytes, converted only after the copies are issued (a conversion next to
@@ -490,7 +509,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   const u32x4 qw0 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff, 0, 0);
   const u32x4 qw1 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 16, 0, 0);
 #pragma unroll
-  for (int u = 0; u < 2 * kGps; ++u) stage_group(g0 + min(u, nj > 0 ? nj - 1 : 0), u);
+  for (int u = 0; u < D * kGps; ++u) stage_group(g0 + min(u, nj > 0 ? nj - 1 : 0), u);
   __builtin_amdgcn_sched_barrier(0);
   float qx[8];
   if (a.q_dtype == KVQ_BF16) {
@@ -692,7 +711,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
     float bias[kGps];
 #pragma unroll
     for (int g = 0; g < kGps; ++g) bias[g] = zero_term(d[g].kz) * coefB;
-    wave_lds_sync();
+    wave_lds_order();
     float v[8 * kGps], pv[8 * kGps];
 #pragma unroll
     for (int g = 0; g < kGps; ++g) {
@@ -734,7 +753,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
       }
       zacc += zs;
     }
-    wave_lds_sync();
+    wave_lds_order();
 #pragma unroll
     for (int g = 0; g < kGps; ++g) {
       const u32x4* pa = reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(PA) + g * LL::kPAStride);
@@ -760,10 +779,15 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
 
   {
     // Steps of kGps groups: step i takes groups kGps i .. kGps i + kGps - 1 from
-    // slot half i % 2 of the ring.  As soon as a step's groups have been read into
-    // registers their slots take the copies of step i + 2, so steps i + 1 and
-    // i + 2 are in flight while step i is computed (past the end of the run the
-    // copies re-read its last group, which is always in bounds).
+    // ring position i % D.  The prologue filled positions 0 .. D - 1.  With D > 2
+    // the copies of step i - 1 + D go to the position step i - 1 was read from,
+    // once step i has been waited for: those reads have been consumed, so no wait
+    // on LDS is needed, and steps i + 1 .. i + D - 2 stay in flight while step i
+    // is computed.  With D == 2 step i's own position takes the copies of step
+    // i + 2 right after it has been read (after a wait for the reads).  Past the
+    // end of a short run the prologue re-reads its last group, which is always
+    // in bounds.  The last step waits for all copies, so the ring is idle
+    // afterwards.
     // Issue priority falls by one level per quarter of the unit's steps: the
     // waves of a SIMD are otherwise served oldest first and would finish far
     // apart; this way a wave that is ahead yields to the ones behind it.
@@ -771,28 +795,41 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
     __builtin_amdgcn_s_setprio(3);
     const int q1 = ns / 4, q2 = ns / 2, q3 = (3 * ns) / 4;
     for (int i = 0; i < ns; ++i) {
-      const int half = i & 1;
+      const int pos = i % D;
       if (i == q1) __builtin_amdgcn_s_setprio(2);
       if (i == q2) __builtin_amdgcn_s_setprio(1);
       if (i == q3) __builtin_amdgcn_s_setprio(0);
-      if (i + 1 < ns)
-        wait_vmcnt<kDmas * kGps>();
-      else
-        wait_vmcnt<0>();
+      if constexpr (D > 2) {
+        // copies issued beyond step i: the prologue's D - 1 at i == 0, later at
+        // most D - 2 (fewer near the end of the run)
+        wait_steps_ahead<kDmas * kGps, D - 1>(i == 0 ? min(D - 1, ns - 1) : min(D - 2, ns - 1 - i));
+      } else {
+        wait_steps_ahead<kDmas * kGps, D - 1>(min(D - 1, ns - 1 - i));
+      }
       GroupLoads d[kGps];
       bool valid[kGps];
 #pragma unroll
       for (int g = 0; g < kGps; ++g) {
-        read_group(half * kGps + g, d[g]);
+        read_group(pos * kGps + g, d[g]);
         valid[g] = kGps * i + g < nj;
       }
-      wave_lds_sync();
-      if (i + 2 < ns) {
+      if constexpr (D > 2) {
+        const int prev = (i + D - 1) % D;
+        if (i >= 1 && i - 1 + D < ns) {
 #pragma unroll
-        for (int g = 0; g < kGps; ++g) stage_group(g0 + min(kGps * (i + 2) + g, nj - 1), half * kGps + g);
+          for (int g = 0; g < kGps; ++g) stage_group(g0 + min(kGps * (i - 1 + D) + g, nj - 1), prev * kGps + g);
+        }
+      } else {
+        wave_lds_sync();
+        if (i + D < ns) {
+#pragma unroll
+          for (int g = 0; g < kGps; ++g) stage_group(g0 + min(kGps * (i + D) + g, nj - 1), pos * kGps + g);
+        }
       }
       process_step(d, valid);
     }
+    // a unit without key groups still issued (empty) copies into the ring
+    wait_vmcnt<0>();
   }
 
   // --------------------------------------------------- retained fp16 rows
@@ -930,21 +967,51 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB>())) void de
   }
 }
 
+#ifndef KVQ_DECODE_MAX_DEPTH
+#define KVQ_DECODE_MAX_DEPTH 4
+#endif
+// Deepest ring (steps in flight, 2..KVQ_DECODE_MAX_DEPTH) whose LDS still lets a
+// compute unit hold 8 waves.
+template <int DK, int DV, int KB, int VB>
+constexpr int deep_ring() {
+  if constexpr (KVQ_DECODE_MAX_DEPTH >= 4 && Lds<DK, DV, KB, VB, 4>::kBytes * 8 <= 160 * 1024)
+    return 4;
+  else if constexpr (KVQ_DECODE_MAX_DEPTH >= 3 && Lds<DK, DV, KB, VB, 3>::kBytes * 8 <= 160 * 1024)
+    return 3;
+  else
+    return 2;
+}
+
+template <int DK, int DV, int KB, int VB, int D>
+hipError_t launch_depth(DecodeArgs a, hipStream_t stream, int cus, int64_t waves) {
+  constexpr size_t lds = Lds<DK, DV, KB, VB, D>::kBytes;
+  static_assert(lds <= 64 * 1024, "LDS budget");
+  constexpr int per_simd = lds_waves_per_simd<DK, DV, KB, VB, D>();
+  const int64_t simds = int64_t(cus) * 4;
+  a.ranks = int(std::min<int64_t>(per_simd, std::max<int64_t>(1, (waves + simds - 1) / simds)));
+  hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, KB, VB, D>), dim3(unsigned(waves)), dim3(64), lds, stream, a);
+  return hipGetLastError();
+}
+
 template <int DK, int DV, int KB, int VB>
 hipError_t launch_one(DecodeArgs a, hipStream_t stream, int cus, int* parts) {
-  constexpr size_t lds = Lds<DK, DV, KB, VB>::kBytes;
-  static_assert(lds <= 64 * 1024, "LDS budget");
   // Units are cut only as far as 8 waves per compute unit: measured on the 128K
   // workload, 2048 long runs stream HBM better than 4096 half-length ones (the
-  // memory system serves the larger set of requests less evenly), and the
-  // kernel still holds two waves per SIMD.
-  const int per_cu = 4 * lds_waves_per_simd<DK, DV, KB, VB>();
+  // memory system serves the larger set of requests less evenly).  A grid that
+  // fits the device at 8 waves per CU takes the deep ring, which keeps more
+  // copies in flight per wave; a larger one keeps the 2-step ring and its
+  // higher occupancy.
+  const int per_cu = 4 * lds_waves_per_simd<DK, DV, KB, VB, 2>();
   a.units = decode_mfma_units(a.L, a.P, int64_t(cus) * (per_cu < 8 ? per_cu : 8));
   *parts = a.units;
-  if (int64_t(a.units) * a.L.B * a.L.Hkv >= (int64_t(1) << 31)) return hipErrorNotSupported;
-  const dim3 grid(unsigned(a.units) * unsigned(a.L.B) * unsigned(a.L.Hkv));
-  hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, KB, VB>), grid, dim3(64), lds, stream, a);
-  return hipGetLastError();
+  const int64_t waves = int64_t(a.units) * a.L.B * a.L.Hkv;
+  if (waves >= (int64_t(1) << 31)) return hipErrorNotSupported;
+  constexpr int DD = deep_ring<DK, DV, KB, VB>();
+  if constexpr (DD > 2) {
+    if (waves <= int64_t(cus) * 4 * lds_waves_per_simd<DK, DV, KB, VB, DD>())
+      return launch_depth<DK, DV, KB, VB, DD>(a, stream, cus, waves);
+  }
+  return launch_depth<DK, DV, KB, VB, 2>(a, stream, cus, waves);
 }
 
 template <int DK, int DV>

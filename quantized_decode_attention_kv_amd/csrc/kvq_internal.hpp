@@ -28,6 +28,7 @@ struct DecodeArgs {
   float scale;
   int P;
   int units;           // work units per slab of the matrix-core kernel (set by its launcher)
+  int ranks;           // waves per SIMD the matrix-core grid puts on the device at once (1..4)
   float* partials;     // [B * Hq, units, Dv + 4]: m (log2 domain), l, 2 unused, unnormalised o (P > 1)
   float* out;          // [B, Hq, Dv]
 };
