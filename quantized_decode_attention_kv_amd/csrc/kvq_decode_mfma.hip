@@ -273,18 +273,19 @@ __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t (&w)[NB < 
 #endif
 constexpr int kGps = KVQ_DECODE_GPS;
 
-// LDS of one workgroup (one wave), in bytes (20 KB for the common shapes: 8
-// waves per compute unit):
-//   QB  kGps Q' operand tiles, KK chunks of 32 channels each; the first holds the
-//       q hi/lo operand B2 for the retained rows;
-//   PA  kGps P' operand tiles; they share the Q' tiles when they fit there
-//       (within a step the Q' operands are consumed before P' is written, and
-//       P' before the next step's Q');
-//   ring of D * kGps staging slots (D steps in flight), one key group each: key
-//       codes, value codes,
-//       key scales, key zeros, value scales, value zeros.  At the end the ring
-//       holds the retained-row probabilities, then the output accumulator and
-//       the value zero-point sums.
+// LDS of one workgroup (one wave), in bytes (at most 20 KB for the common
+// shapes: 8 waves per compute unit):
+//   a ring of D * kGps slots (D steps in flight), one key group each: key codes,
+//   value codes, key scales, key zeros, value scales, value zeros;
+//   per group of a step, its Q' operand tile (KK chunks of 32 channels) and its
+//   P' operand tile, which shares the Q' tile's bytes when it fits there (within
+//   a step the Q' operands are consumed before P' is written).  With D > 2 the
+//   tiles sit in the step's own slots, which are idle once the step's groups
+//   have been read into registers (they are refilled one step later); with
+//   D == 2 the slots are refilled at once, so the tiles have an area of their own.
+//   After the loop the ring holds the q hi/lo operand B2 of the retained rows
+//   (slot 0) and their probabilities PT (slot 1), then the output accumulator
+//   and the value zero-point sums.
 template <int DK, int DV, int KB, int VB, int D>
 struct Lds {
   static constexpr int KK = DK / 32, NGV = DV / 32;
@@ -295,12 +296,14 @@ struct Lds {
   static constexpr int kStS = 256;
   static constexpr int kStage = kStK + kStV + 4 * kStS;
   static constexpr bool kShare = kPA1 <= kQB1;
-  static constexpr int oQB = 0, oPA = kShare ? 0 : kGps * kQB1;
-  static constexpr int kPAStride = kShare ? kQB1 : kPA1;  // bytes between P' tiles
-  static constexpr int oRing = kShare ? kGps * kQB1 : kGps * (kQB1 + kPA1);
+  static constexpr int kTiles = kShare ? kQB1 : kQB1 + kPA1;  // Q' and P' tiles of one group
+  static constexpr int kPAOff = kShare ? 0 : kQB1;             // P' tile inside them
+  static constexpr bool kInSlot = D > 2;
+  static constexpr int kSlot = kInSlot && kTiles > kStage ? kTiles : kStage;
   static constexpr int kSlots = D * kGps;
-  static constexpr int kBytes = oRing + kSlots * kStage;
-  static_assert(kG * 32 * 4 <= kSlots * kStage && kG * (DV + NGV) * 4 <= kSlots * kStage, "aliases");
+  static constexpr int oTiles = kInSlot ? 0 : kSlots * kSlot;  // separate tile area (D == 2)
+  static constexpr int kBytes = kSlots * kSlot + (kInSlot ? 0 : kGps * kTiles);
+  static_assert(kQB1 <= kSlot && kG * 32 * 4 <= kSlot && kG * (DV + NGV) * 4 <= kSlots * kSlot, "aliases");
 };
 
 // 8 consecutive query elements starting at i0 (a multiple of 8; the array is
@@ -409,11 +412,9 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   static_assert(DV == 128 && NV % TPW == 0 && KLB >= 4 && DK % 32 == 0 && DK <= 128, "shape");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  u32x4* QB = reinterpret_cast<u32x4*>(smem + LL::oQB);       // [kGps][KK*4][8]
-  u32x4* PA = reinterpret_cast<u32x4*>(smem + LL::oPA);       // [kGps][NGV*4][8], stride kPAStride
-  unsigned char* stage = smem + LL::oRing;                    // [D kGps][kStage]
-  u32x4* B2 = QB;                                             // q hi/lo, retained rows
-  float* PT = reinterpret_cast<float*>(stage);                // [4][32], retained rows
+  unsigned char* stage = smem;                                 // [D kGps][kSlot]
+  u32x4* B2 = reinterpret_cast<u32x4*>(smem);                  // q hi/lo, retained rows
+  float* PT = reinterpret_cast<float*>(smem + LL::kSlot);      // [4][32], retained rows
   const int lane = threadIdx.x, n = lane & 15, gq = lane >> 4;
 
   // unit-major grid: workgroup L takes unit L / slabs of slab L % slabs
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   const buf_rsrc rks = make_rsrc(ksbase, nsk), rkz = make_rsrc(kzbase, nsk);
   const buf_rsrc rvs = make_rsrc(vsbase, nsv), rvz = make_rsrc(vzbase, nsv);
   auto stage_group = [&](int g, int slot) {
-    unsigned char* sb = stage + slot * LL::kStage;
+    unsigned char* sb = stage + slot * LL::kSlot;
     const uint32_t gk = uint32_t(g) * (32 * KROW);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -668,7 +669,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
     u32x4 vs, vz;         // value scale / zero of the lane's P' channel group, tokens 8gq..
   };
   auto read_group = [&](int slot, GroupLoads& d) {
-    const unsigned char* sb = stage + slot * LL::kStage;
+    const unsigned char* sb = stage + slot * LL::kSlot;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
@@ -697,15 +698,18 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   };
 
   // One step: kGps key groups (valid[g] false: a stand-in whose scores are
-  // masked, for the end of an odd run).
-  auto process_step = [&](const GroupLoads (&d)[kGps], const bool (&valid)[kGps]) {
+  // masked, for the end of an odd run).  score_step takes the groups up to the
+  // P' operands in LDS; value_step applies them to the groups' value codes.
+  // `tiles`: the step's Q' / P' operand area, kSlot bytes per group
+  auto score_step = [&](const GroupLoads (&d)[kGps], const bool (&valid)[kGps], unsigned char* tiles) {
     if (qtask) {
 #pragma unroll
       for (int g = 0; g < kGps; ++g) {
         u32x4 hi, lo;
         split8(qsv, d[g].ks, hi, lo);
-        QB[g * (KK * 32) + qb_entry] = hi;
-        QB[g * (KK * 32) + qb_entry + 4] = lo;
+        u32x4* qb = reinterpret_cast<u32x4*>(tiles + g * LL::kSlot);
+        qb[qb_entry] = hi;
+        qb[qb_entry + 4] = lo;
       }
     }
     float bias[kGps];
@@ -720,7 +724,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
       for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
-          const u32x4 bq = QB[g * (KK * 32) + (kk * 4 + gq) * 8 + 4 * part + iq];
+          const u32x4 bq = reinterpret_cast<const u32x4*>(tiles + g * LL::kSlot)[(kk * 4 + gq) * 8 + 4 * part + iq];
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(key_field<KB>(d[g].kw[tt], kk), bq, sacc[tt]);
         }
@@ -742,7 +746,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
 #pragma unroll
       for (int k = 0; k < 8; ++k) pg[k] = pv[8 * g + k];
       split8(pg, d[g].vs, hi, lo);
-      u32x4* pa = reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(PA) + g * LL::kPAStride);
+      u32x4* pa = reinterpret_cast<u32x4*>(tiles + g * LL::kSlot + LL::kPAOff);
       pa[pa_entry] = hi;
       pa[pa_entry + 4] = lo;
       float zs = 0.0f;
@@ -753,10 +757,12 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
       }
       zacc += zs;
     }
+  };
+  auto value_step = [&](const uint32_t (&vws)[kGps][VLW], const unsigned char* tiles) {
     wave_lds_order();
 #pragma unroll
     for (int g = 0; g < kGps; ++g) {
-      const u32x4* pa = reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(PA) + g * LL::kPAStride);
+      const u32x4* pa = reinterpret_cast<const u32x4*>(tiles + g * LL::kSlot + LL::kPAOff);
 #pragma unroll
       for (int gc = 0; gc < NGV; ++gc) {
         const u32x4 ap = pa[(gc * 4 + gq) * 8 + (n & 7)];
@@ -768,13 +774,14 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
           u32x4 bv;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const uint32_t w = d[g].vw[m * NCH + chunk];
+            const uint32_t w = vws[g][m * NCH + chunk];
             bv[m] = (down ? w >> 8 : w) & (kVMask << sh);
           }
           oacc[t] = mfma16(ap, bv, oacc[t]);
         }
       }
     }
+    wave_lds_order();
   };
 
   {
@@ -826,7 +833,18 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
           for (int g = 0; g < kGps; ++g) stage_group(g0 + min(kGps * (i + D) + g, nj - 1), pos * kGps + g);
         }
       }
-      process_step(d, valid);
+      // the Q' / P' tiles overwrite the slot just read: LDS keeps the wave's
+      // order, the compiler must keep it too
+      wave_lds_order();
+      unsigned char* tiles = LL::kInSlot ? stage + pos * kGps * LL::kSlot : smem + LL::oTiles;
+      uint32_t vws[kGps][VLW];
+#pragma unroll
+      for (int g = 0; g < kGps; ++g) {
+#pragma unroll
+        for (int k = 0; k < VLW; ++k) vws[g][k] = d[g].vw[k];
+      }
+      score_step(d, valid, tiles);
+      value_step(vws, tiles);
     }
     // a unit without key groups still issued (empty) copies into the ring
     wait_vmcnt<0>();
@@ -970,17 +988,6 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
 #ifndef KVQ_DECODE_MAX_DEPTH
 #define KVQ_DECODE_MAX_DEPTH 4
 #endif
-// Deepest ring (steps in flight, 2..KVQ_DECODE_MAX_DEPTH) whose LDS still lets a
-// compute unit hold 8 waves.
-template <int DK, int DV, int KB, int VB>
-constexpr int deep_ring() {
-  if constexpr (KVQ_DECODE_MAX_DEPTH >= 4 && Lds<DK, DV, KB, VB, 4>::kBytes * 8 <= 160 * 1024)
-    return 4;
-  else if constexpr (KVQ_DECODE_MAX_DEPTH >= 3 && Lds<DK, DV, KB, VB, 3>::kBytes * 8 <= 160 * 1024)
-    return 3;
-  else
-    return 2;
-}
 
 template <int DK, int DV, int KB, int VB, int D>
 hipError_t launch_depth(DecodeArgs a, hipStream_t stream, int cus, int64_t waves) {
@@ -997,19 +1004,21 @@ template <int DK, int DV, int KB, int VB>
 hipError_t launch_one(DecodeArgs a, hipStream_t stream, int cus, int* parts) {
   // Units are cut only as far as 8 waves per compute unit: measured on the 128K
   // workload, 2048 long runs stream HBM better than 4096 half-length ones (the
-  // memory system serves the larger set of requests less evenly).  A grid that
-  // fits the device at 8 waves per CU takes the deep ring, which keeps more
-  // copies in flight per wave; a larger one keeps the 2-step ring and its
-  // higher occupancy.
+  // memory system serves the larger set of requests less evenly).  The ring is
+  // then the deepest (most copies in flight per wave) whose LDS still lets the
+  // whole grid be resident at once (up to 4 steps: a 5th measured no faster on
+  // the 128K workload).
   const int per_cu = 4 * lds_waves_per_simd<DK, DV, KB, VB, 2>();
   a.units = decode_mfma_units(a.L, a.P, int64_t(cus) * (per_cu < 8 ? per_cu : 8));
   *parts = a.units;
   const int64_t waves = int64_t(a.units) * a.L.B * a.L.Hkv;
   if (waves >= (int64_t(1) << 31)) return hipErrorNotSupported;
-  constexpr int DD = deep_ring<DK, DV, KB, VB>();
-  if constexpr (DD > 2) {
-    if (waves <= int64_t(cus) * 4 * lds_waves_per_simd<DK, DV, KB, VB, DD>())
-      return launch_depth<DK, DV, KB, VB, DD>(a, stream, cus, waves);
+  const int64_t simds = int64_t(cus) * 4;
+  if constexpr (KVQ_DECODE_MAX_DEPTH >= 4) {
+    if (waves <= simds * lds_waves_per_simd<DK, DV, KB, VB, 4>()) return launch_depth<DK, DV, KB, VB, 4>(a, stream, cus, waves);
+  }
+  if constexpr (KVQ_DECODE_MAX_DEPTH >= 3) {
+    if (waves <= simds * lds_waves_per_simd<DK, DV, KB, VB, 3>()) return launch_depth<DK, DV, KB, VB, 3>(a, stream, cus, waves);
   }
   return launch_depth<DK, DV, KB, VB, 2>(a, stream, cus, waves);
 }
