@@ -370,13 +370,15 @@ __device__ __forceinline__ float pick4(const float (&x)[kG], int i) {
 // unit-major grid and one unit per resident wave the units u < U/R become the
 // oldest wave on their SIMD, the next U/R the second oldest, and so on; waves are
 // served oldest first, so unit sizes fall by rank (integer weights
-// 100 + s (R - 1 - 2 r) for rank r) and the waves of a SIMD finish closer
-// together.  Any weights give the same result up to rounding.
-#ifndef KVQ_UNIT_SKEW
-#define KVQ_UNIT_SKEW 6
+// 100 + s (R - 1 - 2 r) for rank r, s = 16 / (R - 1): the oldest and youngest
+// rank differ by +-16%, measured on the 128K workload to bring the finish times
+// of the two waves of a SIMD within a few microseconds) and the waves of a SIMD
+// finish closer together.  Any weights give the same result up to rounding.
+#ifndef KVQ_UNIT_SKEW_SPAN
+#define KVQ_UNIT_SKEW_SPAN 16
 #endif
 __device__ __forceinline__ int unit_start(int u, int U, int nG, int R) {
-  constexpr int64_t s = KVQ_UNIT_SKEW;
+  const int64_t s = R > 1 ? KVQ_UNIT_SKEW_SPAN / (R - 1) : 0;
   int64_t wu = 0, wall = 0;
   for (int r = 0; r < R; ++r) {
     const int64_t lo = (int64_t(r) * U + R - 1) / R, hi = (int64_t(r + 1) * U + R - 1) / R;  // units of rank r
