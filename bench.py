@@ -155,6 +155,32 @@ def cpu_baseline(w, step_bytes, budget_workers=None):
 
 # ------------------------------------------------------------------------- main
 
+def read_ceiling(torch, api, nbytes, dev, reps=20):
+    """HBM read rate of a plain grid-wide streaming read (kvq_read_probe) over
+    nbytes, median of reps calls (after the timed steps; not part of them)."""
+    buf = torch.zeros((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+    sink = torch.empty(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        api.kvq_read_probe(buf, sink)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        api.kvq_read_probe(buf, sink)
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    med = ts[len(ts) // 2]
+    del buf
+    return {"read_GBps": round(nbytes / (med * 1e-3) / 1e9, 1), "us": round(med * 1e3, 2), "bytes": nbytes,
+            "how": "kvq_read_probe: grid-wide streaming read of the decode's byte count, median of %d calls" % reps}
+
+
+def percentiles(xs):
+    xs = sorted(xs)
+    pick = lambda f: xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]
+    return [round(pick(0.1) * 1e3, 2), round(pick(0.5) * 1e3, 2), round(pick(0.9) * 1e3, 2)]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +272,7 @@ def main():
     dec_gbps = db / (dec_ms * 1e-3) / 1e9
     kern_gbps = db / (kern_ms * 1e-3) / 1e9
     traffic = read_traffic()
+    ceiling = read_ceiling(torch, api, db, dev)
 
     result = {
         "metric": METRIC,
@@ -273,9 +300,12 @@ def main():
                    "pct_of_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
                    "steps_per_s": round(1e3 / dec_ms, 1), "tokens_per_s": round(w.B * 1e3 / dec_ms, 1),
                    "kernel_us": round(kern_ms * 1e3, 2), "merge_us": round(merge_ms * 1e3, 2),
+                   "kernel_us_p10_p50_p90": percentiles([e[1].elapsed_time(e[2]) for e in events]),
                    "algorithmic_bytes": db},
         "pack": ({"us": round(pack_ms * 1e3, 2), "GBps": round(pb / (pack_ms * 1e-3) / 1e9, 1),
+                  "us_p10_p50_p90": percentiles([e[0].elapsed_time(e[1]) for e in events]),
                   "algorithmic_bytes": pb} if chunk else None),
+        "hbm_read_ceiling": ceiling,
         "roofline": {"bound": "hbm", "achieved": round(kern_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "decode_mfma_kernel (first kernel of kv_decode_attn)",

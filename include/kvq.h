@@ -183,6 +183,19 @@ int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq
                       float softmax_scale, int num_partitions, void* workspace, size_t workspace_bytes,
                       float* out, void* stream, void* event_after_decode);
 
+/*
+ * kvq_read_probe — measurement support, not part of the decode path: reads
+ * buf[0, bytes) once (bytes rounded down to a multiple of 16) with a plain
+ * grid-wide streaming read, so that a caller can time the HBM read rate the
+ * device reaches and report it next to the decode kernel's.  buf: 16-byte
+ * aligned device memory, owned by the caller.  sink: 4 bytes of device memory
+ * the kernel may write (it keeps the reads from being optimized away; its
+ * content is unspecified).  stream: hipStream_t (NULL = default).  Errors:
+ * KVQ_ERR_INVALID for a NULL or misaligned pointer, KVQ_ERR_HIP for a failed
+ * launch.
+ */
+int kvq_read_probe(const void* buf, size_t bytes, void* sink, void* stream);
+
 /* Static text for a status code. */
 const char* kvq_status_string(int status);
 

@@ -18,7 +18,7 @@ CACHE_FIELDS = ["k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", 
 # every entry point declared in include/kvq.h
 EXPORTS = ["kvq_layout_init", "kvq_cache_sizes", "kvq_retained_positions", "kvq_quantized_before",
            "kvq_decode_workspace_bytes", "kv_quant_pack", "kv_decode_attn", "kv_decode_attn_ex", "kvq_status_string",
-           "kvq_last_error"]
+           "kvq_last_error", "kvq_read_probe"]
 
 
 class KvqLayout(ctypes.Structure):
@@ -61,6 +61,8 @@ def load() -> ctypes.CDLL:
     lib.kv_decode_attn.restype = c_int
     lib.kv_decode_attn_ex.argtypes = [LP, vp, c_int, CP, ctypes.c_float, c_int, vp, c_sz, vp, vp, vp]
     lib.kv_decode_attn_ex.restype = c_int
+    lib.kvq_read_probe.argtypes = [vp, c_sz, vp, vp]
+    lib.kvq_read_probe.restype = c_int
     lib.kvq_status_string.argtypes = [c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_last_error.argtypes = []

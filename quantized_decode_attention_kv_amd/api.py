@@ -155,3 +155,18 @@ def kv_decode_attn(layout: Layout, q, cache, num_partitions: int = 1, softmax_sc
                                          ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(out.data_ptr()),
                                          _stream(stream), ctypes.c_void_p(ev)))
     return out
+
+
+def kvq_read_probe(buf, sink=None, stream=None):
+    """Measurement support: read the bytes of the contiguous device tensor ``buf``
+    once with a plain streaming read (C ABI kvq_read_probe), so that the caller can
+    time the device's achievable HBM read rate.  ``sink``: a 4-byte device tensor
+    the kernel may write (allocated if None)."""
+    import torch
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device=buf.device)
+    L_.check(L_.load().kvq_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                      ctypes.c_void_p(sink.data_ptr()), _stream(stream)))
+    return sink

@@ -249,6 +249,15 @@ int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq
   return ok();
 }
 
+int kvq_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {
+  if (!buf || !sink) return fail(KVQ_ERR_INVALID, "buf or sink is NULL");
+  if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return fail(KVQ_ERR_INVALID, "buf must be 16-byte aligned and sink 4-byte aligned");
+  const hipError_t e = kvq::launch_read_probe(buf, bytes, static_cast<uint32_t*>(sink), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "read probe launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* kvq_status_string(int status) {
   switch (status) {
     case KVQ_OK: return "KVQ_OK";

@@ -57,6 +57,7 @@ inline size_t ws_partial_bytes(const kvq_layout& L, int P) {
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 // Decode kernel (matrix-core kernel where it applies, else the generic one)
 // followed, when P > 1, by the partition merge; after_decode (if not null) is
 // recorded on the stream between the two.

@@ -174,6 +174,14 @@ def test_decode_errors(lib):
     assert dec(cache=bad) == L_.KVQ_ERR_INVALID
 
 
+def test_read_probe_errors(lib):
+    # argument checks happen on the host, before any launch
+    assert lib.kvq_read_probe(None, 4096, FAKE, None) == L_.KVQ_ERR_INVALID
+    assert lib.kvq_read_probe(FAKE, 4096, None, None) == L_.KVQ_ERR_INVALID
+    assert lib.kvq_read_probe(FAKE + 8, 4096, FAKE, None) == L_.KVQ_ERR_INVALID
+    assert lib.kvq_read_probe(FAKE, 4096, FAKE + 2, None) == L_.KVQ_ERR_INVALID
+
+
 def test_status_strings(lib):
     for s in range(4):
         assert lib.kvq_status_string(s)

@@ -256,3 +256,15 @@ def test_workspace_reuse_needs_no_initialisation():
         assert err <= MAX_ABS_ERR, (P, err)
         outs.append(out.cpu())
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[3])
+
+
+@pytest.mark.gpu
+def test_read_probe_runs():
+    """The measurement probe reads a buffer (with a tail that is not a whole
+    workgroup block) and leaves it untouched."""
+    dev = torch.device("cuda:0")
+    buf = torch.arange((1 << 20) + 12, dtype=torch.int32, device=dev)
+    ref = buf.clone()
+    api.kvq_read_probe(buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)
