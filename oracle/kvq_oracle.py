@@ -26,6 +26,13 @@ open the plainest reading is taken and listed in the design notes):
   every key shifts every score by the same amount (softmax-null direction).
 * "Thin Keys, Full Values" (section 2): softmax(Q K^T / sqrt(d_select)) V with
   d_select (key width) different from the value width.
+* "Quantize What Counts" (technical summary, contributions "orthogonality and
+  integration" and results "rotation integration"): an optional rotation of the
+  keys only before they are quantized, to spread outlier channels; the pages name
+  rotation-based outlier redistribution without fixing the transform, read here as
+  the orthonormal Walsh-Hadamard transform (``hadamard_rotate``), applied to every
+  key row (quantized or kept in fp16) and, at decode, to the query, so that
+  scores are unchanged in exact arithmetic.
 
 Canonical packed layout for one (b, kv-head) slab (the same index formulas appear in
 ``include/kvq.h``; the oracle writes them out here independently):
@@ -72,6 +79,35 @@ def default_scale(Dk: int) -> np.float32:
     """Softmax scale 1/sqrt(d) of the score s = q^T k / sqrt(d) (HeadQ 2.1; Thin Keys 2,
     with d the key width), as one float32 value."""
     return np.float32(1.0) / np.sqrt(np.float32(Dk))
+
+
+# -------------------------------------------------------------------------- rotation
+
+def hadamard_rotate(x: np.ndarray) -> np.ndarray:
+    """Orthonormal Walsh-Hadamard transform (Sylvester order) along the last axis,
+    in float32 with one fixed order of operations: butterflies for h = 1, 2, 4, ...,
+    n/2 (entries j and j + h of every 2h-block become a + b and a - b), then one
+    multiply by fp32(2^(-m/2)) for n = 2^m, i.e. fp32(sqrt(1/2)) * 2^(-(m-1)/2) for
+    odd m.  Any implementation that takes the same steps gets the same bits."""
+    y = np.array(x, dtype=np.float32, copy=True)
+    n = y.shape[-1]
+    m = n.bit_length() - 1
+    if n != 1 << m:
+        raise ValueError("rotation needs a power-of-two width, got %d" % n)
+    lead = y.shape[:-1]
+    h = 1
+    while h < n:
+        v = y.reshape(lead + (n // (2 * h), 2, h))
+        a = v[..., 0, :].copy()
+        b = v[..., 1, :].copy()
+        v[..., 0, :] = a + b
+        v[..., 1, :] = a - b
+        y = v.reshape(lead + (n,))
+        h *= 2
+    c = np.float32(2.0 ** -(m // 2))
+    if m % 2:
+        c = np.float32(np.float32(np.sqrt(0.5)) * c)
+    return (y * c).astype(np.float32)
 
 
 # ------------------------------------------------------------------------- retention
@@ -199,14 +235,18 @@ def unpack_value_codes(words: np.ndarray, bits: int) -> np.ndarray:
     return codes.astype(np.uint8)
 
 
-def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_window: int):
+def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_window: int,
+              key_rotation: bool = False):
     """Quantize and pack one (b, kv-head) slab.  K [T, Dk], V [T, Dv] in storage dtype.
 
     Keys per channel over groups of 32 consecutive quantized tokens (LogQuant
     section 5, "per-channel" keys; group 32 from "Quantize What Counts", results);
     values per token over groups of 32 channels; retained positions copied to fp16.
+    With key_rotation every key row is first rotated (``hadamard_rotate``).
     """
     K32 = upcast(K, dtype)
+    if key_rotation:
+        K32 = hadamard_rotate(K32)
     V32 = upcast(V, dtype)
     T, Dk = K32.shape
     Dv = V32.shape[1]
@@ -250,7 +290,8 @@ def pack_all(K, V, w):
     for b in range(K.shape[0]):
         rows = {key: [] for key in CACHE_KEYS}
         for h in range(K.shape[1]):
-            p = pack_slab(K[b, h], V[b, h], w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window)
+            p = pack_slab(K[b, h], V[b, h], w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window,
+                          getattr(w, "key_rotation", False))
             for key in CACHE_KEYS:
                 rows[key].append(p[key])
         for key in CACHE_KEYS:
@@ -293,10 +334,31 @@ def attention(q, K, V, scale) -> np.ndarray:
     return (p @ np.asarray(V, dtype=np.float64)) / p.sum(axis=-1, keepdims=True)
 
 
-def decode_slab(q_group, p, q_dtype: str, k_bits: int, v_bits: int, scale) -> np.ndarray:
-    """Decode attention of the G query heads of one KV head over its packed slab."""
+def rotate_query(q: np.ndarray) -> np.ndarray:
+    """The key rotation applied to a query, in float64: H q / sqrt(n) with H the
+    Sylvester Hadamard matrix (entry (i, j) = (-1)^popcount(i & j)), so that
+    (H q) . (H k) = n q . k and the rotated scores equal the plain ones."""
+    q = np.asarray(q, dtype=np.float64)
+    n = q.shape[-1]
+    i = np.arange(n)
+    bits = np.bitwise_and.outer(i, i)
+    par = np.zeros_like(bits)
+    while bits.any():
+        par ^= bits & 1
+        bits >>= 1
+    H = np.where(par == 1, -1.0, 1.0)
+    return q @ H.T / np.sqrt(n)
+
+
+def decode_slab(q_group, p, q_dtype: str, k_bits: int, v_bits: int, scale,
+                key_rotation: bool = False) -> np.ndarray:
+    """Decode attention of the G query heads of one KV head over its packed slab
+    (with key_rotation the packed keys are rotated, so the query is rotated too)."""
     Khat, Vhat = dequant_slab(p, k_bits, v_bits)
-    return attention(upcast(q_group, q_dtype), Khat, Vhat, scale)
+    q = upcast(q_group, q_dtype)
+    if key_rotation:
+        q = rotate_query(q)
+    return attention(q, Khat, Vhat, scale)
 
 
 def decode_all(q, packed, w, scale=None) -> np.ndarray:
@@ -310,7 +372,8 @@ def decode_all(q, packed, w, scale=None) -> np.ndarray:
         for h in range(w.Hkv):
             p = {key: packed[key][b, h] for key in CACHE_KEYS}
             out[b, h * G:(h + 1) * G] = decode_slab(q[b, h * G:(h + 1) * G], p, w.dtype,
-                                                    w.k_bits, w.v_bits, scale)
+                                                    w.k_bits, w.v_bits, scale,
+                                                    getattr(w, "key_rotation", False))
     return out
 
 

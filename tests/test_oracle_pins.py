@@ -453,3 +453,85 @@ def test_report_keys_get_more_bits(capsys):
         rv = np.linalg.norm(Vh - V32) / np.linalg.norm(V32)
         lines.append("%d-bit relative reconstruction error K %.3e V %.3e" % (bits, rk, rv))
     print("\n".join(lines))
+
+
+# ------------------------------------------------------------------ key rotation pins
+
+def test_rotation_hand_example():
+    """Butterflies by hand for n = 4 (scale 2^-1, exact): [1,2,3,4] -> h=1: [3,-1,7,-1]
+    -> h=2: [10,-2,-4,0] -> x 1/2 = [5,-1,-2,0]; a unit vector -> a constant row."""
+    assert np.array_equal(O.hadamard_rotate(np.array([1, 2, 3, 4], np.float32)),
+                          np.array([5, -1, -2, 0], np.float32))
+    e0 = np.zeros(8, np.float32)
+    e0[0] = 1.0
+    c = np.float32(np.float32(np.sqrt(0.5)) * np.float32(0.5))     # n = 8: 2^-1.5
+    assert np.array_equal(O.hadamard_rotate(e0), np.full(8, c, np.float32))
+
+
+@pytest.mark.parametrize("n", [32, 64, 128, 256])
+def test_rotation_closed_form(n):
+    """Row i of the rotation of the identity is (-1)^popcount(i & j) * c, c the fp32
+    constant 2^(-m/2): the butterflies reproduce the Sylvester matrix exactly (every
+    partial sum is an integer until the one scaling multiply)."""
+    m = n.bit_length() - 1
+    c = np.float32(2.0 ** -(m // 2))
+    if m % 2:
+        c = np.float32(np.float32(np.sqrt(0.5)) * c)
+    i = np.arange(n)
+    sign = np.array([[1.0 if bin(a & b).count("1") % 2 == 0 else -1.0 for b in i] for a in i], np.float32)
+    assert np.array_equal(O.hadamard_rotate(np.eye(n, dtype=np.float32)), sign * c)
+
+
+def test_rotation_is_orthonormal_and_keeps_scores():
+    """rotate_query (explicit matrix, float64) is orthonormal; rotating q and k leaves
+    dot products and the exact attention output unchanged, and the fp32 butterflies
+    agree with it to float32 rounding."""
+    rng = np.random.default_rng(7)
+    n = 128
+    Q = O.rotate_query(np.eye(n))
+    assert np.allclose(Q @ Q.T, np.eye(n), atol=1e-13)
+    q = rng.standard_normal((4, n))
+    K = rng.standard_normal((300, n)) * 3.0
+    V = rng.standard_normal((300, 64))
+    a = O.attention(q, K, V, 0.1)
+    b = O.attention(O.rotate_query(q), O.rotate_query(K), V, 0.1)
+    assert np.abs(a - b).max() < 1e-12
+    x = rng.standard_normal((5, n)).astype(np.float32)
+    assert np.abs(O.hadamard_rotate(x).astype(np.float64) - O.rotate_query(x)).max() < 1e-5
+
+
+def test_rotated_pack_decodes_to_plain_attention_in_sixteen_bit_mode():
+    """With every token kept in fp16 the rotated cache holds fp16(H k); decoding it with
+    the rotated query gives the exact attention of the fp16-rounded rotated keys,
+    which is the plain attention up to that rounding."""
+    w = _w(T=256, Dk=64, Dv=64, Hq=2, B=1)
+    K, V = make_all(w, workers=1)
+    q = make_queries(w)
+    p = O.pack_slab(K[0, 0], V[0, 0], "bf16", 4, 2, 256, 0, key_rotation=True)
+    out = O.decode_slab(q[0], p, "bf16", 4, 2, O.default_scale(64), key_rotation=True)
+    Kr = O.hadamard_rotate(O.upcast(K[0, 0], "bf16")).astype(np.float16).astype(np.float64)
+    Vr = O.upcast(V[0, 0], "bf16").astype(np.float16).astype(np.float64)
+    ref = O.attention(O.rotate_query(O.upcast(q[0], "bf16")), Kr, Vr, O.default_scale(64))
+    assert np.abs(out - ref).max() < 1e-12
+    plain = O.attention(O.upcast(q[0], "bf16"), O.upcast(K[0, 0], "bf16"), O.upcast(V[0, 0], "bf16"),
+                        O.default_scale(64))
+    assert np.abs(out - plain).max() < 2e-2
+
+
+def test_report_key_rotation(capsys):
+    """Reported, not asserted (parity unpinned: the pages' gain rests on trained
+    weights and their quantizers).  Attention output error vs exact attention with and
+    without the key rotation, per-channel key quantization, synthetic outlier keys."""
+    w = _w(T=1024, Dk=128, Dv=128, Hq=4, B=1)
+    K, V = make_all(w, workers=1)
+    q = make_queries(w)
+    exact = O.attention(O.upcast(q[0], "bf16"), O.upcast(K[0, 0], "bf16"), O.upcast(V[0, 0], "bf16"),
+                        O.default_scale(128))
+    lines = []
+    for kb, vb in [(4, 2), (2, 2)]:
+        for rot in (False, True):
+            p = O.pack_slab(K[0, 0], V[0, 0], "bf16", kb, vb, 0, 0, key_rotation=rot)
+            out = O.decode_slab(q[0], p, "bf16", kb, vb, O.default_scale(128), key_rotation=rot)
+            lines.append("K%dV%d rotation %-5s max|err| %.3e mean|err| %.3e"
+                         % (kb, vb, rot, np.abs(out - exact).max(), np.abs(out - exact).mean()))
+    print("\n".join(lines))

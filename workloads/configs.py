@@ -30,6 +30,7 @@ class Workload:
     partitions: int = 1      # split-K sequence partitions used by decode
     seed: int = 0
     prefill_chunk: int = 0   # tokens of the newest chunk re-packed inside one bench step
+    key_rotation: bool = False  # keys rotated (Walsh-Hadamard) before quantization
     k_group: int = 32
     v_group: int = 32
     n_outliers: int = 4
