@@ -284,7 +284,7 @@ constexpr int kGps = KVQ_DECODE_GPS;
 //   have been read into registers (they are refilled one step later); with
 //   D == 2 the slots are refilled at once, so the tiles have an area of their own.
 //   After the loop the ring holds the q hi/lo operand B2 of the retained rows
-//   (slot 0) and their probabilities PT (slot 1), then the output accumulator
+//   (slot 0) and their probabilities PT (slot 1), then the matrix-core output
 //   and the value zero-point sums.
 template <int DK, int DV, int KB, int VB, int D>
 struct Lds {
@@ -935,29 +935,32 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   }
 
   // ------------------------------------------------------- the unit's result
-  // the ring is idle now: it holds the output accumulator OL [4][DV] and the value
-  // zero-point sums zsm [4][NGV]
-  float* OL = reinterpret_cast<float*>(stage);
-  float* zsm = OL + kG * DV;
-#pragma unroll
-  for (int i = 0; i < kG; ++i) {
-    OL[i * DV + 2 * lane] = o_r[i][0];
-    OL[i * DV + 2 * lane + 1] = o_r[i][1];
-  }
+  // The ring is idle now.  It takes the matrix-core output OM [4][DV] and the value
+  // zero-point sums zsm [4][NGV]; the retained rows' part o_r stays in registers
+  // (lane l owns channels 2l, 2l + 1 of every query, as in the output row).
+  float* OM = reinterpret_cast<float*>(stage);
+  float* zsm = OM + kG * DV;
   {
     // zero-point sums per (query, channel group): lanes 16 gq + 4 gc + i
     const float z16 = zacc + __shfl_xor(zacc, 16, 64);
     const float z = z16 + __shfl_xor(z16, 32, 64);
     if (gq == 0) zsm[iq * NGV + gcP] = z;
   }
-  wave_lds_sync();
-  // matrix-core accumulators (hi and lo rows, in output units) into OL
-  if (gq < 2) {  // lane groups 0 / 1 hold the hi / lo rows of the 4 queries
+  // Matrix-core accumulators: lane groups 0 and 1 hold the hi and lo rows of the 4
+  // queries for column n of each tile.  One row swap of a pair of tiles (t, t + 1)
+  // leaves hi + lo of tile t in lanes 0..15 and of tile t + 1 in lanes 16..31,
+  // each written by exactly one lane (no atomics).
+  static_assert(NV % 2 == 0, "tile pairs");
 #pragma unroll
-    for (int t = 0; t < NV; ++t) {
-      const float sc = 16777216.0f / float(1 << value_tile_shift<VB>(t % TPW));
+  for (int t = 0; t < NV; t += 2) {
+    const float sc0 = 16777216.0f / float(1 << value_tile_shift<VB>(t % TPW));
+    const float sc1 = 16777216.0f / float(1 << value_tile_shift<VB>((t + 1) % TPW));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) atomicAdd(&OL[r * DV + 16 * t + n], oacc[t][r] * sc);
+    for (int r = 0; r < 4; ++r) {
+      const auto h2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(oacc[t][r] * sc0),
+                                                       __float_as_uint(oacc[t + 1][r] * sc1), false, false);
+      const float v = __uint_as_float(h2[0]) + __uint_as_float(h2[1]);
+      if (gq < 2) OM[r * DV + 16 * (t + gq) + n] = v;
     }
   }
   wave_lds_sync();
@@ -971,8 +974,9 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
 #pragma unroll
   for (int i = 0; i < kG; ++i) {
     float2 o;
-    o.x = OL[i * DV + 2 * lane] + zsm[i * NGV + (2 * lane) / 32];
-    o.y = OL[i * DV + 2 * lane + 1] + zsm[i * NGV + (2 * lane + 1) / 32];
+    const float2 om = *reinterpret_cast<const float2*>(OM + i * DV + 2 * lane);
+    o.x = o_r[i][0] + om.x + zsm[i * NGV + (2 * lane) / 32];
+    o.y = o_r[i][1] + om.y + zsm[i * NGV + (2 * lane + 1) / 32];
     if (U == 1) {
       const float inv = 1.0f / lq[i];
       o.x *= inv;
