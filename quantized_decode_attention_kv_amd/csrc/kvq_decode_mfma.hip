@@ -561,6 +561,13 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
     qzv[k] = qtask ? qx[k] * qe : 0.0f;
     qsv[k] = qzv[k] * (1.0f / key_code_scale<KB>(k & 3));
   }
+  // LDS tile entries (16 bytes each) are stored swizzled so that the 16 lanes of
+  // each row of the wave hit 16 different 16-byte bank slots:
+  //   Q' entry (kk*4 + gq)*8 + 4*part + i at e ^ (bit 4 of e) << 2 (rows 2, 3 of
+  //   the 4 gq rows swap their hi and lo halves);
+  //   P' entry (gc*4 + gq)*8 + j at e ^ (gc & 1) << 3 ^ (gc >> 1) << 2.
+  auto qb_at = [](int e) { return e ^ (((e >> 4) & 1) << 2); };
+  auto pa_at = [](int e) { return e ^ (((e >> 5) & 1) << 3) ^ (((e >> 6) & 1) << 2); };
   const int qb_entry = ((qtask ? kk_t : 0) * 4 + gq_t) * 8 + i_t;
   // Key zero-point term of query lane % 4: sum_c q_c z_c (times 2^-E), from the
   // lanes' 8-channel partial sums: the 16 lanes of a query are lane % 4 + 4 m, so
@@ -710,8 +717,8 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
         u32x4 hi, lo;
         split8(qsv, d[g].ks, hi, lo);
         u32x4* qb = reinterpret_cast<u32x4*>(tiles + g * LL::kSlot);
-        qb[qb_entry] = hi;
-        qb[qb_entry + 4] = lo;
+        qb[qb_at(qb_entry)] = hi;
+        qb[qb_at(qb_entry + 4)] = lo;
       }
     }
     float bias[kGps];
@@ -726,7 +733,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
       for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
-          const u32x4 bq = reinterpret_cast<const u32x4*>(tiles + g * LL::kSlot)[(kk * 4 + gq) * 8 + 4 * part + iq];
+          const u32x4 bq = reinterpret_cast<const u32x4*>(tiles + g * LL::kSlot)[qb_at((kk * 4 + gq) * 8 + 4 * part + iq)];
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(key_field<KB>(d[g].kw[tt], kk), bq, sacc[tt]);
         }
@@ -749,8 +756,8 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
       for (int k = 0; k < 8; ++k) pg[k] = pv[8 * g + k];
       split8(pg, d[g].vs, hi, lo);
       u32x4* pa = reinterpret_cast<u32x4*>(tiles + g * LL::kSlot + LL::kPAOff);
-      pa[pa_entry] = hi;
-      pa[pa_entry + 4] = lo;
+      pa[pa_at(pa_entry)] = hi;
+      pa[pa_at(pa_entry + 4)] = lo;
       float zs = 0.0f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -767,7 +774,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
       const u32x4* pa = reinterpret_cast<const u32x4*>(tiles + g * LL::kSlot + LL::kPAOff);
 #pragma unroll
       for (int gc = 0; gc < NGV; ++gc) {
-        const u32x4 ap = pa[(gc * 4 + gq) * 8 + (n & 7)];
+        const u32x4 ap = pa[pa_at((gc * 4 + gq) * 8 + (n & 7))];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int t = 2 * gc + half;
