@@ -16,7 +16,9 @@
 //           the 4 waves through LDS;
 //   values  per-(token, 32-channel group) min / max with a DPP reduction inside
 //           each 16-lane row: a row of lanes holds exactly one channel group;
-//   codes   OR-ed into LDS words at their final bit positions, then stored as one
+//   codes   placed into LDS words at their final bit positions (a lane's two
+//           4- or 8-bit key codes fill whole bytes and are stored plainly; 2-bit
+//           key codes and value codes are OR-ed in), then stored as one
 //           contiguous run per group.
 //
 // The codes follow the quantizer contract of kvq.h bit for bit: code =
@@ -206,7 +208,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
     Raw16<DT> vraw;
     if (v128) vraw = load16<DT>(a.V, (slab * a.t_count + row_of(vtok)) * 128 + 16 * vtile);
 
-    for (int i = tid; i < KVQ_GROUP * kwords; i += kPackThreads) kw_s[i] = 0u;
+    // (4- and 8-bit key words are written byte by byte below, every byte once)
+    if constexpr (KB == 2) {
+      for (int i = tid; i < KVQ_GROUP * kwords; i += kPackThreads) kw_s[i] = 0u;
+    }
     for (int i = tid; i < vwords; i += kPackThreads) vw_s[i] = 0u;
 
     // keys: lane holds channels (2cp, 2cp+1) of the wave's 8 tokens; per-channel
@@ -263,7 +268,18 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
           for (int t = 0; t < 8; ++t) {
             const uint32_t c0 = quant_code(kx[k][t].x, s0, z0, r0, k_levels);
             const uint32_t c1 = quant_code(kx[k][t].y, s1, z1, r1, k_levels);
-            atomicOr(&kw_s[(8 * wave + t) * kwords + word], (c0 | (c1 << KB)) << bit);
+            const uint32_t f = c0 | (c1 << KB);
+            if constexpr (KB == 2) {
+              atomicOr(&kw_s[(8 * wave + t) * kwords + word], f << bit);
+            } else {
+              // the lane's two fields fill one byte (4 bits) or two (8 bits) of the
+              // word: plain stores, no atomics
+              unsigned char* dst = reinterpret_cast<unsigned char*>(kw_s + (8 * wave + t) * kwords + word) + bit / 8;
+              if constexpr (KB == 8)
+                *reinterpret_cast<uint16_t*>(dst) = uint16_t(f);
+              else
+                *dst = uint8_t(f);
+            }
           }
         }
       }
