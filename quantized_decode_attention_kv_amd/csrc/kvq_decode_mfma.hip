@@ -566,8 +566,12 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   //   Q' entry (kk*4 + gq)*8 + 4*part + i at e ^ (bit 4 of e) << 2 (rows 2, 3 of
   //   the 4 gq rows swap their hi and lo halves);
   //   P' entry (gc*4 + gq)*8 + j at e ^ (gc & 1) << 3 ^ (gc >> 1) << 2.
-  auto qb_at = [](int e) { return e ^ (((e >> 4) & 1) << 2); };
-  auto pa_at = [](int e) { return e ^ (((e >> 5) & 1) << 3) ^ (((e >> 6) & 1) << 2); };
+  // The swizzled addresses take a few more registers; instances held to 128 (4
+  // waves per SIMD) keep the plain order, which measured faster there than
+  // spilling.
+  constexpr bool kSwz = lds_waves_per_simd<DK, DV, KB, VB, D>() < 4;
+  auto qb_at = [](int e) { return kSwz ? e ^ (((e >> 4) & 1) << 2) : e; };
+  auto pa_at = [](int e) { return kSwz ? e ^ (((e >> 5) & 1) << 3) ^ (((e >> 6) & 1) << 2) : e; };
   const int qb_entry = ((qtask ? kk_t : 0) * 4 + gq_t) * 8 + i_t;
   // Key zero-point term of query lane % 4: sum_c q_c z_c (times 2^-E), from the
   // lanes' 8-channel partial sums: the 16 lanes of a query are lane % 4 + 4 m, so
