@@ -266,23 +266,16 @@ __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t (&w)[NB < 
   }
 }
 
-// Key groups a wave computes per step: their dependency chains interleave and one
-// set of LDS round trips serves all of them.
-#ifndef KVQ_DECODE_GPS
-#define KVQ_DECODE_GPS 1
-#endif
-constexpr int kGps = KVQ_DECODE_GPS;
-
 // LDS of one workgroup (one wave), in bytes (at most 20 KB for the common
 // shapes: 8 waves per compute unit):
-//   a ring of D * kGps slots (D steps in flight), one key group each: key codes,
+//   a ring of D slots (D key groups in flight), one key group each: key codes,
 //   value codes, key scales, key zeros, value scales, value zeros;
-//   per group of a step, its Q' operand tile (KK chunks of 32 channels) and its
-//   P' operand tile, which shares the Q' tile's bytes when it fits there (within
-//   a step the Q' operands are consumed before P' is written).  With D > 2 the
-//   tiles sit in the step's own slots, which are idle once the step's groups
-//   have been read into registers (they are refilled one step later); with
-//   D == 2 the slots are refilled at once, so the tiles have an area of their own.
+//   the Q' operand tile of the group being computed (KK chunks of 32 channels)
+//   and its P' operand tile, which shares the Q' tile's bytes when it fits there
+//   (the Q' operands are consumed before P' is written).  With D > 2 the tiles
+//   sit in the group's own slot, which is idle once the group has been read into
+//   registers (it is refilled one step later); with D == 2 the slot is refilled
+//   at once, so the tiles have an area of their own.
 //   After the loop the ring holds the q hi/lo operand B2 of the retained rows
 //   (slot 0) and their probabilities PT (slot 1), then the matrix-core output
 //   and the value zero-point sums.
@@ -300,9 +293,9 @@ struct Lds {
   static constexpr int kPAOff = kShare ? 0 : kQB1;             // P' tile inside them
   static constexpr bool kInSlot = D > 2;
   static constexpr int kSlot = kInSlot && kTiles > kStage ? kTiles : kStage;
-  static constexpr int kSlots = D * kGps;
+  static constexpr int kSlots = D;
   static constexpr int oTiles = kInSlot ? 0 : kSlots * kSlot;  // separate tile area (D == 2)
-  static constexpr int kBytes = kSlots * kSlot + (kInSlot ? 0 : kGps * kTiles);
+  static constexpr int kBytes = kSlots * kSlot + (kInSlot ? 0 : kTiles);
   static_assert(kQB1 <= kSlot && kG * 32 * 4 <= kSlot && kG * (DV + NGV) * 4 <= kSlots * kSlot, "aliases");
 };
 
@@ -414,7 +407,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   static_assert(DV == 128 && NV % TPW == 0 && KLB >= 4 && DK % 32 == 0 && DK <= 128, "shape");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* stage = smem;                                 // [D kGps][kSlot]
+  unsigned char* stage = smem;                                 // [D][kSlot]
   u32x4* B2 = reinterpret_cast<u32x4*>(smem);                  // q hi/lo, retained rows
   float* PT = reinterpret_cast<float*>(smem + LL::kSlot);      // [4][32], retained rows
   const int lane = threadIdx.x, n = lane & 15, gq = lane >> 4;
@@ -464,7 +457,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   constexpr int kDmas = 2 * KNP + VNP + 4;  // copies per group
   constexpr int oKZ = LL::kStS, oVS = 2 * LL::kStS, oVZ = 3 * LL::kStS;  // scale area offsets
   static_assert(DK * 2 <= LL::kStS && DV * 2 == LL::kStS, "scale area");
-  static_assert((D - 1) * kDmas * kGps < 64 && D >= 2, "vmcnt");
+  static_assert((D - 1) * kDmas < 64 && D >= 2, "vmcnt");
   static_assert(KLB % KPB == 0 && VLW % 4 == 0 && DK / 8 <= 64 && 4 * NGV <= 64, "staging");
   // per-lane byte offsets inside a group (the group base itself is wave-uniform)
   uint32_t koff[2];
@@ -512,7 +505,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   const u32x4 qw0 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff, 0, 0);
   const u32x4 qw1 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 16, 0, 0);
 #pragma unroll
-  for (int u = 0; u < D * kGps; ++u) stage_group(g0 + min(u, nj > 0 ? nj - 1 : 0), u);
+  for (int u = 0; u < D; ++u) stage_group(g0 + min(u, nj > 0 ? nj - 1 : 0), u);
   __builtin_amdgcn_sched_barrier(0);
   float qx[8];
   if (a.q_dtype == KVQ_BF16) {
@@ -710,108 +703,89 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
     d.vz = *reinterpret_cast<const u32x4*>(ss + oVZ + (gcP * 4 + gq) * 16);
   };
 
-  // One step: kGps key groups (valid[g] false: a stand-in whose scores are
-  // masked, for the end of an odd run).  score_step takes the groups up to the
-  // P' operands in LDS; value_step applies them to the groups' value codes.
-  // `tiles`: the step's Q' / P' operand area, kSlot bytes per group
-  auto score_step = [&](const GroupLoads (&d)[kGps], const bool (&valid)[kGps], unsigned char* tiles) {
+  // One step: one key group.  score_step takes the group up to the P' operands
+  // in LDS; value_step applies them to the group's value codes.
+  // `tiles`: the step's Q' / P' operand area
+  auto score_step = [&](const GroupLoads& d, unsigned char* tiles) {
     if (qtask) {
+      u32x4 hi, lo;
+      split8(qsv, d.ks, hi, lo);
+      u32x4* qb = reinterpret_cast<u32x4*>(tiles);
+      qb[qb_at(qb_entry)] = hi;
+      qb[qb_at(qb_entry + 4)] = lo;
+    }
+    const float bias[1] = {zero_term(d.kz) * coefB};
+    wave_lds_order();
+    float v[8], pv[8];
+    f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-      for (int g = 0; g < kGps; ++g) {
-        u32x4 hi, lo;
-        split8(qsv, d[g].ks, hi, lo);
-        u32x4* qb = reinterpret_cast<u32x4*>(tiles + g * LL::kSlot);
-        qb[qb_at(qb_entry)] = hi;
-        qb[qb_at(qb_entry + 4)] = lo;
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const u32x4 bq = reinterpret_cast<const u32x4*>(tiles)[qb_at((kk * 4 + gq) * 8 + 4 * part + iq)];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(key_field<KB>(d.kw[tt], kk), bq, sacc[tt]);
       }
     }
-    float bias[kGps];
 #pragma unroll
-    for (int g = 0; g < kGps; ++g) bias[g] = zero_term(d[g].kz) * coefB;
-    wave_lds_order();
-    float v[8 * kGps], pv[8 * kGps];
+    for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-    for (int g = 0; g < kGps; ++g) {
-      f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-          const u32x4 bq = reinterpret_cast<const u32x4*>(tiles + g * LL::kSlot)[qb_at((kk * 4 + gq) * 8 + 4 * part + iq)];
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(key_field<KB>(d[g].kw[tt], kk), bq, sacc[tt]);
-        }
-      }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[8 * g + 4 * tt + r] = valid[g] ? sacc[tt][r] : -INFINITY;
-      }
+      for (int r = 0; r < 4; ++r) v[4 * tt + r] = sacc[tt][r];
     }
     softmax_step(v, coefD, bias, pv, rescale_groups);
 
-    // P' = p s (hi, lo) for the lane's (query, channel group, octet) of each
-    // group and the zero-point sums of the same tasks
+    // P' = p s (hi, lo) for the lane's (query, channel group, octet) and the
+    // zero-point sum of the same task
+    u32x4 hi, lo;
+    split8(pv, d.vs, hi, lo);
+    u32x4* pa = reinterpret_cast<u32x4*>(tiles + LL::kPAOff);
+    pa[pa_at(pa_entry)] = hi;
+    pa[pa_at(pa_entry + 4)] = lo;
+    float zs = 0.0f;
 #pragma unroll
-    for (int g = 0; g < kGps; ++g) {
-      u32x4 hi, lo;
-      float pg[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) pg[k] = pv[8 * g + k];
-      split8(pg, d[g].vs, hi, lo);
-      u32x4* pa = reinterpret_cast<u32x4*>(tiles + g * LL::kSlot + LL::kPAOff);
-      pa[pa_at(pa_entry)] = hi;
-      pa[pa_at(pa_entry + 4)] = lo;
-      float zs = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const half2_t zz = as_half2(d[g].vz[k >> 1]);
-        zs = fmaf(pg[k], float(zz[k & 1]), zs);
-      }
-      zacc += zs;
+    for (int k = 0; k < 8; ++k) {
+      const half2_t zz = as_half2(d.vz[k >> 1]);
+      zs = fmaf(pv[k], float(zz[k & 1]), zs);
     }
+    zacc += zs;
   };
-  auto value_step = [&](const uint32_t (&vws)[kGps][VLW], const unsigned char* tiles) {
+  auto value_step = [&](const uint32_t (&vws)[VLW], const unsigned char* tiles) {
     wave_lds_order();
+    const u32x4* pa = reinterpret_cast<const u32x4*>(tiles + LL::kPAOff);
 #pragma unroll
-    for (int g = 0; g < kGps; ++g) {
-      const u32x4* pa = reinterpret_cast<const u32x4*>(tiles + g * LL::kSlot + LL::kPAOff);
+    for (int gc = 0; gc < NGV; ++gc) {
+      const u32x4 ap = pa[pa_at((gc * 4 + gq) * 8 + (n & 7))];
 #pragma unroll
-      for (int gc = 0; gc < NGV; ++gc) {
-        const u32x4 ap = pa[pa_at((gc * 4 + gq) * 8 + (n & 7))];
+      for (int half = 0; half < 2; ++half) {
+        const int t = 2 * gc + half;
+        const int chunk = t / TPW, sh = value_tile_shift<VB>(t % TPW);
+        const bool down = (t % TPW) * VB != sh;
+        u32x4 bv;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int t = 2 * gc + half;
-          const int chunk = t / TPW, sh = value_tile_shift<VB>(t % TPW);
-          const bool down = (t % TPW) * VB != sh;
-          u32x4 bv;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const uint32_t w = vws[g][m * NCH + chunk];
-            bv[m] = (down ? w >> 8 : w) & (kVMask << sh);
-          }
-          oacc[t] = mfma16(ap, bv, oacc[t]);
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t w = vws[m * NCH + chunk];
+          bv[m] = (down ? w >> 8 : w) & (kVMask << sh);
         }
+        oacc[t] = mfma16(ap, bv, oacc[t]);
       }
     }
     wave_lds_order();
   };
 
   {
-    // Steps of kGps groups: step i takes groups kGps i .. kGps i + kGps - 1 from
-    // ring position i % D.  The prologue filled positions 0 .. D - 1.  With D > 2
-    // the copies of step i - 1 + D go to the position step i - 1 was read from,
-    // once step i has been waited for: those reads have been consumed, so no wait
-    // on LDS is needed, and steps i + 1 .. i + D - 2 stay in flight while step i
-    // is computed.  With D == 2 step i's own position takes the copies of step
-    // i + 2 right after it has been read (after a wait for the reads).  Past the
-    // end of a short run the prologue re-reads its last group, which is always
-    // in bounds.  The last step waits for all copies, so the ring is idle
-    // afterwards.
+    // Step i takes key group i from ring position i % D.  The prologue filled
+    // positions 0 .. D - 1.  With D > 2 the copies of group i - 1 + D go to the
+    // position step i - 1 was read from, once group i has been waited for: those
+    // reads have been consumed, so no wait on LDS is needed, and groups i + 1 ..
+    // i + D - 2 stay in flight while group i is computed.  With D == 2 step i's
+    // own position takes the copies of group i + 2 right after it has been read
+    // (after a wait for the reads).  Past the end of a short run the prologue
+    // re-reads its last group, which is always in bounds.  The last step waits
+    // for all copies, so the ring is idle afterwards.
     // Issue priority falls by one level per quarter of the unit's steps: the
     // waves of a SIMD are otherwise served oldest first and would finish far
     // apart; this way a wave that is ahead yields to the ones behind it.
-    const int ns = (nj + kGps - 1) / kGps;
+    const int ns = nj;
     __builtin_amdgcn_s_setprio(3);
     const int q1 = ns / 4, q2 = ns / 2, q3 = (3 * ns) / 4;
     for (int i = 0; i < ns; ++i) {
@@ -822,41 +796,27 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
       if constexpr (D > 2) {
         // copies issued beyond step i: the prologue's D - 1 at i == 0, later at
         // most D - 2 (fewer near the end of the run)
-        wait_steps_ahead<kDmas * kGps, D - 1>(i == 0 ? min(D - 1, ns - 1) : min(D - 2, ns - 1 - i));
+        wait_steps_ahead<kDmas, D - 1>(i == 0 ? min(D - 1, ns - 1) : min(D - 2, ns - 1 - i));
       } else {
-        wait_steps_ahead<kDmas * kGps, D - 1>(min(D - 1, ns - 1 - i));
+        wait_steps_ahead<kDmas, D - 1>(min(D - 1, ns - 1 - i));
       }
-      GroupLoads d[kGps];
-      bool valid[kGps];
-#pragma unroll
-      for (int g = 0; g < kGps; ++g) {
-        read_group(pos * kGps + g, d[g]);
-        valid[g] = kGps * i + g < nj;
-      }
+      GroupLoads d;
+      read_group(pos, d);
       if constexpr (D > 2) {
         const int prev = (i + D - 1) % D;
-        if (i >= 1 && i - 1 + D < ns) {
-#pragma unroll
-          for (int g = 0; g < kGps; ++g) stage_group(g0 + min(kGps * (i - 1 + D) + g, nj - 1), prev * kGps + g);
-        }
+        if (i >= 1 && i - 1 + D < ns) stage_group(g0 + i - 1 + D, prev);
       } else {
         wave_lds_sync();
-        if (i + D < ns) {
-#pragma unroll
-          for (int g = 0; g < kGps; ++g) stage_group(g0 + min(kGps * (i + D) + g, nj - 1), pos * kGps + g);
-        }
+        if (i + D < ns) stage_group(g0 + i + D, pos);
       }
       // the Q' / P' tiles overwrite the slot just read: LDS keeps the wave's
       // order, the compiler must keep it too
       wave_lds_order();
-      unsigned char* tiles = LL::kInSlot ? stage + pos * kGps * LL::kSlot : smem + LL::oTiles;
-      uint32_t vws[kGps][VLW];
+      unsigned char* tiles = LL::kInSlot ? stage + pos * LL::kSlot : smem + LL::oTiles;
+      uint32_t vws[VLW];
 #pragma unroll
-      for (int g = 0; g < kGps; ++g) {
-#pragma unroll
-        for (int k = 0; k < VLW; ++k) vws[g][k] = d[g].vw[k];
-      }
-      score_step(d, valid, tiles);
+      for (int k = 0; k < VLW; ++k) vws[k] = d.vw[k];
+      score_step(d, tiles);
       value_step(vws, tiles);
     }
     // a unit without key groups still issued (empty) copies into the ring
