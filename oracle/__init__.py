@@ -23,3 +23,4 @@ from .kvq_oracle import (  # noqa: F401
     value_bit_position,
     upcast,
 )
+from .kvq_stream import SlabStream  # noqa: F401
