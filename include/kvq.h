@@ -183,6 +183,102 @@ int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq
                       float softmax_scale, int num_partitions, void* workspace, size_t workspace_bytes,
                       float* out, void* stream, void* event_after_decode);
 
+/* ------------------------------------------------------------------ streaming
+ *
+ * A streaming cache grows by one decode-time token per kv_stream_append call
+ * (LogQuant technical summary, section 2, dynamic adjustment: as tokens arrive the
+ * fp16 density of the older windows halves, so tokens leave the fp16 set at
+ * regular intervals; section 4: the cached tokens may be stored in any order).
+ *  - Retention at t tokens is the rule above with T = t.  Positions are absolute,
+ *    so a token that has left the fp16 set never re-enters it; this needs
+ *    log_window == 0 or n_recent >= log_window.
+ *  - An appended token is stored in fp16 (round to nearest even).
+ *  - A token that leaves the fp16 set becomes pending: it stays in its fp16 row and
+ *    is attended as fp16 until 32 tokens are pending.  Then the 32 pending tokens
+ *    of lowest position, in ascending position, are quantized from their fp16
+ *    values as the next key group (the quantizer contract and group format above)
+ *    and their rows are freed.  The rows in use are always [0, n_rows): rows past
+ *    the new end move into the freed ones.
+ *  - Decode attends over the n_groups packed groups and the n_rows fp16 rows.
+ * Buffers: the eight kvq_cache buffers with g_cap groups and r_cap rows per slab
+ * (slab strides; only the first n_groups / n_rows are meaningful):
+ *   k_codes uint32 [B, Hkv, 32*g_cap, Dk*k_bits/32]   (32 rows per group)
+ *   k_scale, k_zero fp16 [B, Hkv, g_cap, Dk]
+ *   v_codes uint32 [B, Hkv, g_cap, Dv*v_bits]
+ *   v_scale, v_zero fp16 [B, Hkv, g_cap, Dv/32, 32]
+ *   k_fp16 fp16 [B, Hkv, r_cap, Dk], v_fp16 fp16 [B, Hkv, r_cap, Dv]
+ * The host state (kvq_stream, caller-owned) advances when a call is enqueued, so
+ * all calls on one stream state must be enqueued in order on one HIP stream.  A
+ * call that fails leaves the state as it was.
+ */
+enum { KVQ_STREAM_MAX_ROWS = 4096 };
+
+typedef struct {
+  kvq_layout L;        /* format: B, Hq, Hkv, Dk, Dv, bits, n_recent, log_window;
+                          L.T = capacity (most tokens the stream may hold);
+                          L.R, L.Tq, L.n_groups are unused (0) */
+  int32_t t;           /* tokens in the stream (positions 0 .. t-1) */
+  int32_t n_groups;    /* key groups packed, per slab */
+  int32_t n_rows;      /* fp16 rows in use, per slab */
+  int32_t n_pending;   /* rows among them whose token has left the fp16 set */
+  int32_t g_cap;       /* group capacity per slab: capacity / 32 */
+  int32_t r_cap;       /* fp16 row capacity per slab (a bound on n_rows over the
+                          stream's life, at most KVQ_STREAM_MAX_ROWS) */
+  int32_t row_pos[KVQ_STREAM_MAX_ROWS];      /* position of the token in row i < n_rows */
+  uint8_t row_pending[KVQ_STREAM_MAX_ROWS];  /* 1 if row i's token is pending */
+} kvq_stream;
+
+/* What one appended token changes on the device (filled by kvq_stream_plan). */
+typedef struct {
+  int32_t new_row;           /* fp16 row the token is written to */
+  int32_t group;             /* index of the key group formed, or -1 */
+  int32_t member_rows[32];   /* rows of the group's tokens (before the moves), ascending position */
+  int32_t member_pos[32];    /* their positions */
+  int32_t n_moves;           /* rows moved into freed rows once the group is packed */
+  int32_t move_src[32], move_dst[32];
+} kvq_stream_step;
+
+/* Start an empty stream (t = 0) for at most `capacity` tokens.  Limits as
+ * kvq_layout_init (without its multiple-of-32 rule), plus: log_window == 0 or
+ * n_recent >= log_window (KVQ_ERR_UNSUPPORTED otherwise), capacity >= 1, and an fp16
+ * row bound of at most KVQ_STREAM_MAX_ROWS (KVQ_ERR_UNSUPPORTED otherwise). */
+int kvq_stream_init(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, int capacity,
+                    int k_bits, int v_bits, int n_recent, int log_window);
+
+/* Byte sizes of the eight buffers of a stream's cache, in kvq_cache field order. */
+int kvq_stream_cache_sizes(const kvq_stream* S, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]);
+
+/* Workspace kv_stream_decode needs for num_partitions (as kvq_decode_workspace_bytes). */
+size_t kvq_stream_workspace_bytes(const kvq_stream* S, int num_partitions);
+
+/* Host-side bookkeeping of one append, no GPU work: advances *S by one token and
+ * describes in *step what the device must do.  kv_stream_append calls it; it is
+ * exported so that the bookkeeping can be inspected and tested on its own.
+ * KVQ_ERR_INVALID if the stream is full (t == capacity). */
+int kvq_stream_plan(kvq_stream* S, kvq_stream_step* step);
+
+/* kv_stream_prefill — start an empty stream from the one-shot cache of its first
+ * T0 tokens (kv_quant_pack's grouping: quantized positions in ascending order,
+ * retained positions in fp16 rows in ascending order; nothing pending).
+ *   K [B, Hkv, T0, Dk], V [B, Hkv, T0, Dv]: device arrays of kv_dtype.
+ * Needs t == 0, 1 <= T0 <= capacity and a quantized count at T0 that is a multiple
+ * of 32 (else KVQ_ERR_UNSUPPORTED). */
+int kv_stream_prefill(kvq_stream* S, int T0, const void* K, const void* V, int kv_dtype,
+                      const kvq_cache* cache, void* stream);
+
+/* kv_stream_append — append the token at position t.  k_new [B, Hkv, Dk] and
+ * v_new [B, Hkv, Dv]: device arrays of kv_dtype, 16-byte aligned.  One kernel
+ * launch: the token's fp16 row, and when a group forms, its codes, scales and
+ * zeros and the row moves.  KVQ_ERR_INVALID when the stream is full. */
+int kv_stream_append(kvq_stream* S, const void* k_new, const void* v_new, int kv_dtype,
+                     const kvq_cache* cache, void* stream);
+
+/* kv_stream_decode — kv_decode_attn over the stream's t tokens (arguments as
+ * there; 1 <= num_partitions <= max(1, ceil(t / 32)); needs t >= 1). */
+int kv_stream_decode(const kvq_stream* S, const void* q, int q_dtype, const kvq_cache* cache,
+                     float softmax_scale, int num_partitions, void* workspace, size_t workspace_bytes,
+                     float* out, void* stream);
+
 /*
  * kvq_read_probe — measurement support, not part of the decode path: reads
  * buf[0, bytes) once (bytes rounded down to a multiple of 16) with a plain

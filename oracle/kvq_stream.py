@@ -95,8 +95,10 @@ class SlabStream:
         for pos in self.rows:
             if not keep[pos]:
                 self.pending.add(pos)
-        # a token outside the rows (packed) must not be retained again
-        assert all(keep[pos] == (pos in self.rows and pos not in self.pending) for pos in range(self.t))
+        # the fp16 set is exactly the retained set (so a packed token is never retained again)
+        in_fp16 = np.zeros(self.t, dtype=bool)
+        in_fp16[[pos for pos in self.rows if pos not in self.pending]] = True
+        assert np.array_equal(keep, in_fp16)
         while len(self.pending) >= GROUP:
             members = sorted(self.pending)[:GROUP]
             self._pack_group(np.array(members, dtype=np.int64))

@@ -4,11 +4,11 @@ The computation lives in libkvq.so (hand-written HIP kernels for gfx950, C ABI i
 include/kvq.h).  ``api`` marshals torch tensors into those calls.
 """
 
-__all__ = ["Layout", "alloc_cache", "alloc_workspace", "kv_quant_pack", "kv_decode_attn", "KvqError"]
+__all__ = ["Layout", "Stream", "alloc_cache", "alloc_workspace", "kv_quant_pack", "kv_decode_attn", "KvqError"]
 
 
 def __getattr__(name):
-    if name in ("Layout", "alloc_cache", "alloc_workspace", "kv_quant_pack", "kv_decode_attn"):
+    if name in ("Layout", "Stream", "alloc_cache", "alloc_workspace", "kv_quant_pack", "kv_decode_attn"):
         from . import api
         return getattr(api, name)
     if name == "KvqError":

@@ -10,6 +10,7 @@ KVQ_OK, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP = 0, 1, 2, 3
 KVQ_F32, KVQ_F16, KVQ_BF16 = 0, 1, 2
 KVQ_GROUP = 32
 KVQ_NUM_CACHE_BUFFERS = 8
+KVQ_STREAM_MAX_ROWS = 4096
 
 LAYOUT_FIELDS = ["B", "Hq", "Hkv", "Dk", "Dv", "T", "k_bits", "v_bits", "n_recent", "log_window",
                  "R", "Tq", "n_groups"]
@@ -18,7 +19,9 @@ CACHE_FIELDS = ["k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", 
 # every entry point declared in include/kvq.h
 EXPORTS = ["kvq_layout_init", "kvq_cache_sizes", "kvq_retained_positions", "kvq_quantized_before",
            "kvq_decode_workspace_bytes", "kv_quant_pack", "kv_decode_attn", "kv_decode_attn_ex", "kvq_status_string",
-           "kvq_last_error", "kvq_read_probe"]
+           "kvq_last_error", "kvq_read_probe", "kvq_stream_init", "kvq_stream_cache_sizes",
+           "kvq_stream_workspace_bytes", "kvq_stream_plan", "kv_stream_prefill", "kv_stream_append",
+           "kv_stream_decode"]
 
 
 class KvqLayout(ctypes.Structure):
@@ -27,6 +30,22 @@ class KvqLayout(ctypes.Structure):
 
 class KvqCache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in CACHE_FIELDS]
+
+
+STREAM_FIELDS = ["t", "n_groups", "n_rows", "n_pending", "g_cap", "r_cap"]
+
+
+class KvqStream(ctypes.Structure):
+    _fields_ = ([("L", KvqLayout)] + [(n, ctypes.c_int32) for n in STREAM_FIELDS]
+                + [("row_pos", ctypes.c_int32 * KVQ_STREAM_MAX_ROWS),
+                   ("row_pending", ctypes.c_uint8 * KVQ_STREAM_MAX_ROWS)])
+
+
+class KvqStreamStep(ctypes.Structure):
+    _fields_ = [("new_row", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("member_rows", ctypes.c_int32 * KVQ_GROUP), ("member_pos", ctypes.c_int32 * KVQ_GROUP),
+                ("n_moves", ctypes.c_int32), ("move_src", ctypes.c_int32 * KVQ_GROUP),
+                ("move_dst", ctypes.c_int32 * KVQ_GROUP)]
 
 
 _lib = None
@@ -63,6 +82,21 @@ def load() -> ctypes.CDLL:
     lib.kv_decode_attn_ex.restype = c_int
     lib.kvq_read_probe.argtypes = [vp, c_sz, vp, vp]
     lib.kvq_read_probe.restype = c_int
+    SP = ctypes.POINTER(KvqStream)
+    lib.kvq_stream_init.argtypes = [SP] + [c_int] * 10
+    lib.kvq_stream_init.restype = c_int
+    lib.kvq_stream_cache_sizes.argtypes = [SP, ctypes.POINTER(c_sz)]
+    lib.kvq_stream_cache_sizes.restype = c_int
+    lib.kvq_stream_workspace_bytes.argtypes = [SP, c_int]
+    lib.kvq_stream_workspace_bytes.restype = c_sz
+    lib.kvq_stream_plan.argtypes = [SP, ctypes.POINTER(KvqStreamStep)]
+    lib.kvq_stream_plan.restype = c_int
+    lib.kv_stream_prefill.argtypes = [SP, c_int, vp, vp, c_int, CP, vp]
+    lib.kv_stream_prefill.restype = c_int
+    lib.kv_stream_append.argtypes = [SP, vp, vp, c_int, CP, vp]
+    lib.kv_stream_append.restype = c_int
+    lib.kv_stream_decode.argtypes = [SP, vp, c_int, CP, ctypes.c_float, c_int, vp, c_sz, vp, vp]
+    lib.kv_stream_decode.restype = c_int
     lib.kvq_status_string.argtypes = [c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_last_error.argtypes = []

@@ -170,3 +170,125 @@ def kvq_read_probe(buf, sink=None, stream=None):
     L_.check(L_.load().kvq_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
                                       ctypes.c_void_p(sink.data_ptr()), _stream(stream)))
     return sink
+
+
+class Stream:
+    """A streaming cache (kvq_stream of include/kvq.h): the host state and, unless
+    device is None, its caller-owned device buffers (``cache``).  Tokens are
+    appended one at a time (``append``); ``prefill`` starts an empty stream from
+    the one-shot cache of its first tokens."""
+
+    def __init__(self, B, Hq, Hkv, Dk, Dv, capacity, k_bits, v_bits, n_recent=0, log_window=0, device="cuda"):
+        self._c = L_.KvqStream()
+        L_.check(L_.load().kvq_stream_init(ctypes.byref(self._c), B, Hq, Hkv, Dk, Dv, capacity, k_bits, v_bits,
+                                           n_recent, log_window))
+        self.cache = None
+        if device is not None:
+            self.cache = {k: torch.empty(shape, dtype=dt, device=device) for k, (shape, dt) in self.shapes().items()}
+
+    def __getattr__(self, name):
+        if name in L_.STREAM_FIELDS:
+            return getattr(self._c, name)
+        if name in L_.LAYOUT_FIELDS:
+            return getattr(self._c.L, name)
+        raise AttributeError(name)
+
+    @property
+    def capacity(self):
+        return self._c.L.T
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._c)
+
+    def shapes(self):
+        """Shape and dtype of each buffer (capacities g_cap groups, r_cap rows per slab)."""
+        c = self._c
+        B, H, G, R, Dk, Dv = c.L.B, c.L.Hkv, c.g_cap, c.r_cap, c.L.Dk, c.L.Dv
+        return {
+            "k_codes": ((B, H, G * 32, Dk * c.L.k_bits // 32), torch.int32),
+            "k_scale": ((B, H, G, Dk), torch.float16),
+            "k_zero": ((B, H, G, Dk), torch.float16),
+            "v_codes": ((B, H, G, Dv * c.L.v_bits), torch.int32),
+            "v_scale": ((B, H, G, Dv // 32, 32), torch.float16),
+            "v_zero": ((B, H, G, Dv // 32, 32), torch.float16),
+            "k_fp16": ((B, H, R, Dk), torch.float16),
+            "v_fp16": ((B, H, R, Dv), torch.float16),
+        }
+
+    def cache_sizes(self):
+        arr = (ctypes.c_size_t * L_.KVQ_NUM_CACHE_BUFFERS)()
+        L_.check(L_.load().kvq_stream_cache_sizes(self.ref, arr))
+        return dict(zip(L_.CACHE_FIELDS, list(arr)))
+
+    def workspace_bytes(self, num_partitions: int) -> int:
+        return int(L_.load().kvq_stream_workspace_bytes(self.ref, num_partitions))
+
+    def row_positions(self):
+        """Position of the token held by each fp16 row in use."""
+        return list(self._c.row_pos[: self._c.n_rows])
+
+    def pending_rows(self):
+        return [i for i in range(self._c.n_rows) if self._c.row_pending[i]]
+
+    def plan(self):
+        """Host bookkeeping of one append without any GPU work (kvq_stream_plan):
+        advances the state by one token and returns what the device would do."""
+        st = L_.KvqStreamStep()
+        L_.check(L_.load().kvq_stream_plan(self.ref, ctypes.byref(st)))
+        return {"new_row": st.new_row, "group": st.group, "member_rows": list(st.member_rows),
+                "member_pos": list(st.member_pos), "moves": list(zip(st.move_src[: st.n_moves], st.move_dst[: st.n_moves]))}
+
+    def _cache_struct(self):
+        if self.cache is None:
+            raise ValueError("this stream has no device buffers (created with device=None)")
+        c = L_.KvqCache()
+        for k, (shape, dt) in self.shapes().items():
+            t = self.cache[k]
+            if tuple(t.shape) != tuple(shape) or t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError("cache[%r] must be a contiguous CUDA %s tensor of shape %s" % (k, dt, shape))
+            setattr(c, k, t.data_ptr() if t.numel() else None)
+        return c
+
+    def prefill(self, K, V, stream=None):
+        """Start the (empty) stream from K [B, Hkv, T0, Dk], V [B, Hkv, T0, Dv]."""
+        T0 = K.shape[2]
+        _check_tensor("K", K, (self.B, self.Hkv, T0, self.Dk))
+        _check_tensor("V", V, (self.B, self.Hkv, T0, self.Dv))
+        if K.dtype != V.dtype:
+            raise ValueError("K and V must share a dtype")
+        cs = self._cache_struct()
+        L_.check(L_.load().kv_stream_prefill(self.ref, T0, ctypes.c_void_p(K.data_ptr()),
+                                             ctypes.c_void_p(V.data_ptr()), _DTYPE_CODES[K.dtype], ctypes.byref(cs),
+                                             _stream(stream)))
+
+    def append(self, k, v, stream=None):
+        """Append one token: k [B, Hkv, Dk], v [B, Hkv, Dv] on the GPU."""
+        _check_tensor("k", k, (self.B, self.Hkv, self.Dk))
+        _check_tensor("v", v, (self.B, self.Hkv, self.Dv))
+        if k.dtype != v.dtype:
+            raise ValueError("k and v must share a dtype")
+        cs = self._cache_struct()
+        L_.check(L_.load().kv_stream_append(self.ref, ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                            _DTYPE_CODES[k.dtype], ctypes.byref(cs), _stream(stream)))
+
+    def decode(self, q, num_partitions: int = 1, softmax_scale=None, out=None, workspace=None, stream=None):
+        """Decode attention of q [B, Hq, Dk] over the stream's tokens -> float32 [B, Hq, Dv]."""
+        _check_tensor("q", q, (self.B, self.Hq, self.Dk))
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(self.Dk)
+        if out is None:
+            out = torch.empty((self.B, self.Hq, self.Dv), dtype=torch.float32, device=q.device)
+        elif out.dtype != torch.float32 or tuple(out.shape) != (self.B, self.Hq, self.Dv) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 tensor [B, Hq, Dv]")
+        need = self.workspace_bytes(num_partitions)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        cs = self._cache_struct()
+        L_.check(L_.load().kv_stream_decode(self.ref, ctypes.c_void_p(q.data_ptr()), _DTYPE_CODES[q.dtype],
+                                            ctypes.byref(cs), ctypes.c_float(softmax_scale), num_partitions,
+                                            ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(out.data_ptr()),
+                                            _stream(stream)))
+        return out

@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["kvq_api.cpp", "kvq_pack.hip", "kvq_decode_generic.hip", "kvq_decode_mfma.hip", "kvq_decode_merge.hip",
+SOURCES = ["kvq_api.cpp", "kvq_stream.cpp", "kvq_pack.hip", "kvq_append.hip", "kvq_decode_generic.hip",
+           "kvq_decode_mfma.hip", "kvq_decode_merge.hip",
            "kvq_probe.hip"]
 
 FLAGS = [

@@ -16,7 +16,9 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
-int fail(int status, const char* fmt, ...) {
+}  // namespace
+
+int kvq::fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
@@ -24,20 +26,44 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
-int ok() {
+int kvq::ok() {
   g_last_error[0] = '\0';
   return KVQ_OK;
 }
 
-bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
-bool valid_gqa(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+namespace {
+
+using kvq::fail;
+using kvq::ok;
+
+using kvq::aligned16;
+using kvq::valid_bits;
+using kvq::valid_gqa;
 
 kvq::RetentionRule rule_of(const kvq_layout& L) { return kvq::RetentionRule{L.T, L.n_recent, L.log_window}; }
 
 // Full validation of a layout (also of one the caller may have edited by hand).
 int check_layout(const kvq_layout* L) {
   if (!L) return fail(KVQ_ERR_INVALID, "layout is NULL");
+  const int st = kvq::check_format(*L);
+  if (st != KVQ_OK) return st;
+  const int64_t R = kvq::retained_before(rule_of(*L), L->T);
+  const int64_t Tq = L->T - R;
+  if (Tq % KVQ_GROUP != 0)
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "%lld quantized tokens is not a multiple of 32; adjust n_recent so T - R is",
+                (long long)Tq);
+  if (L->R != R || L->Tq != Tq || L->n_groups != Tq / KVQ_GROUP)
+    return fail(KVQ_ERR_INVALID, "layout derived fields are stale; call kvq_layout_init");
+  return ok();
+}
+
+}  // namespace
+
+// Shape, bit widths and retention policy of a layout (T is the token count or a
+// stream's capacity); the derived fields are not looked at.
+int kvq::check_format(const kvq_layout& l) {
+  const kvq_layout* L = &l;
   if (L->B < 1 || L->Hq < 1 || L->Hkv < 1 || L->T < 1)
     return fail(KVQ_ERR_INVALID, "B, Hq, Hkv and T must be >= 1 (got %d, %d, %d, %d)", L->B, L->Hq, L->Hkv, L->T);
   if (L->Hq % L->Hkv != 0) return fail(KVQ_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", L->Hq, L->Hkv);
@@ -52,28 +78,121 @@ int check_layout(const kvq_layout* L) {
   if (L->n_recent < 0 || L->n_recent > L->T)
     return fail(KVQ_ERR_INVALID, "n_recent (%d) must be in [0, T=%d]", L->n_recent, L->T);
   if (L->log_window < 0) return fail(KVQ_ERR_INVALID, "log_window (%d) must be >= 0", L->log_window);
-  const int64_t R = kvq::retained_before(rule_of(*L), L->T);
-  const int64_t Tq = L->T - R;
-  if (Tq % KVQ_GROUP != 0)
-    return fail(KVQ_ERR_UNSUPPORTED,
-                "%lld quantized tokens is not a multiple of 32; adjust n_recent so T - R is",
-                (long long)Tq);
-  if (L->R != R || L->Tq != Tq || L->n_groups != Tq / KVQ_GROUP)
-    return fail(KVQ_ERR_INVALID, "layout derived fields are stale; call kvq_layout_init");
-  // every buffer offset used by the kernels must fit comfortably in int64 and the
-  // per-slab token counts in int32 (T <= INT32_MAX by type)
   return ok();
 }
 
-int check_cache_ptr(const void* p, const char* name) {
+namespace {
+
+using kvq::check_cache_ptr;
+using kvq::valid_dtype;
+
+}  // namespace
+
+int kvq::check_cache_ptr(const void* p, const char* name) {
   if (!p) return fail(KVQ_ERR_INVALID, "cache buffer %s is NULL", name);
   if (!aligned16(p)) return fail(KVQ_ERR_INVALID, "cache buffer %s is not 16-byte aligned", name);
   return KVQ_OK;
 }
 
-bool valid_dtype(int d) { return d == KVQ_F32 || d == KVQ_F16 || d == KVQ_BF16; }
+// Checks and launches of a decode over a cache whose layout fields (R, Tq,
+// n_groups) give the token counts and g_stride / r_stride the slab strides.
+int kvq::decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, const void* q, int q_dtype,
+                     const kvq_cache* cache, float softmax_scale, int num_partitions, void* workspace,
+                     size_t workspace_bytes, float* out, void* stream, void* event_after_decode) {
+  int st;
+  if (!cache) return fail(KVQ_ERR_INVALID, "cache is NULL");
+  if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID, "q_dtype %d is not KVQ_F32/F16/BF16", q_dtype);
+  if (!q || !out) return fail(KVQ_ERR_INVALID, "q or out is NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(KVQ_ERR_INVALID, "q and out must be 16-byte aligned");
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID, "softmax_scale is not finite");
+  const int64_t max_p = (int64_t(L.T) + KVQ_GROUP - 1) / KVQ_GROUP;
+  if (num_partitions < 1 || num_partitions > (max_p > 1 ? max_p : 1))
+    return fail(KVQ_ERR_INVALID, "num_partitions %d must be in [1, %lld]", num_partitions, (long long)max_p);
+  if (num_partitions > 65535) return fail(KVQ_ERR_UNSUPPORTED, "num_partitions %d > 65535", num_partitions);
+  const size_t need = num_partitions == 1 ? 0 : kvq::ws_partial_bytes(L, num_partitions);
+  if (need > 0) {
+    if (!workspace) return fail(KVQ_ERR_INVALID, "workspace is NULL but %zu bytes are needed", need);
+    if (!aligned16(workspace)) return fail(KVQ_ERR_INVALID, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(KVQ_ERR_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  if (L.n_groups > 0) {
+    if ((st = check_cache_ptr(cache->k_codes, "k_codes")) || (st = check_cache_ptr(cache->k_scale, "k_scale")) ||
+        (st = check_cache_ptr(cache->k_zero, "k_zero")) || (st = check_cache_ptr(cache->v_codes, "v_codes")) ||
+        (st = check_cache_ptr(cache->v_scale, "v_scale")) || (st = check_cache_ptr(cache->v_zero, "v_zero")))
+      return st;
+  }
+  if (L.R > 0) {
+    if ((st = check_cache_ptr(cache->k_fp16, "k_fp16")) || (st = check_cache_ptr(cache->v_fp16, "v_fp16")))
+      return st;
+  }
+  if (L.B > 65535 || L.Hkv > 65535) return fail(KVQ_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  kvq::DecodeArgs a{};
+  a.L = L;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.cache = *cache;
+  a.scale = softmax_scale;
+  a.P = num_partitions;
+  a.g_stride = g_stride;
+  a.r_stride = r_stride;
+  if (need > 0) {
+    a.partials = static_cast<float*>(workspace);
+  }
+  a.out = out;
+  const hipError_t e =
+      kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(event_after_decode));
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
 
-}  // namespace
+// Checks and launch of a pack into a cache with slab strides g_stride / r_stride
+// (L is a checked layout of the tokens [0, L.T)).
+int kvq::pack_view(const kvq_layout& Lr, int64_t g_stride, int64_t r_stride, int64_t t_begin, int64_t t_count,
+                   const void* K, const void* V, int kv_dtype, const kvq_cache* cache, void* stream) {
+  const kvq_layout* L = &Lr;
+  int st;
+  if (!cache) return fail(KVQ_ERR_INVALID, "cache is NULL");
+  if (!valid_dtype(kv_dtype)) return fail(KVQ_ERR_INVALID, "kv_dtype %d is not KVQ_F32/F16/BF16", kv_dtype);
+  if (t_begin < 0 || t_count < 1 || t_begin + t_count > L->T)
+    return fail(KVQ_ERR_INVALID, "chunk [%lld, %lld) is not inside [0, %d)", (long long)t_begin,
+                (long long)(t_begin + t_count), L->T);
+  if (!K || !V) return fail(KVQ_ERR_INVALID, "K or V is NULL");
+  if (!aligned16(K) || !aligned16(V)) return fail(KVQ_ERR_INVALID, "K and V must be 16-byte aligned");
+  const kvq::RetentionRule r = rule_of(*L);
+  const int64_t q0 = kvq::quantized_before(r, t_begin), q1 = kvq::quantized_before(r, t_begin + t_count);
+  if (q0 % KVQ_GROUP || q1 % KVQ_GROUP)
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "chunk [%lld, %lld) splits a key group (%lld and %lld quantized tokens before its ends)",
+                (long long)t_begin, (long long)(t_begin + t_count), (long long)q0, (long long)q1);
+  kvq::PackArgs a{};
+  a.L = *L;
+  a.t_begin = t_begin;
+  a.t_count = t_count;
+  a.g_begin = q0 / KVQ_GROUP;
+  a.n_groups_chunk = (q1 - q0) / KVQ_GROUP;
+  a.r_begin = t_begin - q0;
+  a.n_ret_chunk = (t_begin + t_count - q1) - a.r_begin;
+  a.K = K;
+  a.V = V;
+  a.dtype = kv_dtype;
+  a.cache = *cache;
+  a.g_stride = g_stride;
+  a.r_stride = r_stride;
+  if (a.n_groups_chunk > 0) {
+    if ((st = check_cache_ptr(cache->k_codes, "k_codes")) || (st = check_cache_ptr(cache->k_scale, "k_scale")) ||
+        (st = check_cache_ptr(cache->k_zero, "k_zero")) || (st = check_cache_ptr(cache->v_codes, "v_codes")) ||
+        (st = check_cache_ptr(cache->v_scale, "v_scale")) || (st = check_cache_ptr(cache->v_zero, "v_zero")))
+      return st;
+  }
+  if (a.n_ret_chunk > 0) {
+    if ((st = check_cache_ptr(cache->k_fp16, "k_fp16")) || (st = check_cache_ptr(cache->v_fp16, "v_fp16")))
+      return st;
+  }
+  const hipError_t e = kvq::launch_pack(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "pack launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
 
 extern "C" {
 
@@ -152,46 +271,9 @@ size_t kvq_decode_workspace_bytes(const kvq_layout* L, int num_partitions) {
 
 int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count, const void* K, const void* V,
                   int kv_dtype, const kvq_cache* cache, void* stream) {
-  int st = check_layout(L);
+  const int st = check_layout(L);
   if (st != KVQ_OK) return st;
-  if (!cache) return fail(KVQ_ERR_INVALID, "cache is NULL");
-  if (!valid_dtype(kv_dtype)) return fail(KVQ_ERR_INVALID, "kv_dtype %d is not KVQ_F32/F16/BF16", kv_dtype);
-  if (t_begin < 0 || t_count < 1 || t_begin + t_count > L->T)
-    return fail(KVQ_ERR_INVALID, "chunk [%lld, %lld) is not inside [0, %d)", (long long)t_begin,
-                (long long)(t_begin + t_count), L->T);
-  if (!K || !V) return fail(KVQ_ERR_INVALID, "K or V is NULL");
-  if (!aligned16(K) || !aligned16(V)) return fail(KVQ_ERR_INVALID, "K and V must be 16-byte aligned");
-  const kvq::RetentionRule r = rule_of(*L);
-  const int64_t q0 = kvq::quantized_before(r, t_begin), q1 = kvq::quantized_before(r, t_begin + t_count);
-  if (q0 % KVQ_GROUP || q1 % KVQ_GROUP)
-    return fail(KVQ_ERR_UNSUPPORTED,
-                "chunk [%lld, %lld) splits a key group (%lld and %lld quantized tokens before its ends)",
-                (long long)t_begin, (long long)(t_begin + t_count), (long long)q0, (long long)q1);
-  kvq::PackArgs a{};
-  a.L = *L;
-  a.t_begin = t_begin;
-  a.t_count = t_count;
-  a.g_begin = q0 / KVQ_GROUP;
-  a.n_groups_chunk = (q1 - q0) / KVQ_GROUP;
-  a.r_begin = t_begin - q0;
-  a.n_ret_chunk = (t_begin + t_count - q1) - a.r_begin;
-  a.K = K;
-  a.V = V;
-  a.dtype = kv_dtype;
-  a.cache = *cache;
-  if (a.n_groups_chunk > 0) {
-    if ((st = check_cache_ptr(cache->k_codes, "k_codes")) || (st = check_cache_ptr(cache->k_scale, "k_scale")) ||
-        (st = check_cache_ptr(cache->k_zero, "k_zero")) || (st = check_cache_ptr(cache->v_codes, "v_codes")) ||
-        (st = check_cache_ptr(cache->v_scale, "v_scale")) || (st = check_cache_ptr(cache->v_zero, "v_zero")))
-      return st;
-  }
-  if (a.n_ret_chunk > 0) {
-    if ((st = check_cache_ptr(cache->k_fp16, "k_fp16")) || (st = check_cache_ptr(cache->v_fp16, "v_fp16")))
-      return st;
-  }
-  const hipError_t e = kvq::launch_pack(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "pack launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return kvq::pack_view(*L, L->n_groups, L->R, t_begin, t_count, K, V, kv_dtype, cache, stream);
 }
 
 int kv_decode_attn(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache, float softmax_scale,
@@ -203,50 +285,10 @@ int kv_decode_attn(const kvq_layout* L, const void* q, int q_dtype, const kvq_ca
 int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache, float softmax_scale,
                       int num_partitions, void* workspace, size_t workspace_bytes, float* out, void* stream,
                       void* event_after_decode) {
-  int st = check_layout(L);
+  const int st = check_layout(L);
   if (st != KVQ_OK) return st;
-  if (!cache) return fail(KVQ_ERR_INVALID, "cache is NULL");
-  if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID, "q_dtype %d is not KVQ_F32/F16/BF16", q_dtype);
-  if (!q || !out) return fail(KVQ_ERR_INVALID, "q or out is NULL");
-  if (!aligned16(q) || !aligned16(out)) return fail(KVQ_ERR_INVALID, "q and out must be 16-byte aligned");
-  if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID, "softmax_scale is not finite");
-  const int64_t max_p = (int64_t(L->T) + KVQ_GROUP - 1) / KVQ_GROUP;
-  if (num_partitions < 1 || num_partitions > (max_p > 1 ? max_p : 1))
-    return fail(KVQ_ERR_INVALID, "num_partitions %d must be in [1, %lld]", num_partitions, (long long)max_p);
-  if (num_partitions > 65535) return fail(KVQ_ERR_UNSUPPORTED, "num_partitions %d > 65535", num_partitions);
-  const size_t need = kvq_decode_workspace_bytes(L, num_partitions);
-  if (need > 0) {
-    if (!workspace) return fail(KVQ_ERR_INVALID, "workspace is NULL but %zu bytes are needed", need);
-    if (!aligned16(workspace)) return fail(KVQ_ERR_INVALID, "workspace is not 16-byte aligned");
-    if (workspace_bytes < need)
-      return fail(KVQ_ERR_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-  }
-  if (L->n_groups > 0) {
-    if ((st = check_cache_ptr(cache->k_codes, "k_codes")) || (st = check_cache_ptr(cache->k_scale, "k_scale")) ||
-        (st = check_cache_ptr(cache->k_zero, "k_zero")) || (st = check_cache_ptr(cache->v_codes, "v_codes")) ||
-        (st = check_cache_ptr(cache->v_scale, "v_scale")) || (st = check_cache_ptr(cache->v_zero, "v_zero")))
-      return st;
-  }
-  if (L->R > 0) {
-    if ((st = check_cache_ptr(cache->k_fp16, "k_fp16")) || (st = check_cache_ptr(cache->v_fp16, "v_fp16")))
-      return st;
-  }
-  if (L->B > 65535 || L->Hkv > 65535) return fail(KVQ_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
-  kvq::DecodeArgs a{};
-  a.L = *L;
-  a.q = q;
-  a.q_dtype = q_dtype;
-  a.cache = *cache;
-  a.scale = softmax_scale;
-  a.P = num_partitions;
-  if (need > 0) {
-    a.partials = static_cast<float*>(workspace);
-  }
-  a.out = out;
-  const hipError_t e =
-      kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(event_after_decode));
-  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return kvq::decode_view(*L, L->n_groups, L->R, q, q_dtype, cache, softmax_scale, num_partitions, workspace,
+                          workspace_bytes, out, stream, event_after_decode);
 }
 
 int kvq_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {

@@ -1,0 +1,160 @@
+// kv_stream_append kernel for gfx950: one decode-time token into a streaming cache.
+//
+// LogQuant: Log-Distributed 2-Bit Quantization of KV Cache (technical summary,
+// section 2, dynamic adjustment; section 4, order-free attention).  The host
+// decides what a step does (the same for every slab); one workgroup per (batch
+// row, kv head) slab then
+//   1. writes the token's fp16 row (round to nearest even);
+//   2. when a group forms, quantizes its 32 fp16 rows with the quantizer contract
+//      of kvq.h: keys per channel over the 32 tokens, values per token over each
+//      32-channel group, codes in the group formats of kvq.h;
+//   3. moves fp16 rows past the new end into the rows the group freed.
+// The appended token's values are taken from the input wherever step 2 or 3
+// needs them, so no thread reads what another thread of the launch has stored.
+// This is a latency-bound launch (a few KB per slab); it favours plain code.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.hpp"
+#include "kvq_vlayout.hpp"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+namespace {
+
+constexpr int kAppendThreads = 256;
+
+__device__ inline float load_as_f32(const void* p, int dtype, int64_t i) {
+  if (dtype == KVQ_F32) return static_cast<const float*>(p)[i];
+  if (dtype == KVQ_F16) return __half2float(static_cast<const __half*>(p)[i]);
+  return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);  // bf16
+}
+__device__ inline uint16_t to_f16_bits(float x) { return __half_as_ushort(__float2half_rn(x)); }
+__device__ inline float f16_to_f32(uint16_t b) { return __half2float(__ushort_as_half(b)); }
+
+struct Quant {
+  float s, z;
+  uint16_t sb, zb;
+};
+
+// s = fp16(fp32(mx - mn) / (2^bits - 1)), z = fp16(mn), a zero of either sign
+// stored as +0
+__device__ inline Quant quant_params(float mn, float mx, float levels) {
+  Quant q;
+  q.sb = to_f16_bits((mx - mn) / levels);
+  q.zb = to_f16_bits(mn);
+  if ((q.sb & 0x7fffu) == 0) q.sb = 0;
+  if ((q.zb & 0x7fffu) == 0) q.zb = 0;
+  q.s = f16_to_f32(q.sb);
+  q.z = f16_to_f32(q.zb);
+  return q;
+}
+
+// code = clamp(rint((x - z) / s), 0, levels) with the correctly rounded division;
+// 0 when s == 0
+__device__ inline uint32_t quant_code(float x, const Quant& q, float levels) {
+  if (q.s == 0.0f) return 0u;
+  const float t = __builtin_rintf((x - q.z) / q.s);
+  return uint32_t(fminf(fmaxf(t, 0.0f), levels));
+}
+
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
+  __shared__ uint32_t vw[KVQ_MAX_HEAD_DIM * 8];  // value code words of the group (Dv * vb <= 2048)
+  const int64_t slab = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int Dk = a.L.Dk, Dv = a.L.Dv, kb = a.L.k_bits, vb = a.L.v_bits;
+  uint16_t* kf = static_cast<uint16_t*>(a.cache.k_fp16) + slab * a.r_stride * Dk;
+  uint16_t* vf = static_cast<uint16_t*>(a.cache.v_fp16) + slab * a.r_stride * Dv;
+  // the appended token's fp16 value of key / value channel c
+  auto k_new16 = [&](int c) { return to_f16_bits(load_as_f32(a.k_new, a.dtype, slab * Dk + c)); };
+  auto v_new16 = [&](int c) { return to_f16_bits(load_as_f32(a.v_new, a.dtype, slab * Dv + c)); };
+
+  // 1. the token's row
+  for (int c = tid; c < Dk; c += kAppendThreads) kf[int64_t(a.new_row) * Dk + c] = k_new16(c);
+  for (int c = tid; c < Dv; c += kAppendThreads) vf[int64_t(a.new_row) * Dv + c] = v_new16(c);
+  if (a.group < 0) return;  // the same for every thread: no barrier below is reached
+
+  // 2. the group
+  for (int i = tid; i < Dv * vb; i += kAppendThreads) vw[i] = 0u;
+  __syncthreads();
+  const int64_t gi = slab * a.g_stride + a.group;
+  auto k_row = [&](int j, int c) {
+    const int row = a.member_rows[j];
+    return f16_to_f32(row == a.new_row ? k_new16(c) : kf[int64_t(row) * Dk + c]);
+  };
+  auto v_row = [&](int j, int c) {
+    const int row = a.member_rows[j];
+    return f16_to_f32(row == a.new_row ? v_new16(c) : vf[int64_t(row) * Dv + c]);
+  };
+  // keys: thread c takes channel c over the 32 tokens; the 32/kb channels of a code
+  // word are adjacent lanes, OR-ed together with lane exchanges
+  const float klev = float((1 << kb) - 1), vlev = float((1 << vb) - 1);
+  const int per = 32 / kb, kwords = Dk * kb / 32;
+  for (int c = tid; c < Dk; c += kAppendThreads) {
+    float x[KVQ_GROUP];
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < KVQ_GROUP; ++j) {
+      x[j] = k_row(j, c);
+      mn = fminf(mn, x[j]);
+      mx = fmaxf(mx, x[j]);
+    }
+    const Quant q = quant_params(mn, mx, klev);
+    static_cast<uint16_t*>(a.cache.k_scale)[gi * Dk + c] = q.sb;
+    static_cast<uint16_t*>(a.cache.k_zero)[gi * Dk + c] = q.zb;
+    uint32_t* kc = static_cast<uint32_t*>(a.cache.k_codes) + gi * KVQ_GROUP * kwords;
+#pragma unroll
+    for (int j = 0; j < KVQ_GROUP; ++j) {
+      uint32_t w = quant_code(x[j], q, klev) << ((c % per) * kb);
+      for (int o = 1; o < per; o <<= 1) w |= uint32_t(__shfl_xor(int(w), o));
+      if (c % per == 0) kc[j * kwords + c / per] = w;
+    }
+  }
+  // values: element e = (token j, channel c); the 32 lanes of a channel group are
+  // adjacent and reduce min / max with lane exchanges; codes are OR-ed into the
+  // group's bit stream in LDS
+  for (int e = tid; e < KVQ_GROUP * Dv; e += kAppendThreads) {
+    const int j = e / Dv, c = e - j * Dv;
+    const float x = v_row(j, c);
+    float mn = x, mx = x;
+    for (int o = 16; o >= 1; o >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o));
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    const Quant q = quant_params(mn, mx, vlev);
+    if ((c & 31) == 0) {
+      const int64_t si = (gi * (Dv / KVQ_GROUP) + c / KVQ_GROUP) * KVQ_GROUP + j;
+      static_cast<uint16_t*>(a.cache.v_scale)[si] = q.sb;
+      static_cast<uint16_t*>(a.cache.v_zero)[si] = q.zb;
+    }
+    const int bit = value_bit_position(j, c, Dv, vb);
+    atomicOr(&vw[bit >> 5], quant_code(x, q, vlev) << (bit & 31));
+  }
+  __syncthreads();  // the group's rows have been read and its value words are complete
+  uint32_t* vc = static_cast<uint32_t*>(a.cache.v_codes) + gi * (Dv * vb);
+  for (int i = tid; i < Dv * vb; i += kAppendThreads) vc[i] = vw[i];
+
+  // 3. moves: sources lie past the new end, destinations are freed rows
+  for (int e = tid; e < a.n_moves * Dk; e += kAppendThreads) {
+    const int m = e / Dk, c = e - m * Dk;
+    const int src = a.move_src[m];
+    kf[int64_t(a.move_dst[m]) * Dk + c] = src == a.new_row ? k_new16(c) : kf[int64_t(src) * Dk + c];
+  }
+  for (int e = tid; e < a.n_moves * Dv; e += kAppendThreads) {
+    const int m = e / Dv, c = e - m * Dv;
+    const int src = a.move_src[m];
+    vf[int64_t(a.move_dst[m]) * Dv + c] = src == a.new_row ? v_new16(c) : vf[int64_t(src) * Dv + c];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  const int64_t slabs = int64_t(a.L.B) * a.L.Hkv;
+  if (slabs < 1 || slabs > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(append_kernel, dim3(unsigned(slabs)), dim3(kAppendThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Dk = a.L.Dk, Dv = a.L.Dv, kb = a.L.k_bits, vb = a.L.v_bits;
   const int ngv = Dv / KVQ_GROUP;
-  const int nG = a.L.n_groups, R = a.L.R, P = a.P, Tq = a.L.Tq;
+  const int nG = a.L.n_groups, R = a.L.R, P = a.P;
   const int64_t slab = int64_t(b) * a.L.Hkv + h;
 
   const int g0 = int(int64_t(p) * nG / P), g1 = int(int64_t(p + 1) * nG / P);
@@ -146,8 +146,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     float bias[G];
     if (active) {
       // q'_c = q_c s_c for this group and the zero-point term sum_c q_c z_c
-      const uint16_t* ks = static_cast<const uint16_t*>(a.cache.k_scale) + (slab * nG + g) * Dk;
-      const uint16_t* kz = static_cast<const uint16_t*>(a.cache.k_zero) + (slab * nG + g) * Dk;
+      const uint16_t* ks = static_cast<const uint16_t*>(a.cache.k_scale) + (slab * a.g_stride + g) * Dk;
+      const uint16_t* kz = static_cast<const uint16_t*>(a.cache.k_zero) + (slab * a.g_stride + g) * Dk;
 #pragma unroll
       for (int i = 0; i < G; ++i) bias[i] = 0.0f;
       for (int c = lane; c < Dk; c += 64) {
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     float pv[G];
     if (active) {
       // scores: lane (t, hf) takes token t and half the key channels
-      const uint32_t* row = static_cast<const uint32_t*>(a.cache.k_codes) + (slab * Tq + int64_t(g) * KVQ_GROUP + t) * kw;
+      const uint32_t* row = static_cast<const uint32_t*>(a.cache.k_codes) + ((slab * a.g_stride + g) * KVQ_GROUP + t) * kw;
       float acc[G];
 #pragma unroll
       for (int i = 0; i < G; ++i) acc[i] = 0.0f;
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
       softmax_update<G>(st, s, pv);
 
       // p_t s_t,g into LDS and the zero-point sums
-      const int64_t vblk = (slab * nG + g) * ngv * KVQ_GROUP;
+      const int64_t vblk = (slab * a.g_stride + g) * ngv * KVQ_GROUP;
       const uint16_t* vs = static_cast<const uint16_t*>(a.cache.v_scale) + vblk;
       const uint16_t* vz = static_cast<const uint16_t*>(a.cache.v_zero) + vblk;
       for (int gc = 0; gc < ngv; ++gc) {
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     if (active) {
       // values: lane owns channels c = lane + 64 j; codes read from the group's
       // bit stream (layout in kvq_vlayout.hpp)
-      const uint32_t* vc = static_cast<const uint32_t*>(a.cache.v_codes) + (slab * nG + g) * (Dv * vb);
+      const uint32_t* vc = static_cast<const uint32_t*>(a.cache.v_codes) + (slab * a.g_stride + g) * (Dv * vb);
       for (int tt = 0; tt < KVQ_GROUP; ++tt) {
 #pragma unroll
         for (int j = 0; j < kMaxVChansPerLane; ++j) {
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < G; ++i) acc[i] = 0.0f;
       if (valid) {
-        const uint16_t* krow = static_cast<const uint16_t*>(a.cache.k_fp16) + (slab * R + r) * Dk;
+        const uint16_t* krow = static_cast<const uint16_t*>(a.cache.k_fp16) + (slab * a.r_stride + r) * Dk;
         for (int c = hf * (Dk / 2); c < (hf + 1) * (Dk / 2); ++c) {
           const float kv = h2f(krow[c]);
 #pragma unroll
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     if (active) {
       const int nrow = min(KVQ_GROUP, r1 - rbeg);
       for (int tt = 0; tt < nrow; ++tt) {
-        const uint16_t* vrow = static_cast<const uint16_t*>(a.cache.v_fp16) + (slab * R + rbeg + tt) * Dv;
+        const uint16_t* vrow = static_cast<const uint16_t*>(a.cache.v_fp16) + (slab * a.r_stride + rbeg + tt) * Dv;
 #pragma unroll
         for (int j = 0; j < kMaxVChansPerLane; ++j) {
           const int c = lane + 64 * j;

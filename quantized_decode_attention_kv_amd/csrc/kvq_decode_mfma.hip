@@ -424,12 +424,12 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   const int nj = g1 - g0;
 
   // per-slab bases (wave-uniform)
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.cache.k_codes) + slab * int64_t(a.L.Tq) * KROW;
-  const uint16_t* ksbase = static_cast<const uint16_t*>(a.cache.k_scale) + slab * int64_t(nG) * DK;
-  const uint16_t* kzbase = static_cast<const uint16_t*>(a.cache.k_zero) + slab * int64_t(nG) * DK;
-  const uint32_t* vbase = static_cast<const uint32_t*>(a.cache.v_codes) + slab * int64_t(nG) * (DV * VB);
-  const uint16_t* vsbase = static_cast<const uint16_t*>(a.cache.v_scale) + slab * int64_t(nG) * DV;
-  const uint16_t* vzbase = static_cast<const uint16_t*>(a.cache.v_zero) + slab * int64_t(nG) * DV;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.cache.k_codes) + slab * a.g_stride * (KVQ_GROUP * KROW);
+  const uint16_t* ksbase = static_cast<const uint16_t*>(a.cache.k_scale) + slab * a.g_stride * DK;
+  const uint16_t* kzbase = static_cast<const uint16_t*>(a.cache.k_zero) + slab * a.g_stride * DK;
+  const uint32_t* vbase = static_cast<const uint32_t*>(a.cache.v_codes) + slab * a.g_stride * (DV * VB);
+  const uint16_t* vsbase = static_cast<const uint16_t*>(a.cache.v_scale) + slab * a.g_stride * DV;
+  const uint16_t* vzbase = static_cast<const uint16_t*>(a.cache.v_zero) + slab * a.g_stride * DV;
 
   // Q' task of this lane: (block tb = 8-channel block kk_t of lane group gq_t,
   // query i_t); it also forms the block's key zero-point partial sum
@@ -846,8 +846,8 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
       B2[e] = v;
     }
     wave_lds_sync();
-    const uint8_t* kr = static_cast<const uint8_t*>(a.cache.k_fp16) + slab * int64_t(R) * (DK * 2);
-    const uint8_t* vr = static_cast<const uint8_t*>(a.cache.v_fp16) + slab * int64_t(R) * (DV * 2);
+    const uint8_t* kr = static_cast<const uint8_t*>(a.cache.k_fp16) + slab * a.r_stride * (DK * 2);
+    const uint8_t* vr = static_cast<const uint8_t*>(a.cache.v_fp16) + slab * a.r_stride * (DV * 2);
     for (int rt = rt0; rt < rt1; ++rt) {
       const int rbase = rt * 32;
       f32x4 sacc[2];

@@ -14,6 +14,7 @@ struct PackArgs {
   int64_t t_begin, t_count;
   int64_t g_begin, n_groups_chunk;   // key groups the chunk owns
   int64_t r_begin, n_ret_chunk;      // retained rows the chunk owns
+  int64_t g_stride, r_stride;        // key groups / fp16 rows per slab in the cache arrays
   const void* K;
   const void* V;
   int dtype;
@@ -27,6 +28,7 @@ struct DecodeArgs {
   kvq_cache cache;
   float scale;
   int P;
+  int64_t g_stride, r_stride;  // key groups / fp16 rows per slab in the cache arrays (>= n_groups, R)
   int units;           // work units per slab of the matrix-core kernel (set by its launcher)
   int ranks;           // waves per SIMD the matrix-core grid puts on the device at once (1..4)
   float* partials;     // [B * Hq, units, Dv + 4]: m (log2 domain), l, 2 unused, unnormalised o (P > 1)
@@ -56,11 +58,45 @@ inline size_t ws_partial_bytes(const kvq_layout& L, int P) {
   return size_t(L.B) * size_t(L.Hq) * units * size_t(L.Dv + 4) * sizeof(float);
 }
 
+// One streaming append on the device (kv_stream_append): one workgroup per slab
+// writes the token's fp16 row, packs the group the step forms (if any) from its
+// fp16 rows and moves rows into the freed ones, in that order.
+struct AppendArgs {
+  kvq_layout L;                 // format (B, Hkv, Dk, Dv, bits)
+  int64_t g_stride, r_stride;   // group / fp16-row capacity per slab
+  const void* k_new;            // [B, Hkv, Dk] of dtype
+  const void* v_new;            // [B, Hkv, Dv] of dtype
+  int dtype;
+  int new_row;                  // row of the appended token
+  int group;                    // group formed, -1 for none
+  int member_rows[KVQ_GROUP];   // its tokens' rows, ascending position
+  int n_moves;
+  int move_src[KVQ_GROUP], move_dst[KVQ_GROUP];
+  kvq_cache cache;
+};
+
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 // Decode kernel (matrix-core kernel where it applies, else the generic one)
 // followed, when P > 1, by the partition merge; after_decode (if not null) is
 // recorded on the stream between the two.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t after_decode);
+
+// Host helpers of the C ABI layer (kvq_api.cpp), shared with the streaming
+// entry points (kvq_stream.cpp).
+int fail(int status, const char* fmt, ...);  // sets the thread's last-error text, returns status
+int ok();                                     // clears it, returns KVQ_OK
+inline bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
+inline bool valid_gqa(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+inline bool valid_dtype(int d) { return d == KVQ_F32 || d == KVQ_F16 || d == KVQ_BF16; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int check_cache_ptr(const void* p, const char* name);
+int check_format(const kvq_layout& L);
+int pack_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, int64_t t_begin, int64_t t_count,
+              const void* K, const void* V, int kv_dtype, const kvq_cache* cache, void* stream);
+int decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, const void* q, int q_dtype,
+                const kvq_cache* cache, float softmax_scale, int num_partitions, void* workspace,
+                size_t workspace_bytes, float* out, void* stream, void* event_after_decode);
 
 }  // namespace kvq

@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
         mx = fmaxf(mx, kmx_s[w][c]);
       }
       const QParams q = make_qparams(mn, mx, k_levels);
-      const int64_t so = (slab * a.L.n_groups + g) * Dk + c;
+      const int64_t so = (slab * a.g_stride + g) * Dk + c;
       static_cast<uint16_t*>(a.cache.k_scale)[so] = q.s_bits;
       static_cast<uint16_t*>(a.cache.k_zero)[so] = q.z_bits;
       ks_s[c] = q.s;
@@ -344,12 +344,12 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
     __syncthreads();
 
     // contiguous stores of the group's key words, value stream and value scale / zero
-    uint32_t* kdst = static_cast<uint32_t*>(a.cache.k_codes) + (slab * a.L.Tq + g * KVQ_GROUP) * kwords;
+    uint32_t* kdst = static_cast<uint32_t*>(a.cache.k_codes) + ((slab * a.g_stride + g) * KVQ_GROUP) * kwords;
     for (int i = tid; i < KVQ_GROUP * kwords; i += kPackThreads) kdst[i] = kw_s[i];
-    uint32_t* vdst = static_cast<uint32_t*>(a.cache.v_codes) + (slab * a.L.n_groups + g) * vwords;
+    uint32_t* vdst = static_cast<uint32_t*>(a.cache.v_codes) + (slab * a.g_stride + g) * vwords;
     for (int i = tid; i < vwords; i += kPackThreads) vdst[i] = vw_s[i];
     const int ngv = Dv / KVQ_GROUP;
-    const int64_t vso = (slab * a.L.n_groups + g) * ngv * KVQ_GROUP;
+    const int64_t vso = (slab * a.g_stride + g) * ngv * KVQ_GROUP;
     for (int i = tid; i < ngv * KVQ_GROUP; i += kPackThreads) {
       static_cast<uint16_t*>(a.cache.v_scale)[vso + i] = vs_s[i / KVQ_GROUP][i % KVQ_GROUP];
       static_cast<uint16_t*>(a.cache.v_zero)[vso + i] = vz_s[i / KVQ_GROUP][i % KVQ_GROUP];
@@ -362,8 +362,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
     if (j >= a.n_ret_chunk) return;
     const int64_t r = a.r_begin + j;                           // rank among all retained rows
     const int64_t row = retained_position(rr, r) - a.t_begin;  // row in the chunk
-    uint16_t* kd = static_cast<uint16_t*>(a.cache.k_fp16) + (slab * a.L.R + r) * Dk;
-    uint16_t* vd = static_cast<uint16_t*>(a.cache.v_fp16) + (slab * a.L.R + r) * Dv;
+    uint16_t* kd = static_cast<uint16_t*>(a.cache.k_fp16) + (slab * a.r_stride + r) * Dk;
+    uint16_t* vd = static_cast<uint16_t*>(a.cache.v_fp16) + (slab * a.r_stride + r) * Dv;
     for (int c = lt; c < Dk; c += kPackThreads / kRetRowsPerBlock)
       kd[c] = f16_bits_rne(load_elem<DT>(a.K, (slab * a.t_count + row) * Dk + c));
     for (int c = lt; c < Dv; c += kPackThreads / kRetRowsPerBlock)

@@ -66,4 +66,17 @@ __host__ __device__ inline int64_t retained_position(const RetentionRule& r, int
   return lo;
 }
 
+// Whether position p (0 <= p < t) is retained when the cache holds t tokens (the
+// rule above with T = t, per position): the newest n_recent, else with W > 0 the
+// span j >= 1 holding the distance d = t - p (W 2^(j-1) < d <= W 2^j) keeps the
+// multiples of 2^j.
+__host__ __device__ inline bool retained_at(int64_t p, int64_t t, int64_t n_recent, int64_t W) {
+  const int64_t d = t - p;
+  if (d <= n_recent) return true;
+  if (W <= 0 || d <= W) return false;
+  int j = 1;
+  while ((W << j) < d) ++j;
+  return (p & ((int64_t(1) << j) - 1)) == 0;
+}
+
 }  // namespace kvq
