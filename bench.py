@@ -11,6 +11,11 @@ Prints one JSON line.  ``value`` is the effective HBM throughput of a whole step
 the algorithmic bytes of the step (each packed byte, scale, zero, fp16 row, query
 and output moved once; the prefill chunk read once and its packed form written
 once) divided by the measured step time.
+
+Beside the step (not part of ``value``), the ``stream`` object times the streaming
+cache at the same shape: after a prefill to just under the full length, decode
+steps that append one token per sequence (kv_stream_append) and then attend over
+the stream (kv_stream_decode), each call bracketed by events.
 """
 
 import argparse
@@ -175,6 +180,63 @@ def read_ceiling(torch, api, nbytes, dev, reps=20):
             "how": "kvq_read_probe: grid-wide streaming read of the decode's byte count, median of %d calls" % reps}
 
 
+def stream_setup(torch, api, w, Kd, Vd, n_steps):
+    """A streaming cache at the workload's shape, prefilled to the longest length
+    (<= T - n_steps) whose quantized count is a multiple of 32, and the K/V rows of
+    the n_steps tokens that follow (one contiguous [B, Hkv, D] tensor each)."""
+    T0 = w.T - n_steps
+    while T0 > 0:
+        try:
+            api.Layout(w.B, w.Hq, w.Hkv, w.Dk, w.Dv, T0, w.k_bits, w.v_bits, min(w.n_recent, T0), w.log_window)
+            break
+        except api.L_.KvqError:
+            T0 -= 1
+    s = api.Stream(w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T, w.k_bits, w.v_bits, w.n_recent, w.log_window)
+    s.prefill(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous())
+    toks = [(Kd[:, :, t].contiguous(), Vd[:, :, t].contiguous()) for t in range(T0, T0 + n_steps)]
+    torch.cuda.synchronize()
+    return {"s": s, "T0": T0, "toks": toks}
+
+
+def stream_run(torch, st, qd, P, scale):
+    """Decode steps on the streaming cache: append one token per sequence, then
+    attend over the stream.  Events bracket each call on the current stream, so an
+    append's time includes the host-side planning and launch of that call (the GPU
+    waits for it)."""
+    s, toks = st["s"], st["toks"]
+    n = len(toks)
+    ws = torch.empty(max(16, s.workspace_bytes(P)), dtype=torch.uint8, device=qd.device)
+    out = torch.empty((s.B, s.Hq, s.Dv), dtype=torch.float32, device=qd.device)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    formed = []
+    torch.cuda.synchronize()
+    host = 0.0
+    for i, (k, v) in enumerate(toks):
+        g0 = s.n_groups
+        ev[i][0].record()
+        h0 = time.perf_counter()
+        s.append(k, v)
+        host += time.perf_counter() - h0
+        ev[i][1].record()
+        s.decode(qd, num_partitions=P, softmax_scale=scale, out=out, workspace=ws)
+        ev[i][2].record()
+        formed.append(s.n_groups > g0)
+    torch.cuda.synchronize()
+    app = [e[0].elapsed_time(e[1]) for e in ev]
+    dec = [e[1].elapsed_time(e[2]) for e in ev]
+    with_group = [a for a, f in zip(app, formed) if f]
+    plain = [a for a, f in zip(app, formed) if not f]
+    return {
+        "prefill_tokens": st["T0"], "decode_steps": n, "groups_formed": len(with_group),
+        "tokens_after": s.t, "fp16_rows": s.n_rows,
+        "append_us_p10_p50_p90": percentiles(plain),
+        "append_with_group_us_p10_p50_p90": percentiles(with_group) if with_group else None,
+        "append_host_us_per_call": round(host * 1e6 / n, 2),
+        "decode_us_p10_p50_p90": percentiles(dec),
+        "step_us_mean": round(sum(a + d for a, d in zip(app, dec)) * 1e3 / n, 2),
+    }
+
+
 def percentiles(xs):
     xs = sorted(xs)
     pick = lambda f: xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]
@@ -190,6 +252,8 @@ def main():
                     help="workload name (the headline step is long_128k; others are for exploration)")
     ap.add_argument("--partitions", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streaming-cache leg")
+    ap.add_argument("--stream-steps", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -218,6 +282,7 @@ def main():
     if chunk:
         Kc = Kd[:, :, t0:].contiguous()
         Vc = Vd[:, :, t0:].contiguous()
+    stream = None if args.no_stream else stream_setup(torch, api, w, Kd, Vd, args.stream_steps)
     del Kd, Vd
     ws = api.alloc_workspace(lay, P, dev)
     out = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.float32, device=dev)
@@ -312,6 +377,9 @@ def main():
                      "kernel_us": round(kern_ms * 1e3, 2),
                      "kernel_source_sha256_16": kernel_source_hash()},
     }
+    if stream is not None:
+        print("# %s: streaming cache, %d decode steps" % (w.name, args.stream_steps), file=sys.stderr, flush=True)
+        result["stream"] = stream_run(torch, stream, qd, P, scale)
     if not args.no_cpu_baseline:
         print("# %s: cpu baseline (oracle)" % w.name, file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, step_bytes)

@@ -11,7 +11,8 @@
 //   3. moves fp16 rows past the new end into the rows the group freed.
 // The appended token's values are taken from the input wherever step 2 or 3
 // needs them, so no thread reads what another thread of the launch has stored.
-// This is a latency-bound launch (a few KB per slab); it favours plain code.
+// This is a latency-bound launch (a few KB per slab): 1024 threads per slab keep
+// the dependent chains short (4 key tokens and 4 value elements per thread).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -23,7 +24,8 @@
 namespace kvq {
 namespace {
 
-constexpr int kAppendThreads = 256;
+constexpr int kAppendThreads = 1024;
+constexpr int kSlices = 8;  // key token slices of 4 tokens: (channel, slice) per thread
 
 __device__ inline float load_as_f32(const void* p, int dtype, int64_t i) {
   if (dtype == KVQ_F32) return static_cast<const float*>(p)[i];
@@ -59,11 +61,13 @@ __device__ inline uint32_t quant_code(float x, const Quant& q, float levels) {
   return uint32_t(fminf(fmaxf(t, 0.0f), levels));
 }
 
+template <int KB, int VB>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
-  __shared__ uint32_t vw[KVQ_MAX_HEAD_DIM * 8];  // value code words of the group (Dv * vb <= 2048)
+  __shared__ uint32_t vw[KVQ_MAX_HEAD_DIM * VB];             // value code words of the group
+  __shared__ float kmn[kSlices][KVQ_MAX_HEAD_DIM], kmx[kSlices][KVQ_MAX_HEAD_DIM];
   const int64_t slab = blockIdx.x;
   const int tid = threadIdx.x;
-  const int Dk = a.L.Dk, Dv = a.L.Dv, kb = a.L.k_bits, vb = a.L.v_bits;
+  const int Dk = a.L.Dk, Dv = a.L.Dv;
   uint16_t* kf = static_cast<uint16_t*>(a.cache.k_fp16) + slab * a.r_stride * Dk;
   uint16_t* vf = static_cast<uint16_t*>(a.cache.v_fp16) + slab * a.r_stride * Dv;
   // the appended token's fp16 value of key / value channel c
@@ -71,13 +75,12 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   auto v_new16 = [&](int c) { return to_f16_bits(load_as_f32(a.v_new, a.dtype, slab * Dv + c)); };
 
   // 1. the token's row
-  for (int c = tid; c < Dk; c += kAppendThreads) kf[int64_t(a.new_row) * Dk + c] = k_new16(c);
-  for (int c = tid; c < Dv; c += kAppendThreads) vf[int64_t(a.new_row) * Dv + c] = v_new16(c);
+  if (tid < Dk) kf[int64_t(a.new_row) * Dk + tid] = k_new16(tid);
+  if (tid < Dv) vf[int64_t(a.new_row) * Dv + tid] = v_new16(tid);
   if (a.group < 0) return;  // the same for every thread: no barrier below is reached
 
   // 2. the group
-  for (int i = tid; i < Dv * vb; i += kAppendThreads) vw[i] = 0u;
-  __syncthreads();
+  for (int i = tid; i < Dv * VB; i += kAppendThreads) vw[i] = 0u;
   const int64_t gi = slab * a.g_stride + a.group;
   auto k_row = [&](int j, int c) {
     const int row = a.member_rows[j];
@@ -87,28 +90,55 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     const int row = a.member_rows[j];
     return f16_to_f32(row == a.new_row ? v_new16(c) : vf[int64_t(row) * Dv + c]);
   };
-  // keys: thread c takes channel c over the 32 tokens; the 32/kb channels of a code
-  // word are adjacent lanes, OR-ed together with lane exchanges
-  const float klev = float((1 << kb) - 1), vlev = float((1 << vb) - 1);
-  const int per = 32 / kb, kwords = Dk * kb / 32;
-  for (int c = tid; c < Dk; c += kAppendThreads) {
-    float x[KVQ_GROUP];
-    float mn = INFINITY, mx = -INFINITY;
+  constexpr float klev = float((1 << KB) - 1), vlev = float((1 << VB) - 1);
+  constexpr int per = 32 / KB;  // key codes per word
+  const int kwords = Dk * KB / 32;
+  // keys: thread (channel c, slice sl) holds tokens 4 sl .. 4 sl + 3 of channel c;
+  // the slices' minima and maxima meet in LDS.  Dk is a multiple of 32, so the
+  // `per` channels of a code word are adjacent lanes of one wave.
+  constexpr int kMaxKeyPasses = KVQ_MAX_HEAD_DIM * kSlices / kAppendThreads;
+  float kx[kMaxKeyPasses][4];
 #pragma unroll
-    for (int j = 0; j < KVQ_GROUP; ++j) {
-      x[j] = k_row(j, c);
-      mn = fminf(mn, x[j]);
-      mx = fmaxf(mx, x[j]);
+  for (int pass = 0; pass < kMaxKeyPasses; ++pass) {
+    const int u = tid + pass * kAppendThreads;
+    if (u < Dk * kSlices) {
+      const int sl = u / Dk, c = u - sl * Dk;
+      float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        kx[pass][k] = k_row(4 * sl + k, c);
+        mn = fminf(mn, kx[pass][k]);
+        mx = fmaxf(mx, kx[pass][k]);
+      }
+      kmn[sl][c] = mn;
+      kmx[sl][c] = mx;
     }
-    const Quant q = quant_params(mn, mx, klev);
-    static_cast<uint16_t*>(a.cache.k_scale)[gi * Dk + c] = q.sb;
-    static_cast<uint16_t*>(a.cache.k_zero)[gi * Dk + c] = q.zb;
-    uint32_t* kc = static_cast<uint32_t*>(a.cache.k_codes) + gi * KVQ_GROUP * kwords;
+  }
+  __syncthreads();
+  uint32_t* kc = static_cast<uint32_t*>(a.cache.k_codes) + gi * KVQ_GROUP * kwords;
 #pragma unroll
-    for (int j = 0; j < KVQ_GROUP; ++j) {
-      uint32_t w = quant_code(x[j], q, klev) << ((c % per) * kb);
-      for (int o = 1; o < per; o <<= 1) w |= uint32_t(__shfl_xor(int(w), o));
-      if (c % per == 0) kc[j * kwords + c / per] = w;
+  for (int pass = 0; pass < kMaxKeyPasses; ++pass) {
+    const int u = tid + pass * kAppendThreads;
+    if (u < Dk * kSlices) {
+      const int sl = u / Dk, c = u - sl * Dk;
+      float mn = kmn[0][c], mx = kmx[0][c];
+#pragma unroll
+      for (int i = 1; i < kSlices; ++i) {
+        mn = fminf(mn, kmn[i][c]);
+        mx = fmaxf(mx, kmx[i][c]);
+      }
+      const Quant q = quant_params(mn, mx, klev);
+      if (sl == 0) {
+        static_cast<uint16_t*>(a.cache.k_scale)[gi * Dk + c] = q.sb;
+        static_cast<uint16_t*>(a.cache.k_zero)[gi * Dk + c] = q.zb;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t w = quant_code(kx[pass][k], q, klev) << ((c % per) * KB);
+#pragma unroll
+        for (int o = 1; o < per; o <<= 1) w |= uint32_t(__shfl_xor(int(w), o));
+        if (c % per == 0) kc[(4 * sl + k) * kwords + c / per] = w;
+      }
     }
   }
   // values: element e = (token j, channel c); the 32 lanes of a channel group are
@@ -118,6 +148,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     const int j = e / Dv, c = e - j * Dv;
     const float x = v_row(j, c);
     float mn = x, mx = x;
+#pragma unroll
     for (int o = 16; o >= 1; o >>= 1) {
       mn = fminf(mn, __shfl_xor(mn, o));
       mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -128,12 +159,12 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       static_cast<uint16_t*>(a.cache.v_scale)[si] = q.sb;
       static_cast<uint16_t*>(a.cache.v_zero)[si] = q.zb;
     }
-    const int bit = value_bit_position(j, c, Dv, vb);
+    const int bit = value_bit_position(j, c, Dv, VB);
     atomicOr(&vw[bit >> 5], quant_code(x, q, vlev) << (bit & 31));
   }
   __syncthreads();  // the group's rows have been read and its value words are complete
-  uint32_t* vc = static_cast<uint32_t*>(a.cache.v_codes) + gi * (Dv * vb);
-  for (int i = tid; i < Dv * vb; i += kAppendThreads) vc[i] = vw[i];
+  uint32_t* vc = static_cast<uint32_t*>(a.cache.v_codes) + gi * (Dv * VB);
+  for (int i = tid; i < Dv * VB; i += kAppendThreads) vc[i] = vw[i];
 
   // 3. moves: sources lie past the new end, destinations are freed rows
   for (int e = tid; e < a.n_moves * Dk; e += kAppendThreads) {
@@ -153,8 +184,17 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const int64_t slabs = int64_t(a.L.B) * a.L.Hkv;
   if (slabs < 1 || slabs > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(append_kernel, dim3(unsigned(slabs)), dim3(kAppendThreads), 0, stream, a);
-  return hipGetLastError();
+  const int kb = a.L.k_bits, vb = a.L.v_bits;
+#define KVQ_APPEND_CASE(K_, V_)                                                                      \
+  if (kb == K_ && vb == V_) {                                                                        \
+    hipLaunchKernelGGL((append_kernel<K_, V_>), dim3(unsigned(slabs)), dim3(kAppendThreads), 0, stream, a); \
+    return hipGetLastError();                                                                        \
+  }
+  KVQ_APPEND_CASE(2, 2) KVQ_APPEND_CASE(2, 4) KVQ_APPEND_CASE(2, 8)
+  KVQ_APPEND_CASE(4, 2) KVQ_APPEND_CASE(4, 4) KVQ_APPEND_CASE(4, 8)
+  KVQ_APPEND_CASE(8, 2) KVQ_APPEND_CASE(8, 4) KVQ_APPEND_CASE(8, 8)
+#undef KVQ_APPEND_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvq
