@@ -51,8 +51,8 @@ Canonical packed layout for one (b, kv-head) slab (the same index formulas appea
   tiles in that chunk and F = Dv*vb/8 bits per (o, n, j%4) field: one field pairs
   tokens j and j+4 of an octet, the first of them in the low half of every chunk
   (library format choice, see ``value_bit_position``);
-* v_scale, v_zero fp16 [Tq/32, Dv/32, 32]  (one pair per token and 32-channel
-  group, the 32 tokens of a group contiguous);
+* v_scale, v_zero fp16 [Tq/32, Dv/gV, 32]  (one pair per token and gV-channel
+  group, gV = 32 by default, the 32 tokens of a group contiguous);
 * k_fp16 [R, Dk], v_fp16 [R, Dv] fp16 rows of the retained positions, ascending.
 """
 
@@ -236,12 +236,13 @@ def unpack_value_codes(words: np.ndarray, bits: int) -> np.ndarray:
 
 
 def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_window: int,
-              key_rotation: bool = False):
+              key_rotation: bool = False, v_group: int = GROUP):
     """Quantize and pack one (b, kv-head) slab.  K [T, Dk], V [T, Dv] in storage dtype.
 
     Keys per channel over groups of 32 consecutive quantized tokens (LogQuant
     section 5, "per-channel" keys; group 32 from "Quantize What Counts", results);
-    values per token over groups of 32 channels; retained positions copied to fp16.
+    values per token over groups of v_group channels (32 by default; "Quantize What
+    Counts", results, sweeps the group size); retained positions copied to fp16.
     With key_rotation every key row is first rotated (``hadamard_rotate``).
     """
     K32 = upcast(K, dtype)
@@ -254,6 +255,8 @@ def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_win
     Tq = len(u)
     if Dk % GROUP or Dv % GROUP:
         raise ValueError("head widths must be multiples of %d" % GROUP)
+    if v_group not in (32, 64, 128) or Dv % v_group:
+        raise ValueError("value group %d must be 32, 64 or 128 and divide Dv = %d" % (v_group, Dv))
     if Tq % GROUP:
         raise ValueError("quantized token count %d is not a multiple of %d" % (Tq, GROUP))
     nG = Tq // GROUP
@@ -262,12 +265,12 @@ def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_win
     Kg = K32[u].reshape(nG, GROUP, Dk).transpose(0, 2, 1)          # [nG, Dk, 32]
     kc, ks, kz = quantize_groups(Kg, k_bits)                          # [nG, Dk, 32], [nG, Dk]
     kc = kc.transpose(0, 2, 1).reshape(Tq, Dk)
-    # values: one (s, z) per token and 32-channel group
-    Vg = V32[u].reshape(Tq, Dv // GROUP, GROUP)
-    vc, vs, vz = quantize_groups(Vg, v_bits)                          # [Tq, Dv/32, 32], [Tq, Dv/32]
+    # values: one (s, z) per token and v_group-channel group
+    Vg = V32[u].reshape(Tq, Dv // v_group, v_group)
+    vc, vs, vz = quantize_groups(Vg, v_bits)                          # [Tq, Dv/gV, gV], [Tq, Dv/gV]
     vc = vc.reshape(nG, GROUP, Dv)                                     # [nG, 32 tokens, Dv]
-    vs = vs.reshape(nG, GROUP, Dv // GROUP).transpose(0, 2, 1)       # [nG, Dv/32, 32]
-    vz = vz.reshape(nG, GROUP, Dv // GROUP).transpose(0, 2, 1)
+    vs = vs.reshape(nG, GROUP, Dv // v_group).transpose(0, 2, 1)     # [nG, Dv/gV, 32]
+    vz = vz.reshape(nG, GROUP, Dv // v_group).transpose(0, 2, 1)
 
     return {
         "k_codes": pack_codes(kc, k_bits),
@@ -291,7 +294,7 @@ def pack_all(K, V, w):
         rows = {key: [] for key in CACHE_KEYS}
         for h in range(K.shape[1]):
             p = pack_slab(K[b, h], V[b, h], w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window,
-                          getattr(w, "key_rotation", False))
+                          getattr(w, "key_rotation", False), getattr(w, "v_group", GROUP))
             for key in CACHE_KEYS:
                 rows[key].append(p[key])
         for key in CACHE_KEYS:
@@ -303,7 +306,8 @@ def pack_all(K, V, w):
 
 def dequant_slab(p, k_bits: int, v_bits: int):
     """float64 keys and values of one packed slab: quantized tokens (compacted order)
-    followed by the retained fp16 tokens.  x_hat = code * s + z (exact in float64)."""
+    followed by the retained fp16 tokens.  x_hat = code * s + z (exact in float64).
+    The value group width is read off the scale array: Dv / its second axis."""
     kc = unpack_codes(p["k_codes"], k_bits).astype(np.float64)      # [Tq, Dk]
     Tq, Dk = kc.shape
     ks = p["k_scale"].view(np.float16).astype(np.float64)            # [nG, Dk]
@@ -313,9 +317,10 @@ def dequant_slab(p, k_bits: int, v_bits: int):
     vc = unpack_value_codes(p["v_codes"], v_bits)                    # [nG, 32, Dv]
     nG, _, Dv = vc.shape
     vc = vc.reshape(Tq, Dv).astype(np.float64)                       # token 32g + t
-    vs = p["v_scale"].view(np.float16).astype(np.float64).transpose(0, 2, 1).reshape(Tq, Dv // GROUP)
-    vz = p["v_zero"].view(np.float16).astype(np.float64).transpose(0, 2, 1).reshape(Tq, Dv // GROUP)
-    Vhat_q = vc * np.repeat(vs, GROUP, axis=1) + np.repeat(vz, GROUP, axis=1)
+    ngv = p["v_scale"].shape[1]                                      # Dv / v_group
+    vs = p["v_scale"].view(np.float16).astype(np.float64).transpose(0, 2, 1).reshape(Tq, ngv)
+    vz = p["v_zero"].view(np.float16).astype(np.float64).transpose(0, 2, 1).reshape(Tq, ngv)
+    Vhat_q = vc * np.repeat(vs, Dv // ngv, axis=1) + np.repeat(vz, Dv // ngv, axis=1)
     Kr = p["k_fp16"].view(np.float16).astype(np.float64)              # [R, Dk]
     Vr = p["v_fp16"].view(np.float16).astype(np.float64)              # [R, Dv]
     return np.concatenate([Khat_q, Kr]), np.concatenate([Vhat_q, Vr])

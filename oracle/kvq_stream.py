@@ -44,13 +44,15 @@ from .kvq_oracle import (CACHE_KEYS, GROUP, attention, dequant_slab, pack_codes,
 class SlabStream:
     """Streaming cache of one slab (see the module header for the state)."""
 
-    def __init__(self, Dk: int, Dv: int, k_bits: int, v_bits: int, n_recent: int, log_window: int):
+    def __init__(self, Dk: int, Dv: int, k_bits: int, v_bits: int, n_recent: int, log_window: int,
+                 v_group: int = GROUP):
         if log_window > 0 and n_recent < log_window:
             raise ValueError("a stream needs log_window == 0 or n_recent >= log_window "
                              "(otherwise a token could re-enter the fp16 set)")
         self.Dk, self.Dv = Dk, Dv
         self.k_bits, self.v_bits = k_bits, v_bits
         self.n_recent, self.log_window = n_recent, log_window
+        self.v_group = v_group
         self.t = 0
         self.rows = {}
         self.pending = set()
@@ -64,7 +66,7 @@ class SlabStream:
         if self.t:
             raise ValueError("prefill starts an empty stream")
         T0 = K.shape[0]
-        p = pack_slab(K, V, dtype, self.k_bits, self.v_bits, self.n_recent, self.log_window)
+        p = pack_slab(K, V, dtype, self.k_bits, self.v_bits, self.n_recent, self.log_window, v_group=self.v_group)
         r, u = split_positions(T0, self.n_recent, self.log_window)
         for g in range(len(u) // GROUP):
             sl = slice(GROUP * g, GROUP * (g + 1))
@@ -108,14 +110,14 @@ class SlabStream:
         K32 = np.stack([self.rows[int(p)][0] for p in members]).view(np.float16).astype(np.float32)
         V32 = np.stack([self.rows[int(p)][1] for p in members]).view(np.float16).astype(np.float32)
         kc, ks, kz = quantize_groups(K32.T, self.k_bits)                  # [Dk, 32], [Dk]
-        vc, vs, vz = quantize_groups(V32.reshape(GROUP, self.Dv // GROUP, GROUP), self.v_bits)
+        vc, vs, vz = quantize_groups(V32.reshape(GROUP, self.Dv // self.v_group, self.v_group), self.v_bits)
         self.groups.append({
             "pos": members.copy(),
             "k_codes": pack_codes(kc.T, self.k_bits),                      # [32, Dk*kb/32]
             "k_scale": ks.view(np.uint16),
             "k_zero": kz.view(np.uint16),
             "v_codes": pack_value_codes(vc.reshape(GROUP, self.Dv), self.v_bits),
-            "v_scale": np.ascontiguousarray(vs.T).view(np.uint16),         # [Dv/32, 32]
+            "v_scale": np.ascontiguousarray(vs.T).view(np.uint16),         # [Dv/gV, 32]
             "v_zero": np.ascontiguousarray(vz.T).view(np.uint16),
         })
         for p in members:
@@ -136,8 +138,8 @@ class SlabStream:
             "k_scale": np.array([g["k_scale"] for g in self.groups], np.uint16).reshape(nG, self.Dk),
             "k_zero": np.array([g["k_zero"] for g in self.groups], np.uint16).reshape(nG, self.Dk),
             "v_codes": np.array([g["v_codes"] for g in self.groups], np.uint32).reshape(nG, self.Dv * self.v_bits),
-            "v_scale": np.array([g["v_scale"] for g in self.groups], np.uint16).reshape(nG, self.Dv // GROUP, GROUP),
-            "v_zero": np.array([g["v_zero"] for g in self.groups], np.uint16).reshape(nG, self.Dv // GROUP, GROUP),
+            "v_scale": np.array([g["v_scale"] for g in self.groups], np.uint16).reshape(nG, self.Dv // self.v_group, GROUP),
+            "v_zero": np.array([g["v_zero"] for g in self.groups], np.uint16).reshape(nG, self.Dv // self.v_group, GROUP),
             "k_fp16": np.array([self.rows[int(q)][0] for q in rpos], np.uint16).reshape(len(rpos), self.Dk),
             "v_fp16": np.array([self.rows[int(q)][1] for q in rpos], np.uint16).reshape(len(rpos), self.Dv),
         }
