@@ -8,7 +8,8 @@
  *    Counts: More for Keys, Less for Values": methodology, K4V2; group size 32 for
  *    keys, results).  Keys are quantized per channel over groups of 32 tokens
  *    ("LogQuant: Log-Distributed 2-Bit Quantization of KV Cache", section 5,
- *    per-channel keys); values per token over groups of 32 channels.
+ *    per-channel keys); values per token over groups of v_group = 32 (default),
+ *    64 or 128 channels (Quantize What Counts, results, sweeps the group size).
  *  - A subset of tokens stays in fp16: the newest n_recent positions and, when
  *    log_window = W > 0, log-spaced positions further back (LogQuant section 2,
  *    log-based filtering): for j = 1, 2, ... every multiple of 2^j inside
@@ -43,9 +44,9 @@
  *            r = min(TPW, Dv/16 - (t/TPW)*TPW).  When Dv*vb is a multiple of 256
  *            each 32-bit word holds, for one (o, n, j%4), the codes of TPW tiles
  *            of token j%4 in its low half and of token j%4 + 4 in its high half.
- *   v_scale  fp16   [B, Hkv, n_groups, Dv/32, 32]  one per token and 32-channel
- *            group; the 32 tokens of a group are contiguous
- *   v_zero   fp16   [B, Hkv, n_groups, Dv/32, 32]
+ *   v_scale  fp16   [B, Hkv, n_groups, Dv/v_group, 32]  one per token and
+ *            v_group-channel group; the 32 tokens of a group are contiguous
+ *   v_zero   fp16   [B, Hkv, n_groups, Dv/v_group, 32]
  *   k_fp16   fp16   [B, Hkv, R, Dk]   retained positions, ascending
  *   v_fp16   fp16   [B, Hkv, R, Dv]
  *
@@ -89,6 +90,7 @@ typedef struct {
   int32_t k_bits, v_bits;         /* each in {2, 4, 8} */
   int32_t n_recent;               /* newest positions kept in fp16 (0..T; T = no quantization) */
   int32_t log_window;             /* W of the log-spaced fp16 positions; 0 = none */
+  int32_t v_group;                /* channels per value group: 32, 64 or 128, dividing Dv */
   int32_t R, Tq, n_groups;        /* derived: retained count, quantized count, Tq / 32 */
 } kvq_layout;
 
@@ -107,6 +109,11 @@ typedef struct {
  * the quantized token count Tq a multiple of 32 (choose n_recent accordingly). */
 int kvq_layout_init(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T,
                     int k_bits, int v_bits, int n_recent, int log_window);
+
+/* kvq_layout_init with values in groups of v_group channels (32, 64 or 128, dividing
+ * Dv; KVQ_ERR_UNSUPPORTED otherwise).  kvq_layout_init is this with v_group = 32. */
+int kvq_layout_init_ex(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T,
+                       int k_bits, int v_bits, int n_recent, int log_window, int v_group);
 
 /* Byte sizes of the eight kvq_cache buffers, in kvq_cache field order. */
 int kvq_cache_sizes(const kvq_layout* L, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]);
@@ -205,7 +212,7 @@ int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq
  *   k_codes uint32 [B, Hkv, 32*g_cap, Dk*k_bits/32]   (32 rows per group)
  *   k_scale, k_zero fp16 [B, Hkv, g_cap, Dk]
  *   v_codes uint32 [B, Hkv, g_cap, Dv*v_bits]
- *   v_scale, v_zero fp16 [B, Hkv, g_cap, Dv/32, 32]
+ *   v_scale, v_zero fp16 [B, Hkv, g_cap, Dv/v_group, 32]
  *   k_fp16 fp16 [B, Hkv, r_cap, Dk], v_fp16 fp16 [B, Hkv, r_cap, Dv]
  * The host state (kvq_stream, caller-owned) advances when a call is enqueued, so
  * all calls on one stream state must be enqueued in order on one HIP stream.  A
@@ -244,6 +251,10 @@ typedef struct {
  * row bound of at most KVQ_STREAM_MAX_ROWS (KVQ_ERR_UNSUPPORTED otherwise). */
 int kvq_stream_init(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, int capacity,
                     int k_bits, int v_bits, int n_recent, int log_window);
+
+/* kvq_stream_init with values in groups of v_group channels (as kvq_layout_init_ex). */
+int kvq_stream_init_ex(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, int capacity,
+                       int k_bits, int v_bits, int n_recent, int log_window, int v_group);
 
 /* Byte sizes of the eight buffers of a stream's cache, in kvq_cache field order. */
 int kvq_stream_cache_sizes(const kvq_stream* S, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]);

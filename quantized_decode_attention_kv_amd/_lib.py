@@ -12,14 +12,15 @@ KVQ_GROUP = 32
 KVQ_NUM_CACHE_BUFFERS = 8
 KVQ_STREAM_MAX_ROWS = 4096
 
-LAYOUT_FIELDS = ["B", "Hq", "Hkv", "Dk", "Dv", "T", "k_bits", "v_bits", "n_recent", "log_window",
+LAYOUT_FIELDS = ["B", "Hq", "Hkv", "Dk", "Dv", "T", "k_bits", "v_bits", "n_recent", "log_window", "v_group",
                  "R", "Tq", "n_groups"]
 CACHE_FIELDS = ["k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_fp16", "v_fp16"]
 
 # every entry point declared in include/kvq.h
 EXPORTS = ["kvq_layout_init", "kvq_cache_sizes", "kvq_retained_positions", "kvq_quantized_before",
            "kvq_decode_workspace_bytes", "kv_quant_pack", "kv_decode_attn", "kv_decode_attn_ex", "kvq_status_string",
-           "kvq_last_error", "kvq_read_probe", "kvq_stream_init", "kvq_stream_cache_sizes",
+           "kvq_last_error", "kvq_read_probe", "kvq_layout_init_ex", "kvq_stream_init", "kvq_stream_init_ex",
+           "kvq_stream_cache_sizes",
            "kvq_stream_workspace_bytes", "kvq_stream_plan", "kv_stream_prefill", "kv_stream_append",
            "kv_stream_decode"]
 
@@ -66,6 +67,8 @@ def load() -> ctypes.CDLL:
     CP = ctypes.POINTER(KvqCache)
     lib.kvq_layout_init.argtypes = [LP] + [c_int] * 10
     lib.kvq_layout_init.restype = c_int
+    lib.kvq_layout_init_ex.argtypes = [LP] + [c_int] * 11
+    lib.kvq_layout_init_ex.restype = c_int
     lib.kvq_cache_sizes.argtypes = [LP, ctypes.POINTER(c_sz)]
     lib.kvq_cache_sizes.restype = c_int
     lib.kvq_retained_positions.argtypes = [LP, ctypes.POINTER(c_i32), c_i32]
@@ -85,6 +88,8 @@ def load() -> ctypes.CDLL:
     SP = ctypes.POINTER(KvqStream)
     lib.kvq_stream_init.argtypes = [SP] + [c_int] * 10
     lib.kvq_stream_init.restype = c_int
+    lib.kvq_stream_init_ex.argtypes = [SP] + [c_int] * 11
+    lib.kvq_stream_init_ex.restype = c_int
     lib.kvq_stream_cache_sizes.argtypes = [SP, ctypes.POINTER(c_sz)]
     lib.kvq_stream_cache_sizes.restype = c_int
     lib.kvq_stream_workspace_bytes.argtypes = [SP, c_int]

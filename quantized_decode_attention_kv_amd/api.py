@@ -17,16 +17,16 @@ _DTYPE_CODES = {torch.float32: L_.KVQ_F32, torch.float16: L_.KVQ_F16, torch.bflo
 class Layout:
     """Shape and fp16-retention policy of one packed cache (kvq_layout)."""
 
-    def __init__(self, B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits, n_recent=0, log_window=0):
+    def __init__(self, B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits, n_recent=0, log_window=0, v_group=32):
         lib = L_.load()
         self._c = L_.KvqLayout()
-        L_.check(lib.kvq_layout_init(ctypes.byref(self._c), B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits,
-                                     n_recent, log_window))
+        L_.check(lib.kvq_layout_init_ex(ctypes.byref(self._c), B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits,
+                                        n_recent, log_window, v_group))
 
     @classmethod
     def from_workload(cls, w, T=None):
         return cls(w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T if T is None else T, w.k_bits, w.v_bits,
-                   w.n_recent, w.log_window)
+                   w.n_recent, w.log_window, getattr(w, "v_group", 32))
 
     def __getattr__(self, name):
         if name in L_.LAYOUT_FIELDS:
@@ -62,8 +62,8 @@ class Layout:
             "k_scale": ((B, H, nG, self.Dk), torch.float16),
             "k_zero": ((B, H, nG, self.Dk), torch.float16),
             "v_codes": ((B, H, nG, self.Dv * self.v_bits), torch.int32),
-            "v_scale": ((B, H, nG, self.Dv // 32, 32), torch.float16),
-            "v_zero": ((B, H, nG, self.Dv // 32, 32), torch.float16),
+            "v_scale": ((B, H, nG, self.Dv // self.v_group, 32), torch.float16),
+            "v_zero": ((B, H, nG, self.Dv // self.v_group, 32), torch.float16),
             "k_fp16": ((B, H, R, self.Dk), torch.float16),
             "v_fp16": ((B, H, R, self.Dv), torch.float16),
         }
@@ -178,10 +178,11 @@ class Stream:
     appended one at a time (``append``); ``prefill`` starts an empty stream from
     the one-shot cache of its first tokens."""
 
-    def __init__(self, B, Hq, Hkv, Dk, Dv, capacity, k_bits, v_bits, n_recent=0, log_window=0, device="cuda"):
+    def __init__(self, B, Hq, Hkv, Dk, Dv, capacity, k_bits, v_bits, n_recent=0, log_window=0, device="cuda",
+                 v_group=32):
         self._c = L_.KvqStream()
-        L_.check(L_.load().kvq_stream_init(ctypes.byref(self._c), B, Hq, Hkv, Dk, Dv, capacity, k_bits, v_bits,
-                                           n_recent, log_window))
+        L_.check(L_.load().kvq_stream_init_ex(ctypes.byref(self._c), B, Hq, Hkv, Dk, Dv, capacity, k_bits, v_bits,
+                                              n_recent, log_window, v_group))
         self.cache = None
         if device is not None:
             self.cache = {k: torch.empty(shape, dtype=dt, device=device) for k, (shape, dt) in self.shapes().items()}
@@ -210,8 +211,8 @@ class Stream:
             "k_scale": ((B, H, G, Dk), torch.float16),
             "k_zero": ((B, H, G, Dk), torch.float16),
             "v_codes": ((B, H, G, Dv * c.L.v_bits), torch.int32),
-            "v_scale": ((B, H, G, Dv // 32, 32), torch.float16),
-            "v_zero": ((B, H, G, Dv // 32, 32), torch.float16),
+            "v_scale": ((B, H, G, Dv // c.L.v_group, 32), torch.float16),
+            "v_zero": ((B, H, G, Dv // c.L.v_group, 32), torch.float16),
             "k_fp16": ((B, H, R, Dk), torch.float16),
             "v_fp16": ((B, H, R, Dv), torch.float16),
         }

@@ -78,6 +78,8 @@ int kvq::check_format(const kvq_layout& l) {
   if (L->n_recent < 0 || L->n_recent > L->T)
     return fail(KVQ_ERR_INVALID, "n_recent (%d) must be in [0, T=%d]", L->n_recent, L->T);
   if (L->log_window < 0) return fail(KVQ_ERR_INVALID, "log_window (%d) must be >= 0", L->log_window);
+  if ((L->v_group != 32 && L->v_group != 64 && L->v_group != 128) || L->Dv % L->v_group)
+    return fail(KVQ_ERR_UNSUPPORTED, "v_group (%d) must be 32, 64 or 128 and divide Dv (%d)", L->v_group, L->Dv);
   return ok();
 }
 
@@ -198,6 +200,11 @@ extern "C" {
 
 int kvq_layout_init(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T, int k_bits, int v_bits,
                     int n_recent, int log_window) {
+  return kvq_layout_init_ex(L, B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits, n_recent, log_window, KVQ_GROUP);
+}
+
+int kvq_layout_init_ex(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T, int k_bits, int v_bits,
+                       int n_recent, int log_window, int v_group) {
   if (!L) return fail(KVQ_ERR_INVALID, "layout is NULL");
   kvq_layout l{};
   l.B = B;
@@ -210,6 +217,7 @@ int kvq_layout_init(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T
   l.v_bits = v_bits;
   l.n_recent = n_recent;
   l.log_window = log_window;
+  l.v_group = v_group;
   if (T >= 1 && n_recent >= 0 && n_recent <= T && log_window >= 0) {
     const int64_t R = kvq::retained_before(rule_of(l), T);
     l.R = int32_t(R);
@@ -232,7 +240,7 @@ int kvq_cache_sizes(const kvq_layout* L, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]
   bytes_out[1] = slabs * nG * size_t(L->Dk) * 2;                    // k_scale
   bytes_out[2] = bytes_out[1];                                      // k_zero
   bytes_out[3] = slabs * Tq * size_t(L->Dv * L->v_bits / 32) * 4;   // v_codes
-  bytes_out[4] = slabs * Tq * size_t(L->Dv / KVQ_GROUP) * 2;        // v_scale
+  bytes_out[4] = slabs * Tq * size_t(L->Dv / L->v_group) * 2;       // v_scale
   bytes_out[5] = bytes_out[4];                                      // v_zero
   bytes_out[6] = slabs * R * size_t(L->Dk) * 2;                     // k_fp16
   bytes_out[7] = slabs * R * size_t(L->Dv) * 2;                     // v_fp16

@@ -7,7 +7,7 @@
 //   1. writes the token's fp16 row (round to nearest even);
 //   2. when a group forms, quantizes its 32 fp16 rows with the quantizer contract
 //      of kvq.h: keys per channel over the 32 tokens, values per token over each
-//      32-channel group, codes in the group formats of kvq.h;
+//      v_group-channel group, codes in the group formats of kvq.h;
 //   3. moves fp16 rows past the new end into the rows the group freed.
 // The appended token's values are taken from the input wherever step 2 or 3
 // needs them, so no thread reads what another thread of the launch has stored.
@@ -26,6 +26,7 @@ namespace {
 
 constexpr int kAppendThreads = 1024;
 constexpr int kSlices = 8;  // key token slices of 4 tokens: (channel, slice) per thread
+constexpr int kMaxValuesPerThread = KVQ_GROUP * KVQ_MAX_HEAD_DIM / kAppendThreads;
 
 __device__ inline float load_as_f32(const void* p, int dtype, int64_t i) {
   if (dtype == KVQ_F32) return static_cast<const float*>(p)[i];
@@ -65,6 +66,7 @@ template <int KB, int VB>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   __shared__ uint32_t vw[KVQ_MAX_HEAD_DIM * VB];             // value code words of the group
   __shared__ float kmn[kSlices][KVQ_MAX_HEAD_DIM], kmx[kSlices][KVQ_MAX_HEAD_DIM];
+  __shared__ float vmn[KVQ_GROUP][KVQ_MAX_HEAD_DIM / 32], vmx[KVQ_GROUP][KVQ_MAX_HEAD_DIM / 32];
   const int64_t slab = blockIdx.x;
   const int tid = threadIdx.x;
   const int Dk = a.L.Dk, Dv = a.L.Dv;
@@ -141,26 +143,49 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       }
     }
   }
-  // values: element e = (token j, channel c); the 32 lanes of a channel group are
-  // adjacent and reduce min / max with lane exchanges; codes are OR-ed into the
-  // group's bit stream in LDS
-  for (int e = tid; e < KVQ_GROUP * Dv; e += kAppendThreads) {
-    const int j = e / Dv, c = e - j * Dv;
-    const float x = v_row(j, c);
-    float mn = x, mx = x;
+  // values: element e = tid + 1024 i = (token j, channel c), Dv / 32 per thread.
+  // Minima and maxima over each 32-channel chunk (32 adjacent lanes) with lane
+  // exchanges, then over the v_group / 32 chunks of a group through LDS; codes are
+  // OR-ed into the group's bit stream in LDS.
+  const int vg = a.L.v_group, nve = KVQ_GROUP * Dv / kAppendThreads;
+  float vx[kMaxValuesPerThread];
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) {
-      mn = fminf(mn, __shfl_xor(mn, o));
-      mx = fmaxf(mx, __shfl_xor(mx, o));
+  for (int i = 0; i < kMaxValuesPerThread; ++i) {
+    if (i < nve) {  // the same for every thread
+      const int e = tid + i * kAppendThreads, j = e / Dv, c = e - j * Dv;
+      vx[i] = v_row(j, c);
+      float mn = vx[i], mx = vx[i];
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o));
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+      }
+      if ((c & 31) == 0) {
+        vmn[j][c >> 5] = mn;
+        vmx[j][c >> 5] = mx;
+      }
     }
-    const Quant q = quant_params(mn, mx, vlev);
-    if ((c & 31) == 0) {
-      const int64_t si = (gi * (Dv / KVQ_GROUP) + c / KVQ_GROUP) * KVQ_GROUP + j;
-      static_cast<uint16_t*>(a.cache.v_scale)[si] = q.sb;
-      static_cast<uint16_t*>(a.cache.v_zero)[si] = q.zb;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kMaxValuesPerThread; ++i) {
+    if (i < nve) {
+      const int e = tid + i * kAppendThreads, j = e / Dv, c = e - j * Dv;
+      const int g = c / vg, c0 = g * (vg >> 5);
+      float mn = vmn[j][c0], mx = vmx[j][c0];
+      for (int k = 1; k < (vg >> 5); ++k) {
+        mn = fminf(mn, vmn[j][c0 + k]);
+        mx = fmaxf(mx, vmx[j][c0 + k]);
+      }
+      const Quant q = quant_params(mn, mx, vlev);
+      if (c == g * vg) {
+        const int64_t si = (gi * (Dv / vg) + g) * KVQ_GROUP + j;
+        static_cast<uint16_t*>(a.cache.v_scale)[si] = q.sb;
+        static_cast<uint16_t*>(a.cache.v_zero)[si] = q.zb;
+      }
+      const int bit = value_bit_position(j, c, Dv, VB);
+      atomicOr(&vw[bit >> 5], quant_code(vx[i], q, vlev) << (bit & 31));
     }
-    const int bit = value_bit_position(j, c, Dv, VB);
-    atomicOr(&vw[bit >> 5], quant_code(x, q, vlev) << (bit & 31));
   }
   __syncthreads();  // the group's rows have been read and its value words are complete
   uint32_t* vc = static_cast<uint32_t*>(a.cache.v_codes) + gi * (Dv * VB);

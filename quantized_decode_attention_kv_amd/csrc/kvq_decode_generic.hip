@@ -6,7 +6,7 @@
 // Single-token decode attention, out = softmax(scale * q K^T) V, computed
 // directly from the packed cache: key x_hat = code * s + z with one (s, z) per
 // (key group, channel), value x_hat = code * s + z with one (s, z) per (token,
-// 32-channel group).  The retained fp16 tokens are visited as a separate segment;
+// group of v_group = 32, 64 or 128 channels).  The retained fp16 tokens are visited as a separate segment;
 // attention does not depend on token order ("LogQuant: Log-Distributed 2-Bit
 // Quantization of KV Cache", section 4, A.V = A_P.V_P).  Scores use the scale of
 // "HeadQ" section 2.1 / "Thin Keys, Full Values" section 2 (Dk may differ from Dv).
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
   const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Dk = a.L.Dk, Dv = a.L.Dv, kb = a.L.k_bits, vb = a.L.v_bits;
-  const int ngv = Dv / KVQ_GROUP;
+  const int vg = a.L.v_group, ngv = Dv / vg;  // value groups per token (the LDS areas are sized for Dv / 32)
   const int nG = a.L.n_groups, R = a.L.R, P = a.P;
   const int64_t slab = int64_t(b) * a.L.Hkv + h;
 
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
           if (c < Dv) {
             const int bit = value_bit_position(tt, c, Dv, vb);
             const float cf = float((vc[bit >> 5] >> (bit & 31)) & vmask);
-            const float* ppt = pp + (tt * ngv + c / KVQ_GROUP) * G;
+            const float* ppt = pp + (tt * ngv + c / vg) * G;
 #pragma unroll
             for (int i = 0; i < G; ++i) st.o[i][j] = fmaf(ppt[i], cf, st.o[i][j]);
           }
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
         const int c = lane + 64 * j;
         if (c < Dv) {
 #pragma unroll
-          for (int i = 0; i < G; ++i) st.o[i][j] += pz[(c / KVQ_GROUP) * G + i];
+          for (int i = 0; i < G; ++i) st.o[i][j] += pz[(c / vg) * G + i];
         }
       }
     }

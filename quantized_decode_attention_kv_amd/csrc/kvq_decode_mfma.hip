@@ -428,8 +428,11 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   const uint16_t* ksbase = static_cast<const uint16_t*>(a.cache.k_scale) + slab * a.g_stride * DK;
   const uint16_t* kzbase = static_cast<const uint16_t*>(a.cache.k_zero) + slab * a.g_stride * DK;
   const uint32_t* vbase = static_cast<const uint32_t*>(a.cache.v_codes) + slab * a.g_stride * (DV * VB);
-  const uint16_t* vsbase = static_cast<const uint16_t*>(a.cache.v_scale) + slab * a.g_stride * DV;
-  const uint16_t* vzbase = static_cast<const uint16_t*>(a.cache.v_zero) + slab * a.g_stride * DV;
+  // value scales / zeros: (Dv / v_group) x 32 per group, v_group = 32 << vsh
+  // (kept in a scalar register: the copies below take it in their descriptors)
+  const int vsh = __builtin_amdgcn_readfirstlane(a.L.v_group == 128 ? 2 : (a.L.v_group == 64 ? 1 : 0));
+  const uint16_t* vsbase = static_cast<const uint16_t*>(a.cache.v_scale) + slab * a.g_stride * (DV >> vsh);
+  const uint16_t* vzbase = static_cast<const uint16_t*>(a.cache.v_zero) + slab * a.g_stride * (DV >> vsh);
 
   // Q' task of this lane: (block tb = 8-channel block kk_t of lane group gq_t,
   // query i_t); it also forms the block's key zero-point partial sum
@@ -466,11 +469,11 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   const uint32_t voff = uint32_t(lane) * (VLW * 4);
   // scale copies: byte offset of this lane's dword (past the end for surplus lanes)
   const uint32_t kso = lane < DK / 2 ? uint32_t(lane) * 4 : 0x80000000u;
-  const uint32_t vso = uint32_t(lane) * 4;
+  const uint32_t vso = lane < ((DV / 2) >> vsh) ? uint32_t(lane) * 4 : 0x80000000u;
   // a unit without key groups gets empty buffers (its cache buffers may be null)
   const int nrec = nj > 0 ? 0x7fffffff : 0;
   const buf_rsrc rk = make_rsrc(kbase, nrec), rv = make_rsrc(vbase, nrec);
-  const int nsk = nj > 0 ? nG * DK * 2 : 0, nsv = nj > 0 ? nG * DV * 2 : 0;
+  const int nsk = nj > 0 ? nG * DK * 2 : 0, nsv = nj > 0 ? nG * ((DV * 2) >> vsh) : 0;
   const buf_rsrc rks = make_rsrc(ksbase, nsk), rkz = make_rsrc(kzbase, nsk);
   const buf_rsrc rvs = make_rsrc(vsbase, nsv), rvz = make_rsrc(vzbase, nsv);
   auto stage_group = [&](int g, int slot) {
@@ -487,8 +490,8 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
     unsigned char* ss = sb + LL::kStK + LL::kStV;
     lds_dma<4>(rks, kso, uint32_t(g) * (DK * 2), ss);
     lds_dma<4>(rkz, kso, uint32_t(g) * (DK * 2), ss + oKZ);
-    lds_dma<4>(rvs, vso, uint32_t(g) * (DV * 2), ss + oVS);
-    lds_dma<4>(rvz, vso, uint32_t(g) * (DV * 2), ss + oVZ);
+    lds_dma<4>(rvs, vso, uint32_t(g) * uint32_t((DV * 2) >> vsh), ss + oVS);
+    lds_dma<4>(rvz, vso, uint32_t(g) * uint32_t((DV * 2) >> vsh), ss + oVZ);
   };
   // The query first (vector-memory operations complete in order, so it would
   // otherwise wait for the staged groups): the 8 elements of the lane's Q' task.
@@ -582,6 +585,7 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   const float coefB = 1.0f / qe;           // q was scaled by 2^-E (query iq = lane % 4)
   const float coefD = 16777216.0f * coefB;  // codes are n 2^-24
   const int pa_entry = (gcP * 4 + gq) * 8 + iq;
+  const int vs_at = ((gcP >> vsh) * 4 + gq) * 16;  // the lane's 8 value scales / zeros in a slot
 
   // online-softmax state: reference maxima per query (wave-uniform) and this
   // lane's copy for its query; l over the lane's tokens; value accumulators
@@ -699,8 +703,8 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
     const unsigned char* ss = sb + LL::kStK + LL::kStV;
     d.ks = *reinterpret_cast<const u32x4*>(ss + tb * 16);
     d.kz = *reinterpret_cast<const u32x4*>(ss + oKZ + tb * 16);
-    d.vs = *reinterpret_cast<const u32x4*>(ss + oVS + (gcP * 4 + gq) * 16);
-    d.vz = *reinterpret_cast<const u32x4*>(ss + oVZ + (gcP * 4 + gq) * 16);
+    d.vs = *reinterpret_cast<const u32x4*>(ss + oVS + vs_at);
+    d.vz = *reinterpret_cast<const u32x4*>(ss + oVZ + vs_at);
   };
 
   // One step: one key group.  score_step takes the group up to the P' operands

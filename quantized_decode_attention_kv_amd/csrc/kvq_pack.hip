@@ -3,8 +3,9 @@
 // Group-wise asymmetric min/max quantization with fp16 scale/zero: keys per
 // channel over 32 consecutive quantized tokens ("LogQuant: Log-Distributed 2-Bit
 // Quantization of KV Cache", section 5, per-channel keys; group 32 from "Quantize
-// What Counts: More for Keys, Less for Values", results), values per token over 32
-// channels, separate key / value bit widths (Quantize What Counts, methodology).
+// What Counts: More for Keys, Less for Values", results), values per token over
+// v_group = 32, 64 or 128 channels (the group sizes that page's results sweep),
+// separate key / value bit widths (Quantize What Counts, methodology).
 // Retained positions (LogQuant section 2) are copied to fp16 rows.
 //
 // One launch per call.  Workgroups [0, n_groups_chunk) each own one key group of
@@ -14,8 +15,8 @@
 // global load is a coalesced row segment:
 //   keys    per-channel min / max over the wave's 8 tokens in registers, across
 //           the 4 waves through LDS;
-//   values  per-(token, 32-channel group) min / max with a DPP reduction inside
-//           each 16-lane row: a row of lanes holds exactly one channel group;
+//   values  per-(token, v_group-channel group) min / max with DPP reductions
+//           over the lanes that hold the group (v_group = 32, 64 or 128);
 //   codes   placed into LDS words at their final bit positions (a lane's two
 //           4- or 8-bit key codes fill whole bytes and are stored plainly; 2-bit
 //           key codes and value codes are OR-ed in), then stored as one
@@ -285,12 +286,13 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
       }
     }
 
-    // values: per (token, 32-channel group)
+    // values: per (token, v_group-channel group)
     constexpr float v_levels = float((1 << VB) - 1);
+    const int vg = a.L.v_group;
     if (v128) {
-      // the thread's 16 channels are one half of a 32-channel group (the other
-      // half is the neighbouring lane) and one 16-channel tile of the code stream:
-      // their codes sit at one bit offset in words 2 * VB apart
+      // the thread's 16 channels are one 16-channel tile of the code stream (their
+      // codes sit at one bit offset in words 2 * VB apart) and one of the vg / 16
+      // adjacent lanes that hold a value group
       float x[16];
       cvt16<DT>(vraw, x);
       float mn = x[0], mx = x[0];
@@ -301,10 +303,19 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
       }
       mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
       mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xF, 0xF, false)));
+      if (vg >= 64) {  // lane ^ 2
+        mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x4E, 0xF, 0xF, false)));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xF, 0xF, false)));
+      }
+      if (vg >= 128) {  // the other quad of the 8 lanes (its lanes already agree)
+        mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x141, 0xF, 0xF, false)));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x141, 0xF, 0xF, false)));
+      }
       const QParams q = make_qparams(mn, mx, v_levels);
-      if ((vtile & 1) == 0) {
-        vs_s[vtile >> 1][vtok] = q.s_bits;
-        vz_s[vtile >> 1][vtok] = q.z_bits;
+      const int tiles_per_group = vg >> 4;
+      if ((vtile & (tiles_per_group - 1)) == 0) {
+        vs_s[vtile / tiles_per_group][vtok] = q.s_bits;
+        vz_s[vtile / tiles_per_group][vtok] = q.z_bits;
       }
       const int p0 = value_bit_position(vtok, 16 * vtile, 128, VB);
       const int w0 = p0 >> 5, sh = p0 & 31;
@@ -312,23 +323,28 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
       for (int n = 0; n < 16; ++n)
         atomicOr(&vw_s[w0 + n * 2 * VB], quant_code(x[n], q.s, q.z, q.r, v_levels) << sh);
     }
-    // other head widths: lanes 16r..16r+15 of a pair block hold one group
+    // other head widths: lanes 16r..16r+15 of a pair block hold 32 channels, the
+    // vg / 32 adjacent rows of 16 lanes one value group (all lanes of a group are on)
 #pragma unroll
     for (int k = 0; k < kMaxPairBlocks && !v128; ++k) {
       const int cp = lane + 64 * k;
       if (128 * k < Dv) {  // wave-uniform: the pair block reaches into the head
         const bool on = 2 * cp < Dv;
-        const int gc = (2 * cp) / KVQ_GROUP;
+        const int gc = (2 * cp) / vg;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int tok = 8 * wave + t;
           const float2 x = on ? load_pair<DT>(a.V, (slab * a.t_count + rows[t]) * Dv + 2 * cp)
                               : make_float2(0.0f, 0.0f);
-          const float mn = row16_reduce<false>(fminf(x.x, x.y));
-          const float mx = row16_reduce<true>(fmaxf(x.x, x.y));
+          float mn = row16_reduce<false>(fminf(x.x, x.y));
+          float mx = row16_reduce<true>(fmaxf(x.x, x.y));
+          for (int o = 16; o < vg / 2; o <<= 1) {
+            mn = fminf(mn, __shfl_xor(mn, o));
+            mx = fmaxf(mx, __shfl_xor(mx, o));
+          }
           if (on) {
             const QParams q = make_qparams(mn, mx, v_levels);
-            if ((lane & 15) == 0) {
+            if ((lane & (vg / 2 - 1)) == 0) {
               vs_s[gc][tok] = q.s_bits;
               vz_s[gc][tok] = q.z_bits;
             }
@@ -348,7 +364,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
     for (int i = tid; i < KVQ_GROUP * kwords; i += kPackThreads) kdst[i] = kw_s[i];
     uint32_t* vdst = static_cast<uint32_t*>(a.cache.v_codes) + (slab * a.g_stride + g) * vwords;
     for (int i = tid; i < vwords; i += kPackThreads) vdst[i] = vw_s[i];
-    const int ngv = Dv / KVQ_GROUP;
+    const int ngv = Dv / vg;
     const int64_t vso = (slab * a.g_stride + g) * ngv * KVQ_GROUP;
     for (int i = tid; i < ngv * KVQ_GROUP; i += kPackThreads) {
       static_cast<uint16_t*>(a.cache.v_scale)[vso + i] = vs_s[i / KVQ_GROUP][i % KVQ_GROUP];

@@ -134,6 +134,11 @@ extern "C" {
 
 int kvq_stream_init(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, int capacity, int k_bits, int v_bits,
                     int n_recent, int log_window) {
+  return kvq_stream_init_ex(S, B, Hq, Hkv, Dk, Dv, capacity, k_bits, v_bits, n_recent, log_window, KVQ_GROUP);
+}
+
+int kvq_stream_init_ex(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, int capacity, int k_bits, int v_bits,
+                       int n_recent, int log_window, int v_group) {
   if (!S) return fail(KVQ_ERR_INVALID, "stream is NULL");
   kvq_layout l{};
   l.B = B;
@@ -146,6 +151,7 @@ int kvq_stream_init(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, int c
   l.v_bits = v_bits;
   l.n_recent = n_recent;
   l.log_window = log_window;
+  l.v_group = v_group;
   int st = kvq::check_format(l);
   if (st != KVQ_OK) return st;
   if (log_window > 0 && n_recent < log_window)
@@ -172,7 +178,7 @@ int kvq_stream_cache_sizes(const kvq_stream* S, size_t bytes_out[KVQ_NUM_CACHE_B
   bytes_out[1] = slabs * G * size_t(L.Dk) * 2;                             // k_scale
   bytes_out[2] = bytes_out[1];                                             // k_zero
   bytes_out[3] = slabs * G * size_t(L.Dv * L.v_bits) * 4;                  // v_codes
-  bytes_out[4] = slabs * G * size_t(L.Dv) * 2;                             // v_scale ([Dv/32, 32] per group)
+  bytes_out[4] = slabs * G * size_t(L.Dv / L.v_group) * KVQ_GROUP * 2;    // v_scale ([Dv/v_group, 32] per group)
   bytes_out[5] = bytes_out[4];                                             // v_zero
   bytes_out[6] = slabs * R * size_t(L.Dk) * 2;                             // k_fp16
   bytes_out[7] = slabs * R * size_t(L.Dv) * 2;                             // v_fp16

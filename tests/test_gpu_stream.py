@@ -91,8 +91,9 @@ def _run_stream(w: Workload, T0: int, T1: int, check_at, partitions, slabs=None,
     for (b, h) in slabs:
         sl = make_slab(w, b, h, 0, T1)
         host[(b, h)] = (sl.K, sl.V)
-    s = api.Stream(w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T, w.k_bits, w.v_bits, w.n_recent, w.log_window)
-    oracles = {bh: SlabStream(w.Dk, w.Dv, w.k_bits, w.v_bits, w.n_recent, w.log_window) for bh in slabs}
+    s = api.Stream(w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T, w.k_bits, w.v_bits, w.n_recent, w.log_window,
+                   v_group=w.v_group)
+    oracles = {bh: SlabStream(w.Dk, w.Dv, w.k_bits, w.v_bits, w.n_recent, w.log_window, w.v_group) for bh in slabs}
     if T0:
         s.prefill(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous())
         for bh, o in oracles.items():
@@ -141,6 +142,23 @@ def test_stream_g8_odd_widths():
     w = Workload("stream_g8_k2v4", B=1, Hq=16, Hkv=2, Dk=96, Dv=64, T=1500, k_bits=2, v_bits=4,
                  n_recent=32, log_window=32, dtype="bf16", seed=24)
     _run_stream(w, 0, 1100, {100, 257, 513, 800}, [1, 2, 5])
+
+
+def test_stream_value_groups_128():
+    """Values in groups of 128 channels (one scale per token row): the append
+    kernel's group minima and maxima span two waves."""
+    w = Workload("stream_k4v2_vg128", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=300, k_bits=4, v_bits=2,
+                 n_recent=16, dtype="bf16", seed=26, v_group=128)
+    _run_stream(w, 0, 240, {17, 48, 49, 112, 200}, [1, 3])
+
+
+def test_stream_value_groups_64_generic():
+    """Values in groups of 64 channels with 64-wide heads and G = 2 (generic decode
+    kernel), float32 inputs, after a prefill."""
+    w = Workload("stream_g2_vg64", B=1, Hq=4, Hkv=2, Dk=64, Dv=64, T=500, k_bits=8, v_bits=4,
+                 n_recent=32, log_window=16, dtype="f32", seed=27, v_group=64)
+    T0 = _valid_prefill(w, 200)
+    _run_stream(w, T0, T0 + 200, {T0 + 1, T0 + 77, T0 + 150}, [1, 2])
 
 
 def test_stream_full_capacity_and_errors():

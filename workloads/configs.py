@@ -89,4 +89,13 @@ def small_cases():
                  n_recent=32, dtype="f32", partitions=4, seed=14),
         Workload("small_g8_k2v4", B=1, Hq=16, Hkv=2, Dk=96, Dv=64, T=579, k_bits=2, v_bits=4,
                  n_recent=0, log_window=32, dtype="bf16", partitions=2, seed=15),
+        # value groups wider than 32 channels (matrix-core and generic paths)
+        Workload("small_k4v2_vg64", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=1064, k_bits=4, v_bits=2,
+                 n_recent=40, dtype="bf16", partitions=5, seed=16, v_group=64),
+        Workload("small_k2v4_vg128_log", B=1, Hq=4, Hkv=1, Dk=128, Dv=128, T=1487, k_bits=2, v_bits=4,
+                 n_recent=64, log_window=64, dtype="bf16", partitions=3, seed=17, v_group=128),
+        Workload("small_g2_k8v8_vg64", B=1, Hq=4, Hkv=2, Dk=64, Dv=64, T=352, k_bits=8, v_bits=8,
+                 n_recent=32, dtype="f32", partitions=4, seed=18, v_group=64),
+        Workload("small_d256_k4v4_vg128", B=1, Hq=2, Hkv=2, Dk=256, Dv=256, T=288, k_bits=4, v_bits=4,
+                 dtype="bf16", partitions=2, seed=19, v_group=128),
     ]
