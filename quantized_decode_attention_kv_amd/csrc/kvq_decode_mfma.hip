@@ -391,8 +391,15 @@ constexpr int lds_waves_per_simd() {
   return per_cu >= 16 ? 4 : (per_cu >= 4 ? per_cu / 4 : 1);
 }
 
+// Waves per workgroup.  The waves of a workgroup are independent units (no
+// barriers, an LDS slice each); grouping them by four places one on each SIMD of
+// a compute unit whatever state the dispatcher is in.  Single-wave workgroups were
+// spread 1 / 2 / 3 per SIMD (8% of SIMDs with 3) when the decode followed the pack
+// kernel, and those SIMDs finished 20 us after the rest.
+constexpr int kWavesPerGroup = 4;
+
 template <int DK, int DV, int KB, int VB, int D>
-__global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void decode_mfma_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void decode_mfma_kernel(const DecodeArgs a) {
   using LL = Lds<DK, DV, KB, VB, D>;
   constexpr int KK = DK / 32;          // 32-channel score steps
   constexpr int NV = DV / 16;          // 16-channel value tiles
@@ -406,15 +413,20 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
   constexpr uint32_t kVMask = ((1u << VB) - 1u) * 0x00010001u;
   static_assert(DV == 128 && NV % TPW == 0 && KLB >= 4 && DK % 32 == 0 && DK <= 128, "shape");
 
-  extern __shared__ __align__(16) unsigned char smem[];
+  extern __shared__ __align__(16) unsigned char lds_all[];
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);  // uniform in the wave
+  unsigned char* const smem = lds_all + wave * LL::kBytes;      // this wave's slice
   unsigned char* stage = smem;                                 // [D][kSlot]
   u32x4* B2 = reinterpret_cast<u32x4*>(smem);                  // q hi/lo, retained rows
   float* PT = reinterpret_cast<float*>(smem + LL::kSlot);      // [4][32], retained rows
-  const int lane = threadIdx.x, n = lane & 15, gq = lane >> 4;
+  const int lane = int(threadIdx.x) & 63, n = lane & 15, gq = lane >> 4;
 
-  // unit-major grid: workgroup L takes unit L / slabs of slab L % slabs
+  // unit-major grid of waves: wave L = 4 block + wave takes unit L / slabs of slab
+  // L % slabs (the last block may hold waves past the grid, which leave at once)
   const int U = a.units, slabs = a.L.B * a.L.Hkv;
-  const int unit = int(blockIdx.x) / slabs, sl = int(blockIdx.x) % slabs;
+  const int gw = int(blockIdx.x) * kWavesPerGroup + wave;
+  const int unit = gw / slabs, sl = gw % slabs;
+  if (unit >= U) return;
   const int h = sl % a.L.Hkv, b = sl / a.L.Hkv;
   const int nG = a.L.n_groups, R = a.L.R;
   const int64_t slab = int64_t(b) * a.L.Hkv + h;
@@ -972,12 +984,20 @@ __global__ __launch_bounds__(64, (lds_waves_per_simd<DK, DV, KB, VB, D>())) void
 
 template <int DK, int DV, int KB, int VB, int D>
 hipError_t launch_depth(DecodeArgs a, hipStream_t stream, int cus, int64_t waves) {
-  constexpr size_t lds = Lds<DK, DV, KB, VB, D>::kBytes;
-  static_assert(lds <= 64 * 1024, "LDS budget");
+  constexpr size_t lds = size_t(kWavesPerGroup) * Lds<DK, DV, KB, VB, D>::kBytes;
+  static_assert(lds <= 160 * 1024, "LDS budget");
   constexpr int per_simd = lds_waves_per_simd<DK, DV, KB, VB, D>();
   const int64_t simds = int64_t(cus) * 4;
   a.ranks = int(std::min<int64_t>(per_simd, std::max<int64_t>(1, (waves + simds - 1) / simds)));
-  hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, KB, VB, D>), dim3(unsigned(waves)), dim3(64), lds, stream, a);
+  if constexpr (lds > 64 * 1024) {
+    // gfx950 has 160 KB of LDS per compute unit; opt in to more than the default 64 KB
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<DK, DV, KB, VB, D>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  const int64_t blocks = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+  hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, KB, VB, D>), dim3(unsigned(blocks)), dim3(64 * kWavesPerGroup), lds,
+                     stream, a);
   return hipGetLastError();
 }
 
