@@ -159,10 +159,11 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float 
 }
 
 // Every output of the pack is written with streaming (non-temporal) stores: the
-// packed cache is read next by decode, a whole cache later, so keeping the freshly
-// written lines in the caches only defers their write-back into that decode's read
-// stream.  Measured with a 32 MB fill right before the 128K decode: ordinary stores
-// cost the decode 13 us, streaming stores nothing.
+// packed cache is read next by decode, a whole cache later, so there is no point in
+// keeping the freshly written lines in the caches, where their write-back would
+// fall into that decode's read stream.  (A plain 32 MB fill right before the 128K
+// decode cost the decode 13 us with ordinary stores and nothing with streaming
+// ones; for this kernel's 35 MB the two measured the same, within noise.)
 template <typename T>
 __device__ __forceinline__ void out_store(T* p, T v) {
   __builtin_nontemporal_store(v, p);
