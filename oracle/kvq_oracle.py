@@ -41,7 +41,8 @@ Canonical packed layout for one (b, kv-head) slab (the same index formulas appea
   u = sorted(the rest); Tq = len(u), groups of 32 consecutive compacted tokens;
 * k_codes  u32 [Tq, Dk*kb/32]: word w of row t holds channel w*(32/kb)+k at bits
   [k*kb, k*kb+kb), little-endian (keys stored token by token);
-* k_scale, k_zero fp16 [Tq/32, Dk]  (one pair per token group and channel);
+* k_scale, k_zero fp16 [Tq/gK, Dk]  (one pair per key group of gK = 32 (default),
+  64 or 128 tokens and channel; codes still come in 32-token groups);
 * v_codes  u32 [Tq/32, Dv*vb]: each 32-token group's value codes form one
   little-endian bit stream (bit i of the stream is bit i%32 of word i/32); the
   code of token 8o+j of the group (octet o, j < 8) and channel c = 16t+n (tile t,
@@ -236,13 +237,13 @@ def unpack_value_codes(words: np.ndarray, bits: int) -> np.ndarray:
 
 
 def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_window: int,
-              key_rotation: bool = False, v_group: int = GROUP):
+              key_rotation: bool = False, v_group: int = GROUP, k_group: int = GROUP):
     """Quantize and pack one (b, kv-head) slab.  K [T, Dk], V [T, Dv] in storage dtype.
 
-    Keys per channel over groups of 32 consecutive quantized tokens (LogQuant
-    section 5, "per-channel" keys; group 32 from "Quantize What Counts", results);
-    values per token over groups of v_group channels (32 by default; "Quantize What
-    Counts", results, sweeps the group size); retained positions copied to fp16.
+    Keys per channel over groups of k_group consecutive quantized tokens (LogQuant
+    section 5, "per-channel" keys; group 32 by default from "Quantize What Counts",
+    results, which also sweeps the group size); values per token over groups of
+    v_group channels (32 by default); retained positions copied to fp16.
     With key_rotation every key row is first rotated (``hadamard_rotate``).
     """
     K32 = upcast(K, dtype)
@@ -257,13 +258,16 @@ def pack_slab(K, V, dtype: str, k_bits: int, v_bits: int, n_recent: int, log_win
         raise ValueError("head widths must be multiples of %d" % GROUP)
     if v_group not in (32, 64, 128) or Dv % v_group:
         raise ValueError("value group %d must be 32, 64 or 128 and divide Dv = %d" % (v_group, Dv))
-    if Tq % GROUP:
-        raise ValueError("quantized token count %d is not a multiple of %d" % (Tq, GROUP))
+    if k_group not in (32, 64, 128):
+        raise ValueError("key group %d must be 32, 64 or 128" % k_group)
+    if Tq % k_group:
+        raise ValueError("quantized token count %d is not a multiple of %d" % (Tq, k_group))
     nG = Tq // GROUP
 
-    # keys: group g = compacted tokens 32g..32g+31, one (s, z) per channel
-    Kg = K32[u].reshape(nG, GROUP, Dk).transpose(0, 2, 1)          # [nG, Dk, 32]
-    kc, ks, kz = quantize_groups(Kg, k_bits)                          # [nG, Dk, 32], [nG, Dk]
+    # keys: key group g = compacted tokens k_group g .. k_group g + k_group - 1, one
+    # (s, z) per channel
+    Kg = K32[u].reshape(Tq // k_group, k_group, Dk).transpose(0, 2, 1)   # [Tq/gK, Dk, gK]
+    kc, ks, kz = quantize_groups(Kg, k_bits)                              # [Tq/gK, Dk, gK], [Tq/gK, Dk]
     kc = kc.transpose(0, 2, 1).reshape(Tq, Dk)
     # values: one (s, z) per token and v_group-channel group
     Vg = V32[u].reshape(Tq, Dv // v_group, v_group)
@@ -294,7 +298,8 @@ def pack_all(K, V, w):
         rows = {key: [] for key in CACHE_KEYS}
         for h in range(K.shape[1]):
             p = pack_slab(K[b, h], V[b, h], w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window,
-                          getattr(w, "key_rotation", False), getattr(w, "v_group", GROUP))
+                          getattr(w, "key_rotation", False), getattr(w, "v_group", GROUP),
+                          getattr(w, "k_group", GROUP))
             for key in CACHE_KEYS:
                 rows[key].append(p[key])
         for key in CACHE_KEYS:
@@ -307,12 +312,13 @@ def pack_all(K, V, w):
 def dequant_slab(p, k_bits: int, v_bits: int):
     """float64 keys and values of one packed slab: quantized tokens (compacted order)
     followed by the retained fp16 tokens.  x_hat = code * s + z (exact in float64).
-    The value group width is read off the scale array: Dv / its second axis."""
+    The key group length is read off the key scale array (Tq / its first axis), the
+    value group width off the value scale array (Dv / its second axis)."""
     kc = unpack_codes(p["k_codes"], k_bits).astype(np.float64)      # [Tq, Dk]
     Tq, Dk = kc.shape
-    ks = p["k_scale"].view(np.float16).astype(np.float64)            # [nG, Dk]
+    ks = p["k_scale"].view(np.float16).astype(np.float64)            # [Tq/gK, Dk]
     kz = p["k_zero"].view(np.float16).astype(np.float64)
-    g = np.arange(Tq) // GROUP
+    g = np.arange(Tq) // (Tq // ks.shape[0]) if ks.shape[0] else np.zeros(0, np.int64)
     Khat_q = kc * ks[g] + kz[g]
     vc = unpack_value_codes(p["v_codes"], v_bits)                    # [nG, 32, Dv]
     nG, _, Dv = vc.shape

@@ -1,4 +1,4 @@
-"""Pins of the value-group width (CPU only).
+"""Pins of the value-group width and the key-group length (CPU only).
 
 "Quantize What Counts" (results) sweeps the quantization group size; the library
 takes values in groups of v_group = 32, 64 or 128 channels per token.  The oracle's
@@ -85,3 +85,69 @@ def test_bad_value_group():
         pack_slab(K, np.zeros((32, 96), np.float32), "f32", 4, 2, 0, 0, v_group=64)
     with pytest.raises(ValueError):
         pack_slab(K, np.zeros((32, 64), np.float32), "f32", 4, 2, 0, 0, v_group=48)
+
+
+# ----------------------------------------------------------------- key group length
+# Keys are quantized per channel over k_group = 32 (default), 64 or 128 consecutive
+# quantized tokens; codes keep their 32-token groups.  Pinned the same way: a closed
+# form with one key group for the whole cache, an exact reduction to the pinned
+# 32-token grouping, and the half-step bound.
+
+def _k_rows(rng, T, Dk):
+    return (rng.standard_normal((T, Dk)) * 2 + 1).astype(np.float32)
+
+
+@pytest.mark.parametrize("kb", [2, 4, 8])
+def test_whole_cache_key_group_closed_form(kb):
+    rng = np.random.default_rng(41)
+    T, Dk, Dv = 128, 64, 32
+    K = _k_rows(rng, T, Dk)
+    V = _v_rows(rng, T, Dv)
+    p = pack_slab(K, V, "f32", kb, 2, 0, 0, k_group=128)
+    assert p["k_scale"].shape == (1, Dk) and p["k_codes"].shape == (T, Dk * kb // 32)
+    levels = np.float32(2 ** kb - 1)
+    want_s = ((K.max(axis=0) - K.min(axis=0)) / levels).astype(np.float16)
+    want_z = K.min(axis=0).astype(np.float16)
+    assert np.array_equal(p["k_scale"][0], want_s.view(np.uint16))
+    assert np.array_equal(p["k_zero"][0], want_z.view(np.uint16))
+
+
+@pytest.mark.parametrize("kb", [2, 4])
+def test_64_key_group_reduces_to_32_when_halves_share_range(kb):
+    rng = np.random.default_rng(42)
+    T, Dk, Dv = 192, 64, 32
+    K = _k_rows(rng, T, Dk)
+    V = _v_rows(rng, T, Dv)
+    lo, hi = K.min(axis=0) - 1.0, K.max(axis=0) + 1.0
+    for g0 in range(0, T, 64):            # both 32-token halves of every 64-group reach lo and hi
+        for h0 in (g0, g0 + 32):
+            K[h0 + 5] = lo
+            K[h0 + 20] = hi
+    p32 = pack_slab(K, V, "f32", kb, 2, 0, 0, k_group=32)
+    p64 = pack_slab(K, V, "f32", kb, 2, 0, 0, k_group=64)
+    assert np.array_equal(p32["k_codes"], p64["k_codes"])
+    for key in ("k_scale", "k_zero"):
+        assert np.array_equal(p32[key][0::2], p64[key]) and np.array_equal(p32[key][1::2], p64[key])
+    for key in ("v_codes", "v_scale", "v_zero"):
+        assert np.array_equal(p32[key], p64[key])
+
+
+@pytest.mark.parametrize("kg", [32, 64, 128])
+def test_key_dequant_within_half_step(kg):
+    rng = np.random.default_rng(43)
+    T, Dk, Dv, kb = 256, 64, 32, 4
+    K = _k_rows(rng, T, Dk)
+    V = _v_rows(rng, T, Dv)
+    p = pack_slab(K, V, "f32", kb, 2, 0, 0, k_group=kg)
+    Khat, _ = dequant_slab(p, kb, 2)
+    s = np.repeat(p["k_scale"].view(np.float16).astype(np.float64), kg, axis=0)
+    z = np.repeat(p["k_zero"].view(np.float16).astype(np.float64), kg, axis=0)
+    mn = np.repeat(K.reshape(T // kg, kg, Dk).min(axis=1).astype(np.float64), kg, axis=0)
+    assert np.all(np.abs(Khat - K.astype(np.float64)) <= 0.5 * s + np.abs(z - mn) + 1e-6)
+
+
+def test_bad_key_group():
+    with pytest.raises(ValueError):
+        pack_slab(np.zeros((96, 32), np.float32), np.zeros((96, 32), np.float32), "f32", 4, 2, 0, 0, k_group=64)
+    with pytest.raises(ValueError):
+        pack_slab(np.zeros((64, 32), np.float32), np.zeros((64, 32), np.float32), "f32", 4, 2, 0, 0, k_group=48)
