@@ -15,7 +15,10 @@ once) divided by the measured step time.
 Beside the step (not part of ``value``), the ``stream`` object times the streaming
 cache at the same shape: after a prefill to just under the full length, decode
 steps that append one token per sequence (kv_stream_append) and then attend over
-the stream (kv_stream_decode), each call bracketed by events.
+the stream (kv_stream_decode), each call bracketed by events; the
+``format_variants`` object times decode at the same shape with keys in groups of
+32 or 128 tokens and values in groups of 32, 64 or 128 channels (fewer scale and
+zero bytes), the caches' calls interleaved one by one.
 """
 
 import argparse
@@ -44,9 +47,9 @@ def decode_bytes(w, R, Tq):
     slabs = w.B * w.Hkv
     qb = 4 if w.dtype == "f32" else 2
     k_codes = slabs * Tq * w.Dk * w.k_bits // 8
-    k_sz = slabs * (Tq // 32) * w.Dk * 2 * 2
+    k_sz = slabs * (Tq // w.k_group) * w.Dk * 2 * 2
     v_codes = slabs * Tq * w.Dv * w.v_bits // 8
-    v_sz = slabs * Tq * (w.Dv // 32) * 2 * 2
+    v_sz = slabs * Tq * (w.Dv // w.v_group) * 2 * 2
     fp16 = slabs * R * (w.Dk + w.Dv) * 2
     return k_codes + k_sz + v_codes + v_sz + fp16 + w.B * w.Hq * w.Dk * qb + w.B * w.Hq * w.Dv * 4
 
@@ -59,7 +62,7 @@ def pack_bytes(w, n_tokens, n_quant):
     read = slabs * n_tokens * (w.Dk + w.Dv) * eb
     n_ret = n_tokens - n_quant
     write = (slabs * n_quant * (w.Dk * w.k_bits + w.Dv * w.v_bits) // 8
-             + slabs * (n_quant // 32) * w.Dk * 4 + slabs * n_quant * (w.Dv // 32) * 4
+             + slabs * (n_quant // w.k_group) * w.Dk * 4 + slabs * n_quant * (w.Dv // w.v_group) * 4
              + slabs * n_ret * (w.Dk + w.Dv) * 2)
     return read + write
 
@@ -92,7 +95,7 @@ def read_traffic():
 def _cpu_worker(args):
     """Runs in a spawned process: oracle on a list of (b, h) slabs of the workload.
     Returns (seconds spent in the oracle, bytes covered)."""
-    wname, slabs = args
+    wname, v_group, k_group, slabs = args
     try:
         from threadpoolctl import threadpool_limits
         threadpool_limits(1)
@@ -101,14 +104,15 @@ def _cpu_worker(args):
     import numpy as np
     import oracle as O
     from workloads import make_queries, make_slab, workload
-    w = workload(wname)
+    w = workload(wname).with_(v_group=v_group, k_group=k_group)
     q = make_queries(w)
     t_chunk = w.T - w.prefill_chunk
     spent = 0.0
     for b, h in slabs:
         s = make_slab(w, b, h)
         # the packed cache before the step (setup, not timed)
-        full = O.pack_slab(s.K, s.V, w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window)
+        full = O.pack_slab(s.K, s.V, w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window, v_group=w.v_group,
+                           k_group=w.k_group)
         t0 = time.perf_counter()
         # the step: pack the prefill chunk ...
         if w.prefill_chunk:
@@ -126,7 +130,8 @@ def _oracle_pack_chunk(O, s, w, t0):
     rest are whole key groups, so the chunk packs like a cache of its own length."""
     assert w.log_window == 0
     n = w.T - t0
-    return O.pack_slab(s.K[t0:], s.V[t0:], w.dtype, w.k_bits, w.v_bits, min(w.n_recent, n), 0)
+    return O.pack_slab(s.K[t0:], s.V[t0:], w.dtype, w.k_bits, w.v_bits, min(w.n_recent, n), 0, v_group=w.v_group,
+                       k_group=w.k_group)
 
 
 def cpu_baseline(w, step_bytes, budget_workers=None):
@@ -138,7 +143,7 @@ def cpu_baseline(w, step_bytes, budget_workers=None):
     ctx = mp.get_context("spawn")
     t0 = time.perf_counter()
     with ctx.Pool(len(per)) as pool:
-        res = pool.map(_cpu_worker, [(w.name, p) for p in per])
+        res = pool.map(_cpu_worker, [(w.name, w.v_group, w.k_group, p) for p in per])
     wall = time.perf_counter() - t0
     busiest = max(r[0] for r in res)
     n_slabs = sum(r[1] for r in res)
@@ -237,6 +242,53 @@ def stream_run(torch, st, qd, P, scale):
     }
 
 
+FORMAT_VARIANTS = [(32, 32), (32, 64), (32, 128), (128, 32), (128, 128)]   # (k_group, v_group)
+
+
+def variants_setup(api, w, Kd, Vd, lay, cache):
+    """Caches of the full workload with keys in groups of 32 or 128 tokens and values
+    in groups of 32, 64 or 128 channels (where the shape allows); the step's own cache
+    serves its own format."""
+    out = {}
+    for kg, vg in FORMAT_VARIANTS:
+        wv = w.with_(k_group=kg, v_group=vg)
+        if (kg, vg) == (w.k_group, w.v_group):
+            out[(kg, vg)] = (lay, cache)
+            continue
+        try:
+            lv = api.Layout.from_workload(wv)
+        except api.L_.KvqError:
+            continue   # this shape's quantized count is not a multiple of the key group
+        out[(kg, vg)] = (lv, api.kv_quant_pack(lv, Kd, Vd))
+    return out
+
+
+def variants_run(torch, api, w, variants, qd, P, scale, reps=30):
+    """Decode over each format variant, calls interleaved one by one so that all see
+    the same clock and thermal state; events around the decode kernel."""
+    ws = {key: api.alloc_workspace(lv, P, qd.device) for key, (lv, _) in variants.items()}
+    out = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.float32, device=qd.device)
+    ev = {key: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)] for key in variants}
+    for key in variants:
+        for e in ev[key]:
+            e[1].record()
+    torch.cuda.synchronize()
+    for i in range(reps):
+        for key, (lv, c) in variants.items():
+            ev[key][i][0].record()
+            api.kv_decode_attn(lv, qd, c, num_partitions=P, softmax_scale=scale, out=out, workspace=ws[key],
+                               after_decode_event=ev[key][i][1])
+    torch.cuda.synchronize()
+    res = {}
+    for (kg, vg), (lv, _) in variants.items():
+        ts = [e[0].elapsed_time(e[1]) for e in ev[(kg, vg)]]
+        p = percentiles(ts)
+        db = decode_bytes(w.with_(k_group=kg, v_group=vg), lv.R, lv.Tq)
+        res["k%d_v%d" % (kg, vg)] = {"decode_kernel_us_p10_p50_p90": p, "algorithmic_bytes": db,
+                                     "GBps_at_p50": round(db / (p[1] * 1e-6) / 1e9, 1)}
+    return res
+
+
 def percentiles(xs):
     xs = sorted(xs)
     pick = lambda f: xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]
@@ -254,6 +306,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-cache leg")
     ap.add_argument("--stream-steps", type=int, default=256)
+    ap.add_argument("--no-variants", action="store_true", help="skip the format-variants leg")
+    ap.add_argument("--v-group", type=int, default=None, help="channels per value group of the step (default 32)")
+    ap.add_argument("--k-group", type=int, default=None, help="tokens per key group of the step (default 32)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -269,6 +324,10 @@ def main():
     from workloads.device import upload_workload
 
     w = workload(args.workload)
+    if args.v_group:
+        w = w.with_(v_group=args.v_group)
+    if args.k_group:
+        w = w.with_(k_group=args.k_group)
     P = args.partitions or w.partitions
     lay = api.Layout.from_workload(w)
     dev = torch.device("cuda:0")
@@ -283,6 +342,7 @@ def main():
         Kc = Kd[:, :, t0:].contiguous()
         Vc = Vd[:, :, t0:].contiguous()
     stream = None if args.no_stream else stream_setup(torch, api, w, Kd, Vd, args.stream_steps)
+    variants = None if args.no_variants else variants_setup(api, w, Kd, Vd, lay, cache)
     del Kd, Vd
     ws = api.alloc_workspace(lay, P, dev)
     out = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.float32, device=dev)
@@ -354,9 +414,11 @@ def main():
         "data": "synthetic: seeded N(0,1) keys with 4 outlier channels x8 and per-channel N(0,2) offsets, "
                 "N(0,0.5) values, N(0,1) queries; bf16 in HBM",
         "config": {
-            "workload": "%s: B%d Hq%d Hkv%d Dk%d Dv%d T%d K%dV%d fp16-window %d log-window %d, %d partitions%s"
+            "workload": "%s: B%d Hq%d Hkv%d Dk%d Dv%d T%d K%dV%d fp16-window %d log-window %d, %d partitions%s%s"
                         % (w.name, w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T, w.k_bits, w.v_bits, w.n_recent,
-                           w.log_window, P, (", + %d-token prefill pack" % chunk) if chunk else ""),
+                           w.log_window, P, (", + %d-token prefill pack" % chunk) if chunk else "",
+                           (", value groups of %d channels" % w.v_group) if w.v_group != 32 else "")
+                        + ((", key groups of %d tokens" % w.k_group) if w.k_group != 32 else ""),
             "batch": w.B, "cached_tokens": w.T, "partitions": P,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
@@ -380,6 +442,9 @@ def main():
     if stream is not None:
         print("# %s: streaming cache, %d decode steps" % (w.name, args.stream_steps), file=sys.stderr, flush=True)
         result["stream"] = stream_run(torch, stream, qd, P, scale)
+    if variants is not None:
+        print("# %s: format variants" % w.name, file=sys.stderr, flush=True)
+        result["format_variants"] = variants_run(torch, api, w, variants, qd, P, scale)
     if not args.no_cpu_baseline:
         print("# %s: cpu baseline (oracle)" % w.name, file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, step_bytes)

@@ -6,9 +6,9 @@
  *  - Keys and values of the attention KV cache are quantized group-wise and
  *    asymmetrically with separate bit widths for keys and values ("Quantize What
  *    Counts: More for Keys, Less for Values": methodology, K4V2; group size 32 for
- *    keys, results).  Keys are quantized per channel over groups of 32 tokens
- *    ("LogQuant: Log-Distributed 2-Bit Quantization of KV Cache", section 5,
- *    per-channel keys); values per token over groups of v_group = 32 (default),
+ *    keys, results).  Keys are quantized per channel over groups of k_group = 32
+ *    (default), 64 or 128 tokens ("LogQuant: Log-Distributed 2-Bit Quantization of
+ *    KV Cache", section 5, per-channel keys); values per token over groups of v_group = 32 (default),
  *    64 or 128 channels (Quantize What Counts, results, sweeps the group size).
  *  - A subset of tokens stays in fp16: the newest n_recent positions and, when
  *    log_window = W > 0, log-spaced positions further back (LogQuant section 2,
@@ -30,11 +30,12 @@
  * Packed cache layout (all buffers caller-allocated, contiguous, row-major;
  * "slab" = one (batch b, kv head h) pair, slabs ordered b-major):
  *   Tq = T - R quantized tokens in ascending position order ("compacted" order),
- *   n_groups = Tq / 32 key groups (group g = compacted tokens 32g .. 32g+31).
+ *   n_groups = Tq / 32 code groups (group g = compacted tokens 32g .. 32g+31);
+ *   Tq is a multiple of k_group, and key group j = code groups j*k_group/32 .. .
  *   k_codes  uint32 [B, Hkv, Tq, Dk*k_bits/32]  word w of a row holds channel
  *            w*(32/k_bits)+k at bits [k*k_bits, (k+1)*k_bits), little-endian
- *   k_scale  fp16   [B, Hkv, n_groups, Dk]
- *   k_zero   fp16   [B, Hkv, n_groups, Dk]
+ *   k_scale  fp16   [B, Hkv, Tq/k_group, Dk]  one per (key group, channel)
+ *   k_zero   fp16   [B, Hkv, Tq/k_group, Dk]
  *   v_codes  uint32 [B, Hkv, n_groups, Dv*v_bits]  the codes of one key group
  *            form a little-endian bit stream (bit i is bit i%32 of word i/32).
  *            With vb = v_bits, TPW = 16/vb, F = Dv*vb/8, the code of compacted
@@ -90,6 +91,7 @@ typedef struct {
   int32_t k_bits, v_bits;         /* each in {2, 4, 8} */
   int32_t n_recent;               /* newest positions kept in fp16 (0..T; T = no quantization) */
   int32_t log_window;             /* W of the log-spaced fp16 positions; 0 = none */
+  int32_t k_group;                /* tokens per key group: 32, 64 or 128 (Tq a multiple of it) */
   int32_t v_group;                /* channels per value group: 32, 64 or 128, dividing Dv */
   int32_t R, Tq, n_groups;        /* derived: retained count, quantized count, Tq / 32 */
 } kvq_layout;
@@ -110,10 +112,12 @@ typedef struct {
 int kvq_layout_init(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T,
                     int k_bits, int v_bits, int n_recent, int log_window);
 
-/* kvq_layout_init with values in groups of v_group channels (32, 64 or 128, dividing
- * Dv; KVQ_ERR_UNSUPPORTED otherwise).  kvq_layout_init is this with v_group = 32. */
+/* kvq_layout_init with keys in groups of k_group tokens (32, 64 or 128; the quantized
+ * count Tq must be a multiple of it) and values in groups of v_group channels (32, 64
+ * or 128, dividing Dv); KVQ_ERR_UNSUPPORTED otherwise.  kvq_layout_init is this with
+ * k_group = v_group = 32. */
 int kvq_layout_init_ex(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T,
-                       int k_bits, int v_bits, int n_recent, int log_window, int v_group);
+                       int k_bits, int v_bits, int n_recent, int log_window, int k_group, int v_group);
 
 /* Byte sizes of the eight kvq_cache buffers, in kvq_cache field order. */
 int kvq_cache_sizes(const kvq_layout* L, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]);
@@ -143,7 +147,7 @@ size_t kvq_decode_workspace_bytes(const kvq_layout* L, int num_partitions);
  *      packed independently (e.g. a prefill chunk appended to an existing cache).
  *   stream: hipStream_t to enqueue on (NULL = default stream).
  * The number of quantized positions before t_begin and before t_begin + t_count
- * must both be multiples of 32 (else KVQ_ERR_UNSUPPORTED).  Output is
+ * must both be multiples of k_group (else KVQ_ERR_UNSUPPORTED).  Output is
  * deterministic: codes, scales and zeros follow the quantizer contract above bit
  * for bit.
  */
@@ -252,7 +256,8 @@ typedef struct {
 int kvq_stream_init(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, int capacity,
                     int k_bits, int v_bits, int n_recent, int log_window);
 
-/* kvq_stream_init with values in groups of v_group channels (as kvq_layout_init_ex). */
+/* kvq_stream_init with values in groups of v_group channels (as kvq_layout_init_ex).
+ * Stream key groups are 32 tokens (a group forms from 32 pending tokens). */
 int kvq_stream_init_ex(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, int capacity,
                        int k_bits, int v_bits, int n_recent, int log_window, int v_group);
 

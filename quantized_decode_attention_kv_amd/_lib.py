@@ -12,7 +12,7 @@ KVQ_GROUP = 32
 KVQ_NUM_CACHE_BUFFERS = 8
 KVQ_STREAM_MAX_ROWS = 4096
 
-LAYOUT_FIELDS = ["B", "Hq", "Hkv", "Dk", "Dv", "T", "k_bits", "v_bits", "n_recent", "log_window", "v_group",
+LAYOUT_FIELDS = ["B", "Hq", "Hkv", "Dk", "Dv", "T", "k_bits", "v_bits", "n_recent", "log_window", "k_group", "v_group",
                  "R", "Tq", "n_groups"]
 CACHE_FIELDS = ["k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_fp16", "v_fp16"]
 
@@ -67,7 +67,7 @@ def load() -> ctypes.CDLL:
     CP = ctypes.POINTER(KvqCache)
     lib.kvq_layout_init.argtypes = [LP] + [c_int] * 10
     lib.kvq_layout_init.restype = c_int
-    lib.kvq_layout_init_ex.argtypes = [LP] + [c_int] * 11
+    lib.kvq_layout_init_ex.argtypes = [LP] + [c_int] * 12
     lib.kvq_layout_init_ex.restype = c_int
     lib.kvq_cache_sizes.argtypes = [LP, ctypes.POINTER(c_sz)]
     lib.kvq_cache_sizes.restype = c_int

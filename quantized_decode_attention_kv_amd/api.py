@@ -17,16 +17,16 @@ _DTYPE_CODES = {torch.float32: L_.KVQ_F32, torch.float16: L_.KVQ_F16, torch.bflo
 class Layout:
     """Shape and fp16-retention policy of one packed cache (kvq_layout)."""
 
-    def __init__(self, B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits, n_recent=0, log_window=0, v_group=32):
+    def __init__(self, B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits, n_recent=0, log_window=0, v_group=32, k_group=32):
         lib = L_.load()
         self._c = L_.KvqLayout()
         L_.check(lib.kvq_layout_init_ex(ctypes.byref(self._c), B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits,
-                                        n_recent, log_window, v_group))
+                                        n_recent, log_window, k_group, v_group))
 
     @classmethod
     def from_workload(cls, w, T=None):
         return cls(w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T if T is None else T, w.k_bits, w.v_bits,
-                   w.n_recent, w.log_window, getattr(w, "v_group", 32))
+                   w.n_recent, w.log_window, getattr(w, "v_group", 32), getattr(w, "k_group", 32))
 
     def __getattr__(self, name):
         if name in L_.LAYOUT_FIELDS:
@@ -59,8 +59,8 @@ class Layout:
         B, H, Tq, nG, R = self.B, self.Hkv, self.Tq, self.n_groups, self.R
         return {
             "k_codes": ((B, H, Tq, self.Dk * self.k_bits // 32), torch.int32),
-            "k_scale": ((B, H, nG, self.Dk), torch.float16),
-            "k_zero": ((B, H, nG, self.Dk), torch.float16),
+            "k_scale": ((B, H, Tq // self.k_group, self.Dk), torch.float16),
+            "k_zero": ((B, H, Tq // self.k_group, self.Dk), torch.float16),
             "v_codes": ((B, H, nG, self.Dv * self.v_bits), torch.int32),
             "v_scale": ((B, H, nG, self.Dv // self.v_group, 32), torch.float16),
             "v_zero": ((B, H, nG, self.Dv // self.v_group, 32), torch.float16),

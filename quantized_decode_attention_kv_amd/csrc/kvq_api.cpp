@@ -49,10 +49,10 @@ int check_layout(const kvq_layout* L) {
   if (st != KVQ_OK) return st;
   const int64_t R = kvq::retained_before(rule_of(*L), L->T);
   const int64_t Tq = L->T - R;
-  if (Tq % KVQ_GROUP != 0)
+  if (Tq % L->k_group != 0)
     return fail(KVQ_ERR_UNSUPPORTED,
-                "%lld quantized tokens is not a multiple of 32; adjust n_recent so T - R is",
-                (long long)Tq);
+                "%lld quantized tokens is not a multiple of the key group (%d); adjust n_recent so T - R is",
+                (long long)Tq, L->k_group);
   if (L->R != R || L->Tq != Tq || L->n_groups != Tq / KVQ_GROUP)
     return fail(KVQ_ERR_INVALID, "layout derived fields are stale; call kvq_layout_init");
   return ok();
@@ -78,6 +78,8 @@ int kvq::check_format(const kvq_layout& l) {
   if (L->n_recent < 0 || L->n_recent > L->T)
     return fail(KVQ_ERR_INVALID, "n_recent (%d) must be in [0, T=%d]", L->n_recent, L->T);
   if (L->log_window < 0) return fail(KVQ_ERR_INVALID, "log_window (%d) must be >= 0", L->log_window);
+  if (L->k_group != 32 && L->k_group != 64 && L->k_group != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "k_group (%d) must be 32, 64 or 128", L->k_group);
   if ((L->v_group != 32 && L->v_group != 64 && L->v_group != 128) || L->Dv % L->v_group)
     return fail(KVQ_ERR_UNSUPPORTED, "v_group (%d) must be 32, 64 or 128 and divide Dv (%d)", L->v_group, L->Dv);
   return ok();
@@ -163,7 +165,7 @@ int kvq::pack_view(const kvq_layout& Lr, int64_t g_stride, int64_t r_stride, int
   if (!aligned16(K) || !aligned16(V)) return fail(KVQ_ERR_INVALID, "K and V must be 16-byte aligned");
   const kvq::RetentionRule r = rule_of(*L);
   const int64_t q0 = kvq::quantized_before(r, t_begin), q1 = kvq::quantized_before(r, t_begin + t_count);
-  if (q0 % KVQ_GROUP || q1 % KVQ_GROUP)
+  if (q0 % L->k_group || q1 % L->k_group)
     return fail(KVQ_ERR_UNSUPPORTED,
                 "chunk [%lld, %lld) splits a key group (%lld and %lld quantized tokens before its ends)",
                 (long long)t_begin, (long long)(t_begin + t_count), (long long)q0, (long long)q1);
@@ -200,11 +202,11 @@ extern "C" {
 
 int kvq_layout_init(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T, int k_bits, int v_bits,
                     int n_recent, int log_window) {
-  return kvq_layout_init_ex(L, B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits, n_recent, log_window, KVQ_GROUP);
+  return kvq_layout_init_ex(L, B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits, n_recent, log_window, KVQ_GROUP, KVQ_GROUP);
 }
 
 int kvq_layout_init_ex(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T, int k_bits, int v_bits,
-                       int n_recent, int log_window, int v_group) {
+                       int n_recent, int log_window, int k_group, int v_group) {
   if (!L) return fail(KVQ_ERR_INVALID, "layout is NULL");
   kvq_layout l{};
   l.B = B;
@@ -217,6 +219,7 @@ int kvq_layout_init_ex(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, in
   l.v_bits = v_bits;
   l.n_recent = n_recent;
   l.log_window = log_window;
+  l.k_group = k_group;
   l.v_group = v_group;
   if (T >= 1 && n_recent >= 0 && n_recent <= T && log_window >= 0) {
     const int64_t R = kvq::retained_before(rule_of(l), T);
@@ -237,7 +240,7 @@ int kvq_cache_sizes(const kvq_layout* L, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]
   const size_t slabs = size_t(L->B) * size_t(L->Hkv);
   const size_t Tq = size_t(L->Tq), nG = size_t(L->n_groups), R = size_t(L->R);
   bytes_out[0] = slabs * Tq * size_t(L->Dk * L->k_bits / 32) * 4;   // k_codes
-  bytes_out[1] = slabs * nG * size_t(L->Dk) * 2;                    // k_scale
+  bytes_out[1] = slabs * (Tq / size_t(L->k_group)) * size_t(L->Dk) * 2;  // k_scale
   bytes_out[2] = bytes_out[1];                                      // k_zero
   bytes_out[3] = slabs * Tq * size_t(L->Dv * L->v_bits / 32) * 4;   // v_codes
   bytes_out[4] = slabs * Tq * size_t(L->Dv / L->v_group) * 2;       // v_scale

@@ -5,7 +5,7 @@
 //
 // Single-token decode attention, out = softmax(scale * q K^T) V, computed
 // directly from the packed cache: key x_hat = code * s + z with one (s, z) per
-// (key group, channel), value x_hat = code * s + z with one (s, z) per (token,
+// (key group of k_group tokens, channel), value x_hat = code * s + z with one (s, z) per (token,
 // group of v_group = 32, 64 or 128 channels).  The retained fp16 tokens are visited as a separate segment;
 // attention does not depend on token order ("LogQuant: Log-Distributed 2-Bit
 // Quantization of KV Cache", section 4, A.V = A_P.V_P).  Scores use the scale of
@@ -106,6 +106,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Dk = a.L.Dk, Dv = a.L.Dv, kb = a.L.k_bits, vb = a.L.v_bits;
   const int vg = a.L.v_group, ngv = Dv / vg;  // value groups per token (the LDS areas are sized for Dv / 32)
+  const int ksh = a.L.k_group == 128 ? 2 : (a.L.k_group == 64 ? 1 : 0);  // key group = code groups >> ksh
   const int nG = a.L.n_groups, R = a.L.R, P = a.P;
   const int64_t slab = int64_t(b) * a.L.Hkv + h;
 
@@ -146,8 +147,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     float bias[G];
     if (active) {
       // q'_c = q_c s_c for this group and the zero-point term sum_c q_c z_c
-      const uint16_t* ks = static_cast<const uint16_t*>(a.cache.k_scale) + (slab * a.g_stride + g) * Dk;
-      const uint16_t* kz = static_cast<const uint16_t*>(a.cache.k_zero) + (slab * a.g_stride + g) * Dk;
+      const int64_t kgi = slab * (a.g_stride >> ksh) + (g >> ksh);  // key group of code group g
+      const uint16_t* ks = static_cast<const uint16_t*>(a.cache.k_scale) + kgi * Dk;
+      const uint16_t* kz = static_cast<const uint16_t*>(a.cache.k_zero) + kgi * Dk;
 #pragma unroll
       for (int i = 0; i < G; ++i) bias[i] = 0.0f;
       for (int c = lane; c < Dk; c += 64) {

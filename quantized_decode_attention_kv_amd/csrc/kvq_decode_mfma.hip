@@ -437,8 +437,11 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
 
   // per-slab bases (wave-uniform)
   const uint8_t* kbase = static_cast<const uint8_t*>(a.cache.k_codes) + slab * a.g_stride * (KVQ_GROUP * KROW);
-  const uint16_t* ksbase = static_cast<const uint16_t*>(a.cache.k_scale) + slab * a.g_stride * DK;
-  const uint16_t* kzbase = static_cast<const uint16_t*>(a.cache.k_zero) + slab * a.g_stride * DK;
+  // key scales / zeros: one row of DK per key group of 32 << ksh tokens, i.e. per
+  // 1 << ksh code groups (scalar register, as vsh below)
+  const int ksh = __builtin_amdgcn_readfirstlane(a.L.k_group == 128 ? 2 : (a.L.k_group == 64 ? 1 : 0));
+  const uint16_t* ksbase = static_cast<const uint16_t*>(a.cache.k_scale) + slab * (a.g_stride >> ksh) * DK;
+  const uint16_t* kzbase = static_cast<const uint16_t*>(a.cache.k_zero) + slab * (a.g_stride >> ksh) * DK;
   const uint32_t* vbase = static_cast<const uint32_t*>(a.cache.v_codes) + slab * a.g_stride * (DV * VB);
   // value scales / zeros: (Dv / v_group) x 32 per group, v_group = 32 << vsh
   // (kept in a scalar register: the copies below take it in their descriptors)
@@ -485,7 +488,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   // a unit without key groups gets empty buffers (its cache buffers may be null)
   const int nrec = nj > 0 ? 0x7fffffff : 0;
   const buf_rsrc rk = make_rsrc(kbase, nrec), rv = make_rsrc(vbase, nrec);
-  const int nsk = nj > 0 ? nG * DK * 2 : 0, nsv = nj > 0 ? nG * ((DV * 2) >> vsh) : 0;
+  const int nsk = nj > 0 ? (nG >> ksh) * DK * 2 : 0, nsv = nj > 0 ? nG * ((DV * 2) >> vsh) : 0;
   const buf_rsrc rks = make_rsrc(ksbase, nsk), rkz = make_rsrc(kzbase, nsk);
   const buf_rsrc rvs = make_rsrc(vsbase, nsv), rvz = make_rsrc(vzbase, nsv);
   auto stage_group = [&](int g, int slot) {
@@ -500,8 +503,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
 #pragma unroll
     for (int k = 0; k < VNP; ++k) lds_dma<16>(rv, voff + 16 * k, gv, sb + LL::kStK + k * 1024);
     unsigned char* ss = sb + LL::kStK + LL::kStV;
-    lds_dma<4>(rks, kso, uint32_t(g) * (DK * 2), ss);
-    lds_dma<4>(rkz, kso, uint32_t(g) * (DK * 2), ss + oKZ);
+    lds_dma<4>(rks, kso, uint32_t(g >> ksh) * (DK * 2), ss);
+    lds_dma<4>(rkz, kso, uint32_t(g >> ksh) * (DK * 2), ss + oKZ);
     lds_dma<4>(rvs, vso, uint32_t(g) * uint32_t((DV * 2) >> vsh), ss + oVS);
     lds_dma<4>(rvz, vso, uint32_t(g) * uint32_t((DV * 2) >> vsh), ss + oVZ);
   };

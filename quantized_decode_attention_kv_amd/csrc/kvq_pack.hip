@@ -145,6 +145,22 @@ __device__ __forceinline__ QParams make_qparams(float mn, float mx, float levels
   return q;
 }
 
+// the same parameters from stored fp16 bits (key groups longer than 32 tokens)
+__device__ __forceinline__ QParams qparams_of(uint16_t sb, uint16_t zb) {
+  QParams q;
+  q.s_bits = sb;
+  q.z_bits = zb;
+  q.s = f16_bits_to_f32(sb);
+  q.z = f16_bits_to_f32(zb);
+  q.r = q.s == 0.0f ? 0.0f : 1.0f / q.s;
+  return q;
+}
+
+// log2(k_group / 32): key group of code group g is g >> key_group_shift
+__device__ __host__ __forceinline__ int key_group_shift(int k_group) {
+  return k_group == 128 ? 2 : (k_group == 64 ? 1 : 0);
+}
+
 // code = 0 if s == 0 else clamp(rint(fl(x - z) / s), 0, levels) (see the header)
 __device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float r, float levels) {
   const float u = x - z;
@@ -249,20 +265,32 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
       }
     }
     __syncthreads();
+    // key groups of 64 or 128 tokens span several workgroups: their scales and
+    // zeros come from key_range_kernel, launched before this kernel
+    const int ksh = key_group_shift(a.L.k_group);
     for (int c = tid; c < Dk; c += kPackThreads) {
-      float mn = kmn_s[0][c], mx = kmx_s[0][c];
+      if (ksh == 0) {
+        float mn = kmn_s[0][c], mx = kmx_s[0][c];
 #pragma unroll
-      for (int w = 1; w < kPackWaves; ++w) {
-        mn = fminf(mn, kmn_s[w][c]);
-        mx = fmaxf(mx, kmx_s[w][c]);
+        for (int w = 1; w < kPackWaves; ++w) {
+          mn = fminf(mn, kmn_s[w][c]);
+          mx = fmaxf(mx, kmx_s[w][c]);
+        }
+        const QParams q = make_qparams(mn, mx, k_levels);
+        const int64_t so = (slab * a.g_stride + g) * Dk + c;
+        out_store(static_cast<uint16_t*>(a.cache.k_scale) + so, q.s_bits);
+        out_store(static_cast<uint16_t*>(a.cache.k_zero) + so, q.z_bits);
+        ks_s[c] = q.s;
+        kz_s[c] = q.z;
+        kr_s[c] = q.r;
+      } else {
+        const int64_t so = (slab * (a.g_stride >> ksh) + (g >> ksh)) * Dk + c;
+        const QParams q = qparams_of(static_cast<const uint16_t*>(a.cache.k_scale)[so],
+                                     static_cast<const uint16_t*>(a.cache.k_zero)[so]);
+        ks_s[c] = q.s;
+        kz_s[c] = q.z;
+        kr_s[c] = q.r;
       }
-      const QParams q = make_qparams(mn, mx, k_levels);
-      const int64_t so = (slab * a.g_stride + g) * Dk + c;
-      out_store(static_cast<uint16_t*>(a.cache.k_scale) + so, q.s_bits);
-      out_store(static_cast<uint16_t*>(a.cache.k_zero) + so, q.z_bits);
-      ks_s[c] = q.s;
-      kz_s[c] = q.z;
-      kr_s[c] = q.r;
     }
     __syncthreads();
     {
@@ -399,8 +427,56 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
   }
 }
 
+// Key groups of k_group = 64 or 128 tokens: per-channel min / max over the key
+// group's tokens, then its scale and zero (make_qparams, as for 32-token groups).
+// One workgroup per (key group of the chunk, kv head, batch row); thread (channel
+// c, slice sl) takes tokens sl, sl + nsl, ...; the slices meet in LDS.
+template <int DT>
+__global__ __launch_bounds__(kPackThreads) void key_range_kernel(const PackArgs a) {
+  __shared__ float mn_s[kPackThreads], mx_s[kPackThreads];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int Dk = a.L.Dk, kg = a.L.k_group, ksh = key_group_shift(kg);
+  const int64_t slab = int64_t(b) * a.L.Hkv + h;
+  const RetentionRule rr{a.L.T, a.L.n_recent, a.L.log_window};
+  const int64_t kj = (a.g_begin >> ksh) + blockIdx.x;  // key group in the slab
+  const int64_t q0 = kj * kg;                          // its first compacted token
+  const bool plain = quantized_before(rr, q0 + kg) == q0 + kg;
+  const int nsl = kPackThreads / Dk;
+  const int c = tid % Dk, sl = tid / Dk;
+  float mn = INFINITY, mx = -INFINITY;
+  if (sl < nsl) {
+    for (int t = sl; t < kg; t += nsl) {
+      const int64_t row = (plain ? q0 + t : quantized_position(rr, q0 + t)) - a.t_begin;
+      const float x = load_elem<DT>(a.K, (slab * a.t_count + row) * Dk + c);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+  }
+  mn_s[tid] = mn;
+  mx_s[tid] = mx;
+  __syncthreads();
+  if (tid < Dk) {
+    for (int i = 1; i < nsl; ++i) {
+      mn = fminf(mn, mn_s[i * Dk + tid]);
+      mx = fmaxf(mx, mx_s[i * Dk + tid]);
+    }
+    const QParams q = make_qparams(mn, mx, float((1 << a.L.k_bits) - 1));
+    const int64_t so = (slab * (a.g_stride >> ksh) + kj) * Dk + tid;
+    out_store(static_cast<uint16_t*>(a.cache.k_scale) + so, q.s_bits);
+    out_store(static_cast<uint16_t*>(a.cache.k_zero) + so, q.z_bits);
+  }
+}
+
 template <int DT>
 hipError_t launch_dt(const PackArgs& a, dim3 grid, hipStream_t stream) {
+  const int ksh = key_group_shift(a.L.k_group);
+  if (ksh > 0 && a.n_groups_chunk > 0) {
+    const dim3 kgrid(unsigned(a.n_groups_chunk >> ksh), unsigned(a.L.Hkv), unsigned(a.L.B));
+    hipLaunchKernelGGL((key_range_kernel<DT>), kgrid, dim3(kPackThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int kb = a.L.k_bits, vb = a.L.v_bits;
 #define KVQ_PACK_CASE(K_, V_)                                                                     \
   if (kb == K_ && vb == V_) {                                                                     \

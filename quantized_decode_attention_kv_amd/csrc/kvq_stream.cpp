@@ -40,6 +40,7 @@ int check_stream(const kvq_stream* S) {
   const kvq_layout& L = S->L;
   const int st = kvq::check_format(L);
   if (st != KVQ_OK) return st;
+  if (L.k_group != KVQ_GROUP) return fail(KVQ_ERR_UNSUPPORTED, "stream key groups are %d tokens", KVQ_GROUP);
   if (L.log_window > 0 && L.n_recent < L.log_window)
     return fail(KVQ_ERR_UNSUPPORTED, "a stream needs log_window == 0 or n_recent (%d) >= log_window (%d)",
                 L.n_recent, L.log_window);
@@ -151,6 +152,7 @@ int kvq_stream_init_ex(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, in
   l.v_bits = v_bits;
   l.n_recent = n_recent;
   l.log_window = log_window;
+  l.k_group = KVQ_GROUP;
   l.v_group = v_group;
   int st = kvq::check_format(l);
   if (st != KVQ_OK) return st;

@@ -72,7 +72,7 @@ def test_layout_matches_oracle_retention(lib, w):
 def test_retention_host_vs_oracle(lib, T, n_recent, W):
     r, u = O.split_positions(T, n_recent, W)
     lay = L_.KvqLayout(B=1, Hq=1, Hkv=1, Dk=32, Dv=32, T=T, k_bits=4, v_bits=2, n_recent=n_recent, log_window=W,
-                       v_group=32, R=len(r), Tq=len(u), n_groups=len(u) // 32)
+                       k_group=32, v_group=32, R=len(r), Tq=len(u), n_groups=len(u) // 32)
     if len(u) % 32:
         # layouts with a partial group are refused; the counting itself is checked via init's message
         st, _ = _layout(lib, 1, 1, 1, 32, 32, T, 4, 2, n_recent, W)
@@ -87,13 +87,14 @@ def test_cache_sizes_match_oracle_arrays(lib):
     for w in small_cases():
         lay = L_.KvqLayout()
         st = lib.kvq_layout_init_ex(ctypes.byref(lay), w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T, w.k_bits, w.v_bits,
-                                    w.n_recent, w.log_window, w.v_group)
+                                    w.n_recent, w.log_window, w.k_group, w.v_group)
         assert st == 0
         sizes = (ctypes.c_size_t * 8)()
         assert lib.kvq_cache_sizes(ctypes.byref(lay), sizes) == 0
         from workloads import make_all
         K, V = make_all(w.with_(B=1, Hkv=1, Hq=w.G), workers=1)
-        p = O.pack_slab(K[0, 0], V[0, 0], w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window, v_group=w.v_group)
+        p = O.pack_slab(K[0, 0], V[0, 0], w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window, v_group=w.v_group,
+                        k_group=w.k_group)
         for i, k in enumerate(O.CACHE_KEYS):
             assert sizes[i] == p[k].nbytes * w.B * w.Hkv, k
 
@@ -195,10 +196,25 @@ def test_status_strings(lib):
                                           (192, 64, L_.KVQ_OK)])
 def test_value_group_limits(lib, Dv, vg, status):
     lay = L_.KvqLayout()
-    assert lib.kvq_layout_init_ex(ctypes.byref(lay), 1, 4, 2, 128, Dv, 256, 4, 2, 0, 0, vg) == status
+    assert lib.kvq_layout_init_ex(ctypes.byref(lay), 1, 4, 2, 128, Dv, 256, 4, 2, 0, 0, 32, vg) == status
     if status == L_.KVQ_OK:
         sizes = (ctypes.c_size_t * 8)()
         assert lib.kvq_cache_sizes(ctypes.byref(lay), sizes) == 0
         assert sizes[4] == 2 * (256 // 32) * 32 * (Dv // vg) * 2   # v_scale: slabs x groups x Dv/vg x 32 fp16
     # the default init is value groups of 32
     assert lib.kvq_layout_init(ctypes.byref(lay), 1, 4, 2, 128, 128, 256, 4, 2, 0, 0) == 0 and lay.v_group == 32
+
+
+@pytest.mark.parametrize("T,n_recent,kg,status", [(256, 0, 64, L_.KVQ_OK), (256, 0, 128, L_.KVQ_OK),
+                                                  (288, 32, 128, L_.KVQ_OK), (288, 0, 128, L_.KVQ_ERR_UNSUPPORTED),
+                                                  (256, 0, 96, L_.KVQ_ERR_UNSUPPORTED)])
+def test_key_group_limits(lib, T, n_recent, kg, status):
+    lay = L_.KvqLayout()
+    assert lib.kvq_layout_init_ex(ctypes.byref(lay), 1, 4, 2, 128, 128, T, 4, 2, n_recent, 0, kg, 32) == status
+    if status == L_.KVQ_OK:
+        sizes = (ctypes.c_size_t * 8)()
+        assert lib.kvq_cache_sizes(ctypes.byref(lay), sizes) == 0
+        assert sizes[1] == 2 * (lay.Tq // kg) * 128 * 2     # k_scale: slabs x key groups x Dk fp16
+        # a chunk must not split a key group
+        assert lib.kv_quant_pack(ctypes.byref(lay), 0, 32, ctypes.c_void_p(16), ctypes.c_void_p(16), L_.KVQ_BF16,
+                                 ctypes.byref(L_.KvqCache()), None) == L_.KVQ_ERR_UNSUPPORTED

@@ -98,4 +98,11 @@ def small_cases():
                  n_recent=32, dtype="f32", partitions=4, seed=18, v_group=64),
         Workload("small_d256_k4v4_vg128", B=1, Hq=2, Hkv=2, Dk=256, Dv=256, T=288, k_bits=4, v_bits=4,
                  dtype="bf16", partitions=2, seed=19, v_group=128),
+        # key groups longer than 32 tokens (matrix-core and generic paths, log-spaced fp16 tokens)
+        Workload("small_k4v2_kg128", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=1064, k_bits=4, v_bits=2,
+                 n_recent=40, dtype="bf16", partitions=5, seed=20, k_group=128),
+        Workload("small_k2v2_kg64_log", B=1, Hq=4, Hkv=1, Dk=128, Dv=128, T=1487, k_bits=2, v_bits=2,
+                 n_recent=64, log_window=64, dtype="bf16", partitions=3, seed=21, k_group=64, v_group=64),
+        Workload("small_g2_k8v4_kg64_f32", B=1, Hq=4, Hkv=2, Dk=96, Dv=64, T=416, k_bits=8, v_bits=4,
+                 n_recent=32, dtype="f32", partitions=4, seed=22, k_group=64),
     ]
