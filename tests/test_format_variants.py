@@ -151,3 +151,59 @@ def test_bad_key_group():
         pack_slab(np.zeros((96, 32), np.float32), np.zeros((96, 32), np.float32), "f32", 4, 2, 0, 0, k_group=64)
     with pytest.raises(ValueError):
         pack_slab(np.zeros((64, 32), np.float32), np.zeros((64, 32), np.float32), "f32", 4, 2, 0, 0, k_group=48)
+
+
+# ------------------------------------------------------------------- 1-bit codes
+# With one bit, the quantizer contract reduces to a threshold: code = rint(t) clamped
+# to [0, 1] with t = (x - z) / s, i.e. 1 exactly when t > 0.5 (rint sends 0.5 to the
+# even 0).  Key words are plain little-endian bit strings along the channels, which
+# numpy's packbits writes out independently.
+
+@pytest.mark.parametrize("seed", [51, 52])
+def test_one_bit_codes_are_a_threshold(seed):
+    from oracle import quantize_groups
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((40, 32)) * 3).astype(np.float32)
+    x[0, :] = np.linspace(-1, 1, 32, dtype=np.float32)            # includes exact midpoints
+    codes, s16, z16 = quantize_groups(x, 1)
+    s = s16.astype(np.float32)[:, None]
+    z = z16.astype(np.float32)[:, None]
+    t = (x - z) / s
+    assert np.array_equal(codes, (t > np.float32(0.5)).astype(np.uint8))
+
+
+def test_one_bit_key_words_match_packbits():
+    from oracle import pack_codes
+    rng = np.random.default_rng(53)
+    codes = rng.integers(0, 2, size=(7, 96), dtype=np.uint8)
+    words = pack_codes(codes, 1)
+    want = np.packbits(codes, axis=1, bitorder="little").view("<u4")
+    assert np.array_equal(words, want)
+
+
+@pytest.mark.parametrize("Dv", [32, 64, 128])
+def test_one_bit_value_layout(Dv):
+    from oracle import pack_value_codes, unpack_value_codes, value_bit_position
+    tau, c = np.meshgrid(np.arange(32), np.arange(Dv), indexing="ij")
+    pos = value_bit_position(tau, c, Dv, 1)
+    assert np.array_equal(np.sort(pos.ravel()), np.arange(32 * Dv))  # one bit per code, no gaps
+    # hand-derived at Dv = 128 (one 16-bit field per (octet, column, pair): 8 tiles of the first
+    # token of the pair, then 8 of the second): token 13 = octet 1, j = 5; channel 37 = tile 2, column 5
+    if Dv == 128:
+        assert value_bit_position(13, 37, 128, 1) == ((16 * 1 + 5) * 4 + 1) * 16 + 8 + 2
+        assert value_bit_position(0, 0, 128, 1) == 0 and value_bit_position(4, 0, 128, 1) == 8
+    rng = np.random.default_rng(54)
+    codes = rng.integers(0, 2, size=(3, 32, Dv), dtype=np.uint8)
+    assert np.array_equal(unpack_value_codes(pack_value_codes(codes, 1), 1), codes)
+
+
+def test_one_bit_pack_slab_round_trip():
+    rng = np.random.default_rng(55)
+    T, Dk, Dv = 96, 64, 128
+    K = rng.standard_normal((T, Dk)).astype(np.float32)
+    V = rng.standard_normal((T, Dv)).astype(np.float32)
+    p = pack_slab(K, V, "f32", 1, 1, 32, 0)
+    assert p["k_codes"].shape == (64, 2) and p["v_codes"].shape == (2, 128)
+    Khat, Vhat = dequant_slab(p, 1, 1)
+    ks = np.repeat(p["k_scale"].view(np.float16).astype(np.float64), 32, axis=0)
+    assert np.all(np.abs(Khat[:64] - K[:64]) <= 0.5 * ks + 1e-2)
