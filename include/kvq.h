@@ -88,7 +88,7 @@ enum { KVQ_GROUP = 32, KVQ_MAX_HEAD_DIM = 256, KVQ_MAX_GQA = 16, KVQ_NUM_CACHE_B
  * read-only afterwards (calls re-derive and check R, Tq, n_groups). */
 typedef struct {
   int32_t B, Hq, Hkv, Dk, Dv, T;
-  int32_t k_bits, v_bits;         /* each in {2, 4, 8} */
+  int32_t k_bits, v_bits;         /* each in {1, 2, 4, 8} (1-bit caches decode on the vector-ALU kernel) */
   int32_t n_recent;               /* newest positions kept in fp16 (0..T; T = no quantization) */
   int32_t log_window;             /* W of the log-spaced fp16 positions; 0 = none */
   int32_t k_group;                /* tokens per key group: 32, 64 or 128 (Tq a multiple of it) */
@@ -107,7 +107,7 @@ typedef struct {
 /* Fill *L and derive R, Tq, n_groups.  Limits (else KVQ_ERR_INVALID, or
  * KVQ_ERR_UNSUPPORTED where the request is well-formed): all sizes >= 1,
  * Hq % Hkv == 0 with Hq / Hkv <= KVQ_MAX_GQA, Dk and Dv multiples of 32 up to
- * KVQ_MAX_HEAD_DIM, bits in {2, 4, 8}, 0 <= n_recent <= T, log_window >= 0, and
+ * KVQ_MAX_HEAD_DIM, bits in {1, 2, 4, 8}, 0 <= n_recent <= T, log_window >= 0, and
  * the quantized token count Tq a multiple of 32 (choose n_recent accordingly). */
 int kvq_layout_init(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T,
                     int k_bits, int v_bits, int n_recent, int log_window);

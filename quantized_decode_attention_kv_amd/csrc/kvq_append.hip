@@ -215,9 +215,10 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((append_kernel<K_, V_>), dim3(unsigned(slabs)), dim3(kAppendThreads), 0, stream, a); \
     return hipGetLastError();                                                                        \
   }
-  KVQ_APPEND_CASE(2, 2) KVQ_APPEND_CASE(2, 4) KVQ_APPEND_CASE(2, 8)
-  KVQ_APPEND_CASE(4, 2) KVQ_APPEND_CASE(4, 4) KVQ_APPEND_CASE(4, 8)
-  KVQ_APPEND_CASE(8, 2) KVQ_APPEND_CASE(8, 4) KVQ_APPEND_CASE(8, 8)
+  KVQ_APPEND_CASE(1, 1) KVQ_APPEND_CASE(1, 2) KVQ_APPEND_CASE(1, 4) KVQ_APPEND_CASE(1, 8)
+  KVQ_APPEND_CASE(2, 1) KVQ_APPEND_CASE(2, 2) KVQ_APPEND_CASE(2, 4) KVQ_APPEND_CASE(2, 8)
+  KVQ_APPEND_CASE(4, 1) KVQ_APPEND_CASE(4, 2) KVQ_APPEND_CASE(4, 4) KVQ_APPEND_CASE(4, 8)
+  KVQ_APPEND_CASE(8, 1) KVQ_APPEND_CASE(8, 2) KVQ_APPEND_CASE(8, 4) KVQ_APPEND_CASE(8, 8)
 #undef KVQ_APPEND_CASE
   return hipErrorInvalidValue;
 }

@@ -173,11 +173,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
       float acc[G];
 #pragma unroll
       for (int i = 0; i < G; ++i) acc[i] = 0.0f;
-      for (int w = hf * (kw / 2); w < (hf + 1) * (kw / 2); ++w) {
+      // channels [hf Dk / 2, (hf + 1) Dk / 2) in ascending order (a half may start
+      // inside a word: at 1 bit a 32-channel row is one word)
+      const int c_end = (hf + 1) * (Dk / 2);
+      for (int c = hf * (Dk / 2); c < c_end;) {
+        const int w = c / kper;
         const uint32_t word = row[w];
-        for (int k = 0; k < kper; ++k) {
-          const float cf = float((word >> (k * kb)) & kmask);
-          const float* kqc = kq + (w * kper + k) * G;
+        const int w_end = min(c_end, (w + 1) * kper);
+        for (; c < w_end; ++c) {
+          const float cf = float((word >> ((c - w * kper) * kb)) & kmask);
+          const float* kqc = kq + c * G;
 #pragma unroll
           for (int i = 0; i < G; ++i) acc[i] = fmaf(kqc[i], cf, acc[i]);
         }

@@ -231,13 +231,13 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
     for (int t = 0; t < 8; ++t) rows[t] = row_of(8 * wave + t);
     // Dv == 128: thread (token tid / 8, 16-channel tile tid % 8) takes its value
     // row segment now, so that its load latency overlaps the key phase
-    const bool v128 = Dv == 128;
+    const bool v128 = Dv == 128 && VB >= 2;  // 1-bit values take the generic path
     const int vtok = tid >> 3, vtile = tid & 7;
     Raw16<DT> vraw;
     if (v128) vraw = load16<DT>(a.V, (slab * a.t_count + row_of(vtok)) * 128 + 16 * vtile);
 
     // (4- and 8-bit key words are written byte by byte below, every byte once)
-    if constexpr (KB == 2) {
+    if constexpr (KB <= 2) {
       for (int i = tid; i < KVQ_GROUP * kwords; i += kPackThreads) kw_s[i] = 0u;
     }
     for (int i = tid; i < vwords; i += kPackThreads) vw_s[i] = 0u;
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
             const uint32_t c0 = quant_code(kx[k][t].x, s0, z0, r0, k_levels);
             const uint32_t c1 = quant_code(kx[k][t].y, s1, z1, r1, k_levels);
             const uint32_t f = c0 | (c1 << KB);
-            if constexpr (KB == 2) {
+            if constexpr (KB <= 2) {
               atomicOr(&kw_s[(8 * wave + t) * kwords + word], f << bit);
             } else {
               // the lane's two fields fill one byte (4 bits) or two (8 bits) of the
@@ -483,9 +483,10 @@ hipError_t launch_dt(const PackArgs& a, dim3 grid, hipStream_t stream) {
     hipLaunchKernelGGL((pack_kernel<DT, K_, V_>), grid, dim3(kPackThreads), 0, stream, a);       \
     return hipGetLastError();                                                                     \
   }
-  KVQ_PACK_CASE(2, 2) KVQ_PACK_CASE(2, 4) KVQ_PACK_CASE(2, 8)
-  KVQ_PACK_CASE(4, 2) KVQ_PACK_CASE(4, 4) KVQ_PACK_CASE(4, 8)
-  KVQ_PACK_CASE(8, 2) KVQ_PACK_CASE(8, 4) KVQ_PACK_CASE(8, 8)
+  KVQ_PACK_CASE(1, 1) KVQ_PACK_CASE(1, 2) KVQ_PACK_CASE(1, 4) KVQ_PACK_CASE(1, 8)
+  KVQ_PACK_CASE(2, 1) KVQ_PACK_CASE(2, 2) KVQ_PACK_CASE(2, 4) KVQ_PACK_CASE(2, 8)
+  KVQ_PACK_CASE(4, 1) KVQ_PACK_CASE(4, 2) KVQ_PACK_CASE(4, 4) KVQ_PACK_CASE(4, 8)
+  KVQ_PACK_CASE(8, 1) KVQ_PACK_CASE(8, 2) KVQ_PACK_CASE(8, 4) KVQ_PACK_CASE(8, 8)
 #undef KVQ_PACK_CASE
   return hipErrorInvalidValue;
 }

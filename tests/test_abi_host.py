@@ -101,7 +101,7 @@ def test_cache_sizes_match_oracle_arrays(lib):
 
 @pytest.mark.parametrize("args,status", [
     ((1, 4, 2, 128, 128, 256, 3, 2, 0, 0), L_.KVQ_ERR_UNSUPPORTED),   # 3-bit keys
-    ((1, 4, 2, 128, 128, 256, 4, 1, 0, 0), L_.KVQ_ERR_UNSUPPORTED),   # 1-bit values
+    ((1, 4, 2, 128, 128, 256, 4, 3, 0, 0), L_.KVQ_ERR_UNSUPPORTED),   # 3-bit values
     ((1, 5, 2, 128, 128, 256, 4, 2, 0, 0), L_.KVQ_ERR_INVALID),       # Hq % Hkv
     ((1, 6, 2, 128, 128, 256, 4, 2, 0, 0), L_.KVQ_ERR_UNSUPPORTED),   # group of 3 queries
     ((1, 4, 2, 100, 128, 256, 4, 2, 0, 0), L_.KVQ_ERR_INVALID),       # Dk not a multiple of 32

@@ -161,6 +161,13 @@ def test_stream_value_groups_64_generic():
     _run_stream(w, T0, T0 + 200, {T0 + 1, T0 + 77, T0 + 150}, [1, 2])
 
 
+def test_stream_one_bit():
+    """1-bit keys and values in a stream (the append kernel's 1-bit words), f32 inputs."""
+    w = Workload("stream_k1v1", B=1, Hq=4, Hkv=2, Dk=64, Dv=128, T=300, k_bits=1, v_bits=1,
+                 n_recent=8, dtype="f32", seed=28)
+    _run_stream(w, 0, 200, {9, 40, 41, 104, 160}, [1, 2])
+
+
 def test_stream_full_capacity_and_errors():
     """A stream filled to its capacity refuses another token and keeps its state."""
     w = Workload("stream_full", B=1, Hq=4, Hkv=1, Dk=64, Dv=64, T=96, k_bits=4, v_bits=4,
