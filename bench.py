@@ -68,11 +68,17 @@ def pack_bytes(w, n_tokens, n_quant):
 
 
 def kernel_source_hash():
-    """Hash of the decode kernel sources, to tell whether stored counter data is current."""
+    """Hash of the decode kernel sources without their comments and blank lines, to
+    tell whether stored counter data is current (a comment edit changes no kernel)."""
     h = hashlib.sha256()
     for path in DECODE_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for line in text.splitlines():
+            code = re.sub(r"//.*", "", line).rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

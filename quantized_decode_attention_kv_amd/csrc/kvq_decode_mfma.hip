@@ -15,19 +15,22 @@
 // 9 are first shifted down by 8).
 // Per-channel key scales and per-token value scales are folded into the other
 // operand and the zero points become separate terms:
-//   scores  s_t = sum_c (q_c s_c) n_tc + sum_c q_c z_c                (per key group)
-//   values  o_c = sum_t (p_t s_t,g) n_tc + sum_t p_t z_t,g   (g = 32-channel group of c)
+//   scores  s_t = sum_c (q_c s_c) n_tc + sum_c q_c z_c   (s_c, z_c of the key group
+//           of 32, 64 or 128 tokens that holds the 32-token code group)
+//   values  o_c = sum_t (p_t s_t,g) n_tc + sum_t p_t z_t,g   (g = value group of c:
+//           32, 64 or 128 channels)
 // The folded operands q_c s_c and p_t s_t,g are split into fp16 hi + lo parts
 // (each rounded to nearest, about 22 significant bits together).
 //
-// Work units: one workgroup of one wave per contiguous run of key groups of one
-// (batch, kv head) slab; a split-K partition is one run or is cut into 2 or 4
+// Work units: one wave per contiguous run of key groups of one (batch, kv head)
+// slab, four independent waves per workgroup (one on each SIMD of a compute
+// unit, see kWavesPerGroup); a split-K partition is one run or is cut into 2 or 4
 // (see decode_mfma_units).  Units share nothing and need no barriers: each stages
-// its groups through a two-slot LDS ring (buffer loads straight into LDS, so
-// groups j + 1 and j + 2 are in flight while group j is computed), keeps its own
-// online-softmax state and writes its own partial result.  A unit needs 10 KB of
-// LDS and at most 128 VGPRs for the common shapes, so 16 waves share a compute
-// unit.  Per group:
+// its groups through an LDS ring of D = 2..4 slots (buffer loads straight into
+// LDS, so up to D - 1 later groups are in flight while one is computed), keeps its
+// own online-softmax state and writes its own partial result.  The launcher takes
+// the deepest ring whose LDS still keeps the whole grid resident (D = 4, 8 waves
+// per compute unit, on the 128K-token workload).  Per group:
 //   1. Q' = q s (hi, lo) for 64 (query, 8-channel block) tasks, one per lane, into
 //      a wave-private LDS tile;
 //   2. scores S^T[token, column] = codes (A: 16 tokens x 32 channels) x Q' (B), two
@@ -47,8 +50,8 @@
 //      tiles.  A lane's B operand for tile t is its code word of that tile's
 //      chunk masked to the tile's bit slot: one AND per operand register (plus
 //      one shift per word for the slots above the mantissa).
-// Retained fp16 rows (recent window, log-spaced tokens) are folded into the same
-// online state first: scores on the MFMA (A = fp16 key rows), values on the VALU.
+// Retained fp16 rows (recent window, log-spaced tokens) join the same online state
+// after the key groups: scores on the MFMA (A = fp16 key rows), values on the VALU.
 #include <algorithm>
 
 #include <hip/hip_fp16.h>
