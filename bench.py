@@ -379,11 +379,13 @@ def main():
     scale = 1.0 / (w.Dk ** 0.5)
     torch.cuda.synchronize()
 
-    # events per step: before the pack, before the decode call, after its decode
-    # kernel (recorded by the library between the decode and the merge kernel),
-    # after the call; all on the stream the kernels run on
-    def step(ev=None):
-        if ev is not None:
+    # Events on the stream the kernels run on.  The timed steps carry only the two
+    # the roofline needs: before the decode call and after its decode kernel (the
+    # library records the latter between the decode and the merge kernel); every
+    # event recorded costs the step time (measured ~2 us each), so the pack and merge
+    # are timed in a separate breakdown pass right after, with all four events.
+    def step(ev=None, full=False):
+        if full:
             ev[0].record()
         if chunk:
             api.kv_quant_pack(lay, Kc, Vc, cache=cache, t_begin=t0)
@@ -391,25 +393,35 @@ def main():
             ev[1].record()
         api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws,
                            after_decode_event=None if ev is None else ev[2])
-        if ev is not None:
+        if full:
             ev[3].record()
+
+    def new_events(n):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        for e in evs:
+            for x in e:
+                x.record()  # torch creates an event at its first record: not inside a timed region
+        torch.cuda.synchronize()
+        return evs
 
     print("# %s: warmup %d" % (w.name, args.warmup), file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for e in events:
-        e[2].record()  # torch creates events lazily, at their first record
-    torch.cuda.synchronize()
+    events = new_events(args.steps)
     start = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - start
-    pack_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    dec_ms = sum(e[1].elapsed_time(e[3]) for e in events) / args.steps
     kern_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-    merge_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    n_bd = min(args.steps, 20)
+    bd = new_events(n_bd)
+    for i in range(n_bd):
+        step(bd[i], full=True)
+    torch.cuda.synchronize()
+    pack_ms = sum(e[0].elapsed_time(e[1]) for e in bd) / n_bd
+    dec_ms = sum(e[1].elapsed_time(e[3]) for e in bd) / n_bd
+    merge_ms = sum(e[2].elapsed_time(e[3]) for e in bd) / n_bd
     ms_per_step = wall * 1e3 / args.steps
 
     if args.copy_calibration:
@@ -461,7 +473,7 @@ def main():
                    "kernel_us_p10_p50_p90": percentiles([e[1].elapsed_time(e[2]) for e in events]),
                    "cold": cold, "algorithmic_bytes": db},
         "pack": ({"us": round(pack_ms * 1e3, 2), "GBps": round(pb / (pack_ms * 1e-3) / 1e9, 1),
-                  "us_p10_p50_p90": percentiles([e[0].elapsed_time(e[1]) for e in events]),
+                  "us_p10_p50_p90": percentiles([e[0].elapsed_time(e[1]) for e in bd]),
                   "algorithmic_bytes": pb} if chunk else None),
         "hbm_read_ceiling": ceiling,
         "roofline": {"bound": "hbm", "achieved": round(kern_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
