@@ -337,6 +337,7 @@ def main():
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-cache leg")
     ap.add_argument("--stream-steps", type=int, default=256)
     ap.add_argument("--no-variants", action="store_true", help="skip the format-variants leg")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cache-cold decode leg")
     ap.add_argument("--v-group", type=int, default=None, help="channels per value group of the step (default 32)")
     ap.add_argument("--k-group", type=int, default=None, help="tokens per key group of the step (default 32)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -440,7 +441,7 @@ def main():
     kern_gbps = db / (kern_ms * 1e-3) / 1e9
     traffic = read_traffic()
     ceiling = read_ceiling(torch, api, db, dev)
-    cold = decode_cold(torch, api, lay, cache, qd, P, scale, dev)
+    cold = None if args.no_cold else decode_cold(torch, api, lay, cache, qd, P, scale, dev)
 
     result = {
         "metric": METRIC,
