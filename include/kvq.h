@@ -157,9 +157,8 @@ int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count,
 
 /*
  * kv_decode_attn — single-token decode attention over a packed cache: one decode
- * kernel whose workgroups each take a contiguous run of key groups of one
- * (batch row, kv head) pair and, when P > 1, one merge kernel after it on the
- * same stream.
+ * kernel whose waves each take a contiguous run of key groups of one (batch row,
+ * kv head) pair and, when P > 1, one merge kernel after it on the same stream.
  *   q:   [B, Hq, Dk] device array of dtype q_dtype; query head i reads KV head
  *        i / (Hq / Hkv) (grouped-query attention: the Hq/Hkv queries of one KV head
  *        share each read of its cache).

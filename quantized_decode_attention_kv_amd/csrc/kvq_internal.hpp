@@ -36,7 +36,8 @@ struct DecodeArgs {
 };
 
 // Work units of the matrix-core decode kernel: each of the P split-K partitions
-// is cut into c = 1, 2 or 4 contiguous runs, one single-wave workgroup each.  c
+// is cut into c = 1, 2 or 4 contiguous runs, one wave each (four independent waves
+// share a workgroup, one per SIMD of a compute unit).  c
 // is the largest that keeps the grid within `resident` waves (what the device
 // holds at once for the kernel's occupancy), so short caches still fill the chip
 // while long ones keep each wave on a long run of key groups.  P == 1 is one
