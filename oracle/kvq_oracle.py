@@ -52,6 +52,10 @@ Canonical packed layout for one (b, kv-head) slab (the same index formulas appea
   tiles in that chunk and F = Dv*vb/8 bits per (o, n, j%4) field: one field pairs
   tokens j and j+4 of an octet, the first of them in the low half of every chunk
   (library format choice, see ``value_bit_position``);
+* 3-bit codes (32 is not a multiple of 3) are plain little-endian bit streams
+  instead, so a code may straddle two words: key row t holds channel c at stream
+  bits [3c, 3c+3), and a group's value stream holds token tau, channel c at bits
+  [3(tau*Dv + c), 3(tau*Dv + c) + 3);
 * v_scale, v_zero fp16 [Tq/32, Dv/gV, 32]  (one pair per token and gV-channel
   group, gV = 32 by default, the 32 tokens of a group contiguous);
 * k_fp16 [R, Dk], v_fp16 [R, Dv] fp16 rows of the retained positions, ascending.
@@ -173,7 +177,10 @@ def quantize_groups(x: np.ndarray, bits: int):
 
 
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
-    """codes [..., n] -> uint32 [..., n*bits/32]; code k of each word at bits [k*bits, k*bits+bits)."""
+    """codes [..., n] -> uint32 [..., n*bits/32]; code k of each word at bits [k*bits, k*bits+bits).
+    3-bit codes: code c at bits [3c, 3c+3) of the row's little-endian bit stream."""
+    if bits == 3:
+        return _stream_pack(codes, 3)
     per = 32 // bits
     c = np.asarray(codes, dtype=np.uint32)
     c = c.reshape(c.shape[:-1] + (c.shape[-1] // per, per))
@@ -183,11 +190,33 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
 
 def unpack_codes(words: np.ndarray, bits: int) -> np.ndarray:
     """Inverse of pack_codes: uint32 [..., w] -> uint8 [..., w*32/bits]."""
+    if bits == 3:
+        return _stream_unpack(words, 3)
     per = 32 // bits
     w = np.asarray(words, dtype=np.uint32)[..., None]
     shifts = (np.arange(per, dtype=np.uint32) * np.uint32(bits))
     c = (w >> shifts) & np.uint32(2 ** bits - 1)
     return c.reshape(c.shape[:-2] + (c.shape[-2] * per,)).astype(np.uint8)
+
+
+def _stream_pack(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes [..., n] -> uint32 [..., n*bits/32]: code k at bits [k*bits, (k+1)*bits)
+    of a little-endian bit stream (bit i of the stream = bit i%32 of word i/32)."""
+    c = np.asarray(codes, dtype=np.uint32)
+    n = c.shape[-1]
+    if (n * bits) % 32:
+        raise ValueError("a %d-bit stream of %d codes is not a whole number of words" % (bits, n))
+    planes = (c[..., :, None] >> np.arange(bits, dtype=np.uint32)) & np.uint32(1)   # [..., n, bits]
+    stream = planes.reshape(c.shape[:-1] + (n * bits // 32, 32))                      # bit i at [i/32, i%32]
+    return (stream << np.arange(32, dtype=np.uint32)).sum(axis=-1, dtype=np.uint64).astype(np.uint32)
+
+
+def _stream_unpack(words: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of _stream_pack: uint32 [..., w] -> uint8 [..., w*32/bits]."""
+    w = np.asarray(words, dtype=np.uint32)
+    stream = (w[..., :, None] >> np.arange(32, dtype=np.uint32)) & np.uint32(1)     # [..., w, 32]
+    planes = stream.reshape(w.shape[:-1] + (w.shape[-1] * 32 // bits, bits))
+    return (planes << np.arange(bits, dtype=np.uint32)).sum(axis=-1).astype(np.uint8)
 
 
 def value_bit_position(tau, c, Dv: int, bits: int):
@@ -196,6 +225,8 @@ def value_bit_position(tau, c, Dv: int, bits: int):
     module header).  Works elementwise on integer arrays."""
     tau = np.asarray(tau, dtype=np.int64)
     c = np.asarray(c, dtype=np.int64)
+    if bits == 3:                              # plain token-major stream
+        return 3 * (tau * Dv + c)
     n_tiles = Dv // 16
     per_chunk = 16 // bits                     # tiles whose codes share one chunk
     field = Dv * bits // 8                     # bits per (octet, column, token pair)
@@ -223,6 +254,11 @@ def pack_value_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     for row in range(flat.shape[0]):
         # disjoint fields: adding each code at its position is the same as OR-ing it in
         np.add.at(words[row], pos // 32, flat[row] << (pos % 32).astype(np.uint64))
+    # a 3-bit code may straddle two words: its bits past 31 belong to the next word
+    carry = words >> np.uint64(32)
+    words &= np.uint64(0xFFFFFFFF)
+    words[:, 1:] += carry[:, :-1]
+    assert not carry[:, -1].any()
     return words.astype(np.uint32).reshape(lead + (Dv * bits,))
 
 
@@ -232,6 +268,9 @@ def unpack_value_codes(words: np.ndarray, bits: int) -> np.ndarray:
     Dv = w.shape[-1] // bits
     tau, ch = np.meshgrid(np.arange(GROUP), np.arange(Dv), indexing="ij")
     pos = value_bit_position(tau, ch, Dv, bits)
+    # each word joined with the next one (zero past the end): a 3-bit code may straddle two
+    nxt = np.concatenate([w[..., 1:], np.zeros(w.shape[:-1] + (1,), np.uint64)], axis=-1)
+    w = w | (nxt << np.uint64(32))
     codes = (w[..., pos // 32] >> (pos % 32).astype(np.uint64)) & np.uint64(2 ** bits - 1)
     return codes.astype(np.uint8)
 

@@ -17,14 +17,14 @@ grouping is pinned against:
 import numpy as np
 import pytest
 
-from oracle import dequant_slab, pack_slab, unpack_value_codes
+from oracle import dequant_slab, pack_slab, unpack_codes, unpack_value_codes
 
 
 def _v_rows(rng, T, Dv):
     return (rng.standard_normal((T, Dv)) * 0.5).astype(np.float32)
 
 
-@pytest.mark.parametrize("vb", [2, 4, 8])
+@pytest.mark.parametrize("vb", [2, 3, 4, 8])
 def test_whole_row_group_closed_form(vb):
     rng = np.random.default_rng(31)
     T, Dk, Dv = 64, 32, 128
@@ -97,7 +97,7 @@ def _k_rows(rng, T, Dk):
     return (rng.standard_normal((T, Dk)) * 2 + 1).astype(np.float32)
 
 
-@pytest.mark.parametrize("kb", [2, 4, 8])
+@pytest.mark.parametrize("kb", [2, 3, 4, 8])
 def test_whole_cache_key_group_closed_form(kb):
     rng = np.random.default_rng(41)
     T, Dk, Dv = 128, 64, 32
@@ -207,3 +207,66 @@ def test_one_bit_pack_slab_round_trip():
     Khat, Vhat = dequant_slab(p, 1, 1)
     ks = np.repeat(p["k_scale"].view(np.float16).astype(np.float64), 32, axis=0)
     assert np.all(np.abs(Khat[:64] - K[:64]) <= 0.5 * ks + 1e-2)
+
+
+# ------------------------------------------------------------------- 3-bit codes
+# 32 is not a multiple of 3, so 3-bit codes are plain little-endian bit streams and a
+# code may straddle two words: key row bit 3c holds channel c; a value group's stream
+# holds (token tau, channel c) at bit 3 (tau Dv + c).  Pinned against streams built
+# as one Python integer per row (sum of code << position), cut into 32-bit words.
+
+def _words_of_int(v, n_words):
+    return np.array([(v >> (32 * k)) & 0xFFFFFFFF for k in range(n_words)], dtype=np.uint32)
+
+
+@pytest.mark.parametrize("n", [32, 96, 128, 256])
+def test_three_bit_key_rows_are_bit_streams(n):
+    from oracle import pack_codes, unpack_codes
+    rng = np.random.default_rng(60 + n)
+    codes = rng.integers(0, 8, size=(5, n), dtype=np.uint8)
+    codes[0, 10] = 7                                  # bits 30..32: straddles words 0 and 1
+    words = pack_codes(codes, 3)
+    assert words.shape == (5, 3 * n // 32)
+    for r in range(5):
+        v = sum(int(c) << (3 * k) for k, c in enumerate(codes[r]))
+        assert np.array_equal(words[r], _words_of_int(v, 3 * n // 32))
+    assert (words[0, 0] >> 30) & 3 == 3 and words[0, 1] & 1 == 1
+    assert np.array_equal(unpack_codes(words, 3), codes)
+
+
+@pytest.mark.parametrize("Dv", [32, 96, 128])
+def test_three_bit_value_stream(Dv):
+    from oracle import pack_value_codes, unpack_value_codes, value_bit_position
+    tau, c = np.meshgrid(np.arange(32), np.arange(Dv), indexing="ij")
+    pos = value_bit_position(tau, c, Dv, 3)
+    assert np.array_equal(np.sort(pos.ravel()), np.arange(0, 96 * Dv, 3))   # token-major, no gaps
+    assert value_bit_position(1, 2, Dv, 3) == 3 * (Dv + 2)
+    rng = np.random.default_rng(70 + Dv)
+    codes = rng.integers(0, 8, size=(2, 32, Dv), dtype=np.uint8)
+    words = pack_value_codes(codes, 3)
+    assert words.shape == (2, 3 * Dv)
+    for g in range(2):
+        v = sum(int(codes[g, t, ch]) << (3 * (t * Dv + ch)) for t in range(32) for ch in range(Dv))
+        assert np.array_equal(words[g], _words_of_int(v, 3 * Dv))
+    assert np.array_equal(unpack_value_codes(words, 3), codes)
+
+
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (96, 64)])
+def test_three_bit_pack_slab_within_half_step(Dk, Dv):
+    rng = np.random.default_rng(80)
+    T = 96
+    K = (rng.standard_normal((T, Dk)) * 2 + 1).astype(np.float32)
+    V = rng.standard_normal((T, Dv)).astype(np.float32)
+    p = pack_slab(K, V, "f32", 3, 3, 32, 0)
+    assert p["k_codes"].shape == (64, 3 * Dk // 32) and p["v_codes"].shape == (2, 3 * Dv)
+    Khat, Vhat = dequant_slab(p, 3, 3)
+    ks = np.repeat(p["k_scale"].view(np.float16).astype(np.float64), 32, axis=0)
+    kz = np.repeat(p["k_zero"].view(np.float16).astype(np.float64), 32, axis=0)
+    kmin = np.repeat(K[:64].reshape(2, 32, Dk).min(axis=1).astype(np.float64), 32, axis=0)
+    assert np.all(np.abs(Khat[:64] - K[:64]) <= 0.5 * ks + np.abs(kz - kmin) + 1e-6)
+    vs = p["v_scale"].view(np.float16).astype(np.float64).transpose(0, 2, 1).reshape(64, Dv // 32)
+    vz = p["v_zero"].view(np.float16).astype(np.float64).transpose(0, 2, 1).reshape(64, Dv // 32)
+    vmin = V[:64].reshape(64, Dv // 32, 32).min(axis=2).astype(np.float64)
+    err = np.abs(Vhat[:64] - V[:64]).reshape(64, Dv // 32, 32)
+    assert np.all(err <= (0.5 * vs + np.abs(vz - vmin))[:, :, None] + 1e-6)
+    assert unpack_codes(p["k_codes"], 3).max() == 7
