@@ -50,6 +50,10 @@
  *   v_zero   fp16   [B, Hkv, n_groups, Dv/v_group, 32]
  *   k_fp16   fp16   [B, Hkv, R, Dk]   retained positions, ascending
  *   v_fp16   fp16   [B, Hkv, R, Dv]
+ *   3-bit codes (32 is not a multiple of 3; the bit sweep of Quantize What Counts,
+ *   results) use plain little-endian bit streams instead, and a code may straddle
+ *   two words: key row bits [3c, 3c+3) hold channel c, and the value stream of a
+ *   group holds compacted token 32g + tau, channel c at bits 3*(tau*Dv + c) .. +3.
  *
  * Threading and ownership: the library allocates no device memory, keeps no
  * state between calls (apart from the thread-local last-error text), never
@@ -88,7 +92,7 @@ enum { KVQ_GROUP = 32, KVQ_MAX_HEAD_DIM = 256, KVQ_MAX_GQA = 16, KVQ_NUM_CACHE_B
  * read-only afterwards (calls re-derive and check R, Tq, n_groups). */
 typedef struct {
   int32_t B, Hq, Hkv, Dk, Dv, T;
-  int32_t k_bits, v_bits;         /* each in {1, 2, 4, 8} (1-bit caches decode on the vector-ALU kernel) */
+  int32_t k_bits, v_bits;         /* each in {1, 2, 3, 4, 8} (1- and 3-bit caches decode on the vector-ALU kernel) */
   int32_t n_recent;               /* newest positions kept in fp16 (0..T; T = no quantization) */
   int32_t log_window;             /* W of the log-spaced fp16 positions; 0 = none */
   int32_t k_group;                /* tokens per key group: 32, 64 or 128 (Tq a multiple of it) */
@@ -107,7 +111,7 @@ typedef struct {
 /* Fill *L and derive R, Tq, n_groups.  Limits (else KVQ_ERR_INVALID, or
  * KVQ_ERR_UNSUPPORTED where the request is well-formed): all sizes >= 1,
  * Hq % Hkv == 0 with Hq / Hkv <= KVQ_MAX_GQA, Dk and Dv multiples of 32 up to
- * KVQ_MAX_HEAD_DIM, bits in {1, 2, 4, 8}, 0 <= n_recent <= T, log_window >= 0, and
+ * KVQ_MAX_HEAD_DIM, bits in {1, 2, 3, 4, 8}, 0 <= n_recent <= T, log_window >= 0, and
  * the quantized token count Tq a multiple of 32 (choose n_recent accordingly). */
 int kvq_layout_init(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T,
                     int k_bits, int v_bits, int n_recent, int log_window);

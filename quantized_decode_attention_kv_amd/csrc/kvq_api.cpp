@@ -74,7 +74,7 @@ int kvq::check_format(const kvq_layout& l) {
   if (L->Dk > KVQ_MAX_HEAD_DIM || L->Dv > KVQ_MAX_HEAD_DIM)
     return fail(KVQ_ERR_UNSUPPORTED, "Dk (%d) and Dv (%d) must be <= %d", L->Dk, L->Dv, KVQ_MAX_HEAD_DIM);
   if (!valid_bits(L->k_bits) || !valid_bits(L->v_bits))
-    return fail(KVQ_ERR_UNSUPPORTED, "k_bits (%d) and v_bits (%d) must be 1, 2, 4 or 8", L->k_bits, L->v_bits);
+    return fail(KVQ_ERR_UNSUPPORTED, "k_bits (%d) and v_bits (%d) must be 1, 2, 3, 4 or 8", L->k_bits, L->v_bits);
   if (L->n_recent < 0 || L->n_recent > L->T)
     return fail(KVQ_ERR_INVALID, "n_recent (%d) must be in [0, T=%d]", L->n_recent, L->T);
   if (L->log_window < 0) return fail(KVQ_ERR_INVALID, "log_window (%d) must be >= 0", L->log_window);

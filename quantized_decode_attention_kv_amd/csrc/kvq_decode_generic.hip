@@ -176,7 +176,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
       // channels [hf Dk / 2, (hf + 1) Dk / 2) in ascending order (a half may start
       // inside a word: at 1 bit a 32-channel row is one word)
       const int c_end = (hf + 1) * (Dk / 2);
-      for (int c = hf * (Dk / 2); c < c_end;) {
+      if (kb == 3) {  // a bit stream: a code may straddle two words
+        for (int c = hf * (Dk / 2); c < c_end; ++c) {
+          const float cf = float(stream_code(row, 3 * c, 3));
+          const float* kqc = kq + c * G;
+#pragma unroll
+          for (int i = 0; i < G; ++i) acc[i] = fmaf(kqc[i], cf, acc[i]);
+        }
+      }
+      for (int c = kb == 3 ? c_end : hf * (Dk / 2); c < c_end;) {
         const int w = c / kper;
         const uint32_t word = row[w];
         const int w_end = min(c_end, (w + 1) * kper);
@@ -218,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
           const int c = lane + 64 * j;
           if (c < Dv) {
             const int bit = value_bit_position(tt, c, Dv, vb);
-            const float cf = float((vc[bit >> 5] >> (bit & 31)) & vmask);
+            const float cf = float(vb == 3 ? stream_code(vc, bit, 3) : (vc[bit >> 5] >> (bit & 31)) & vmask);
             const float* ppt = pp + (tt * ngv + c / vg) * G;
 #pragma unroll
             for (int i = 0; i < G; ++i) st.o[i][j] = fmaf(ppt[i], cf, st.o[i][j]);

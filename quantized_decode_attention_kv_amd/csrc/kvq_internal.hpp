@@ -88,7 +88,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t aft
 // entry points (kvq_stream.cpp).
 int fail(int status, const char* fmt, ...);  // sets the thread's last-error text, returns status
 int ok();                                     // clears it, returns KVQ_OK
-inline bool valid_bits(int b) { return b == 1 || b == 2 || b == 4 || b == 8; }
+inline bool valid_bits(int b) { return b == 1 || b == 2 || b == 3 || b == 4 || b == 8; }
 inline bool valid_gqa(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 inline bool valid_dtype(int d) { return d == KVQ_F32 || d == KVQ_F16 || d == KVQ_BF16; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -196,6 +196,17 @@ __device__ __forceinline__ float row16_reduce(float v) {
   return v;
 }
 
+// OR a B-bit code into LDS words at stream bit `bit`; a 3-bit code may straddle
+// into the next word (other widths never do)
+template <int B>
+__device__ __forceinline__ void or_code(uint32_t* w, int bit, uint32_t code) {
+  const int sh = bit & 31;
+  atomicOr(&w[bit >> 5], code << sh);
+  if constexpr (B == 3) {
+    if (sh > 32 - B) atomicOr(&w[(bit >> 5) + 1], code >> (32 - sh));
+  }
+}
+
 template <int DT, int KB, int VB>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
   __shared__ int32_t row_s[KVQ_GROUP];
@@ -231,13 +242,13 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
     for (int t = 0; t < 8; ++t) rows[t] = row_of(8 * wave + t);
     // Dv == 128: thread (token tid / 8, 16-channel tile tid % 8) takes its value
     // row segment now, so that its load latency overlaps the key phase
-    const bool v128 = Dv == 128 && VB >= 2;  // 1-bit values take the generic path
+    const bool v128 = Dv == 128 && VB >= 2 && VB != 3;  // 1- and 3-bit values take the generic path
     const int vtok = tid >> 3, vtile = tid & 7;
     Raw16<DT> vraw;
     if (v128) vraw = load16<DT>(a.V, (slab * a.t_count + row_of(vtok)) * 128 + 16 * vtile);
 
     // (4- and 8-bit key words are written byte by byte below, every byte once)
-    if constexpr (KB <= 2) {
+    if constexpr (KB <= 3) {
       for (int i = tid; i < KVQ_GROUP * kwords; i += kPackThreads) kw_s[i] = 0u;
     }
     for (int i = tid; i < vwords; i += kPackThreads) vw_s[i] = 0u;
@@ -294,7 +305,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
     }
     __syncthreads();
     {
-      // key words: row t, word c / (32/KB), channel c at bit (c % (32/KB)) * KB;
+      // key words: row t, word c / (32/KB), channel c at bit (c % (32/KB)) * KB
+      // (3 bits: channel c at bit 3c of the row's bit stream);
       // the lane's two channels are adjacent fields of one word
       constexpr int per = 32 / KB;
 #pragma unroll
@@ -309,7 +321,12 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
             const uint32_t c0 = quant_code(kx[k][t].x, s0, z0, r0, k_levels);
             const uint32_t c1 = quant_code(kx[k][t].y, s1, z1, r1, k_levels);
             const uint32_t f = c0 | (c1 << KB);
-            if constexpr (KB <= 2) {
+            if constexpr (KB == 3) {
+              // a bit stream: channel c at bit 3c of the row
+              uint32_t* kr = kw_s + (8 * wave + t) * kwords;
+              or_code<3>(kr, 6 * cp, c0);
+              or_code<3>(kr, 6 * cp + 3, c1);
+            } else if constexpr (KB <= 2) {
               atomicOr(&kw_s[(8 * wave + t) * kwords + word], f << bit);
             } else {
               // the lane's two fields fill one byte (4 bits) or two (8 bits) of the
@@ -390,8 +407,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
             const uint32_t c0 = quant_code(x.x, q.s, q.z, q.r, v_levels);
             const uint32_t c1 = quant_code(x.y, q.s, q.z, q.r, v_levels);
             const int p0 = value_bit_position(tok, 2 * cp, Dv, VB), p1 = value_bit_position(tok, 2 * cp + 1, Dv, VB);
-            atomicOr(&vw_s[p0 >> 5], c0 << (p0 & 31));
-            atomicOr(&vw_s[p1 >> 5], c1 << (p1 & 31));
+            or_code<VB>(vw_s, p0, c0);
+            or_code<VB>(vw_s, p1, c1);
           }
         }
       }
@@ -487,6 +504,8 @@ hipError_t launch_dt(const PackArgs& a, dim3 grid, hipStream_t stream) {
   KVQ_PACK_CASE(2, 1) KVQ_PACK_CASE(2, 2) KVQ_PACK_CASE(2, 4) KVQ_PACK_CASE(2, 8)
   KVQ_PACK_CASE(4, 1) KVQ_PACK_CASE(4, 2) KVQ_PACK_CASE(4, 4) KVQ_PACK_CASE(4, 8)
   KVQ_PACK_CASE(8, 1) KVQ_PACK_CASE(8, 2) KVQ_PACK_CASE(8, 4) KVQ_PACK_CASE(8, 8)
+  KVQ_PACK_CASE(3, 1) KVQ_PACK_CASE(3, 2) KVQ_PACK_CASE(3, 3) KVQ_PACK_CASE(3, 4) KVQ_PACK_CASE(3, 8)
+  KVQ_PACK_CASE(1, 3) KVQ_PACK_CASE(2, 3) KVQ_PACK_CASE(4, 3) KVQ_PACK_CASE(8, 3)
 #undef KVQ_PACK_CASE
   return hipErrorInvalidValue;
 }

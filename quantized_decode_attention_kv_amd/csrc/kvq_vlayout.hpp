@@ -14,6 +14,11 @@
 // 16-bit lanes holding code * 2^(k*vb): two fp16 subnormals, one per token.
 //
 // Codes never straddle a word: every field and chunk starts at a multiple of vb.
+//
+// 3-bit codes (32 is not a multiple of 3) use a plain token-major stream instead:
+// token tau, channel c at bit 3*(tau*Dv + c), so a code may straddle two words
+// (stream_code reads it).  Key rows of 3-bit codes are streams too: channel c at
+// bit 3c of the row.
 #pragma once
 
 #include <stdint.h>
@@ -27,6 +32,7 @@ struct ValueCodeSpot {
 
 // bit offset of (token tau of the group, channel c) in the group's stream
 __host__ __device__ inline int value_bit_position(int tau, int c, int Dv, int vb) {
+  if (vb == 3) return 3 * (tau * Dv + c);
   const int n_tiles = Dv / 16, per_chunk = 16 / vb, field = Dv * vb / 8;
   const int octet = tau >> 3, j = tau & 7;
   const int tile = c >> 4, col = c & 15;
@@ -37,6 +43,7 @@ __host__ __device__ inline int value_bit_position(int tau, int c, int Dv, int vb
 
 // inverse: which (token, channel) code sits at stream bit `bit` (a multiple of vb)
 __host__ __device__ inline ValueCodeSpot value_code_at(int bit, int Dv, int vb) {
+  if (vb == 3) return ValueCodeSpot{bit / 3 / Dv, bit / 3 % Dv};
   const int n_tiles = Dv / 16, per_chunk = 16 / vb, field = Dv * vb / 8;
   const int f = bit / field, within = bit - f * field;
   const int octet = f >> 6, col = (f >> 2) & 15, pair = f & 3;
@@ -45,6 +52,15 @@ __host__ __device__ inline ValueCodeSpot value_code_at(int bit, int Dv, int vb) 
   const int upper = inner / (in_chunk * vb);
   const int slot = (inner - upper * in_chunk * vb) / vb;
   return ValueCodeSpot{octet * 8 + pair + 4 * upper, (chunk * per_chunk + slot) * 16 + col};
+}
+
+// the vb-bit code at stream bit `bit` of little-endian words w (the next word is
+// read only when the code straddles into it, which only 3-bit codes do)
+__host__ __device__ inline uint32_t stream_code(const uint32_t* w, int bit, int vb) {
+  const int sh = bit & 31;
+  uint32_t v = w[bit >> 5] >> sh;
+  if (sh + vb > 32) v |= w[(bit >> 5) + 1] << (32 - sh);
+  return v & ((1u << vb) - 1u);
 }
 
 }  // namespace kvq

@@ -105,6 +105,13 @@ def small_cases():
                  n_recent=64, log_window=64, dtype="bf16", partitions=3, seed=21, k_group=64, v_group=64),
         Workload("small_g2_k8v4_kg64_f32", B=1, Hq=4, Hkv=2, Dk=96, Dv=64, T=416, k_bits=8, v_bits=4,
                  n_recent=32, dtype="f32", partitions=4, seed=22, k_group=64),
+        # 3-bit codes (bit streams, codes straddle words; vector-ALU decode kernel)
+        Workload("small_k3v3", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=1064, k_bits=3, v_bits=3,
+                 n_recent=40, dtype="bf16", partitions=5, seed=26),
+        Workload("small_k3v2_kg64_log", B=1, Hq=4, Hkv=1, Dk=96, Dv=128, T=1487, k_bits=3, v_bits=2,
+                 n_recent=64, log_window=64, dtype="bf16", partitions=3, seed=27, k_group=64),
+        Workload("small_g2_k4v3_vg64_f32", B=1, Hq=4, Hkv=2, Dk=64, Dv=64, T=352, k_bits=4, v_bits=3,
+                 n_recent=32, dtype="f32", partitions=4, seed=28, v_group=64),
         # 1-bit codes (vector-ALU decode kernel)
         Workload("small_k1v1", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=544, k_bits=1, v_bits=1,
                  n_recent=32, dtype="bf16", partitions=3, seed=23),
