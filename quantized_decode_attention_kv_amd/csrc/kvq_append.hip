@@ -62,9 +62,19 @@ __device__ inline uint32_t quant_code(float x, const Quant& q, float levels) {
   return uint32_t(fminf(fmaxf(t, 0.0f), levels));
 }
 
+// OR a 3-bit code into LDS words at stream bit `bit`, into the next word too when
+// it straddles
+__device__ __forceinline__ void or_code3(uint32_t* w, int bit, uint32_t code) {
+  const int sh = bit & 31;
+  atomicOr(&w[bit >> 5], code << sh);
+  if (sh > 29) atomicOr(&w[(bit >> 5) + 1], code >> (32 - sh));
+}
+
 template <int KB, int VB>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   __shared__ uint32_t vw[KVQ_MAX_HEAD_DIM * VB];             // value code words of the group
+  // 3-bit key rows are bit streams whose codes may straddle words: built in LDS
+  __shared__ uint32_t kw3[KB == 3 ? KVQ_GROUP * KVQ_MAX_HEAD_DIM * 3 / 32 : 1];
   __shared__ float kmn[kSlices][KVQ_MAX_HEAD_DIM], kmx[kSlices][KVQ_MAX_HEAD_DIM];
   __shared__ float vmn[KVQ_GROUP][KVQ_MAX_HEAD_DIM / 32], vmx[KVQ_GROUP][KVQ_MAX_HEAD_DIM / 32];
   const int64_t slab = blockIdx.x;
@@ -83,6 +93,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
 
   // 2. the group
   for (int i = tid; i < Dv * VB; i += kAppendThreads) vw[i] = 0u;
+  if constexpr (KB == 3) {
+    for (int i = tid; i < KVQ_GROUP * Dk * 3 / 32; i += kAppendThreads) kw3[i] = 0u;
+  }
   const int64_t gi = slab * a.g_stride + a.group;
   auto k_row = [&](int j, int c) {
     const int row = a.member_rows[j];
@@ -136,10 +149,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        uint32_t w = quant_code(kx[pass][k], q, klev) << ((c % per) * KB);
+        if constexpr (KB == 3) {
+          or_code3(kw3 + (4 * sl + k) * kwords, 3 * c, quant_code(kx[pass][k], q, klev));
+        } else {
+          uint32_t w = quant_code(kx[pass][k], q, klev) << ((c % per) * KB);
 #pragma unroll
-        for (int o = 1; o < per; o <<= 1) w |= uint32_t(__shfl_xor(int(w), o));
-        if (c % per == 0) kc[(4 * sl + k) * kwords + c / per] = w;
+          for (int o = 1; o < per; o <<= 1) w |= uint32_t(__shfl_xor(int(w), o));
+          if (c % per == 0) kc[(4 * sl + k) * kwords + c / per] = w;
+        }
       }
     }
   }
@@ -184,12 +201,18 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         static_cast<uint16_t*>(a.cache.v_zero)[si] = q.zb;
       }
       const int bit = value_bit_position(j, c, Dv, VB);
-      atomicOr(&vw[bit >> 5], quant_code(vx[i], q, vlev) << (bit & 31));
+      if constexpr (VB == 3)
+        or_code3(vw, bit, quant_code(vx[i], q, vlev));
+      else
+        atomicOr(&vw[bit >> 5], quant_code(vx[i], q, vlev) << (bit & 31));
     }
   }
   __syncthreads();  // the group's rows have been read and its value words are complete
   uint32_t* vc = static_cast<uint32_t*>(a.cache.v_codes) + gi * (Dv * VB);
   for (int i = tid; i < Dv * VB; i += kAppendThreads) vc[i] = vw[i];
+  if constexpr (KB == 3) {
+    for (int i = tid; i < KVQ_GROUP * kwords; i += kAppendThreads) kc[i] = kw3[i];
+  }
 
   // 3. moves: sources lie past the new end, destinations are freed rows
   for (int e = tid; e < a.n_moves * Dk; e += kAppendThreads) {
@@ -219,6 +242,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   KVQ_APPEND_CASE(2, 1) KVQ_APPEND_CASE(2, 2) KVQ_APPEND_CASE(2, 4) KVQ_APPEND_CASE(2, 8)
   KVQ_APPEND_CASE(4, 1) KVQ_APPEND_CASE(4, 2) KVQ_APPEND_CASE(4, 4) KVQ_APPEND_CASE(4, 8)
   KVQ_APPEND_CASE(8, 1) KVQ_APPEND_CASE(8, 2) KVQ_APPEND_CASE(8, 4) KVQ_APPEND_CASE(8, 8)
+  KVQ_APPEND_CASE(3, 1) KVQ_APPEND_CASE(3, 2) KVQ_APPEND_CASE(3, 3) KVQ_APPEND_CASE(3, 4) KVQ_APPEND_CASE(3, 8)
+  KVQ_APPEND_CASE(1, 3) KVQ_APPEND_CASE(2, 3) KVQ_APPEND_CASE(4, 3) KVQ_APPEND_CASE(8, 3)
 #undef KVQ_APPEND_CASE
   return hipErrorInvalidValue;
 }

@@ -41,9 +41,6 @@ int check_stream(const kvq_stream* S) {
   const int st = kvq::check_format(L);
   if (st != KVQ_OK) return st;
   if (L.k_group != KVQ_GROUP) return fail(KVQ_ERR_UNSUPPORTED, "stream key groups are %d tokens", KVQ_GROUP);
-  if (L.k_bits == 3 || L.v_bits == 3)
-    return fail(KVQ_ERR_UNSUPPORTED, "streams take 1-, 2-, 4- or 8-bit codes (k_bits %d, v_bits %d)", L.k_bits,
-                L.v_bits);
   if (L.log_window > 0 && L.n_recent < L.log_window)
     return fail(KVQ_ERR_UNSUPPORTED, "a stream needs log_window == 0 or n_recent (%d) >= log_window (%d)",
                 L.n_recent, L.log_window);
@@ -159,8 +156,6 @@ int kvq_stream_init_ex(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, in
   l.v_group = v_group;
   int st = kvq::check_format(l);
   if (st != KVQ_OK) return st;
-  if (k_bits == 3 || v_bits == 3)
-    return fail(KVQ_ERR_UNSUPPORTED, "streams take 1-, 2-, 4- or 8-bit codes (k_bits %d, v_bits %d)", k_bits, v_bits);
   if (log_window > 0 && n_recent < log_window)
     return fail(KVQ_ERR_UNSUPPORTED, "a stream needs log_window == 0 or n_recent (%d) >= log_window (%d)",
                 n_recent, log_window);

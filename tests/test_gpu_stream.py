@@ -168,6 +168,22 @@ def test_stream_one_bit():
     _run_stream(w, 0, 200, {9, 40, 41, 104, 160}, [1, 2])
 
 
+def test_stream_three_bit():
+    """3-bit keys and values in a stream (bit streams with straddling codes; Dk = 96
+    gives 9-word key rows)."""
+    w = Workload("stream_k3v3", B=1, Hq=4, Hkv=2, Dk=96, Dv=128, T=300, k_bits=3, v_bits=3,
+                 n_recent=8, dtype="bf16", seed=29)
+    _run_stream(w, 0, 200, {9, 40, 41, 104, 160}, [1, 2])
+
+
+def test_stream_three_bit_values_log_after_prefill():
+    """K2V3 with 64-channel value groups and log-spaced fp16 tokens, after a prefill."""
+    w = Workload("stream_k2v3_log_vg64", B=1, Hq=8, Hkv=2, Dk=128, Dv=128, T=1400, k_bits=2, v_bits=3,
+                 n_recent=64, log_window=64, dtype="f32", seed=30, v_group=64)
+    T0 = _valid_prefill(w, 900)
+    _run_stream(w, T0, T0 + 300, {T0 + 1, T0 + 64, T0 + 299}, [1, 3])
+
+
 def test_stream_full_capacity_and_errors():
     """A stream filled to its capacity refuses another token and keeps its state."""
     w = Workload("stream_full", B=1, Hq=4, Hkv=1, Dk=64, Dv=64, T=96, k_bits=4, v_bits=4,

@@ -50,7 +50,7 @@ def test_planner_errors():
         q.Stream(1, 4, 1, 32, 32, 100000, 4, 2, n_recent=5000, log_window=0, device=None)
     assert e.value.status == L_.KVQ_ERR_UNSUPPORTED   # more fp16 rows than the state can track
     with pytest.raises(q.KvqError) as e:
-        q.Stream(1, 4, 1, 32, 32, 100, 3, 2, n_recent=4, device=None)
+        q.Stream(1, 4, 1, 32, 32, 100, 5, 2, n_recent=4, device=None)
     assert e.value.status == L_.KVQ_ERR_UNSUPPORTED
     s = q.Stream(1, 4, 1, 32, 32, 3, 4, 2, n_recent=3, device=None)
     for _ in range(3):

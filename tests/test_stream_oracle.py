@@ -97,7 +97,7 @@ def test_groups_replayed_from_closed_form(n_recent, W, T):
         assert most_waiting > 32
 
 
-@pytest.mark.parametrize("kb,vb,n_recent", [(4, 2, 16), (2, 2, 0), (8, 4, 40)])
+@pytest.mark.parametrize("kb,vb,n_recent", [(4, 2, 16), (2, 2, 0), (8, 4, 40), (3, 3, 8)])
 def test_stream_equals_one_shot_without_log_window(kb, vb, n_recent):
     rng = np.random.default_rng(13)
     Dk, Dv = 64, 128
