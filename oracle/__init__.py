@@ -24,3 +24,10 @@ from .kvq_oracle import (  # noqa: F401
     upcast,
 )
 from .kvq_stream import SlabStream  # noqa: F401
+from .kvq_headq import (  # noqa: F401
+    corrected_keys,
+    decode_slab_headq,
+    headq_side_slab,
+    project_residual,
+    side_code,
+)
