@@ -309,6 +309,36 @@ int kv_stream_decode(const kvq_stream* S, const void* q, int q_dtype, const kvq_
  * KVQ_ERR_INVALID for a NULL or misaligned pointer, KVQ_ERR_HIP for a failed
  * launch.
  */
+/* ---- HeadQ side code ("HeadQ", section 3, methodology): write and read mechanics.
+ * Write: for every quantized token j of a packed cache, e_j = k_j - k_hat_j (k_hat_j
+ * from the cache's codes, scales and zeros), y_j = U_h^T e_j (summed in float64 over
+ * channels in ascending order, rounded once to float32), and the r coefficients of
+ * y_j quantized as one group with side_bits bits under the quantizer contract above.
+ * Read: decode adds (U_h^T q) . z_hat_j, in the scores' units, to each quantized
+ * token's score; fp16-retained tokens get no correction.  U is caller-supplied
+ * (the page learns it by PCA on calibration queries): float32 [Hkv, Dk, rank],
+ * 1 <= rank <= min(Dk, 16).  Buffers (caller-allocated, sizes from kvq_side_sizes):
+ *   codes uint8 [B, Hkv, Tq, rank] (one code per byte), scale / zero fp16 [B, Hkv, Tq].
+ * Only caches packed with kvq_layout_init(_ex) (not streams).  Decode with a side
+ * code runs on the vector-ALU kernel. */
+typedef struct {
+  void *codes, *scale, *zero;
+} kvq_side;
+
+/* Byte sizes of the three side buffers (codes, scale, zero). */
+int kvq_side_sizes(const kvq_layout* L, int rank, size_t bytes_out[3]);
+
+/* Write the side code of every quantized token.  K: the same [B, Hkv, T, Dk] keys the
+ * cache was packed from (device, kv_dtype); cache: a packed cache (k_codes, k_scale,
+ * k_zero are read); side_bits in {2, 4, 8}.  Enqueued on `stream`. */
+int kv_side_pack(const kvq_layout* L, int rank, int side_bits, const float* U, const void* K, int kv_dtype,
+                 const kvq_cache* cache, const kvq_side* side, void* stream);
+
+/* kv_decode_attn with the HeadQ logit correction of `side` (same arguments otherwise). */
+int kv_decode_attn_side(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache, int rank,
+                        const float* U, const kvq_side* side, float softmax_scale, int num_partitions,
+                        void* workspace, size_t workspace_bytes, float* out, void* stream);
+
 int kvq_read_probe(const void* buf, size_t bytes, void* sink, void* stream);
 
 /* Static text for a status code. */

@@ -22,7 +22,11 @@ EXPORTS = ["kvq_layout_init", "kvq_cache_sizes", "kvq_retained_positions", "kvq_
            "kvq_last_error", "kvq_read_probe", "kvq_layout_init_ex", "kvq_stream_init", "kvq_stream_init_ex",
            "kvq_stream_cache_sizes",
            "kvq_stream_workspace_bytes", "kvq_stream_plan", "kv_stream_prefill", "kv_stream_append",
-           "kv_stream_decode"]
+           "kv_stream_decode", "kvq_side_sizes", "kv_side_pack", "kv_decode_attn_side"]
+
+
+class KvqSide(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("zero", ctypes.c_void_p)]
 
 
 class KvqLayout(ctypes.Structure):
@@ -83,6 +87,13 @@ def load() -> ctypes.CDLL:
     lib.kv_decode_attn.restype = c_int
     lib.kv_decode_attn_ex.argtypes = [LP, vp, c_int, CP, ctypes.c_float, c_int, vp, c_sz, vp, vp, vp]
     lib.kv_decode_attn_ex.restype = c_int
+    SDP = ctypes.POINTER(KvqSide)
+    lib.kvq_side_sizes.argtypes = [LP, c_int, ctypes.POINTER(c_sz)]
+    lib.kvq_side_sizes.restype = c_int
+    lib.kv_side_pack.argtypes = [LP, c_int, c_int, vp, vp, c_int, CP, SDP, vp]
+    lib.kv_side_pack.restype = c_int
+    lib.kv_decode_attn_side.argtypes = [LP, vp, c_int, CP, c_int, vp, SDP, ctypes.c_float, c_int, vp, c_sz, vp, vp]
+    lib.kv_decode_attn_side.restype = c_int
     lib.kvq_read_probe.argtypes = [vp, c_sz, vp, vp]
     lib.kvq_read_probe.restype = c_int
     SP = ctypes.POINTER(KvqStream)

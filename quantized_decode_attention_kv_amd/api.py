@@ -293,3 +293,46 @@ class Stream:
                                             ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(out.data_ptr()),
                                             _stream(stream)))
         return out
+
+
+# ------------------------------------------------------------ HeadQ side code
+def side_pack(layout: Layout, K, cache, U, side_bits: int = 8, stream=None):
+    """HeadQ write path over a packed cache: side code of every quantized token.
+    K: the [B, Hkv, T, Dk] keys the cache was packed from; U float32 [Hkv, Dk, r].
+    Returns (codes uint8 [B, Hkv, Tq, r], scale, zero int16 fp16 bits [B, Hkv, Tq])."""
+    _check_tensor("K", K, (layout.B, layout.Hkv, layout.T, layout.Dk))
+    if U.dtype != torch.float32 or not U.is_cuda or not U.is_contiguous() or U.dim() != 3 \
+            or tuple(U.shape[:2]) != (layout.Hkv, layout.Dk):
+        raise ValueError("U must be a contiguous float32 CUDA tensor [Hkv, Dk, r]")
+    r = U.shape[2]
+    Tq = layout.Tq
+    codes = torch.empty((layout.B, layout.Hkv, Tq, r), dtype=torch.uint8, device=K.device)
+    scale = torch.empty((layout.B, layout.Hkv, Tq), dtype=torch.int16, device=K.device)
+    zero = torch.empty_like(scale)
+    side = L_.KvqSide(codes.data_ptr(), scale.data_ptr(), zero.data_ptr())
+    cs = _cache_struct(layout, cache)
+    L_.check(L_.load().kv_side_pack(layout.ref, r, side_bits, ctypes.c_void_p(U.data_ptr()),
+                                    ctypes.c_void_p(K.data_ptr()), _DTYPE_CODES[K.dtype], ctypes.byref(cs),
+                                    ctypes.byref(side), _stream(stream)))
+    return codes, scale, zero
+
+
+def kv_decode_attn_side(layout: Layout, q, cache, U, side, num_partitions: int = 1, softmax_scale=None,
+                        stream=None):
+    """kv_decode_attn with the HeadQ logit correction of ``side`` (from side_pack)."""
+    _check_tensor("q", q, (layout.B, layout.Hq, layout.Dk))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(layout.Dk)
+    out = torch.empty((layout.B, layout.Hq, layout.Dv), dtype=torch.float32, device=q.device)
+    need = layout.workspace_bytes(num_partitions)
+    workspace = alloc_workspace(layout, num_partitions, q.device) if need else None
+    codes, scale, zero = side
+    sd = L_.KvqSide(codes.data_ptr(), scale.data_ptr(), zero.data_ptr())
+    cs = _cache_struct(layout, cache)
+    L_.check(L_.load().kv_decode_attn_side(
+        layout.ref, ctypes.c_void_p(q.data_ptr()), _DTYPE_CODES[q.dtype], ctypes.byref(cs), U.shape[2],
+        ctypes.c_void_p(U.data_ptr()), ctypes.byref(sd), ctypes.c_float(softmax_scale), num_partitions,
+        ctypes.c_void_p(workspace.data_ptr() if workspace is not None else None),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+    return out

@@ -102,7 +102,8 @@ int kvq::check_cache_ptr(const void* p, const char* name) {
 // n_groups) give the token counts and g_stride / r_stride the slab strides.
 int kvq::decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, const void* q, int q_dtype,
                      const kvq_cache* cache, float softmax_scale, int num_partitions, void* workspace,
-                     size_t workspace_bytes, float* out, void* stream, void* event_after_decode) {
+                     size_t workspace_bytes, float* out, void* stream, void* event_after_decode,
+                     const DecodeArgs* side) {
   int st;
   if (!cache) return fail(KVQ_ERR_INVALID, "cache is NULL");
   if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID, "q_dtype %d is not KVQ_F32/F16/BF16", q_dtype);
@@ -144,6 +145,13 @@ int kvq::decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, co
     a.partials = static_cast<float*>(workspace);
   }
   a.out = out;
+  if (side) {
+    a.side_u = side->side_u;
+    a.side_codes = side->side_codes;
+    a.side_scale = side->side_scale;
+    a.side_zero = side->side_zero;
+    a.side_rank = side->side_rank;
+  }
   const hipError_t e =
       kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(event_after_decode));
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
@@ -300,6 +308,77 @@ int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq
   if (st != KVQ_OK) return st;
   return kvq::decode_view(*L, L->n_groups, L->R, q, q_dtype, cache, softmax_scale, num_partitions, workspace,
                           workspace_bytes, out, stream, event_after_decode);
+}
+
+// ------------------------------------------------------------ HeadQ side code
+namespace {
+int check_side(const kvq_layout* L, int rank, const float* U, const kvq_side* side) {
+  if (rank < 1 || rank > kvq::kMaxSideRank || rank > L->Dk)
+    return fail(KVQ_ERR_UNSUPPORTED, "side rank %d must be in [1, min(Dk, %d)]", rank, kvq::kMaxSideRank);
+  if (!U || !side) return fail(KVQ_ERR_INVALID, "U or side is NULL");
+  if (L->n_groups > 0 && (!side->codes || !side->scale || !side->zero))
+    return fail(KVQ_ERR_INVALID, "side buffers must not be NULL");
+  return ok();
+}
+}  // namespace
+
+int kvq_side_sizes(const kvq_layout* L, int rank, size_t bytes_out[3]) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (!bytes_out) return fail(KVQ_ERR_INVALID, "bytes_out is NULL");
+  if (rank < 1 || rank > kvq::kMaxSideRank || rank > L->Dk)
+    return fail(KVQ_ERR_UNSUPPORTED, "side rank %d must be in [1, min(Dk, %d)]", rank, kvq::kMaxSideRank);
+  const size_t toks = size_t(L->B) * L->Hkv * L->Tq;
+  bytes_out[0] = toks * rank;  // codes, one byte each
+  bytes_out[1] = toks * 2;     // scale
+  bytes_out[2] = toks * 2;     // zero
+  return ok();
+}
+
+int kv_side_pack(const kvq_layout* L, int rank, int side_bits, const float* U, const void* K, int kv_dtype,
+                 const kvq_cache* cache, const kvq_side* side, void* stream) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if ((st = check_side(L, rank, U, side))) return st;
+  if (side_bits != 2 && side_bits != 4 && side_bits != 8)
+    return fail(KVQ_ERR_UNSUPPORTED, "side_bits %d must be 2, 4 or 8", side_bits);
+  if (!valid_dtype(kv_dtype)) return fail(KVQ_ERR_INVALID, "kv_dtype %d is not KVQ_F32/F16/BF16", kv_dtype);
+  if (!K || !cache) return fail(KVQ_ERR_INVALID, "K or cache is NULL");
+  if (L->n_groups == 0) return ok();
+  if ((st = check_cache_ptr(cache->k_codes, "k_codes")) || (st = check_cache_ptr(cache->k_scale, "k_scale")) ||
+      (st = check_cache_ptr(cache->k_zero, "k_zero")))
+    return st;
+  if (L->B > 65535 || L->Hkv > 65535) return fail(KVQ_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  kvq::SideArgs a{};
+  a.L = *L;
+  a.K = K;
+  a.dtype = kv_dtype;
+  a.cache = *cache;
+  a.U = U;
+  a.rank = rank;
+  a.bits = side_bits;
+  a.codes = static_cast<uint8_t*>(side->codes);
+  a.scale = static_cast<uint16_t*>(side->scale);
+  a.zero = static_cast<uint16_t*>(side->zero);
+  const hipError_t e = kvq::launch_side_pack(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "side pack launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kv_decode_attn_side(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache, int rank,
+                        const float* U, const kvq_side* side, float softmax_scale, int num_partitions,
+                        void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if ((st = check_side(L, rank, U, side))) return st;
+  kvq::DecodeArgs s{};
+  s.side_u = U;
+  s.side_codes = static_cast<const uint8_t*>(side->codes);
+  s.side_scale = static_cast<const uint16_t*>(side->scale);
+  s.side_zero = static_cast<const uint16_t*>(side->zero);
+  s.side_rank = rank;
+  return kvq::decode_view(*L, L->n_groups, L->R, q, q_dtype, cache, softmax_scale, num_partitions, workspace,
+                          workspace_bytes, out, stream, nullptr, &s);
 }
 
 int kvq_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {

@@ -125,6 +125,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     qs[i] = a.scale * kLog2e * load_q<QDT>(a.q, (int64_t(b) * a.L.Hq + int64_t(h) * G + qi) * Dk + c);
   }
 
+  // HeadQ side code: pr[i][k] = (U^T q_i)_k in the same scaled units as the scores
+  __shared__ float pr[KVQ_MAX_GQA * kMaxSideRank];
+  const int rank = a.side_rank;
+  if (rank > 0) {
+    __syncthreads();  // qs complete
+    for (int i = tid; i < G * rank; i += kThreads) {
+      const int qi = i / rank, k = i - qi * rank;
+      float acc = 0.0f;
+      for (int c = 0; c < Dk; ++c) acc = fmaf(qs[qi * Dk + c], a.side_u[(int64_t(h) * Dk + c) * rank + k], acc);
+      pr[i] = acc;
+    }
+  }
+
   SoftmaxState<G> st;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
@@ -198,6 +211,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
       float s[G];
 #pragma unroll
       for (int i = 0; i < G; ++i) s[i] = acc[i] + __shfl_xor(acc[i], 32, 64) + bias[i];
+      if (rank > 0) {  // logit correction (U^T q) . z_hat of this token
+        const int64_t j = (slab * a.g_stride + g) * KVQ_GROUP + t;
+        const float zs = h2f(a.side_scale[j]), zz = h2f(a.side_zero[j]);
+        for (int k = 0; k < rank; ++k) {
+          const float zh = fmaf(float(a.side_codes[j * rank + k]), zs, zz);
+#pragma unroll
+          for (int i = 0; i < G; ++i) s[i] = fmaf(pr[i * rank + k], zh, s[i]);
+        }
+      }
       softmax_update<G>(st, s, pv);
 
       // p_t s_t,g into LDS and the zero-point sums
@@ -372,7 +394,8 @@ hipError_t launch_q(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t after_decode) {
   int parts = a.P;  // partial rows per query head written by the decode kernel
-  hipError_t e = launch_decode_mfma(a, stream, &parts);
+  // the side-code correction is carried by the vector-ALU kernel only
+  hipError_t e = a.side_rank > 0 ? hipErrorNotSupported : launch_decode_mfma(a, stream, &parts);
   if (e == hipErrorNotSupported) {
     parts = a.P;
     switch (a.q_dtype) {

@@ -33,7 +33,29 @@ struct DecodeArgs {
   int ranks;           // waves per SIMD the matrix-core grid puts on the device at once (1..4)
   float* partials;     // [B * Hq, units, Dv + 4]: m (log2 domain), l, 2 unused, unnormalised o (P > 1)
   float* out;          // [B, Hq, Dv]
+  // HeadQ side code (side_rank == 0: none; the vector-ALU kernel then adds the
+  // logit correction (U^T q) . z_hat per quantized token)
+  const float* side_u;        // [Hkv, Dk, side_rank]
+  const uint8_t* side_codes;  // [B, Hkv, g_stride * 32, side_rank]
+  const uint16_t* side_scale; // [B, Hkv, g_stride * 32] fp16
+  const uint16_t* side_zero;
+  int side_rank;
 };
+
+// Side-code write of the HeadQ mechanics: one workgroup per (code group, kv head, batch)
+struct SideArgs {
+  kvq_layout L;
+  const void* K;  // [B, Hkv, T, Dk] in dtype
+  int dtype;
+  kvq_cache cache;
+  const float* U;  // [Hkv, Dk, rank]
+  int rank, bits;
+  uint8_t* codes;
+  uint16_t* scale;
+  uint16_t* zero;
+};
+hipError_t launch_side_pack(const SideArgs& a, hipStream_t stream);
+constexpr int kMaxSideRank = 16;
 
 // Work units of the matrix-core decode kernel: each of the P split-K partitions
 // is cut into c = 1, 2 or 4 contiguous runs, one wave each (four independent waves
@@ -98,6 +120,7 @@ int pack_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, int64_t t
               const void* K, const void* V, int kv_dtype, const kvq_cache* cache, void* stream);
 int decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, const void* q, int q_dtype,
                 const kvq_cache* cache, float softmax_scale, int num_partitions, void* workspace,
-                size_t workspace_bytes, float* out, void* stream, void* event_after_decode);
+                size_t workspace_bytes, float* out, void* stream, void* event_after_decode,
+                const DecodeArgs* side = nullptr);
 
 }  // namespace kvq

@@ -524,4 +524,74 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
   }
 }
 
+// ----------------------------------------------------- HeadQ side code (write path)
+// Thread (token t = tid / 16, coefficient k = tid % 16) of the workgroup of code
+// group g: y_k = sum_c (k_c - k_hat_c) U[c][k] in float64, channels in ascending
+// order with no fused multiply-add, rounded once to float32; then the token's r
+// coefficients are one quantizer group (the library's min/max contract).
+namespace {
+template <int DT>
+__device__ __forceinline__ float load_one(const void* p, int64_t i) {
+  if constexpr (DT == KVQ_F32) return static_cast<const float*>(p)[i];
+  else if constexpr (DT == KVQ_F16) return __half2float(static_cast<const __half*>(p)[i]);
+  else return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
+}
+
+template <int DT>
+__global__ __launch_bounds__(KVQ_GROUP * kMaxSideRank) void side_pack_kernel(const SideArgs a) {
+  __shared__ float ys[KVQ_GROUP][kMaxSideRank];
+  const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int t = int(threadIdx.x) / kMaxSideRank, k = int(threadIdx.x) % kMaxSideRank;
+  const int Dk = a.L.Dk, kb = a.L.k_bits, R = a.rank;
+  const int64_t slab = int64_t(b) * a.L.Hkv + h;
+  const int64_t Tq = a.L.Tq;
+  const int64_t j = int64_t(g) * KVQ_GROUP + t;  // compacted token
+  const RetentionRule rule{a.L.T, a.L.n_recent, a.L.log_window};
+  const int ksh = key_group_shift(a.L.k_group);
+  if (k < R) {
+    const int64_t pos = quantized_position(rule, j);
+    const uint32_t* row = static_cast<const uint32_t*>(a.cache.k_codes) + (slab * Tq + j) * (Dk * kb / 32);
+    const int64_t kgi = slab * (Tq / a.L.k_group) + (g >> ksh);
+    const uint16_t* ks = static_cast<const uint16_t*>(a.cache.k_scale) + kgi * Dk;
+    const uint16_t* kz = static_cast<const uint16_t*>(a.cache.k_zero) + kgi * Dk;
+    const int64_t krow = (slab * a.L.T + pos) * Dk;
+    double y = 0.0;
+    for (int c = 0; c < Dk; ++c) {
+      // k_hat = code * s + z is exact in float64
+      const double khat = double(stream_code(row, c * kb, kb)) * double(f16_bits_to_f32(ks[c])) +
+                          double(f16_bits_to_f32(kz[c]));
+      const double e = __dsub_rn(double(load_one<DT>(a.K, krow + c)), khat);
+      y = __dadd_rn(y, __dmul_rn(e, double(a.U[(int64_t(h) * Dk + c) * R + k])));
+    }
+    ys[t][k] = float(y);
+  }
+  __syncthreads();
+  if (k < R) {
+    float mn = ys[t][0], mx = ys[t][0];
+    for (int i = 1; i < R; ++i) {
+      mn = fminf(mn, ys[t][i]);
+      mx = fmaxf(mx, ys[t][i]);
+    }
+    const float levels = float((1 << a.bits) - 1);
+    const QParams q = make_qparams(mn, mx, levels);
+    a.codes[(slab * Tq + j) * R + k] = uint8_t(quant_code(ys[t][k], q.s, q.z, q.r, levels));
+    if (k == 0) {
+      a.scale[slab * Tq + j] = q.s_bits;
+      a.zero[slab * Tq + j] = q.z_bits;
+    }
+  }
+}
+}  // namespace
+
+hipError_t launch_side_pack(const SideArgs& a, hipStream_t stream) {
+  const dim3 grid(unsigned(a.L.n_groups), unsigned(a.L.Hkv), unsigned(a.L.B)), block(KVQ_GROUP * kMaxSideRank);
+  switch (a.dtype) {
+    case KVQ_F32: hipLaunchKernelGGL(side_pack_kernel<KVQ_F32>, grid, block, 0, stream, a); break;
+    case KVQ_F16: hipLaunchKernelGGL(side_pack_kernel<KVQ_F16>, grid, block, 0, stream, a); break;
+    case KVQ_BF16: hipLaunchKernelGGL(side_pack_kernel<KVQ_BF16>, grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace kvq
