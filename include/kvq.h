@@ -174,9 +174,10 @@ int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count,
  *        vector-ALU kernel; for the matrix-core kernel the P runs may be cut further
  *        into 2P or 4P and sized by dispatch order (within about +-20% of equal).
  *        Results differ only in rounding.  1 <= P <= max(1, ceil(T/32)).
- *   workspace / workspace_bytes: at least kvq_decode_workspace_bytes(L, P) bytes of
- *        16-byte aligned device memory (may be NULL when P == 1); no
- *        initialisation needed.  A workspace serves one call at a time: calls that
+ *   workspace / workspace_bytes: 16-byte aligned device memory for the partial
+ *        results: kvq_decode_workspace_bytes(L, P) bytes always suffice (the exact
+ *        need is B * Hq * units * (Dv + 4) floats, units from kvq_decode_plan; 0
+ *        when units == 1, and then workspace may be NULL); no initialisation needed.  A workspace serves one call at a time: calls that
  *        overlap on the GPU (different streams) need separate workspaces.
  *   out: [B, Hq, Dv] float32 device array.
  * Partial results of the partitions are merged on the device.
@@ -196,6 +197,34 @@ int kv_decode_attn(const kvq_layout* L, const void* q, int q_dtype, const kvq_ca
 int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache,
                       float softmax_scale, int num_partitions, void* workspace, size_t workspace_bytes,
                       float* out, void* stream, void* event_after_decode);
+
+/*
+ * kvq_decode_plan — which decode kernel kv_decode_attn (with_side_code = 0) or
+ * kv_decode_attn_side (with_side_code != 0) runs for this layout and partition
+ * count on the calling thread's current device, and how it cuts the work.  No GPU
+ * work is enqueued; the device's compute-unit count is read (once per device).
+ *   kernel: KVQ_KERNEL_MFMA, the matrix-core kernel, for 4 query heads per KV head,
+ *     Dv = 128, Dk in {32, 64, 128} and 2/4/8-bit codes with Dk * k_bits >= 128, no
+ *     side code; KVQ_KERNEL_VALU, the vector-ALU kernel, for every other layout.  A
+ *     layout the matrix-core kernel takes never runs on the other one: a failure
+ *     there is returned as KVQ_ERR_HIP.
+ *   units: partial results per query head that the merge kernel folds (1: the
+ *     decode kernel writes the output and no merge runs).
+ *   ring_depth: key groups each wave of the matrix-core kernel keeps in its LDS
+ *     ring (2..4); waves_per_simd: waves of that grid per SIMD; both 0 for the
+ *     vector-ALU kernel.  waves: waves the decode kernel launches.
+ * Errors: as kv_decode_attn for the layout and num_partitions; KVQ_ERR_HIP if the
+ * device cannot be queried.
+ */
+enum { KVQ_KERNEL_MFMA = 1, KVQ_KERNEL_VALU = 2 };
+typedef struct {
+  int32_t kernel;
+  int32_t units;
+  int32_t ring_depth;
+  int32_t waves_per_simd;
+  int64_t waves;
+} kvq_decode_info;
+int kvq_decode_plan(const kvq_layout* L, int num_partitions, int with_side_code, kvq_decode_info* info);
 
 /* ------------------------------------------------------------------ streaming
  *
@@ -298,17 +327,6 @@ int kv_stream_decode(const kvq_stream* S, const void* q, int q_dtype, const kvq_
                      float softmax_scale, int num_partitions, void* workspace, size_t workspace_bytes,
                      float* out, void* stream);
 
-/*
- * kvq_read_probe — measurement support, not part of the decode path: reads
- * buf[0, bytes) once (bytes rounded down to a multiple of 16) with a plain
- * grid-wide streaming read, so that a caller can time the HBM read rate the
- * device reaches and report it next to the decode kernel's.  buf: 16-byte
- * aligned device memory, owned by the caller.  sink: 4 bytes of device memory
- * the kernel may write (it keeps the reads from being optimized away; its
- * content is unspecified).  stream: hipStream_t (NULL = default).  Errors:
- * KVQ_ERR_INVALID for a NULL or misaligned pointer, KVQ_ERR_HIP for a failed
- * launch.
- */
 /* ---- HeadQ side code ("HeadQ", section 3, methodology): write and read mechanics.
  * Write: for every quantized token j of a packed cache, e_j = k_j - k_hat_j (k_hat_j
  * from the cache's codes, scales and zeros), y_j = U_h^T e_j (summed in float64 over
@@ -339,6 +357,17 @@ int kv_decode_attn_side(const kvq_layout* L, const void* q, int q_dtype, const k
                         const float* U, const kvq_side* side, float softmax_scale, int num_partitions,
                         void* workspace, size_t workspace_bytes, float* out, void* stream);
 
+/*
+ * kvq_read_probe — measurement support, not part of the decode path: reads
+ * buf[0, bytes) once (bytes rounded down to a multiple of 16) with a plain
+ * grid-wide streaming read, so that a caller can time the HBM read rate the
+ * device reaches and report it next to the decode kernel's.  buf: 16-byte
+ * aligned device memory, owned by the caller.  sink: 4 bytes of device memory
+ * the kernel may write (it keeps the reads from being optimized away; its
+ * content is unspecified).  stream: hipStream_t (NULL = default).  Errors:
+ * KVQ_ERR_INVALID for a NULL or misaligned pointer, KVQ_ERR_HIP for a failed
+ * launch.
+ */
 int kvq_read_probe(const void* buf, size_t bytes, void* sink, void* stream);
 
 /* Static text for a status code. */

@@ -69,6 +69,16 @@ class Layout:
         }
 
 
+def decode_plan(layout: Layout, num_partitions: int, side_code: bool = False) -> dict:
+    """Which decode kernel a request runs on the current device and how it is cut
+    (kvq_decode_plan): kernel "mfma" or "valu", partial rows per query head, the
+    matrix-core kernel's LDS ring depth and waves per SIMD, and the waves launched."""
+    info = L_.KvqDecodeInfo()
+    L_.check(L_.load().kvq_decode_plan(layout.ref, num_partitions, 1 if side_code else 0, ctypes.byref(info)))
+    return {"kernel": {L_.KVQ_KERNEL_MFMA: "mfma", L_.KVQ_KERNEL_VALU: "valu"}[info.kernel], "units": info.units,
+            "ring_depth": info.ring_depth, "waves_per_simd": info.waves_per_simd, "waves": info.waves}
+
+
 def alloc_workspace(layout: Layout, num_partitions: int, device="cuda"):
     """Decode workspace for num_partitions partitions (needs no initialisation)."""
     need = layout.workspace_bytes(num_partitions)

@@ -58,6 +58,27 @@ int check_layout(const kvq_layout* L) {
   return ok();
 }
 
+// Split-K partition count of a decode over the tokens of L.
+int check_partitions(const kvq_layout& L, int num_partitions) {
+  const int64_t max_p = (int64_t(L.T) + KVQ_GROUP - 1) / KVQ_GROUP;
+  if (num_partitions < 1 || num_partitions > (max_p > 1 ? max_p : 1))
+    return fail(KVQ_ERR_INVALID, "num_partitions %d must be in [1, %lld]", num_partitions, (long long)max_p);
+  if (num_partitions > 65535) return fail(KVQ_ERR_UNSUPPORTED, "num_partitions %d > 65535", num_partitions);
+  if (L.B > 65535 || L.Hkv > 65535) return fail(KVQ_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  return KVQ_OK;
+}
+
+// A workspace too small for the partial results: a caller's (KVQ_ERR_INVALID) or
+// the library's static scratch (KVQ_ERR_UNSUPPORTED).
+int workspace_short(int status, size_t have, size_t need) {
+  if (status == KVQ_ERR_UNSUPPORTED)
+    return fail(status,
+                "the partial results need %zu bytes, more than the static scratch of %zu bytes; use "
+                "kv_decode_attn with a workspace, or fewer partitions",
+                need, have);
+  return fail(status, "workspace has %zu bytes, %zu needed", have, need);
+}
+
 }  // namespace
 
 // Shape, bit widths and retention policy of a layout (T is the token count or a
@@ -103,24 +124,14 @@ int kvq::check_cache_ptr(const void* p, const char* name) {
 int kvq::decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, const void* q, int q_dtype,
                      const kvq_cache* cache, float softmax_scale, int num_partitions, void* workspace,
                      size_t workspace_bytes, float* out, void* stream, void* event_after_decode,
-                     const DecodeArgs* side) {
+                     const DecodeArgs* side, int workspace_short_status) {
   int st;
   if (!cache) return fail(KVQ_ERR_INVALID, "cache is NULL");
   if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID, "q_dtype %d is not KVQ_F32/F16/BF16", q_dtype);
   if (!q || !out) return fail(KVQ_ERR_INVALID, "q or out is NULL");
   if (!aligned16(q) || !aligned16(out)) return fail(KVQ_ERR_INVALID, "q and out must be 16-byte aligned");
   if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID, "softmax_scale is not finite");
-  const int64_t max_p = (int64_t(L.T) + KVQ_GROUP - 1) / KVQ_GROUP;
-  if (num_partitions < 1 || num_partitions > (max_p > 1 ? max_p : 1))
-    return fail(KVQ_ERR_INVALID, "num_partitions %d must be in [1, %lld]", num_partitions, (long long)max_p);
-  if (num_partitions > 65535) return fail(KVQ_ERR_UNSUPPORTED, "num_partitions %d > 65535", num_partitions);
-  const size_t need = num_partitions == 1 ? 0 : kvq::ws_partial_bytes(L, num_partitions);
-  if (need > 0) {
-    if (!workspace) return fail(KVQ_ERR_INVALID, "workspace is NULL but %zu bytes are needed", need);
-    if (!aligned16(workspace)) return fail(KVQ_ERR_INVALID, "workspace is not 16-byte aligned");
-    if (workspace_bytes < need)
-      return fail(KVQ_ERR_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-  }
+  if ((st = check_partitions(L, num_partitions))) return st;
   if (L.n_groups > 0) {
     if ((st = check_cache_ptr(cache->k_codes, "k_codes")) || (st = check_cache_ptr(cache->k_scale, "k_scale")) ||
         (st = check_cache_ptr(cache->k_zero, "k_zero")) || (st = check_cache_ptr(cache->v_codes, "v_codes")) ||
@@ -131,7 +142,14 @@ int kvq::decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, co
     if ((st = check_cache_ptr(cache->k_fp16, "k_fp16")) || (st = check_cache_ptr(cache->v_fp16, "v_fp16")))
       return st;
   }
-  if (L.B > 65535 || L.Hkv > 65535) return fail(KVQ_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  // Partial rows: at least P per query head whenever P > 1 (the exact count comes
+  // from the plan, which needs the device), so these checks need no HIP call.
+  if (num_partitions > 1) {
+    const size_t least = size_t(L.B) * size_t(L.Hq) * size_t(num_partitions) * size_t(L.Dv + 4) * sizeof(float);
+    if (!workspace) return fail(KVQ_ERR_INVALID, "workspace is NULL but at least %zu bytes are needed", least);
+    if (!aligned16(workspace)) return fail(KVQ_ERR_INVALID, "workspace is not 16-byte aligned");
+    if (workspace_bytes < least) return workspace_short(workspace_short_status, workspace_bytes, least);
+  }
   kvq::DecodeArgs a{};
   a.L = L;
   a.q = q;
@@ -141,9 +159,6 @@ int kvq::decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, co
   a.P = num_partitions;
   a.g_stride = g_stride;
   a.r_stride = r_stride;
-  if (need > 0) {
-    a.partials = static_cast<float*>(workspace);
-  }
   a.out = out;
   if (side) {
     a.side_u = side->side_u;
@@ -152,8 +167,15 @@ int kvq::decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, co
     a.side_zero = side->side_zero;
     a.side_rank = side->side_rank;
   }
-  const hipError_t e =
-      kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(event_after_decode));
+  kvq::DecodePlan plan{};
+  hipError_t e = kvq::plan_decode(a, &plan);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode planning failed: %s", hipGetErrorString(e));
+  const size_t need = kvq::plan_partial_bytes(L, plan);
+  if (need > 0) {
+    if (workspace_bytes < need) return workspace_short(workspace_short_status, workspace_bytes, need);
+    a.partials = static_cast<float*>(workspace);
+  }
+  e = kvq::launch_decode(a, plan, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(event_after_decode));
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -310,14 +332,38 @@ int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq
                           workspace_bytes, out, stream, event_after_decode);
 }
 
+int kvq_decode_plan(const kvq_layout* L, int num_partitions, int with_side_code, kvq_decode_info* info) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (!info) return fail(KVQ_ERR_INVALID, "info is NULL");
+  if ((st = check_partitions(*L, num_partitions))) return st;
+  kvq::DecodeArgs a{};
+  a.L = *L;
+  a.P = num_partitions;
+  a.side_rank = with_side_code ? 1 : 0;
+  kvq::DecodePlan p{};
+  const hipError_t e = kvq::plan_decode(a, &p);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode planning failed: %s", hipGetErrorString(e));
+  info->kernel = p.kernel;
+  info->units = p.units;
+  info->ring_depth = p.depth;
+  info->waves_per_simd = p.ranks;
+  info->waves = p.waves;
+  return ok();
+}
+
 // ------------------------------------------------------------ HeadQ side code
 namespace {
 int check_side(const kvq_layout* L, int rank, const float* U, const kvq_side* side) {
   if (rank < 1 || rank > kvq::kMaxSideRank || rank > L->Dk)
     return fail(KVQ_ERR_UNSUPPORTED, "side rank %d must be in [1, min(Dk, %d)]", rank, kvq::kMaxSideRank);
   if (!U || !side) return fail(KVQ_ERR_INVALID, "U or side is NULL");
-  if (L->n_groups > 0 && (!side->codes || !side->scale || !side->zero))
-    return fail(KVQ_ERR_INVALID, "side buffers must not be NULL");
+  if (!aligned16(U)) return fail(KVQ_ERR_INVALID, "U is not 16-byte aligned");
+  if (L->n_groups > 0) {
+    if (!side->codes || !side->scale || !side->zero) return fail(KVQ_ERR_INVALID, "side buffers must not be NULL");
+    if (!aligned16(side->codes) || !aligned16(side->scale) || !aligned16(side->zero))
+      return fail(KVQ_ERR_INVALID, "side buffers must be 16-byte aligned");
+  }
   return ok();
 }
 }  // namespace
@@ -344,6 +390,7 @@ int kv_side_pack(const kvq_layout* L, int rank, int side_bits, const float* U, c
     return fail(KVQ_ERR_UNSUPPORTED, "side_bits %d must be 2, 4 or 8", side_bits);
   if (!valid_dtype(kv_dtype)) return fail(KVQ_ERR_INVALID, "kv_dtype %d is not KVQ_F32/F16/BF16", kv_dtype);
   if (!K || !cache) return fail(KVQ_ERR_INVALID, "K or cache is NULL");
+  if (!aligned16(K)) return fail(KVQ_ERR_INVALID, "K is not 16-byte aligned");
   if (L->n_groups == 0) return ok();
   if ((st = check_cache_ptr(cache->k_codes, "k_codes")) || (st = check_cache_ptr(cache->k_scale, "k_scale")) ||
       (st = check_cache_ptr(cache->k_zero, "k_zero")))

@@ -1,7 +1,7 @@
-// kv_decode_attn, generic kernel for gfx950: any supported shape (head widths that
-// are multiples of 32 up to 256, 1..16 query heads per KV head, 2/4/8-bit codes).
-// The MFMA kernel (kvq_decode_mfma.hip) takes the common shapes; this one is the
-// reference-style fallback and the dispatcher of both.
+// kv_decode_attn, vector-ALU kernel for gfx950: any supported shape (head widths
+// that are multiples of 32 up to 256, 1..16 query heads per KV head, 1/2/3/4/8-bit
+// codes, the HeadQ side code).  The matrix-core kernel (kvq_decode_mfma.hip) takes
+// the shapes mfma_takes() accepts; this file also holds the dispatcher of both.
 //
 // Single-token decode attention, out = softmax(scale * q K^T) V, computed
 // directly from the packed cache: key x_hat = code * s + z with one (s, z) per
@@ -24,6 +24,8 @@
 //   sum_t p_t v_hat_tc = sum_t (p_t s_t,g(c)) code_tc + sum_t p_t z_t,g(c)   (values)
 // so the inner loops are one integer extract, one int->float convert and G fused
 // multiply-adds per code.
+#include <atomic>
+
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -33,9 +35,6 @@
 
 namespace kvq {
 
-// MFMA kernel launcher (kvq_decode_mfma.hip); returns hipErrorNotSupported for
-// shapes it does not take.
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream, int* parts);
 hipError_t launch_merge(const DecodeArgs& a, int parts, hipStream_t stream);
 
 namespace {
@@ -369,10 +368,24 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = size_t(loop_floats > merge_floats ? loop_floats : merge_floats) * sizeof(float);
   const dim3 grid(unsigned(a.P), unsigned(a.L.Hkv), unsigned(a.L.B));
   if (lds > 64 * 1024) {
-    // gfx950 has 160 KB of LDS per CU; opt in to more than the default 64 KB
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<G, QDT>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    // gfx950 has 160 KB of LDS per CU: opt in to more than the default 64 KB, once
+    // per device, for the largest head widths (the attribute is an upper bound)
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t(1) << dev) : 0;
+    if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
+      constexpr int W = KVQ_MAX_HEAD_DIM;
+      constexpr int lf = G * W + kWaves * (W * G + KVQ_GROUP * (W / KVQ_GROUP) * G + (W / KVQ_GROUP) * G);
+      constexpr int mf = G * W + (kWaves + 1) * G * (W + 2);
+      constexpr size_t most = size_t(lf > mf ? lf : mf) * sizeof(float);
+      static_assert(most <= 160 * 1024, "LDS budget");
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<G, QDT>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(most));
+      if (e != hipSuccess) return e;
+      if (bit) done.fetch_or(bit, std::memory_order_release);
+    }
   }
   hipLaunchKernelGGL((decode_kernel<G, QDT>), grid, dim3(kThreads), lds, stream, a);
   return hipGetLastError();
@@ -392,12 +405,24 @@ hipError_t launch_q(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t after_decode) {
-  int parts = a.P;  // partial rows per query head written by the decode kernel
+hipError_t plan_decode(const DecodeArgs& a, DecodePlan* plan) {
   // the side-code correction is carried by the vector-ALU kernel only
-  hipError_t e = a.side_rank > 0 ? hipErrorNotSupported : launch_decode_mfma(a, stream, &parts);
-  if (e == hipErrorNotSupported) {
-    parts = a.P;
+  if (a.side_rank == 0 && mfma_takes(a.L, a.P)) return mfma_decode(a, nullptr, plan, false);
+  plan->kernel = KVQ_KERNEL_VALU;
+  plan->units = a.P;
+  plan->depth = 0;
+  plan->ranks = 0;
+  plan->waves = int64_t(a.P) * a.L.Hkv * a.L.B * kWaves;
+  return hipSuccess;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream, hipEvent_t after_decode) {
+  hipError_t e;
+  if (plan.kernel == KVQ_KERNEL_MFMA) {
+    DecodePlan p = plan;
+    e = mfma_decode(a, stream, &p, true);
+    if (e == hipSuccess && p.units != plan.units) e = hipErrorInvalidValue;  // the device changed since planning
+  } else {
     switch (a.q_dtype) {
       case KVQ_F32: e = launch_q<KVQ_F32>(a, stream); break;
       case KVQ_F16: e = launch_q<KVQ_F16>(a, stream); break;
@@ -407,8 +432,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t aft
   }
   if (e != hipSuccess) return e;
   if (after_decode && (e = hipEventRecord(after_decode, stream)) != hipSuccess) return e;
-  if (parts == 1) return hipSuccess;
-  return launch_merge(a, parts, stream);
+  if (plan.units == 1) return hipSuccess;
+  return launch_merge(a, plan.units, stream);
 }
 
 }  // namespace kvq

@@ -53,6 +53,7 @@
 // Retained fp16 rows (recent window, log-spaced tokens) join the same online state
 // after the key groups: scores on the MFMA (A = fp16 key rows), values on the VALU.
 #include <algorithm>
+#include <atomic>
 
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -988,27 +989,37 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
 #define KVQ_DECODE_MAX_DEPTH 4
 #endif
 
+// Opt an instance into more than the default 64 KB of LDS (gfx950 has 160 KB per
+// compute unit), once per device: the attribute stays set for the process.
 template <int DK, int DV, int KB, int VB, int D>
-hipError_t launch_depth(DecodeArgs a, hipStream_t stream, int cus, int64_t waves) {
+hipError_t lds_optin(int dev, int bytes) {
+  static std::atomic<uint64_t> done{0};
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<DK, DV, KB, VB, D>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
+template <int DK, int DV, int KB, int VB, int D>
+hipError_t launch_depth(DecodeArgs a, hipStream_t stream, int dev, const DecodePlan& plan) {
   constexpr size_t lds = size_t(kWavesPerGroup) * Lds<DK, DV, KB, VB, D>::kBytes;
   static_assert(lds <= 160 * 1024, "LDS budget");
-  constexpr int per_simd = lds_waves_per_simd<DK, DV, KB, VB, D>();
-  const int64_t simds = int64_t(cus) * 4;
-  a.ranks = int(std::min<int64_t>(per_simd, std::max<int64_t>(1, (waves + simds - 1) / simds)));
+  a.units = plan.units;
+  a.ranks = plan.ranks;
   if constexpr (lds > 64 * 1024) {
-    // gfx950 has 160 KB of LDS per compute unit; opt in to more than the default 64 KB
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<DK, DV, KB, VB, D>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    const hipError_t e = lds_optin<DK, DV, KB, VB, D>(dev, int(lds));
     if (e != hipSuccess) return e;
   }
-  const int64_t blocks = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int64_t blocks = (plan.waves + kWavesPerGroup - 1) / kWavesPerGroup;
   hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, KB, VB, D>), dim3(unsigned(blocks)), dim3(64 * kWavesPerGroup), lds,
                      stream, a);
   return hipGetLastError();
 }
 
 template <int DK, int DV, int KB, int VB>
-hipError_t launch_one(DecodeArgs a, hipStream_t stream, int cus, int* parts) {
+hipError_t run_one(const DecodeArgs& a, hipStream_t stream, int dev, int cus, DecodePlan* plan, bool launch) {
   // Units are cut only as far as 8 waves per compute unit: measured on the 128K
   // workload, 2048 long runs stream HBM better than 4096 half-length ones (the
   // memory system serves the larger set of requests less evenly).  The ring is
@@ -1016,53 +1027,83 @@ hipError_t launch_one(DecodeArgs a, hipStream_t stream, int cus, int* parts) {
   // whole grid be resident at once (up to 4 steps: a 5th measured no faster on
   // the 128K workload).
   const int per_cu = 4 * lds_waves_per_simd<DK, DV, KB, VB, 2>();
-  a.units = decode_mfma_units(a.L, a.P, int64_t(cus) * (per_cu < 8 ? per_cu : 8));
-  *parts = a.units;
-  const int64_t waves = int64_t(a.units) * a.L.B * a.L.Hkv;
-  if (waves >= (int64_t(1) << 31)) return hipErrorNotSupported;
+  const int units = decode_mfma_units(a.L, a.P, int64_t(cus) * (per_cu < 8 ? per_cu : 8));
+  const int64_t waves = int64_t(units) * a.L.B * a.L.Hkv;
   const int64_t simds = int64_t(cus) * 4;
-  if constexpr (KVQ_DECODE_MAX_DEPTH >= 4) {
-    if (waves <= simds * lds_waves_per_simd<DK, DV, KB, VB, 4>()) return launch_depth<DK, DV, KB, VB, 4>(a, stream, cus, waves);
+  int depth = 2, per_simd = lds_waves_per_simd<DK, DV, KB, VB, 2>();
+  if (KVQ_DECODE_MAX_DEPTH >= 4 && waves <= simds * lds_waves_per_simd<DK, DV, KB, VB, 4>()) {
+    depth = 4;
+    per_simd = lds_waves_per_simd<DK, DV, KB, VB, 4>();
+  } else if (KVQ_DECODE_MAX_DEPTH >= 3 && waves <= simds * lds_waves_per_simd<DK, DV, KB, VB, 3>()) {
+    depth = 3;
+    per_simd = lds_waves_per_simd<DK, DV, KB, VB, 3>();
   }
-  if constexpr (KVQ_DECODE_MAX_DEPTH >= 3) {
-    if (waves <= simds * lds_waves_per_simd<DK, DV, KB, VB, 3>()) return launch_depth<DK, DV, KB, VB, 3>(a, stream, cus, waves);
-  }
-  return launch_depth<DK, DV, KB, VB, 2>(a, stream, cus, waves);
+  plan->kernel = KVQ_KERNEL_MFMA;
+  plan->units = units;
+  plan->depth = depth;
+  plan->ranks = int(std::min<int64_t>(per_simd, std::max<int64_t>(1, (waves + simds - 1) / simds)));
+  plan->waves = waves;
+  if (!launch) return hipSuccess;
+  if (depth == 4) return launch_depth<DK, DV, KB, VB, 4>(a, stream, dev, *plan);
+  if (depth == 3) return launch_depth<DK, DV, KB, VB, 3>(a, stream, dev, *plan);
+  return launch_depth<DK, DV, KB, VB, 2>(a, stream, dev, *plan);
 }
 
 template <int DK, int DV>
-hipError_t launch_bits(const DecodeArgs& a, hipStream_t stream, int cus, int* parts) {
+hipError_t run_bits(const DecodeArgs& a, hipStream_t stream, int dev, int cus, DecodePlan* plan, bool launch) {
   const int kb = a.L.k_bits, vb = a.L.v_bits;
   // key rows must give every lane at least 4 bytes of a tile (staged as dwords)
-#define KVQ_BITS_CASE(K_, V_)                                             \
-  if constexpr (DK * K_ / 32 >= 4) {                                      \
-    if (kb == K_ && vb == V_) return launch_one<DK, DV, K_, V_>(a, stream, cus, parts); \
+#define KVQ_BITS_CASE(K_, V_)                                                          \
+  if constexpr (DK * K_ / 32 >= 4) {                                                   \
+    if (kb == K_ && vb == V_) return run_one<DK, DV, K_, V_>(a, stream, dev, cus, plan, launch); \
   }
   KVQ_BITS_CASE(2, 2) KVQ_BITS_CASE(2, 4) KVQ_BITS_CASE(2, 8)
   KVQ_BITS_CASE(4, 2) KVQ_BITS_CASE(4, 4) KVQ_BITS_CASE(4, 8)
   KVQ_BITS_CASE(8, 2) KVQ_BITS_CASE(8, 4) KVQ_BITS_CASE(8, 8)
 #undef KVQ_BITS_CASE
-  return hipErrorNotSupported;
+  return hipErrorInvalidValue;  // unreachable for a shape mfma_takes accepts
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream, int* parts) {
-  *parts = a.P;
-  if (a.L.Hq != kG * a.L.Hkv || a.L.Dv != 128) return hipErrorNotSupported;
-  // per-slab offsets are 32-bit in this kernel
-  const int64_t widest = a.L.Dk > a.L.Dv ? a.L.Dk : a.L.Dv;
-  if (int64_t(a.L.Tq) * widest >= (int64_t(1) << 31) || int64_t(a.L.R) * widest * 2 >= (int64_t(1) << 31))
-    return hipErrorNotSupported;
+hipError_t device_cus(int* dev, int* cus) {
+  static std::atomic<int> cached[64];
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return e;
+  if (*dev >= 0 && *dev < 64) {
+    const int c = cached[*dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, *dev);
+  if (e != hipSuccess) return e;
+  if (*cus < 1) return hipErrorInvalidDevice;
+  if (*dev >= 0 && *dev < 64) cached[*dev].store(*cus, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
+bool mfma_takes(const kvq_layout& L, int P) {
+  if (L.Hq != kG * L.Hkv || L.Dv != 128) return false;
+  if (L.Dk != 32 && L.Dk != 64 && L.Dk != 128) return false;
+  const auto ok_bits = [](int b) { return b == 2 || b == 4 || b == 8; };
+  if (!ok_bits(L.k_bits) || !ok_bits(L.v_bits) || L.Dk * L.k_bits / 32 < 4) return false;
+  // per-slab offsets are 32-bit in this kernel, and so is the wave index
+  const int64_t widest = L.Dk > L.Dv ? L.Dk : L.Dv;
+  if (int64_t(L.Tq) * widest >= (int64_t(1) << 31) || int64_t(L.R) * widest * 2 >= (int64_t(1) << 31)) return false;
+  return int64_t(kMaxUnitsPerPartition) * P * L.B * L.Hkv < (int64_t(1) << 31);
+}
+
+hipError_t mfma_decode(const DecodeArgs& a, hipStream_t stream, DecodePlan* plan, bool launch) {
   int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const hipError_t e = device_cus(&dev, &cus);
   if (e != hipSuccess) return e;
   switch (a.L.Dk) {
-    case 32: return launch_bits<32, 128>(a, stream, cus, parts);
-    case 64: return launch_bits<64, 128>(a, stream, cus, parts);
-    case 128: return launch_bits<128, 128>(a, stream, cus, parts);
-    default: return hipErrorNotSupported;
+    case 32: return run_bits<32, 128>(a, stream, dev, cus, plan, launch);
+    case 64: return run_bits<64, 128>(a, stream, dev, cus, plan, launch);
+    case 128: return run_bits<128, 128>(a, stream, dev, cus, plan, launch);
+    default: return hipErrorInvalidValue;  // unreachable for a shape mfma_takes accepts
   }
 }
 

@@ -101,10 +101,37 @@ struct AppendArgs {
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
-// Decode kernel (matrix-core kernel where it applies, else the generic one)
-// followed, when P > 1, by the partition merge; after_decode (if not null) is
-// recorded on the stream between the two.
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t after_decode);
+
+// Current device and its compute-unit count (the attribute is read once per device
+// and kept).
+hipError_t device_cus(int* dev, int* cus);
+
+// How a decode request is carried out: which kernel, how many partial rows each
+// query head gets (the merge folds them; 1 = the decode kernel writes the output),
+// the matrix-core kernel's LDS ring depth and its grid.
+struct DecodePlan {
+  int kernel;       // KVQ_KERNEL_MFMA or KVQ_KERNEL_VALU
+  int units;        // partial rows per query head
+  int depth;        // key groups in a wave's LDS ring (matrix-core kernel), else 0
+  int ranks;        // waves per SIMD of the matrix-core grid, else 0
+  int64_t waves;    // waves the decode kernel launches
+};
+// Shapes the matrix-core kernel takes: 4 query heads per KV head, value width 128,
+// key width 32, 64 or 128, 2/4/8-bit codes with at least 4 key-code bytes per lane
+// and a tile row, per-slab offsets inside 32 bits.  Everything else runs on the
+// vector-ALU kernel; a request the matrix-core kernel takes never falls back.
+bool mfma_takes(const kvq_layout& L, int P);
+// Matrix-core kernel: fill *plan and, when `launch`, enqueue the kernel.
+hipError_t mfma_decode(const DecodeArgs& a, hipStream_t stream, DecodePlan* plan, bool launch);
+// The plan of a request (a.L, a.P, a.side_rank are read).
+hipError_t plan_decode(const DecodeArgs& a, DecodePlan* plan);
+// Bytes of partial rows a planned decode writes (0 when units == 1).
+inline size_t plan_partial_bytes(const kvq_layout& L, const DecodePlan& p) {
+  return p.units <= 1 ? 0 : size_t(L.B) * size_t(L.Hq) * size_t(p.units) * size_t(L.Dv + 4) * sizeof(float);
+}
+// Decode kernel of `plan` followed, when plan.units > 1, by the partition merge;
+// after_decode (if not null) is recorded on the stream between the two.
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream, hipEvent_t after_decode);
 
 // Host helpers of the C ABI layer (kvq_api.cpp), shared with the streaming
 // entry points (kvq_stream.cpp).
@@ -121,6 +148,6 @@ int pack_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, int64_t t
 int decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, const void* q, int q_dtype,
                 const kvq_cache* cache, float softmax_scale, int num_partitions, void* workspace,
                 size_t workspace_bytes, float* out, void* stream, void* event_after_decode,
-                const DecodeArgs* side = nullptr);
+                const DecodeArgs* side = nullptr, int workspace_short_status = KVQ_ERR_INVALID);
 
 }  // namespace kvq

@@ -42,8 +42,7 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipS
   const int64_t n16 = int64_t(bytes / 16);
   if (n16 == 0) return hipSuccess;
   int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const hipError_t e = device_cus(&dev, &cus);
   if (e != hipSuccess) return e;
   // 8 workgroups per CU: measured as fast as more on a 537 MB read
   const int64_t want = int64_t(cus > 0 ? cus : 1) * 8;

@@ -171,7 +171,9 @@ def test_decode_errors(lib):
     assert dec(P=0) == L_.KVQ_ERR_INVALID
     assert dec(P=35) == L_.KVQ_ERR_INVALID                        # > ceil(T/32) = 34
     assert dec(ws=None) == L_.KVQ_ERR_INVALID
-    assert dec(wsb=need - 4) == L_.KVQ_ERR_INVALID
+    assert dec(ws=FAKE + 4) == L_.KVQ_ERR_INVALID
+    least = 2 * 8 * 4 * 132 * 4                                    # at least P partial rows per query head
+    assert dec(wsb=least - 4) == L_.KVQ_ERR_INVALID
     bad = _cache()
     bad.k_fp16 = None
     assert dec(cache=bad) == L_.KVQ_ERR_INVALID

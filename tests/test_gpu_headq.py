@@ -21,7 +21,7 @@ from workloads.device import upload_workload
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("idx,rank,bits", [(0, 4, 8), (3, 8, 4), (13, 16, 2)])
+@pytest.mark.parametrize("idx,rank,bits", [(0, 4, 8), (3, 8, 4), (13, 16, 2), (19, 6, 4)])
 def test_side_code_and_corrected_decode(idx, rank, bits):
     w = small_cases()[idx]
     print("headq case %s rank %d bits %d" % (w.name, rank, bits), flush=True)

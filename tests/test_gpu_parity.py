@@ -40,8 +40,10 @@ def _compare_pack(gpu: dict, ref: dict, where=""):
                                  % (where, k, len(bad), bad[0].tolist(), g[tuple(bad[0])], r[tuple(bad[0])]))
 
 
-def _run_small(w: Workload, partitions=None):
-    _log("case %s" % w.name)
+def _run_small(w: Workload, partitions=None, kernel=None):
+    """Pack and decode the whole workload; returns (cache, oracle arrays, {P: plan}).
+    kernel: the decode kernel every partition count must run on ("mfma" / "valu")."""
+    _log("case %s (%s)" % (w.name, w.dtype))
     K, V = make_all(w, workers=4)
     q = make_queries(w)
     lay = api.Layout.from_workload(w)
@@ -54,28 +56,70 @@ def _run_small(w: Workload, partitions=None):
     want = O.decode_all(q, ref, w, scale)
     oracle_cache = cache_from_numpy(ref)
     max_p = max(1, (w.T + 31) // 32)
+    plans = {}
     for P in partitions or sorted(p for p in {1, 2, w.partitions, max_p} if p <= max_p):
+        plans[P] = plan = api.decode_plan(lay, P)
+        if kernel is not None:
+            assert plan["kernel"] == kernel, (w.name, P, plan)
+        errs = []
         for name, c in (("oracle-packed", oracle_cache), ("gpu-packed", cache)):
             out = api.kv_decode_attn(lay, qd, c, num_partitions=P, softmax_scale=scale)
             torch.cuda.synchronize()
             err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
+            errs.append(err)
             assert err <= MAX_ABS_ERR, (w.name, name, P, err)
-    return cache, ref
+        _log("  P=%d %s kernel, %d units, ring %d: max|err| %.2e (oracle-packed) %.2e (gpu-packed)"
+             % (P, plan["kernel"], plan["units"], plan["ring_depth"], errs[0], errs[1]))
+    return cache, ref, plans
+
+
+def _expected_kernel(w: Workload) -> str:
+    """The decode kernel include/kvq.h promises for a layout (no side code)."""
+    mfma = (w.Hq == 4 * w.Hkv and w.Dv == 128 and w.Dk in (32, 64, 128) and w.k_bits in (2, 4, 8)
+            and w.v_bits in (2, 4, 8) and w.Dk * w.k_bits >= 128)
+    return "mfma" if mfma else "valu"
 
 
 @pytest.mark.parametrize("w", small_cases(), ids=lambda w: w.name)
 def test_small_cases(w):
-    _run_small(w)
+    _run_small(w, kernel=_expected_kernel(w))
+
+
+# Every (Dk, key bits, value bits) instance the matrix-core kernel is built for:
+# Dk in {32, 64, 128}, 2/4/8-bit codes with at least 4 key-code bytes per lane.
+MFMA_INSTANCES = [(dk, kb, vb) for dk in (32, 64, 128) for kb in (2, 4, 8) for vb in (2, 4, 8)
+                  if dk * kb // 32 >= 4]
+_DTYPES = ("bf16", "f16", "f32")
+
+
+def test_mfma_instance_list():
+    assert len(MFMA_INSTANCES) == 24
+
+
+@pytest.mark.parametrize("dk,kb,vb", MFMA_INSTANCES, ids=lambda x: str(x))
+def test_mfma_instances(dk, kb, vb):
+    """Each matrix-core instance on a small cache: 2 batch rows x 2 KV heads, 10 code
+    groups per slab plus a 12-token fp16 window, one, three and four partitions (the
+    last cut into more units than there are groups); the input dtype cycles through
+    bf16, fp16 and fp32 so every dtype meets every key width."""
+    i = MFMA_INSTANCES.index((dk, kb, vb))
+    w = Workload("mfma_d%d_k%dv%d" % (dk, kb, vb), B=2, Hq=8, Hkv=2, Dk=dk, Dv=128, T=332, k_bits=kb, v_bits=vb,
+                 n_recent=12, dtype=_DTYPES[i % 3], partitions=4, seed=100 + i)
+    _run_small(w, partitions=[1, 3, 4], kernel="mfma")
 
 
 def test_tiny_ref_full():
     """The 256-token fp32 reference workload, whole."""
-    _run_small(workload("tiny_ref"))
+    _run_small(workload("tiny_ref"), kernel="valu")
 
 
 def test_llama8b_gqa_4k_full():
-    """Llama-8B-shaped GQA decode at 4096 tokens, every slab compared."""
-    _run_small(workload("llama8b_gqa_4k"), partitions=[1, 4, 16])
+    """Llama-8B-shaped GQA decode at 4096 tokens, every slab compared, at partition
+    counts that take the matrix-core kernel's ring depths 4, 3 and 2 (40 and 128
+    partitions put more waves on the device than the deeper rings fit; 128 also
+    gives units without key groups)."""
+    _, _, plans = _run_small(workload("llama8b_gqa_4k"), partitions=[1, 4, 16, 40, 128], kernel="mfma")
+    assert {p["ring_depth"] for p in plans.values()} == {2, 3, 4}, plans
 
 
 @pytest.mark.parametrize("w", [
@@ -191,7 +235,9 @@ def _full_size(w: Workload, n_slabs: int):
     _log("full-size %s: pack" % w.name)
     cache = api.kv_quant_pack(lay, Kd, Vd)
     scale = float(O.default_scale(w.Dk))
-    _log("full-size %s: decode P=%d" % (w.name, w.partitions))
+    plan = api.decode_plan(lay, w.partitions)
+    _log("full-size %s: decode P=%d (%s)" % (w.name, w.partitions, plan))
+    assert plan["kernel"] == _expected_kernel(w)
     out = api.kv_decode_attn(lay, qd, cache, num_partitions=w.partitions, softmax_scale=scale)
     torch.cuda.synchronize()
     out = out.cpu().numpy().astype(np.float64)
@@ -206,6 +252,7 @@ def _full_size(w: Workload, n_slabs: int):
         _compare_pack(gpu, ref, "%s slab (%d,%d) " % (w.name, b, h))
         want = O.decode_slab(q[b, h * G:(h + 1) * G], ref, w.dtype, w.k_bits, w.v_bits, scale)
         err = np.abs(out[b, h * G:(h + 1) * G] - want).max()
+        _log("  slab (%d, %d): packed bytes equal, decode max|err| %.2e" % (b, h, err))
         assert err <= MAX_ABS_ERR, (w.name, b, h, err)
     return Kd, Vd, qd, lay, cache
 

@@ -161,6 +161,14 @@ def test_stream_value_groups_64_generic():
     _run_stream(w, T0, T0 + 200, {T0 + 1, T0 + 77, T0 + 150}, [1, 2])
 
 
+def test_stream_f16_inputs_log_after_prefill():
+    """fp16 keys, values and queries (K4V2, log-spaced fp16 tokens), after a prefill."""
+    w = Workload("stream_k4v2_f16_log", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=1400, k_bits=4, v_bits=2,
+                 n_recent=64, log_window=64, dtype="f16", seed=31)
+    T0 = _valid_prefill(w, 900)
+    _run_stream(w, T0, T0 + 200, {T0 + 1, T0 + 64, T0 + 199}, [1, 3])
+
+
 def test_stream_one_bit():
     """1-bit keys and values in a stream (the append kernel's 1-bit words), f32 inputs."""
     w = Workload("stream_k1v1", B=1, Hq=4, Hkv=2, Dk=64, Dv=128, T=300, k_bits=1, v_bits=1,

@@ -278,6 +278,38 @@ def test_attention_permutation_invariance():
     assert np.abs(O.attention(q, K, V, 0.3) - O.attention(q, K[perm], V[perm], 0.3)).max() <= 1e-12
 
 
+# ------------------------------------------------------------------- softmax scale
+
+@pytest.mark.parametrize("d", [16, 32, 64, 96, 128, 256])
+def test_default_scale_is_inverse_sqrt_of_key_width(d):
+    """The score is q.k / sqrt(d) (HeadQ section 2.1; Thin Keys section 2): the float32
+    scale lies within one float32 step of 1/sqrt(d) taken in float64 with math.sqrt,
+    and is exact where that is a power of two (d = 16, 64, 256: 1/4, 1/8, 1/16)."""
+    got = O.default_scale(d)
+    assert isinstance(got, np.float32)
+    want = 1.0 / math.sqrt(d)
+    assert abs(float(got) - want) <= float(np.spacing(np.float32(want)))
+    if d in (16, 64, 256):
+        assert float(got) == want
+
+
+def test_thin_keys_default_scale_uses_key_width():
+    """Thin keys (Dk = 32, Dv = 128; Thin Keys section 2 scales by sqrt(d_select)): the
+    oracle's default decode equals textbook attention (explicit loops) with
+    1/sqrt(Dk) from math.sqrt, and is far from the one with 1/sqrt(Dv)."""
+    w = _w(T=64, Dk=32, Dv=128, Hq=2, k_bits=8, v_bits=4)
+    K, V = make_all(w, workers=1)
+    q = make_queries(w)
+    packed = O.pack_all(K, V, w)
+    out = O.decode_all(q, packed, w)[0]
+    Kh, Vh = O.dequant_slab(O.slab_of(packed, 0, 0), 8, 4)
+    qf = O.upcast(q[0], "bf16")
+    with_dk = _explicit_attention(qf, Kh, Vh, 1.0 / math.sqrt(32))
+    with_dv = _explicit_attention(qf, Kh, Vh, 1.0 / math.sqrt(128))
+    assert np.abs(out - with_dk).max() < 1e-6
+    assert np.abs(out - with_dv).max() > 1e-2
+
+
 # ----------------------------------------------------------- whole-pipeline pins
 
 def _w(**kw):

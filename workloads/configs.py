@@ -26,7 +26,7 @@ class Workload:
     v_bits: int
     n_recent: int = 0        # newest tokens kept in fp16
     log_window: int = 0      # W of the log-spaced fp16 regions (0 = off)
-    dtype: str = "bf16"      # dtype of q, K and V as handed to both sides: "f32" | "bf16"
+    dtype: str = "bf16"      # dtype of q, K and V as handed to both sides: "f32" | "bf16" | "f16"
     partitions: int = 1      # split-K sequence partitions used by decode
     seed: int = 0
     prefill_chunk: int = 0   # tokens of the newest chunk re-packed inside one bench step
@@ -119,4 +119,9 @@ def small_cases():
                  n_recent=64, log_window=64, dtype="bf16", partitions=2, seed=24, v_group=64),
         Workload("small_k1v4_f32", B=1, Hq=2, Hkv=1, Dk=32, Dv=96, T=352, k_bits=1, v_bits=4,
                  n_recent=32, dtype="f32", partitions=4, seed=25),
+        # fp16 keys, values and queries (matrix-core and vector-ALU paths)
+        Workload("small_k4v2_f16", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=1064, k_bits=4, v_bits=2,
+                 n_recent=40, dtype="f16", partitions=5, seed=29),
+        Workload("small_g2_k4v4_f16_log", B=1, Hq=4, Hkv=2, Dk=64, Dv=96, T=579, k_bits=4, v_bits=4,
+                 n_recent=0, log_window=32, dtype="f16", partitions=3, seed=30),
     ]

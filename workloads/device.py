@@ -6,12 +6,14 @@ from .synth import make_all, make_queries
 
 
 def to_device(arr: np.ndarray, dtype: str, device="cuda"):
-    """Storage-dtype numpy array -> torch tensor (bf16 travels as bit patterns)."""
+    """Storage-dtype numpy array -> torch tensor (bf16 and fp16 travel as bit patterns)."""
     import torch
     if dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    if dtype == "f16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.float16)
     raise ValueError(dtype)
 
 
@@ -22,7 +24,7 @@ def upload_workload(w, t_lo=0, t_hi=None, device="cuda"):
     if t_hi is None:
         t_hi = w.T
     n = t_hi - t_lo
-    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
     K = torch.empty((w.B, w.Hkv, n, w.Dk), dtype=tdt, device=device)
     V = torch.empty((w.B, w.Hkv, n, w.Dv), dtype=tdt, device=device)
 

@@ -14,8 +14,8 @@ Streams are independent per unit so any slab can be drawn alone:
 ``SeedSequence([seed, 1, h])`` draws the per-head outlier channels and offsets,
 ``SeedSequence([seed, 2, b, h])`` draws the (T, Dk) keys then the (T, Dv) values of
 slab (b, h), ``SeedSequence([seed, 3, b])`` draws the (Hq, Dk) queries of row b.
-All draws are float32; for bf16 workloads the float32 values are rounded to the
-nearest bf16 (ties to even) and handed over as uint16 bit patterns.
+All draws are float32; for bf16 (fp16) workloads the float32 values are rounded to
+the nearest bf16 (fp16), ties to even, and handed over as uint16 bit patterns.
 """
 
 from concurrent.futures import ThreadPoolExecutor
@@ -62,6 +62,8 @@ def _to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
         return x.astype(np.float32, copy=False)
     if dtype == "bf16":
         return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)   # numpy rounds to nearest, ties to even
     raise ValueError(dtype)
 
 
