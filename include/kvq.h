@@ -199,6 +199,22 @@ int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq
                       float* out, void* stream, void* event_after_decode);
 
 /*
+ * kv_decode_attn_noalloc — kv_decode_attn for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace, and the same kernels.
+ * The partial results go to a static device array of KVQ_STATIC_SCRATCH_BYTES
+ * (16 MiB) that each GPU the library runs on holds until the process ends; the call
+ * allocates nothing.  A request whose partial results exceed it (B * Hq * units *
+ * (Dv + 4) floats, units from kvq_decode_plan; nothing when units == 1) returns
+ * KVQ_ERR_UNSUPPORTED before any launch.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on the GPU (other streams, other threads) race and
+ * give wrong results; calls enqueued on one stream are ordered and safe.
+ */
+enum { KVQ_STATIC_SCRATCH_BYTES = 16 << 20 };
+int kv_decode_attn_noalloc(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache,
+                           float softmax_scale, int num_partitions, float* out, void* stream);
+
+/*
  * kvq_decode_plan — which decode kernel kv_decode_attn (with_side_code = 0) or
  * kv_decode_attn_side (with_side_code != 0) runs for this layout and partition
  * count on the calling thread's current device, and how it cuts the work.  No GPU

@@ -167,6 +167,25 @@ def kv_decode_attn(layout: Layout, q, cache, num_partitions: int = 1, softmax_sc
     return out
 
 
+def kv_decode_attn_noalloc(layout: Layout, q, cache, num_partitions: int = 1, softmax_scale=None, out=None,
+                           stream=None):
+    """kv_decode_attn without a workspace (C ABI kv_decode_attn_noalloc): the partial
+    results go to the library's static per-GPU scratch, so the call allocates no
+    device memory when ``out`` is given.  Calls that overlap on one GPU race."""
+    _check_tensor("q", q, (layout.B, layout.Hq, layout.Dk))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(layout.Dk)
+    if out is None:
+        out = torch.empty((layout.B, layout.Hq, layout.Dv), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (layout.B, layout.Hq, layout.Dv) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor [B, Hq, Dv]")
+    cs = _cache_struct(layout, cache)
+    L_.check(L_.load().kv_decode_attn_noalloc(layout.ref, ctypes.c_void_p(q.data_ptr()), _DTYPE_CODES[q.dtype],
+                                              ctypes.byref(cs), ctypes.c_float(softmax_scale), num_partitions,
+                                              ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+    return out
+
+
 def kvq_read_probe(buf, sink=None, stream=None):
     """Measurement support: read the bytes of the contiguous device tensor ``buf``
     once with a plain streaming read (C ABI kvq_read_probe), so that the caller can

@@ -19,7 +19,7 @@ ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["kvq_api.cpp", "kvq_stream.cpp", "kvq_pack.hip", "kvq_append.hip", "kvq_decode_generic.hip",
            "kvq_decode_mfma.hip", "kvq_decode_merge.hip",
-           "kvq_probe.hip"]
+           "kvq_probe.hip", "kvq_scratch.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-x", "hip",

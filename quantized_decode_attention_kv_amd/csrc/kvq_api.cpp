@@ -332,6 +332,17 @@ int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq
                           workspace_bytes, out, stream, event_after_decode);
 }
 
+int kv_decode_attn_noalloc(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache,
+                           float softmax_scale, int num_partitions, float* out, void* stream) {
+  const int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  void* scratch = nullptr;
+  const hipError_t e = kvq::static_scratch(&scratch);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+  return kvq::decode_view(*L, L->n_groups, L->R, q, q_dtype, cache, softmax_scale, num_partitions, scratch,
+                          KVQ_STATIC_SCRATCH_BYTES, out, stream, nullptr, nullptr, KVQ_ERR_UNSUPPORTED);
+}
+
 int kvq_decode_plan(const kvq_layout* L, int num_partitions, int with_side_code, kvq_decode_info* info) {
   int st = check_layout(L);
   if (st != KVQ_OK) return st;

@@ -102,6 +102,10 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
+// Device address of the static scratch array on the current device (looked up
+// once per device; kv_decode_attn_noalloc).
+hipError_t static_scratch(void** ptr);
+
 // Current device and its compute-unit count (the attribute is read once per device
 // and kept).
 hipError_t device_cus(int* dev, int* cus);
