@@ -12,7 +12,12 @@ the algorithmic bytes of the step (each packed byte, scale, zero, fp16 row, quer
 and output moved once; the prefill chunk read once and its packed form written
 once) divided by the measured step time.
 
-Beside the step (not part of ``value``), the ``stream`` object times the streaming
+Beside the step (not part of ``value``), the ``configs`` object times decode alone on
+the other workloads of the list (the Llama-8B-shaped 4096-token cache, the 32K-token
+cache with log-spaced fp16 tokens and the thin-key 16K-token cache), each call after
+an untimed cache-evicting read, with its own roofline and CPU baseline; the
+``valu_variants`` object times the formats that decode on the vector-ALU kernel
+(1- and 3-bit codes, the HeadQ side code) at the 128K shape; the ``stream`` object times the streaming
 cache at the same shape: after a prefill to just under the full length, decode
 steps that append one token per sequence (kv_stream_append) and then attend over
 the stream (kv_stream_decode), each call bracketed by events; the
@@ -82,18 +87,31 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per decode launch from the committed counter summary, if it was taken
+def _profile_value(path, key):
+    """A figure ``key: value`` of a committed profile summary, if the summary was taken
     on the current decode kernel source (else None)."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    t = re.search(r"%s:\s*([0-9.eE+]+)" % re.escape(key), text)
     if not h or not t or h.group(1) != kernel_source_hash():
         return None
     return float(t.group(1))
+
+
+def read_traffic(name="long_128k"):
+    """HBM bytes per decode launch on a workload from the committed counter summary,
+    if it was taken on the current decode kernel source (else None)."""
+    path = TRAFFIC_FILE if name == "long_128k" else os.path.join(ROOT, "profiles", "decode_%s_hbm_traffic.txt" % name)
+    return _profile_value(path, "hbm_bytes_per_launch")
+
+
+def read_rocprof_us(name):
+    """Mean decode-kernel duration (us) that rocprofv3 measured on a workload, from the
+    committed kernel-trace summary, if taken on the current decode source (else None)."""
+    return _profile_value(os.path.join(ROOT, "profiles", "decode_%s_kernel_trace.txt" % name), "decode_kernel_avg_us")
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -140,9 +158,10 @@ def _oracle_pack_chunk(O, s, w, t0):
                        k_group=w.k_group)
 
 
-def cpu_baseline(w, step_bytes, budget_workers=None):
+def cpu_baseline(w, step_bytes, budget_workers=None, max_workers=16):
     import multiprocessing as mp
-    cores = budget_workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    cores = budget_workers or max(1, min(max_workers, affinity))
     slabs = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     per = [slabs[i::cores] for i in range(cores)]
     per = [p[:1] for p in per if p]          # one slab per worker: about 1-2 s of oracle work each
@@ -158,14 +177,15 @@ def cpu_baseline(w, step_bytes, budget_workers=None):
         "value": covered / busiest / 1e9,
         "unit": "GB/s",
         "cores": len(per),
+        "host_cpus": affinity,
         "kind": "oracle",
         "sample": ("%d of %d (batch, kv-head) slabs of the step, one per worker process (1 BLAS thread each): "
                    "%sfloat64 decode over the whole %d-token slab; throughput = the slabs' share of the step's "
                    "algorithmic bytes / the busiest worker's oracle time (%.2f s; %.1f s wall incl. input "
-                   "generation and the untimed full-slab pack)"
+                   "generation and the untimed full-slab pack; workers capped at %d of the host's %d CPUs)"
                    % (n_slabs, w.B * w.Hkv,
                       ("oracle pack of the %d-token prefill chunk + " % w.prefill_chunk) if w.prefill_chunk else "",
-                      w.T, busiest, wall)),
+                      w.T, busiest, wall, max_workers, affinity)),
     }
 
 
@@ -299,24 +319,139 @@ def decode_cold(torch, api, lay, cache, qd, P, scale, dev, reps=20):
     """Decode kernel time with nothing of the cache left in the caches: before each
     call an untimed plain read of 1 GiB (four times the 256 MB memory-side cache)
     evicts it.  A read, not a write: freshly written lines would be written back
-    inside the decode.  Events bracket the decode kernel."""
+    inside the decode.  Events bracket the decode kernel and the whole call."""
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     sink = torch.empty(1, dtype=torch.int32, device=dev)
     ws = api.alloc_workspace(lay, P, dev)
     out = torch.empty((lay.B, lay.Hq, lay.Dv), dtype=torch.float32, device=dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
     for e in ev:
-        e[1].record()
+        for x in e:
+            x.record()
     torch.cuda.synchronize()
     for i in range(reps):
         api.kvq_read_probe(flush, sink)
         ev[i][0].record()
         api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws,
                            after_decode_event=ev[i][1])
+        ev[i][2].record()
     torch.cuda.synchronize()
     del flush
-    return {"kernel_us_p10_p50_p90": percentiles([e[0].elapsed_time(e[1]) for e in ev]),
+    kern = [e[0].elapsed_time(e[1]) for e in ev]
+    call = [e[0].elapsed_time(e[2]) for e in ev]
+    return {"kernel_us_p10_p50_p90": percentiles(kern), "kernel_us_mean": round(sum(kern) * 1e3 / reps, 2),
+            "call_us_p10_p50_p90": percentiles(call), "call_us_mean": round(sum(call) * 1e3 / reps, 2),
             "how": "1 GiB untimed read before each of %d calls" % reps}
+
+
+# Decode alone on the other workloads of the list (each its own cache).
+DECODE_CONFIGS = ["llama8b_gqa_4k", "logquant_32k", "thin_keys_16k"]
+
+
+def describe(w, P):
+    return ("%s: B%d Hq%d Hkv%d Dk%d Dv%d T%d K%dV%d fp16-window %d log-window %d, %d partitions"
+            % (w.name, w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T, w.k_bits, w.v_bits, w.n_recent, w.log_window, P))
+
+
+def decode_config(torch, api, name, dev, reps, with_cpu):
+    """Decode on one workload: cache packed once (untimed), then calls timed after a
+    cache-evicting read (decode_cold); roofline of the decode kernel from the mean
+    event time, beside rocprofv3's mean from the committed summary when current."""
+    from workloads import workload
+    from workloads.device import upload_workload
+    w = workload(name)
+    P = w.partitions
+    print("# %s: generating inputs" % name, file=sys.stderr, flush=True)
+    Kd, Vd, qd = upload_workload(w)
+    lay = api.Layout.from_workload(w)
+    cache = api.kv_quant_pack(lay, Kd, Vd)
+    del Kd, Vd
+    plan = api.decode_plan(lay, P)
+    scale = 1.0 / (w.Dk ** 0.5)
+    for _ in range(3):
+        api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale)
+    torch.cuda.synchronize()
+    print("# %s: decode, %d cold calls" % (name, reps), file=sys.stderr, flush=True)
+    cold = decode_cold(torch, api, lay, cache, qd, P, scale, dev, reps)
+    db = decode_bytes(w, lay.R, lay.Tq)
+    kern_us = cold["kernel_us_mean"]
+    call_us = cold["call_us_mean"]
+    achieved = db / (kern_us * 1e-6) / 1e9
+    rp_us = read_rocprof_us(name)
+    res = {
+        "workload": describe(w, P),
+        "plan": plan,
+        "algorithmic_bytes": db,
+        "decode": {"kernel": cold, "GBps_call": round(db / (call_us * 1e-6) / 1e9, 1),
+                   "steps_per_s": round(1e6 / call_us, 1), "tokens_per_s": round(w.B * 1e6 / call_us, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": read_traffic(name),
+                     "kernel": "decode_%s_kernel (first kernel of kv_decode_attn)" % plan["kernel"],
+                     "kernel_us": kern_us, "timing": "HIP events, mean over the cold calls",
+                     "rocprof_kernel_us": rp_us,
+                     "frac_rocprof": None if rp_us is None else round(db / (rp_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+    }
+    del cache
+    torch.cuda.empty_cache()
+    if with_cpu:
+        print("# %s: cpu baseline (oracle)" % name, file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, db)
+    return res
+
+
+def valu_setup(torch, api, w, Kd, Vd, dev):
+    """Caches of the formats that decode on the vector-ALU kernel, at the workload's
+    shape: 1- and 3-bit codes and the HeadQ side code (rank 8, 8-bit side codes, a
+    random orthonormal basis per KV head), next to K4V4 on the matrix-core kernel.
+    Each is packed once (untimed set-up)."""
+    import numpy as np
+    caches = {}
+    for name, kb, vb in (("k1v1", 1, 1), ("k3v3", 3, 3), ("k4v4", 4, 4)):
+        wv = w.with_(k_bits=kb, v_bits=vb)
+        lv = api.Layout.from_workload(wv)
+        caches[name] = (wv, lv, api.kv_quant_pack(lv, Kd, Vd), None)
+    rank = 8
+    rng = np.random.default_rng(7)
+    U = np.stack([np.linalg.qr(rng.standard_normal((w.Dk, rank)))[0] for _ in range(w.Hkv)]).astype(np.float32)
+    Ud = torch.from_numpy(U).to(dev)
+    ls = api.Layout.from_workload(w)
+    cs = api.kv_quant_pack(ls, Kd, Vd)
+    side = api.side_pack(ls, Kd, cs, Ud, side_bits=8)
+    caches["k%dv%d_side_r%d" % (w.k_bits, w.v_bits, rank)] = (w, ls, cs, (Ud, side))
+    return caches
+
+
+def valu_run(torch, api, w, caches, qd, P, scale, dev, reps=10):
+    """Decode over each cache of valu_setup, calls interleaved one by one; events
+    around each call (decode kernel and merge)."""
+    rank = 8
+    out = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.float32, device=dev)
+    ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)] for k in caches}
+    for k in caches:
+        for e in ev[k]:
+            e[0].record()
+            e[1].record()
+    torch.cuda.synchronize()
+    for i in range(reps):
+        for k, (wv, lv, c, sd) in caches.items():
+            ev[k][i][0].record()
+            if sd is None:
+                api.kv_decode_attn(lv, qd, c, num_partitions=P, softmax_scale=scale, out=out)
+            else:
+                api.kv_decode_attn_side(lv, qd, c, sd[0], sd[1], num_partitions=P, softmax_scale=scale)
+            ev[k][i][1].record()
+    torch.cuda.synchronize()
+    res = {}
+    for k, (wv, lv, c, sd) in caches.items():
+        ts = [e[0].elapsed_time(e[1]) for e in ev[k]]
+        p = percentiles(ts)
+        db = decode_bytes(wv, lv.R, lv.Tq)
+        if sd is not None:   # side codes (one byte each), their fp16 scale and zero, and the basis
+            db += w.B * w.Hkv * lv.Tq * (rank + 4) + w.Hkv * w.Dk * rank * 4
+        res[k] = {"kernel": api.decode_plan(lv, P, side_code=sd is not None)["kernel"],
+                  "decode_call_us_p10_p50_p90": p, "algorithmic_bytes": db,
+                  "GBps_at_p50": round(db / (p[1] * 1e-6) / 1e9, 1)}
+    return res
 
 
 def percentiles(xs):
@@ -338,6 +473,11 @@ def main():
     ap.add_argument("--stream-steps", type=int, default=256)
     ap.add_argument("--no-variants", action="store_true", help="skip the format-variants leg")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-cold decode leg")
+    ap.add_argument("--no-valu", action="store_true", help="skip the vector-ALU formats leg")
+    ap.add_argument("--no-configs", action="store_true", help="skip the decode legs of the other workloads")
+    ap.add_argument("--configs", default=",".join(DECODE_CONFIGS),
+                    help="comma-separated workloads of the decode-only legs")
+    ap.add_argument("--config-reps", type=int, default=30, help="timed cold calls per decode-only leg")
     ap.add_argument("--v-group", type=int, default=None, help="channels per value group of the step (default 32)")
     ap.add_argument("--k-group", type=int, default=None, help="tokens per key group of the step (default 32)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -374,6 +514,7 @@ def main():
         Vc = Vd[:, :, t0:].contiguous()
     stream = None if args.no_stream else stream_setup(torch, api, w, Kd, Vd, args.stream_steps)
     variants = None if args.no_variants else variants_setup(api, w, Kd, Vd, lay, cache)
+    valu = None if args.no_valu else valu_setup(torch, api, w, Kd, Vd, dev)
     del Kd, Vd
     ws = api.alloc_workspace(lay, P, dev)
     out = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.float32, device=dev)
@@ -440,6 +581,7 @@ def main():
     dec_gbps = db / (dec_ms * 1e-3) / 1e9
     kern_gbps = db / (kern_ms * 1e-3) / 1e9
     traffic = read_traffic()
+    rp_us = read_rocprof_us(w.name) if (w.k_group, w.v_group) == (32, 32) and args.partitions is None else None
     ceiling = read_ceiling(torch, api, db, dev)
     cold = None if args.no_cold else decode_cold(torch, api, lay, cache, qd, P, scale, dev)
 
@@ -455,6 +597,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "dtype_detail": "float32 accumulation and softmax; the matrix-core products take fp16 operands, codes exact "
+                        "and the folded scales q*s and p*s split into fp16 hi + lo parts (about 22 significant bits)",
         "data": "synthetic: seeded N(0,1) keys with 4 outlier channels x8 and per-channel N(0,2) offsets, "
                 "N(0,0.5) values, N(0,1) queries; bf16 in HBM",
         "config": {
@@ -481,6 +625,10 @@ def main():
                      "frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "decode_mfma_kernel (first kernel of kv_decode_attn)",
                      "kernel_us": round(kern_ms * 1e3, 2),
+                     "timing": "HIP events: before the decode call to after its decode kernel (includes the "
+                               "dispatch gap), mean over the timed steps",
+                     "rocprof_kernel_us": rp_us,
+                     "frac_rocprof": None if rp_us is None else round(db / (rp_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                      "kernel_source_sha256_16": kernel_source_hash()},
     }
     if stream is not None:
@@ -489,6 +637,16 @@ def main():
     if variants is not None:
         print("# %s: format variants" % w.name, file=sys.stderr, flush=True)
         result["format_variants"] = variants_run(torch, api, w, variants, qd, P, scale)
+    if valu is not None:
+        print("# %s: vector-ALU formats" % w.name, file=sys.stderr, flush=True)
+        result["valu_variants"] = valu_run(torch, api, w, valu, qd, P, scale, dev)
+    del cache, variants, valu, stream, ws
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        result["configs"] = {}
+        for name in [c for c in args.configs.split(",") if c and c != w.name]:
+            result["configs"][name] = decode_config(torch, api, name, dev, args.config_reps,
+                                                    not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         print("# %s: cpu baseline (oracle)" % w.name, file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, step_bytes)
