@@ -425,19 +425,38 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   float* PT = reinterpret_cast<float*>(smem + LL::kSlot);      // [4][32], retained rows
   const int lane = int(threadIdx.x) & 63, n = lane & 15, gq = lane >> 4;
 
-  // unit-major grid of waves: wave L = 4 block + wave takes unit L / slabs of slab
-  // L % slabs (the last block may hold waves past the grid, which leave at once)
+  // Teams.  When the unit count is a multiple of 4, the 4 waves of a workgroup are
+  // the 4 units of one team, which shares one run of key groups of one slab: wave w
+  // takes groups first + w, first + w + 4, ..., so the workgroup reads 4
+  // consecutive groups at a time (measured: the memory system streams the cache
+  // about 7% faster this way than as 4 separate runs).  The grid is team-major:
+  // workgroup L is team L / slabs of slab L % slabs.  Otherwise each wave is a team
+  // of its own and the grid is unit-major: wave L = 4 block + wave is unit L / slabs
+  // of slab L % slabs (the last block may hold waves past the grid, which leave at
+  // once).
   const int U = a.units, slabs = a.L.B * a.L.Hkv;
-  const int gw = int(blockIdx.x) * kWavesPerGroup + wave;
-  const int unit = gw / slabs, sl = gw % slabs;
+  const int TS = (U % kWavesPerGroup) == 0 ? kWavesPerGroup : 1;  // waves per team
+  int team, unit, sl;
+  if (TS == kWavesPerGroup) {
+    team = int(blockIdx.x) / slabs;
+    sl = int(blockIdx.x) % slabs;
+    unit = team * kWavesPerGroup + wave;
+  } else {
+    const int gw = int(blockIdx.x) * kWavesPerGroup + wave;
+    team = unit = gw / slabs;
+    sl = gw % slabs;
+  }
   if (unit >= U) return;
   const int h = sl % a.L.Hkv, b = sl / a.L.Hkv;
   const int nG = a.L.n_groups, R = a.L.R;
   const int64_t slab = int64_t(b) * a.L.Hkv + h;
-  const int g0 = unit_start(unit, U, nG, a.ranks), g1 = unit_start(unit + 1, U, nG, a.ranks);
+  // the team's run [tg0, tg1); this wave's groups are g0 + TS j, j < nj
+  const int T = U / TS;
+  const int tg0 = unit_start(team, T, nG, a.ranks), tg1 = unit_start(team + 1, T, nG, a.ranks);
+  const int g0 = tg0 + (unit - team * TS);
+  const int nj = g0 < tg1 ? (tg1 - g0 + TS - 1) / TS : 0;
   const int nRT = (R + 31) / 32;  // 32-row tiles of retained rows
   const int rt0 = int(int64_t(unit) * nRT / U), rt1 = int(int64_t(unit + 1) * nRT / U);
-  const int nj = g1 - g0;
 
   // per-slab bases (wave-uniform)
   const uint8_t* kbase = static_cast<const uint8_t*>(a.cache.k_codes) + slab * a.g_stride * (KVQ_GROUP * KROW);
@@ -473,10 +492,16 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   //   zeros into the unused part of the array's 256-byte area).
   // Every copy is a buffer load with all lanes active, so the wave's copies
   // complete in issue order and the waits below can count them.
+  // Key rows of 32 bytes (8 bytes per lane and tile) are the exception: the
+  // group's 1 KB of key codes is one 16-byte copy per lane (four 4-byte pieces
+  // measured about 6% slower to stream).  Copy lane i = 16 (2 tt + h) + 4 j + q
+  // fetches half h of row 8 j + 4 tt + q, so the lanes that read tile tt, half h
+  // find their 16 rows in 16 consecutive 16-byte places (conflict-free 8-byte reads).
   constexpr int KPB = KLB >= 16 ? 16 : 4;   // bytes per key piece
   constexpr int KNP = KLB / KPB;            // key pieces per tile
   constexpr int VNP = VLW / 4;              // value pieces
-  constexpr int kDmas = 2 * KNP + VNP + 4;  // copies per group
+  constexpr bool KLIN = KROW == 32;         // the group's key codes as one copy in memory order
+  constexpr int kDmas = (KLIN ? 1 : 2 * KNP) + VNP + 4;  // copies per group
   constexpr int oKZ = LL::kStS, oVS = 2 * LL::kStS, oVZ = 3 * LL::kStS;  // scale area offsets
   static_assert(DK * 2 <= LL::kStS && DV * 2 == LL::kStS, "scale area");
   static_assert((D - 1) * kDmas < 64 && D >= 2, "vmcnt");
@@ -485,6 +510,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   uint32_t koff[2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) koff[tt] = uint32_t(8 * (n >> 2) + 4 * tt + (n & 3)) * KROW + gq * KLB;
+  const uint32_t klin = uint32_t(8 * ((lane >> 2) & 3) + 4 * (lane >> 5) + (lane & 3)) * 32u + 16u * ((lane >> 4) & 1);
   const uint32_t voff = uint32_t(lane) * (VLW * 4);
   // scale copies: byte offset of this lane's dword (past the end for surplus lanes)
   const uint32_t kso = lane < DK / 2 ? uint32_t(lane) * 4 : 0x80000000u;
@@ -498,10 +524,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   auto stage_group = [&](int g, int slot) {
     unsigned char* sb = stage + slot * LL::kSlot;
     const uint32_t gk = uint32_t(g) * (32 * KROW);
+    if constexpr (KLIN) {
+      lds_dma<16>(rk, klin, gk, sb);
+    } else {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-      for (int hp = 0; hp < KNP; ++hp) lds_dma<KPB>(rk, koff[tt] + hp * KPB, gk, sb + (tt * KNP + hp) * 64 * KPB);
+        for (int hp = 0; hp < KNP; ++hp) lds_dma<KPB>(rk, koff[tt] + hp * KPB, gk, sb + (tt * KNP + hp) * 64 * KPB);
+      }
     }
     const uint32_t gv = uint32_t(g) * (DV * VB * 4);
 #pragma unroll
@@ -527,7 +557,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   const u32x4 qw0 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff, 0, 0);
   const u32x4 qw1 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 16, 0, 0);
 #pragma unroll
-  for (int u = 0; u < D; ++u) stage_group(g0 + min(u, nj > 0 ? nj - 1 : 0), u);
+  for (int u = 0; u < D; ++u) stage_group(g0 + TS * min(u, nj > 0 ? nj - 1 : 0), u);
   __builtin_amdgcn_sched_barrier(0);
   float qx[8];
   if (a.q_dtype == KVQ_BF16) {
@@ -701,15 +731,23 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
     const unsigned char* sb = stage + slot * LL::kSlot;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
+      if constexpr (KLIN) {
+        // two 4-byte reads: with one 8-byte read the compiler cannot tell it from
+        // the copies in flight and waits for all of them
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(sb + (32 * tt + 16 * (gq >> 1) + n) * 16 + 8 * (gq & 1));
+        d.kw[tt][0] = src[0];
+        d.kw[tt][1] = src[1];
+      } else {
 #pragma unroll
-      for (int hp = 0; hp < KNP; ++hp) {
-        const unsigned char* src = sb + (tt * KNP + hp) * 64 * KPB + lane * KPB;
-        if constexpr (KPB == 16) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+        for (int hp = 0; hp < KNP; ++hp) {
+          const unsigned char* src = sb + (tt * KNP + hp) * 64 * KPB + lane * KPB;
+          if constexpr (KPB == 16) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) d.kw[tt][4 * hp + e] = w[e];
-        } else {
-          d.kw[tt][hp] = *reinterpret_cast<const uint32_t*>(src);
+            for (int e = 0; e < 4; ++e) d.kw[tt][4 * hp + e] = w[e];
+          } else {
+            d.kw[tt][hp] = *reinterpret_cast<const uint32_t*>(src);
+          }
         }
       }
     }
@@ -798,9 +836,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   {
     // Step i takes key group i from ring position i % D.  The prologue filled
     // positions 0 .. D - 1.  With D > 2 the copies of group i - 1 + D go to the
-    // position step i - 1 was read from, once group i has been waited for: those
-    // reads have been consumed, so no wait on LDS is needed, and groups i + 1 ..
-    // i + D - 2 stay in flight while group i is computed.  With D == 2 step i's
+    // position step i - 1 was read from, before the wait for group i: those reads
+    // have been consumed, so no wait on LDS is needed, and groups i + 1 ..
+    // i + D - 1 stay in flight while the wave waits for group i.  With D == 2 step i's
     // own position takes the copies of group i + 2 right after it has been read
     // (after a wait for the reads).  Past the end of a short run the prologue
     // re-reads its last group, which is always in bounds.  The last step waits
@@ -817,20 +855,23 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
       if (i == q2) __builtin_amdgcn_s_setprio(1);
       if (i == q3) __builtin_amdgcn_s_setprio(0);
       if constexpr (D > 2) {
-        // copies issued beyond step i: the prologue's D - 1 at i == 0, later at
-        // most D - 2 (fewer near the end of the run)
-        wait_steps_ahead<kDmas, D - 1>(i == 0 ? min(D - 1, ns - 1) : min(D - 2, ns - 1 - i));
-      } else {
-        wait_steps_ahead<kDmas, D - 1>(min(D - 1, ns - 1 - i));
+        // the position step i - 1 computed from is free (its reads were consumed
+        // there): it takes group i - 1 + D before the wait, so D - 1 later groups
+        // are in flight while the wave waits for group i
+        const int prev = (i + D - 1) % D;
+        if (i >= 1 && i - 1 + D < ns) {
+          wave_lds_order();
+          stage_group(g0 + TS * (i - 1 + D), prev);
+        }
       }
+      // copy steps issued after group i: D - 1 (fewer near the end of the run;
+      // waiting for more than needed there is harmless)
+      wait_steps_ahead<kDmas, D - 1>(min(D - 1, ns - 1 - i));
       GroupLoads d;
       read_group(pos, d);
-      if constexpr (D > 2) {
-        const int prev = (i + D - 1) % D;
-        if (i >= 1 && i - 1 + D < ns) stage_group(g0 + i - 1 + D, prev);
-      } else {
+      if constexpr (D == 2) {
         wave_lds_sync();
-        if (i + D < ns) stage_group(g0 + i + D, pos);
+        if (i + D < ns) stage_group(g0 + TS * (i + D), pos);
       }
       // the Q' / P' tiles overwrite the slot just read: LDS keeps the wave's
       // order, the compiler must keep it too
