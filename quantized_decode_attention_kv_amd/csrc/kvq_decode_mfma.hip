@@ -359,31 +359,52 @@ __device__ __forceinline__ float pick4(const float (&x)[kG], int i) {
   return i == 0 ? x[0] : (i == 1 ? x[1] : (i == 2 ? x[2] : x[3]));
 }
 
-// One workgroup = one wave = one unit: a contiguous piece of a split-K partition
-// of one (batch, kv head) slab (the whole slab when P == 1).  Units are
-// independent: no barriers, and each writes its own partial result.
-// First key group of unit u of U over nG groups, for R waves per SIMD.  The
+// Work units.  A unit is one wave; a team is TS units (4, one workgroup, or 1)
+// that share a contiguous run of key groups of one (batch, kv head) slab.  Units
+// are independent: no barriers, and each writes its own partial result.
+//
+// First key group of team t of T over nG groups, for R waves per SIMD.  The
 // workgroup dispatcher fills the SIMDs round-robin in grid order, so with the
-// unit-major grid and one unit per resident wave the units u < U/R become the
-// oldest wave on their SIMD, the next U/R the second oldest, and so on; waves are
-// served oldest first, so unit sizes fall by rank (integer weights
+// team-major grid and one team per resident workgroup the teams t < T/R become
+// the oldest waves on their SIMDs, the next T/R the second oldest, and so on;
+// waves are served oldest first, so run lengths fall by rank (integer weights
 // 100 + s (R - 1 - 2 r) for rank r, s = 16 / (R - 1): the oldest and youngest
 // rank differ by +-16%, measured on the 128K workload to bring the finish times
-// of the two waves of a SIMD within a few microseconds) and the waves of a SIMD
-// finish closer together.  Any weights give the same result up to rounding.
+// of the two waves of a SIMD within a few microseconds).
+// Retained fp16 rows come in 32-row tiles; unit u takes tiles u, u + U, ..., so
+// the waves of a team take the same number of tiles (tq, plus one in the first
+// ceil(tm / TS) teams, tm = tiles % U), and a team's run is shortened by what its
+// waves spend on tiles: teams share nG plus the tiles' cost (tc16 sixteenths of a
+// group per tile and wave) by rank weight, less their own tiles' cost.  The
+// cost is capped so that every team keeps at least one group per rank weight
+// unit's share, which keeps the starts increasing.  Any split gives the same
+// result up to rounding.
 #ifndef KVQ_UNIT_SKEW_SPAN
 #define KVQ_UNIT_SKEW_SPAN 16
 #endif
-__device__ __forceinline__ int unit_start(int u, int U, int nG, int R) {
+__device__ __forceinline__ int team_start(int t, int T, int TS, int nG, int R, int tq, int tm, int tc16) {
   const int64_t s = R > 1 ? KVQ_UNIT_SKEW_SPAN / (R - 1) : 0;
-  int64_t wu = 0, wall = 0;
+  int64_t wb = 0, wall = 0;
   for (int r = 0; r < R; ++r) {
-    const int64_t lo = (int64_t(r) * U + R - 1) / R, hi = (int64_t(r + 1) * U + R - 1) / R;  // units of rank r
+    const int64_t lo = (int64_t(r) * T + R - 1) / R, hi = (int64_t(r + 1) * T + R - 1) / R;  // teams of rank r
     const int64_t w = 100 + s * (R - 1 - 2 * r);
     wall += w * (hi - lo);
-    wu += w * (u < lo ? 0 : (u < hi ? u - lo : hi - lo));
+    wb += w * (t < lo ? 0 : (t < hi ? t - lo : hi - lo));
   }
-  return int(int64_t(nG) * wu / wall);
+  const int64_t tmt = (tm + TS - 1) / TS;            // teams whose waves take tq + 1 tiles
+  const int64_t emax = tq + (tmt > 0 ? 1 : 0);       // most tiles a wave takes
+  int64_t c = tc16;
+  if (emax > 0) {
+    // every team's share stays >= 1 group: 16 nG wmin / wall - TS c emax >= 16
+    const int64_t wmin = 100 - s * (R - 1);
+    const int64_t room = (16 * int64_t(nG) * wmin) / wall - 16;
+    c = room > 0 ? min(c, room / (int64_t(TS) * emax)) : 0;
+  }
+  const int64_t e_before = int64_t(t) * tq + min(int64_t(t), tmt);
+  const int64_t e_all = int64_t(T) * tq + min(int64_t(T), tmt);
+  const int64_t w16 = 16 * int64_t(nG) + int64_t(TS) * c * e_all;
+  const int64_t st16 = w16 * wb / wall - int64_t(TS) * c * e_before;
+  return int(max(int64_t(0), min(int64_t(nG), st16 / 16)));
 }
 
 // Waves per SIMD that the LDS of one unit allows on a 160 KB compute unit (at most
@@ -452,11 +473,19 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   const int64_t slab = int64_t(b) * a.L.Hkv + h;
   // the team's run [tg0, tg1); this wave's groups are g0 + TS j, j < nj
   const int T = U / TS;
-  const int tg0 = unit_start(team, T, nG, a.ranks), tg1 = unit_start(team + 1, T, nG, a.ranks);
+  // retained tiles: this unit takes tiles unit, unit + U, ... (tq or tq + 1 of them)
+  const int nRT = (R + 31) / 32;  // 32-row tiles of retained rows
+  const int tq = nRT / U, tm = nRT % U;
+  // cost of a tile in sixteenths of a key group (measured: about 2.5 groups' time
+  // where a tile is 4 groups' bytes, so 5/8 of the byte ratio)
+  constexpr int64_t kTileBytes = 32 * (DK + DV) * 2;
+  const int64_t group_bytes = 32 * (DK * KB + DV * VB) / 8 + ((DK * 4) >> (a.L.k_group == 128 ? 2 : (a.L.k_group == 64 ? 1 : 0))) +
+                              ((DV / 32 * 32 * 4) >> (a.L.v_group == 128 ? 2 : (a.L.v_group == 64 ? 1 : 0)));
+  const int tc16 = int(16 * 5 * kTileBytes / (8 * group_bytes));
+  const int tg0 = team_start(team, T, TS, nG, a.ranks, tq, tm, tc16);
+  const int tg1 = team_start(team + 1, T, TS, nG, a.ranks, tq, tm, tc16);
   const int g0 = tg0 + (unit - team * TS);
   const int nj = g0 < tg1 ? (tg1 - g0 + TS - 1) / TS : 0;
-  const int nRT = (R + 31) / 32;  // 32-row tiles of retained rows
-  const int rt0 = int(int64_t(unit) * nRT / U), rt1 = int(int64_t(unit + 1) * nRT / U);
 
   // per-slab bases (wave-uniform)
   const uint8_t* kbase = static_cast<const uint8_t*>(a.cache.k_codes) + slab * a.g_stride * (KVQ_GROUP * KROW);
@@ -891,7 +920,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   // After the key groups (the order of tokens does not matter): the ring is idle
   // (the last group waited for every copy) and holds the probabilities PT; the
   // Q' tile takes the q hi/lo operand B2 again.
-  if (rt0 < rt1) {
+  if (unit < nRT) {
     // B2: q 2^-E split hi/lo, entry (kk*4 + gq)*8 + i + 4*part, channels of block
     // gq*KK + kk in natural order (dword d = channels 2d, 2d+1); query i = e % 4
     // is this lane's query
@@ -912,7 +941,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
     wave_lds_sync();
     const uint8_t* kr = static_cast<const uint8_t*>(a.cache.k_fp16) + slab * a.r_stride * (DK * 2);
     const uint8_t* vr = static_cast<const uint8_t*>(a.cache.v_fp16) + slab * a.r_stride * (DV * 2);
-    for (int rt = rt0; rt < rt1; ++rt) {
+    for (int rt = unit; rt < nRT; rt += U) {
       const int rbase = rt * 32;
       f32x4 sacc[2];
 #pragma unroll
