@@ -376,9 +376,8 @@ __device__ __forceinline__ float pick4(const float (&x)[kG], int i) {
 // ceil(tm / TS) teams, tm = tiles % U), and a team's run is shortened by what its
 // waves spend on tiles: teams share nG plus the tiles' cost (tc16 sixteenths of a
 // group per tile and wave) by rank weight, less their own tiles' cost.  The
-// cost is capped so that every team keeps at least one group per rank weight
-// unit's share, which keeps the starts increasing.  Any split gives the same
-// result up to rounding.
+// cost is capped so that every team keeps at least one group, which keeps the
+// starts increasing.  Any split gives the same result up to rounding.
 #ifndef KVQ_UNIT_SKEW_SPAN
 #define KVQ_UNIT_SKEW_SPAN 16
 #endif
