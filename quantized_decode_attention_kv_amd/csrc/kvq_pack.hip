@@ -45,6 +45,7 @@ namespace {
 constexpr int kPackThreads = 256;
 constexpr int kPackWaves = kPackThreads / 64;
 constexpr int kRetRowsPerBlock = 4;
+constexpr int kRetRows128 = 32;  // retained rows per workgroup of pack128_kernel
 constexpr int kMaxPairBlocks = KVQ_MAX_HEAD_DIM / 128;  // 64-lane blocks of channel pairs
 
 template <int DT>
@@ -172,6 +173,32 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float 
   }
   rt = fminf(fmaxf(rt, 0.0f), levels);
   return uint32_t(rt);
+}
+
+// quant_code for N elements with one check: when no element's fast quotient lies
+// within 2^-12 of a half-integer (the usual case) no element takes the division, and
+// the wave tests that once instead of once per element.
+template <int N>
+__device__ __forceinline__ void quant_codes(const float (&x)[N], const float (&s)[N], const float (&z)[N],
+                                            const float (&r)[N], float levels, uint32_t (&code)[N]) {
+  float u[N], rt[N];
+  float worst = 0.0f;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    u[k] = x[k] - z[k];
+    const float t = u[k] * r[k];  // s == 0: r == 0, t == 0, code 0
+    rt[k] = __builtin_rintf(t);
+    worst = fmaxf(worst, fabsf(t - rt[k]));
+  }
+  if (__builtin_expect(worst > 0.5f - 1.0f / 4096.0f, 0)) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const float t = u[k] * r[k];
+      if (fabsf(t - rt[k]) > 0.5f - 1.0f / 4096.0f) rt[k] = __builtin_rintf(u[k] / s[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) code[k] = uint32_t(fminf(fmaxf(rt[k], 0.0f), levels));
 }
 
 // Every output of the pack is written with streaming (non-temporal) stores: the
@@ -444,6 +471,265 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
   }
 }
 
+// Pack kernel for the common shape: Dk = Dv = 128, 32-token key groups, 2/4/8-bit
+// codes, 16-bit inputs.  Same contract and outputs as pack_kernel; arranged so
+// that every load is a 16-byte row segment and the codes leave in whole words.
+// Workgroup = one key group; wave w holds tokens 8w..8w+7 (one octet of the value
+// code layout), lane (p = lane / 16, c = lane % 16) the channels 8c..8c+7 of the
+// token pair (8w + p, 8w + p + 4):
+//   keys    per-channel min / max: lane partials through LDS (16 per channel),
+//           reduced by one thread per channel, which also forms the scale and zero;
+//           each lane's 8 codes of a row are whole key-code bits of one word (4- and
+//           8-bit: 1 or 2 words; 2-bit: half a word, joined with the next lane), stored
+//           straight to the cache;
+//   values  per (token, v_group channels) min / max over the 8 lanes' quads (DPP),
+//           scale and zero formed by one lane per token of a quad; the lane's codes
+//           of tile c / 2, columns 8 (c % 2) + k, go to 8 words of its wave's octet in
+//           LDS (round k sends column k + t: the 8 lanes that share a word never write
+//           it in the same round), and each wave stores its octet's words itself.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT, int KB, int VB>
+__global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a) {
+  static_assert(DT != KVQ_F32 && (KB == 2 || KB == 4 || KB == 8) && (VB == 2 || VB == 4 || VB == 8), "shape");
+  constexpr int D = 128, kWords = D * KB / 32, vWords = D * VB;
+  constexpr int kChunkWords = VB / 2;             // words of a (octet, column, pair) field
+  constexpr int kTilesPerWord = 16 / VB;
+  __shared__ int32_t row_s[KVQ_GROUP];
+  __shared__ float4 kmn_s[16][D / 4], kmx_s[16][D / 4];   // lane partials: (wave, pair) x channel
+  __shared__ float4 ks_s[D / 4], kz_s[D / 4], kr_s[D / 4];
+  __shared__ uint32_t vw_s[vWords];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t slab = int64_t(b) * a.L.Hkv + h;
+  const RetentionRule rr{a.L.T, a.L.n_recent, a.L.log_window};
+
+  if (int64_t(blockIdx.x) >= a.n_groups_chunk) {
+    // retained rows -> fp16: kRetRows128 rows per workgroup, 16 threads per row, 8
+    // channels (one 16-byte load of K and of V) per thread
+    for (int i = tid; i < kRetRows128 * 16; i += kPackThreads) {
+      const int64_t j = (int64_t(blockIdx.x) - a.n_groups_chunk) * kRetRows128 + i / 16;
+      if (j >= a.n_ret_chunk) break;
+      const int c8 = 8 * (i % 16);
+      const int64_t r = a.r_begin + j;
+      const int64_t e = (slab * a.t_count + (retained_position(rr, r) - a.t_begin)) * D + c8;
+      const uint4 kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.K) + e);
+      const uint4 vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.V) + e);
+      const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
+      u32x4_t ko, vo;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (DT == KVQ_BF16) {
+          ko[k] = uint32_t(f16_bits_rne(__uint_as_float(kw[k] << 16))) |
+                  (uint32_t(f16_bits_rne(__uint_as_float(kw[k] & 0xFFFF0000u))) << 16);
+          vo[k] = uint32_t(f16_bits_rne(__uint_as_float(vw[k] << 16))) |
+                  (uint32_t(f16_bits_rne(__uint_as_float(vw[k] & 0xFFFF0000u))) << 16);
+        } else {  // fp16 rows are stored as they are
+          ko[k] = kw[k];
+          vo[k] = vw[k];
+        }
+      }
+      out_store(reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.cache.k_fp16) + (slab * a.r_stride + r) * D + c8), ko);
+      out_store(reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.cache.v_fp16) + (slab * a.r_stride + r) * D + c8), vo);
+    }
+    return;
+  }
+
+  const int64_t g = a.g_begin + blockIdx.x;
+  const bool plain = quantized_before(rr, (g + 1) * KVQ_GROUP) == (g + 1) * KVQ_GROUP;
+  if (!plain) {
+    if (tid < KVQ_GROUP) row_s[tid] = int32_t(quantized_position(rr, g * KVQ_GROUP + tid) - a.t_begin);
+    __syncthreads();
+  }
+  const int p = lane >> 4, c = lane & 15;
+  const int tok[2] = {8 * wave + p, 8 * wave + p + 4};
+  Raw16<DT> kraw[2], vraw[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t row = plain ? g * KVQ_GROUP + tok[j] - a.t_begin : row_s[tok[j]];
+    const int64_t e = (slab * a.t_count + row) * D + 8 * c;
+    const uint4 kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.K) + e);
+    const uint4 vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.V) + e);
+    kraw[j].w[0] = kv.x; kraw[j].w[1] = kv.y; kraw[j].w[2] = kv.z; kraw[j].w[3] = kv.w;
+    vraw[j].w[0] = vv.x; vraw[j].w[1] = vv.y; vraw[j].w[2] = vv.z; vraw[j].w[3] = vv.w;
+  }
+  float kx[2][8], vx[2][8];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (DT == KVQ_BF16) {
+        kx[j][2 * k] = __uint_as_float(kraw[j].w[k] << 16);
+        kx[j][2 * k + 1] = __uint_as_float(kraw[j].w[k] & 0xFFFF0000u);
+        vx[j][2 * k] = __uint_as_float(vraw[j].w[k] << 16);
+        vx[j][2 * k + 1] = __uint_as_float(vraw[j].w[k] & 0xFFFF0000u);
+      } else {
+        kx[j][2 * k] = __half2float(__ushort_as_half(uint16_t(kraw[j].w[k] & 0xFFFFu)));
+        kx[j][2 * k + 1] = __half2float(__ushort_as_half(uint16_t(kraw[j].w[k] >> 16)));
+        vx[j][2 * k] = __half2float(__ushort_as_half(uint16_t(vraw[j].w[k] & 0xFFFFu)));
+        vx[j][2 * k + 1] = __half2float(__ushort_as_half(uint16_t(vraw[j].w[k] >> 16)));
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- keys
+  {
+    float mn[8], mx[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      mn[k] = fminf(kx[0][k], kx[1][k]);
+      mx[k] = fmaxf(kx[0][k], kx[1][k]);
+    }
+    const int pr = wave * 4 + p;
+    kmn_s[pr][2 * c] = make_float4(mn[0], mn[1], mn[2], mn[3]);
+    kmn_s[pr][2 * c + 1] = make_float4(mn[4], mn[5], mn[6], mn[7]);
+    kmx_s[pr][2 * c] = make_float4(mx[0], mx[1], mx[2], mx[3]);
+    kmx_s[pr][2 * c + 1] = make_float4(mx[4], mx[5], mx[6], mx[7]);
+  }
+  __syncthreads();
+  constexpr float k_levels = float((1 << KB) - 1);
+  if (tid < D) {
+    const float* mnp = reinterpret_cast<const float*>(kmn_s);
+    const float* mxp = reinterpret_cast<const float*>(kmx_s);
+    float mn = mnp[tid], mx = mxp[tid];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      mn = fminf(mn, mnp[r * D + tid]);
+      mx = fmaxf(mx, mxp[r * D + tid]);
+    }
+    const QParams q = make_qparams(mn, mx, k_levels);
+    const int64_t so = (slab * a.g_stride + g) * D + tid;
+    out_store(static_cast<uint16_t*>(a.cache.k_scale) + so, q.s_bits);
+    out_store(static_cast<uint16_t*>(a.cache.k_zero) + so, q.z_bits);
+    reinterpret_cast<float*>(ks_s)[tid] = q.s;
+    reinterpret_cast<float*>(kz_s)[tid] = q.z;
+    reinterpret_cast<float*>(kr_s)[tid] = q.r;
+  }
+  __syncthreads();
+  {
+    float ks[8], kz[8], kr[8];
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) {
+      const float4 s4 = ks_s[2 * c + hq], z4 = kz_s[2 * c + hq], r4 = kr_s[2 * c + hq];
+      ks[4 * hq] = s4.x; ks[4 * hq + 1] = s4.y; ks[4 * hq + 2] = s4.z; ks[4 * hq + 3] = s4.w;
+      kz[4 * hq] = z4.x; kz[4 * hq + 1] = z4.y; kz[4 * hq + 2] = z4.z; kz[4 * hq + 3] = z4.w;
+      kr[4 * hq] = r4.x; kr[4 * hq + 1] = r4.y; kr[4 * hq + 2] = r4.z; kr[4 * hq + 3] = r4.w;
+    }
+    uint32_t* kdst = static_cast<uint32_t*>(a.cache.k_codes) + ((slab * a.g_stride + g) * KVQ_GROUP) * kWords;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t lo = 0, hi = 0;  // channels 8c .. 8c+7 at bits (k * KB) of a 64-bit field
+      uint32_t codes[8];
+      quant_codes<8>(kx[j], ks, kz, kr, k_levels, codes);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t code = codes[k];
+        if constexpr (KB == 8) {
+          if (k < 4) lo |= code << (8 * k); else hi |= code << (8 * (k - 4));
+        } else {
+          lo |= code << (KB * k);
+        }
+      }
+      uint32_t* rowp = kdst + tok[j] * kWords;
+      if constexpr (KB == 8) {
+        out_store(reinterpret_cast<u32x2_t*>(rowp) + c, u32x2_t{lo, hi});
+      } else if constexpr (KB == 4) {
+        out_store(rowp + c, lo);
+      } else {
+        // 16 bits per lane: lanes 2m, 2m + 1 fill word m
+        const uint32_t nb = uint32_t(__builtin_amdgcn_mov_dpp(int(lo), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+        if ((c & 1) == 0) out_store(rowp + (c >> 1), lo | (nb << 16));
+      }
+    }
+  }
+
+  // -------------------------------------------------------------- values
+  constexpr float v_levels = float((1 << VB) - 1);
+  const int vg = a.L.v_group, lpg = vg / 8;  // channels and lanes per value group
+  // zero the wave's octet words (this wave alone writes them, in issue order)
+  uint32_t* oct = vw_s + wave * (32 * VB);
+#pragma unroll
+  for (int i = 0; i < kChunkWords; ++i) oct[lane * kChunkWords + i] = 0u;
+  float vmn[2], vmx[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float mn = vx[j][0], mx = vx[j][0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+      mn = fminf(mn, vx[j][k]);
+      mx = fmaxf(mx, vx[j][k]);
+    }
+    mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xF, 0xF, false)));
+    mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xF, 0xF, false)));
+    if (lpg >= 8) {
+      mn = fminf(mn, __shfl_xor(mn, 4));
+      mx = fmaxf(mx, __shfl_xor(mx, 4));
+    }
+    if (lpg >= 16) {
+      mn = fminf(mn, __shfl_xor(mn, 8));
+      mx = fmaxf(mx, __shfl_xor(mx, 8));
+    }
+    vmn[j] = mn;
+    vmx[j] = mx;
+  }
+  // lane c forms the parameters of row c & 1; the other row's come from lane c ^ 1
+  const int jm = c & 1;
+  const QParams qm = make_qparams(jm ? vmn[1] : vmn[0], jm ? vmx[1] : vmx[0], v_levels);
+  const float os = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(qm.s), 0xB1, 0xF, 0xF, false));
+  const float oz = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(qm.z), 0xB1, 0xF, 0xF, false));
+  const float orr = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(qm.r), 0xB1, 0xF, 0xF, false));
+  const float vs[2] = {jm ? os : qm.s, jm ? qm.s : os};
+  const float vz[2] = {jm ? oz : qm.z, jm ? qm.z : oz};
+  const float vr[2] = {jm ? orr : qm.r, jm ? qm.r : orr};
+  if ((c & (lpg - 1)) < 2) {
+    // one lane per (token, value group) stores its scale and zero
+    const int ngv = D / vg, gc = (8 * c) / vg;
+    const int64_t vso = (slab * a.g_stride + g) * ngv * KVQ_GROUP + gc * KVQ_GROUP + tok[jm];
+    out_store(static_cast<uint16_t*>(a.cache.v_scale) + vso, qm.s_bits);
+    out_store(static_cast<uint16_t*>(a.cache.v_zero) + vso, qm.z_bits);
+  }
+  {
+    // the lane's codes: tile t = c / 2, columns 8 (c % 2) + k, tokens pair (p, p + 4)
+    const int t = c >> 1, hc = c & 1;
+    const int chunk = t / kTilesPerWord, slot = t % kTilesPerWord;
+    uint32_t part[8], c0[8], c1[8];
+    {
+      float s8[8], z8[8], r8[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) { s8[k] = vs[0]; z8[k] = vz[0]; r8[k] = vr[0]; }
+      quant_codes<8>(vx[0], s8, z8, r8, v_levels, c0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) { s8[k] = vs[1]; z8[k] = vz[1]; r8[k] = vr[1]; }
+      quant_codes<8>(vx[1], s8, z8, r8, v_levels, c1);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) part[k] = (c0[k] << (slot * VB)) | (c1[k] << (16 + slot * VB));
+    // round k: column n = 8 hc + ((k + t) & 7); field (16 wave + n) * 4 + p
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int col = (k + t) & 7;
+      uint32_t v = part[0];
+#pragma unroll
+      for (int m = 1; m < 8; ++m) v = col == m ? part[m] : v;
+      const int field = (8 * hc + col) * 4 + p;  // within the wave's octet
+      atomicOr(&oct[field * kChunkWords + chunk], v);
+    }
+  }
+  // the octet's words, contiguous in the group's stream: (16 wave + n) * 4 + p fields
+  uint32_t* vdst = static_cast<uint32_t*>(a.cache.v_codes) + (slab * a.g_stride + g) * vWords + wave * (32 * VB);
+  if constexpr (kChunkWords == 1) {
+    out_store(vdst + lane, oct[lane]);
+  } else if constexpr (kChunkWords == 2) {
+    out_store(reinterpret_cast<u32x2_t*>(vdst) + lane, *reinterpret_cast<const u32x2_t*>(oct + 2 * lane));
+  } else {
+    out_store(reinterpret_cast<u32x4_t*>(vdst) + lane, *reinterpret_cast<const u32x4_t*>(oct + 4 * lane));
+  }
+}
+
 // Key groups of k_group = 64 or 128 tokens: per-channel min / max over the key
 // group's tokens, then its scale and zero (make_qparams, as for 32-token groups).
 // One workgroup per (key group of the chunk, kv head, batch row); thread (channel
@@ -495,6 +781,20 @@ hipError_t launch_dt(const PackArgs& a, dim3 grid, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const int kb = a.L.k_bits, vb = a.L.v_bits;
+  if constexpr (DT != KVQ_F32) {
+    if (a.L.Dk == 128 && a.L.Dv == 128 && a.L.k_group == 32) {
+      const dim3 g128(unsigned(a.n_groups_chunk + (a.n_ret_chunk + kRetRows128 - 1) / kRetRows128), grid.y, grid.z);
+#define KVQ_PACK128_CASE(K_, V_)                                                                    \
+      if (kb == K_ && vb == V_) {                                                                   \
+        hipLaunchKernelGGL((pack128_kernel<DT, K_, V_>), g128, dim3(kPackThreads), 0, stream, a);  \
+        return hipGetLastError();                                                                   \
+      }
+      KVQ_PACK128_CASE(2, 2) KVQ_PACK128_CASE(2, 4) KVQ_PACK128_CASE(2, 8)
+      KVQ_PACK128_CASE(4, 2) KVQ_PACK128_CASE(4, 4) KVQ_PACK128_CASE(4, 8)
+      KVQ_PACK128_CASE(8, 2) KVQ_PACK128_CASE(8, 4) KVQ_PACK128_CASE(8, 8)
+#undef KVQ_PACK128_CASE
+    }
+  }
 #define KVQ_PACK_CASE(K_, V_)                                                                     \
   if (kb == K_ && vb == V_) {                                                                     \
     hipLaunchKernelGGL((pack_kernel<DT, K_, V_>), grid, dim3(kPackThreads), 0, stream, a);       \

@@ -101,10 +101,13 @@ def test_mfma_instances(dk, kb, vb):
     """Each matrix-core instance on a small cache: 2 batch rows x 2 KV heads, 10 code
     groups per slab plus a 12-token fp16 window, one, three and four partitions (the
     last cut into more units than there are groups); the input dtype cycles through
-    bf16, fp16 and fp32 so every dtype meets every key width."""
+    bf16, fp16 and fp32 so every dtype meets the matrix-core kernel at several key widths."""
     i = MFMA_INSTANCES.index((dk, kb, vb))
+    # 128-wide keys take 16-bit inputs only, so that every bit pair also runs through
+    # the 16-bit inputs' dedicated pack kernel (fp32 meets the other key widths)
+    dtype = _DTYPES[i % 2] if dk == 128 else _DTYPES[i % 3]
     w = Workload("mfma_d%d_k%dv%d" % (dk, kb, vb), B=2, Hq=8, Hkv=2, Dk=dk, Dv=128, T=332, k_bits=kb, v_bits=vb,
-                 n_recent=12, dtype=_DTYPES[i % 3], partitions=4, seed=100 + i)
+                 n_recent=12, dtype=dtype, partitions=4, seed=100 + i)
     _run_small(w, partitions=[1, 3, 4], kernel="mfma")
 
 
@@ -185,20 +188,22 @@ def test_constant_and_degenerate_groups():
     _compare_pack(cache_to_numpy(cache), O.pack_all(K, V, w))
 
 
-def test_pack_rounding_ties_and_near_ties():
+@pytest.mark.parametrize("D", [64, 128])
+def test_pack_rounding_ties_and_near_ties(D):
     """Quotients (x - z) / s exactly on a half-integer (round half to even) and one
-    float32 step either side of it, for every bit width and dtype: the codes must be
-    the contract's, which the kernel gets by multiplying with 1/s and falling back
-    to the exact division near a rounding boundary."""
+    float32 step either side of it, for every bit width and dtype (head width 128 is
+    the 16-bit inputs' dedicated pack kernel): the codes must be the contract's,
+    which the kernels get by multiplying with 1/s and falling back to the exact
+    division near a rounding boundary."""
     for bits in (2, 4, 8):
-        for dtype in ("f32", "bf16"):
-            w = Workload("ties%d_%s" % (bits, dtype), B=1, Hq=4, Hkv=1, Dk=64, Dv=64, T=64, k_bits=bits,
+        for dtype in ("f32", "bf16", "f16"):
+            w = Workload("ties%d_%s_d%d" % (bits, dtype, D), B=1, Hq=4, Hkv=1, Dk=D, Dv=D, T=64, k_bits=bits,
                          v_bits=bits, dtype=dtype, seed=42)
             levels = 2 ** bits - 1
             # s = 1, z = 0 for every group: min 0 and max = levels in each column / row
-            grid = np.arange(64, dtype=np.float32) % (levels + 1)
-            K = np.zeros((1, 1, 64, 64), dtype=np.float32)
-            V = np.zeros((1, 1, 64, 64), dtype=np.float32)
+            grid = np.arange(D, dtype=np.float32) % (levels + 1)
+            K = np.zeros((1, 1, 64, D), dtype=np.float32)
+            V = np.zeros((1, 1, 64, D), dtype=np.float32)
             for t in range(64):
                 K[0, 0, t, :] = (grid + 0.5 * (t % 3 == 1)) % (levels + 0.5)
                 V[0, 0, t, :] = (grid + 0.5 * (t % 2)) % (levels + 0.5)
@@ -209,9 +214,12 @@ def test_pack_rounding_ties_and_near_ties():
                 K[0, 0, 4, 1::4] = np.nextafter(K[0, 0, 4, 1::4], np.float32(-1))
                 V[0, 0, 5, 2::5] = np.nextafter(V[0, 0, 5, 2::5], np.float32(levels + 1))
                 Kin, Vin = K, V
-            else:
+            elif dtype == "bf16":
                 Kin = (K.view(np.uint32) >> 16).astype(np.uint16)
                 Vin = (V.view(np.uint32) >> 16).astype(np.uint16)
+            else:
+                Kin = K.astype(np.float16).view(np.uint16)   # every value here is exact in fp16
+                Vin = V.astype(np.float16).view(np.uint16)
             lay = api.Layout.from_workload(w)
             cache = api.kv_quant_pack(lay, to_device(Kin, dtype), to_device(Vin, dtype))
             torch.cuda.synchronize()
