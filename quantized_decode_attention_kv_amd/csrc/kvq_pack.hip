@@ -484,9 +484,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
 //           straight to the cache;
 //   values  per (token, v_group channels) min / max over the 8 lanes' quads (DPP),
 //           scale and zero formed by one lane per token of a quad; the lane's codes
-//           of tile c / 2, columns 8 (c % 2) + k, go to 8 words of its wave's octet in
-//           LDS (round k sends column k + t: the 8 lanes that share a word never write
-//           it in the same round), and each wave stores its octet's words itself.
+//           of tile t = c / 2, columns 8 (c % 2) + k, make 8 partial words, one for each
+//           of 8 words of its wave's octet; each goes to its own LDS slot (word, t % TPW),
+//           so every slot is written once with a plain store, and each lane then ORs
+//           the TPW slots of the words it stores.
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -497,9 +498,14 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
   constexpr int kChunkWords = VB / 2;             // words of a (octet, column, pair) field
   constexpr int kTilesPerWord = 16 / VB;
   __shared__ int32_t row_s[KVQ_GROUP];
-  __shared__ float4 kmn_s[16][D / 4], kmx_s[16][D / 4];   // lane partials: (wave, pair) x channel
+  // the key partials (lane partials: (wave, pair) x channel) are dead after the
+  // second barrier, when the value slots (per wave: (word, tile slot) partial words)
+  // come into use: they share the memory
+  __shared__ __align__(16) float4 part_s[2 * 16 * (D / 4)];
+  float4 (*kmn_s)[D / 4] = reinterpret_cast<float4 (*)[D / 4]>(part_s);
+  float4 (*kmx_s)[D / 4] = reinterpret_cast<float4 (*)[D / 4]>(part_s + 16 * (D / 4));
+  static_assert(sizeof(float4) * 2 * 16 * (D / 4) >= sizeof(uint32_t) * kPackWaves * 64 * 8, "value slots");
   __shared__ float4 ks_s[D / 4], kz_s[D / 4], kr_s[D / 4];
-  __shared__ uint32_t vw_s[vWords];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -555,24 +561,22 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
     kraw[j].w[0] = kv.x; kraw[j].w[1] = kv.y; kraw[j].w[2] = kv.z; kraw[j].w[3] = kv.w;
     vraw[j].w[0] = vv.x; vraw[j].w[1] = vv.y; vraw[j].w[2] = vv.z; vraw[j].w[3] = vv.w;
   }
-  float kx[2][8], vx[2][8];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  // 16-bit words -> floats (values stay raw until the value phase)
+  auto widen = [](const Raw16<DT>& r, float (&x)[8]) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if constexpr (DT == KVQ_BF16) {
-        kx[j][2 * k] = __uint_as_float(kraw[j].w[k] << 16);
-        kx[j][2 * k + 1] = __uint_as_float(kraw[j].w[k] & 0xFFFF0000u);
-        vx[j][2 * k] = __uint_as_float(vraw[j].w[k] << 16);
-        vx[j][2 * k + 1] = __uint_as_float(vraw[j].w[k] & 0xFFFF0000u);
+        x[2 * k] = __uint_as_float(r.w[k] << 16);
+        x[2 * k + 1] = __uint_as_float(r.w[k] & 0xFFFF0000u);
       } else {
-        kx[j][2 * k] = __half2float(__ushort_as_half(uint16_t(kraw[j].w[k] & 0xFFFFu)));
-        kx[j][2 * k + 1] = __half2float(__ushort_as_half(uint16_t(kraw[j].w[k] >> 16)));
-        vx[j][2 * k] = __half2float(__ushort_as_half(uint16_t(vraw[j].w[k] & 0xFFFFu)));
-        vx[j][2 * k + 1] = __half2float(__ushort_as_half(uint16_t(vraw[j].w[k] >> 16)));
+        x[2 * k] = __half2float(__ushort_as_half(uint16_t(r.w[k] & 0xFFFFu)));
+        x[2 * k + 1] = __half2float(__ushort_as_half(uint16_t(r.w[k] >> 16)));
       }
     }
-  }
+  };
+  float kx[2][8];
+  widen(kraw[0], kx[0]);
+  widen(kraw[1], kx[1]);
 
   // ---------------------------------------------------------------- keys
   {
@@ -648,10 +652,10 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
   // -------------------------------------------------------------- values
   constexpr float v_levels = float((1 << VB) - 1);
   const int vg = a.L.v_group, lpg = vg / 8;  // channels and lanes per value group
-  // zero the wave's octet words (this wave alone writes them, in issue order)
-  uint32_t* oct = vw_s + wave * (32 * VB);
-#pragma unroll
-  for (int i = 0; i < kChunkWords; ++i) oct[lane * kChunkWords + i] = 0u;
+  uint32_t* slots = reinterpret_cast<uint32_t*>(part_s) + wave * (64 * 8);  // this wave's alone, in issue order
+  float vx[2][8];
+  widen(vraw[0], vx[0]);
+  widen(vraw[1], vx[1]);
   float vmn[2], vmx[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -708,25 +712,31 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) part[k] = (c0[k] << (slot * VB)) | (c1[k] << (16 + slot * VB));
-    // round k: column n = 8 hc + ((k + t) & 7); field (16 wave + n) * 4 + p
+    // column n = 8 hc + k: word (field (n * 4 + p) of the octet, chunk), slot t % TPW;
+    // (word, slot) = 8 (n * 4 + p) + t since a field's chunks hold 8 tiles' slots
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int col = (k + t) & 7;
-      uint32_t v = part[0];
-#pragma unroll
-      for (int m = 1; m < 8; ++m) v = col == m ? part[m] : v;
-      const int field = (8 * hc + col) * 4 + p;  // within the wave's octet
-      atomicOr(&oct[field * kChunkWords + chunk], v);
-    }
+    for (int k = 0; k < 8; ++k) slots[8 * ((8 * hc + k) * 4 + p) + t] = part[k];
+    (void)chunk;
   }
-  // the octet's words, contiguous in the group's stream: (16 wave + n) * 4 + p fields
+  // the octet's words, contiguous in the group's stream: field (16 wave + n) * 4 + p
+  // is words kChunkWords * ((n * 4 + p)) .. of the wave's block; lane l stores words
+  // kChunkWords * l .. kChunkWords * l + kChunkWords - 1, each the OR of its TPW slots
+  uint32_t wv[kChunkWords];
+#pragma unroll
+  for (int i = 0; i < kChunkWords; ++i) {
+    const int word = kChunkWords * lane + i;
+    uint32_t v = 0;
+#pragma unroll
+    for (int m = 0; m < kTilesPerWord; ++m) v |= slots[word * kTilesPerWord + m];
+    wv[i] = v;
+  }
   uint32_t* vdst = static_cast<uint32_t*>(a.cache.v_codes) + (slab * a.g_stride + g) * vWords + wave * (32 * VB);
   if constexpr (kChunkWords == 1) {
-    out_store(vdst + lane, oct[lane]);
+    out_store(vdst + lane, wv[0]);
   } else if constexpr (kChunkWords == 2) {
-    out_store(reinterpret_cast<u32x2_t*>(vdst) + lane, *reinterpret_cast<const u32x2_t*>(oct + 2 * lane));
+    out_store(reinterpret_cast<u32x2_t*>(vdst) + lane, u32x2_t{wv[0], wv[1]});
   } else {
-    out_store(reinterpret_cast<u32x4_t*>(vdst) + lane, *reinterpret_cast<const u32x4_t*>(oct + 4 * lane));
+    out_store(reinterpret_cast<u32x4_t*>(vdst) + lane, u32x4_t{wv[0], wv[1], wv[2], wv[3]});
   }
 }
 
