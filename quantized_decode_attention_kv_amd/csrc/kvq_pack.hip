@@ -24,9 +24,11 @@
 //
 // The codes follow the quantizer contract of kvq.h bit for bit: code =
 // clamp(rint(fl(x - z) / s)) with the correctly rounded division.  The division is
-// replaced by a multiply with fl(1/s): the two quotients differ by at most
-// 3 * 2^-24 * |t| (< 5e-5 while |t| <= 256; a larger |t| clamps the same way), so
-// rint gives the same integer unless the quotient lies within 2^-12 of a
+// replaced by a multiply with r, the hardware reciprocal of s (within one ulp):
+// the product and the correctly rounded quotient differ by at most
+// 4 * 2^-24 * |t| (< 1.3e-4 while |t| <= 512, and t stays below 2 * (2^bits - 1)
+// because s is at least about half of range / levels; larger t clamp the same
+// way), so rint gives the same integer unless the quotient lies within 2^-12 of a
 // half-integer; such elements (about one in two thousand) take the exact division.
 // Scale and zero use the exact division, with contraction off, as the contract
 // spells out.
@@ -142,7 +144,7 @@ __device__ __forceinline__ QParams make_qparams(float mn, float mx, float levels
   q.z_bits = zb;
   q.s = f16_bits_to_f32(sb);
   q.z = f16_bits_to_f32(zb);
-  q.r = q.s == 0.0f ? 0.0f : 1.0f / q.s;
+  q.r = q.s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(q.s);
   return q;
 }
 
@@ -153,7 +155,7 @@ __device__ __forceinline__ QParams qparams_of(uint16_t sb, uint16_t zb) {
   q.z_bits = zb;
   q.s = f16_bits_to_f32(sb);
   q.z = f16_bits_to_f32(zb);
-  q.r = q.s == 0.0f ? 0.0f : 1.0f / q.s;
+  q.r = q.s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(q.s);
   return q;
 }
 
@@ -551,13 +553,17 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
   }
   const int p = lane >> 4, c = lane & 15;
   const int tok[2] = {8 * wave + p, 8 * wave + p + 4};
+  // wave-uniform 64-bit bases, 32-bit lane offsets (a slab's chunk is < 2^31 bytes)
+  const uint16_t* Kb = static_cast<const uint16_t*>(a.K) + slab * a.t_count * D;
+  const uint16_t* Vb = static_cast<const uint16_t*>(a.V) + slab * a.t_count * D;
+  const int32_t row0 = int32_t(g * KVQ_GROUP - a.t_begin);  // chunk row of token 0 of a plain group
   Raw16<DT> kraw[2], vraw[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int64_t row = plain ? g * KVQ_GROUP + tok[j] - a.t_begin : row_s[tok[j]];
-    const int64_t e = (slab * a.t_count + row) * D + 8 * c;
-    const uint4 kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.K) + e);
-    const uint4 vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.V) + e);
+    const uint32_t row = uint32_t(plain ? row0 + tok[j] : row_s[tok[j]]);
+    const uint32_t e = row * D + 8 * c;
+    const uint4 kv = *reinterpret_cast<const uint4*>(Kb + e);
+    const uint4 vv = *reinterpret_cast<const uint4*>(Vb + e);
     kraw[j].w[0] = kv.x; kraw[j].w[1] = kv.y; kraw[j].w[2] = kv.z; kraw[j].w[3] = kv.w;
     vraw[j].w[0] = vv.x; vraw[j].w[1] = vv.y; vraw[j].w[2] = vv.z; vraw[j].w[3] = vv.w;
   }
@@ -604,9 +610,9 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
       mx = fmaxf(mx, mxp[r * D + tid]);
     }
     const QParams q = make_qparams(mn, mx, k_levels);
-    const int64_t so = (slab * a.g_stride + g) * D + tid;
-    out_store(static_cast<uint16_t*>(a.cache.k_scale) + so, q.s_bits);
-    out_store(static_cast<uint16_t*>(a.cache.k_zero) + so, q.z_bits);
+    const int64_t so = (slab * a.g_stride + g) * D;
+    out_store(static_cast<uint16_t*>(a.cache.k_scale) + so + uint32_t(tid), q.s_bits);
+    out_store(static_cast<uint16_t*>(a.cache.k_zero) + so + uint32_t(tid), q.z_bits);
     reinterpret_cast<float*>(ks_s)[tid] = q.s;
     reinterpret_cast<float*>(kz_s)[tid] = q.z;
     reinterpret_cast<float*>(kr_s)[tid] = q.r;
@@ -636,7 +642,7 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
           lo |= code << (KB * k);
         }
       }
-      uint32_t* rowp = kdst + tok[j] * kWords;
+      uint32_t* rowp = kdst + uint32_t(tok[j] * kWords);
       if constexpr (KB == 8) {
         out_store(reinterpret_cast<u32x2_t*>(rowp) + c, u32x2_t{lo, hi});
       } else if constexpr (KB == 4) {
@@ -692,9 +698,10 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
   if ((c & (lpg - 1)) < 2) {
     // one lane per (token, value group) stores its scale and zero
     const int ngv = D / vg, gc = (8 * c) / vg;
-    const int64_t vso = (slab * a.g_stride + g) * ngv * KVQ_GROUP + gc * KVQ_GROUP + tok[jm];
-    out_store(static_cast<uint16_t*>(a.cache.v_scale) + vso, qm.s_bits);
-    out_store(static_cast<uint16_t*>(a.cache.v_zero) + vso, qm.z_bits);
+    const int64_t vso = (slab * a.g_stride + g) * ngv * KVQ_GROUP;
+    const uint32_t vo = uint32_t(gc * KVQ_GROUP + tok[jm]);
+    out_store(static_cast<uint16_t*>(a.cache.v_scale) + vso + vo, qm.s_bits);
+    out_store(static_cast<uint16_t*>(a.cache.v_zero) + vso + vo, qm.z_bits);
   }
   {
     // the lane's codes: tile t = c / 2, columns 8 (c % 2) + k, tokens pair (p, p + 4)
@@ -732,11 +739,11 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
   }
   uint32_t* vdst = static_cast<uint32_t*>(a.cache.v_codes) + (slab * a.g_stride + g) * vWords + wave * (32 * VB);
   if constexpr (kChunkWords == 1) {
-    out_store(vdst + lane, wv[0]);
+    out_store(vdst + uint32_t(lane), wv[0]);
   } else if constexpr (kChunkWords == 2) {
-    out_store(reinterpret_cast<u32x2_t*>(vdst) + lane, u32x2_t{wv[0], wv[1]});
+    out_store(reinterpret_cast<u32x2_t*>(vdst) + uint32_t(lane), u32x2_t{wv[0], wv[1]});
   } else {
-    out_store(reinterpret_cast<u32x4_t*>(vdst) + lane, u32x4_t{wv[0], wv[1], wv[2], wv[3]});
+    out_store(reinterpret_cast<u32x4_t*>(vdst) + uint32_t(lane), u32x4_t{wv[0], wv[1], wv[2], wv[3]});
   }
 }
 
