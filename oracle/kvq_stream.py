@@ -24,7 +24,11 @@ the readings taken here:
   values exactly like a group of the one-shot cache (keys per channel, values per
   token and 32-channel group) and appended after the groups packed so far;
 * decode attends over every packed group and every fp16 token (retained or
-  pending).
+  pending);
+* with key rotation ("Quantize What Counts", rotation integration; the transform
+  read as ``hadamard_rotate``, as for the one-shot cache) a new token's key row is
+  rotated in float32 before its fp16 rounding, so the fp16 rows and the groups
+  formed from them hold rotated keys, and decode rotates the query.
 
 State of one (batch row, kv head) slab, all host NumPy:
   t              tokens appended so far (positions 0 .. t-1)
@@ -37,15 +41,16 @@ State of one (batch row, kv head) slab, all host NumPy:
 
 import numpy as np
 
-from .kvq_oracle import (CACHE_KEYS, GROUP, attention, dequant_slab, pack_codes, pack_slab,
-                         pack_value_codes, quantize_groups, retained_mask, split_positions, upcast)
+from .kvq_oracle import (CACHE_KEYS, GROUP, attention, dequant_slab, hadamard_rotate, pack_codes, pack_slab,
+                         pack_value_codes, quantize_groups, retained_mask, rotate_query, split_positions,
+                         upcast)
 
 
 class SlabStream:
     """Streaming cache of one slab (see the module header for the state)."""
 
     def __init__(self, Dk: int, Dv: int, k_bits: int, v_bits: int, n_recent: int, log_window: int,
-                 v_group: int = GROUP):
+                 v_group: int = GROUP, key_rotation: bool = False):
         if log_window > 0 and n_recent < log_window:
             raise ValueError("a stream needs log_window == 0 or n_recent >= log_window "
                              "(otherwise a token could re-enter the fp16 set)")
@@ -53,6 +58,7 @@ class SlabStream:
         self.k_bits, self.v_bits = k_bits, v_bits
         self.n_recent, self.log_window = n_recent, log_window
         self.v_group = v_group
+        self.key_rotation = key_rotation
         self.t = 0
         self.rows = {}
         self.pending = set()
@@ -66,7 +72,8 @@ class SlabStream:
         if self.t:
             raise ValueError("prefill starts an empty stream")
         T0 = K.shape[0]
-        p = pack_slab(K, V, dtype, self.k_bits, self.v_bits, self.n_recent, self.log_window, v_group=self.v_group)
+        p = pack_slab(K, V, dtype, self.k_bits, self.v_bits, self.n_recent, self.log_window,
+                      key_rotation=self.key_rotation, v_group=self.v_group)
         r, u = split_positions(T0, self.n_recent, self.log_window)
         for g in range(len(u) // GROUP):
             sl = slice(GROUP * g, GROUP * (g + 1))
@@ -89,7 +96,10 @@ class SlabStream:
         1. store it in fp16;  2. every stored token that is no longer retained at
         t + 1 tokens becomes pending;  3. while 32 or more are pending, the 32 of
         lowest position become the next group."""
-        k16 = upcast(k_row, dtype).astype(np.float16).view(np.uint16)
+        k32 = upcast(k_row, dtype)
+        if self.key_rotation:
+            k32 = hadamard_rotate(k32)
+        k16 = k32.astype(np.float16).view(np.uint16)
         v16 = upcast(v_row, dtype).astype(np.float16).view(np.uint16)
         self.rows[self.t] = (k16, v16)
         self.t += 1
@@ -151,7 +161,10 @@ class SlabStream:
         token in the stream (float64; LogQuant section 4: order-free)."""
         p, _, _ = self.as_packed()
         Khat, Vhat = dequant_slab(p, self.k_bits, self.v_bits)
-        return attention(upcast(q_group, q_dtype), Khat, Vhat, scale)
+        q = upcast(q_group, q_dtype)
+        if self.key_rotation:
+            q = rotate_query(q)
+        return attention(q, Khat, Vhat, scale)
 
 
 def stream_keys():

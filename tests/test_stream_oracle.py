@@ -171,3 +171,59 @@ def test_all_retained_decode_is_plain_attention():
 def test_stream_rejects_reentering_window():
     with pytest.raises(ValueError):
         SlabStream(32, 32, 4, 2, 2, 4)
+
+
+# ------------------------------------------------------------------ key rotation
+# With key rotation ("Quantize What Counts", rotation integration) the stream stores
+# each key rotated by the orthonormal Walsh-Hadamard transform (Sylvester order,
+# scipy.linalg.hadamard) and decode rotates the query.
+
+def _sylvester(n):
+    from scipy.linalg import hadamard
+    return hadamard(n).astype(np.float64)
+
+
+def test_rotated_stream_equals_rotated_one_shot_without_log_window():
+    """Keys built as H Y / 8 (Dk = 64) from integer multiples of 1/8: every step of the
+    rotation is exact, so the rotated keys are Y, exact in fp16, and the rotated stream
+    must equal the rotated one-shot cache bit for bit (the rotation comes before the
+    fp16 copy, and groups form from the rotated rows)."""
+    rng = np.random.default_rng(17)
+    Dk, Dv, n_recent = 64, 64, 8
+    T = n_recent + 32 * 4
+    Y = rng.integers(-16, 17, size=(T, Dk)) / 8.0
+    Y[:, 5] += 24.0                                           # an outlier channel after rotation
+    K = (Y @ _sylvester(Dk).T / 8.0).astype(np.float32)       # exact: sums of multiples of 1/64
+    V = rng.standard_normal((T, Dv)).astype(np.float16).view(np.uint16).view(np.float16).astype(np.float32)
+    s = SlabStream(Dk, Dv, 4, 2, n_recent, 0, key_rotation=True)
+    for t in range(T):
+        s.append(K[t], V[t], "f32")
+    p, _, _ = s.as_packed()
+    ref = pack_slab(K, V, "f32", 4, 2, n_recent, 0, key_rotation=True)
+    for key in ref:
+        assert np.array_equal(p[key], ref[key]), key
+    assert np.array_equal(p["k_fp16"].view(np.float16).astype(np.float64), Y[-n_recent:])
+    plain = pack_slab(K, V, "f32", 4, 2, n_recent, 0)
+    assert not np.array_equal(plain["k_codes"], ref["k_codes"])
+
+
+def test_rotated_stream_all_retained_decode_keeps_scores():
+    """Every token retained: the fp16 rows are fp16(H k / 8) (within one fp16 rounding of
+    the float64 product) and decode with the rotated query is plain attention, since
+    (H q) . (H k) / 64 = q . k: it matches scipy's softmax over the plain keys to the
+    error of one fp16 rounding of each key."""
+    rng = np.random.default_rng(18)
+    Dk, Dv, T, G = 64, 32, 40, 4
+    K = rng.standard_normal((T, Dk)).astype(np.float32)
+    V = rng.standard_normal((T, Dv)).astype(np.float32)
+    q = rng.standard_normal((G, Dk)).astype(np.float32)
+    s = SlabStream(Dk, Dv, 2, 2, T, 0, key_rotation=True)
+    for t in range(T):
+        s.append(K[t], V[t], "f32")
+    p, _, _ = s.as_packed()
+    rot64 = K.astype(np.float64) @ _sylvester(Dk).T / 8.0
+    got = p["k_fp16"].view(np.float16).astype(np.float64)
+    assert np.all(np.abs(got - rot64) <= np.abs(rot64) * 2.0 ** -10 + 2.0 ** -24)
+    scale = 0.125
+    ref = softmax(scale * (q.astype(np.float64) @ K.astype(np.float64).T), axis=-1) @ V.astype(np.float16).astype(np.float64)
+    assert np.abs(s.decode(q, "f32", scale) - ref).max() < 5e-3
