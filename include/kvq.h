@@ -98,6 +98,7 @@ typedef struct {
   int32_t k_group;                /* tokens per key group: 32, 64 or 128 (Tq a multiple of it) */
   int32_t v_group;                /* channels per value group: 32, 64 or 128, dividing Dv */
   int32_t R, Tq, n_groups;        /* derived: retained count, quantized count, Tq / 32 */
+  int32_t flags;                  /* KVQ_KEY_ROTATION or 0 (kvq_layout_set_flags) */
 } kvq_layout;
 
 /* Device pointers of the eight cache buffers described above.  Buffers a call
@@ -122,6 +123,25 @@ int kvq_layout_init(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T
  * k_group = v_group = 32. */
 int kvq_layout_init_ex(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, int T,
                        int k_bits, int v_bits, int n_recent, int log_window, int k_group, int v_group);
+
+/* Key-only rotation ("Quantize What Counts", technical summary: contributions,
+ * orthogonality and integration; results, rotation integration: rotating only the
+ * keys before they are quantized spreads outlier channels over all channels).
+ * With KVQ_KEY_ROTATION every key row k (quantized or kept in fp16) is replaced by
+ * H k before it is stored, H the orthonormal Walsh-Hadamard transform of width Dk
+ * in Sylvester order, computed in float32 as butterflies for h = 1, 2, 4, ..., Dk/2
+ * (entries j and j + h of every 2h-block become a + b and a - b, in that order)
+ * followed by one multiply with float32(2^(-m/2)), Dk = 2^m (for odd m,
+ * float32(sqrt(1/2)) * 2^(-(m-1)/2)); decode applies the same H to the query, so
+ * scores are unchanged in exact arithmetic.  The packed cache then holds the
+ * rotated keys; a cache must be decoded with the flags it was packed with. */
+enum { KVQ_KEY_ROTATION = 1 };
+
+/* Set the flags of a layout filled by kvq_layout_init(_ex): 0 or KVQ_KEY_ROTATION
+ * (KVQ_ERR_INVALID for other bits; KVQ_ERR_UNSUPPORTED for rotation unless Dk is a
+ * power of two).  Streams take their flags from kvq_stream_set_flags; HeadQ side
+ * codes take a layout without flags. */
+int kvq_layout_set_flags(kvq_layout* L, int flags);
 
 /* Byte sizes of the eight kvq_cache buffers, in kvq_cache field order. */
 int kvq_cache_sizes(const kvq_layout* L, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]);
@@ -308,6 +328,12 @@ int kvq_stream_init(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, int c
  * Stream key groups are 32 tokens (a group forms from 32 pending tokens). */
 int kvq_stream_init_ex(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, int capacity,
                        int k_bits, int v_bits, int n_recent, int log_window, int v_group);
+
+/* Set the layout flags of an empty stream (t == 0, else KVQ_ERR_INVALID), as
+ * kvq_layout_set_flags: with KVQ_KEY_ROTATION prefill packs rotated keys, append
+ * rotates each new key row in float32 before its fp16 rounding (so groups form from
+ * rotated rows), and decode rotates the query. */
+int kvq_stream_set_flags(kvq_stream* S, int flags);
 
 /* Byte sizes of the eight buffers of a stream's cache, in kvq_cache field order. */
 int kvq_stream_cache_sizes(const kvq_stream* S, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]);

@@ -13,7 +13,7 @@ KVQ_NUM_CACHE_BUFFERS = 8
 KVQ_STREAM_MAX_ROWS = 4096
 
 LAYOUT_FIELDS = ["B", "Hq", "Hkv", "Dk", "Dv", "T", "k_bits", "v_bits", "n_recent", "log_window", "k_group", "v_group",
-                 "R", "Tq", "n_groups"]
+                 "R", "Tq", "n_groups", "flags"]
 CACHE_FIELDS = ["k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_fp16", "v_fp16"]
 
 # every entry point declared in include/kvq.h
@@ -23,10 +23,11 @@ EXPORTS = ["kvq_layout_init", "kvq_cache_sizes", "kvq_retained_positions", "kvq_
            "kvq_stream_cache_sizes",
            "kvq_stream_workspace_bytes", "kvq_stream_plan", "kv_stream_prefill", "kv_stream_append",
            "kv_stream_decode", "kvq_side_sizes", "kv_side_pack", "kv_decode_attn_side", "kvq_decode_plan",
-           "kv_decode_attn_noalloc"]
+           "kv_decode_attn_noalloc", "kvq_layout_set_flags", "kvq_stream_set_flags"]
 
 KVQ_KERNEL_MFMA, KVQ_KERNEL_VALU = 1, 2
 KVQ_STATIC_SCRATCH_BYTES = 16 << 20
+KVQ_KEY_ROTATION = 1
 
 
 class KvqSide(ctypes.Structure):
@@ -82,6 +83,8 @@ def load() -> ctypes.CDLL:
     lib.kvq_layout_init.restype = c_int
     lib.kvq_layout_init_ex.argtypes = [LP] + [c_int] * 12
     lib.kvq_layout_init_ex.restype = c_int
+    lib.kvq_layout_set_flags.argtypes = [LP, c_int]
+    lib.kvq_layout_set_flags.restype = c_int
     lib.kvq_cache_sizes.argtypes = [LP, ctypes.POINTER(c_sz)]
     lib.kvq_cache_sizes.restype = c_int
     lib.kvq_retained_positions.argtypes = [LP, ctypes.POINTER(c_i32), c_i32]
@@ -114,6 +117,8 @@ def load() -> ctypes.CDLL:
     lib.kvq_stream_init.restype = c_int
     lib.kvq_stream_init_ex.argtypes = [SP] + [c_int] * 11
     lib.kvq_stream_init_ex.restype = c_int
+    lib.kvq_stream_set_flags.argtypes = [SP, c_int]
+    lib.kvq_stream_set_flags.restype = c_int
     lib.kvq_stream_cache_sizes.argtypes = [SP, ctypes.POINTER(c_sz)]
     lib.kvq_stream_cache_sizes.restype = c_int
     lib.kvq_stream_workspace_bytes.argtypes = [SP, c_int]

@@ -17,16 +17,20 @@ _DTYPE_CODES = {torch.float32: L_.KVQ_F32, torch.float16: L_.KVQ_F16, torch.bflo
 class Layout:
     """Shape and fp16-retention policy of one packed cache (kvq_layout)."""
 
-    def __init__(self, B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits, n_recent=0, log_window=0, v_group=32, k_group=32):
+    def __init__(self, B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits, n_recent=0, log_window=0, v_group=32, k_group=32,
+                 key_rotation=False):
         lib = L_.load()
         self._c = L_.KvqLayout()
         L_.check(lib.kvq_layout_init_ex(ctypes.byref(self._c), B, Hq, Hkv, Dk, Dv, T, k_bits, v_bits,
                                         n_recent, log_window, k_group, v_group))
+        if key_rotation:
+            L_.check(lib.kvq_layout_set_flags(ctypes.byref(self._c), L_.KVQ_KEY_ROTATION))
 
     @classmethod
     def from_workload(cls, w, T=None):
         return cls(w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T if T is None else T, w.k_bits, w.v_bits,
-                   w.n_recent, w.log_window, getattr(w, "v_group", 32), getattr(w, "k_group", 32))
+                   w.n_recent, w.log_window, getattr(w, "v_group", 32), getattr(w, "k_group", 32),
+                   getattr(w, "key_rotation", False))
 
     def __getattr__(self, name):
         if name in L_.LAYOUT_FIELDS:
@@ -208,10 +212,13 @@ class Stream:
     the one-shot cache of its first tokens."""
 
     def __init__(self, B, Hq, Hkv, Dk, Dv, capacity, k_bits, v_bits, n_recent=0, log_window=0, device="cuda",
-                 v_group=32):
+                 v_group=32, key_rotation=False):
         self._c = L_.KvqStream()
-        L_.check(L_.load().kvq_stream_init_ex(ctypes.byref(self._c), B, Hq, Hkv, Dk, Dv, capacity, k_bits, v_bits,
-                                              n_recent, log_window, v_group))
+        lib = L_.load()
+        L_.check(lib.kvq_stream_init_ex(ctypes.byref(self._c), B, Hq, Hkv, Dk, Dv, capacity, k_bits, v_bits,
+                                        n_recent, log_window, v_group))
+        if key_rotation:
+            L_.check(lib.kvq_stream_set_flags(ctypes.byref(self._c), L_.KVQ_KEY_ROTATION))
         self.cache = None
         if device is not None:
             self.cache = {k: torch.empty(shape, dtype=dt, device=device) for k, (shape, dt) in self.shapes().items()}

@@ -103,6 +103,9 @@ int kvq::check_format(const kvq_layout& l) {
     return fail(KVQ_ERR_UNSUPPORTED, "k_group (%d) must be 32, 64 or 128", L->k_group);
   if ((L->v_group != 32 && L->v_group != 64 && L->v_group != 128) || L->Dv % L->v_group)
     return fail(KVQ_ERR_UNSUPPORTED, "v_group (%d) must be 32, 64 or 128 and divide Dv (%d)", L->v_group, L->Dv);
+  if (L->flags & ~int32_t(KVQ_KEY_ROTATION)) return fail(KVQ_ERR_INVALID, "unknown layout flags 0x%x", L->flags);
+  if ((L->flags & KVQ_KEY_ROTATION) && (L->Dk & (L->Dk - 1)))
+    return fail(KVQ_ERR_UNSUPPORTED, "key rotation needs a power-of-two Dk (got %d)", L->Dk);
   return ok();
 }
 
@@ -263,6 +266,16 @@ int kvq_layout_init_ex(kvq_layout* L, int B, int Hq, int Hkv, int Dk, int Dv, in
   return ok();
 }
 
+int kvq_layout_set_flags(kvq_layout* L, int flags) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  kvq_layout l = *L;
+  l.flags = flags;
+  if ((st = kvq::check_format(l)) != KVQ_OK) return st;
+  *L = l;
+  return ok();
+}
+
 int kvq_cache_sizes(const kvq_layout* L, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]) {
   int st = check_layout(L);
   if (st != KVQ_OK) return st;
@@ -366,6 +379,7 @@ int kvq_decode_plan(const kvq_layout* L, int num_partitions, int with_side_code,
 // ------------------------------------------------------------ HeadQ side code
 namespace {
 int check_side(const kvq_layout* L, int rank, const float* U, const kvq_side* side) {
+  if (L->flags) return fail(KVQ_ERR_UNSUPPORTED, "HeadQ side codes take a layout without flags");
   if (rank < 1 || rank > kvq::kMaxSideRank || rank > L->Dk)
     return fail(KVQ_ERR_UNSUPPORTED, "side rank %d must be in [1, min(Dk, %d)]", rank, kvq::kMaxSideRank);
   if (!U || !side) return fail(KVQ_ERR_INVALID, "U or side is NULL");

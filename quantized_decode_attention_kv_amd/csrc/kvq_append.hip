@@ -9,6 +9,9 @@
 //      of kvq.h: keys per channel over the 32 tokens, values per token over each
 //      v_group-channel group, codes in the group formats of kvq.h;
 //   3. moves fp16 rows past the new end into the rows the group freed.
+// With key rotation the token's key row is rotated first (Walsh-Hadamard, the
+// butterfly order of kvq.h, through LDS), so its fp16 row and the groups formed
+// from such rows hold rotated keys.
 // The appended token's values are taken from the input wherever step 2 or 3
 // needs them, so no thread reads what another thread of the launch has stored.
 // This is a latency-bound launch (a few KB per slab): 1024 threads per slab keep
@@ -17,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.hpp"
+#include "kvq_rotate.hpp"
 #include "kvq_vlayout.hpp"
 
 #pragma clang fp contract(off)
@@ -82,8 +86,27 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int Dk = a.L.Dk, Dv = a.L.Dv;
   uint16_t* kf = static_cast<uint16_t*>(a.cache.k_fp16) + slab * a.r_stride * Dk;
   uint16_t* vf = static_cast<uint16_t*>(a.cache.v_fp16) + slab * a.r_stride * Dv;
+  // rotated keys: the token's rotated key row in fp16, formed by all threads before
+  // the first use (one butterfly h per pass, partner channel c ^ h)
+  __shared__ float krot[KVQ_MAX_HEAD_DIM];
+  __shared__ uint16_t knew16[KVQ_MAX_HEAD_DIM];
+  const bool rot = (a.L.flags & KVQ_KEY_ROTATION) != 0;  // the same for every thread
+  if (rot) {
+    float x = tid < Dk ? load_as_f32(a.k_new, a.dtype, slab * Dk + tid) : 0.0f;
+    for (int hh = 1; hh < Dk; hh <<= 1) {
+      if (tid < Dk) krot[tid] = x;
+      __syncthreads();
+      const float partner = tid < Dk ? krot[tid ^ hh] : 0.0f;
+      __syncthreads();
+      x = butterfly(x, partner, (tid & hh) != 0);
+    }
+    if (tid < Dk) knew16[tid] = to_f16_bits(x * rotation_scale(31 - __builtin_clz(unsigned(Dk))));
+    __syncthreads();
+  }
   // the appended token's fp16 value of key / value channel c
-  auto k_new16 = [&](int c) { return to_f16_bits(load_as_f32(a.k_new, a.dtype, slab * Dk + c)); };
+  auto k_new16 = [&](int c) {
+    return rot ? knew16[c] : to_f16_bits(load_as_f32(a.k_new, a.dtype, slab * Dk + c));
+  };
   auto v_new16 = [&](int c) { return to_f16_bits(load_as_f32(a.v_new, a.dtype, slab * Dv + c)); };
 
   // 1. the token's row

@@ -31,6 +31,7 @@
 
 #include "kvq_decode_common.hpp"
 #include "kvq_internal.hpp"
+#include "kvq_rotate.hpp"
 #include "kvq_vlayout.hpp"
 
 namespace kvq {
@@ -122,6 +123,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
   for (int i = tid; i < G * Dk; i += kThreads) {
     const int qi = i / Dk, c = i - qi * Dk;
     qs[i] = a.scale * kLog2e * load_q<QDT>(a.q, (int64_t(b) * a.L.Hq + int64_t(h) * G + qi) * Dk + c);
+  }
+  if (a.L.flags & KVQ_KEY_ROTATION) {
+    // the packed keys are rotated: rotate the queries the same way (butterflies in
+    // increasing h over LDS, one pass per h), so the scores keep their values
+    for (int hh = 1; hh < Dk; hh <<= 1) {
+      __syncthreads();
+      for (int i = tid; i < G * Dk / 2; i += kThreads) {
+        const int lo = (i / hh) * 2 * hh + i % hh;  // rows are Dk wide and Dk is a power of two
+        const float u = qs[lo], v = qs[lo + hh];
+        qs[lo] = u + v;
+        qs[lo + hh] = u - v;
+      }
+    }
+    __syncthreads();
+    const float sc = rotation_scale(31 - __builtin_clz(unsigned(Dk)));
+    for (int i = tid; i < G * Dk; i += kThreads) qs[i] *= sc;
   }
 
   // HeadQ side code: pr[i][k] = (U^T q_i)_k in the same scaled units as the scores

@@ -60,6 +60,7 @@
 
 #include "kvq_decode_common.hpp"
 #include "kvq_internal.hpp"
+#include "kvq_rotate.hpp"
 
 namespace kvq {
 namespace {
@@ -302,35 +303,6 @@ struct Lds {
   static constexpr int kBytes = kSlots * kSlot + (kInSlot ? 0 : kTiles);
   static_assert(kQB1 <= kSlot && kG * 32 * 4 <= kSlot && kG * (DV + NGV) * 4 <= kSlots * kSlot, "aliases");
 };
-
-// 8 consecutive query elements starting at i0 (a multiple of 8; the array is
-// 16-byte aligned) as floats
-__device__ __forceinline__ void load_q8(const void* p, int qdt, int64_t i0, float (&x)[8]) {
-  if (qdt == KVQ_BF16) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + i0);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      x[2 * d] = __uint_as_float(w[d] << 16);
-      x[2 * d + 1] = __uint_as_float(w[d] & 0xFFFF0000u);
-    }
-  } else if (qdt == KVQ_F16) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + i0);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const half2_t hh = as_half2(w[d]);
-      x[2 * d] = float(hh[0]);
-      x[2 * d + 1] = float(hh[1]);
-    }
-  } else {
-    const f32x4* f = reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i0);
-    const f32x4 u = f[0], v = f[1];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      x[d] = u[d];
-      x[4 + d] = v[d];
-    }
-  }
-}
 
 // Sum (or max) of v over the 16 lanes l with l % 4 == lane % 4: two rotations
 // inside each row of 16, then the two gfx950 half swaps across rows; every lane
@@ -607,6 +579,27 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
       qx[d] = __uint_as_float(qw0[d]);
       qx[4 + d] = __uint_as_float(qw1[d]);
     }
+  }
+
+  if (a.L.flags & KVQ_KEY_ROTATION) {
+    // the packed keys are rotated: rotate the query the same way.  Channel
+    // 8 tb + k of the task: butterflies 1, 2, 4 over k in registers, then bit s of
+    // tb, which is bit s of kk_t (lane ^ 16 << s) for s < log2 KK, else bit
+    // s - log2 KK of gq_t (lane ^ 4 << (s - log2 KK)); lanes without a task
+    // exchange only among themselves
+    constexpr int LKK = KK == 1 ? 0 : (KK == 2 ? 1 : (KK == 4 ? 2 : 3));
+    static_assert((1 << LKK) == KK, "power-of-two key width");
+    butterflies8(qx);
+#pragma unroll
+    for (int st = 0; st < LKK + 2; ++st) {
+      const int pl = st < LKK ? (16 << st) : (4 << (st - LKK));
+      const bool up = ((tb >> st) & 1) != 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qx[k] = butterfly(qx[k], __shfl_xor(qx[k], pl), up);
+    }
+    const float sc = rotation_scale(LKK + 5);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qx[k] *= sc;
   }
 
   // ---------------------------------------------------------------- set-up
@@ -922,20 +915,26 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   if (unit < nRT) {
     // B2: q 2^-E split hi/lo, entry (kk*4 + gq)*8 + i + 4*part, channels of block
     // gq*KK + kk in natural order (dword d = channels 2d, 2d+1); query i = e % 4
-    // is this lane's query
-    for (int e = lane; e < KK * 32; e += 64) {
+    // is this lane's query.  The channels are the Q' task of lane 16 kk + 4 gq + i,
+    // whose q 2^-E (qzv, after any rotation) is read across lanes.
+    // (every lane runs the same passes, so that the cross-lane reads see all lanes;
+    // lanes past the last entry read a lane in range and store nothing)
+    for (int e0 = 0; e0 < KK * 32; e0 += 64) {
+      const int e = e0 + lane;
       const int gqe = (e >> 3) & 3, kke = e >> 5, part = (e >> 2) & 1;
+      const int src = (16 * kke + 4 * gqe + (e & 3)) & 63;
       float x[8];
-      load_q8(a.q, a.q_dtype, qhead + (e & 3) * DK + 8 * (gqe * KK + kke), x);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = __shfl(qzv[k], src);
       u32x4 v;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const float x0 = x[2 * d] * (a.scale * kLog2e) * qe, x1 = x[2 * d + 1] * (a.scale * kLog2e) * qe;
+        const float x0 = x[2 * d], x1 = x[2 * d + 1];
         const half2_t hh = __builtin_convertvector(float2_t{x0, x1}, half2_t);
         const half2_t ll = __builtin_convertvector(float2_t{x0 - float(hh[0]), x1 - float(hh[1])}, half2_t);
         v[d] = __builtin_bit_cast(uint32_t, part ? ll : hh);
       }
-      B2[e] = v;
+      if (e < KK * 32) B2[e] = v;
     }
     wave_lds_sync();
     const uint8_t* kr = static_cast<const uint8_t*>(a.cache.k_fp16) + slab * a.r_stride * (DK * 2);

@@ -37,6 +37,7 @@
 
 #include "kvq_internal.hpp"
 #include "kvq_retention.hpp"
+#include "kvq_rotate.hpp"
 #include "kvq_vlayout.hpp"
 
 #pragma clang fp contract(off)
@@ -236,6 +237,56 @@ __device__ __forceinline__ void or_code(uint32_t* w, int bit, uint32_t code) {
   }
 }
 
+// Key rotation of the wave's 8 rows as pack_kernel holds them: channels 2cp and
+// 2cp + 1 of pair block k (cp = lane + 64k) in x[k][t].x / .y, so channel bit 0 is
+// the pair, bits 1 .. 6 the lane and bits 7 .. the block.  Butterfly h = 1 in the
+// pair, 2 .. 64 with lane ^ h/2, 128 and up across blocks, in increasing h; lanes
+// past the row hold zeros and meet only each other.
+template <int P>
+__device__ __forceinline__ void rotate_pair_rows(float2 (&x)[P][8], int lane, int Dk) {
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    if (128 * k >= Dk) break;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float u = x[k][t].x, v = x[k][t].y;
+      x[k][t] = make_float2(u + v, u - v);
+    }
+  }
+  for (int hl = 1; hl < 64 && 2 * hl < Dk; hl <<= 1) {
+    const bool upper = (lane & hl) != 0;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      if (128 * k >= Dk) break;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        x[k][t].x = butterfly(x[k][t].x, __shfl_xor(x[k][t].x, hl), upper);
+        x[k][t].y = butterfly(x[k][t].y, __shfl_xor(x[k][t].y, hl), upper);
+      }
+    }
+  }
+#pragma unroll
+  for (int hk = 1; hk < P; hk <<= 1) {
+    if (128 * hk >= Dk) break;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      if ((k & hk) || 128 * (k + hk) >= Dk) continue;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float2 u = x[k][t], v = x[k + hk][t];
+        x[k][t] = make_float2(u.x + v.x, u.y + v.y);
+        x[k + hk][t] = make_float2(u.x - v.x, u.y - v.y);
+      }
+    }
+  }
+  const float sc = rotation_scale(31 - __builtin_clz(unsigned(Dk)));
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x[k][t] = make_float2(x[k][t].x * sc, x[k][t].y * sc);
+  }
+}
+
 template <int DT, int KB, int VB>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
   __shared__ int32_t row_s[KVQ_GROUP];
@@ -289,9 +340,15 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
 #pragma unroll
     for (int k = 0; k < kMaxPairBlocks; ++k) {
       const int cp = lane + 64 * k;
-      if (2 * cp < Dk) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) kx[k][t] = load_pair<DT>(a.K, (slab * a.t_count + rows[t]) * Dk + 2 * cp);
+      for (int t = 0; t < 8; ++t)
+        kx[k][t] = 2 * cp < Dk ? load_pair<DT>(a.K, (slab * a.t_count + rows[t]) * Dk + 2 * cp) : make_float2(0.0f, 0.0f);
+    }
+    if (a.L.flags & KVQ_KEY_ROTATION) rotate_pair_rows(kx, lane, Dk);
+#pragma unroll
+    for (int k = 0; k < kMaxPairBlocks; ++k) {
+      const int cp = lane + 64 * k;
+      if (2 * cp < Dk) {
         float2 mn = kx[k][0], mx = kx[k][0];
 #pragma unroll
         for (int t = 1; t < 8; ++t) {
@@ -466,11 +523,55 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
     const int64_t row = retained_position(rr, r) - a.t_begin;  // row in the chunk
     uint16_t* kd = static_cast<uint16_t*>(a.cache.k_fp16) + (slab * a.r_stride + r) * Dk;
     uint16_t* vd = static_cast<uint16_t*>(a.cache.v_fp16) + (slab * a.r_stride + r) * Dv;
-    for (int c = lt; c < Dk; c += kPackThreads / kRetRowsPerBlock)
-      out_store(kd + c, f16_bits_rne(load_elem<DT>(a.K, (slab * a.t_count + row) * Dk + c)));
+    static_assert(kPackThreads / kRetRowsPerBlock == 64 && KVQ_MAX_HEAD_DIM <= 256, "one wave per retained row");
+    if (a.L.flags & KVQ_KEY_ROTATION) {
+      // the wave holds the row as x[j] = channel lane + 64j: butterflies h = 1 .. 32
+      // with lane ^ h, then 64 and 128 across j
+      float x[4];
+#pragma unroll
+      for (int j2 = 0; j2 < 4; ++j2) {
+        const int c = lt + 64 * j2;
+        x[j2] = c < Dk ? load_elem<DT>(a.K, (slab * a.t_count + row) * Dk + c) : 0.0f;
+      }
+      for (int hl = 1; hl < 64 && hl < Dk; hl <<= 1) {
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2) x[j2] = butterfly(x[j2], __shfl_xor(x[j2], hl), (lt & hl) != 0);
+      }
+      if (Dk > 64) {
+        const float u0 = x[0], u1 = x[1], u2 = x[2], u3 = x[3];
+        x[0] = u0 + u1; x[1] = u0 - u1; x[2] = u2 + u3; x[3] = u2 - u3;
+      }
+      if (Dk > 128) {
+        const float u0 = x[0], u1 = x[1], u2 = x[2], u3 = x[3];
+        x[0] = u0 + u2; x[1] = u1 + u3; x[2] = u0 - u2; x[3] = u1 - u3;
+      }
+      const float sc = rotation_scale(31 - __builtin_clz(unsigned(Dk)));
+#pragma unroll
+      for (int j2 = 0; j2 < 4; ++j2) {
+        const int c = lt + 64 * j2;
+        if (c < Dk) out_store(kd + c, f16_bits_rne(x[j2] * sc));
+      }
+    } else {
+      for (int c = lt; c < Dk; c += kPackThreads / kRetRowsPerBlock)
+        out_store(kd + c, f16_bits_rne(load_elem<DT>(a.K, (slab * a.t_count + row) * Dk + c)));
+    }
     for (int c = lt; c < Dv; c += kPackThreads / kRetRowsPerBlock)
       out_store(vd + c, f16_bits_rne(load_elem<DT>(a.V, (slab * a.t_count + row) * Dv + c)));
   }
+}
+
+// Key rotation of a 128-wide row held by 16 consecutive lanes, lane c owning
+// channels 8c .. 8c+7: butterflies 1, 2, 4 in registers, 8 .. 64 with lane c ^ h/8.
+__device__ __forceinline__ void rotate_row128(float (&x)[8], int c) {
+  butterflies8(x);
+#pragma unroll
+  for (int hl = 1; hl < 16; hl <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = butterfly(x[k], __shfl_xor(x[k], hl), (c & hl) != 0);
+  }
+  const float sc = rotation_scale(7);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] *= sc;
 }
 
 // Pack kernel for the common shape: Dk = Dv = 128, 32-token key groups, 2/4/8-bit
@@ -539,6 +640,23 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
           vo[k] = vw[k];
         }
       }
+      if (a.L.flags & KVQ_KEY_ROTATION) {
+        // the row's 16 threads are 16 consecutive lanes (i % 16 == lane % 16)
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if constexpr (DT == KVQ_BF16) {
+            x[2 * k] = __uint_as_float(kw[k] << 16);
+            x[2 * k + 1] = __uint_as_float(kw[k] & 0xFFFF0000u);
+          } else {
+            x[2 * k] = __half2float(__ushort_as_half(uint16_t(kw[k] & 0xFFFFu)));
+            x[2 * k + 1] = __half2float(__ushort_as_half(uint16_t(kw[k] >> 16)));
+          }
+        }
+        rotate_row128(x, i % 16);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ko[k] = uint32_t(f16_bits_rne(x[2 * k])) | (uint32_t(f16_bits_rne(x[2 * k + 1])) << 16);
+      }
       out_store(reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.cache.k_fp16) + (slab * a.r_stride + r) * D + c8), ko);
       out_store(reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.cache.v_fp16) + (slab * a.r_stride + r) * D + c8), vo);
     }
@@ -583,6 +701,10 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
   float kx[2][8];
   widen(kraw[0], kx[0]);
   widen(kraw[1], kx[1]);
+  if (a.L.flags & KVQ_KEY_ROTATION) {  // wave-uniform
+    rotate_row128(kx[0], c);
+    rotate_row128(kx[1], c);
+  }
 
   // ---------------------------------------------------------------- keys
   {
@@ -765,7 +887,26 @@ __global__ __launch_bounds__(kPackThreads) void key_range_kernel(const PackArgs 
   const int nsl = kPackThreads / Dk;
   const int c = tid % Dk, sl = tid / Dk;
   float mn = INFINITY, mx = -INFINITY;
-  if (sl < nsl) {
+  if (a.L.flags & KVQ_KEY_ROTATION) {
+    // rotated keys: Dk is a power of two, so the workgroup is nsl whole rows and
+    // every thread takes part; each pass rotates nsl rows through LDS, butterflies
+    // in increasing h (partner channel c ^ h of the same row)
+    for (int t0 = 0; t0 < kg; t0 += nsl) {
+      const int t = t0 + sl;
+      const int64_t row = (plain ? q0 + t : quantized_position(rr, q0 + t)) - a.t_begin;
+      float x = load_elem<DT>(a.K, (slab * a.t_count + row) * Dk + c);
+      for (int hh = 1; hh < Dk; hh <<= 1) {
+        mn_s[tid] = x;
+        __syncthreads();
+        const float partner = mn_s[tid ^ hh];
+        __syncthreads();
+        x = butterfly(x, partner, (c & hh) != 0);
+      }
+      x *= rotation_scale(31 - __builtin_clz(unsigned(Dk)));
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+  } else if (sl < nsl) {
     for (int t = sl; t < kg; t += nsl) {
       const int64_t row = (plain ? q0 + t : quantized_position(rr, q0 + t)) - a.t_begin;
       const float x = load_elem<DT>(a.K, (slab * a.t_count + row) * Dk + c);

@@ -170,6 +170,18 @@ int kvq_stream_init_ex(kvq_stream* S, int B, int Hq, int Hkv, int Dk, int Dv, in
   return ok();
 }
 
+int kvq_stream_set_flags(kvq_stream* S, int flags) {
+  const int st = check_stream(S);
+  if (st != KVQ_OK) return st;
+  if (S->t != 0) return fail(KVQ_ERR_INVALID, "flags are set on an empty stream (t is %d)", S->t);
+  kvq_layout l = S->L;
+  l.flags = flags;
+  const int fs = kvq::check_format(l);
+  if (fs != KVQ_OK) return fs;
+  S->L = l;
+  return ok();
+}
+
 int kvq_stream_cache_sizes(const kvq_stream* S, size_t bytes_out[KVQ_NUM_CACHE_BUFFERS]) {
   const int st = check_stream(S);
   if (st != KVQ_OK) return st;

@@ -223,3 +223,38 @@ def test_key_group_limits(lib, T, n_recent, kg, status):
         # a chunk must not split a key group
         assert lib.kv_quant_pack(ctypes.byref(lay), 0, 32, ctypes.c_void_p(16), ctypes.c_void_p(16), L_.KVQ_BF16,
                                  ctypes.byref(L_.KvqCache()), None) == L_.KVQ_ERR_UNSUPPORTED
+
+
+def test_layout_and_stream_flags(lib):
+    """Key rotation is a layout flag: set on a power-of-two key width, refused
+    otherwise, unknown bits refused, the layout untouched by a refused call; side
+    codes refuse a flagged layout; a stream takes flags only while empty."""
+    st, lay = _layout(lib, 1, 4, 2, 128, 128, 256, 4, 2, 0, 0)
+    assert st == L_.KVQ_OK and lay.flags == 0
+    assert lib.kvq_layout_set_flags(ctypes.byref(lay), L_.KVQ_KEY_ROTATION) == L_.KVQ_OK
+    assert lay.flags == L_.KVQ_KEY_ROTATION
+    assert lib.kvq_layout_set_flags(ctypes.byref(lay), 2) == L_.KVQ_ERR_INVALID
+    assert lay.flags == L_.KVQ_KEY_ROTATION
+    st, lay96 = _layout(lib, 1, 4, 2, 96, 128, 256, 4, 2, 0, 0)
+    assert lib.kvq_layout_set_flags(ctypes.byref(lay96), L_.KVQ_KEY_ROTATION) == L_.KVQ_ERR_UNSUPPORTED
+    assert lay96.flags == 0
+    bad = L_.KvqLayout.from_buffer_copy(lay)
+    bad.flags = 4                                                  # set behind the library's back
+    cache = _cache()
+    assert lib.kv_quant_pack(ctypes.byref(bad), 0, 256, FAKE, FAKE, L_.KVQ_BF16, ctypes.byref(cache),
+                             None) == L_.KVQ_ERR_INVALID
+    side = L_.KvqSide(FAKE, FAKE, FAKE)
+    assert lib.kv_side_pack(ctypes.byref(lay), 4, 4, FAKE, FAKE, L_.KVQ_BF16, ctypes.byref(cache),
+                            ctypes.byref(side), None) == L_.KVQ_ERR_UNSUPPORTED
+    S = L_.KvqStream()
+    assert lib.kvq_stream_init(ctypes.byref(S), 1, 4, 1, 64, 64, 200, 4, 2, 8, 0) == L_.KVQ_OK
+    assert lib.kvq_stream_set_flags(ctypes.byref(S), 8) == L_.KVQ_ERR_INVALID
+    assert lib.kvq_stream_set_flags(ctypes.byref(S), L_.KVQ_KEY_ROTATION) == L_.KVQ_OK
+    assert S.L.flags == L_.KVQ_KEY_ROTATION
+    step = L_.KvqStreamStep()
+    assert lib.kvq_stream_plan(ctypes.byref(S), ctypes.byref(step)) == L_.KVQ_OK
+    assert lib.kvq_stream_set_flags(ctypes.byref(S), 0) == L_.KVQ_ERR_INVALID   # no longer empty
+    assert S.L.flags == L_.KVQ_KEY_ROTATION
+    S96 = L_.KvqStream()
+    assert lib.kvq_stream_init(ctypes.byref(S96), 1, 4, 1, 96, 64, 200, 4, 2, 8, 0) == L_.KVQ_OK
+    assert lib.kvq_stream_set_flags(ctypes.byref(S96), L_.KVQ_KEY_ROTATION) == L_.KVQ_ERR_UNSUPPORTED

@@ -92,8 +92,9 @@ def _run_stream(w: Workload, T0: int, T1: int, check_at, partitions, slabs=None,
         sl = make_slab(w, b, h, 0, T1)
         host[(b, h)] = (sl.K, sl.V)
     s = api.Stream(w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T, w.k_bits, w.v_bits, w.n_recent, w.log_window,
-                   v_group=w.v_group)
-    oracles = {bh: SlabStream(w.Dk, w.Dv, w.k_bits, w.v_bits, w.n_recent, w.log_window, w.v_group) for bh in slabs}
+                   v_group=w.v_group, key_rotation=w.key_rotation)
+    oracles = {bh: SlabStream(w.Dk, w.Dv, w.k_bits, w.v_bits, w.n_recent, w.log_window, w.v_group,
+                              key_rotation=w.key_rotation) for bh in slabs}
     if T0:
         s.prefill(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous())
         for bh, o in oracles.items():
@@ -190,6 +191,24 @@ def test_stream_three_bit_values_log_after_prefill():
                  n_recent=64, log_window=64, dtype="f32", seed=30, v_group=64)
     T0 = _valid_prefill(w, 900)
     _run_stream(w, T0, T0 + 300, {T0 + 1, T0 + 64, T0 + 299}, [1, 3])
+
+
+def test_stream_key_rotation_after_prefill():
+    """Rotated keys in a stream: K4V2 with log-spaced fp16 tokens after a prefill (the
+    pack kernel's rotated groups and rows), then appends that rotate each new key row
+    before its fp16 copy and form groups from rotated rows (MFMA decode, rotated q)."""
+    w = Workload("stream_k4v2_rot", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=1400, k_bits=4, v_bits=2,
+                 n_recent=64, log_window=64, dtype="bf16", seed=32, key_rotation=True)
+    T0 = _valid_prefill(w, 900)
+    _run_stream(w, T0, T0 + 200, {T0 + 1, T0 + 64, T0 + 199}, [1, 3])
+
+
+def test_stream_key_rotation_generic_from_empty():
+    """Rotated 64-wide keys, G = 2 (vector-ALU decode), float32 inputs, K8V4, from an
+    empty stream."""
+    w = Workload("stream_g2_rot", B=1, Hq=4, Hkv=2, Dk=64, Dv=64, T=300, k_bits=8, v_bits=4,
+                 n_recent=16, dtype="f32", seed=33, key_rotation=True)
+    _run_stream(w, 0, 200, {17, 48, 49, 112}, [1, 2])
 
 
 def test_stream_full_capacity_and_errors():

@@ -124,4 +124,20 @@ def small_cases():
                  n_recent=40, dtype="f16", partitions=5, seed=29),
         Workload("small_g2_k4v4_f16_log", B=1, Hq=4, Hkv=2, Dk=64, Dv=96, T=579, k_bits=4, v_bits=4,
                  n_recent=0, log_window=32, dtype="f16", partitions=3, seed=30),
+        # keys rotated before quantization (every pack and decode path: 128-wide and
+        # generic pack, key groups of 64 tokens, retained rows, both decode kernels)
+        Workload("small_k4v2_rot", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=1064, k_bits=4, v_bits=2,
+                 n_recent=40, dtype="bf16", partitions=5, seed=31, key_rotation=True),
+        Workload("small_k2v2_log_rot_f16", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=2048, k_bits=2, v_bits=2,
+                 n_recent=64, log_window=64, dtype="f16", partitions=7, seed=32, key_rotation=True),
+        Workload("small_k8v4_thin_rot", B=2, Hq=8, Hkv=2, Dk=32, Dv=128, T=800, k_bits=8, v_bits=4,
+                 n_recent=32, dtype="bf16", partitions=3, seed=33, key_rotation=True),
+        Workload("small_k4v4_d64_rot_log", B=1, Hq=8, Hkv=2, Dk=64, Dv=128, T=1431, k_bits=4, v_bits=4,
+                 n_recent=32, log_window=32, dtype="bf16", partitions=3, seed=34, key_rotation=True),
+        Workload("small_g2_k8v4_kg64_rot_f32", B=1, Hq=4, Hkv=2, Dk=64, Dv=64, T=416, k_bits=8, v_bits=4,
+                 n_recent=32, dtype="f32", partitions=4, seed=35, k_group=64, key_rotation=True),
+        Workload("small_d256_k4v4_rot", B=1, Hq=2, Hkv=2, Dk=256, Dv=256, T=320, k_bits=4, v_bits=4,
+                 n_recent=32, dtype="bf16", partitions=2, seed=36, v_group=128, key_rotation=True),
+        Workload("small_k4v2_kg128_rot", B=1, Hq=8, Hkv=2, Dk=128, Dv=128, T=1064, k_bits=4, v_bits=2,
+                 n_recent=40, dtype="bf16", partitions=5, seed=37, k_group=128, key_rotation=True),
     ]
