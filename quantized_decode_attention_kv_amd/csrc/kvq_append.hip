@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       __syncthreads();
       x = butterfly(x, partner, (tid & hh) != 0);
     }
-    if (tid < Dk) knew16[tid] = to_f16_bits(x * rotation_scale(31 - __builtin_clz(unsigned(Dk))));
+    if (tid < Dk) knew16[tid] = to_f16_bits(rotation_scaled(x, rotation_scale(31 - __builtin_clz(unsigned(Dk)))));
     __syncthreads();
   }
   // the appended token's fp16 value of key / value channel c

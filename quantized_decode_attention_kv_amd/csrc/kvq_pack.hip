@@ -283,7 +283,7 @@ __device__ __forceinline__ void rotate_pair_rows(float2 (&x)[P][8], int lane, in
 #pragma unroll
   for (int k = 0; k < P; ++k) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) x[k][t] = make_float2(x[k][t].x * sc, x[k][t].y * sc);
+    for (int t = 0; t < 8; ++t) x[k][t] = make_float2(rotation_scaled(x[k][t].x, sc), rotation_scaled(x[k][t].y, sc));
   }
 }
 
@@ -549,7 +549,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
 #pragma unroll
       for (int j2 = 0; j2 < 4; ++j2) {
         const int c = lt + 64 * j2;
-        if (c < Dk) out_store(kd + c, f16_bits_rne(x[j2] * sc));
+        if (c < Dk) out_store(kd + c, f16_bits_rne(rotation_scaled(x[j2], sc)));
       }
     } else {
       for (int c = lt; c < Dk; c += kPackThreads / kRetRowsPerBlock)
@@ -571,7 +571,7 @@ __device__ __forceinline__ void rotate_row128(float (&x)[8], int c) {
   }
   const float sc = rotation_scale(7);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) x[k] *= sc;
+  for (int k = 0; k < 8; ++k) x[k] = rotation_scaled(x[k], sc);
 }
 
 // Pack kernel for the common shape: Dk = Dv = 128, 32-token key groups, 2/4/8-bit
@@ -902,7 +902,7 @@ __global__ __launch_bounds__(kPackThreads) void key_range_kernel(const PackArgs 
         __syncthreads();
         x = butterfly(x, partner, (c & hh) != 0);
       }
-      x *= rotation_scale(31 - __builtin_clz(unsigned(Dk)));
+      x = rotation_scaled(x, rotation_scale(31 - __builtin_clz(unsigned(Dk))));
       mn = fminf(mn, x);
       mx = fmaxf(mx, x);
     }

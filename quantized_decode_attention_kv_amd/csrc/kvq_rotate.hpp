@@ -17,6 +17,17 @@ __host__ __device__ inline float rotation_scale(int m) {
   return (m & 1) ? 0.70710677f * p : p;
 }
 
+// x times the scale, rounded to float32 on its own.  Left visible, a multiply
+// whose result is next converted to fp16 may be folded into one mixed-precision
+// instruction that rounds the exact product once, straight to fp16, which differs
+// from rounding to float32 first whenever the float32 product is an fp16 tie; the
+// empty asm hands the compiler an opaque float32 value.
+__device__ __forceinline__ float rotation_scaled(float x, float scale) {
+  float y = x * scale;
+  asm("" : "+v"(y));
+  return y;
+}
+
 // One butterfly of an element held apart from its partner (the element h away):
 // the lower element of the pair becomes self + partner, the upper partner - self.
 __device__ __forceinline__ float butterfly(float self, float partner, bool upper) {
