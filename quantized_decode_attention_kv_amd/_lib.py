@@ -4,7 +4,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvq.so")
+# KVQ_LIBRARY names another build of the same sources (the host sanitizer test
+# loads a host-only build through it); by default the in-tree libkvq.so
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(HERE, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP = 0, 1, 2, 3
 KVQ_F32, KVQ_F16, KVQ_BF16 = 0, 1, 2
