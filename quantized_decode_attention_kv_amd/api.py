@@ -94,17 +94,32 @@ def alloc_cache(layout: Layout, device="cuda"):
     return {k: torch.empty(shape, dtype=dt, device=device) for k, (shape, dt) in layout.shapes().items()}
 
 
-def _cache_struct(layout: Layout, cache):
+def _bind_cache(holder, shapes_fn, cache, allow_missing=True):
+    """The kvq_cache struct of `cache` for a layout or stream `holder`.  It is built
+    and checked once per set of tensor objects and reused while the same tensors
+    are passed again (a decode loop passes the same cache every step); replacing a
+    tensor's storage in place (``set_``) is not noticed."""
+    tensors = tuple(cache.get(k) for k in L_.CACHE_FIELDS)
+    memo = holder.__dict__.get("_cache_memo")
+    if memo is not None and all(a is b for a, b in zip(memo[0], tensors)):
+        return memo[1]
     c = L_.KvqCache()
-    for k, (shape, dt) in layout.shapes().items():
+    for k, (shape, dt) in shapes_fn().items():
         t = cache.get(k)
         if t is None:
+            if not allow_missing:
+                raise ValueError("cache[%r] is missing" % k)
             setattr(c, k, None)
             continue
         if tuple(t.shape) != tuple(shape) or t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
             raise ValueError("cache[%r] must be a contiguous CUDA %s tensor of shape %s" % (k, dt, shape))
         setattr(c, k, t.data_ptr() if t.numel() else None)
+    holder.__dict__["_cache_memo"] = (tensors, c)
     return c
+
+
+def _cache_struct(layout: Layout, cache):
+    return _bind_cache(layout, layout.shapes, cache)
 
 
 def _stream(stream):
@@ -279,13 +294,7 @@ class Stream:
     def _cache_struct(self):
         if self.cache is None:
             raise ValueError("this stream has no device buffers (created with device=None)")
-        c = L_.KvqCache()
-        for k, (shape, dt) in self.shapes().items():
-            t = self.cache[k]
-            if tuple(t.shape) != tuple(shape) or t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
-                raise ValueError("cache[%r] must be a contiguous CUDA %s tensor of shape %s" % (k, dt, shape))
-            setattr(c, k, t.data_ptr() if t.numel() else None)
-        return c
+        return _bind_cache(self, self.shapes, self.cache, allow_missing=False)
 
     def prefill(self, K, V, stream=None):
         """Start the (empty) stream from K [B, Hkv, T0, Dk], V [B, Hkv, T0, Dv]."""

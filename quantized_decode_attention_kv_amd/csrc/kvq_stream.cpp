@@ -113,6 +113,22 @@ int plan_step(kvq_stream& S, kvq_stream_step& step) {
   return KVQ_OK;
 }
 
+// Copy of a stream's state limited to the rows in use plus the one an append adds
+// (a step only touches rows below n_rows + 1): the row arrays are 20 KB, of which
+// a stream uses a few hundred entries.
+void copy_state(kvq_stream& dst, const kvq_stream& src) {
+  const int rows = std::min<int>(KVQ_STREAM_MAX_ROWS, src.n_rows + 1);
+  dst.L = src.L;
+  dst.t = src.t;
+  dst.n_groups = src.n_groups;
+  dst.n_rows = src.n_rows;
+  dst.n_pending = src.n_pending;
+  dst.g_cap = src.g_cap;
+  dst.r_cap = src.r_cap;
+  std::memcpy(dst.row_pos, src.row_pos, sizeof(int32_t) * size_t(rows));
+  std::memcpy(dst.row_pending, src.row_pending, size_t(rows));
+}
+
 int check_stream_cache(const kvq_cache* cache, bool groups) {
   int st;
   if (!cache) return fail(KVQ_ERR_INVALID, "cache is NULL");
@@ -208,10 +224,11 @@ int kvq_stream_plan(kvq_stream* S, kvq_stream_step* step) {
   int st = check_stream(S);
   if (st != KVQ_OK) return st;
   if (!step) return fail(KVQ_ERR_INVALID, "step is NULL");
-  kvq_stream next = *S;
+  kvq_stream next;
+  copy_state(next, *S);
   st = plan_step(next, *step);
   if (st != KVQ_OK) return st;
-  *S = next;
+  copy_state(*S, next);
   return ok();
 }
 
@@ -256,7 +273,8 @@ int kv_stream_append(kvq_stream* S, const void* k_new, const void* v_new, int kv
   if (!k_new || !v_new) return fail(KVQ_ERR_INVALID, "k_new or v_new is NULL");
   if (!kvq::aligned16(k_new) || !kvq::aligned16(v_new))
     return fail(KVQ_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
-  kvq_stream next = *S;
+  kvq_stream next;
+  copy_state(next, *S);
   kvq_stream_step step;
   st = plan_step(next, step);
   if (st != KVQ_OK) return st;
@@ -279,7 +297,7 @@ int kv_stream_append(kvq_stream* S, const void* k_new, const void* v_new, int kv
   a.cache = *cache;
   const hipError_t e = kvq::launch_append(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
-  *S = next;
+  copy_state(*S, next);
   return ok();
 }
 
