@@ -353,7 +353,7 @@ __device__ __forceinline__ float pick4(const float (&x)[kG], int i) {
 #ifndef KVQ_UNIT_SKEW_SPAN
 #define KVQ_UNIT_SKEW_SPAN 16
 #endif
-__device__ __forceinline__ int team_start(int t, int T, int TS, int nG, int R, int tq, int tm, int tc16) {
+__host__ __device__ inline int team_start(int t, int T, int TS, int nG, int R, int tq, int tm, int tc16) {
   const int64_t s = R > 1 ? KVQ_UNIT_SKEW_SPAN / (R - 1) : 0;
   int64_t wb = 0, wall = 0;
   for (int r = 0; r < R; ++r) {
@@ -369,13 +369,24 @@ __device__ __forceinline__ int team_start(int t, int T, int TS, int nG, int R, i
     // every team's share stays >= 1 group: 16 nG wmin / wall - TS c emax >= 16
     const int64_t wmin = 100 - s * (R - 1);
     const int64_t room = (16 * int64_t(nG) * wmin) / wall - 16;
-    c = room > 0 ? min(c, room / (int64_t(TS) * emax)) : 0;
+    c = room > 0 ? (c < room / (int64_t(TS) * emax) ? c : room / (int64_t(TS) * emax)) : 0;
   }
-  const int64_t e_before = int64_t(t) * tq + min(int64_t(t), tmt);
-  const int64_t e_all = int64_t(T) * tq + min(int64_t(T), tmt);
+  const int64_t e_before = int64_t(t) * tq + (int64_t(t) < tmt ? int64_t(t) : tmt);
+  const int64_t e_all = int64_t(T) * tq + (int64_t(T) < tmt ? int64_t(T) : tmt);
   const int64_t w16 = 16 * int64_t(nG) + int64_t(TS) * c * e_all;
   const int64_t st16 = w16 * wb / wall - int64_t(TS) * c * e_before;
-  return int(max(int64_t(0), min(int64_t(nG), st16 / 16)));
+  const int64_t g = st16 / 16;
+  return int(g < 0 ? 0 : (g > nG ? int64_t(nG) : g));
+}
+
+// Cost of a retained 32-row tile in sixteenths of a key group's time (measured:
+// about 2.5 groups' time where a tile is 4 groups' bytes, so 5/8 of the byte ratio).
+template <int DK, int DV, int KB, int VB>
+__host__ __device__ inline int tile_cost16(const kvq_layout& L) {
+  constexpr int64_t kTileBytes = 32 * (DK + DV) * 2;
+  const int64_t group_bytes = 32 * (DK * KB + DV * VB) / 8 + ((DK * 4) >> (L.k_group == 128 ? 2 : (L.k_group == 64 ? 1 : 0))) +
+                              ((DV / 32 * 32 * 4) >> (L.v_group == 128 ? 2 : (L.v_group == 64 ? 1 : 0)));
+  return int(16 * 5 * kTileBytes / (8 * group_bytes));
 }
 
 // Waves per SIMD that the LDS of one unit allows on a 160 KB compute unit (at most
@@ -447,14 +458,17 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   // retained tiles: this unit takes tiles unit, unit + U, ... (tq or tq + 1 of them)
   const int nRT = (R + 31) / 32;  // 32-row tiles of retained rows
   const int tq = nRT / U, tm = nRT % U;
-  // cost of a tile in sixteenths of a key group (measured: about 2.5 groups' time
-  // where a tile is 4 groups' bytes, so 5/8 of the byte ratio)
-  constexpr int64_t kTileBytes = 32 * (DK + DV) * 2;
-  const int64_t group_bytes = 32 * (DK * KB + DV * VB) / 8 + ((DK * 4) >> (a.L.k_group == 128 ? 2 : (a.L.k_group == 64 ? 1 : 0))) +
-                              ((DV / 32 * 32 * 4) >> (a.L.v_group == 128 ? 2 : (a.L.v_group == 64 ? 1 : 0)));
-  const int tc16 = int(16 * 5 * kTileBytes / (8 * group_bytes));
-  const int tg0 = team_start(team, T, TS, nG, a.ranks, tq, tm, tc16);
-  const int tg1 = team_start(team + 1, T, TS, nG, a.ranks, tq, tm, tc16);
+  // (the host passes the run starts of up to kMaxTeamTable teams with the launch:
+  // computing them here would delay the first copies by a few microseconds)
+  int tg0, tg1;
+  if (a.n_team_first > 0) {
+    tg0 = a.team_first[team];
+    tg1 = a.team_first[team + 1];
+  } else {
+    const int tc16 = tile_cost16<DK, DV, KB, VB>(a.L);
+    tg0 = team_start(team, T, TS, nG, a.ranks, tq, tm, tc16);
+    tg1 = team_start(team + 1, T, TS, nG, a.ranks, tq, tm, tc16);
+  }
   const int g0 = tg0 + (unit - team * TS);
   const int nj = g0 < tg1 ? (tg1 - g0 + TS - 1) / TS : 0;
 
@@ -1076,6 +1090,17 @@ hipError_t launch_depth(DecodeArgs a, hipStream_t stream, int dev, const DecodeP
   static_assert(lds <= 160 * 1024, "LDS budget");
   a.units = plan.units;
   a.ranks = plan.ranks;
+  {
+    // the teams' run starts, as the kernel would compute them (team_start)
+    const int U = a.units, TS = (U % kWavesPerGroup) == 0 ? kWavesPerGroup : 1, T = U / TS;
+    const int nRT = (a.L.R + 31) / 32, tq = nRT / U, tm = nRT % U;
+    const int tc16 = tile_cost16<DK, DV, KB, VB>(a.L);
+    a.n_team_first = 0;
+    if (T <= kMaxTeamTable) {
+      for (int t = 0; t <= T; ++t) a.team_first[t] = team_start(t, T, TS, a.L.n_groups, a.ranks, tq, tm, tc16);
+      a.n_team_first = T + 1;
+    }
+  }
   if constexpr (lds > 64 * 1024) {
     const hipError_t e = lds_optin<DK, DV, KB, VB, D>(dev, int(lds));
     if (e != hipSuccess) return e;

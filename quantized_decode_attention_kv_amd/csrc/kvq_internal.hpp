@@ -21,6 +21,8 @@ struct PackArgs {
   kvq_cache cache;
 };
 
+constexpr int kMaxTeamTable = 128;  // teams per slab whose run starts travel with the launch
+
 struct DecodeArgs {
   kvq_layout L;
   const void* q;
@@ -31,6 +33,11 @@ struct DecodeArgs {
   int64_t g_stride, r_stride;  // key groups / fp16 rows per slab in the cache arrays (>= n_groups, R)
   int units;           // work units per slab of the matrix-core kernel (set by its launcher)
   int ranks;           // waves per SIMD the matrix-core grid puts on the device at once (1..4)
+  // first key group of each team's run, teams 0 .. T (set by the matrix-core
+  // launcher on the host when T <= kMaxTeamTable; n_team_first = 0: the kernel
+  // computes them itself)
+  int n_team_first;
+  int team_first[kMaxTeamTable + 1];
   float* partials;     // [B * Hq, units, Dv + 4]: m (log2 domain), l, 2 unused, unnormalised o (P > 1)
   float* out;          // [B, Hq, Dv]
   // HeadQ side code (side_rank == 0: none; the vector-ALU kernel then adds the
