@@ -180,10 +180,11 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float 
 
 // quant_code for N elements with one check: when no element's fast quotient lies
 // within 2^-12 of a half-integer (the usual case) no element takes the division, and
-// the wave tests that once instead of once per element.
+// the wave tests that once instead of once per element.  The codes come back as
+// exact integers held in floats (clamped with one med3).
 template <int N>
-__device__ __forceinline__ void quant_codes(const float (&x)[N], const float (&s)[N], const float (&z)[N],
-                                            const float (&r)[N], float levels, uint32_t (&code)[N]) {
+__device__ __forceinline__ void quant_levels(const float (&x)[N], const float (&s)[N], const float (&z)[N],
+                                             const float (&r)[N], float levels, float (&code)[N]) {
   float u[N], rt[N];
   float worst = 0.0f;
 #pragma unroll
@@ -201,7 +202,14 @@ __device__ __forceinline__ void quant_codes(const float (&x)[N], const float (&s
     }
   }
 #pragma unroll
-  for (int k = 0; k < N; ++k) code[k] = uint32_t(fminf(fmaxf(rt[k], 0.0f), levels));
+  for (int k = 0; k < N; ++k) code[k] = __builtin_amdgcn_fmed3f(rt[k], 0.0f, levels);
+}
+
+// Byte `b` of `w` replaced by the code q (an integer in [0, 255] held as a float,
+// so the conversion is exact whatever its rounding): one instruction that both
+// converts and places the code.
+__device__ __forceinline__ uint32_t put_byte(float q, uint32_t b, uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_u8_f32(q, b, w);
 }
 
 // Every output of the pack is written with streaming (non-temporal) stores: the
@@ -753,16 +761,29 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint32_t lo = 0, hi = 0;  // channels 8c .. 8c+7 at bits (k * KB) of a 64-bit field
-      uint32_t codes[8];
-      quant_codes<8>(kx[j], ks, kz, kr, k_levels, codes);
+      float q[8];
+      quant_levels<8>(kx[j], ks, kz, kr, k_levels, q);
+      if constexpr (KB == 8) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t code = codes[k];
-        if constexpr (KB == 8) {
-          if (k < 4) lo |= code << (8 * k); else hi |= code << (8 * (k - 4));
-        } else {
-          lo |= code << (KB * k);
+        for (int k = 0; k < 4; ++k) {
+          lo = put_byte(q[k], k, lo);
+          hi = put_byte(q[4 + k], k, hi);
         }
+      } else if constexpr (KB == 4) {
+        // even channels in the low nibbles of the bytes, odd ones in the high
+        uint32_t ev = 0, od = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          ev = put_byte(q[2 * k], k, ev);
+          od = put_byte(q[2 * k + 1], k, od);
+        }
+        lo = ev | (od << 4);
+      } else {
+        // channel k at bits 2k: byte k / 4, bit pair k % 4
+        uint32_t f[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k & 3] = put_byte(q[k], k >> 2, f[k & 3]);
+        lo = f[0] | (f[1] << 2) | (f[2] << 4) | (f[3] << 6);
       }
       uint32_t* rowp = kdst + uint32_t(tok[j] * kWords);
       if constexpr (KB == 8) {
@@ -829,18 +850,20 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
     // the lane's codes: tile t = c / 2, columns 8 (c % 2) + k, tokens pair (p, p + 4)
     const int t = c >> 1, hc = c & 1;
     const int chunk = t / kTilesPerWord, slot = t % kTilesPerWord;
-    uint32_t part[8], c0[8], c1[8];
+    uint32_t part[8];
+    float c0[8], c1[8];
     {
       float s8[8], z8[8], r8[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) { s8[k] = vs[0]; z8[k] = vz[0]; r8[k] = vr[0]; }
-      quant_codes<8>(vx[0], s8, z8, r8, v_levels, c0);
+      quant_levels<8>(vx[0], s8, z8, r8, v_levels, c0);
 #pragma unroll
       for (int k = 0; k < 8; ++k) { s8[k] = vs[1]; z8[k] = vz[1]; r8[k] = vr[1]; }
-      quant_codes<8>(vx[1], s8, z8, r8, v_levels, c1);
+      quant_levels<8>(vx[1], s8, z8, r8, v_levels, c1);
     }
+    // token p's code at bit slot * VB, token p + 4's 16 bits higher
 #pragma unroll
-    for (int k = 0; k < 8; ++k) part[k] = (c0[k] << (slot * VB)) | (c1[k] << (16 + slot * VB));
+    for (int k = 0; k < 8; ++k) part[k] = put_byte(c1[k], 2, put_byte(c0[k], 0, 0u)) << (slot * VB);
     // column n = 8 hc + k: word (field (n * 4 + p) of the octet, chunk), slot t % TPW;
     // (word, slot) = 8 (n * 4 + p) + t since a field's chunks hold 8 tiles' slots
 #pragma unroll
