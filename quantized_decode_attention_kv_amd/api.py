@@ -6,6 +6,7 @@ computation runs in the library's HIP kernels.  Names follow include/kvq.h.
 
 import ctypes
 import math
+import types
 
 import torch
 
@@ -25,21 +26,17 @@ class Layout:
                                         n_recent, log_window, k_group, v_group))
         if key_rotation:
             L_.check(lib.kvq_layout_set_flags(ctypes.byref(self._c), L_.KVQ_KEY_ROTATION))
+        # the fields never change after this point: plain attributes, so that the
+        # per-call wrappers read them without a lookup into the struct
+        self.__dict__.update({f: getattr(self._c, f) for f in L_.LAYOUT_FIELDS})
+        self.ref = ctypes.byref(self._c)
+        self._ws = {}
 
     @classmethod
     def from_workload(cls, w, T=None):
         return cls(w.B, w.Hq, w.Hkv, w.Dk, w.Dv, w.T if T is None else T, w.k_bits, w.v_bits,
                    w.n_recent, w.log_window, getattr(w, "v_group", 32), getattr(w, "k_group", 32),
                    getattr(w, "key_rotation", False))
-
-    def __getattr__(self, name):
-        if name in L_.LAYOUT_FIELDS:
-            return getattr(self._c, name)
-        raise AttributeError(name)
-
-    @property
-    def ref(self):
-        return ctypes.byref(self._c)
 
     def cache_sizes(self):
         arr = (ctypes.c_size_t * L_.KVQ_NUM_CACHE_BUFFERS)()
@@ -56,7 +53,10 @@ class Layout:
         return int(L_.load().kvq_quantized_before(self.ref, t))
 
     def workspace_bytes(self, num_partitions: int) -> int:
-        return int(L_.load().kvq_decode_workspace_bytes(self.ref, num_partitions))
+        n = self._ws.get(num_partitions)
+        if n is None:
+            n = self._ws[num_partitions] = int(L_.load().kvq_decode_workspace_bytes(self.ref, num_partitions))
+        return n
 
     def shapes(self):
         """Tensor shape and dtype of each cache buffer (codes as int32 bit patterns)."""
@@ -122,10 +122,18 @@ def _cache_struct(layout: Layout, cache):
     return _bind_cache(layout, layout.shapes, cache)
 
 
-def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, t=None):
+    """The HIP stream to enqueue on: `stream`, else the current stream of the device
+    tensor t lives on (read without building a Stream object: a decode loop asks
+    once per call), else of the current device."""
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    if t is not None and _raw_stream is not None:
+        return ctypes.c_void_p(_raw_stream(t.get_device()))
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 def _check_tensor(name, t, shape):
@@ -150,7 +158,7 @@ def kv_quant_pack(layout: Layout, K, V, cache=None, t_begin: int = 0, stream=Non
     cs = _cache_struct(layout, cache)
     L_.check(L_.load().kv_quant_pack(layout.ref, t_begin, t_count, ctypes.c_void_p(K.data_ptr()),
                                      ctypes.c_void_p(V.data_ptr()), _DTYPE_CODES[K.dtype], ctypes.byref(cs),
-                                     _stream(stream)))
+                                     _stream(stream, K)))
     return cache
 
 
@@ -182,7 +190,7 @@ def kv_decode_attn(layout: Layout, q, cache, num_partitions: int = 1, softmax_sc
     L_.check(L_.load().kv_decode_attn_ex(layout.ref, ctypes.c_void_p(q.data_ptr()), _DTYPE_CODES[q.dtype],
                                          ctypes.byref(cs), ctypes.c_float(softmax_scale), num_partitions,
                                          ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(out.data_ptr()),
-                                         _stream(stream), ctypes.c_void_p(ev)))
+                                         _stream(stream, q), ctypes.c_void_p(ev)))
     return out
 
 
@@ -201,7 +209,7 @@ def kv_decode_attn_noalloc(layout: Layout, q, cache, num_partitions: int = 1, so
     cs = _cache_struct(layout, cache)
     L_.check(L_.load().kv_decode_attn_noalloc(layout.ref, ctypes.c_void_p(q.data_ptr()), _DTYPE_CODES[q.dtype],
                                               ctypes.byref(cs), ctypes.c_float(softmax_scale), num_partitions,
-                                              ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+                                              ctypes.c_void_p(out.data_ptr()), _stream(stream, q)))
     return out
 
 
@@ -216,7 +224,7 @@ def kvq_read_probe(buf, sink=None, stream=None):
     if sink is None:
         sink = torch.empty(1, dtype=torch.int32, device=buf.device)
     L_.check(L_.load().kvq_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
-                                      ctypes.c_void_p(sink.data_ptr()), _stream(stream)))
+                                      ctypes.c_void_p(sink.data_ptr()), _stream(stream, buf)))
     return sink
 
 
@@ -236,7 +244,20 @@ class Stream:
             L_.check(lib.kvq_stream_set_flags(ctypes.byref(self._c), L_.KVQ_KEY_ROTATION))
         self.cache = None
         if device is not None:
-            self.cache = {k: torch.empty(shape, dtype=dt, device=device) for k, (shape, dt) in self.shapes().items()}
+            # read-only view: the buffers are the stream's for its whole life, so the
+            # kvq_cache struct is built once (a new mapping assigned to `cache` is
+            # bound again)
+            self.cache = types.MappingProxyType(
+                {k: torch.empty(shape, dtype=dt, device=device) for k, (shape, dt) in self.shapes().items()})
+        self._lib = lib
+        self._ref = ctypes.byref(self._c)
+        self._ws = {}
+        # the format fields never change: plain attributes (the stream's state fields
+        # t, n_groups, ... are read from the struct on every access)
+        self.__dict__.update({f: getattr(self._c.L, f) for f in ("B", "Hq", "Hkv", "Dk", "Dv", "k_bits", "v_bits",
+                                                                  "n_recent", "log_window", "k_group", "v_group")})
+        self._kshape = torch.Size((B, Hkv, Dk))
+        self._vshape = torch.Size((B, Hkv, Dv))
 
     def __getattr__(self, name):
         if name in L_.STREAM_FIELDS:
@@ -274,7 +295,10 @@ class Stream:
         return dict(zip(L_.CACHE_FIELDS, list(arr)))
 
     def workspace_bytes(self, num_partitions: int) -> int:
-        return int(L_.load().kvq_stream_workspace_bytes(self.ref, num_partitions))
+        n = self._ws.get(num_partitions)
+        if n is None:
+            n = self._ws[num_partitions] = int(L_.load().kvq_stream_workspace_bytes(self.ref, num_partitions))
+        return n
 
     def row_positions(self):
         """Position of the token held by each fp16 row in use."""
@@ -296,6 +320,14 @@ class Stream:
             raise ValueError("this stream has no device buffers (created with device=None)")
         return _bind_cache(self, self.shapes, self.cache, allow_missing=False)
 
+    def _cache_ref(self):
+        """byref of the bound kvq_cache struct, rebuilt only when `cache` is replaced."""
+        bound = self.__dict__.get("_bound")
+        if bound is None or bound[0] is not self.cache:
+            bound = (self.cache, ctypes.byref(self._cache_struct()))
+            self.__dict__["_bound"] = bound
+        return bound[1]
+
     def prefill(self, K, V, stream=None):
         """Start the (empty) stream from K [B, Hkv, T0, Dk], V [B, Hkv, T0, Dv]."""
         T0 = K.shape[2]
@@ -306,17 +338,19 @@ class Stream:
         cs = self._cache_struct()
         L_.check(L_.load().kv_stream_prefill(self.ref, T0, ctypes.c_void_p(K.data_ptr()),
                                              ctypes.c_void_p(V.data_ptr()), _DTYPE_CODES[K.dtype], ctypes.byref(cs),
-                                             _stream(stream)))
+                                             _stream(stream, K)))
 
     def append(self, k, v, stream=None):
-        """Append one token: k [B, Hkv, Dk], v [B, Hkv, Dv] on the GPU."""
-        _check_tensor("k", k, (self.B, self.Hkv, self.Dk))
-        _check_tensor("v", v, (self.B, self.Hkv, self.Dv))
-        if k.dtype != v.dtype:
+        """Append one token: k [B, Hkv, Dk], v [B, Hkv, Dv] on the GPU.  (Called once
+        per decode step: the checks read as few attributes as possible.)"""
+        code = _DTYPE_CODES.get(k.dtype)
+        if (code is None or k.dtype != v.dtype or k.shape != self._kshape or v.shape != self._vshape
+                or not (k.is_cuda and v.is_cuda and k.is_contiguous() and v.is_contiguous())):
+            _check_tensor("k", k, tuple(self._kshape))
+            _check_tensor("v", v, tuple(self._vshape))
             raise ValueError("k and v must share a dtype")
-        cs = self._cache_struct()
-        L_.check(L_.load().kv_stream_append(self.ref, ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-                                            _DTYPE_CODES[k.dtype], ctypes.byref(cs), _stream(stream)))
+        L_.check(self._lib.kv_stream_append(self._ref, k.data_ptr(), v.data_ptr(), code, self._cache_ref(),
+                                            _stream(stream, k)))
 
     def decode(self, q, num_partitions: int = 1, softmax_scale=None, out=None, workspace=None, stream=None):
         """Decode attention of q [B, Hq, Dk] over the stream's tokens -> float32 [B, Hq, Dv]."""
@@ -332,11 +366,9 @@ class Stream:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        cs = self._cache_struct()
-        L_.check(L_.load().kv_stream_decode(self.ref, ctypes.c_void_p(q.data_ptr()), _DTYPE_CODES[q.dtype],
-                                            ctypes.byref(cs), ctypes.c_float(softmax_scale), num_partitions,
-                                            ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(out.data_ptr()),
-                                            _stream(stream)))
+        L_.check(self._lib.kv_stream_decode(self._ref, q.data_ptr(), _DTYPE_CODES[q.dtype], self._cache_ref(),
+                                            ctypes.c_float(softmax_scale), num_partitions, ws_ptr, ws_bytes,
+                                            out.data_ptr(), _stream(stream, q)))
         return out
 
 
@@ -358,7 +390,7 @@ def side_pack(layout: Layout, K, cache, U, side_bits: int = 8, stream=None):
     cs = _cache_struct(layout, cache)
     L_.check(L_.load().kv_side_pack(layout.ref, r, side_bits, ctypes.c_void_p(U.data_ptr()),
                                     ctypes.c_void_p(K.data_ptr()), _DTYPE_CODES[K.dtype], ctypes.byref(cs),
-                                    ctypes.byref(side), _stream(stream)))
+                                    ctypes.byref(side), _stream(stream, K)))
     return codes, scale, zero
 
 
@@ -379,5 +411,5 @@ def kv_decode_attn_side(layout: Layout, q, cache, U, side, num_partitions: int =
         ctypes.c_void_p(U.data_ptr()), ctypes.byref(sd), ctypes.c_float(softmax_scale), num_partitions,
         ctypes.c_void_p(workspace.data_ptr() if workspace is not None else None),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
-        ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+        ctypes.c_void_p(out.data_ptr()), _stream(stream, q)))
     return out
