@@ -22,10 +22,12 @@
 // The folded operands q_c s_c and p_t s_t,g are split into fp16 hi + lo parts
 // (each rounded to nearest, about 22 significant bits together).
 //
-// Work units: one wave per contiguous run of key groups of one (batch, kv head)
-// slab, four independent waves per workgroup (one on each SIMD of a compute
-// unit, see kWavesPerGroup); a split-K partition is one run or is cut into 2 or 4
-// (see decode_mfma_units).  Units share nothing and need no barriers: each stages
+// Work units: one wave per unit, four independent waves per workgroup (one on
+// each SIMD of a compute unit, see kWavesPerGroup); a split-K partition is one
+// unit or is cut into 2 or 4 (see decode_mfma_units).  The four waves of a
+// workgroup form a team that shares one run of key groups of one (batch, kv head)
+// slab, wave w taking every fourth group from w (see Teams below); the run starts
+// come from the host with the launch.  Units share nothing and need no barriers: each stages
 // its groups through an LDS ring of D = 2..4 slots (buffer loads straight into
 // LDS, so up to D - 1 later groups are in flight while one is computed), keeps its
 // own online-softmax state and writes its own partial result.  The launcher takes
@@ -52,6 +54,8 @@
 //      one shift per word for the slots above the mantissa).
 // Retained fp16 rows (recent window, log-spaced tokens) join the same online state
 // after the key groups: scores on the MFMA (A = fp16 key rows), values on the VALU.
+// With key rotation (KVQ_KEY_ROTATION) the lane's query task is rotated before
+// step 1, so the scores are those of the rotated cache.
 #include <algorithm>
 #include <atomic>
 

@@ -8,7 +8,12 @@
 // separate key / value bit widths (Quantize What Counts, methodology).
 // Retained positions (LogQuant section 2) are copied to fp16 rows.
 //
-// One launch per call.  Workgroups [0, n_groups_chunk) each own one key group of
+// One launch per call (two when key groups span 64 or 128 tokens: key_range_kernel
+// first forms their scales and zeros).  Heads of 128 channels with 16-bit inputs
+// and 32-token key groups take pack128_kernel (described at its definition); the
+// rest take pack_kernel.  With key rotation (KVQ_KEY_ROTATION) every key row is
+// rotated in float32 before its min / max, codes or fp16 copy.
+// pack_kernel: workgroups [0, n_groups_chunk) each own one key group of
 // one (batch, kv-head) slab; the remaining workgroups copy the chunk's retained
 // rows to fp16.  In a group workgroup, wave w holds tokens 8w..8w+7 and lane l the
 // channel pair (2l, 2l+1) (and 2l+128, 2l+129 for heads wider than 128), so every
