@@ -40,7 +40,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak, 8 TB/s
 METRIC = "quantized-KV decode attn: effective HBM GB/s (% of peak) + decode steps/sec"
 CSRC = os.path.join(ROOT, "quantized_decode_attention_kv_amd", "csrc")
-DECODE_SRCS = [os.path.join(CSRC, f) for f in ("kvq_decode_mfma.hip", "kvq_decode_common.hpp", "kvq_decode_generic.hip", "kvq_decode_merge.hip")]
+DECODE_SRCS = [os.path.join(CSRC, f) for f in ("kvq_decode_mfma.hip", "kvq_decode_common.hpp", "kvq_decode_generic.hip",
+                                                "kvq_decode_merge.hip", "kvq_internal.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_long_128k_hbm_traffic.txt")
 
 

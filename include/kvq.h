@@ -192,7 +192,7 @@ int kv_quant_pack(const kvq_layout* L, int64_t t_begin, int64_t t_count,
  *        a share of the retained tokens, and the partial results are merged.  The
  *        library chooses the run boundaries: near-equal (integer division) for the
  *        vector-ALU kernel; for the matrix-core kernel the P runs may be cut further
- *        into 2P or 4P and sized by dispatch order (within about +-20% of equal).
+ *        into 2P, 4P or 8P and sized by dispatch order (within about +-20% of equal).
  *        Results differ only in rounding.  1 <= P <= max(1, ceil(T/32)).
  *   workspace / workspace_bytes: 16-byte aligned device memory for the partial
  *        results: kvq_decode_workspace_bytes(L, P) bytes always suffice (the exact

@@ -24,7 +24,7 @@
 //
 // Work units: one wave per unit, four independent waves per workgroup (one on
 // each SIMD of a compute unit, see kWavesPerGroup); a split-K partition is one
-// unit or is cut into 2 or 4 (see decode_mfma_units).  The four waves of a
+// unit or is cut into 2, 4 or 8 (see decode_mfma_units).  The four waves of a
 // workgroup form a team that shares one run of key groups of one (batch, kv head)
 // slab, wave w taking every fourth group from w (see Teams below); the run starts
 // come from the host with the launch.  Units share nothing and need no barriers: each stages

@@ -65,13 +65,13 @@ hipError_t launch_side_pack(const SideArgs& a, hipStream_t stream);
 constexpr int kMaxSideRank = 16;
 
 // Work units of the matrix-core decode kernel: each of the P split-K partitions
-// is cut into c = 1, 2 or 4 contiguous runs, one wave each (four independent waves
-// share a workgroup, one per SIMD of a compute unit).  c
+// is cut into c = 1, 2, 4 or 8 units, one wave each (four independent waves share
+// a workgroup, one per SIMD of a compute unit).  c
 // is the largest that keeps the grid within `resident` waves (what the device
 // holds at once for the kernel's occupancy), so short caches still fill the chip
 // while long ones keep each wave on a long run of key groups.  P == 1 is one
 // unit, which writes the output directly.
-constexpr int kMaxUnitsPerPartition = 4;
+constexpr int kMaxUnitsPerPartition = 8;
 inline int decode_mfma_units(const kvq_layout& L, int P, int64_t resident) {
   if (P == 1) return 1;
   const int64_t slabs = int64_t(L.B) * L.Hkv;

@@ -71,7 +71,7 @@ def test_stream_sizes_and_capacities():
     assert sizes["k_fp16"] == slabs * s.r_cap * 64 * 2
     for k, (shape, dt) in s.shapes().items():
         assert int(np.prod(shape)) * (4 if "codes" in k else 2) == sizes[k], k
-    assert s.workspace_bytes(1) == 0 and s.workspace_bytes(4) == 2 * 8 * 4 * 4 * (128 + 4) * 4
+    assert s.workspace_bytes(1) == 0 and s.workspace_bytes(4) == 2 * 8 * 4 * 8 * (128 + 4) * 4
 
 
 def test_row_bound_holds_over_a_long_stream():

@@ -21,7 +21,7 @@ from workloads.device import to_device
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # matrix-core kernel, 5 partitions cut into 20 units per slab
+    # matrix-core kernel, 5 partitions cut into 40 units per slab
     Workload("noalloc_k4v2", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=1064, k_bits=4, v_bits=2, n_recent=40,
              dtype="bf16", partitions=5, seed=51),
     # a smaller input on the same scratch
