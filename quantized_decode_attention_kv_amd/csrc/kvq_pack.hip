@@ -137,10 +137,26 @@ struct QParams {
   uint16_t s_bits, z_bits;
 };
 
+// fl(a / L), correctly rounded, for a level count L = 2^b - 1 (b in {1, 2, 3, 4, 8})
+// and any non-negative finite a, without a divide: q0 = a * fl(1/L) and one
+// fma-corrected step (Markstein's correction with an exact residual).  Checked
+// against the correctly rounded quotient for every non-negative finite float and
+// each of those five L: bit-identical.  fl(1/L) folds to a constant where L is one.
+// The result is kept opaque so that its fp16 conversion cannot be fused into the
+// last fma (one rounding of the exact value instead of two).
+__device__ __forceinline__ float quotient_by_levels(float a, float L) {
+  const float y = 1.0f / L;
+  const float q0 = a * y;
+  const float r = fmaf(-q0, L, a);
+  float q = fmaf(r, y, q0);
+  asm("" : "+v"(q));
+  return q;
+}
+
 // s = fp16(fp32(mx - mn) / (2^bits - 1)), z = fp16(mn); zeros stored as +0.
 __device__ __forceinline__ QParams make_qparams(float mn, float mx, float levels) {
   const float range = mx - mn;
-  const float s32 = range / levels;
+  const float s32 = quotient_by_levels(range, levels);
   uint16_t sb = f16_bits_rne(s32);
   uint16_t zb = f16_bits_rne(mn);
   if ((sb & 0x7fffu) == 0) sb = 0;
