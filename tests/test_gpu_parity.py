@@ -125,6 +125,17 @@ def test_llama8b_gqa_4k_full():
     assert {p["ring_depth"] for p in plans.values()} == {2, 3, 4}, plans
 
 
+def test_many_teams_one_slab():
+    """One slab cut into many units: 64 and 256 partitions of 8 units give 128 and
+    512 teams of four waves, at and past the 128 teams whose run starts the host
+    passes with the launch (past it the kernel computes them itself), and most units
+    hold one key group or none."""
+    w = Workload("many_teams", B=1, Hq=4, Hkv=1, Dk=128, Dv=128, T=8224, k_bits=4, v_bits=2, n_recent=32,
+                 dtype="bf16", partitions=256, seed=36)
+    _, _, plans = _run_small(w, partitions=[64, 256], kernel="mfma")
+    assert plans[64]["units"] == 512 and plans[256]["units"] == 2048, plans
+
+
 @pytest.mark.parametrize("w", [
     Workload("one_group", B=1, Hq=4, Hkv=4, Dk=32, Dv=32, T=32, k_bits=2, v_bits=8, dtype="bf16", seed=31),
     Workload("all_fp16", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=200, k_bits=4, v_bits=2, n_recent=200,
