@@ -821,7 +821,9 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
 
   // -------------------------------------------------------------- values
   constexpr float v_levels = float((1 << VB) - 1);
-  const int vg = a.L.v_group, lpg = vg / 8;  // channels and lanes per value group
+  // channels and lanes per value group (v_group is 32, 64 or 128: shifts, no divides)
+  const int vsh = a.L.v_group == 128 ? 2 : (a.L.v_group == 64 ? 1 : 0);
+  const int lpg = 4 << vsh;
   uint32_t* slots = reinterpret_cast<uint32_t*>(part_s) + wave * (64 * 8);  // this wave's alone, in issue order
   float vx[2][8];
   widen(vraw[0], vx[0]);
@@ -861,7 +863,7 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
   const float vr[2] = {jm ? orr : qm.r, jm ? qm.r : orr};
   if ((c & (lpg - 1)) < 2) {
     // one lane per (token, value group) stores its scale and zero
-    const int ngv = D / vg, gc = (8 * c) / vg;
+    const int ngv = D >> (5 + vsh), gc = (8 * c) >> (5 + vsh);
     const int64_t vso = (slab * a.g_stride + g) * ngv * KVQ_GROUP;
     const uint32_t vo = uint32_t(gc * KVQ_GROUP + tok[jm]);
     out_store(static_cast<uint16_t*>(a.cache.v_scale) + vso + vo, qm.s_bits);
