@@ -58,6 +58,7 @@
 // step 1, so the scores are those of the rotated cache.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -888,8 +889,11 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
     const int ns = nj;
     __builtin_amdgcn_s_setprio(3);
     const int q1 = ns / 4, q2 = ns / 2, q3 = (3 * ns) / 4;
-    for (int i = 0; i < ns; ++i) {
-      const int pos = i % D;
+    // step i at ring position pos_c == i % D: a compile-time constant where the
+    // loop below is unrolled by D (every LDS address of a step is then a fixed
+    // offset), a plain int otherwise
+    auto one_step = [&](int i, auto pos_c) {
+      const int pos = pos_c;
       if (i == q1) __builtin_amdgcn_s_setprio(2);
       if (i == q2) __builtin_amdgcn_s_setprio(1);
       if (i == q3) __builtin_amdgcn_s_setprio(0);
@@ -897,7 +901,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
         // the position step i - 1 computed from is free (its reads were consumed
         // there): it takes group i - 1 + D before the wait, so D - 1 later groups
         // are in flight while the wave waits for group i
-        const int prev = (i + D - 1) % D;
+        const int prev = (pos + D - 1) % D;
         if (i >= 1 && i - 1 + D < ns) {
           wave_lds_order();
           stage_group(g0 + TS * (i - 1 + D), prev);
@@ -921,6 +925,23 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
       for (int k = 0; k < VLW; ++k) vws[k] = d.vw[k];
       score_step(d, tiles);
       value_step(vws, tiles);
+    };
+    static_assert(D >= 2 && D <= 4, "ring depth");
+    if constexpr (lds_waves_per_simd<DK, DV, KB, VB, D>() <= 2) {
+      for (int i0 = 0; i0 < ns; i0 += D) {
+        one_step(i0, std::integral_constant<int, 0>{});
+        if (i0 + 1 < ns) one_step(i0 + 1, std::integral_constant<int, 1>{});
+        if constexpr (D > 2) {
+          if (i0 + 2 < ns) one_step(i0 + 2, std::integral_constant<int, 2 % D>{});
+        }
+        if constexpr (D > 3) {
+          if (i0 + 3 < ns) one_step(i0 + 3, std::integral_constant<int, 3 % D>{});
+        }
+      }
+    } else {
+      // instances held to 128 registers (3 or 4 waves per SIMD): the unrolled loop
+      // keeps more addresses live and spills there, so the position stays a variable
+      for (int i = 0; i < ns; ++i) one_step(i, i % D);
     }
     // a unit without key groups still issued (empty) copies into the ring
     wait_vmcnt<0>();
