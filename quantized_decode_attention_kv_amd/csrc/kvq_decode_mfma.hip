@@ -37,15 +37,16 @@
 //      a wave-private LDS tile;
 //   2. scores S^T[token, column] = codes (A: 16 tokens x 32 channels) x Q' (B), two
 //      16-token tiles, with the hi and lo parts of Q' as two K steps of the same
-//      accumulator.  Column n holds query n%4, so every lane holds the scores of
-//      query n%4; tile rows are ordered so that lane group j holds tokens
-//      8j..8j+7;
+//      accumulator.  Columns 4i..4i+3 hold query i, so every lane holds the
+//      scores of one query, each quad of lanes the same ones; tile rows are
+//      ordered so that lane group j holds tokens 8j..8j+7;
 //   3. the key zero-point term sum_c q_c z_c: each Q' lane forms the partial sum
 //      of its block, and the 16 partial sums of a query are added across lanes
-//      (two row rotations, two half swaps) in fp32;
-//   4. online softmax in the log2 domain on the 8 scores of each lane; the running
-//      maximum of a query only moves (and the state is rescaled) when a score
-//      exceeds it by more than 2^kHeadroom, so most groups skip the rescale;
+//      (two exchanges inside quads, two half swaps) in fp32;
+//   4. online softmax in the log2 domain: each lane of a quad exponentiates 2 of
+//      its octet's 8 scores and the quad shares the results (DPP broadcasts); the
+//      running maximum of a query only moves (and the state is rescaled) when a
+//      score exceeds it by more than 2^kHeadroom, so most groups skip the rescale;
 //   5. P' = p s (hi, lo) for 64 (query, channel group, 8-token octet) tasks, again
 //      one per lane and already holding the probabilities they need, into LDS;
 //   6. values O[(query, part), channel] += P' (A) x codes (B), eight 16-channel
@@ -309,31 +310,30 @@ struct Lds {
   static_assert(kQB1 <= kSlot && kG * 32 * 4 <= kSlot && kG * (DV + NGV) * 4 <= kSlots * kSlot, "aliases");
 };
 
-// Sum (or max) of v over the 16 lanes l with l % 4 == lane % 4: two rotations
-// inside each row of 16, then the two gfx950 half swaps across rows; every lane
-// gets its class's total.
+// v from lane j' of each quad of lanes (quad_perm broadcast: all four lanes of a
+// quad read lane j')
+template <int J>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), J * 0x55, 0xF, 0xF, false));
+}
+// op over the four lanes of each quad (two exchanges: lanes l ^ 1, then l ^ 2)
 template <bool MAX>
-__device__ __forceinline__ float mod4_allreduce(float v) {
+__device__ __forceinline__ float quad_allreduce(float v) {
   auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
-  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false)));  // row_ror:4
-  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false)));  // row_ror:8
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+  return op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+}
+// Sum (or max) of v over the 16 lanes l with (l / 4) % 4 == (lane / 4) % 4: the
+// quad, then the two gfx950 half swaps across rows.  Every step pairs lanes
+// symmetrically, so all 16 lanes end with the same bits.
+template <bool MAX>
+__device__ __forceinline__ float query_allreduce(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  v = quad_allreduce<MAX>(v);
   const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = op(__uint_as_float(h32[0]), __uint_as_float(h32[1]));
   const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return op(__uint_as_float(h16[0]), __uint_as_float(h16[1]));
-}
-
-// max over the 64 lanes of a wave (DPP inside rows, then the four row results)
-__device__ __forceinline__ float wave_max_rows(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));  // row_mirror
-  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
-}
-// x[i] for a per-lane index i < 4 into a wave-uniform array (select chain)
-__device__ __forceinline__ float pick4(const float (&x)[kG], int i) {
-  return i == 0 ? x[0] : (i == 1 ? x[1] : (i == 2 ? x[2] : x[3]));
 }
 
 // Work units.  A unit is one wave; a team is TS units (4, one workgroup, or 1)
@@ -493,12 +493,13 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
 
   // Q' task of this lane: (block tb = 8-channel block kk_t of lane group gq_t,
   // query i_t); it also forms the block's key zero-point partial sum
-  const int kk_t = lane >> 4, gq_t = (lane >> 2) & 3, i_t = lane & 3;
+  const int kk_t = lane >> 4, i_t = (lane >> 2) & 3, gq_t = lane & 3;
   const bool qtask = kk_t < KK;
   const int tb = gq_t * KK + (qtask ? kk_t : 0);
-  // score columns: query iq = n % 4; P' task: (query iq, channel group n / 4, octet gq)
-  const int iq = n & 3;
-  const int gcP = n >> 2;
+  // score columns: n = 4 iq + rep holds query iq (rep: which of its four copies);
+  // P' task: (query iq, channel group rep, octet gq)
+  const int iq = n >> 2, rep = n & 3;
+  const int gcP = rep;
 
   // ------------------------------------------------- staging of key groups
   // Every piece of a group is copied so that the lane that consumes it reads it
@@ -604,14 +605,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
     // the packed keys are rotated: rotate the query the same way.  Channel
     // 8 tb + k of the task: butterflies 1, 2, 4 over k in registers, then bit s of
     // tb, which is bit s of kk_t (lane ^ 16 << s) for s < log2 KK, else bit
-    // s - log2 KK of gq_t (lane ^ 4 << (s - log2 KK)); lanes without a task
+    // s - log2 KK of gq_t (lane ^ 1 << (s - log2 KK)); lanes without a task
     // exchange only among themselves
     constexpr int LKK = KK == 1 ? 0 : (KK == 2 ? 1 : (KK == 4 ? 2 : 3));
     static_assert((1 << LKK) == KK, "power-of-two key width");
     butterflies8(qx);
 #pragma unroll
     for (int st = 0; st < LKK + 2; ++st) {
-      const int pl = st < LKK ? (16 << st) : (4 << (st - LKK));
+      const int pl = st < LKK ? (16 << st) : (1 << (st - LKK));
       const bool up = ((tb >> st) & 1) != 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k) qx[k] = butterfly(qx[k], __shfl_xor(qx[k], pl), up);
@@ -622,16 +623,16 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   }
 
   // ---------------------------------------------------------------- set-up
-  // Query lane % 4 is scaled by 2^-E, E >= 0 the smallest exponent such that
+  // Query i_t is scaled by 2^-E, E >= 0 the smallest exponent such that
   // |q 2^-E| <= 1, which keeps q_c s_c inside the fp16 range; every use of the
-  // exponent in this lane concerns query lane % 4.
+  // exponent in this lane concerns query (lane / 4) % 4 (= i_t = iq).
   float qmax = 0.0f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     qx[k] *= a.scale * kLog2e;
     qmax = fmaxf(qmax, fabsf(qx[k]));
   }
-  qmax = mod4_allreduce<true>(qtask ? qmax : 0.0f);
+  qmax = query_allreduce<true>(qtask ? qmax : 0.0f);
   float qe;
   {
     int e = 0;
@@ -658,9 +659,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   auto qb_at = [](int e) { return kSwz ? e ^ (((e >> 4) & 1) << 2) : e; };
   auto pa_at = [](int e) { return kSwz ? e ^ (((e >> 5) & 1) << 3) ^ (((e >> 6) & 1) << 2) : e; };
   const int qb_entry = ((qtask ? kk_t : 0) * 4 + gq_t) * 8 + i_t;
-  // Key zero-point term of query lane % 4: sum_c q_c z_c (times 2^-E), from the
-  // lanes' 8-channel partial sums: the 16 lanes of a query are lane % 4 + 4 m, so
-  // two rotations inside each row of 16 and two row swaps give every lane the
+  // Key zero-point term of query i_t: sum_c q_c z_c (times 2^-E), from the lanes'
+  // 8-channel partial sums: the 16 lanes of a query are the quads 16 kk + 4 i_t,
+  // so two exchanges inside each quad and two row swaps give every lane the
   // total of its query.
   auto zero_term = [&](const u32x4& kz) -> float {
     float zp = 0.0f;
@@ -669,9 +670,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
       const half2_t zz = as_half2(kz[k >> 1]);
       zp = fmaf(qzv[k], float(zz[k & 1]), zp);
     }
-    return mod4_allreduce<false>(zp);
+    return query_allreduce<false>(zp);
   };
-  const float coefB = 1.0f / qe;           // q was scaled by 2^-E (query iq = lane % 4)
+  const float coefB = 1.0f / qe;           // q was scaled by 2^-E (query iq)
   const float coefD = 16777216.0f * coefB;  // codes are n 2^-24
   const int pa_entry = (gcP * 4 + gq) * 8 + iq;
   const int vs_at = ((gcP >> vsh) * 4 + gq) * 16;  // the lane's 8 value scales / zeros in a slot
@@ -689,35 +690,31 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
 #pragma unroll
   for (int i = 0; i < kG; ++i) o_r[i][0] = o_r[i][1] = 0.0f;
 
-  // Softmax update of 8 new scores per lane and key group: v = raw MFMA outputs,
-  // score = v * coef + bias of the group (log2 domain).  Returns the
-  // probabilities relative to the (possibly moved) reference maximum;
-  // rescale_acc(alpha) rescales the value accumulators when a reference moves.
-  auto softmax_step = [&](const auto& v, float coef, const auto& bias, auto& pv, auto&& rescale_acc) {
-    constexpr int N = sizeof(v) / sizeof(float);
-    float sv[N];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      sv[k] = fmaf(v[k], coef, bias[k / 8] - m_lane);
-      mloc = fmaxf(mloc, sv[k]);
-    }
-    if (__builtin_expect(__any(mloc > float(kHeadroom)), 0)) {
+  // Softmax update of one key group (or 32-row tile of retained rows).  v = the
+  // lane's raw MFMA outputs: the scores of query iq for the 8 tokens of octet gq
+  // (v[4 tt + r] = token 8 gq + 4 tt + r), the same in the four lanes of a quad;
+  // score = v * coef + bias (log2 domain).  Lane rep of the quad exponentiates
+  // tokens 2 rep and 2 rep + 1 and adds them to its l; the quad shares the results,
+  // so pv returns all 8 probabilities of the octet, relative to the (possibly
+  // moved) reference maximum.  rescale_acc(alpha) rescales the value accumulators
+  // when a reference moves.
+  const bool rep_hi = (rep & 2) != 0, rep_odd = (rep & 1) != 0;
+  auto softmax_step = [&](const float (&v)[8], float coef, float bias, float (&pv)[8], auto&& rescale_acc) {
+    const float a0 = rep_hi ? v[4] : v[0], a1 = rep_hi ? v[5] : v[1];
+    const float a2 = rep_hi ? v[6] : v[2], a3 = rep_hi ? v[7] : v[3];
+    const float x0 = rep_odd ? a2 : a0, x1 = rep_odd ? a3 : a1;
+    float s0 = fmaf(x0, coef, bias - m_lane), s1 = fmaf(x1, coef, bias - m_lane);
+    if (__builtin_expect(__any(fmaxf(s0, s1) > float(kHeadroom)), 0)) {
       // some score left the headroom: move those references to the group maxima
-      // (queries repeat every 4 columns; the 4 lane groups hold different tokens)
-      float sabs[N];
-      float mab = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < N; ++k) {
-        sabs[k] = fmaf(v[k], coef, bias[k / 8]);
-        mab = fmaxf(mab, sabs[k]);
-      }
+      // (the quad's maximum, then one lane per octet)
+      const float b0 = fmaf(x0, coef, bias), b1 = fmaf(x1, coef, bias);
+      const float mab = quad_allreduce<true>(fmaxf(b0, b1));
       float alpha[kG];
 #pragma unroll
       for (int i = 0; i < kG; ++i) {
-        float mg = readlane_f32(mab, i);
+        float mg = readlane_f32(mab, 4 * i);
 #pragma unroll
-        for (int j = 1; j < 4; ++j) mg = fmaxf(mg, readlane_f32(mab, 16 * j + i));
+        for (int j = 1; j < 4; ++j) mg = fmaxf(mg, readlane_f32(mab, 16 * j + 4 * i));
         const float m_new = mg > m_q[i] + float(kHeadroom) ? mg : m_q[i];
         alpha[i] = lse_weight(m_q[i], m_new);
         m_q[i] = m_new;
@@ -734,14 +731,19 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
       l_run *= al;
       zacc *= al;
       rescale_acc(alpha);
-#pragma unroll
-      for (int k = 0; k < N; ++k) sv[k] = sabs[k] - m_lane;
+      s0 = b0 - m_lane;
+      s1 = b1 - m_lane;
     }
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      pv[k] = fast_exp2(sv[k]);
-      l_run += pv[k];
-    }
+    const float e0 = fast_exp2(s0), e1 = fast_exp2(s1);
+    l_run += e0 + e1;
+    pv[0] = quad_bcast<0>(e0);
+    pv[1] = quad_bcast<0>(e1);
+    pv[2] = quad_bcast<1>(e0);
+    pv[3] = quad_bcast<1>(e1);
+    pv[4] = quad_bcast<2>(e0);
+    pv[5] = quad_bcast<2>(e1);
+    pv[6] = quad_bcast<3>(e0);
+    pv[7] = quad_bcast<3>(e1);
   };
   auto rescale_retained = [&](const float (&alpha)[kG]) {
 #pragma unroll
@@ -815,7 +817,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
       qb[qb_at(qb_entry)] = hi;
       qb[qb_at(qb_entry + 4)] = lo;
     }
-    const float bias[1] = {zero_term(d.kz) * coefB};
+    const float bias = zero_term(d.kz) * coefB;
     wave_lds_order();
     float v[8], pv[8];
     f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -954,14 +956,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   if (unit < nRT) {
     // B2: q 2^-E split hi/lo, entry (kk*4 + gq)*8 + i + 4*part, channels of block
     // gq*KK + kk in natural order (dword d = channels 2d, 2d+1); query i = e % 4
-    // is this lane's query.  The channels are the Q' task of lane 16 kk + 4 gq + i,
+    // is this lane's query.  The channels are the Q' task of lane 16 kk + 4 i + gq,
     // whose q 2^-E (qzv, after any rotation) is read across lanes.
     // (every lane runs the same passes, so that the cross-lane reads see all lanes;
     // lanes past the last entry read a lane in range and store nothing)
     for (int e0 = 0; e0 < KK * 32; e0 += 64) {
       const int e = e0 + lane;
       const int gqe = (e >> 3) & 3, kke = e >> 5, part = (e >> 2) & 1;
-      const int src = (16 * kke + 4 * gqe + (e & 3)) & 63;
+      const int src = (16 * kke + 4 * (e & 3) + gqe) & 63;
       float x[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) x[k] = __shfl(qzv[k], src);
@@ -999,11 +1001,10 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[4 * tt + r] = rbase + 8 * gq + 4 * tt + r < R ? sacc[tt][r] : -INFINITY;
       }
-      const float no_bias[1] = {0.0f};
-      softmax_step(v, coefB, no_bias, pv, rescale_groups);
-      if (n < kG) {
-        *reinterpret_cast<f32x4*>(PT + n * 32 + 8 * gq) = f32x4{pv[0], pv[1], pv[2], pv[3]};
-        *reinterpret_cast<f32x4*>(PT + n * 32 + 8 * gq + 4) = f32x4{pv[4], pv[5], pv[6], pv[7]};
+      softmax_step(v, coefB, 0.0f, pv, rescale_groups);
+      if (rep == 0) {
+        *reinterpret_cast<f32x4*>(PT + iq * 32 + 8 * gq) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+        *reinterpret_cast<f32x4*>(PT + iq * 32 + 8 * gq + 4) = f32x4{pv[4], pv[5], pv[6], pv[7]};
       }
       wave_lds_sync();
       // values on the VALU: lane owns channels 2 lane, 2 lane + 1 of every row
@@ -1042,7 +1043,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   float* OM = reinterpret_cast<float*>(stage);
   float* zsm = OM + kG * DV;
   {
-    // zero-point sums per (query, channel group): lanes 16 gq + 4 gc + i
+    // zero-point sums per (query, channel group): lanes 16 gq + 4 i + gc
     const float z16 = zacc + __shfl_xor(zacc, 16, 64);
     const float z = z16 + __shfl_xor(z16, 32, 64);
     if (gq == 0) zsm[iq * NGV + gcP] = z;
@@ -1065,12 +1066,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
     }
   }
   wave_lds_sync();
-  // l per query: lanes i, 16 + i, 32 + i, 48 + i hold its four token octets
+  // l per query: the quads 16 gq + 4 i hold its tokens, two per lane: a sum over
+  // each quad, then over the four octets
+  const float lquad = quad_allreduce<false>(l_run);
   float lq[kG];
 #pragma unroll
   for (int i = 0; i < kG; ++i)
-    lq[i] = readlane_f32(l_run, i) + readlane_f32(l_run, 16 + i) + readlane_f32(l_run, 32 + i) +
-            readlane_f32(l_run, 48 + i);
+    lq[i] = readlane_f32(lquad, 4 * i) + readlane_f32(lquad, 16 + 4 * i) + readlane_f32(lquad, 32 + 4 * i) +
+            readlane_f32(lquad, 48 + 4 * i);
   const int64_t qh0 = int64_t(b) * a.L.Hq + int64_t(h) * kG;
 #pragma unroll
   for (int i = 0; i < kG; ++i) {
