@@ -36,15 +36,16 @@
 //   1. Q' = q s (hi, lo) for 64 (query, 8-channel block) tasks, one per lane, into
 //      a wave-private LDS tile;
 //   2. scores S^T[token, column] = codes (A: 16 tokens x 32 channels) x Q' (B), two
-//      16-token tiles, with the hi and lo parts of Q' as two K steps of the same
-//      accumulator.  Columns 4i..4i+3 hold query i, so every lane holds the
-//      scores of one query, each quad of lanes the same ones; tile rows are
-//      ordered so that lane group j holds tokens 8j..8j+7;
+//      16-token tiles.  Columns 4i..4i+3 hold query i, the even ones the hi part
+//      of Q', the odd ones the lo part, so one pass over the channels gives both
+//      parts and every lane holds one part of the scores of one query; tile rows
+//      are ordered so that lane group j holds tokens 8j..8j+7;
 //   3. the key zero-point term sum_c q_c z_c: each Q' lane forms the partial sum
 //      of its block, and the 16 partial sums of a query are added across lanes
 //      (two exchanges inside quads, two half swaps) in fp32;
-//   4. online softmax in the log2 domain: each lane of a quad exponentiates 2 of
-//      its octet's 8 scores and the quad shares the results (DPP broadcasts); the
+//   4. online softmax in the log2 domain: each lane of a quad adds the two parts
+//      of 2 of its octet's 8 scores (DPP exchange with the neighbouring column),
+//      exponentiates them and the quad shares the results (DPP broadcasts); the
 //      running maximum of a query only moves (and the state is rescaled) when a
 //      score exceeds it by more than 2^kHeadroom, so most groups skip the rescale;
 //   5. P' = p s (hi, lo) for 64 (query, channel group, 8-token octet) tasks, again
@@ -314,14 +315,23 @@ struct Lds {
 // quad read lane j')
 template <int J>
 __device__ __forceinline__ float quad_bcast(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), J * 0x55, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), J * 0x55, 0xF, 0xF, true));
+}
+// v of lane l ^ 1 and of lane l ^ 2 (quad_perm 1,0,3,2 and 2,3,0,1; every source
+// lane exists, and bound_ctrl lets the compiler fold the move into the ALU
+// operation that consumes it)
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
 // op over the four lanes of each quad (two exchanges: lanes l ^ 1, then l ^ 2)
 template <bool MAX>
 __device__ __forceinline__ float quad_allreduce(float v) {
   auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
-  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
-  return op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+  v = op(v, quad_xor1(v));
+  return op(v, quad_xor2(v));
 }
 // Sum (or max) of v over the 16 lanes l with (l / 4) % 4 == (lane / 4) % 4: the
 // quad, then the two gfx950 half swaps across rows.  Every step pairs lanes
@@ -496,7 +506,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   const int kk_t = lane >> 4, i_t = (lane >> 2) & 3, gq_t = lane & 3;
   const bool qtask = kk_t < KK;
   const int tb = gq_t * KK + (qtask ? kk_t : 0);
-  // score columns: n = 4 iq + rep holds query iq (rep: which of its four copies);
+  // score columns: n = 4 iq + rep holds part rep % 2 (hi, lo) of query iq;
   // P' task: (query iq, channel group rep, octet gq)
   const int iq = n >> 2, rep = n & 3;
   const int gcP = rep;
@@ -691,18 +701,23 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   for (int i = 0; i < kG; ++i) o_r[i][0] = o_r[i][1] = 0.0f;
 
   // Softmax update of one key group (or 32-row tile of retained rows).  v = the
-  // lane's raw MFMA outputs: the scores of query iq for the 8 tokens of octet gq
-  // (v[4 tt + r] = token 8 gq + 4 tt + r), the same in the four lanes of a quad;
-  // score = v * coef + bias (log2 domain).  Lane rep of the quad exponentiates
-  // tokens 2 rep and 2 rep + 1 and adds them to its l; the quad shares the results,
-  // so pv returns all 8 probabilities of the octet, relative to the (possibly
-  // moved) reference maximum.  rescale_acc(alpha) rescales the value accumulators
-  // when a reference moves.
+  // lane's raw MFMA outputs: part rep % 2 of the scores of query iq for the 8
+  // tokens of octet gq (v[4 tt + r] = token 8 gq + 4 tt + r); lanes rep and
+  // rep ^ 1 of a quad hold the two parts.  score = v * coef + bias (log2 domain).
+  // Lane rep of the quad adds the parts of tokens 2 rep and 2 rep + 1 (those of
+  // tile rep / 2, exchanged with its neighbour), exponentiates them and adds them
+  // to its l; the quad shares the results, so pv returns all 8 probabilities of
+  // the octet, relative to the (possibly moved) reference maximum.
+  // rescale_acc(alpha) rescales the value accumulators when a reference moves.
   const bool rep_hi = (rep & 2) != 0, rep_odd = (rep & 1) != 0;
   auto softmax_step = [&](const float (&v)[8], float coef, float bias, float (&pv)[8], auto&& rescale_acc) {
-    const float a0 = rep_hi ? v[4] : v[0], a1 = rep_hi ? v[5] : v[1];
-    const float a2 = rep_hi ? v[6] : v[2], a3 = rep_hi ? v[7] : v[3];
-    const float x0 = rep_odd ? a2 : a0, x1 = rep_odd ? a3 : a1;
+    // (scalars, not an array: a select between two elements of a local array can
+    // become a load through a selected address, which puts the array on the stack)
+    const float m0 = rep_hi ? v[4] : v[0], m1 = rep_hi ? v[5] : v[1];
+    const float m2 = rep_hi ? v[6] : v[2], m3 = rep_hi ? v[7] : v[3];
+    const float f0 = quad_xor1(m0) + m0, f1 = quad_xor1(m1) + m1;
+    const float f2 = quad_xor1(m2) + m2, f3 = quad_xor1(m3) + m3;
+    const float x0 = rep_odd ? f2 : f0, x1 = rep_odd ? f3 : f1;
     float s0 = fmaf(x0, coef, bias - m_lane), s1 = fmaf(x1, coef, bias - m_lane);
     if (__builtin_expect(__any(fmaxf(s0, s1) > float(kHeadroom)), 0)) {
       // some score left the headroom: move those references to the group maxima
@@ -823,12 +838,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
     f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
+      const u32x4 bq = reinterpret_cast<const u32x4*>(tiles)[qb_at((kk * 4 + gq) * 8 + 4 * (rep & 1) + iq)];
 #pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const u32x4 bq = reinterpret_cast<const u32x4*>(tiles)[qb_at((kk * 4 + gq) * 8 + 4 * part + iq)];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(key_field<KB>(d.kw[tt], kk), bq, sacc[tt]);
-      }
+      for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(key_field<KB>(d.kw[tt], kk), bq, sacc[tt]);
     }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -990,8 +1002,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const u32x4 ak = *reinterpret_cast<const u32x4*>(kr + (uint32_t(row) * (DK * 2) + 16 * (gq * KK + kk)));
-#pragma unroll
-          for (int part = 0; part < 2; ++part) sacc[tt] = mfma16(ak, B2[(kk * 4 + gq) * 8 + 4 * part + iq], sacc[tt]);
+          sacc[tt] = mfma16(ak, B2[(kk * 4 + gq) * 8 + 4 * (rep & 1) + iq], sacc[tt]);
         }
       }
       // lane (n, gq): tile tt, register r -> token 8 gq + 4 tt + r
