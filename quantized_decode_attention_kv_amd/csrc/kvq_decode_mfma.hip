@@ -662,10 +662,10 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   //   Q' entry (kk*4 + gq)*8 + 4*part + i at e ^ (bit 4 of e) << 2 (rows 2, 3 of
   //   the 4 gq rows swap their hi and lo halves);
   //   P' entry (gc*4 + gq)*8 + j at e ^ (gc & 1) << 3 ^ (gc >> 1) << 2.
-  // The swizzled addresses take a few more registers; instances held to 128 (4
-  // waves per SIMD) keep the plain order, which measured faster there than
-  // spilling.
-  constexpr bool kSwz = lds_waves_per_simd<DK, DV, KB, VB, D>() < 4;
+  // The swizzled addresses take a few more registers; the D = 2 instances held
+  // to 128 (4 waves per SIMD) keep the plain order, where the swizzle would
+  // spill.
+  constexpr bool kSwz = lds_waves_per_simd<DK, DV, KB, VB, D>() < 4 || D > 2;
   auto qb_at = [](int e) { return kSwz ? e ^ (((e >> 4) & 1) << 2) : e; };
   auto pa_at = [](int e) { return kSwz ? e ^ (((e >> 5) & 1) << 3) ^ (((e >> 6) & 1) << 2) : e; };
   const int qb_entry = ((qtask ? kk_t : 0) * 4 + gq_t) * 8 + i_t;
