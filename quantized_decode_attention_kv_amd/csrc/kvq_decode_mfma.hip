@@ -291,19 +291,25 @@ __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t (&w)[NB < 
 //   After the loop the ring holds the q hi/lo operand B2 of the retained rows
 //   (slot 0) and their probabilities PT (slot 1), then the matrix-core output
 //   and the value zero-point sums.
+// P' tiles of the ring instances: the entries of channel group gc start at
+// gc * kPASkew (16-byte entries, see the kernel)
+constexpr int kPASkew = 36;
 template <int DK, int DV, int KB, int VB, int D>
 struct Lds {
   static constexpr int KK = DK / 32, NGV = DV / 32;
+  static constexpr bool kInSlot = D > 2;
   static constexpr int kQB1 = KK * 32 * 16;   // one Q' tile
-  static constexpr int kPA1 = NGV * 32 * 16;  // one P' tile
+  static constexpr int kPA1 = (kInSlot ? (NGV - 1) * kPASkew + 32 : NGV * 32) * 16;  // one P' tile
   static constexpr int kStK = 32 * DK * KB / 8;
   static constexpr int kStV = 32 * DV * VB / 8;
   static constexpr int kStS = 256;
   static constexpr int kStage = kStK + kStV + 4 * kStS;
-  static constexpr bool kShare = kPA1 <= kQB1;
-  static constexpr int kTiles = kShare ? kQB1 : kQB1 + kPA1;  // Q' and P' tiles of one group
-  static constexpr int kPAOff = kShare ? 0 : kQB1;             // P' tile inside them
-  static constexpr bool kInSlot = D > 2;
+  // the P' tile of a group is written after its Q' tile has been read, so the two
+  // can share one area (ring instances; with D == 2 they share it only when the
+  // P' tile is not the larger, which keeps those instances' occupancy)
+  static constexpr bool kShare = kInSlot || kPA1 <= kQB1;
+  static constexpr int kTiles = kShare ? (kPA1 > kQB1 ? kPA1 : kQB1) : kQB1 + kPA1;
+  static constexpr int kPAOff = kShare ? 0 : kQB1;
   static constexpr int kSlot = kInSlot && kTiles > kStage ? kTiles : kStage;
   static constexpr int kSlots = D;
   static constexpr int oTiles = kInSlot ? 0 : kSlots * kSlot;  // separate tile area (D == 2)
@@ -661,13 +667,20 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   // each row of the wave hit 16 different 16-byte bank slots:
   //   Q' entry (kk*4 + gq)*8 + 4*part + i at e ^ (bit 4 of e) << 2 (rows 2, 3 of
   //   the 4 gq rows swap their hi and lo halves);
-  //   P' entry (gc*4 + gq)*8 + j at e ^ (gc & 1) << 3 ^ (gc >> 1) << 2.
+  //   P' entry (gc*4 + gq)*8 + j: with a ring of 3 or more at gc * kPASkew + gq*8 + j
+  //   (the skew of 4 entries per channel group spreads a row's writes over 16
+  //   bank slots and keeps the lane part of every address independent of gc),
+  //   else at e ^ (gc & 1) << 3 ^ (gc >> 1) << 2.
   // The swizzled addresses take a few more registers; the D = 2 instances held
   // to 128 (4 waves per SIMD) keep the plain order, where the swizzle would
   // spill.
   constexpr bool kSwz = lds_waves_per_simd<DK, DV, KB, VB, D>() < 4 || D > 2;
   auto qb_at = [](int e) { return kSwz ? e ^ (((e >> 4) & 1) << 2) : e; };
   auto pa_at = [](int e) { return kSwz ? e ^ (((e >> 5) & 1) << 3) ^ (((e >> 6) & 1) << 2) : e; };
+  // place of P' entry (gc, x = gq*8 + j)
+  auto pa_pos = [&](int gc, int x) { return LL::kInSlot ? gc * kPASkew + x : pa_at(gc * 32 + x); };
+  // this lane's Q' read (channel block kk adds kk * 512 bytes) and P' read (any gc)
+  const int qb_rd = qb_at(gq * 8 + 4 * (rep & 1) + iq) * 16;
   const int qb_entry = ((qtask ? kk_t : 0) * 4 + gq_t) * 8 + i_t;
   // Key zero-point term of query i_t: sum_c q_c z_c (times 2^-E), from the lanes'
   // 8-channel partial sums: the 16 lanes of a query are the quads 16 kk + 4 i_t,
@@ -684,7 +697,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   };
   const float coefB = 1.0f / qe;           // q was scaled by 2^-E (query iq)
   const float coefD = 16777216.0f * coefB;  // codes are n 2^-24
-  const int pa_entry = (gcP * 4 + gq) * 8 + iq;
+  const int pa_hi = pa_pos(gcP, gq * 8 + iq) * 16, pa_lo = pa_pos(gcP, gq * 8 + iq + 4) * 16;
   const int vs_at = ((gcP >> vsh) * 4 + gq) * 16;  // the lane's 8 value scales / zeros in a slot
 
   // online-softmax state: reference maxima per query (wave-uniform) and this
@@ -838,7 +851,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
     f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 bq = reinterpret_cast<const u32x4*>(tiles)[qb_at((kk * 4 + gq) * 8 + 4 * (rep & 1) + iq)];
+      const u32x4 bq = *reinterpret_cast<const u32x4*>(tiles + kk * 512 + qb_rd);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(key_field<KB>(d.kw[tt], kk), bq, sacc[tt]);
     }
@@ -853,9 +866,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
     // zero-point sum of the same task
     u32x4 hi, lo;
     split8(pv, d.vs, hi, lo);
-    u32x4* pa = reinterpret_cast<u32x4*>(tiles + LL::kPAOff);
-    pa[pa_at(pa_entry)] = hi;
-    pa[pa_at(pa_entry + 4)] = lo;
+    *reinterpret_cast<u32x4*>(tiles + LL::kPAOff + pa_hi) = hi;
+    *reinterpret_cast<u32x4*>(tiles + LL::kPAOff + pa_lo) = lo;
     float zs = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -866,10 +878,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   };
   auto value_step = [&](const uint32_t (&vws)[VLW], const unsigned char* tiles) {
     wave_lds_order();
-    const u32x4* pa = reinterpret_cast<const u32x4*>(tiles + LL::kPAOff);
 #pragma unroll
     for (int gc = 0; gc < NGV; ++gc) {
-      const u32x4 ap = pa[pa_at((gc * 4 + gq) * 8 + (n & 7))];
+      const u32x4 ap = *reinterpret_cast<const u32x4*>(tiles + LL::kPAOff + pa_pos(gc, gq * 8 + (n & 7)) * 16);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int t = 2 * gc + half;
@@ -954,8 +965,15 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
       }
     } else {
       // instances held to 128 registers (3 or 4 waves per SIMD): the unrolled loop
-      // keeps more addresses live and spills there, so the position stays a variable
-      for (int i = 0; i < ns; ++i) one_step(i, i % D);
+      // keeps more addresses live and spills there, so the position stays a
+      // variable.  It is hidden from the compiler, which would otherwise keep one
+      // address per LDS access advanced by a slot every step and corrected at the
+      // wrap (two vector additions per access instead of one).
+      for (int i = 0; i < ns; ++i) {
+        int pos = i % D;
+        asm volatile("" : "+s"(pos));
+        one_step(i, pos);
+      }
     }
     // a unit without key groups still issued (empty) copies into the ring
     wait_vmcnt<0>();
