@@ -247,7 +247,7 @@ int kv_decode_attn_noalloc(const kvq_layout* L, const void* q, int q_dtype, cons
  *   units: partial results per query head that the merge kernel folds (1: the
  *     decode kernel writes the output and no merge runs).
  *   ring_depth: key groups each wave of the matrix-core kernel keeps in its LDS
- *     ring (2..4); waves_per_simd: waves of that grid per SIMD; both 0 for the
+ *     ring (2 or 3); waves_per_simd: waves of that grid per SIMD; both 0 for the
  *     vector-ALU kernel.  waves: waves the decode kernel launches.
  * Errors: as kv_decode_attn for the layout and num_partitions; KVQ_ERR_HIP if the
  * device cannot be queried.

@@ -28,11 +28,11 @@
 // workgroup form a team that shares one run of key groups of one (batch, kv head)
 // slab, wave w taking every fourth group from w (see Teams below); the run starts
 // come from the host with the launch.  Units share nothing and need no barriers: each stages
-// its groups through an LDS ring of D = 2..4 slots (buffer loads straight into
+// its groups through an LDS ring of D = 2 or 3 slots (buffer loads straight into
 // LDS, so up to D - 1 later groups are in flight while one is computed), keeps its
 // own online-softmax state and writes its own partial result.  The launcher takes
-// the deepest ring whose LDS still keeps the whole grid resident (D = 4, 8 waves
-// per compute unit, on the 128K-token workload).  Per group:
+// D = 3 where its LDS keeps the whole grid resident (8 waves per compute unit on
+// the 128K-token workload), else 2.  Per group:
 //   1. Q' = q s (hi, lo) for 64 (query, 8-channel block) tasks, one per lane, into
 //      a wave-private LDS tile;
 //   2. scores S^T[token, column] = codes (A: 16 tokens x 32 channels) x Q' (B), two
@@ -557,32 +557,36 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   const int nsk = nj > 0 ? (nG >> ksh) * DK * 2 : 0, nsv = nj > 0 ? nG * ((DV * 2) >> vsh) : 0;
   const buf_rsrc rks = make_rsrc(ksbase, nsk), rkz = make_rsrc(kzbase, nsk);
   const buf_rsrc rvs = make_rsrc(vsbase, nsv), rvz = make_rsrc(vzbase, nsv);
-  auto stage_group = [&](int g, int slot) {
+  const buf_rsrc r_none = make_rsrc(nullptr, 0);  // copies from it touch no memory
+  // `live` false: the same copies from an empty buffer (counted like the others,
+  // no memory traffic)
+  auto stage_group = [&](int g, int slot, bool live) {
     unsigned char* sb = stage + slot * LL::kSlot;
     const uint32_t gk = uint32_t(g) * (32 * KROW);
+    const buf_rsrc rk_ = live ? rk : r_none, rv_ = live ? rv : r_none;
     if constexpr (KLIN) {
-      lds_dma<16>(rk, klin, gk, sb);
+      lds_dma<16>(rk_, klin, gk, sb);
     } else {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-        for (int hp = 0; hp < KNP; ++hp) lds_dma<KPB>(rk, koff[tt] + hp * KPB, gk, sb + (tt * KNP + hp) * 64 * KPB);
+        for (int hp = 0; hp < KNP; ++hp) lds_dma<KPB>(rk_, koff[tt] + hp * KPB, gk, sb + (tt * KNP + hp) * 64 * KPB);
       }
     }
     const uint32_t gv = uint32_t(g) * (DV * VB * 4);
 #pragma unroll
-    for (int k = 0; k < VNP; ++k) lds_dma<16>(rv, voff + 16 * k, gv, sb + LL::kStK + k * 1024);
+    for (int k = 0; k < VNP; ++k) lds_dma<16>(rv_, voff + 16 * k, gv, sb + LL::kStK + k * 1024);
     unsigned char* ss = sb + LL::kStK + LL::kStV;
-    lds_dma<4>(rks, kso, uint32_t(g >> ksh) * (DK * 2), ss);
-    lds_dma<4>(rkz, kso, uint32_t(g >> ksh) * (DK * 2), ss + oKZ);
-    lds_dma<4>(rvs, vso, uint32_t(g) * uint32_t((DV * 2) >> vsh), ss + oVS);
-    lds_dma<4>(rvz, vso, uint32_t(g) * uint32_t((DV * 2) >> vsh), ss + oVZ);
+    lds_dma<4>(live ? rks : r_none, kso, uint32_t(g >> ksh) * (DK * 2), ss);
+    lds_dma<4>(live ? rkz : r_none, kso, uint32_t(g >> ksh) * (DK * 2), ss + oKZ);
+    lds_dma<4>(live ? rvs : r_none, vso, uint32_t(g) * uint32_t((DV * 2) >> vsh), ss + oVS);
+    lds_dma<4>(live ? rvz : r_none, vso, uint32_t(g) * uint32_t((DV * 2) >> vsh), ss + oVZ);
   };
   // The query first (vector-memory operations complete in order, so it would
   // otherwise wait for the staged groups): the 8 elements of the lane's Q' task.
-  // Then the groups of the first D steps into the ring (a unit with fewer
-  // groups re-reads its last one; a unit without groups issues copies that touch
-  // no memory).
+  // Then the groups of the first D steps into the ring (a unit with fewer groups
+  // issues the rest as copies that touch no memory, so every unit has D steps'
+  // copies counted).
   // Raw bytes, converted only after the copies are issued (a conversion next to
   // the load would make the wave wait for it first); the buffer spans the kG
   // query rows of this KV head, so the 32-byte read of a 16-bit query stays inside.
@@ -593,7 +597,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   const u32x4 qw0 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff, 0, 0);
   const u32x4 qw1 = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 16, 0, 0);
 #pragma unroll
-  for (int u = 0; u < D; ++u) stage_group(g0 + TS * min(u, nj > 0 ? nj - 1 : 0), u);
+  for (int u = 0; u < D; ++u) stage_group(g0 + TS * u, u, u < nj);
   __builtin_amdgcn_sched_barrier(0);
   float qx[8];
   if (a.q_dtype == KVQ_BF16) {
@@ -905,9 +909,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
     // have been consumed, so no wait on LDS is needed, and groups i + 1 ..
     // i + D - 1 stay in flight while the wave waits for group i.  With D == 2 step i's
     // own position takes the copies of group i + 2 right after it has been read
-    // (after a wait for the reads).  Past the end of a short run the prologue
-    // re-reads its last group, which is always in bounds.  The last step waits
-    // for all copies, so the ring is idle afterwards.
+    // (after a wait for the reads).  Past the end of a short run the prologue's
+    // copies came from an empty buffer.  The last step waits for all copies, so
+    // the ring is idle afterwards.
     // Issue priority falls by one level per quarter of the unit's steps: the
     // waves of a SIMD are otherwise served oldest first and would finish far
     // apart; this way a wave that is ahead yields to the ones behind it.
@@ -929,7 +933,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
         const int prev = (pos + D - 1) % D;
         if (i >= 1 && i - 1 + D < ns) {
           wave_lds_order();
-          stage_group(g0 + TS * (i - 1 + D), prev);
+          stage_group(g0 + TS * (i - 1 + D), prev, true);
         }
       }
       // copy steps issued after group i: D - 1 (fewer near the end of the run;
@@ -939,7 +943,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
       read_group(pos, d);
       if constexpr (D == 2) {
         wave_lds_sync();
-        if (i + D < ns) stage_group(g0 + TS * (i + D), pos);
+        if (i + D < ns) stage_group(g0 + TS * (i + D), pos, true);
       }
       // the Q' / P' tiles overwrite the slot just read: LDS keeps the wave's
       // order, the compiler must keep it too
@@ -951,7 +955,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
       score_step(d, tiles);
       value_step(vws, tiles);
     };
-    static_assert(D >= 2 && D <= 4, "ring depth");
+    static_assert(D == 2 || D == 3, "ring depth");
     if constexpr (lds_waves_per_simd<DK, DV, KB, VB, D>() <= 2) {
       for (int i0 = 0; i0 < ns; i0 += D) {
         one_step(i0, std::integral_constant<int, 0>{});
@@ -959,16 +963,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
         if constexpr (D > 2) {
           if (i0 + 2 < ns) one_step(i0 + 2, std::integral_constant<int, 2 % D>{});
         }
-        if constexpr (D > 3) {
-          if (i0 + 3 < ns) one_step(i0 + 3, std::integral_constant<int, 3 % D>{});
-        }
       }
     } else {
-      // instances held to 128 registers (3 or 4 waves per SIMD): the unrolled loop
-      // keeps more addresses live and spills there, so the position stays a
-      // variable.  It is hidden from the compiler, which would otherwise keep one
-      // address per LDS access advanced by a slot every step and corrected at the
-      // wrap (two vector additions per access instead of one).
+      // instances whose LDS admits 3 or 4 waves per SIMD (at most 168 or 128
+      // registers): unrolled, the 128-register ones spill and the 168-register
+      // ones measured no faster, so the position stays a variable.  It is hidden
+      // from the compiler, which would otherwise keep one address per LDS access
+      // advanced by a slot every step and corrected at the wrap (two vector
+      // additions per access instead of one).
       for (int i = 0; i < ns; ++i) {
         int pos = i % D;
         asm volatile("" : "+s"(pos));
@@ -1124,10 +1126,6 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   }
 }
 
-#ifndef KVQ_DECODE_MAX_DEPTH
-#define KVQ_DECODE_MAX_DEPTH 4
-#endif
-
 // Opt an instance into more than the default 64 KB of LDS (gfx950 has 160 KB per
 // compute unit), once per device: the attribute stays set for the process.
 template <int DK, int DV, int KB, int VB, int D>
@@ -1172,19 +1170,17 @@ template <int DK, int DV, int KB, int VB>
 hipError_t run_one(const DecodeArgs& a, hipStream_t stream, int dev, int cus, DecodePlan* plan, bool launch) {
   // Units are cut only as far as 8 waves per compute unit: measured on the 128K
   // workload, 2048 long runs stream HBM better than 4096 half-length ones (the
-  // memory system serves the larger set of requests less evenly).  The ring is
-  // then the deepest (most copies in flight per wave) whose LDS still lets the
-  // whole grid be resident at once (up to 4 steps: a 5th measured no faster on
-  // the 128K workload).
+  // memory system serves the larger set of requests less evenly).  The ring has
+  // 3 steps where that LDS still lets the whole grid be resident at once, else 2:
+  // with the grid's 2048 waves, 4 steps (more copies in flight) measured no faster
+  // on the 128K workload and slower on the 16K and 4K ones (50.5 against 51.1 us,
+  // 17.7 against 18.5), and a 5th no faster either.
   const int per_cu = 4 * lds_waves_per_simd<DK, DV, KB, VB, 2>();
   const int units = decode_mfma_units(a.L, a.P, int64_t(cus) * (per_cu < 8 ? per_cu : 8));
   const int64_t waves = int64_t(units) * a.L.B * a.L.Hkv;
   const int64_t simds = int64_t(cus) * 4;
   int depth = 2, per_simd = lds_waves_per_simd<DK, DV, KB, VB, 2>();
-  if (KVQ_DECODE_MAX_DEPTH >= 4 && waves <= simds * lds_waves_per_simd<DK, DV, KB, VB, 4>()) {
-    depth = 4;
-    per_simd = lds_waves_per_simd<DK, DV, KB, VB, 4>();
-  } else if (KVQ_DECODE_MAX_DEPTH >= 3 && waves <= simds * lds_waves_per_simd<DK, DV, KB, VB, 3>()) {
+  if (waves <= simds * lds_waves_per_simd<DK, DV, KB, VB, 3>()) {
     depth = 3;
     per_simd = lds_waves_per_simd<DK, DV, KB, VB, 3>();
   }
@@ -1194,7 +1190,6 @@ hipError_t run_one(const DecodeArgs& a, hipStream_t stream, int dev, int cus, De
   plan->ranks = int(std::min<int64_t>(per_simd, std::max<int64_t>(1, (waves + simds - 1) / simds)));
   plan->waves = waves;
   if (!launch) return hipSuccess;
-  if (depth == 4) return launch_depth<DK, DV, KB, VB, 4>(a, stream, dev, *plan);
   if (depth == 3) return launch_depth<DK, DV, KB, VB, 3>(a, stream, dev, *plan);
   return launch_depth<DK, DV, KB, VB, 2>(a, stream, dev, *plan);
 }
