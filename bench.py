@@ -320,9 +320,11 @@ def decode_cold(torch, api, lay, cache, qd, P, scale, dev, reps=20):
     """Decode kernel time with nothing of the cache left in the caches: before each
     call an untimed plain read of 1 GiB (four times the 256 MB memory-side cache)
     evicts it.  A read, not a write: freshly written lines would be written back
-    inside the decode.  Events bracket the decode kernel and the whole call."""
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    sink = torch.empty(1, dtype=torch.int32, device=dev)
+    inside the decode.  The read is a torch reduction (plain loads that allocate in
+    the caches), not kvq_read_probe, whose loads carry the non-temporal hint.
+    Events bracket the decode kernel and the whole call."""
+    flush = torch.zeros(1 << 27, dtype=torch.int64, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
     ws = api.alloc_workspace(lay, P, dev)
     out = torch.empty((lay.B, lay.Hq, lay.Dv), dtype=torch.float32, device=dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
@@ -331,7 +333,7 @@ def decode_cold(torch, api, lay, cache, qd, P, scale, dev, reps=20):
             x.record()
     torch.cuda.synchronize()
     for i in range(reps):
-        api.kvq_read_probe(flush, sink)
+        torch.sum(flush, dim=0, out=sink)
         ev[i][0].record()
         api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws,
                            after_decode_event=ev[i][1])

@@ -5,7 +5,9 @@
 // Whole-grid sweep: 256-thread workgroups, each iteration a workgroup reads one
 // contiguous 16 KB block (four 16-byte loads per thread, all issued before any is
 // used) and the grid strides over the buffer, so at any moment the reads in
-// flight cover one contiguous window of the buffer.  Each workgroup folds what it
+// flight cover one contiguous window of the buffer.  The loads carry the
+// non-temporal hint, as the decode kernel's copies do (measured: 7.06 TB/s on a
+// 538 MB buffer against 6.14 TB/s with plain loads).  Each workgroup folds what it
 // read into an XOR and stores it only if it equals a constant no buffer of
 // non-zero length produces by accident in practice; that keeps the loads alive.
 #include <algorithm>
@@ -20,18 +22,20 @@ namespace {
 constexpr int kProbeThreads = 256;
 constexpr int kProbeBlock = 4 * kProbeThreads;  // 16-byte units per workgroup iteration
 
-__global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const uint4* p, int64_t n16, uint32_t* sink) {
+typedef uint32_t probe_u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const probe_u32x4* p, int64_t n16, uint32_t* sink) {
   uint32_t acc = 0;
   const int64_t stride = int64_t(gridDim.x) * kProbeBlock;
   for (int64_t base = int64_t(blockIdx.x) * kProbeBlock; base < n16; base += stride) {
-    uint4 x[4];
+    probe_u32x4 x[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int64_t i = base + k * kProbeThreads + threadIdx.x;
-      x[k] = i < n16 ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+      x[k] = i < n16 ? __builtin_nontemporal_load(p + i) : probe_u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc ^= x[k].x ^ x[k].y ^ x[k].z ^ x[k].w;
+    for (int k = 0; k < 4; ++k) acc ^= x[k][0] ^ x[k][1] ^ x[k][2] ^ x[k][3];
   }
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
@@ -48,7 +52,7 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipS
   const int64_t want = int64_t(cus > 0 ? cus : 1) * 8;
   const int64_t blocks = std::min<int64_t>(want, (n16 + kProbeBlock - 1) / kProbeBlock);
   hipLaunchKernelGGL(read_probe_kernel, dim3(unsigned(blocks)), dim3(kProbeThreads), 0, stream,
-                     static_cast<const uint4*>(buf), n16, sink);
+                     static_cast<const probe_u32x4*>(buf), n16, sink);
   return hipGetLastError();
 }
 
