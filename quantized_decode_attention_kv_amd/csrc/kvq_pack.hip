@@ -226,6 +226,40 @@ __device__ __forceinline__ void quant_levels(const float (&x)[N], const float (&
   for (int k = 0; k < N; ++k) code[k] = __builtin_amdgcn_fmed3f(rt[k], 0.0f, levels);
 }
 
+// quant_levels with one fma per element for the fast quotient: t = fl(x r + nzr),
+// nzr = fl(-z r), r = rcp(s) (one ulp).  Against the contract's V = fl(fl(x - z) / s),
+// |t - V| <= |Q| 2^-21.6 + |z r| 2^-23.9 with Q = (x - z) / s (rounding of the fma,
+// of nzr and of the reciprocal, and the contract's own two roundings); where
+// |Q| > levels + 1 both sides clamp to the same code, so with |Q| <= 256 the bound
+// delta = 2^-13 + |z r| 2^-23 holds, and an element whose t lies within
+// lim = 0.5 - delta of an integer gets the same code as V (|V - rint(t)| < 0.5).
+// The others (near-ties; rare) take the division.  nzr_max: the largest |nzr| of
+// the elements; s == 0 gives r == 0, t = -0 or +0 and code 0, as the contract says.
+// exact(k) returns fl(fl(x_k - z_k) / s_k) (the contract's quotient; called rarely).
+__device__ __forceinline__ float fma_quant_limit(float nzr_max) {
+  return 0.5f - (0x1p-13f + nzr_max * 0x1p-23f);
+}
+template <int N, typename Exact>
+__device__ __forceinline__ void quant_levels_fma(const float (&x)[N], const float (&r)[N], const float (&nzr)[N],
+                                                 float lim, float levels, float (&code)[N], Exact&& exact) {
+  float t[N], rt[N];
+  float worst = 0.0f;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    t[k] = fmaf(x[k], r[k], nzr[k]);
+    rt[k] = __builtin_rintf(t[k]);
+    worst = fmaxf(worst, fabsf(t[k] - rt[k]));
+  }
+  if (__builtin_expect(worst > lim, 0)) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      if (fabsf(t[k] - rt[k]) > lim) rt[k] = __builtin_rintf(exact(k));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) code[k] = __builtin_amdgcn_fmed3f(rt[k], 0.0f, levels);
+}
+
 // Byte `b` of `w` replaced by the code q (an integer in [0, 255] held as a float,
 // so the conversion is exact whatever its rounding): one instruction that both
 // converts and places the code.
@@ -637,7 +671,7 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
   float4 (*kmn_s)[D / 4] = reinterpret_cast<float4 (*)[D / 4]>(part_s);
   float4 (*kmx_s)[D / 4] = reinterpret_cast<float4 (*)[D / 4]>(part_s + 16 * (D / 4));
   static_assert(sizeof(float4) * 2 * 16 * (D / 4) >= sizeof(uint32_t) * kPackWaves * 64 * 8, "value slots");
-  __shared__ float4 ks_s[D / 4], kz_s[D / 4], kr_s[D / 4];
+  __shared__ float4 ks_s[D / 4], kz_s[D / 4], kr_s[D / 4], knzr_s[D / 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -767,23 +801,29 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
     reinterpret_cast<float*>(ks_s)[tid] = q.s;
     reinterpret_cast<float*>(kz_s)[tid] = q.z;
     reinterpret_cast<float*>(kr_s)[tid] = q.r;
+    reinterpret_cast<float*>(knzr_s)[tid] = -q.z * q.r;
   }
   __syncthreads();
   {
-    float ks[8], kz[8], kr[8];
+    float kr[8], knzr[8];
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
-      const float4 s4 = ks_s[2 * c + hq], z4 = kz_s[2 * c + hq], r4 = kr_s[2 * c + hq];
-      ks[4 * hq] = s4.x; ks[4 * hq + 1] = s4.y; ks[4 * hq + 2] = s4.z; ks[4 * hq + 3] = s4.w;
-      kz[4 * hq] = z4.x; kz[4 * hq + 1] = z4.y; kz[4 * hq + 2] = z4.z; kz[4 * hq + 3] = z4.w;
+      const float4 r4 = kr_s[2 * c + hq], n4 = knzr_s[2 * c + hq];
       kr[4 * hq] = r4.x; kr[4 * hq + 1] = r4.y; kr[4 * hq + 2] = r4.z; kr[4 * hq + 3] = r4.w;
+      knzr[4 * hq] = n4.x; knzr[4 * hq + 1] = n4.y; knzr[4 * hq + 2] = n4.z; knzr[4 * hq + 3] = n4.w;
     }
+    float nmax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) nmax = fmaxf(nmax, fabsf(knzr[k]));
+    const float klim = fma_quant_limit(nmax);
+    const float* ksf = reinterpret_cast<const float*>(ks_s) + 8 * c;
+    const float* kzf = reinterpret_cast<const float*>(kz_s) + 8 * c;
     uint32_t* kdst = static_cast<uint32_t*>(a.cache.k_codes) + ((slab * a.g_stride + g) * KVQ_GROUP) * kWords;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint32_t lo = 0, hi = 0;  // channels 8c .. 8c+7 at bits (k * KB) of a 64-bit field
       float q[8];
-      quant_levels<8>(kx[j], ks, kz, kr, k_levels, q);
+      quant_levels_fma<8>(kx[j], kr, knzr, klim, k_levels, q, [&](int k) { return (kx[j][k] - kzf[k]) / ksf[k]; });
       if constexpr (KB == 8) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -876,13 +916,16 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
     uint32_t part[8];
     float c0[8], c1[8];
     {
-      float s8[8], z8[8], r8[8];
+      float r8[8], n8[8];
+      const float n0 = -vz[0] * vr[0], n1 = -vz[1] * vr[1];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) { s8[k] = vs[0]; z8[k] = vz[0]; r8[k] = vr[0]; }
-      quant_levels<8>(vx[0], s8, z8, r8, v_levels, c0);
+      for (int k = 0; k < 8; ++k) { r8[k] = vr[0]; n8[k] = n0; }
+      quant_levels_fma<8>(vx[0], r8, n8, fma_quant_limit(fabsf(n0)), v_levels, c0,
+                          [&](int k) { return (vx[0][k] - vz[0]) / vs[0]; });
 #pragma unroll
-      for (int k = 0; k < 8; ++k) { s8[k] = vs[1]; z8[k] = vz[1]; r8[k] = vr[1]; }
-      quant_levels<8>(vx[1], s8, z8, r8, v_levels, c1);
+      for (int k = 0; k < 8; ++k) { r8[k] = vr[1]; n8[k] = n1; }
+      quant_levels_fma<8>(vx[1], r8, n8, fma_quant_limit(fabsf(n1)), v_levels, c1,
+                          [&](int k) { return (vx[1][k] - vz[1]) / vs[1]; });
     }
     // token p's code at bit slot * VB, token p + 4's 16 bits higher
 #pragma unroll
