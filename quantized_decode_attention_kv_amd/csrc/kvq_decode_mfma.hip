@@ -1021,6 +1021,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
     const uint8_t* vr = static_cast<const uint8_t*>(a.cache.v_fp16) + slab * a.r_stride * (DV * 2);
     for (int rt = unit; rt < nRT; rt += U) {
       const int rbase = rt * 32;
+      // the tile's value rows, loaded first so that their latency passes under the
+      // scores and the softmax (channels 2 lane, 2 lane + 1 of each row)
+      uint32_t vv[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int row = min(rbase + u, R - 1);
+        vv[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vr + (uint32_t(row) * (DV * 2) + 4 * lane)));
+      }
       f32x4 sacc[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -1048,12 +1056,6 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
       // values on the VALU: lane owns channels 2 lane, 2 lane + 1 of every row
 #pragma unroll
       for (int t0 = 0; t0 < 32; t0 += 8) {
-        uint32_t vv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int row = min(rbase + t0 + u, R - 1);
-          vv[u] = *reinterpret_cast<const uint32_t*>(vr + (uint32_t(row) * (DV * 2) + 4 * lane));
-        }
 #pragma unroll
         for (int u4 = 0; u4 < 8; u4 += 4) {
           f32x4 pq[kG];
@@ -1061,7 +1063,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
           for (int i = 0; i < kG; ++i) pq[i] = *reinterpret_cast<const f32x4*>(PT + i * 32 + t0 + u4);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const half2_t hv = as_half2(vv[u4 + u]);
+            const half2_t hv = as_half2(vv[t0 + u4 + u]);
 #pragma unroll
             for (int i = 0; i < kG; ++i) {
               o_r[i][0] = fmaf(pq[i][u], float(hv[0]), o_r[i][0]);
