@@ -278,14 +278,19 @@ __device__ __forceinline__ void out_store(T* p, T v) {
   __builtin_nontemporal_store(v, p);
 }
 
+// The DPP exchanges below (quad permutations and row mirrors, all rows and banks
+// enabled) read a lane of the same row that always exists, so bound_ctrl changes
+// nothing about their results; it is set so that the compiler can fold the
+// exchange into the ALU instruction that consumes it (one instruction instead of a
+// move and the operation).
 // min / max over the 16 lanes of a DPP row (every lane gets the result)
 template <bool MAX>
 __device__ __forceinline__ float row16_reduce(float v) {
   auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
-  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
-  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
-  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
-  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));  // row_mirror
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));   // quad_perm 1,0,3,2
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));   // quad_perm 2,3,0,1
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));  // row_half_mirror
+  v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));  // row_mirror
   return v;
 }
 
@@ -506,15 +511,15 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackArgs a) {
         mn = fminf(mn, x[k]);
         mx = fmaxf(mx, x[k]);
       }
-      mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
-      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xF, 0xF, false)));
+      mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0xB1, 0xF, 0xF, true)));  // lane ^ 1
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xF, 0xF, true)));
       if (vg >= 64) {  // lane ^ 2
-        mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x4E, 0xF, 0xF, false)));
-        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xF, 0xF, false)));
+        mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x4E, 0xF, 0xF, true)));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xF, 0xF, true)));
       }
       if (vg >= 128) {  // the other quad of the 8 lanes (its lanes already agree)
-        mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x141, 0xF, 0xF, false)));
-        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x141, 0xF, 0xF, false)));
+        mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x141, 0xF, 0xF, true)));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x141, 0xF, 0xF, true)));
       }
       const QParams q = make_qparams(mn, mx, v_levels);
       const int tiles_per_group = vg >> 4;
@@ -853,7 +858,7 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
         out_store(rowp + c, lo);
       } else {
         // 16 bits per lane: lanes 2m, 2m + 1 fill word m
-        const uint32_t nb = uint32_t(__builtin_amdgcn_mov_dpp(int(lo), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+        const uint32_t nb = uint32_t(__builtin_amdgcn_mov_dpp(int(lo), 0xB1, 0xF, 0xF, true));  // lane ^ 1
         if ((c & 1) == 0) out_store(rowp + (c >> 1), lo | (nb << 16));
       }
     }
@@ -877,10 +882,10 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
       mn = fminf(mn, vx[j][k]);
       mx = fmaxf(mx, vx[j][k]);
     }
-    mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
-    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xF, 0xF, false)));
-    mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
-    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xF, 0xF, false)));
+    mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0xB1, 0xF, 0xF, true)));  // lane ^ 1
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xF, 0xF, true)));
+    mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x4E, 0xF, 0xF, true)));  // lane ^ 2
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xF, 0xF, true)));
     if (lpg >= 8) {
       mn = fminf(mn, __shfl_xor(mn, 4));
       mx = fmaxf(mx, __shfl_xor(mx, 4));
@@ -895,9 +900,9 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
   // lane c forms the parameters of row c & 1; the other row's come from lane c ^ 1
   const int jm = c & 1;
   const QParams qm = make_qparams(jm ? vmn[1] : vmn[0], jm ? vmx[1] : vmx[0], v_levels);
-  const float os = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(qm.s), 0xB1, 0xF, 0xF, false));
-  const float oz = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(qm.z), 0xB1, 0xF, 0xF, false));
-  const float orr = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(qm.r), 0xB1, 0xF, 0xF, false));
+  const float os = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(qm.s), 0xB1, 0xF, 0xF, true));
+  const float oz = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(qm.z), 0xB1, 0xF, 0xF, true));
+  const float orr = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(qm.r), 0xB1, 0xF, 0xF, true));
   const float vs[2] = {jm ? os : qm.s, jm ? qm.s : os};
   const float vz[2] = {jm ? oz : qm.z, jm ? qm.z : oz};
   const float vr[2] = {jm ? orr : qm.r, jm ? qm.r : orr};
