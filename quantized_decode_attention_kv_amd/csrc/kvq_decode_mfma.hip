@@ -31,8 +31,8 @@
 // its groups through an LDS ring of D = 2 or 3 slots (buffer loads straight into
 // LDS, so up to D - 1 later groups are in flight while one is computed), keeps its
 // own online-softmax state and writes its own partial result.  The launcher takes
-// D = 3 where its LDS keeps the whole grid resident (8 waves per compute unit on
-// the 128K-token workload), else 2.  Per group:
+// D = 3 where its LDS keeps the whole grid resident, else 2 (the 128K-token
+// workload: 16 waves per compute unit on a 2-deep ring).  Per group:
 //   1. Q' = q s (hi, lo) for 64 (query, 8-channel block) tasks, one per lane, into
 //      a wave-private LDS tile;
 //   2. scores S^T[token, column] = codes (A: 16 tokens x 32 channels) x Q' (B), two
@@ -285,8 +285,8 @@ __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t (&w)[NB < 
   }
 }
 
-// LDS of one workgroup (one wave), in bytes (at most 20 KB for the common
-// shapes: 8 waves per compute unit):
+// LDS of one wave, in bytes (at most 20 KB for the common shapes, 10 KB or less
+// where 16 waves share a compute unit):
 //   a ring of D slots (D key groups in flight), one key group each: key codes,
 //   value codes, key scales, key zeros, value scales, value zeros;
 //   the Q' operand tile of the group being computed (KK chunks of 32 channels)
@@ -1177,15 +1177,17 @@ hipError_t launch_depth(DecodeArgs a, hipStream_t stream, int dev, const DecodeP
 
 template <int DK, int DV, int KB, int VB>
 hipError_t run_one(const DecodeArgs& a, hipStream_t stream, int dev, int cus, DecodePlan* plan, bool launch) {
-  // Units are cut only as far as 8 waves per compute unit: measured on the 128K
-  // workload, 2048 long runs stream HBM better than 4096 half-length ones (the
-  // memory system serves the larger set of requests less evenly).  The ring has
+  // Units are cut as far as the 2-deep ring's LDS keeps every wave resident (up to
+  // 16 waves per compute unit).  With the non-temporal copies the 128K workload
+  // runs faster as 4096 half-length runs on a 2-deep ring than as 2048 long ones on
+  // a 3-deep ring (cold calls 103.6 -> 101.0 us p50, inside the step 103.9 -> 100.0,
+  // interleaved); with plain copies it had been the other way round.  The ring has
   // 3 steps where that LDS still lets the whole grid be resident at once, else 2:
-  // with the grid's 2048 waves, 4 steps (more copies in flight) measured no faster
+  // with a grid of 2048 waves, 4 steps (more copies in flight) measured no faster
   // on the 128K workload and slower on the 16K and 4K ones (50.5 against 51.1 us,
   // 17.7 against 18.5), and a 5th no faster either.
   const int per_cu = 4 * lds_waves_per_simd<DK, DV, KB, VB, 2>();
-  const int units = decode_mfma_units(a.L, a.P, int64_t(cus) * (per_cu < 8 ? per_cu : 8));
+  const int units = decode_mfma_units(a.L, a.P, int64_t(cus) * (per_cu < 16 ? per_cu : 16));
   const int64_t waves = int64_t(units) * a.L.B * a.L.Hkv;
   const int64_t simds = int64_t(cus) * 4;
   int depth = 2, per_simd = lds_waves_per_simd<DK, DV, KB, VB, 2>();
