@@ -682,10 +682,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
   //   (the skew of 4 entries per channel group spreads a row's writes over 16
   //   bank slots and keeps the lane part of every address independent of gc),
   //   else at e ^ (gc & 1) << 3 ^ (gc >> 1) << 2.
-  // The swizzled addresses take a few more registers; the D = 2 instances held
-  // to 128 (4 waves per SIMD) keep the plain order, where the swizzle would
-  // spill.
-  constexpr bool kSwz = lds_waves_per_simd<DK, DV, KB, VB, D>() < 4 || D > 2;
+  // The swizzled addresses take a few more registers: three instances held to 128
+  // (the 2-deep rings of K2V4 at key widths 64 and 128 and of K8V2 at width 32,
+  // 4 waves per SIMD) would spill with them and keep the plain order.  Measured
+  // on the 2-deep K4V2 ring of the 128K workload: 101.1 -> 92.1 us p50 inside the
+  // step, 102.9 -> 94.1 as cold calls (LDS bank-conflict cycles per LDS
+  // instruction 4.8 with the plain order).
+  constexpr bool kSwz = !(D == 2 && lds_waves_per_simd<DK, DV, KB, VB, D>() == 4 &&
+                          ((KB == 2 && VB == 4 && DK >= 64) || (DK == 32 && KB == 8 && VB == 2)));
   auto qb_at = [](int e) { return kSwz ? e ^ (((e >> 4) & 1) << 2) : e; };
   auto pa_at = [](int e) { return kSwz ? e ^ (((e >> 5) & 1) << 3) ^ (((e >> 6) & 1) << 2) : e; };
   // place of P' entry (gc, x = gq*8 + j)
