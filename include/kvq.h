@@ -401,8 +401,9 @@ int kv_decode_attn_side(const kvq_layout* L, const void* q, int q_dtype, const k
 
 /*
  * kvq_read_probe — measurement support, not part of the decode path: reads
- * buf[0, bytes) once (bytes rounded down to a multiple of 16) with a plain
- * grid-wide streaming read, so that a caller can time the HBM read rate the
+ * buf[0, bytes) once (bytes rounded down to a multiple of 16) with a grid-wide
+ * streaming read of non-temporal loads (the cache policy of the decode kernel's
+ * copies), so that a caller can time the HBM read rate the
  * device reaches and report it next to the decode kernel's.  buf: 16-byte
  * aligned device memory, owned by the caller.  sink: 4 bytes of device memory
  * the kernel may write (it keeps the reads from being optimized away; its
