@@ -237,6 +237,51 @@ def test_pack_rounding_ties_and_near_ties(D):
             _compare_pack(cache_to_numpy(cache), O.pack_all(Kin, Vin, w), w.name + " ")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_pack_ties_with_offset_groups(dtype):
+    """Exact half-integer quotients in groups whose minimum is far from zero (z = +-32
+    .. +-47), on the 16-bit inputs' 128-wide pack kernel: that kernel forms the fast
+    quotient as one fma, x r - z r, whose error grows with |z r|, and widens its
+    window of elements that take the exact division to match; the codes must still
+    be the contract's (round half to even of fl(fl(x - z) / s)).  Values x = z + k s/2
+    with s a power of two, every k from 0 to 2 levels in each group, so that every
+    group's range is exactly levels * s and every odd k is a tie."""
+    D = 128
+    for bits in ((2, 4, 8) if dtype == "f16" else (2, 4)):
+        levels = 2 ** bits - 1
+        # half-steps s / 2 must be exact in the input format at |x| < 64
+        s = 1.0 / 16 if dtype == "f16" else 0.5
+        w = Workload("ties_off%d_%s" % (bits, dtype), B=1, Hq=4, Hkv=1, Dk=D, Dv=D, T=64, k_bits=bits, v_bits=bits,
+                     dtype=dtype, seed=43)
+        K = np.zeros((1, 1, 64, D), dtype=np.float32)
+        V = np.zeros((1, 1, 64, D), dtype=np.float32)
+        nk = 2 * levels + 1
+        for t in range(64):
+            for c in range(D):
+                zk = (32.0 + (c % 8)) * (1 if c % 3 else -1)
+                kk = 0 if t % 32 == 0 else (nk - 1 if t % 32 == 31 else (7 * t + 3 * c) % nk)
+                K[0, 0, t, c] = zk + kk * s / 2
+                zv = (40.0 + (t % 8)) * (1 if (t + c // 32) % 2 else -1)
+                kv = 0 if c % 32 == 0 else (nk - 1 if c % 32 == 31 else (5 * c + 11 * t) % nk)
+                V[0, 0, t, c] = zv + kv * s / 2
+        if dtype == "f16":
+            for x in (K, V):
+                assert np.array_equal(x.astype(np.float16).astype(np.float32), x)
+            Kin, Vin = K.astype(np.float16).view(np.uint16), V.astype(np.float16).view(np.uint16)
+        else:
+            assert not (K.view(np.uint32) & 0xFFFF).any() and not (V.view(np.uint32) & 0xFFFF).any()
+            Kin = (K.view(np.uint32) >> 16).astype(np.uint16)
+            Vin = (V.view(np.uint32) >> 16).astype(np.uint16)
+        lay = api.Layout.from_workload(w)
+        cache = api.kv_quant_pack(lay, to_device(Kin, dtype), to_device(Vin, dtype))
+        torch.cuda.synchronize()
+        ref = O.pack_all(Kin, Vin, w)
+        # the construction gives s exactly and z exactly (so the ties are real ties)
+        for key in ("k_scale", "v_scale"):
+            assert np.all(ref[key].view(np.float16).astype(np.float32) == np.float32(s))
+        _compare_pack(cache_to_numpy(cache), ref, w.name + " ")
+
+
 # ------------------------------------------------------------------ full-size runs
 
 def _sample_slabs(w, n):
