@@ -1186,8 +1186,12 @@ hipError_t run_one(const DecodeArgs& a, hipStream_t stream, int dev, int cus, De
   // runs faster as 4096 half-length runs on a 2-deep ring than as 2048 long ones on
   // a 3-deep ring (cold calls 103.6 -> 101.0 us p50, inside the step 103.9 -> 100.0,
   // interleaved); with plain copies it had been the other way round.  The ring has
-  // 3 steps where that LDS still lets the whole grid be resident at once, else 2:
-  // with a grid of 2048 waves, 4 steps (more copies in flight) measured no faster
+  // 3 steps where the grid puts at most 2 waves on a SIMD and that LDS still lets
+  // the whole grid be resident at once, else 2: with 4 waves per SIMD the other
+  // waves keep enough copies in flight (32K workload, 4096 waves: 156.9 -> 153.9 us
+  // p50 with the 2-deep ring as cold calls, 181.4 -> 178.1 back to back); with 2
+  // per SIMD the third slot pays (4K workload 16.4 -> 16.0 us, 16K 47.2 -> 46.8).
+  // With a grid of 2048 waves, 4 steps (more copies in flight) measured no faster
   // on the 128K workload and slower on the 16K and 4K ones (50.5 against 51.1 us,
   // 17.7 against 18.5), and a 5th no faster either.
   const int per_cu = 4 * lds_waves_per_simd<DK, DV, KB, VB, 2>();
@@ -1195,7 +1199,7 @@ hipError_t run_one(const DecodeArgs& a, hipStream_t stream, int dev, int cus, De
   const int64_t waves = int64_t(units) * a.L.B * a.L.Hkv;
   const int64_t simds = int64_t(cus) * 4;
   int depth = 2, per_simd = lds_waves_per_simd<DK, DV, KB, VB, 2>();
-  if (waves <= simds * lds_waves_per_simd<DK, DV, KB, VB, 3>()) {
+  if (waves <= simds * std::min(2, lds_waves_per_simd<DK, DV, KB, VB, 3>())) {
     depth = 3;
     per_simd = lds_waves_per_simd<DK, DV, KB, VB, 3>();
   }
