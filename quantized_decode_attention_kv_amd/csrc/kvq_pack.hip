@@ -239,9 +239,21 @@ __device__ __forceinline__ void quant_levels(const float (&x)[N], const float (&
 __device__ __forceinline__ float fma_quant_limit(float nzr_max) {
   return 0.5f - (0x1p-13f + nzr_max * 0x1p-23f);
 }
+//
+// clamp (wave-uniform) false skips the clamp to [0, levels]; the caller passes
+// false only when every element's group has |z r| <= 128 and s >= 2^-14 (r <=
+// 2^14) or s == 0 (clamp_free below), where the contract's clamp changes nothing:
+// with z = fp16(mn), |mn - z| <= 2^-11 |mn| (or <= 2^-25 for fp16-subnormal mn),
+// so (x - z) / s >= -2^-11 |z| / s >= -0.07; and s >= fl(fl(mx - mn) / levels)
+// (1 - 2^-11), so (x - z) / s <= levels (1 + 2^-10.9) + 0.07 < levels + 0.5.
+// Both round into [0, levels] (a -0 code converts to 0).
+__device__ __forceinline__ bool clamp_free(float nzr_max, float r_max) {
+  return nzr_max <= 128.0f && r_max <= 16384.0f;
+}
 template <int N, typename Exact>
 __device__ __forceinline__ void quant_levels_fma(const float (&x)[N], const float (&r)[N], const float (&nzr)[N],
-                                                 float lim, float levels, float (&code)[N], Exact&& exact) {
+                                                 float lim, float levels, bool clamp, float (&code)[N],
+                                                 Exact&& exact) {
   float t[N], rt[N];
   float worst = 0.0f;
 #pragma unroll
@@ -256,8 +268,12 @@ __device__ __forceinline__ void quant_levels_fma(const float (&x)[N], const floa
       if (fabsf(t[k] - rt[k]) > lim) rt[k] = __builtin_rintf(exact(k));
     }
   }
+  if (clamp) {
 #pragma unroll
-  for (int k = 0; k < N; ++k) code[k] = __builtin_amdgcn_fmed3f(rt[k], 0.0f, levels);
+    for (int k = 0; k < N; ++k) rt[k] = __builtin_amdgcn_fmed3f(rt[k], 0.0f, levels);
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) code[k] = rt[k];
 }
 
 // Byte `b` of `w` replaced by the code q (an integer in [0, 255] held as a float,
@@ -817,10 +833,14 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
       kr[4 * hq] = r4.x; kr[4 * hq + 1] = r4.y; kr[4 * hq + 2] = r4.z; kr[4 * hq + 3] = r4.w;
       knzr[4 * hq] = n4.x; knzr[4 * hq + 1] = n4.y; knzr[4 * hq + 2] = n4.z; knzr[4 * hq + 3] = n4.w;
     }
-    float nmax = 0.0f;
+    float nmax = 0.0f, rmax = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) nmax = fmaxf(nmax, fabsf(knzr[k]));
+    for (int k = 0; k < 8; ++k) {
+      nmax = fmaxf(nmax, fabsf(knzr[k]));
+      rmax = fmaxf(rmax, kr[k]);
+    }
     const float klim = fma_quant_limit(nmax);
+    const bool kclamp = !__all(clamp_free(nmax, rmax));
     const float* ksf = reinterpret_cast<const float*>(ks_s) + 8 * c;
     const float* kzf = reinterpret_cast<const float*>(kz_s) + 8 * c;
     uint32_t* kdst = static_cast<uint32_t*>(a.cache.k_codes) + ((slab * a.g_stride + g) * KVQ_GROUP) * kWords;
@@ -828,7 +848,8 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
     for (int j = 0; j < 2; ++j) {
       uint32_t lo = 0, hi = 0;  // channels 8c .. 8c+7 at bits (k * KB) of a 64-bit field
       float q[8];
-      quant_levels_fma<8>(kx[j], kr, knzr, klim, k_levels, q, [&](int k) { return (kx[j][k] - kzf[k]) / ksf[k]; });
+      quant_levels_fma<8>(kx[j], kr, knzr, klim, k_levels, kclamp, q,
+                          [&](int k) { return (kx[j][k] - kzf[k]) / ksf[k]; });
       if constexpr (KB == 8) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -923,13 +944,14 @@ __global__ __launch_bounds__(kPackThreads) void pack128_kernel(const PackArgs a)
     {
       float r8[8], n8[8];
       const float n0 = -vz[0] * vr[0], n1 = -vz[1] * vr[1];
+      const bool vclamp = !__all(clamp_free(fmaxf(fabsf(n0), fabsf(n1)), fmaxf(vr[0], vr[1])));
 #pragma unroll
       for (int k = 0; k < 8; ++k) { r8[k] = vr[0]; n8[k] = n0; }
-      quant_levels_fma<8>(vx[0], r8, n8, fma_quant_limit(fabsf(n0)), v_levels, c0,
+      quant_levels_fma<8>(vx[0], r8, n8, fma_quant_limit(fabsf(n0)), v_levels, vclamp, c0,
                           [&](int k) { return (vx[0][k] - vz[0]) / vs[0]; });
 #pragma unroll
       for (int k = 0; k < 8; ++k) { r8[k] = vr[1]; n8[k] = n1; }
-      quant_levels_fma<8>(vx[1], r8, n8, fma_quant_limit(fabsf(n1)), v_levels, c1,
+      quant_levels_fma<8>(vx[1], r8, n8, fma_quant_limit(fabsf(n1)), v_levels, vclamp, c1,
                           [&](int k) { return (vx[1][k] - vz[1]) / vs[1]; });
     }
     // token p's code at bit slot * VB, token p + 4's 16 bits higher
