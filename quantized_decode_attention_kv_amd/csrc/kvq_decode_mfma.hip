@@ -31,8 +31,9 @@
 // its groups through an LDS ring of D = 2 or 3 slots (buffer loads straight into
 // LDS, so up to D - 1 later groups are in flight while one is computed), keeps its
 // own online-softmax state and writes its own partial result.  The launcher takes
-// D = 3 where its LDS keeps the whole grid resident, else 2 (the 128K-token
-// workload: 16 waves per compute unit on a 2-deep ring).  Per group:
+// D = 3 where the grid puts at most 2 waves on a SIMD and its LDS keeps the whole
+// grid resident, else 2 (the 128K- and 32K-token workloads: 16 waves per compute
+// unit on a 2-deep ring).  Per group:
 //   1. Q' = q s (hi, lo) for 64 (query, 8-channel block) tasks, one per lane, into
 //      a wave-private LDS tile;
 //   2. scores S^T[token, column] = codes (A: 16 tokens x 32 channels) x Q' (B), two
