@@ -427,6 +427,7 @@ hipError_t plan_decode(const DecodeArgs& a, DecodePlan* plan) {
   if (a.side_rank == 0 && mfma_takes(a.L, a.P)) return mfma_decode(a, nullptr, plan, false);
   plan->kernel = KVQ_KERNEL_VALU;
   plan->units = a.P;
+  plan->rows = a.P;
   plan->depth = 0;
   plan->ranks = 0;
   plan->waves = int64_t(a.P) * a.L.Hkv * a.L.B * kWaves;
@@ -438,7 +439,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
   if (plan.kernel == KVQ_KERNEL_MFMA) {
     DecodePlan p = plan;
     e = mfma_decode(a, stream, &p, true);
-    if (e == hipSuccess && p.units != plan.units) e = hipErrorInvalidValue;  // the device changed since planning
+    if (e == hipSuccess && (p.units != plan.units || p.rows != plan.rows))
+      e = hipErrorInvalidValue;  // the device changed since planning
   } else {
     switch (a.q_dtype) {
       case KVQ_F32: e = launch_q<KVQ_F32>(a, stream); break;
@@ -449,8 +451,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
   }
   if (e != hipSuccess) return e;
   if (after_decode && (e = hipEventRecord(after_decode, stream)) != hipSuccess) return e;
-  if (plan.units == 1) return hipSuccess;
-  return launch_merge(a, plan.units, stream);
+  if (plan.rows == 1) return hipSuccess;
+  return launch_merge(a, plan.rows, stream);
 }
 
 }  // namespace kvq

@@ -1120,6 +1120,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
     lq[i] = readlane_f32(lquad, 4 * i) + readlane_f32(lquad, 16 + 4 * i) + readlane_f32(lquad, 32 + 4 * i) +
             readlane_f32(lquad, 48 + 4 * i);
   const int64_t qh0 = int64_t(b) * a.L.Hq + int64_t(h) * kG;
+  // this unit's state per query, m, l: after the zero-point sums
+  float* ML = zsm + kG * NGV;
+  static_assert(4 * (kG * DV + kG * NGV + 2 * kG) <= LL::kBytes, "team state");
 #pragma unroll
   for (int i = 0; i < kG; ++i) {
     float2 o;
@@ -1131,11 +1134,61 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, (lds_waves_per_simd<DK, DV, KB
       o.x *= inv;
       o.y *= inv;
       *reinterpret_cast<float2*>(a.out + (qh0 + i) * DV + 2 * lane) = o;
+    } else if (TS == kWavesPerGroup) {
+      // kept for the team: each lane overwrites the elements it alone read
+      *reinterpret_cast<float2*>(OM + i * DV + 2 * lane) = o;
     } else {
       // partial row of (query, unit): m, l, two unused floats, o[DV]
       float* row = a.partials + ((qh0 + i) * U + unit) * (DV + 4);
       *reinterpret_cast<float2*>(row + 4 + 2 * lane) = o;
       if (lane == 0) *reinterpret_cast<float4*>(row) = make_float4(m_q[i], lq[i], 0.0f, 0.0f);
+    }
+  }
+  if (U > 1 && TS == kWavesPerGroup) {
+    // The four units of the team combine their states by the merge's rule, wave w
+    // taking query w, and the team writes one partial row per query (or, when the
+    // team is the slab's only one, the output): a quarter of the rows for the
+    // merge to read.  Every wave of the workgroup is a unit of the team, so all
+    // of them reach the barrier.
+    static_assert(kG == kWavesPerGroup, "one query per wave");
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < kG; ++i) {
+        ML[i] = m_q[i];
+        ML[kG + i] = lq[i];
+      }
+    }
+    __syncthreads();
+    const int i = wave;
+    float mw[kWavesPerGroup], lw[kWavesPerGroup];
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w) {
+      const float* mlw = reinterpret_cast<const float*>(lds_all + w * LL::kBytes) + kG * DV + kG * NGV;
+      mw[w] = mlw[i];
+      lw[w] = mlw[kG + i];
+      M = fmaxf(M, mw[w]);
+    }
+    float2 o = make_float2(0.0f, 0.0f);
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w) {
+      const float wt = lse_weight(mw[w], M);
+      const float2 ow = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(lds_all + w * LL::kBytes) +
+                                                         i * DV + 2 * lane);
+      o.x = fmaf(wt, ow.x, o.x);
+      o.y = fmaf(wt, ow.y, o.y);
+      L = fmaf(wt, lw[w], L);
+    }
+    const int T = U / TS;
+    if (T == 1) {
+      const float inv = 1.0f / L;
+      *reinterpret_cast<float2*>(a.out + (qh0 + i) * DV + 2 * lane) = make_float2(o.x * inv, o.y * inv);
+    } else {
+      // partial row of (query, team): m, l, two unused floats, o[DV]
+      float* row = a.partials + ((qh0 + i) * T + team) * (DV + 4);
+      *reinterpret_cast<float2*>(row + 4 + 2 * lane) = o;
+      if (lane == 0) *reinterpret_cast<float4*>(row) = make_float4(M, L, 0.0f, 0.0f);
     }
   }
 }
@@ -1206,6 +1259,8 @@ hipError_t run_one(const DecodeArgs& a, hipStream_t stream, int dev, int cus, De
   }
   plan->kernel = KVQ_KERNEL_MFMA;
   plan->units = units;
+  // teams of four units combine their states in the kernel (one partial row per team)
+  plan->rows = units % kWavesPerGroup == 0 ? units / kWavesPerGroup : units;
   plan->depth = depth;
   plan->ranks = int(std::min<int64_t>(per_simd, std::max<int64_t>(1, (waves + simds - 1) / simds)));
   plan->waves = waves;

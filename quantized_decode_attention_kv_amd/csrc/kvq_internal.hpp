@@ -122,7 +122,8 @@ hipError_t device_cus(int* dev, int* cus);
 // the matrix-core kernel's LDS ring depth and its grid.
 struct DecodePlan {
   int kernel;       // KVQ_KERNEL_MFMA or KVQ_KERNEL_VALU
-  int units;        // partial rows per query head
+  int units;        // work units per (batch, KV head) slab
+  int rows;         // partial rows per query head that the merge combines (1: none)
   int depth;        // key groups in a wave's LDS ring (matrix-core kernel), else 0
   int ranks;        // waves per SIMD of the matrix-core grid, else 0
   int64_t waves;    // waves the decode kernel launches
