@@ -27,10 +27,12 @@
 // unit or is cut into 2, 4 or 8 (see decode_mfma_units).  The four waves of a
 // workgroup form a team that shares one run of key groups of one (batch, kv head)
 // slab, wave w taking every fourth group from w (see Teams below); the run starts
-// come from the host with the launch.  Units share nothing and need no barriers: each stages
-// its groups through an LDS ring of D = 2 or 3 slots (buffer loads straight into
-// LDS, so up to D - 1 later groups are in flight while one is computed), keeps its
-// own online-softmax state and writes its own partial result.  The launcher takes
+// come from the host with the launch.  Units share nothing until their last step: each
+// stages its groups through an LDS ring of D = 2 or 3 slots (buffer loads straight
+// into LDS, so up to D - 1 later groups are in flight while one is computed) and
+// keeps its own online-softmax state; at the end the four units of a team combine
+// their states (one barrier) and the team writes one partial result per query
+// head (a unit that is a team of its own writes its own).  The launcher takes
 // D = 3 where the grid puts at most 2 waves on a SIMD and its LDS keeps the whole
 // grid resident, else 2 (the 128K- and 32K-token workloads: 16 waves per compute
 // unit on a 2-deep ring).  Per group:
@@ -362,7 +364,8 @@ __device__ __forceinline__ float query_allreduce(float v) {
 
 // Work units.  A unit is one wave; a team is TS units (4, one workgroup, or 1)
 // that share a contiguous run of key groups of one (batch, kv head) slab.  Units
-// are independent: no barriers, and each writes its own partial result.
+// are independent until the epilogue, where a team of 4 combines its units'
+// states after one barrier and writes one partial result.
 //
 // First key group of team t of T over nG groups, for R waves per SIMD.  The
 // workgroup dispatcher fills the SIMDs round-robin in grid order, so with the
