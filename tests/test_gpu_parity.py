@@ -136,6 +136,17 @@ def test_many_teams_one_slab():
     assert plans[64]["units"] == 512 and plans[256]["units"] == 2048, plans
 
 
+def test_units_per_slab_four_and_not_a_multiple_of_four():
+    """520 slabs with 2 or 3 partitions: the plan cuts each partition into 2 units,
+    so with 2 partitions a slab is one team of four units whose combined state is the
+    output itself (no merge), and with 3 partitions its 6 units are teams of their
+    own that each write a partial row (unit counts not a multiple of 4)."""
+    w = Workload("team_per_slab", B=130, Hq=16, Hkv=4, Dk=128, Dv=128, T=96, k_bits=4, v_bits=2, n_recent=32,
+                 dtype="bf16", partitions=2, seed=38)
+    _, _, plans = _run_small(w, partitions=[2, 3], kernel="mfma")
+    assert plans[2]["units"] == 4 and plans[3]["units"] == 6, plans
+
+
 @pytest.mark.parametrize("w", [
     Workload("one_group", B=1, Hq=4, Hkv=4, Dk=32, Dv=32, T=32, k_bits=2, v_bits=8, dtype="bf16", seed=31),
     Workload("all_fp16", B=2, Hq=8, Hkv=2, Dk=128, Dv=128, T=200, k_bits=4, v_bits=2, n_recent=200,
