@@ -138,10 +138,11 @@ hipError_t mfma_decode(const DecodeArgs& a, hipStream_t stream, DecodePlan* plan
 // The plan of a request (a.L, a.P, a.side_rank are read).
 hipError_t plan_decode(const DecodeArgs& a, DecodePlan* plan);
 // Bytes of partial rows a planned decode writes (0 when units == 1).
+// (sized by the unit count, an upper bound of the rows the kernels write)
 inline size_t plan_partial_bytes(const kvq_layout& L, const DecodePlan& p) {
   return p.units <= 1 ? 0 : size_t(L.B) * size_t(L.Hq) * size_t(p.units) * size_t(L.Dv + 4) * sizeof(float);
 }
-// Decode kernel of `plan` followed, when plan.units > 1, by the partition merge;
+// Decode kernel of `plan` followed, when plan.rows > 1, by the partition merge;
 // after_decode (if not null) is recorded on the stream between the two.
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream, hipEvent_t after_decode);
 
