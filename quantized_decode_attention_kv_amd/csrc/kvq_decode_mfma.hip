@@ -372,9 +372,12 @@ __device__ __forceinline__ float query_allreduce(float v) {
 // team-major grid and one team per resident workgroup the teams t < T/R become
 // the oldest waves on their SIMDs, the next T/R the second oldest, and so on;
 // waves are served oldest first, so run lengths fall by rank (integer weights
-// 100 + s (R - 1 - 2 r) for rank r, s = 16 / (R - 1): the oldest and youngest
-// rank differ by +-16%, measured on the 128K workload to bring the finish times
-// of the two waves of a SIMD within a few microseconds).
+// 100 + s (R - 1 - 2 r) for rank r, s = span / (R - 1): with 2 waves per SIMD
+// span 16, the oldest and youngest rank differing by +-16%, measured on the 128K
+// workload (then on 2048 waves) to bring the finish times of the two waves of a
+// SIMD within a few microseconds, and slower on the 16K workload with 28; with 3
+// or 4 waves per SIMD span 28 (128K workload on 4096 waves: 93.3 -> 91.5 and
+// 97.9 -> 96.2 us p50 inside the step on two boxes, interleaved)).
 // Retained fp16 rows come in 32-row tiles; unit u takes tiles u, u + U, ..., so
 // the waves of a team take the same number of tiles (tq, plus one in the first
 // ceil(tm / TS) teams, tm = tiles % U), and a team's run is shortened by what its
@@ -382,11 +385,8 @@ __device__ __forceinline__ float query_allreduce(float v) {
 // group per tile and wave) by rank weight, less their own tiles' cost.  The
 // cost is capped so that every team keeps at least one group, which keeps the
 // starts increasing.  Any split gives the same result up to rounding.
-#ifndef KVQ_UNIT_SKEW_SPAN
-#define KVQ_UNIT_SKEW_SPAN 16
-#endif
 __host__ __device__ inline int team_start(int t, int T, int TS, int nG, int R, int tq, int tm, int tc16) {
-  const int64_t s = R > 1 ? KVQ_UNIT_SKEW_SPAN / (R - 1) : 0;
+  const int64_t s = R > 1 ? (R > 2 ? 28 : 16) / (R - 1) : 0;
   int64_t wb = 0, wall = 0;
   for (int r = 0; r < R; ++r) {
     const int64_t lo = (int64_t(r) * T + R - 1) / R, hi = (int64_t(r + 1) * T + R - 1) / R;  // teams of rank r
