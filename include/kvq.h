@@ -80,7 +80,7 @@ extern "C" {
 typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_INVALID = 1,      /* bad argument (null pointer, out-of-range value, misalignment) */
-  KVQ_ERR_UNSUPPORTED = 2,  /* valid request this build does not handle (see limits below) */
+  KVQ_ERR_UNSUPPORTED = 2,  /* valid request the library does not handle (see limits below) */
   KVQ_ERR_HIP = 3           /* a HIP runtime call or kernel launch failed */
 } kvq_status;
 

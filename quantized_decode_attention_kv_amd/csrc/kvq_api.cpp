@@ -466,7 +466,7 @@ const char* kvq_status_string(int status) {
   switch (status) {
     case KVQ_OK: return "KVQ_OK";
     case KVQ_ERR_INVALID: return "KVQ_ERR_INVALID: invalid argument";
-    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED: request outside this build's limits";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED: request outside the library's limits";
     case KVQ_ERR_HIP: return "KVQ_ERR_HIP: HIP runtime error";
     default: return "unknown kvq status";
   }
