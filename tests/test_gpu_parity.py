@@ -345,7 +345,8 @@ def test_thin_keys_16k_full_size():
 @pytest.mark.slow
 def test_long_128k_full_size_and_prefill_chunk():
     """128K-token cache at 64 partitions, then the 8192-token prefill chunk re-packed
-    on its own into the same cache must leave every byte unchanged."""
+    on its own into the same cache must leave every byte unchanged, and that chunk's
+    part of the cache equals the oracle's on every slab."""
     w = workload("long_128k")
     Kd, Vd, qd, lay, cache = _full_size(w, 3)
     before = {k: v.clone() for k, v in cache.items()}
@@ -354,6 +355,23 @@ def test_long_128k_full_size_and_prefill_chunk():
     torch.cuda.synchronize()
     for k in cache:
         assert torch.equal(before[k], cache[k]), k
+    # The chunk's part of the cache on every slab against the oracle: with a
+    # window-only retention the chunk packs like a cache of its own length (its
+    # 8064 oldest tokens are the cache's last 252 key groups, its newest 128 the
+    # fp16 rows).
+    Kc = Kd[:, :, t0:].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    Vc = Vd[:, :, t0:].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    gpu_all = cache_to_numpy(cache)
+    nq = w.prefill_chunk - w.n_recent
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            ref = O.pack_slab(Kc[b, h], Vc[b, h], w.dtype, w.k_bits, w.v_bits, w.n_recent, w.log_window)
+            gpu = {"k_codes": gpu_all["k_codes"][b, h, -nq:], "k_scale": gpu_all["k_scale"][b, h, -nq // 32:],
+                   "k_zero": gpu_all["k_zero"][b, h, -nq // 32:], "v_codes": gpu_all["v_codes"][b, h, -nq // 32:],
+                   "v_scale": gpu_all["v_scale"][b, h, -nq // 32:], "v_zero": gpu_all["v_zero"][b, h, -nq // 32:],
+                   "k_fp16": gpu_all["k_fp16"][b, h], "v_fp16": gpu_all["v_fp16"][b, h]}
+            _compare_pack(gpu, ref, "%s chunk slab (%d,%d) " % (w.name, b, h))
+    _log("  prefill chunk: every slab's packed bytes equal the oracle's")
 
 
 def test_workspace_reuse_needs_no_initialisation():
