@@ -292,19 +292,20 @@ def variants_setup(api, w, Kd, Vd, lay, cache):
 
 def variants_run(torch, api, w, variants, qd, P, scale, reps=30):
     """Decode over each format variant, calls interleaved one by one so that all see
-    the same clock and thermal state; events around the decode kernel."""
+    the same clock and thermal state; events set by the decode kernel's launch
+    to its own start and end."""
     ws = {key: api.alloc_workspace(lv, P, qd.device) for key, (lv, _) in variants.items()}
     out = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.float32, device=qd.device)
     ev = {key: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)] for key in variants}
     for key in variants:
         for e in ev[key]:
-            e[1].record()
+            for x in e:
+                x.record()
     torch.cuda.synchronize()
     for i in range(reps):
         for key, (lv, c) in variants.items():
-            ev[key][i][0].record()
             api.kv_decode_attn(lv, qd, c, num_partitions=P, softmax_scale=scale, out=out, workspace=ws[key],
-                               after_decode_event=ev[key][i][1])
+                               kernel_events=(ev[key][i][0], ev[key][i][1]))
     torch.cuda.synchronize()
     res = {}
     for (kg, vg), (lv, _) in variants.items():
@@ -327,24 +328,31 @@ def decode_cold(torch, api, lay, cache, qd, P, scale, dev, reps=20):
     sink = torch.empty((), dtype=torch.int64, device=dev)
     ws = api.alloc_workspace(lay, P, dev)
     out = torch.empty((lay.B, lay.Hq, lay.Dv), dtype=torch.float32, device=dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(2 * reps)]
     for e in ev:
         for x in e:
             x.record()
     torch.cuda.synchronize()
-    for i in range(reps):
+    # alternate calls: the kernel's own events on one, events around a plain call
+    # on the next (a timed launch costs the call a few microseconds)
+    for i in range(2 * reps):
         torch.sum(flush, dim=0, out=sink)
-        ev[i][0].record()
-        api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws,
-                           after_decode_event=ev[i][1])
-        ev[i][2].record()
+        if i % 2 == 0:
+            api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws,
+                               kernel_events=(ev[i][0], ev[i][1]))
+        else:
+            ev[i][0].record()
+            api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws)
+            ev[i][1].record()
     torch.cuda.synchronize()
     del flush
-    kern = [e[0].elapsed_time(e[1]) for e in ev]
-    call = [e[0].elapsed_time(e[2]) for e in ev]
+    kern = [e[0].elapsed_time(e[1]) for e in ev[0::2]]
+    call = [e[0].elapsed_time(e[1]) for e in ev[1::2]]
     return {"kernel_us_p10_p50_p90": percentiles(kern), "kernel_us_mean": round(sum(kern) * 1e3 / reps, 2),
             "call_us_p10_p50_p90": percentiles(call), "call_us_mean": round(sum(call) * 1e3 / reps, 2),
-            "how": "1 GiB untimed read before each of %d calls" % reps}
+            "how": "1 GiB untimed read before each of 2 x %d calls; kernel: the decode kernel's start and stop "
+                   "events (hipExtLaunchKernel) on every other call, call: events around the other, plain calls"
+                   % reps}
 
 
 def decode_back_to_back(torch, api, lay, cache, qd, P, scale, dev, reps=20):
@@ -359,13 +367,12 @@ def decode_back_to_back(torch, api, lay, cache, qd, P, scale, dev, reps=20):
             x.record()
     torch.cuda.synchronize()
     for i in range(reps):
-        ev[i][0].record()
         api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws,
-                           after_decode_event=ev[i][1])
+                           kernel_events=(ev[i][0], ev[i][1]))
     torch.cuda.synchronize()
     kern = [e[0].elapsed_time(e[1]) for e in ev]
     return {"kernel_us_p10_p50_p90": percentiles(kern), "kernel_us_mean": round(sum(kern) * 1e3 / reps, 2),
-            "how": "%d calls back to back, events before each call and after its decode kernel" % reps}
+            "how": "%d calls back to back, events set by each decode kernel's launch to its own start and end" % reps}
 
 
 # Decode alone on the other workloads of the list (each its own cache).
@@ -413,7 +420,9 @@ def decode_config(torch, api, name, dev, reps, with_cpu):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": read_traffic(name),
                      "kernel": "decode_%s_kernel (first kernel of kv_decode_attn)" % plan["kernel"],
-                     "kernel_us": kern_us, "timing": "HIP events, mean over the cold calls",
+                     "kernel_us": kern_us,
+                     "timing": "HIP events set by the decode kernel's launch (hipExtLaunchKernel) to its own start "
+                               "and end, mean over the cold calls",
                      "rocprof_kernel_us": rp_us,
                      "frac_rocprof": None if rp_us is None else round(db / (rp_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
     }
@@ -551,21 +560,24 @@ def main():
     torch.cuda.synchronize()
 
     # Events on the stream the kernels run on.  The timed steps carry only the two
-    # the roofline needs: before the decode call and after its decode kernel (the
-    # library records the latter between the decode and the merge kernel); every
-    # event recorded costs the step time (measured ~2 us each), so the pack and merge
-    # are timed in a separate breakdown pass right after, with all four events.
+    # the roofline needs, which the decode kernel's launch sets to that kernel's own
+    # start and end; the pack and merge are timed in a separate breakdown pass right
+    # after, with four events recorded between the kernels (each such record costs
+    # the step a few microseconds).
     def step(ev=None, full=False):
         if full:
             ev[0].record()
         if chunk:
             api.kv_quant_pack(lay, Kc, Vc, cache=cache, t_begin=t0)
-        if ev is not None:
-            ev[1].record()
-        api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws,
-                           after_decode_event=None if ev is None else ev[2])
         if full:
+            ev[1].record()
+            api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws,
+                               after_decode_event=ev[2])
             ev[3].record()
+        else:
+            # ev[1], ev[2]: set by the decode kernel's launch to its own start and end
+            api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws,
+                               kernel_events=None if ev is None else (ev[1], ev[2]))
 
     def new_events(n):
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
@@ -578,8 +590,7 @@ def main():
     print("# %s: warmup %d" % (w.name, args.warmup), file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
-    # Every event recorded between two kernels holds the next one back until the
-    # previous has drained (measured: about 6 us per event), so only every
+    # A timed launch may hold the next kernel back a little, so only every
     # event_every-th timed step carries the two decode events; the others run as
     # they would in a decode loop.
     ev_steps = list(range(0, args.steps, max(1, args.event_every)))
@@ -598,6 +609,7 @@ def main():
     torch.cuda.synchronize()
     pack_ms = sum(e[0].elapsed_time(e[1]) for e in bd) / n_bd
     dec_ms = sum(e[1].elapsed_time(e[3]) for e in bd) / n_bd
+    gap_kern_ms = sum(e[1].elapsed_time(e[2]) for e in bd) / n_bd
     merge_ms = sum(e[2].elapsed_time(e[3]) for e in bd) / n_bd
     ms_per_step = wall * 1e3 / args.steps
 
@@ -650,6 +662,7 @@ def main():
                    "pct_of_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
                    "steps_per_s": round(1e3 / dec_ms, 1), "tokens_per_s": round(w.B * 1e3 / dec_ms, 1),
                    "kernel_us": round(kern_ms * 1e3, 2), "merge_us": round(merge_ms * 1e3, 2),
+                   "kernel_us_with_dispatch_gap": round(gap_kern_ms * 1e3, 2),
                    "kernel_us_p10_p50_p90": percentiles([e[1].elapsed_time(e[2]) for e in events]),
                    "cold": cold, "algorithmic_bytes": db},
         "pack": ({"us": round(pack_ms * 1e3, 2), "GBps": round(pb / (pack_ms * 1e-3) / 1e9, 1),
@@ -660,8 +673,9 @@ def main():
                      "frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "decode_mfma_kernel (first kernel of kv_decode_attn)",
                      "kernel_us": round(kern_ms * 1e3, 2),
-                     "timing": "HIP events: before the decode call to after its decode kernel (includes the "
-                               "dispatch gap), mean over %d of the %d timed steps (every %d-th)"
+                     "timing": "HIP events set by the decode kernel's launch (hipExtLaunchKernel) to its own start "
+                               "and end, mean over %d of the %d timed steps (every %d-th); with the dispatch gap "
+                               "before it (events around the call, breakdown pass): decode.kernel_us_with_dispatch_gap"
                                % (len(events), args.steps, max(1, args.event_every)),
                      "rocprof_kernel_us": rp_us,
                      "frac_rocprof": None if rp_us is None else round(db / (rp_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),

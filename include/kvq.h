@@ -219,6 +219,20 @@ int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq
                       float* out, void* stream, void* event_after_decode);
 
 /*
+ * kv_decode_attn_timed — kv_decode_attn for callers that time the decode kernel
+ * alone (the work unit whose bytes the decode's roofline counts).  kernel_start,
+ * kernel_stop: hipEvent_t handles created by the caller (either may be NULL, both
+ * NULL = kv_decode_attn).  The decode kernel is launched with hipExtLaunchKernel,
+ * which sets them to that kernel's own start and end, so the interval between them
+ * is the kernel's duration without the dispatch gap before it; the merge kernel
+ * (when P > 1) follows untimed.  A failed launch returns KVQ_ERR_HIP.  All other
+ * arguments, results and errors as kv_decode_attn.
+ */
+int kv_decode_attn_timed(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache,
+                         float softmax_scale, int num_partitions, void* workspace, size_t workspace_bytes,
+                         float* out, void* stream, void* kernel_start, void* kernel_stop);
+
+/*
  * kv_decode_attn_noalloc — kv_decode_attn for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): the same arguments without the workspace, and the same kernels.

@@ -25,7 +25,7 @@ EXPORTS = ["kvq_layout_init", "kvq_cache_sizes", "kvq_retained_positions", "kvq_
            "kvq_stream_cache_sizes",
            "kvq_stream_workspace_bytes", "kvq_stream_plan", "kv_stream_prefill", "kv_stream_append",
            "kv_stream_decode", "kvq_side_sizes", "kv_side_pack", "kv_decode_attn_side", "kvq_decode_plan",
-           "kv_decode_attn_noalloc", "kvq_layout_set_flags", "kvq_stream_set_flags"]
+           "kv_decode_attn_noalloc", "kv_decode_attn_timed", "kvq_layout_set_flags", "kvq_stream_set_flags"]
 
 KVQ_KERNEL_MFMA, KVQ_KERNEL_VALU = 1, 2
 KVQ_STATIC_SCRATCH_BYTES = 16 << 20
@@ -101,6 +101,8 @@ def load() -> ctypes.CDLL:
     lib.kv_decode_attn.restype = c_int
     lib.kv_decode_attn_ex.argtypes = [LP, vp, c_int, CP, ctypes.c_float, c_int, vp, c_sz, vp, vp, vp]
     lib.kv_decode_attn_ex.restype = c_int
+    lib.kv_decode_attn_timed.argtypes = [LP, vp, c_int, CP, ctypes.c_float, c_int, vp, c_sz, vp, vp, vp, vp]
+    lib.kv_decode_attn_timed.restype = c_int
     lib.kv_decode_attn_noalloc.argtypes = [LP, vp, c_int, CP, ctypes.c_float, c_int, vp, vp]
     lib.kv_decode_attn_noalloc.restype = c_int
     lib.kvq_decode_plan.argtypes = [LP, c_int, c_int, ctypes.POINTER(KvqDecodeInfo)]

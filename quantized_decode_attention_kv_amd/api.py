@@ -163,12 +163,15 @@ def kv_quant_pack(layout: Layout, K, V, cache=None, t_begin: int = 0, stream=Non
 
 
 def kv_decode_attn(layout: Layout, q, cache, num_partitions: int = 1, softmax_scale=None, out=None,
-                   workspace=None, stream=None, after_decode_event=None):
+                   workspace=None, stream=None, after_decode_event=None, kernel_events=None):
     """Decode attention of q [B, Hq, Dk] over a packed cache -> float32 [B, Hq, Dv].
 
     after_decode_event: optional torch.cuda.Event, recorded on the stream between
-    the decode kernel and the merge kernel (it must have been recorded once
-    before, so that torch has created it)."""
+    the decode kernel and the merge kernel (C ABI kv_decode_attn_ex).
+    kernel_events: optional pair of torch.cuda.Event (start, stop) that the decode
+    kernel's launch sets to its own start and end (C ABI kv_decode_attn_timed);
+    not together with after_decode_event.  Events must have been recorded once
+    before, so that torch has created them."""
     _check_tensor("q", q, (layout.B, layout.Hq, layout.Dk))
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(layout.Dk)
@@ -182,6 +185,17 @@ def kv_decode_attn(layout: Layout, q, cache, num_partitions: int = 1, softmax_sc
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     cs = _cache_struct(layout, cache)
+    if kernel_events is not None:
+        if after_decode_event is not None:
+            raise ValueError("kernel_events and after_decode_event are exclusive")
+        k0, k1 = (e.cuda_event for e in kernel_events)
+        if not k0 or not k1:
+            raise ValueError("kernel_events have not been created yet (record them once first)")
+        L_.check(L_.load().kv_decode_attn_timed(layout.ref, ctypes.c_void_p(q.data_ptr()), _DTYPE_CODES[q.dtype],
+                                                ctypes.byref(cs), ctypes.c_float(softmax_scale), num_partitions,
+                                                ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(out.data_ptr()),
+                                                _stream(stream, q), ctypes.c_void_p(k0), ctypes.c_void_p(k1)))
+        return out
     ev = None
     if after_decode_event is not None:
         ev = after_decode_event.cuda_event

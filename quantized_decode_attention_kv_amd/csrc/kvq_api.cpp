@@ -127,7 +127,8 @@ int kvq::check_cache_ptr(const void* p, const char* name) {
 int kvq::decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, const void* q, int q_dtype,
                      const kvq_cache* cache, float softmax_scale, int num_partitions, void* workspace,
                      size_t workspace_bytes, float* out, void* stream, void* event_after_decode,
-                     const DecodeArgs* side, int workspace_short_status) {
+                     const DecodeArgs* side, int workspace_short_status, void* kernel_start,
+                     void* kernel_stop) {
   int st;
   if (!cache) return fail(KVQ_ERR_INVALID, "cache is NULL");
   if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID, "q_dtype %d is not KVQ_F32/F16/BF16", q_dtype);
@@ -163,6 +164,8 @@ int kvq::decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, co
   a.g_stride = g_stride;
   a.r_stride = r_stride;
   a.out = out;
+  a.kernel_start = static_cast<hipEvent_t>(kernel_start);
+  a.kernel_stop = static_cast<hipEvent_t>(kernel_stop);
   if (side) {
     a.side_u = side->side_u;
     a.side_codes = side->side_codes;
@@ -343,6 +346,16 @@ int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq
   if (st != KVQ_OK) return st;
   return kvq::decode_view(*L, L->n_groups, L->R, q, q_dtype, cache, softmax_scale, num_partitions, workspace,
                           workspace_bytes, out, stream, event_after_decode);
+}
+
+int kv_decode_attn_timed(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache,
+                         float softmax_scale, int num_partitions, void* workspace, size_t workspace_bytes,
+                         float* out, void* stream, void* kernel_start, void* kernel_stop) {
+  const int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  return kvq::decode_view(*L, L->n_groups, L->R, q, q_dtype, cache, softmax_scale, num_partitions, workspace,
+                          workspace_bytes, out, stream, nullptr, nullptr, KVQ_ERR_INVALID, kernel_start,
+                          kernel_stop);
 }
 
 int kv_decode_attn_noalloc(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache,

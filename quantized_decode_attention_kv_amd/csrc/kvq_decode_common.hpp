@@ -10,12 +10,23 @@
 // Cache", section 4).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.hpp"
 
 namespace kvq {
+
+// Launch of a decode kernel whose one argument is `a` through hipExtLaunchKernel,
+// which sets a.kernel_start / a.kernel_stop to the kernel's own start and end (so
+// their interval leaves out the dispatch gap before the kernel).  The callers take
+// this path only when one of the two events is set.
+inline hipError_t launch_decode_timed(const void* kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                                      DecodeArgs a) {
+  void* args[] = {&a};
+  return hipExtLaunchKernel(kernel, grid, block, args, lds, stream, a.kernel_start, a.kernel_stop, 0);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDecodeThreads = 256;

@@ -404,6 +404,9 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
       if (bit) done.fetch_or(bit, std::memory_order_release);
     }
   }
+  if (a.kernel_start || a.kernel_stop)
+    return launch_decode_timed(reinterpret_cast<const void*>(&decode_kernel<G, QDT>), grid, dim3(kThreads), lds,
+                               stream, a);
   hipLaunchKernelGGL((decode_kernel<G, QDT>), grid, dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }

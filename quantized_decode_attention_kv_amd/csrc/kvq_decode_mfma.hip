@@ -1231,6 +1231,9 @@ hipError_t launch_depth(DecodeArgs a, hipStream_t stream, int dev, const DecodeP
     if (e != hipSuccess) return e;
   }
   const int64_t blocks = (plan.waves + kWavesPerGroup - 1) / kWavesPerGroup;
+  if (a.kernel_start || a.kernel_stop)
+    return launch_decode_timed(reinterpret_cast<const void*>(&decode_mfma_kernel<DK, DV, KB, VB, D>),
+                               dim3(unsigned(blocks)), dim3(64 * kWavesPerGroup), lds, stream, a);
   hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, KB, VB, D>), dim3(unsigned(blocks)), dim3(64 * kWavesPerGroup), lds,
                      stream, a);
   return hipGetLastError();

@@ -47,6 +47,8 @@ struct DecodeArgs {
   const uint16_t* side_scale; // [B, Hkv, g_stride * 32] fp16
   const uint16_t* side_zero;
   int side_rank;
+  // host side only: timing events of the decode kernel's own dispatch (null: none)
+  hipEvent_t kernel_start, kernel_stop;
 };
 
 // Side-code write of the HeadQ mechanics: one workgroup per (code group, kv head, batch)
@@ -161,6 +163,7 @@ int pack_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, int64_t t
 int decode_view(const kvq_layout& L, int64_t g_stride, int64_t r_stride, const void* q, int q_dtype,
                 const kvq_cache* cache, float softmax_scale, int num_partitions, void* workspace,
                 size_t workspace_bytes, float* out, void* stream, void* event_after_decode,
-                const DecodeArgs* side = nullptr, int workspace_short_status = KVQ_ERR_INVALID);
+                const DecodeArgs* side = nullptr, int workspace_short_status = KVQ_ERR_INVALID,
+                void* kernel_start = nullptr, void* kernel_stop = nullptr);
 
 }  // namespace kvq

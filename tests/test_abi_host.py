@@ -180,6 +180,11 @@ def test_decode_errors(lib):
     bad = _cache()
     bad.v_codes = None
     assert dec(cache=bad) == L_.KVQ_ERR_INVALID
+    # the timed entry point runs the same checks before any launch
+    timed = lambda q=FAKE, P=4: lib.kv_decode_attn_timed(ctypes.byref(lay), q, L_.KVQ_BF16, ctypes.byref(c),
+                                                         ctypes.c_float(0.1), P, FAKE, need, FAKE, None, None, None)
+    assert timed(q=None) == L_.KVQ_ERR_INVALID
+    assert timed(P=35) == L_.KVQ_ERR_INVALID
 
 
 def test_read_probe_errors(lib):

@@ -399,6 +399,42 @@ def test_workspace_reuse_needs_no_initialisation():
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[3])
 
 
+@pytest.mark.parametrize("name,kernel", [("small_k4v2_win", "mfma"), ("small_k4v8_f32", "valu")])
+def test_timed_decode_events(name, kernel):
+    """kv_decode_attn_timed: the same output bits as kv_decode_attn, with its two
+    events set to the decode kernel's own start and end: a positive interval that
+    lies inside events recorded around the whole call, for both decode kernels, at
+    P = 1 (no merge) and at the configured P."""
+    w = {c.name: c for c in small_cases()}[name]
+    K, V = make_all(w, workers=4)
+    q = make_queries(w)
+    lay = api.Layout.from_workload(w)
+    cache = api.kv_quant_pack(lay, to_device(K, w.dtype), to_device(V, w.dtype))
+    qd = to_device(q, w.dtype)
+    scale = float(O.default_scale(w.Dk))
+    want = O.decode_all(q, O.pack_all(K, V, w), w, scale)
+    for P in (1, w.partitions):
+        plan = api.decode_plan(lay, P)
+        assert plan["kernel"] == kernel, (name, P, plan)
+        plain = api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in ev:
+            e.record()
+        torch.cuda.synchronize()
+        ev[0].record()
+        timed = api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale,
+                                   kernel_events=(ev[1], ev[2]))
+        ev[3].record()
+        torch.cuda.synchronize()
+        assert torch.equal(plain.cpu(), timed.cpu()), (name, P)
+        err = np.abs(timed.cpu().numpy().astype(np.float64) - want).max()
+        assert err <= MAX_ABS_ERR, (name, P, err)
+        kern, call = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+        before, after = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+        _log("%s P=%d kernel %.1f us, call %.1f us" % (name, P, kern * 1e3, call * 1e3))
+        assert 0 < kern <= call and before >= 0 and after >= 0, (name, P, kern, call, before, after)
+
+
 @pytest.mark.gpu
 def test_read_probe_runs():
     """The measurement probe reads a buffer (with a tail that is not a whole
