@@ -292,8 +292,8 @@ def variants_setup(api, w, Kd, Vd, lay, cache):
 
 def variants_run(torch, api, w, variants, qd, P, scale, reps=30):
     """Decode over each format variant, calls interleaved one by one so that all see
-    the same clock and thermal state; events set by the decode kernel's launch
-    to its own start and end."""
+    the same clock and thermal state; the start and stop events of each decode
+    kernel's launch."""
     ws = {key: api.alloc_workspace(lv, P, qd.device) for key, (lv, _) in variants.items()}
     out = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.float32, device=qd.device)
     ev = {key: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)] for key in variants}
@@ -372,7 +372,7 @@ def decode_back_to_back(torch, api, lay, cache, qd, P, scale, dev, reps=20):
     torch.cuda.synchronize()
     kern = [e[0].elapsed_time(e[1]) for e in ev]
     return {"kernel_us_p10_p50_p90": percentiles(kern), "kernel_us_mean": round(sum(kern) * 1e3 / reps, 2),
-            "how": "%d calls back to back, events set by each decode kernel's launch to its own start and end" % reps}
+            "how": "%d calls back to back, the start and stop events of each decode kernel's launch" % reps}
 
 
 # Decode alone on the other workloads of the list (each its own cache).
@@ -421,8 +421,8 @@ def decode_config(torch, api, name, dev, reps, with_cpu):
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": read_traffic(name),
                      "kernel": "decode_%s_kernel (first kernel of kv_decode_attn)" % plan["kernel"],
                      "kernel_us": kern_us,
-                     "timing": "HIP events set by the decode kernel's launch (hipExtLaunchKernel) to its own start "
-                               "and end, mean over the cold calls",
+                     "timing": "HIP start and stop events of the decode kernel's launch (hipExtLaunchKernel), "
+                               "mean over the cold calls",
                      "rocprof_kernel_us": rp_us,
                      "frac_rocprof": None if rp_us is None else round(db / (rp_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
     }
@@ -560,8 +560,8 @@ def main():
     torch.cuda.synchronize()
 
     # Events on the stream the kernels run on.  The timed steps carry only the two
-    # the roofline needs, which the decode kernel's launch sets to that kernel's own
-    # start and end; the pack and merge are timed in a separate breakdown pass right
+    # the roofline needs, the start and stop events of the decode kernel's launch
+    # (hipExtLaunchKernel); the pack and merge are timed in a separate breakdown pass right
     # after, with four events recorded between the kernels (each such record costs
     # the step a few microseconds).
     def step(ev=None, full=False):
@@ -575,7 +575,7 @@ def main():
                                after_decode_event=ev[2])
             ev[3].record()
         else:
-            # ev[1], ev[2]: set by the decode kernel's launch to its own start and end
+            # ev[1], ev[2]: the start and stop events of the decode kernel's launch
             api.kv_decode_attn(lay, qd, cache, num_partitions=P, softmax_scale=scale, out=out, workspace=ws,
                                kernel_events=None if ev is None else (ev[1], ev[2]))
 
@@ -673,8 +673,8 @@ def main():
                      "frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "decode_mfma_kernel (first kernel of kv_decode_attn)",
                      "kernel_us": round(kern_ms * 1e3, 2),
-                     "timing": "HIP events set by the decode kernel's launch (hipExtLaunchKernel) to its own start "
-                               "and end, mean over %d of the %d timed steps (every %d-th); with the dispatch gap "
+                     "timing": "HIP start and stop events of the decode kernel's launch (hipExtLaunchKernel), "
+                               "mean over %d of the %d timed steps (every %d-th); with the dispatch gap "
                                "before it (events around the call, breakdown pass): decode.kernel_us_with_dispatch_gap"
                                % (len(events), args.steps, max(1, args.event_every)),
                      "rocprof_kernel_us": rp_us,

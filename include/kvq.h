@@ -222,10 +222,10 @@ int kv_decode_attn_ex(const kvq_layout* L, const void* q, int q_dtype, const kvq
  * kv_decode_attn_timed — kv_decode_attn for callers that time the decode kernel
  * alone (the work unit whose bytes the decode's roofline counts).  kernel_start,
  * kernel_stop: hipEvent_t handles created by the caller (either may be NULL, both
- * NULL = kv_decode_attn).  The decode kernel is launched with hipExtLaunchKernel,
- * which sets them to that kernel's own start and end, so the interval between them
- * is the kernel's duration without the dispatch gap before it; the merge kernel
- * (when P > 1) follows untimed.  A failed launch returns KVQ_ERR_HIP.  All other
+ * NULL = kv_decode_attn).  The decode kernel is launched with hipExtLaunchKernel
+ * with them as its start and stop events (the runtime's timing of that one kernel
+ * command, which leaves out the host's launch time); the merge kernel (when P > 1)
+ * follows untimed.  A failed launch returns KVQ_ERR_HIP.  All other
  * arguments, results and errors as kv_decode_attn.
  */
 int kv_decode_attn_timed(const kvq_layout* L, const void* q, int q_dtype, const kvq_cache* cache,

@@ -168,8 +168,8 @@ def kv_decode_attn(layout: Layout, q, cache, num_partitions: int = 1, softmax_sc
 
     after_decode_event: optional torch.cuda.Event, recorded on the stream between
     the decode kernel and the merge kernel (C ABI kv_decode_attn_ex).
-    kernel_events: optional pair of torch.cuda.Event (start, stop) that the decode
-    kernel's launch sets to its own start and end (C ABI kv_decode_attn_timed);
+    kernel_events: optional pair of torch.cuda.Event (start, stop), the start and
+    stop events of the decode kernel's launch (C ABI kv_decode_attn_timed);
     not together with after_decode_event.  Events must have been recorded once
     before, so that torch has created them."""
     _check_tensor("q", q, (layout.B, layout.Hq, layout.Dk))

@@ -19,9 +19,9 @@
 namespace kvq {
 
 // Launch of a decode kernel whose one argument is `a` through hipExtLaunchKernel,
-// which sets a.kernel_start / a.kernel_stop to the kernel's own start and end (so
-// their interval leaves out the dispatch gap before the kernel).  The callers take
-// this path only when one of the two events is set.
+// with a.kernel_start / a.kernel_stop as the start and stop events of that one
+// kernel command (the runtime's timing of it).  The callers take this path only
+// when one of the two events is set.
 inline hipError_t launch_decode_timed(const void* kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
                                       DecodeArgs a) {
   void* args[] = {&a};

@@ -402,7 +402,7 @@ def test_workspace_reuse_needs_no_initialisation():
 @pytest.mark.parametrize("name,kernel", [("small_k4v2_win", "mfma"), ("small_k4v8_f32", "valu")])
 def test_timed_decode_events(name, kernel):
     """kv_decode_attn_timed: the same output bits as kv_decode_attn, with its two
-    events set to the decode kernel's own start and end: a positive interval that
+    events as the start and stop events of the decode kernel: a positive interval that
     lies inside events recorded around the whole call, for both decode kernels, at
     P = 1 (no merge) and at the configured P."""
     w = {c.name: c for c in small_cases()}[name]
